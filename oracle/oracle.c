@@ -1,0 +1,317 @@
+/*
+ * CPU oracle for sparse matrix-vector multiplication and for the storage
+ * format conversions -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * load this library.  It shares no code, header, table or helper with the GPU
+ * library: it is a plain, slow, obviously correct statement of what the GPU
+ * path must compute, used to check it.
+ *
+ * What it computes (the pages' definitions restated):
+ *
+ *   spmv:  y_i = alpha * sum_{k in row i} val[k] * x[col[k]] + beta * y_i
+ *          over the stored entries of a CSR matrix (the sparse mat-vec whose
+ *          storage variants are compared in "Sparse matrix-vector
+ *          multiplication on GPGPU clusters", Sect. 2, and in "Development of
+ *          Krylov and AMG linear solvers...", Sect. 2.1, Figs. 1-3).
+ *          Duplicated (row, col) entries are summed: the matrix is the sum
+ *          of its stored triples.  beta == 0 means y is not read.
+ *          Each row sum is accumulated in fp64 with the compensated dot
+ *          product "Dot2" of Ogita, Rump and Oishi ("Accurate sum and dot
+ *          product", SIAM J. Sci. Comput. 26(6), 2005, Algorithm 5.3): a
+ *          TwoProduct error-free split of every product, a TwoSum of the
+ *          running sum, and a separately accumulated correction term.  The
+ *          result is as accurate as if computed in twice the working
+ *          precision and rounded once.  The scale d_i = |alpha| * sum |a*x|
+ *          + |beta * y_i| is returned beside it for the tolerance test.
+ *
+ *   converters (bit-exact references for the GPU-built layouts):
+ *     ELLPACK-R  -- rows shifted left into an N x Nmax rectangle stored
+ *                   column by column, with the row count padded to a
+ *                   multiple of the SIMD width (64 here) and a per-row
+ *                   length array ("Sparse matrix-vector multiplication on
+ *                   GPGPU clusters", Sect. 2.1, Fig. 1 and footnote 2).
+ *     SELL-64    -- the pJDS idea of the same page (Sect. 2.2, Fig. 1 "sort"
+ *                   and "pad"): rows sorted by length, longest first, in
+ *                   blocks of 64 rows padded to the block's longest row;
+ *                   stored slice by slice with a row permutation.
+ *     HYB / HEC  -- a regular ELL part of width K plus the remaining
+ *                   entries of each row as COO (HYB) or CSR (HEC)
+ *                   ("Development of Krylov and AMG linear solvers...",
+ *                   Sect. 2.1, Figs. 2-3; "Load-balancing Sparse Matrix
+ *                   Vector Product Kernels on GPUs", abstract).
+ *   Where the pages leave a convention open the reading taken is:
+ *     - ELL stride S = 64 * ceil(n / 64); slot (i, j) at j * S + i; pad
+ *       slots hold column 0 and value +0.0; padded rows have length 0.
+ *     - SELL sort key (length descending, row ascending) -- unique, so the
+ *       permutation is unique; slice s has width w_s = length of its first
+ *       (longest) row; entry j of sorted row r sits at
+ *       slice_ptr[r / 64] + 64 * j + r % 64.
+ *     - HYB/HEC width K = max{k >= 0 : #{i : len_i >= k} >= ceil(n / 3)}
+ *       unless a width is given (clamped to the longest row); the first K
+ *       entries of each row (CSR order) go to the ELL part, the rest to the
+ *       tail in row order.
+ *
+ * Values are handled as opaque bytes of the stated element size in the
+ * converters, so the references move value bits exactly.
+ *
+ * Built with -O2 -ffp-contract=off and without fast-math, so that the only
+ * fused multiply-add is the explicit fma() of TwoProduct.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------------- */
+/* error-free transformations                                              */
+/* ---------------------------------------------------------------------- */
+
+/* Knuth's TwoSum: s + e == a + b exactly, s = fl(a + b). */
+static void two_sum(double a, double b, double *s, double *e)
+{
+    double x = a + b;
+    double z = x - a;
+    *e = (a - (x - z)) + (b - z);
+    *s = x;
+}
+
+/* TwoProduct via FMA: p + e == a * b exactly, p = fl(a * b). */
+static void two_prod(double a, double b, double *p, double *e)
+{
+    double x = a * b;
+    *e = fma(a, b, -x);
+    *p = x;
+}
+
+/* Dot2 over one CSR row, plus the plain sum of |a * x| for the scale. */
+static double row_dot2(int64_t k0, int64_t k1, const int32_t *col,
+                       const double *val, const double *x, double *absum)
+{
+    double s = 0.0, c = 0.0, ab = 0.0;
+    for (int64_t k = k0; k < k1; ++k) {
+        double p, ep, q;
+        two_prod(val[k], x[col[k]], &p, &ep);
+        two_sum(s, p, &s, &q);
+        c += q + ep;
+        ab += fabs(p);
+    }
+    *absum = ab;
+    return s + c;
+}
+
+/*
+ * y_out[i] = alpha * A x + beta * y_in[i] for every row (or for the rows
+ * listed in `rows` when rows != NULL; then y_out/scale_out are indexed by
+ * position in that list and y_in by row).  y_in may be NULL when beta == 0.
+ * nthreads <= 0 lets OpenMP choose; 1 runs serially.  Returns 0.
+ */
+int oracle_spmv(int64_t n, const int64_t *rowptr, const int32_t *col,
+                const double *val, const double *x, const double *y_in,
+                double alpha, double beta, double *y_out, double *scale_out,
+                const int64_t *rows, int64_t nrows, int nthreads)
+{
+    int64_t m = rows ? nrows : n;
+#ifdef _OPENMP
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nt)
+#endif
+    for (int64_t t = 0; t < m; ++t) {
+        int64_t i = rows ? rows[t] : t;
+        double ab;
+        double r = row_dot2(rowptr[i], rowptr[i + 1], col, val, x, &ab);
+        double yv;
+        double sc = fabs(alpha) * ab;
+        if (beta == 0.0) {
+            yv = alpha * r;
+        } else {
+            double by = beta * y_in[i];
+            yv = alpha * r + by;
+            sc += fabs(by);
+        }
+        y_out[t] = yv;
+        if (scale_out)
+            scale_out[t] = sc;
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* number of threads OpenMP would use by default (1 without OpenMP) */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------------- */
+/* converters                                                              */
+/* ---------------------------------------------------------------------- */
+
+static int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
+/* longest row */
+int64_t oracle_max_len(int64_t n, const int64_t *rowptr)
+{
+    int64_t w = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t l = rowptr[i + 1] - rowptr[i];
+        if (l > w)
+            w = l;
+    }
+    return w;
+}
+
+/*
+ * ELLPACK-R of width W (W >= every row length handled; entries j >= W of a
+ * row are skipped, which is how the ELL part of HYB/HEC is built).
+ * out_col/out_val hold W * S slots, out_len S lengths, S = pad64(n).
+ */
+void oracle_ell(int64_t n, const int64_t *rowptr, const int32_t *col,
+                const void *val, int vsize, int64_t W,
+                int32_t *out_col, void *out_val, int32_t *out_len)
+{
+    int64_t S = pad64(n);
+    char *ov = (char *)out_val;
+    const char *iv = (const char *)val;
+    memset(out_col, 0, (size_t)(W * S) * sizeof(int32_t));
+    memset(ov, 0, (size_t)(W * S) * (size_t)vsize);
+    for (int64_t i = 0; i < S; ++i)
+        out_len[i] = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t len = rowptr[i + 1] - rowptr[i];
+        if (len > W)
+            len = W;
+        out_len[i] = (int32_t)len;
+        for (int64_t j = 0; j < len; ++j) {
+            int64_t slot = j * S + i;
+            int64_t k = rowptr[i] + j;
+            out_col[slot] = col[k];
+            memcpy(ov + slot * vsize, iv + k * vsize, (size_t)vsize);
+        }
+    }
+}
+
+/* sort key: length descending, then row ascending */
+static const int64_t *g_rowptr;
+static int cmp_rows(const void *pa, const void *pb)
+{
+    int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    int64_t la = g_rowptr[a + 1] - g_rowptr[a];
+    int64_t lb = g_rowptr[b + 1] - g_rowptr[b];
+    if (la != lb)
+        return la > lb ? -1 : 1;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+/*
+ * SELL-64 layout sizes and permutation.  perm[r] (r < pad64(n)) is the
+ * original row at sorted position r (rows >= n are padding, perm = -1 kept
+ * out: perm has n entries); slice_ptr has nslices + 1 entries; len_sorted has
+ * pad64(n) entries.  Returns the total number of slots.
+ */
+int64_t oracle_sell_layout(int64_t n, const int64_t *rowptr, int64_t *perm,
+                           int64_t *slice_ptr, int32_t *len_sorted)
+{
+    int64_t S = pad64(n), ns = S / 64;
+    for (int64_t i = 0; i < n; ++i)
+        perm[i] = i;
+    g_rowptr = rowptr;
+    qsort(perm, (size_t)n, sizeof(int64_t), cmp_rows);
+    for (int64_t r = 0; r < S; ++r)
+        len_sorted[r] = r < n ? (int32_t)(rowptr[perm[r] + 1] - rowptr[perm[r]]) : 0;
+    slice_ptr[0] = 0;
+    for (int64_t s = 0; s < ns; ++s)
+        slice_ptr[s + 1] = slice_ptr[s] + 64 * (int64_t)len_sorted[64 * s];
+    return slice_ptr[ns];
+}
+
+/* SELL-64 fill given the layout from oracle_sell_layout */
+void oracle_sell_fill(int64_t n, const int64_t *rowptr, const int32_t *col,
+                      const void *val, int vsize, const int64_t *perm,
+                      const int64_t *slice_ptr, int32_t *out_col, void *out_val)
+{
+    int64_t S = pad64(n), ns = S / 64;
+    int64_t total = slice_ptr[ns];
+    char *ov = (char *)out_val;
+    const char *iv = (const char *)val;
+    memset(out_col, 0, (size_t)total * sizeof(int32_t));
+    memset(ov, 0, (size_t)total * (size_t)vsize);
+    for (int64_t r = 0; r < n; ++r) {
+        int64_t i = perm[r];
+        int64_t len = rowptr[i + 1] - rowptr[i];
+        for (int64_t j = 0; j < len; ++j) {
+            int64_t slot = slice_ptr[r / 64] + 64 * j + r % 64;
+            int64_t k = rowptr[i] + j;
+            out_col[slot] = col[k];
+            memcpy(ov + slot * vsize, iv + k * vsize, (size_t)vsize);
+        }
+    }
+}
+
+/* HYB/HEC ELL width: the ceil(n/3) rule, or the requested width clamped */
+int64_t oracle_hyb_width(int64_t n, const int64_t *rowptr, int64_t requested)
+{
+    int64_t W = oracle_max_len(n, rowptr);
+    if (requested >= 0)
+        return requested < W ? requested : W;
+    int64_t need = (n + 2) / 3;
+    int64_t K = 0;
+    for (int64_t k = 1; k <= W; ++k) {
+        int64_t cnt = 0;
+        for (int64_t i = 0; i < n; ++i)
+            if (rowptr[i + 1] - rowptr[i] >= k)
+                ++cnt;
+        if (cnt >= need)
+            K = k;
+        else
+            break;
+    }
+    return K;
+}
+
+/* number of tail entries for width K */
+int64_t oracle_tail_nnz(int64_t n, const int64_t *rowptr, int64_t K)
+{
+    int64_t t = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t len = rowptr[i + 1] - rowptr[i];
+        if (len > K)
+            t += len - K;
+    }
+    return t;
+}
+
+/*
+ * Tail of the HYB/HEC split: entries j >= K of every row, in row order and
+ * in-row order.  Writes COO row ids (out_row, may be NULL), the CSR row
+ * pointer of the tail (out_ptr, n + 1 entries, may be NULL), columns and
+ * value bytes.
+ */
+void oracle_tail(int64_t n, const int64_t *rowptr, const int32_t *col,
+                 const void *val, int vsize, int64_t K, int32_t *out_row,
+                 int32_t *out_ptr, int32_t *out_col, void *out_val)
+{
+    char *ov = (char *)out_val;
+    const char *iv = (const char *)val;
+    int64_t t = 0;
+    if (out_ptr)
+        out_ptr[0] = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        for (int64_t k = rowptr[i] + K; k < rowptr[i + 1]; ++k) {
+            if (out_row)
+                out_row[t] = (int32_t)i;
+            out_col[t] = col[k];
+            memcpy(ov + t * vsize, iv + k * vsize, (size_t)vsize);
+            ++t;
+        }
+        if (out_ptr)
+            out_ptr[i + 1] = (int32_t)t;
+    }
+}

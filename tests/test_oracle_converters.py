@@ -1,0 +1,191 @@
+"""Pins of the oracle's reference converters (ELLPACK-R, SELL-64, HYB/HEC).
+
+Slot counts are checked against the closed forms of "Sparse matrix-vector
+multiplication on GPGPU clusters" (Sect. 2.1-2.2: N x Nmax for ELLPACK with N
+padded to the SIMD width; (b_r + 1) N - b_r for pJDS in the one-full-row
+case; no overhead at constant row length), every layout is decoded back to
+the input CSR bit for bit by code written here, and the HYB/HEC width rule is
+checked on hand-counted examples.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gen import CSR, c1_laplace2d, random_csr, stencil
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_kv(name):
+    out = {}
+    for line in open(os.path.join(GOLD, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split()
+            out[k] = int(v)
+    return out
+
+
+def one_full_row(N, full=0):
+    lens = np.ones(N, dtype=np.int64)
+    lens[full] = N
+    rowptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    col = np.concatenate([np.arange(N) if i == full else [i] for i in range(N)]).astype(np.int32)
+    return CSR(N, rowptr, col, np.arange(1, rowptr[-1] + 1, dtype=np.float64))
+
+
+def ell_to_csr(n, oc, ov, ol):
+    S = oracle.pad64(n)
+    rows_c, rows_v = [], []
+    for i in range(n):
+        idx = np.arange(ol[i]) * S + i
+        rows_c.append(oc[idx])
+        rows_v.append(ov[idx])
+    return rows_c, rows_v
+
+
+def sell_to_csr(n, perm, sp, ls, oc, ov):
+    rows_c = [None] * n
+    rows_v = [None] * n
+    for r in range(n):
+        idx = sp[r // 64] + 64 * np.arange(ls[r]) + r % 64
+        rows_c[perm[r]] = oc[idx]
+        rows_v[perm[r]] = ov[idx]
+    return rows_c, rows_v
+
+
+def same_rows(a, rows_c, rows_v):
+    for i in range(a.n):
+        s, e = a.rowptr[i], a.rowptr[i + 1]
+        assert np.array_equal(rows_c[i], a.col[s:e])
+        assert rows_v[i].tobytes() == a.val[s:e].tobytes()
+
+
+MATS = [
+    ("c1", lambda: c1_laplace2d()),
+    ("rand_ragged", lambda: random_csr(1000, seed=31, density=0.01, empty_frac=0.2,
+                                       long_rows=3, long_len=700)),
+    ("rand_dups_unsorted", lambda: random_csr(129, seed=32, density=0.05, dup_frac=0.3,
+                                              zero_frac=0.1, unsorted=True)),
+    ("fp32", lambda: random_csr(300, seed=33, density=0.03, dtype=np.float32)),
+    ("n1", lambda: CSR(1, np.array([0, 3], np.int64), np.array([0, 0, 0], np.int32),
+                       np.array([1.0, -0.0, 2.0]))),
+    ("nnz0", lambda: CSR(65, np.zeros(66, np.int64), np.zeros(0, np.int32), np.zeros(0))),
+]
+
+
+def test_ell_slot_counts_closed_form():
+    a = c1_laplace2d()
+    oc, ov, ol = oracle.ell(a)
+    assert oc.size == 20480 == 64 * 64 * 5
+    # 27-point stencil on 128^3 (sizes only, from the closed form)
+    assert oracle.pad64(128 ** 3) * 27 == 56_623_104
+
+
+def test_pjds_worst_case_fixture():
+    g = read_kv("p1_pjds_worst_case.txt")
+    N, br = g["N"], g["b_r"]
+    a = one_full_row(N)
+    oc, _, _ = oracle.ell(a)
+    assert oc.size == g["ell_slots"] == N * N
+    perm, sp, ls, sc, _ = oracle.sell(a)
+    assert sc.size == g["sell_slots"] == (br + 1) * N - br
+    # the full row sorts first
+    assert perm[0] == 0
+
+
+def test_constant_length_has_no_padding():
+    n, L = 256, 7
+    lens = np.full(n, L)
+    a = random_csr(n, seed=34, lens=lens)
+    assert oracle.ell(a)[0].size == a.nnz
+    assert oracle.sell(a)[3].size == a.nnz
+
+
+def test_sell_slot_counts_stencils():
+    a = c1_laplace2d()
+    assert oracle.sell(a)[3].size == 20288
+    # 27-point stencil: the sorted layout pads only inside mixed slices
+    b = stencil((16, 16, 16), "box", 26.0, -1.0)
+    perm, sp, ls, sc, _ = oracle.sell(b)
+    L = np.sort(b.row_lengths())[::-1]
+    Lp = np.concatenate([L, np.zeros(oracle.pad64(b.n) - b.n, L.dtype)])
+    assert sc.size == int(sum(64 * Lp[s * 64] for s in range(Lp.size // 64)))
+
+
+@pytest.mark.parametrize("name,mk", MATS)
+def test_ell_round_trip(name, mk):
+    a = mk()
+    oc, ov, ol = oracle.ell(a)
+    W = oracle.max_len(a)
+    S = oracle.pad64(a.n)
+    assert oc.size == W * S and ol.size == S
+    assert np.all(ol[a.n:] == 0)
+    same_rows(a, *ell_to_csr(a.n, oc, ov, ol))
+    # pads are column 0 / +0.0
+    used = np.zeros(W * S, bool)
+    for i in range(a.n):
+        used[np.arange(ol[i]) * S + i] = True
+    assert np.all(oc[~used] == 0)
+    assert ov[~used].tobytes() == np.zeros((~used).sum(), ov.dtype).tobytes()
+
+
+@pytest.mark.parametrize("name,mk", MATS)
+def test_sell_round_trip(name, mk):
+    a = mk()
+    perm, sp, ls, oc, ov = oracle.sell(a)
+    L = a.row_lengths()
+    # perm is a bijection sorted by (length desc, row asc)
+    assert np.array_equal(np.sort(perm), np.arange(a.n))
+    key = list(zip(-L[perm], perm))
+    assert key == sorted(key)
+    assert np.array_equal(ls[:a.n], L[perm]) and np.all(ls[a.n:] == 0)
+    widths = np.diff(sp) // 64
+    assert np.all(np.diff(sp) % 64 == 0)
+    assert np.array_equal(widths, ls[::64])
+    same_rows(a, *sell_to_csr(a.n, perm, sp, ls, oc, ov))
+
+
+def test_hyb_width_fixture():
+    for line in open(os.path.join(GOLD, "hyb_width_examples.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, lens = line.split("|")
+        lens = np.array([int(v) for v in lens.split()], dtype=np.int64)
+        a = random_csr(lens.size, seed=1, lens=lens)
+        assert oracle.hyb_width(a) == int(k), (k, lens)
+
+
+def test_hyb_width_stencils_and_override():
+    a = c1_laplace2d()
+    assert oracle.hyb_width(a) == 5
+    b = stencil((12, 12, 12), "box", 26.0, -1.0)
+    assert oracle.hyb_width(b) == 27
+    assert oracle.hyb_width(a, 20) == 5      # clamped to the longest row
+    assert oracle.hyb_width(a, 3) == 3
+    assert oracle.hyb_width(a, 0) == 0
+
+
+@pytest.mark.parametrize("name,mk", MATS)
+@pytest.mark.parametrize("K", [0, 1, 3, None, 10 ** 6])
+def test_split_round_trip(name, mk, K):
+    """ELL part (width K) + tail (COO and CSR) rebuild the input exactly."""
+    a = mk()
+    K = oracle.hyb_width(a) if K is None else oracle.hyb_width(a, K)
+    oc, ov, ol = oracle.ell(a, K)
+    L = a.row_lengths()
+    assert np.array_equal(ol[:a.n], np.minimum(L, K))
+    trow, tptr, tcol, tval = oracle.tail(a, K)
+    assert trow.size == int(np.maximum(L - K, 0).sum())
+    assert np.array_equal(np.diff(tptr), np.maximum(L - K, 0))
+    assert np.all(np.diff(trow) >= 0)
+    ec, ev = ell_to_csr(a.n, oc, ov, ol)
+    rows_c, rows_v = [], []
+    for i in range(a.n):
+        sel = slice(tptr[i], tptr[i + 1])
+        assert np.all(trow[sel] == i)
+        rows_c.append(np.concatenate([ec[i], tcol[sel]]))
+        rows_v.append(np.concatenate([ev[i], tval[sel]]))
+    same_rows(a, rows_c, rows_v)
