@@ -1,0 +1,282 @@
+"""SpMV throughput per storage format on one MI355X.
+
+A step is one pass of the hot path over the resident matrix: y = A x in every
+storage format the workload admits (CSR, ELLPACK-R, SELL-64, HYB, HEC; ELL-R is
+refused where its padding exceeds the memory budget).  Conversions happen once
+before timing (they are paid once per solve).  Inputs are already in HBM when
+the timed region starts.
+
+Reported per format: median apply time, GFLOP/s = 2 nnz / t, effective GB/s =
+B_model / t with
+
+    B_model = nnz (s_v + 4) + R_fmt + n s_v (y written) [+ n s_v if beta != 0]
+              + n s_v (x read once)
+
+(R_fmt = the format's row information), and that rate as a fraction of the
+measured streaming copy (the library's copy kernel over 2 x 2 GiB) and of the
+nominal 8 TB/s.  The CPU oracle (Dot2 CSR, OpenMP over the host cores) is
+timed on the same matrix as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--dtype f64|f32] [--formats csr,hyb] [--no-cpu]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ALL_FORMATS = ["csr", "ellr", "sell64", "hyb", "hec"]
+KERNELS = {
+    "csr": "k_csr_vector",
+    "ellr": "k_ell",
+    "sell64": "k_sell (+ k_sell_chunks)",
+    "hyb": "k_ell + k_tail<COO>",
+    "hec": "k_ell + k_tail<CSR>",
+}
+
+
+def row_info_bytes(fmt: str, n: int, tail_nnz: int = 0) -> int:
+    """Bytes of row information an apply must read in each format."""
+    if fmt == "csr":
+        return 4 * (n + 1)
+    if fmt == "ellr":
+        return 4 * n
+    if fmt == "sell64":
+        ns = (n + 63) // 64
+        return 4 * n + 4 * n + 8 * (ns + 1)       # lengths, permutation, slice starts
+    if fmt == "hyb":
+        return 4 * n + 4 * tail_nnz               # ELL lengths, COO row ids
+    if fmt == "hec":
+        return 4 * n + 4 * (n + 1)                # ELL lengths, tail row pointer
+    raise ValueError(fmt)
+
+
+def bytes_model(fmt: str, n: int, nnz: int, s_v: int, tail_nnz: int = 0,
+                beta_nonzero: bool = False, x_alpha: float | None = None) -> float:
+    """Algorithmic bytes of one apply.
+
+    ``x_alpha`` is the fraction of x loads that reach memory per stored entry
+    (alpha in the code balance of "Sparse matrix-vector multiplication on
+    GPGPU clusters", Sect. 2.3); the default n / nnz is one pass over x.
+    """
+    xa = (n / nnz if nnz else 0.0) if x_alpha is None else x_alpha
+    b = nnz * (s_v + 4) + row_info_bytes(fmt, n, tail_nnz) + n * s_v
+    if beta_nonzero:
+        b += n * s_v
+    return b + xa * nnz * s_v
+
+
+def _stream_handle(torch):
+    return torch.cuda.current_stream()
+
+
+def measure_stream_copy(torch, sf, gib: float = 2.0, reps: int = 20) -> float:
+    """Median GB/s of the library's copy kernel over two 2 GiB buffers."""
+    nbytes = int(gib * (1 << 30))
+    src = torch.empty(nbytes // 8, dtype=torch.float64, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        sf.stream_copy(dst, src)
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sf.stream_copy(dst, src)
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(a, x, target_s: float = 10.0):
+    """Time the CPU oracle (Dot2 CSR) on the full matrix over all host cores."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    oracle.spmv(a, x, nthreads=cores)              # warm caches / threads
+    reps, t = 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        oracle.spmv(a, x, nthreads=cores)
+        reps += 1
+        t = time.perf_counter() - t0
+        if t >= target_s or reps >= 200:
+            break
+    gflops = 2.0 * a.nnz * reps / t / 1e9
+    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%d full applies of the same %d-row matrix (Dot2 fp64, OpenMP static "
+                      "rows) in %.1f s" % (reps, a.n, t)}
+
+
+def traffic_for(kernel_key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the
+    kernel sources have not changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_key)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in sorted(rec.get("sources", [])):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec.get("sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2_hmep_6.2m")
+    ap.add_argument("--dtype", default="f64", choices=["f64", "f32"])
+    ap.add_argument("--formats", default=",".join(ALL_FORMATS))
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-stream", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this SpMV path runs on a single MI355X and has no "
+              "multi-GPU mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import gen
+    import sparse_formats_amd as sf
+
+    def log(m):
+        print("[bench] " + m, file=sys.stderr, flush=True)
+
+    npdt = np.float64 if args.dtype == "f64" else np.float32
+    tdt = torch.float64 if args.dtype == "f64" else torch.float32
+    s_v = 8 if args.dtype == "f64" else 4
+    t0 = time.time()
+    a, x_np, _, _ = gen.by_name(args.workload, npdt)
+    log("workload %s: n=%d nnz=%d (generated in %.1fs)" % (args.workload, a.n, a.nnz,
+                                                           time.time() - t0))
+    rp = torch.from_numpy(a.rowptr).cuda()
+    col = torch.from_numpy(a.col).cuda()
+    val = torch.from_numpy(np.ascontiguousarray(a.val, npdt)).cuda()
+    x = torch.from_numpy(x_np).cuda()
+    y = torch.zeros(a.n, dtype=tdt, device="cuda")
+
+    mats = {}
+    setup_ms = {}
+    refused = {}
+    for fmt in args.formats.split(","):
+        t1 = time.perf_counter()
+        M = sf.Matrix.from_csr(rp, col, val, n=a.n)
+        try:
+            M.convert(fmt)
+        except sf.SpmvError as e:
+            refused[fmt] = str(e)
+            M.close()
+            log("%s refused: %s" % (fmt, e))
+            continue
+        torch.cuda.synchronize()
+        setup_ms[fmt] = (time.perf_counter() - t1) * 1e3
+        mats[fmt] = M
+        log("%s built in %.0f ms: %s" % (fmt, setup_ms[fmt], M.info()))
+    del rp, col, val
+    torch.cuda.empty_cache()
+
+    stream_gbs = None if args.no_stream else measure_stream_copy(torch, sf)
+    if stream_gbs:
+        log("stream copy %.1f GB/s" % stream_gbs)
+
+    fmts = list(mats)
+    for _ in range(args.warmup):
+        for f in fmts:
+            mats[f].apply(y, x)
+    torch.cuda.synchronize()
+    ev = {f: [] for f in fmts}
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        for f in fmts:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            mats[f].apply(y, x)
+            e1.record()
+            ev[f].append((e0, e1))
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+
+    per = {}
+    for f in fmts:
+        ts = np.array([e0.elapsed_time(e1) for e0, e1 in ev[f]])
+        med = float(np.median(ts))
+        info = mats[f].info()
+        bm = bytes_model(f, a.n, a.nnz, s_v, info["tail_nnz"])
+        gbs = bm / (med * 1e-3) / 1e9
+        per[f] = {
+            "ms_median": round(med, 5), "ms_min": round(float(ts.min()), 5),
+            "ms_p90": round(float(np.percentile(ts, 90)), 5),
+            "gflops": round(2 * a.nnz / (med * 1e-3) / 1e9, 2),
+            "eff_gbs": round(gbs, 1), "bytes_model": int(bm),
+            "frac_stream": round(gbs / stream_gbs, 4) if stream_gbs else None,
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "slots": info["slots"], "ell_width": info["ell_width"],
+            "tail_nnz": info["tail_nnz"], "setup_ms": round(setup_ms[f], 1),
+            "kernels": KERNELS[f],
+        }
+    best = max(per, key=lambda f: per[f]["gflops"])
+    dom = max(per, key=lambda f: per[f]["ms_median"])
+    d = per[dom]
+    achieved = d["bytes_model"] / (d["ms_median"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_for("%s:%s:%s" % (args.workload, args.dtype, dom)),
+                "kernel": "%s apply (%s)" % (dom, KERNELS[dom]),
+                "frac_of_stream": d["frac_stream"]}
+    flops_step = 2.0 * a.nnz * len(fmts)
+    out = {
+        "metric": "SpMV GFLOP/s and effective HBM GB/s (% of roofline) per format, " + args.dtype,
+        "value": round(flops_step * args.steps / (total_ms * 1e-3) / 1e9, 2),
+        "unit": "GFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "n": a.n, "nnz": a.nnz,
+                   "formats": fmts, "refused": refused,
+                   "step": "one apply y = A x in each listed format",
+                   "value": "2 nnz x formats per step / step time"},
+        "best_format": {"format": best, "gflops": per[best]["gflops"],
+                        "eff_gbs": per[best]["eff_gbs"],
+                        "frac_stream": per[best]["frac_stream"]},
+        "stream_copy_gbs": round(stream_gbs, 1) if stream_gbs else None,
+        "formats": per,
+        "roofline": roofline,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(a, x_np)
+    for M in mats.values():
+        M.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,228 @@
+/*
+ * spmv_amd.h -- C ABI of the MI355X sparse matrix-vector library.
+ *
+ * The library computes y = alpha * A * x + beta * y for a large, very sparse
+ * general square matrix A held on one GPU in one of five storage formats:
+ *
+ *   CSR       compressed sparse rows (row pointer, column, value), the input
+ *             form and the canonical copy ("Development of Krylov and AMG
+ *             linear solvers for large-scale sparse matrices on GPUs",
+ *             Sect. 2.1, Fig. 3: Ap holds the start of each row, Aj and Ax
+ *             the columns and values).
+ *   ELLPACK-R rows shifted left into an n x Nmax rectangle stored column by
+ *             column, the row count padded to a multiple of the SIMD width
+ *             (64 on gfx950), plus the length of every row so that work
+ *             stops at the row's end ("Sparse matrix-vector multiplication
+ *             on GPGPU clusters", Sect. 2.1, Fig. 1, footnote 2, Fig. 2b).
+ *   SELL-64   the pJDS idea of the same page (Sect. 2.2): rows sorted by
+ *             length, longest first, cut into blocks of 64 rows each padded
+ *             to its longest row, stored block by block, with the row
+ *             permutation.  apply() works in the caller's row order.
+ *   HYB       an ELL part of width K plus the remaining entries of every row
+ *             in coordinate (row, col, val) form ("Development of Krylov...",
+ *             Sect. 2.1, Fig. 2; "Load-balancing Sparse Matrix Vector
+ *             Product Kernels on GPUs", abstract).
+ *   HEC       an ELL part of width K plus the remaining entries in CSR form
+ *             ("Development of Krylov...", Sect. 2.1, Fig. 3); the ELL part
+ *             is applied first, then the irregular part.
+ *
+ * Conventions shared by all entry points
+ *   - Every array argument is a DEVICE pointer (e.g. a torch tensor's
+ *     data_ptr()), never a host pointer.  Host pointers appear only in
+ *     spmv_export (destination buffer) and in the out-parameters.
+ *   - Indices are 0-based.  Rows and columns lie in [0, n).  n < 2^31 and
+ *     nnz < 2^31.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Functions return 0 (SPMV_OK) or a negative spmv_status; nothing is
+ *     thrown across the ABI.  After a non-zero return spmv_last_error()
+ *     holds a message for the calling thread.  Kernel faults inside
+ *     spmv_apply surface at the caller's next synchronisation, since apply
+ *     is asynchronous.
+ *   - A handle may be used by several threads for spmv_apply at once (on
+ *     different streams); spmv_convert / spmv_destroy must not overlap any
+ *     other call on the same handle.
+ */
+#ifndef SPMV_AMD_H
+#define SPMV_AMD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spmv_handle *spmv_t;
+
+/* value type */
+typedef enum { SPMV_F32 = 1, SPMV_F64 = 2 } spmv_dtype;
+
+/* storage formats */
+typedef enum {
+    SPMV_CSR = 0,
+    SPMV_ELLR = 1,
+    SPMV_SELL64 = 2,
+    SPMV_HYB = 3,
+    SPMV_HEC = 4
+} spmv_format;
+
+/* input layout of spmv_create */
+typedef enum { SPMV_IN_CSR = 0, SPMV_IN_COO = 1 } spmv_input;
+
+/* return codes */
+typedef enum {
+    SPMV_OK = 0,
+    SPMV_ERR_INVALID_ARG = -1,    /* null pointer, bad size or enum, x/y overlap */
+    SPMV_ERR_INVALID_MATRIX = -2, /* rowptr not monotone / rowptr[0] != 0 /
+                                     rowptr[n] != nnz / index outside [0, n) */
+    SPMV_ERR_NO_MEMORY = -3,      /* a device allocation failed */
+    SPMV_ERR_FOOTPRINT = -4,      /* padded format larger than the budget */
+    SPMV_ERR_HIP = -5,            /* HIP runtime error (message has details) */
+    SPMV_ERR_STATE = -6           /* null handle, or array not present */
+} spmv_status;
+
+/* options of spmv_convert (pass NULL for all defaults) */
+typedef struct {
+    /* HYB/HEC: width K of the ELL part.  -1 picks
+     * K = max{k >= 0 : #{rows with length >= k} >= ceil(n/3)};
+     * a value >= 0 is used as given, clamped to the longest row. */
+    int32_t ell_width;
+    /* CSR: lanes cooperating on one row, a power of two in 1..64; 0 picks
+     * the smallest power of two >= the longest row, at most 64 (the
+     * subwarp rule of "Sparse Linear Algebra on AMD and NVIDIA GPUs -- The
+     * Race Is On": threads per row follow the maximum row length). */
+    int32_t subwave;
+    /* Largest device footprint a padded format (ELL-R) may take, in bytes;
+     * 0 means 75% of the device's memory. */
+    uint64_t footprint_budget_bytes;
+} spmv_convert_opts;
+
+/* description of a handle (spmv_info) */
+typedef struct {
+    int64_t n;             /* rows = columns */
+    int64_t nnz;           /* stored entries (duplicates and zeros kept) */
+    int32_t dtype;         /* spmv_dtype */
+    int32_t format;        /* active spmv_format */
+    int32_t max_len;       /* longest row */
+    int32_t ell_width;     /* ELL-R: max_len; HYB/HEC: K; otherwise 0 */
+    int64_t tail_nnz;      /* HYB/HEC: entries outside the ELL part */
+    int64_t ell_stride;    /* ELL-R / HYB / HEC: 64 * ceil(n / 64) */
+    int64_t slots;         /* stored slots of the active format incl. padding */
+    int32_t subwave;       /* CSR: lanes per row */
+    int32_t nslices;       /* SELL-64: slices */
+    uint64_t footprint_bytes; /* device bytes held by the handle */
+} spmv_info_t;
+
+/* arrays readable with spmv_export */
+typedef enum {
+    SPMV_A_ROWPTR = 0,     /* CSR row pointer, int32[n+1] */
+    SPMV_A_COL = 1,        /* CSR columns, int32[nnz] */
+    SPMV_A_VAL = 2,        /* CSR values, dtype[nnz] */
+    SPMV_A_ELL_COL = 3,    /* ELL-R / ELL part: int32[width * stride], column-major */
+    SPMV_A_ELL_VAL = 4,    /* dtype[width * stride]; pad slots col 0, value +0 */
+    SPMV_A_ELL_LEN = 5,    /* int32[stride]: entries of each row held in ELL */
+    SPMV_A_SELL_PERM = 6,  /* int32[n]: original row at sorted position r */
+    SPMV_A_SELL_SLICE_PTR = 7, /* int64[nslices+1]: first slot of each slice */
+    SPMV_A_SELL_LEN = 8,   /* int32[64 * nslices]: length of sorted row r */
+    SPMV_A_SELL_COL = 9,   /* int32[slots]: entry j of sorted row r at
+                              slice_ptr[r/64] + 64*j + r%64 */
+    SPMV_A_SELL_VAL = 10,  /* dtype[slots] */
+    SPMV_A_TAIL_ROW = 11,  /* HYB: int32[tail_nnz] row of each tail entry */
+    SPMV_A_TAIL_PTR = 12,  /* HEC: int32[n+1] start of each row's tail */
+    SPMV_A_TAIL_COL = 13,  /* HYB/HEC: int32[tail_nnz] */
+    SPMV_A_TAIL_VAL = 14   /* HYB/HEC: dtype[tail_nnz] */
+} spmv_array;
+
+/*
+ * spmv_create -- copy a matrix onto the device and validate it.
+ *
+ *   out        host out-parameter: the new handle (set only on success)
+ *   kind       SPMV_IN_CSR: `rowidx` is the CSR row pointer, int64[n+1];
+ *              SPMV_IN_COO: `rowidx` is the row of every entry, int64[nnz]
+ *              (any order; entries are ordered by (row, input position),
+ *              which keeps the input order inside a row)
+ *   n, nnz     matrix size and stored entries (0 <= n, nnz < 2^31)
+ *   rowidx     device pointer as above (may be NULL only if COO and nnz == 0)
+ *   col        device int32[nnz], may be NULL when nnz == 0
+ *   val        device dtype[nnz], may be NULL when nnz == 0
+ *   dtype      SPMV_F32 or SPMV_F64
+ *   stream     the work is ordered on this stream; the call synchronises it
+ *              before returning, after which the caller may free its arrays
+ *
+ * Duplicated (row, col) pairs and explicit zeros are kept and summed by
+ * apply; columns need not be sorted.  The handle owns device copies (CSR with
+ * int32 row pointer).  The active format is SPMV_CSR.
+ * Errors: INVALID_ARG, INVALID_MATRIX (nothing allocated is kept), NO_MEMORY,
+ * HIP.
+ */
+int spmv_create(spmv_t *out, int kind, int64_t n, int64_t nnz,
+                const int64_t *rowidx, const int32_t *col, const void *val,
+                int dtype, void *stream);
+
+/*
+ * spmv_convert -- build `format` on the device from the CSR copy and make it
+ * the active format.  Synchronous (small size read-backs are needed).
+ * The previous non-CSR format is released once the new one is built; on any
+ * error the handle is left exactly as it was.  Converting to SPMV_CSR only
+ * switches the active format (and applies opts->subwave).
+ *   opts  may be NULL (defaults, see spmv_convert_opts)
+ * Errors: STATE, INVALID_ARG (unknown format, bad subwave), FOOTPRINT (the
+ * padded layout exceeds the budget; e.g. ELL-R of a matrix with a few very
+ * long rows), NO_MEMORY, HIP.
+ */
+int spmv_convert(spmv_t h, int format, const spmv_convert_opts *opts);
+
+/*
+ * spmv_apply -- y = alpha * A * x + beta * y with the active format.
+ *   y      device dtype[n], read only when beta != 0, always written
+ *   x      device dtype[n]; must not overlap y
+ *   alpha, beta  scalars (rounded to float for SPMV_F32 handles)
+ *   stream the kernels are enqueued on this stream; no host synchronisation
+ * Accumulation is in the handle's dtype with fused multiply-adds; HYB/HEC
+ * and split SELL slices add partial sums with atomics, so their last bits
+ * may vary between runs.  Errors: STATE, INVALID_ARG (null or overlapping
+ * vectors), HIP (launch failure).
+ */
+int spmv_apply(spmv_t h, void *y, const void *x, double alpha, double beta,
+               void *stream);
+
+/* spmv_destroy -- free every device buffer of the handle (synchronises the
+ * device first).  A NULL handle is accepted.  Errors: HIP. */
+int spmv_destroy(spmv_t h);
+
+/*
+ * spmv_info -- fill *out (host) with the handle's description.
+ * Errors: STATE, INVALID_ARG.
+ */
+int spmv_info(spmv_t h, spmv_info_t *out);
+
+/*
+ * spmv_export -- copy one of the handle's device arrays to host memory
+ * (synchronous).  With host_dst == NULL only *bytes is set.  The array must
+ * belong to the active format (or to CSR).  capacity_bytes below the
+ * array's size gives INVALID_ARG.  Errors: STATE (array not present),
+ * INVALID_ARG, HIP.
+ */
+int spmv_export(spmv_t h, int array, void *host_dst, int64_t capacity_bytes,
+                int64_t *bytes);
+
+/*
+ * spmv_stream_copy -- dst[0..bytes) = src[0..bytes) with the same load/store
+ * style as the SpMV kernels (16-byte nontemporal loads, grid-stride); the
+ * reference bandwidth that the SpMV kernels are compared with.  Both device
+ * pointers must be 16-byte aligned and not overlap.  Asynchronous on stream.
+ * Errors: INVALID_ARG, HIP.
+ */
+int spmv_stream_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
+/* spmv_last_error -- message of the calling thread's last failed call
+ * ("" if none).  The pointer stays valid until that thread's next call. */
+const char *spmv_last_error(void);
+
+/* spmv_version -- library version string */
+const char *spmv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPMV_AMD_H */

@@ -1,0 +1,891 @@
+// Handle management, validation, COO/CSR ingest and the device-side format
+// converters behind the C ABI declared in include/spmv_amd.h.
+//
+// Conversions run on the device from the handle's CSR copy.  Only a few
+// scalars (and, for HYB/HEC, the row-length histogram; for SELL-64, the slice
+// widths) come back to the host to size allocations and pick the split.
+#include <cstring>
+#include <hip/hip_runtime.h>
+#include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/device/device_scan.hpp>
+#include <rocprim/iterator/counting_iterator.hpp>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <functional>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/spmv_amd.h"
+#include "internal.h"
+
+using namespace spmv;
+
+namespace {
+
+thread_local std::string g_err;
+
+struct Error {
+    int code;
+    std::string msg;
+};
+
+[[noreturn]] void fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    throw Error{code, buf};
+}
+
+void hip_check(hipError_t e, const char* what) {
+    if (e == hipSuccess) return;
+    (void)hipGetLastError();
+    fail(e == hipErrorOutOfMemory ? SPMV_ERR_NO_MEMORY : SPMV_ERR_HIP, "%s: %s", what,
+         hipGetErrorString(e));
+}
+
+// owning device buffer
+struct DevBuf {
+    void* p = nullptr;
+    size_t bytes = 0;
+    DevBuf() = default;
+    explicit DevBuf(size_t n) { alloc(n); }
+    DevBuf(const DevBuf&) = delete;
+    DevBuf& operator=(const DevBuf&) = delete;
+    DevBuf(DevBuf&& o) noexcept : p(o.p), bytes(o.bytes) { o.p = nullptr, o.bytes = 0; }
+    DevBuf& operator=(DevBuf&& o) noexcept {
+        if (this != &o) {
+            release();
+            p = o.p, bytes = o.bytes;
+            o.p = nullptr, o.bytes = 0;
+        }
+        return *this;
+    }
+    ~DevBuf() { release(); }
+    void alloc(size_t n) {
+        release();
+        void* q = nullptr;
+        hipError_t e = hipMalloc(&q, std::max<size_t>(n, 256));
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            fail(SPMV_ERR_NO_MEMORY, "device allocation of %zu bytes failed: %s", n,
+                 hipGetErrorString(e));
+        }
+        p = q;
+        bytes = n;
+    }
+    void release() {
+        if (p) (void)hipFree(p);
+        p = nullptr;
+        bytes = 0;
+    }
+    template <typename T>
+    T* as() const {
+        return static_cast<T*>(p);
+    }
+};
+
+int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
+// the arrays of one converted (non-CSR) format
+struct Built {
+    int format = SPMV_CSR;
+    // ELL-R, or the ELL part of HYB / HEC
+    int64_t ell_width = 0, ell_stride = 0;
+    DevBuf ell_col, ell_val, ell_len;
+    // SELL-64
+    int64_t nslices = 0, sell_slots = 0;
+    DevBuf slice_ptr, sell_len, perm, sell_col, sell_val;
+    int64_t nchunks = 0;
+    DevBuf chunks;
+    // tail of HYB / HEC
+    int64_t tail_nnz = 0, tail_chunks = 0;
+    DevBuf tail_row, tail_ptr, tail_col, tail_val, chunk_row;
+
+    size_t bytes() const {
+        return ell_col.bytes + ell_val.bytes + ell_len.bytes + slice_ptr.bytes + sell_len.bytes +
+               perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + tail_row.bytes +
+               tail_ptr.bytes + tail_col.bytes + tail_val.bytes + chunk_row.bytes;
+    }
+};
+
+}  // namespace
+
+struct spmv_handle {
+    int64_t n = 0, nnz = 0;
+    int dtype = SPMV_F64;
+    size_t vsize = 8;
+    int max_len = 0;
+    int subwave = 1;
+    DevBuf rowptr, col, val;  // canonical CSR (int32 row pointer)
+    Built fmt;                // active non-CSR format (format == CSR: none)
+    int format = SPMV_CSR;
+};
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// setup kernels
+// ---------------------------------------------------------------------------
+enum : int { F_FIRST = 1, F_LAST = 2, F_MONO = 4, F_COL = 8, F_ROW = 16 };
+
+__global__ void k_validate_csr(int64_t n, int64_t nnz, const int64_t* __restrict__ rp,
+                               const int32_t* __restrict__ col, int* flags,
+                               int* __restrict__ rp32) {
+    const int64_t m = std::max(n + 1, nnz);
+    int f = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < m;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i <= n) {
+            const int64_t v = rp[i];
+            rp32[i] = (int)v;
+            if (i == 0 && v != 0) f |= F_FIRST;
+            if (i == n && v != nnz) f |= F_LAST;
+            if (i < n && rp[i + 1] < v) f |= F_MONO;
+        }
+        if (i < nnz) {
+            const int c = col[i];
+            if (c < 0 || c >= n) f |= F_COL;
+        }
+    }
+    if (f) atomicOr(flags, f);
+}
+
+__global__ void k_validate_coo(int64_t n, int64_t nnz, const int64_t* __restrict__ row,
+                               const int32_t* __restrict__ col, int* flags,
+                               unsigned* __restrict__ row32) {
+    int f = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nnz;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = row[i];
+        const int c = col[i];
+        if (r < 0 || r >= n) f |= F_ROW;
+        if (c < 0 || c >= n) f |= F_COL;
+        row32[i] = (unsigned)r;
+    }
+    if (f) atomicOr(flags, f);
+}
+
+// gather the CSR entries of COO input in sorted order
+__global__ void k_gather(int64_t nnz, const int* __restrict__ order,
+                         const int32_t* __restrict__ col_in, const char* __restrict__ val_in,
+                         int vsize, int* __restrict__ col, char* __restrict__ val) {
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t s = order[k];
+        col[k] = col_in[s];
+        if (vsize == 8)
+            reinterpret_cast<double*>(val)[k] = reinterpret_cast<const double*>(val_in)[s];
+        else
+            reinterpret_cast<float*>(val)[k] = reinterpret_cast<const float*>(val_in)[s];
+    }
+}
+
+// rowptr[r] = first sorted entry with row >= r
+__global__ void k_rowptr_from_sorted(int64_t n, int64_t nnz, const unsigned* __restrict__ rows,
+                                     int* __restrict__ rowptr) {
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r <= n;
+         r += (int64_t)gridDim.x * blockDim.x) {
+        int64_t lo = 0, hi = nnz;
+        while (lo < hi) {
+            const int64_t m = (lo + hi) >> 1;
+            if ((int64_t)rows[m] < r)
+                lo = m + 1;
+            else
+                hi = m;
+        }
+        rowptr[r] = (int)lo;
+    }
+}
+
+__global__ void k_max_len(int64_t n, const int* __restrict__ rowptr, int* out) {
+    int m = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        m = max(m, rowptr[i + 1] - rowptr[i]);
+    if (m) atomicMax(out, m);
+}
+
+__global__ void k_len_hist(int64_t n, const int* __restrict__ rowptr, int* __restrict__ hist) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        atomicAdd(hist + (rowptr[i + 1] - rowptr[i]), 1);
+}
+
+// ELL slots: slot t = j * S + i holds entry j of row i (j < min(len_i, W)),
+// otherwise column 0 / value +0.  len[i] = min(len_i, W), 0 for padded rows.
+template <typename V>
+__global__ void k_ell_fill(int64_t n, int64_t S, int64_t W, const int* __restrict__ rowptr,
+                           const int* __restrict__ col, const V* __restrict__ val,
+                           int* __restrict__ ecol, V* __restrict__ eval, int* __restrict__ elen) {
+    const int64_t total = S * W;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = t / S, i = t - j * S;
+        int c = 0;
+        V v = V(0);
+        if (i < n) {
+            const int k0 = rowptr[i];
+            const int64_t L = std::min<int64_t>(rowptr[i + 1] - k0, W);
+            if (j < L) {
+                c = col[k0 + j];
+                v = val[k0 + j];
+            }
+        }
+        ecol[t] = c;
+        eval[t] = v;
+    }
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S;
+         i += (int64_t)gridDim.x * blockDim.x)
+        elen[i] = i < n ? (int)std::min<int64_t>(rowptr[i + 1] - rowptr[i], W) : 0;
+}
+
+// sort key for SELL: rows by length descending; the radix sort is stable,
+// so equal lengths keep ascending row order
+__global__ void k_sell_keys(int64_t n, int W, const int* __restrict__ rowptr,
+                            unsigned* __restrict__ key) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        key[i] = (unsigned)(W - (rowptr[i + 1] - rowptr[i]));
+}
+
+// sorted lengths and per-slice slot counts 64 * width (width = first row)
+__global__ void k_sell_len(int64_t n, int64_t S, const int* __restrict__ rowptr,
+                           const int* __restrict__ perm, int* __restrict__ slen,
+                           int64_t* __restrict__ slots) {
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < S;
+         r += (int64_t)gridDim.x * blockDim.x) {
+        const int L = r < n ? rowptr[perm[r] + 1] - rowptr[perm[r]] : 0;
+        slen[r] = L;
+        if ((r & 63) == 0) slots[r >> 6] = 64 * (int64_t)L;
+    }
+}
+
+// one wave per slice
+template <typename V>
+__global__ void k_sell_fill(int64_t n, int64_t nslices, const int* __restrict__ rowptr,
+                            const int* __restrict__ col, const V* __restrict__ val,
+                            const int* __restrict__ perm, const int64_t* __restrict__ sp,
+                            const int* __restrict__ slen, int* __restrict__ scol,
+                            V* __restrict__ sval) {
+    const int64_t s = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (s >= nslices) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t r = s * 64 + lane;
+    const int64_t base = sp[s];
+    const int64_t w = (sp[s + 1] - base) >> 6;
+    const int L = slen[r];
+    const int k0 = r < n ? rowptr[perm[r]] : 0;
+    for (int64_t j = 0; j < w; ++j) {
+        const int64_t slot = base + 64 * j + lane;
+        if (j < L) {
+            scol[slot] = col[k0 + j];
+            sval[slot] = val[k0 + j];
+        } else {
+            scol[slot] = 0;
+            sval[slot] = V(0);
+        }
+    }
+}
+
+// tail lengths max(len - K, 0)
+__global__ void k_tail_len(int64_t n, int K, const int* __restrict__ rowptr,
+                           int* __restrict__ tlen) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        tlen[i] = max(rowptr[i + 1] - rowptr[i] - K, 0);
+}
+
+// one wave per row: entries K.. of row i go to tail slots tptr[i]..
+template <typename V>
+__global__ void k_tail_fill(int64_t n, int K, const int* __restrict__ rowptr,
+                            const int* __restrict__ col, const V* __restrict__ val,
+                            const int* __restrict__ tptr, int* __restrict__ trow,
+                            int* __restrict__ tcol, V* __restrict__ tval) {
+    const int64_t i = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (i >= n) return;
+    const int lane = threadIdx.x & 63;
+    const int t0 = tptr[i], t1 = tptr[i + 1];
+    const int k0 = rowptr[i] + K;
+    for (int t = t0 + lane; t < t1; t += 64) {
+        tcol[t] = col[k0 + (t - t0)];
+        tval[t] = val[k0 + (t - t0)];
+        if (trow) trow[t] = (int)i;
+    }
+}
+
+// chunk_row[k] = row holding tail entry k * chunk (k < nchunks); last = n - 1
+__global__ void k_chunk_rows(int64_t n, int64_t nchunks, int64_t chunk,
+                             const int* __restrict__ tptr, int* __restrict__ out) {
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k <= nchunks;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        if (k == nchunks) {
+            out[k] = (int)(n - 1);
+            continue;
+        }
+        const int64_t e = k * chunk;
+        int64_t lo = 0, hi = n - 1;  // largest r with tptr[r] <= e
+        while (lo < hi) {
+            const int64_t m = (lo + hi + 1) >> 1;
+            if (tptr[m] <= e)
+                lo = m;
+            else
+                hi = m - 1;
+        }
+        out[k] = (int)lo;
+    }
+}
+
+unsigned grid_for(int64_t work, int64_t per_block = 256) {
+    int64_t b = (work + per_block - 1) / per_block;
+    return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 65536));
+}
+
+unsigned bits_for(uint64_t v) {
+    unsigned b = 1;
+    while (b < 32 && (v >> b)) ++b;
+    return b;
+}
+
+void sync(hipStream_t s) { hip_check(hipStreamSynchronize(s), "hipStreamSynchronize"); }
+
+template <typename T>
+T read_scalar(const void* dev, hipStream_t s) {
+    T v{};
+    hip_check(hipMemcpyAsync(&v, dev, sizeof(T), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+    sync(s);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// converters
+// ---------------------------------------------------------------------------
+uint64_t budget_bytes(const spmv_convert_opts& o) {
+    if (o.footprint_budget_bytes) return o.footprint_budget_bytes;
+    size_t fr = 0, tot = 0;
+    hip_check(hipMemGetInfo(&fr, &tot), "hipMemGetInfo");
+    return (uint64_t)(0.75 * (double)tot);
+}
+
+template <typename V>
+void build_ell_part(const spmv_handle* h, int64_t W, Built& b, hipStream_t s) {
+    const int64_t S = pad64(h->n);
+    b.ell_width = W;
+    b.ell_stride = S;
+    b.ell_col.alloc((size_t)(W * S) * 4);
+    b.ell_val.alloc((size_t)(W * S) * sizeof(V));
+    b.ell_len.alloc((size_t)S * 4);
+    hipLaunchKernelGGL(k_ell_fill<V>, dim3(grid_for(std::max<int64_t>(W * S, S))), dim3(256), 0,
+                       s, h->n, S, W, h->rowptr.as<int>(), h->col.as<int>(), h->val.as<V>(),
+                       b.ell_col.as<int>(), b.ell_val.as<V>(), b.ell_len.as<int>());
+    hip_check(hipGetLastError(), "ell fill");
+}
+
+template <typename V>
+void build_sell(const spmv_handle* h, Built& b, hipStream_t s) {
+    const int64_t n = h->n, S = pad64(n), ns = S / 64;
+    b.nslices = ns;
+    b.perm.alloc((size_t)std::max<int64_t>(n, 1) * 4);
+    b.sell_len.alloc((size_t)S * 4);
+    b.slice_ptr.alloc((size_t)(ns + 1) * 8);
+    if (n > 0) {
+        DevBuf keys((size_t)n * 4), keys_out((size_t)n * 4);
+        hipLaunchKernelGGL(k_sell_keys, dim3(grid_for(n)), dim3(256), 0, s, n, h->max_len,
+                           h->rowptr.as<int>(), keys.as<unsigned>());
+        hip_check(hipGetLastError(), "sell keys");
+        size_t tmp = 0;
+        rocprim::counting_iterator<int> iota(0);
+        const unsigned nb = bits_for((uint64_t)h->max_len);
+        hip_check(rocprim::radix_sort_pairs(nullptr, tmp, keys.as<unsigned>(),
+                                            keys_out.as<unsigned>(), iota, b.perm.as<int>(),
+                                            (size_t)n, 0, nb, s),
+                  "radix_sort_pairs");
+        DevBuf work(tmp);
+        hip_check(rocprim::radix_sort_pairs(work.p, tmp, keys.as<unsigned>(),
+                                            keys_out.as<unsigned>(), iota, b.perm.as<int>(),
+                                            (size_t)n, 0, nb, s),
+                  "radix_sort_pairs");
+        sync(s);  // before the temporaries are freed
+    }
+    DevBuf slots((size_t)std::max<int64_t>(ns, 1) * 8);
+    if (ns > 0) {
+        hipLaunchKernelGGL(k_sell_len, dim3(grid_for(S)), dim3(256), 0, s, n, S,
+                           h->rowptr.as<int>(), b.perm.as<int>(), b.sell_len.as<int>(),
+                           slots.as<int64_t>());
+        hip_check(hipGetLastError(), "sell lengths");
+        hip_check(hipMemsetAsync(b.slice_ptr.p, 0, 8, s), "hipMemsetAsync");
+        size_t tmp = 0;
+        hip_check(rocprim::inclusive_scan(nullptr, tmp, slots.as<int64_t>(),
+                                          b.slice_ptr.as<int64_t>() + 1, (size_t)ns,
+                                          rocprim::plus<int64_t>(), s),
+                  "inclusive_scan");
+        DevBuf work(tmp);
+        hip_check(rocprim::inclusive_scan(work.p, tmp, slots.as<int64_t>(),
+                                          b.slice_ptr.as<int64_t>() + 1, (size_t)ns,
+                                          rocprim::plus<int64_t>(), s),
+                  "inclusive_scan");
+        sync(s);
+    } else {
+        hip_check(hipMemsetAsync(b.slice_ptr.p, 0, 8, s), "hipMemsetAsync");
+    }
+    // slice widths decide the split of long slices into column chunks
+    std::vector<int64_t> sp((size_t)ns + 1);
+    hip_check(hipMemcpyAsync(sp.data(), b.slice_ptr.p, sp.size() * 8, hipMemcpyDeviceToHost, s),
+              "hipMemcpyAsync");
+    sync(s);
+    b.sell_slots = sp[(size_t)ns];
+    std::vector<int4> ch;
+    for (int64_t q = 0; q < ns; ++q) {
+        const int64_t w = (sp[(size_t)q + 1] - sp[(size_t)q]) / 64;
+        if (w > kSellSplitWidth)
+            for (int64_t j = 0; j < w; j += kSellChunk)
+                ch.push_back(make_int4((int)q, (int)j, (int)std::min<int64_t>(w, j + kSellChunk), 0));
+    }
+    b.nchunks = (int64_t)ch.size();
+    b.chunks.alloc(std::max<size_t>(ch.size(), 1) * sizeof(int4));
+    if (!ch.empty())
+        hip_check(hipMemcpyAsync(b.chunks.p, ch.data(), ch.size() * sizeof(int4),
+                                 hipMemcpyHostToDevice, s),
+                  "hipMemcpyAsync");
+    b.sell_col.alloc((size_t)b.sell_slots * 4);
+    b.sell_val.alloc((size_t)b.sell_slots * sizeof(V));
+    if (ns > 0) {
+        hipLaunchKernelGGL(k_sell_fill<V>, dim3((unsigned)((ns + 3) / 4)), dim3(256), 0, s, n,
+                           ns, h->rowptr.as<int>(), h->col.as<int>(), h->val.as<V>(),
+                           b.perm.as<int>(), b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
+                           b.sell_col.as<int>(), b.sell_val.as<V>());
+        hip_check(hipGetLastError(), "sell fill");
+    }
+    sync(s);
+}
+
+// row-length histogram -> HYB/HEC width K (ceil(n/3) rule unless requested)
+int64_t choose_width(const spmv_handle* h, int requested, std::vector<int>& hist, hipStream_t s) {
+    const int W = h->max_len;
+    hist.assign((size_t)W + 1, 0);
+    DevBuf dh((size_t)(W + 1) * 4);
+    hip_check(hipMemsetAsync(dh.p, 0, (size_t)(W + 1) * 4, s), "hipMemsetAsync");
+    if (h->n > 0) {
+        hipLaunchKernelGGL(k_len_hist, dim3(grid_for(h->n)), dim3(256), 0, s, h->n,
+                           h->rowptr.as<int>(), dh.as<int>());
+        hip_check(hipGetLastError(), "histogram");
+    }
+    hip_check(hipMemcpyAsync(hist.data(), dh.p, (size_t)(W + 1) * 4, hipMemcpyDeviceToHost, s),
+              "hipMemcpyAsync");
+    sync(s);
+    if (requested >= 0) return std::min<int64_t>(requested, W);
+    const int64_t need = (h->n + 2) / 3;
+    int64_t at_least = h->n;  // rows with length >= k, starting at k = 0
+    int64_t K = 0;
+    for (int64_t k = 1; k <= W; ++k) {
+        at_least -= hist[(size_t)k - 1];
+        if (at_least >= need)
+            K = k;
+        else
+            break;
+    }
+    return K;
+}
+
+template <typename V>
+void build_split(const spmv_handle* h, int format, int requested, Built& b, hipStream_t s) {
+    std::vector<int> hist;
+    const int64_t K = choose_width(h, requested, hist, s);
+    int64_t tail = 0;
+    for (size_t l = (size_t)K + 1; l < hist.size(); ++l) tail += (int64_t)hist[l] * ((int64_t)l - K);
+    build_ell_part<V>(h, K, b, s);
+    b.tail_nnz = tail;
+    const int64_t n = h->n;
+    b.tail_ptr.alloc((size_t)(n + 1) * 4);
+    {
+        DevBuf tlen((size_t)std::max<int64_t>(n, 1) * 4);
+        hip_check(hipMemsetAsync(b.tail_ptr.p, 0, 4, s), "hipMemsetAsync");
+        if (n > 0) {
+            hipLaunchKernelGGL(k_tail_len, dim3(grid_for(n)), dim3(256), 0, s, n, (int)K,
+                               h->rowptr.as<int>(), tlen.as<int>());
+            hip_check(hipGetLastError(), "tail lengths");
+            size_t tmp = 0;
+            hip_check(rocprim::inclusive_scan(nullptr, tmp, tlen.as<int>(), b.tail_ptr.as<int>() + 1,
+                                              (size_t)n, rocprim::plus<int>(), s),
+                      "inclusive_scan");
+            DevBuf work(tmp);
+            hip_check(rocprim::inclusive_scan(work.p, tmp, tlen.as<int>(), b.tail_ptr.as<int>() + 1,
+                                              (size_t)n, rocprim::plus<int>(), s),
+                      "inclusive_scan");
+            sync(s);
+        }
+        sync(s);
+    }
+    if (format == SPMV_HYB) b.tail_row.alloc((size_t)std::max<int64_t>(tail, 1) * 4);
+    b.tail_col.alloc((size_t)std::max<int64_t>(tail, 1) * 4);
+    b.tail_val.alloc((size_t)std::max<int64_t>(tail, 1) * sizeof(V));
+    if (tail > 0) {
+        hipLaunchKernelGGL(k_tail_fill<V>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, n,
+                           (int)K, h->rowptr.as<int>(), h->col.as<int>(), h->val.as<V>(),
+                           b.tail_ptr.as<int>(), format == SPMV_HYB ? b.tail_row.as<int>() : nullptr,
+                           b.tail_col.as<int>(), b.tail_val.as<V>());
+        hip_check(hipGetLastError(), "tail fill");
+    }
+    b.tail_chunks = (tail + kTailChunk - 1) / kTailChunk;
+    if (format == SPMV_HEC) {
+        b.chunk_row.alloc((size_t)(b.tail_chunks + 1) * 4);
+        if (n > 0) {
+            hipLaunchKernelGGL(k_chunk_rows, dim3(grid_for(b.tail_chunks + 1)), dim3(256), 0, s, n,
+                               b.tail_chunks, (int64_t)kTailChunk, b.tail_ptr.as<int>(),
+                               b.chunk_row.as<int>());
+            hip_check(hipGetLastError(), "chunk rows");
+        }
+    } else {
+        b.tail_ptr.release();  // HYB keeps the COO rows only
+    }
+    sync(s);
+}
+
+int run_guarded(const std::function<void()>& body) {
+    try {
+        body();
+        return SPMV_OK;
+    } catch (const Error& e) {
+        g_err = e.msg;
+        return e.code;
+    } catch (const std::bad_alloc&) {
+        g_err = "host allocation failed";
+        return SPMV_ERR_NO_MEMORY;
+    } catch (...) {
+        g_err = "unexpected internal error";
+        return SPMV_ERR_HIP;
+    }
+}
+
+bool valid_format(int f) { return f >= SPMV_CSR && f <= SPMV_HEC; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char* spmv_last_error(void) { return g_err.c_str(); }
+
+const char* spmv_version(void) { return "sparse_formats_amd 0.1 (gfx950)"; }
+
+int spmv_create(spmv_t* out, int kind, int64_t n, int64_t nnz, const int64_t* rowidx,
+                const int32_t* col, const void* val, int dtype, void* stream) {
+    g_err.clear();
+    return run_guarded([&] {
+        if (!out) fail(SPMV_ERR_INVALID_ARG, "out is NULL");
+        if (kind != SPMV_IN_CSR && kind != SPMV_IN_COO)
+            fail(SPMV_ERR_INVALID_ARG, "unknown input kind %d", kind);
+        if (dtype != SPMV_F32 && dtype != SPMV_F64)
+            fail(SPMV_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+        if (n < 0 || nnz < 0) fail(SPMV_ERR_INVALID_ARG, "negative size (n=%lld nnz=%lld)",
+                                   (long long)n, (long long)nnz);
+        if (n >= INT32_MAX || nnz >= INT32_MAX)
+            fail(SPMV_ERR_INVALID_ARG, "n and nnz must be below 2^31-1");
+        if (kind == SPMV_IN_CSR && !rowidx) fail(SPMV_ERR_INVALID_ARG, "rowptr is NULL");
+        if (nnz > 0 && (!rowidx || !col || !val))
+            fail(SPMV_ERR_INVALID_ARG, "row/col/val pointer is NULL");
+        hipStream_t s = (hipStream_t)stream;
+        auto* h = new spmv_handle;
+        try {
+            h->n = n;
+            h->nnz = nnz;
+            h->dtype = dtype;
+            h->vsize = dtype == SPMV_F64 ? 8 : 4;
+            h->rowptr.alloc((size_t)(n + 1) * 4);
+            h->col.alloc((size_t)nnz * 4);
+            h->val.alloc((size_t)nnz * h->vsize);
+            DevBuf flags(8);
+            hip_check(hipMemsetAsync(flags.p, 0, 8, s), "hipMemsetAsync");
+            if (kind == SPMV_IN_CSR) {
+                hipLaunchKernelGGL(k_validate_csr, dim3(grid_for(std::max(n + 1, nnz))), dim3(256),
+                                   0, s, n, nnz, rowidx, col, flags.as<int>(), h->rowptr.as<int>());
+                hip_check(hipGetLastError(), "validate");
+                const int f = read_scalar<int>(flags.p, s);
+                if (f)
+                    fail(SPMV_ERR_INVALID_MATRIX, "invalid CSR:%s%s%s%s",
+                         f & F_FIRST ? " rowptr[0] != 0;" : "",
+                         f & F_LAST ? " rowptr[n] != nnz;" : "",
+                         f & F_MONO ? " rowptr decreases;" : "",
+                         f & F_COL ? " column outside [0, n);" : "");
+                if (nnz > 0) {
+                    hip_check(hipMemcpyAsync(h->col.p, col, (size_t)nnz * 4,
+                                             hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
+                    hip_check(hipMemcpyAsync(h->val.p, val, (size_t)nnz * h->vsize,
+                                             hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
+                }
+            } else {
+                DevBuf rows32((size_t)nnz * 4), rows_sorted((size_t)nnz * 4), order((size_t)nnz * 4);
+                if (nnz > 0) {
+                    hipLaunchKernelGGL(k_validate_coo, dim3(grid_for(nnz)), dim3(256), 0, s, n, nnz,
+                                       rowidx, col, flags.as<int>(), rows32.as<unsigned>());
+                    hip_check(hipGetLastError(), "validate");
+                }
+                const int f = read_scalar<int>(flags.p, s);
+                if (f)
+                    fail(SPMV_ERR_INVALID_MATRIX, "invalid COO:%s%s",
+                         f & F_ROW ? " row outside [0, n);" : "",
+                         f & F_COL ? " column outside [0, n);" : "");
+                if (nnz > 0) {
+                    size_t tmp = 0;
+                    rocprim::counting_iterator<int> iota(0);
+                    const unsigned nb = bits_for((uint64_t)n);
+                    hip_check(rocprim::radix_sort_pairs(nullptr, tmp, rows32.as<unsigned>(),
+                                                        rows_sorted.as<unsigned>(), iota,
+                                                        order.as<int>(), (size_t)nnz, 0, nb, s),
+                              "radix_sort_pairs");
+                    DevBuf work(tmp);
+                    hip_check(rocprim::radix_sort_pairs(work.p, tmp, rows32.as<unsigned>(),
+                                                        rows_sorted.as<unsigned>(), iota,
+                                                        order.as<int>(), (size_t)nnz, 0, nb, s),
+                              "radix_sort_pairs");
+                    hipLaunchKernelGGL(k_gather, dim3(grid_for(nnz)), dim3(256), 0, s, nnz,
+                                       order.as<int>(), col, (const char*)val, (int)h->vsize,
+                                       h->col.as<int>(), h->val.as<char>());
+                    hip_check(hipGetLastError(), "gather");
+                    sync(s);
+                }
+                hipLaunchKernelGGL(k_rowptr_from_sorted, dim3(grid_for(n + 1)), dim3(256), 0, s, n,
+                                   nnz, rows_sorted.as<unsigned>(), h->rowptr.as<int>());
+                hip_check(hipGetLastError(), "rowptr");
+                sync(s);
+            }
+            hip_check(hipMemsetAsync(flags.p, 0, 4, s), "hipMemsetAsync");
+            if (n > 0) {
+                hipLaunchKernelGGL(k_max_len, dim3(grid_for(n)), dim3(256), 0, s, n,
+                                   h->rowptr.as<int>(), flags.as<int>());
+                hip_check(hipGetLastError(), "max length");
+            }
+            h->max_len = read_scalar<int>(flags.p, s);
+            int sw = 1;
+            while (sw < 64 && sw < h->max_len) sw <<= 1;
+            h->subwave = sw;
+        } catch (...) {
+            delete h;
+            throw;
+        }
+        *out = h;
+    });
+}
+
+int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
+    g_err.clear();
+    return run_guarded([&] {
+        if (!h) fail(SPMV_ERR_STATE, "null handle");
+        if (!valid_format(format)) fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
+        spmv_convert_opts o{-1, 0, 0};
+        if (opts) o = *opts;
+        if (format == SPMV_CSR) {
+            int sw = o.subwave;
+            if (sw == 0) {
+                sw = 1;
+                while (sw < 64 && sw < h->max_len) sw <<= 1;
+            }
+            if (sw < 1 || sw > 64 || (sw & (sw - 1)))
+                fail(SPMV_ERR_INVALID_ARG, "subwave must be a power of two in 1..64 (got %d)", sw);
+            h->subwave = sw;
+            h->fmt = Built{};
+            h->format = SPMV_CSR;
+            return;
+        }
+        hipStream_t s = nullptr;
+        const bool f64 = h->dtype == SPMV_F64;
+        Built b;
+        b.format = format;
+        if (format == SPMV_ELLR) {
+            const int64_t S = pad64(h->n), W = h->max_len;
+            const double need = (double)W * (double)S * (4.0 + (double)h->vsize) + 4.0 * (double)S;
+            const uint64_t budget = budget_bytes(o);
+            if (need > (double)budget)
+                fail(SPMV_ERR_FOOTPRINT,
+                     "ELL-R needs %.3g bytes (%lld rows padded to %lld x width %lld) over the "
+                     "budget of %.3g bytes",
+                     need, (long long)h->n, (long long)S, (long long)W, (double)budget);
+            if (f64)
+                build_ell_part<double>(h, W, b, s);
+            else
+                build_ell_part<float>(h, W, b, s);
+            sync(s);
+        } else if (format == SPMV_SELL64) {
+            if (f64)
+                build_sell<double>(h, b, s);
+            else
+                build_sell<float>(h, b, s);
+        } else {
+            if (f64)
+                build_split<double>(h, format, o.ell_width, b, s);
+            else
+                build_split<float>(h, format, o.ell_width, b, s);
+        }
+        h->fmt = std::move(b);
+        h->format = format;
+    });
+}
+
+int spmv_apply(spmv_t h, void* y, const void* x, double alpha, double beta, void* stream) {
+    if (!h) {
+        g_err = "null handle";
+        return SPMV_ERR_STATE;
+    }
+    if (h->n > 0 && (!y || !x)) {
+        g_err = "x or y is NULL";
+        return SPMV_ERR_INVALID_ARG;
+    }
+    const uintptr_t yb = (uintptr_t)y, xb = (uintptr_t)x, len = (uintptr_t)(h->n * h->vsize);
+    if (h->n > 0 && yb < xb + len && xb < yb + len) {
+        g_err = "x and y overlap";
+        return SPMV_ERR_INVALID_ARG;
+    }
+    if (h->n == 0) return SPMV_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const bool f64 = h->dtype == SPMV_F64;
+    const Built& b = h->fmt;
+    hipError_t e = hipSuccess;
+    switch (h->format) {
+        case SPMV_CSR: {
+            CsrView a{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
+            e = launch_csr(a, h->subwave, f64, y, x, alpha, beta, s);
+            break;
+        }
+        case SPMV_ELLR:
+        case SPMV_HYB:
+        case SPMV_HEC: {
+            EllView a{(int)h->n, b.ell_stride, b.ell_len.as<int>(), b.ell_col.as<int>(), b.ell_val.p};
+            e = launch_ell(a, f64, y, x, alpha, beta, s);
+            if (e == hipSuccess && h->format != SPMV_ELLR && b.tail_nnz > 0) {
+                TailView t{(int)h->n, b.tail_nnz, b.tail_row.as<int>(), b.tail_ptr.as<int>(),
+                           b.chunk_row.as<int>(), b.tail_col.as<int>(), b.tail_val.p};
+                e = launch_tail(t, f64, y, x, alpha, s);
+            }
+            break;
+        }
+        case SPMV_SELL64: {
+            SellView a{(int)h->n, (int)b.nslices, b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
+                       b.perm.as<int>(), b.sell_col.as<int>(), b.sell_val.p, (int)b.nchunks,
+                       b.chunks.as<int4>()};
+            e = launch_sell(a, f64, y, x, alpha, beta, s);
+            break;
+        }
+    }
+    if (e != hipSuccess) {
+        g_err = std::string("kernel launch failed: ") + hipGetErrorString(e);
+        return SPMV_ERR_HIP;
+    }
+    return SPMV_OK;
+}
+
+int spmv_destroy(spmv_t h) {
+    g_err.clear();
+    if (!h) return SPMV_OK;
+    return run_guarded([&] {
+        hipError_t e = hipDeviceSynchronize();
+        delete h;
+        hip_check(e, "hipDeviceSynchronize");
+    });
+}
+
+int spmv_info(spmv_t h, spmv_info_t* out) {
+    g_err.clear();
+    if (!h) {
+        g_err = "null handle";
+        return SPMV_ERR_STATE;
+    }
+    if (!out) {
+        g_err = "out is NULL";
+        return SPMV_ERR_INVALID_ARG;
+    }
+    spmv_info_t i{};
+    i.n = h->n;
+    i.nnz = h->nnz;
+    i.dtype = h->dtype;
+    i.format = h->format;
+    i.max_len = h->max_len;
+    i.subwave = h->subwave;
+    const Built& b = h->fmt;
+    switch (h->format) {
+        case SPMV_CSR: i.slots = h->nnz; break;
+        case SPMV_ELLR:
+            i.ell_width = (int32_t)b.ell_width;
+            i.ell_stride = b.ell_stride;
+            i.slots = b.ell_width * b.ell_stride;
+            break;
+        case SPMV_SELL64:
+            i.nslices = (int32_t)b.nslices;
+            i.slots = b.sell_slots;
+            break;
+        default:
+            i.ell_width = (int32_t)b.ell_width;
+            i.ell_stride = b.ell_stride;
+            i.tail_nnz = b.tail_nnz;
+            i.slots = b.ell_width * b.ell_stride + b.tail_nnz;
+    }
+    i.footprint_bytes = h->rowptr.bytes + h->col.bytes + h->val.bytes + b.bytes();
+    *out = i;
+    return SPMV_OK;
+}
+
+int spmv_export(spmv_t h, int array, void* host_dst, int64_t capacity_bytes, int64_t* bytes) {
+    g_err.clear();
+    return run_guarded([&] {
+        if (!h) fail(SPMV_ERR_STATE, "null handle");
+        const Built& b = h->fmt;
+        const int f = h->format;
+        const bool ell = f == SPMV_ELLR || f == SPMV_HYB || f == SPMV_HEC;
+        const void* src = nullptr;
+        int64_t sz = -1;
+        const int64_t vs = (int64_t)h->vsize;
+        switch (array) {
+            case SPMV_A_ROWPTR: src = h->rowptr.p, sz = (h->n + 1) * 4; break;
+            case SPMV_A_COL: src = h->col.p, sz = h->nnz * 4; break;
+            case SPMV_A_VAL: src = h->val.p, sz = h->nnz * vs; break;
+            case SPMV_A_ELL_COL: if (ell) src = b.ell_col.p, sz = b.ell_width * b.ell_stride * 4; break;
+            case SPMV_A_ELL_VAL: if (ell) src = b.ell_val.p, sz = b.ell_width * b.ell_stride * vs; break;
+            case SPMV_A_ELL_LEN: if (ell) src = b.ell_len.p, sz = b.ell_stride * 4; break;
+            case SPMV_A_SELL_PERM: if (f == SPMV_SELL64) src = b.perm.p, sz = h->n * 4; break;
+            case SPMV_A_SELL_SLICE_PTR: if (f == SPMV_SELL64) src = b.slice_ptr.p, sz = (b.nslices + 1) * 8; break;
+            case SPMV_A_SELL_LEN: if (f == SPMV_SELL64) src = b.sell_len.p, sz = b.nslices * 64 * 4; break;
+            case SPMV_A_SELL_COL: if (f == SPMV_SELL64) src = b.sell_col.p, sz = b.sell_slots * 4; break;
+            case SPMV_A_SELL_VAL: if (f == SPMV_SELL64) src = b.sell_val.p, sz = b.sell_slots * vs; break;
+            case SPMV_A_TAIL_ROW: if (f == SPMV_HYB) src = b.tail_row.p, sz = b.tail_nnz * 4; break;
+            case SPMV_A_TAIL_PTR: if (f == SPMV_HEC) src = b.tail_ptr.p, sz = (h->n + 1) * 4; break;
+            case SPMV_A_TAIL_COL: if (f == SPMV_HYB || f == SPMV_HEC) src = b.tail_col.p, sz = b.tail_nnz * 4; break;
+            case SPMV_A_TAIL_VAL: if (f == SPMV_HYB || f == SPMV_HEC) src = b.tail_val.p, sz = b.tail_nnz * vs; break;
+            default: fail(SPMV_ERR_INVALID_ARG, "unknown array id %d", array);
+        }
+        if (sz < 0) fail(SPMV_ERR_STATE, "array %d does not belong to the active format", array);
+        if (bytes) *bytes = sz;
+        if (!host_dst) return;
+        if (capacity_bytes < sz)
+            fail(SPMV_ERR_INVALID_ARG, "destination holds %lld bytes, array needs %lld",
+                 (long long)capacity_bytes, (long long)sz);
+        if (sz > 0) {
+            hip_check(hipMemcpy(host_dst, src, (size_t)sz, hipMemcpyDeviceToHost), "hipMemcpy");
+        }
+    });
+}
+
+int spmv_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+    g_err.clear();
+    if (bytes < 0 || (bytes > 0 && (!dst || !src)) || ((uintptr_t)dst | (uintptr_t)src) % 16) {
+        g_err = "bad copy arguments (null, negative or not 16-byte aligned)";
+        return SPMV_ERR_INVALID_ARG;
+    }
+    const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
+    if (bytes > 0 && d < s + (uintptr_t)bytes && s < d + (uintptr_t)bytes) {
+        g_err = "copy buffers overlap";
+        return SPMV_ERR_INVALID_ARG;
+    }
+    hipError_t e = launch_stream_copy(dst, src, bytes, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        g_err = std::string("kernel launch failed: ") + hipGetErrorString(e);
+        return SPMV_ERR_HIP;
+    }
+    return SPMV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device helpers shared by the gfx950 SpMV kernels: XCD-aware block order,
+// streaming loads, cross-lane sums on wave64 and fp atomics.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spmv {
+
+constexpr int kWave = 64;
+
+// MI355X dispatches workgroup b of a grid to XCD (b mod 8).  Each XCD has its
+// own L2, so neighbouring tiles (which share x entries of a banded matrix)
+// should run on the same XCD.  This maps dispatch order to a logical tile
+// index such that XCD k works on the k-th contiguous eighth of the tiles.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t grid) {
+    const int64_t xcd = b & 7, idx = b >> 3;
+    const int64_t per = grid >> 3, rem = grid & 7;
+    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// Streaming (non-temporal) loads for matrix data that is read exactly once
+// per apply, so it does not evict x from the caches.
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane moves.  DPP controls (gfx9 encoding):
+//   quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2)
+//   row_half_mirror = 0x141 (lane i <-> 7-i inside 8), row_mirror = 0x140
+//   (lane i <-> 15-i inside 16).  After the sums of the smaller groups are
+//   in every lane, a mirror pairs each lane with one of the other half, so
+//   the butterfly stays a full reduction.
+// ds_swizzle bit mode 0x401F: and_mask 0x1F, xor_mask 0x10 -> lane ^ 16
+// inside each 32-lane half.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+    const int64_t b = __double_as_longlong(v);
+    const int lo = dpp_i32<CTRL>((int)(b & 0xffffffff));
+    const int hi = dpp_i32<CTRL>((int)(b >> 32));
+    return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ float swz16_move(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+
+__device__ __forceinline__ double swz16_move(double v) {
+    const int64_t b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_ds_swizzle((int)(b & 0xffffffff), 0x401F);
+    const int hi = __builtin_amdgcn_ds_swizzle((int)(b >> 32), 0x401F);
+    return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ float lane_read(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ double lane_read(double v, int lane) {
+    const int64_t b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffff), lane);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+    return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum over aligned groups of S lanes (S a power of two, 1..64).  For S <= 32
+// every lane of the group ends with the group sum; for S == 64 lane 0 holds
+// the wave's sum.  All lanes of a group must be active.
+template <int S, typename T>
+__device__ __forceinline__ T group_sum(T v) {
+    if constexpr (S >= 2) v += dpp_move<0xB1>(v);
+    if constexpr (S >= 4) v += dpp_move<0x4E>(v);
+    if constexpr (S >= 8) v += dpp_move<0x141>(v);
+    if constexpr (S >= 16) v += dpp_move<0x140>(v);
+    if constexpr (S >= 32) v += swz16_move(v);
+    if constexpr (S >= 64) v += lane_read(v, 32);
+    return v;
+}
+
+// fp atomic add in L2 (device-scope, relaxed); hardware fp32/fp64 atomics
+// on coarse-grained device memory.
+__device__ __forceinline__ void atomic_add(double* p, double v) {
+    unsafeAtomicAdd(p, v);
+}
+__device__ __forceinline__ void atomic_add(float* p, float v) {
+    unsafeAtomicAdd(p, v);
+}
+
+// y = alpha * s + beta * y; beta == 0 never reads y.
+template <typename T>
+__device__ __forceinline__ T axpby(T s, T alpha, T beta, const T* y) {
+    return beta == T(0) ? alpha * s : alpha * s + beta * *y;
+}
+
+}  // namespace spmv

@@ -1,0 +1,204 @@
+// ELLPACK-R and SELL-64 apply: one lane per row.
+//
+// "Sparse matrix-vector multiplication on GPGPU clusters" (Sect. 2.1-2.2)
+// maps consecutive rows to consecutive threads and stores the padded
+// rectangle column by column, so that for a fixed entry index the lanes of a
+// wave read consecutive slots; ELLPACK-R stops each row at its stored length
+// (Fig. 2b).  The sorted variant (pJDS, here SELL-64 with one wave per slice
+// of 64 sorted rows) pads each slice only to its own longest row.
+// "Sparse Linear Algebra on AMD and NVIDIA GPUs -- The Race Is On" notes that
+// on AMD GPUs the column-major layout must be read with one lane per row (a
+// group of lanes on one row reads slots a whole stride apart); that is the
+// mapping kept here.
+#include "common.h"
+#include "internal.h"
+
+namespace spmv {
+
+// ---------------------------------------------------------------------------
+// ELLPACK-R (also the ELL part of HYB / HEC)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_ell(int n, int64_t stride, const int* __restrict__ len,
+                                             const int* __restrict__ col,
+                                             const T* __restrict__ val, const T* __restrict__ x,
+                                             T* __restrict__ y, T alpha, T beta) {
+    const int64_t i = xcd_tile(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int L = len[i];
+    const int* c = col + i;
+    const T* v = val + i;
+    T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    int j = 0;
+    for (; j + 4 <= L; j += 4) {
+        const int64_t o = (int64_t)j * stride;
+        const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + stride);
+        const T v2 = ld_nt(v + o + 2 * stride), v3 = ld_nt(v + o + 3 * stride);
+        const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + stride);
+        const int c2 = ld_nt(c + o + 2 * stride), c3 = ld_nt(c + o + 3 * stride);
+        s0 = fma(v0, x[c0], s0);
+        s1 = fma(v1, x[c1], s1);
+        s2 = fma(v2, x[c2], s2);
+        s3 = fma(v3, x[c3], s3);
+    }
+    for (; j < L; ++j) {
+        const int64_t o = (int64_t)j * stride;
+        s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
+    }
+    y[i] = axpby((s0 + s1) + (s2 + s3), alpha, beta, y + i);
+}
+
+hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double alpha,
+                      double beta, hipStream_t stream) {
+    const int64_t blocks = ((int64_t)a.n + 255) / 256;
+    if (blocks == 0) return hipSuccess;
+    if (f64)
+        hipLaunchKernelGGL(k_ell<double>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
+                           a.stride, a.len, a.col, (const double*)a.val, (const double*)x,
+                           (double*)y, alpha, beta);
+    else
+        hipLaunchKernelGGL(k_ell<float>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
+                           a.stride, a.len, a.col, (const float*)a.val, (const float*)x,
+                           (float*)y, (float)alpha, (float)beta);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SELL-64: wave s runs slice s; lane l runs sorted row 64 s + l and writes
+// y[perm[row]].  Slices wider than kSellSplitWidth only get beta * y here;
+// their columns are added by k_sell_chunks.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_sell(int n, int nslices,
+                                              const int64_t* __restrict__ slice_ptr,
+                                              const int* __restrict__ len,
+                                              const int* __restrict__ perm,
+                                              const int* __restrict__ col,
+                                              const T* __restrict__ val, const T* __restrict__ x,
+                                              T* __restrict__ y, T alpha, T beta) {
+    const int64_t s = xcd_tile(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+    if (s >= nslices) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t r = s * 64 + lane;
+    const int64_t base = slice_ptr[s];
+    const int64_t width = (slice_ptr[s + 1] - base) >> 6;
+    int L = len[r];
+    if (width > kSellSplitWidth) L = 0;
+    const int* c = col + base + lane;
+    const T* v = val + base + lane;
+    T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    int j = 0;
+    for (; j + 4 <= L; j += 4) {
+        const int64_t o = (int64_t)j * 64;
+        const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + 64);
+        const T v2 = ld_nt(v + o + 128), v3 = ld_nt(v + o + 192);
+        const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + 64);
+        const int c2 = ld_nt(c + o + 128), c3 = ld_nt(c + o + 192);
+        s0 = fma(v0, x[c0], s0);
+        s1 = fma(v1, x[c1], s1);
+        s2 = fma(v2, x[c2], s2);
+        s3 = fma(v3, x[c3], s3);
+    }
+    for (; j < L; ++j) {
+        const int64_t o = (int64_t)j * 64;
+        s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
+    }
+    if (r < n) {
+        const int row = perm[r];
+        y[row] = axpby((s0 + s1) + (s2 + s3), alpha, beta, y + row);
+    }
+}
+
+// one wave per column chunk (slice, j0, j1) of a split slice
+template <typename T>
+__global__ __launch_bounds__(256) void k_sell_chunks(int n, int nchunks,
+                                                     const int4* __restrict__ chunks,
+                                                     const int64_t* __restrict__ slice_ptr,
+                                                     const int* __restrict__ len,
+                                                     const int* __restrict__ perm,
+                                                     const int* __restrict__ col,
+                                                     const T* __restrict__ val,
+                                                     const T* __restrict__ x, T* __restrict__ y,
+                                                     T alpha) {
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= nchunks) return;
+    const int4 ch = chunks[w];
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)ch.x * 64 + lane;
+    const int L = min(len[r], ch.z);
+    const int* c = col + slice_ptr[ch.x] + lane;
+    const T* v = val + slice_ptr[ch.x] + lane;
+    T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    int j = ch.y;
+    for (; j + 4 <= L; j += 4) {
+        const int64_t o = (int64_t)j * 64;
+        const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + 64);
+        const T v2 = ld_nt(v + o + 128), v3 = ld_nt(v + o + 192);
+        const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + 64);
+        const int c2 = ld_nt(c + o + 128), c3 = ld_nt(c + o + 192);
+        s0 = fma(v0, x[c0], s0);
+        s1 = fma(v1, x[c1], s1);
+        s2 = fma(v2, x[c2], s2);
+        s3 = fma(v3, x[c3], s3);
+    }
+    for (; j < L; ++j) {
+        const int64_t o = (int64_t)j * 64;
+        s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
+    }
+    if (r < n && ch.y < L) atomic_add(y + perm[r], alpha * ((s0 + s1) + (s2 + s3)));
+}
+
+template <typename T>
+static hipError_t run_sell(const SellView& a, void* y, const void* x, double alpha, double beta,
+                           hipStream_t stream) {
+    const int64_t blocks = ((int64_t)a.nslices + 3) / 4;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_sell<T>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n, a.nslices,
+                       a.slice_ptr, a.len, a.perm, a.col, (const T*)a.val, (const T*)x, (T*)y,
+                       (T)alpha, (T)beta);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nchunks == 0) return e;
+    hipLaunchKernelGGL(k_sell_chunks<T>, dim3((unsigned)((a.nchunks + 3) / 4)), dim3(256), 0,
+                       stream, a.n, a.nchunks, a.chunks, a.slice_ptr, a.len, a.perm, a.col,
+                       (const T*)a.val, (const T*)x, (T*)y, (T)alpha);
+    return hipGetLastError();
+}
+
+hipError_t launch_sell(const SellView& a, bool f64, void* y, const void* x, double alpha,
+                       double beta, hipStream_t stream) {
+    return f64 ? run_sell<double>(a, y, x, alpha, beta, stream)
+               : run_sell<float>(a, y, x, alpha, beta, stream);
+}
+
+// ---------------------------------------------------------------------------
+// reference copy with the kernels' load style (16-byte nontemporal loads)
+// ---------------------------------------------------------------------------
+typedef int copy_vec_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_copy(copy_vec_t* __restrict__ dst,
+                                              const copy_vec_t* __restrict__ src, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+__global__ void k_copy_tail(char* dst, const char* src, int64_t from, int64_t bytes) {
+    const int64_t i = from + threadIdx.x;
+    if (i < bytes) dst[i] = src[i];
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+    const int64_t n16 = bytes / 16;
+    if (n16 > 0) {
+        int64_t blocks = (n16 + 255) / 256;
+        if (blocks > 256 * 64) blocks = 256 * 64;
+        hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (copy_vec_t*)dst, (const copy_vec_t*)src, n16);
+    }
+    if (bytes % 16)
+        hipLaunchKernelGGL(k_copy_tail, dim3(1), dim3(16), 0, stream, (char*)dst,
+                           (const char*)src, n16 * 16, bytes);
+    return hipGetLastError();
+}
+
+}  // namespace spmv

@@ -1,0 +1,296 @@
+"""GPU parity on small and medium matrices: every format, both dtypes, several
+alpha/beta, edge cases (empty rows, duplicates, explicit zeros, unsorted
+columns, very long rows, n % 64 != 0, n = 1, nnz = 0), converter layouts
+bit-exact against the oracle's reference converters, and the error paths."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gen import CSR, c1_laplace2d, random_csr, stencil, vectors
+
+from gpu_util import AB, FORMATS, TOL, apply, check, to_dev
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import sparse_formats_amd as sf
+
+
+def _mats():
+    return {
+        "c1": lambda: c1_laplace2d(),
+        "ragged": lambda: random_csr(3001, seed=41, density=0.003, empty_frac=0.25,
+                                     long_rows=3, long_len=2500),
+        "dups_unsorted": lambda: random_csr(777, seed=42, density=0.01, dup_frac=0.3,
+                                            zero_frac=0.1, unsorted=True),
+        "n1": lambda: CSR(1, np.array([0, 3], np.int64), np.array([0, 0, 0], np.int32),
+                          np.array([1.0, -2.0, 0.5])),
+        "nnz0": lambda: CSR(130, np.zeros(131, np.int64), np.zeros(0, np.int32), np.zeros(0)),
+        "n0": lambda: CSR(0, np.zeros(1, np.int64), np.zeros(0, np.int32), np.zeros(0)),
+        "box27": lambda: stencil((13, 11, 9), "box", 26.0, -1.0, noise=1e-3, seed=3),
+        "every_len": lambda: random_csr(700, seed=43, lens=np.arange(700) % 601),
+        "long_spans": lambda: random_csr(5000, seed=44, lens=np.where(
+            np.arange(5000) % 997 == 0, 4000, np.arange(5000) % 7)),
+    }
+
+
+MATS = _mats()
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("name", list(MATS))
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_format_parity(fmt, name, dtype):
+    a = MATS[name]()
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    x_np, y0_np = vectors(a.n, 7)
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    x_np, y0_np = x_np.astype(npdt), y0_np.astype(npdt)
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n)
+    M.convert(fmt)
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    for alpha, beta in AB:
+        y = apply(M, x, y0, alpha, beta)
+        check(a, x_np, y0_np, alpha, beta, y, dtype, what="%s/%s/%s a=%g b=%g" % (
+            fmt, name, dtype, alpha, beta))
+    M.close()
+
+
+@pytest.mark.parametrize("fmt", ["hyb", "hec"])
+@pytest.mark.parametrize("K", [0, 1, 5, 20, 10 ** 6])
+def test_split_width_any(fmt, K):
+    a = MATS["long_spans"]()
+    x_np, y0_np = vectors(a.n, 8)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt, ell_width=K)
+    info = M.info()
+    assert info["ell_width"] == min(K, oracle.max_len(a))
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    for alpha, beta in AB[:2]:
+        check(a, x_np, y0_np, alpha, beta, apply(M, x, y0, alpha, beta), torch.float64,
+              what="%s K=%d" % (fmt, K))
+
+
+@pytest.mark.parametrize("sw", [1, 2, 4, 8, 16, 32, 64])
+def test_csr_every_subwave(sw):
+    a = MATS["every_len"]()
+    x_np, y0_np = vectors(a.n, 9)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("csr", subwave=sw)
+    assert M.info()["subwave"] == sw
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    check(a, x_np, y0_np, 1.5, -0.5, apply(M, x, y0, 1.5, -0.5), torch.float64)
+
+
+def test_sell_split_slices():
+    """Slices wider than the split width go through column chunks + atomics."""
+    n = 9000
+    L = np.arange(n) % 13
+    L[[5, 700, 701, 4000, 8999]] = [3000, 2900, 257, 8999, 1000]
+    a = random_csr(n, seed=45, lens=L)
+    x_np, y0_np = vectors(n, 10)
+    M = sf.Matrix.from_csr(*to_dev(a), n=n).convert("sell64")
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    for alpha, beta in AB:
+        check(a, x_np, y0_np, alpha, beta, apply(M, x, y0, alpha, beta), torch.float64)
+
+
+@pytest.mark.parametrize("name", ["c1", "ragged", "dups_unsorted", "every_len", "nnz0", "n1"])
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+def test_layouts_bit_exact(name, dtype):
+    a = MATS[name]()
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    a = CSR(a.n, a.rowptr, a.col, a.val.astype(npdt))
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n)
+    assert np.array_equal(M.export("rowptr"), a.rowptr.astype(np.int32))
+    assert np.array_equal(M.export("col"), a.col)
+    assert M.export("val").tobytes() == a.val.tobytes()
+    M.convert("ellr")
+    oc, ov, ol = oracle.ell(a)
+    assert np.array_equal(M.export("ell_col"), oc)
+    assert M.export("ell_val").tobytes() == ov.tobytes()
+    assert np.array_equal(M.export("ell_len"), ol)
+    M.convert("sell64")
+    perm, sp, ls, sc, sv = oracle.sell(a)
+    assert np.array_equal(M.export("sell_perm"), perm.astype(np.int32))
+    assert np.array_equal(M.export("sell_slice_ptr"), sp)
+    assert np.array_equal(M.export("sell_len"), ls)
+    assert np.array_equal(M.export("sell_col"), sc)
+    assert M.export("sell_val").tobytes() == sv.tobytes()
+    for fmt in ("hyb", "hec"):
+        for req in (-1, 0, 3):
+            M.convert(fmt, ell_width=req)
+            K = oracle.hyb_width(a, req)
+            assert M.info()["ell_width"] == K
+            oc, ov, ol = oracle.ell(a, K)
+            assert np.array_equal(M.export("ell_col"), oc)
+            assert M.export("ell_val").tobytes() == ov.tobytes()
+            assert np.array_equal(M.export("ell_len"), ol)
+            trow, tptr, tcol, tval = oracle.tail(a, K)
+            assert M.info()["tail_nnz"] == tcol.size
+            if fmt == "hyb":
+                assert np.array_equal(M.export("tail_row"), trow)
+            else:
+                assert np.array_equal(M.export("tail_ptr"), tptr)
+            assert np.array_equal(M.export("tail_col"), tcol)
+            assert M.export("tail_val").tobytes() == tval.tobytes()
+
+
+def test_coo_ingest_orders_by_row_then_position():
+    a = MATS["dups_unsorted"]()
+    rows = np.repeat(np.arange(a.n), a.row_lengths())
+    rng = np.random.default_rng(5)
+    p = rng.permutation(a.nnz)
+    r_t = torch.from_numpy(rows[p].astype(np.int64)).cuda()
+    c_t = torch.from_numpy(a.col[p]).cuda()
+    v_t = torch.from_numpy(a.val[p]).cuda()
+    M = sf.Matrix.from_coo(r_t, c_t, v_t, a.n)
+    # expected: stable order by row of the shuffled input
+    order = np.argsort(rows[p], kind="stable")
+    assert np.array_equal(M.export("rowptr"), a.rowptr.astype(np.int32))
+    assert np.array_equal(M.export("col"), a.col[p][order])
+    assert M.export("val").tobytes() == a.val[p][order].tobytes()
+    x_np, y0_np = vectors(a.n, 11)
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    check(a, x_np, y0_np, 1.0, 0.0, apply(M, x, y0, 1.0, 0.0), torch.float64)
+
+
+def test_invalid_matrices_rejected():
+    a = random_csr(200, seed=46, density=0.05)
+    rp, col, val = to_dev(a)
+    bad = rp.clone()
+    bad[0] = 1
+    with pytest.raises(sf.SpmvError) as e:
+        sf.Matrix.from_csr(bad, col, val)
+    assert e.value.code == -2 and "rowptr[0]" in str(e.value)
+    bad = rp.clone()
+    bad[50] = bad[52] + 1
+    with pytest.raises(sf.SpmvError) as e:
+        sf.Matrix.from_csr(bad, col, val)
+    assert e.value.code == -2
+    bad = rp.clone()
+    bad[-1] -= 1
+    with pytest.raises(sf.SpmvError) as e:
+        sf.Matrix.from_csr(bad, col, val)
+    assert e.value.code == -2 and "rowptr[n]" in str(e.value)
+    badc = col.clone()
+    badc[7] = a.n
+    with pytest.raises(sf.SpmvError) as e:
+        sf.Matrix.from_csr(rp, badc, val)
+    assert e.value.code == -2 and "column" in str(e.value)
+    badc[7] = -1
+    with pytest.raises(sf.SpmvError):
+        sf.Matrix.from_csr(rp, badc, val)
+    rows = torch.zeros(a.nnz, dtype=torch.int64, device="cuda")
+    rows[3] = a.n
+    with pytest.raises(sf.SpmvError) as e:
+        sf.Matrix.from_coo(rows, col, val, a.n)
+    assert e.value.code == -2 and "row" in str(e.value)
+
+
+def test_footprint_refusal_keeps_handle():
+    a = MATS["ragged"]()
+    x_np, y0_np = vectors(a.n, 12)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("sell64")
+    with pytest.raises(sf.SpmvError) as e:
+        M.convert("ellr", footprint_budget=1 << 20)
+    assert e.value.code == -4
+    assert M.info()["format"] == "sell64"
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    check(a, x_np, y0_np, 1.0, 0.0, apply(M, x, y0, 1.0, 0.0), torch.float64)
+    with pytest.raises(sf.SpmvError) as e:
+        M.export("ell_col")
+    assert e.value.code == -6
+
+
+def test_argument_errors_on_device():
+    a = MATS["c1"]()
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
+    buf = torch.zeros(2 * a.n, dtype=torch.float64, device="cuda")
+    with pytest.raises(sf.SpmvError) as e:
+        M.apply(buf[10:10 + a.n], buf[:a.n])
+    assert e.value.code == -1 and "overlap" in str(e.value)
+    with pytest.raises(sf.SpmvError) as e:
+        M.convert("csr", subwave=3)
+    assert e.value.code == -1
+    with pytest.raises(TypeError):
+        M.apply(torch.zeros(a.n, dtype=torch.float32, device="cuda"),
+                torch.zeros(a.n, dtype=torch.float32, device="cuda"))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_beta_zero_ignores_nan_y(fmt):
+    a = MATS["ragged"]()
+    x_np, _ = vectors(a.n, 13)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt)
+    x = torch.from_numpy(x_np).cuda()
+    y = torch.full((a.n,), float("nan"), dtype=torch.float64, device="cuda")
+    M.apply(y, x, 1.0, 0.0)
+    yn = y.cpu().numpy()
+    assert np.all(np.isfinite(yn))
+    check(a, x_np, None, 1.0, 0.0, yn, torch.float64)
+
+
+def test_determinism():
+    a = MATS["long_spans"]()
+    x_np, _ = vectors(a.n, 14)
+    x = torch.from_numpy(x_np).cuda()
+    for fmt in FORMATS:
+        M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt)
+        y1 = torch.zeros(a.n, dtype=torch.float64, device="cuda")
+        y2 = torch.zeros_like(y1)
+        M.apply(y1, x)
+        M.apply(y2, x)
+        torch.cuda.synchronize()
+        if fmt in ("csr", "ellr"):
+            assert torch.equal(y1, y2), fmt
+        else:
+            ref, sc = oracle.spmv(a, x_np)
+            assert oracle.check(y1.cpu().numpy(), ref, sc, 1e-12)[0]
+            assert oracle.check(y2.cpu().numpy(), ref, sc, 1e-12)[0]
+        M.convert(fmt)  # converting twice gives the same layout
+        M.close()
+
+
+def test_convert_twice_same_arrays():
+    a = MATS["ragged"]()
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
+    for fmt, arrays in [("sell64", ["sell_perm", "sell_col", "sell_val", "sell_slice_ptr"]),
+                        ("hec", ["ell_col", "tail_ptr", "tail_col", "tail_val"])]:
+        M.convert(fmt)
+        first = [M.export(n).tobytes() for n in arrays]
+        M.convert(fmt)
+        assert first == [M.export(n).tobytes() for n in arrays]
+
+
+def test_stream_copy():
+    src = torch.randn(1 << 20, dtype=torch.float64, device="cuda")
+    dst = torch.empty_like(src)
+    sf.stream_copy(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    s2 = torch.arange(1000, dtype=torch.int8, device="cuda")  # 1000 bytes: ragged tail
+    d2 = torch.zeros_like(s2)
+    sf.stream_copy(d2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(d2, s2)
+
+
+def test_apply_on_side_stream():
+    a = MATS["ragged"]()
+    x_np, _ = vectors(a.n, 15)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("hec")
+    x = torch.from_numpy(x_np).cuda()
+    s = torch.cuda.Stream()
+    y = torch.zeros(a.n, dtype=torch.float64, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        M.apply(y, x)
+    s.synchronize()
+    check(a, x_np, None, 1.0, 0.0, y.cpu().numpy(), torch.float64)
