@@ -171,15 +171,25 @@ hipError_t launch_sell(const SellView& a, bool f64, void* y, const void* x, doub
 }
 
 // ---------------------------------------------------------------------------
-// reference copy with the kernels' load style (16-byte nontemporal loads)
+// reference copy with the kernels' load style: 16-byte nontemporal loads and
+// stores, four per lane in flight, grid-stride over a capped grid
 // ---------------------------------------------------------------------------
 typedef int copy_vec_t __attribute__((ext_vector_type(4)));
+constexpr int kCopyUnroll = 4;
 
 __global__ __launch_bounds__(256) void k_copy(copy_vec_t* __restrict__ dst,
                                               const copy_vec_t* __restrict__ src, int64_t n16) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    const int64_t stride = (int64_t)gridDim.x * 256 * kCopyUnroll;
+    for (int64_t i = (int64_t)blockIdx.x * 256 * kCopyUnroll + threadIdx.x; i < n16;
+         i += stride) {
+        copy_vec_t t[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            if (i + u * 256 < n16) t[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            if (i + u * 256 < n16) __builtin_nontemporal_store(t[u], dst + i + u * 256);
+    }
 }
 
 __global__ void k_copy_tail(char* dst, const char* src, int64_t from, int64_t bytes) {
@@ -190,7 +200,7 @@ __global__ void k_copy_tail(char* dst, const char* src, int64_t from, int64_t by
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
     const int64_t n16 = bytes / 16;
     if (n16 > 0) {
-        int64_t blocks = (n16 + 255) / 256;
+        int64_t blocks = (n16 + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll);
         if (blocks > 256 * 64) blocks = 256 * 64;
         hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(256), 0, stream,
                            (copy_vec_t*)dst, (const copy_vec_t*)src, n16);

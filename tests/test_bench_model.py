@@ -1,0 +1,88 @@
+"""The benchmark's bytes model, pinned by the pages' PCIe thresholds and by
+hand-computed byte counts, plus the shape of the bench JSON line."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "p1_pcie_thresholds.txt")
+
+
+def threshold(alpha_kind, ratio, penalty):
+    """N_nzr at which device spMVM time equals (50 %) or is 10x (10 %) the
+    PCIe time of moving RHS in and LHS out (16 bytes per row, DP).
+
+    Device time per row = bytes_model per row / B_GPU for an ELL-R matrix with
+    N_nzr entries per row; PCIe time per row = 16 / B_PCI.
+    """
+    def dev_bytes_per_row(nnzr):
+        n = 1000
+        alpha = 1.0 / nnzr if alpha_kind == "inv" else 1.0
+        return bench.bytes_model("ellr", n, int(n * nnzr), 8, x_alpha=alpha) / n
+
+    target = 16.0 * ratio * (1 if penalty == 50 else 10)
+    lo, hi = 0.01, 1e4
+    for _ in range(200):
+        mid = (lo + hi) / 2
+        if dev_bytes_per_row(mid) < target:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def test_pcie_thresholds_from_code_balance():
+    """[GPGPU clusters] Sect. 2.3 prints 25, 7, 80, 266; the reconstructed
+    code balance (8 + 4 + 8 alpha per entry, 4 + 8 per row) gives them
+    within one."""
+    for line in open(GOLD):
+        if line.startswith("#") or not line.strip():
+            continue
+        _, kind, ratio, penalty, page = line.split()
+        got = threshold(kind, float(ratio), int(penalty))
+        assert abs(got - float(page)) <= 1.0, (kind, ratio, penalty, got, page)
+
+
+def test_bytes_model_exact_counts():
+    # C1: 20,224 entries, 4,096 rows, fp64, CSR: 12*20224 + 4*4097 + 8*4096 + 8*4096
+    assert bench.bytes_model("csr", 4096, 20224, 8) == 12 * 20224 + 4 * 4097 + 16 * 4096
+    assert bench.bytes_model("csr", 4096, 20224, 8) == 324_612
+    # C3: 55,742,968 entries on 2,097,152 rows
+    assert bench.bytes_model("csr", 2_097_152, 55_742_968, 8) == 710_858_660
+    assert bench.bytes_model("csr", 2_097_152, 55_742_968, 4) == 471_109_572
+    # beta != 0 reads y once more
+    assert bench.bytes_model("ellr", 100, 1000, 8, beta_nonzero=True) == \
+        bench.bytes_model("ellr", 100, 1000, 8) + 800
+    # per-format row information
+    assert bench.row_info_bytes("hyb", 10, tail_nnz=7) == 40 + 28
+    assert bench.row_info_bytes("hec", 10) == 40 + 44
+    assert bench.row_info_bytes("sell64", 130) == 4 * 130 * 2 + 8 * 4
+
+
+def test_gpus_above_one_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+@pytest.mark.gpu
+def test_bench_json_line():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload",
+                        "c1_laplace2d_64", "--steps", "3", "--warmup", "1", "--no-cpu",
+                        "--no-stream"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+              "roofline", "formats", "best_format"):
+        assert k in out, k
+    assert out["config"]["workload"] == "c1_laplace2d_64"
+    assert set(out["formats"]) == {"csr", "ellr", "sell64", "hyb", "hec"}
+    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert k in out["roofline"]
