@@ -24,7 +24,10 @@
  *             Product Kernels on GPUs", abstract).
  *   HEC       an ELL part of width K plus the remaining entries in CSR form
  *             ("Development of Krylov...", Sect. 2.1, Fig. 3); the ELL part
- *             is applied first, then the irregular part.
+ *             is applied first, then the irregular part.  The ELL part of
+ *             HYB and HEC is stored column by column in blocks of 1024 rows
+ *             (the same page sets the ELL stride to "256 or other multiples"
+ *             of the SIMD width rather than to the matrix height).
  *
  * Conventions shared by all entry points
  *   - Every array argument is a DEVICE pointer (e.g. a torch tensor's
@@ -86,11 +89,21 @@ typedef struct {
      * K = max{k >= 0 : #{rows with length >= k} >= ceil(n/3)};
      * a value >= 0 is used as given, clamped to the longest row. */
     int32_t ell_width;
-    /* CSR: lanes cooperating on one row, a power of two in 1..64; 0 picks
-     * the smallest power of two >= the longest row, at most 64 (the
-     * subwarp rule of "Sparse Linear Algebra on AMD and NVIDIA GPUs -- The
-     * Race Is On": threads per row follow the maximum row length). */
+    /* CSR: lanes cooperating on one row, a power of two in 1..64.  0 times
+     * every candidate on the device during the conversion and keeps the
+     * fastest.  (The subwarp rule of "Sparse Linear Algebra on AMD and
+     * NVIDIA GPUs -- The Race Is On" -- threads per row follow the maximum
+     * row length -- is the value spmv_create starts with.) */
     int32_t subwave;
+    /* ELL-R / HYB / HEC: stage x in LDS.  The workgroup keeps the x entries
+     * within about +-9,700 (fp64) or +-19,900 (fp32) positions of its rows
+     * in a window that slides with the rows (the "banded" structure of FEM
+     * and stencil matrices); entries outside the window are read from
+     * global memory.  -1 decides from the matrix (on when at least half of
+     * the entries fall inside the window, and for ELL-R only when the
+     * longest row has at most 128 entries), 0 off, 1 on. */
+    int32_t x_window;
+    int32_t reserved;      /* must be 0 */
     /* Largest device footprint a padded format (ELL-R) may take, in bytes;
      * 0 means 75% of the device's memory. */
     uint64_t footprint_budget_bytes;
@@ -105,11 +118,18 @@ typedef struct {
     int32_t max_len;       /* longest row */
     int32_t ell_width;     /* ELL-R: max_len; HYB/HEC: K; otherwise 0 */
     int64_t tail_nnz;      /* HYB/HEC: entries outside the ELL part */
-    int64_t ell_stride;    /* ELL-R / HYB / HEC: 64 * ceil(n / 64) */
+    int64_t ell_stride;    /* ELL-R / HYB / HEC: slots between consecutive
+                              entries of a row (rows per column-major block):
+                              ELL-R 64 * ceil(n / 64), HYB/HEC 1024 */
     int64_t slots;         /* stored slots of the active format incl. padding */
     int32_t subwave;       /* CSR: lanes per row */
     int32_t nslices;       /* SELL-64: slices */
     uint64_t footprint_bytes; /* device bytes held by the handle */
+    int32_t x_window;      /* 1 when the active format stages x in LDS */
+    int32_t reserved;
+    double band_fraction;  /* share of entries within the window's reach
+                              (computed by ELL-R / HYB / HEC conversions) */
+    int64_t ell_rows;      /* ELL-R / HYB / HEC: rows padded to whole blocks */
 } spmv_info_t;
 
 /* arrays readable with spmv_export */
@@ -117,9 +137,13 @@ typedef enum {
     SPMV_A_ROWPTR = 0,     /* CSR row pointer, int32[n+1] */
     SPMV_A_COL = 1,        /* CSR columns, int32[nnz] */
     SPMV_A_VAL = 2,        /* CSR values, dtype[nnz] */
-    SPMV_A_ELL_COL = 3,    /* ELL-R / ELL part: int32[width * stride], column-major */
-    SPMV_A_ELL_VAL = 4,    /* dtype[width * stride]; pad slots col 0, value +0 */
-    SPMV_A_ELL_LEN = 5,    /* int32[stride]: entries of each row held in ELL */
+    SPMV_A_ELL_COL = 3,    /* ELL-R / ELL part: int32[width * ell_rows] in
+                              column-major blocks of B = ell_stride rows: entry j
+                              of row i at (i / B) * width * B + j * B + i % B
+                              (ELL-R: a single block, B = 64 * ceil(n / 64);
+                              HYB/HEC: B = 1024) */
+    SPMV_A_ELL_VAL = 4,    /* dtype[width * ell_rows]; pad slots col 0, value +0 */
+    SPMV_A_ELL_LEN = 5,    /* int32[ell_rows]: entries of each row held in ELL */
     SPMV_A_SELL_PERM = 6,  /* int32[n]: original row at sorted position r */
     SPMV_A_SELL_SLICE_PTR = 7, /* int64[nslices+1]: first slot of each slice */
     SPMV_A_SELL_LEN = 8,   /* int32[64 * nslices]: length of sorted row r */

@@ -9,7 +9,8 @@ Functions (each restates a definition from the pages; see oracle.c):
 
 * ``spmv``       -- y = alpha*A*x + beta*y with Dot2 row sums in fp64, and
                     the per-row scale |alpha|*sum|a*x| + |beta*y|.
-* ``ell``        -- ELLPACK-R arrays (column-major, stride a multiple of 64).
+* ``ell``        -- ELLPACK arrays: ELLPACK-R (column-major, stride a multiple of
+                    64) or the HYB/HEC ELL part (column-major blocks of rows).
 * ``sell``       -- SELL-64 (sorted, sliced, padded) arrays and permutation.
 * ``hyb_width``  -- the ELL width of the HYB/HEC split.
 * ``tail``       -- the irregular part of the split as COO and CSR.
@@ -57,7 +58,7 @@ def _load():
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_len.argtypes = [I64, P]
         lib.oracle_max_len.restype = I64
-        lib.oracle_ell.argtypes = [I64, P, P, P, ctypes.c_int, I64, P, P, P]
+        lib.oracle_ell.argtypes = [I64, P, P, P, ctypes.c_int, I64, I64, P, P, P]
         lib.oracle_sell_layout.argtypes = [I64, P, P, P, P]
         lib.oracle_sell_layout.restype = I64
         lib.oracle_sell_fill.argtypes = [I64, P, P, P, ctypes.c_int, P, P, P, P]
@@ -133,21 +134,26 @@ def max_len(a) -> int:
     return int(_load().oracle_max_len(a.n, _p(_c(a.rowptr, np.int64))))
 
 
-def ell(a, width: int | None = None):
-    """ELLPACK-R of the given width (default: longest row).
+ELL_BLOCK_SPLIT = 1024   # rows per column-major block of the HYB/HEC ELL part
 
-    Returns (col[W*S] int32, val[W*S], len[S] int32) with S = pad64(n).
+
+def ell(a, width: int | None = None, block: int = 0):
+    """ELLPACK arrays of the given width (default: longest row).
+
+    block == 0: ELLPACK-R, one column-major block of pad64(n) rows.
+    block > 0: column-major blocks of `block` rows (the HYB/HEC ELL part).
+    Returns (col[W*R] int32, val[W*R], len[R] int32), R the padded rows.
     """
     lib = _load()
     rowptr = _c(a.rowptr, np.int64)
     W = max_len(a) if width is None else int(width)
-    S = pad64(a.n)
+    R = pad64(a.n) if block <= 0 else -(-a.n // block) * block
     val = np.ascontiguousarray(a.val)
-    oc = np.empty(W * S, dtype=np.int32)
-    ov = np.empty(W * S, dtype=val.dtype)
-    ol = np.empty(S, dtype=np.int32)
+    oc = np.empty(W * R, dtype=np.int32)
+    ov = np.empty(W * R, dtype=val.dtype)
+    ol = np.empty(R, dtype=np.int32)
     lib.oracle_ell(a.n, _p(rowptr), _p(_c(a.col, np.int32)), _p(val), val.itemsize,
-                   W, _p(oc), _p(ov), _p(ol))
+                   W, int(block), _p(oc), _p(ov), _p(ol))
     return oc, ov, ol
 
 

@@ -41,8 +41,12 @@
  *                   Sect. 2.1, Figs. 2-3; "Load-balancing Sparse Matrix
  *                   Vector Product Kernels on GPUs", abstract).
  *   Where the pages leave a convention open the reading taken is:
- *     - ELL stride S = 64 * ceil(n / 64); slot (i, j) at j * S + i; pad
+ *     - ELL-R stride S = 64 * ceil(n / 64); slot (i, j) at j * S + i; pad
  *       slots hold column 0 and value +0.0; padded rows have length 0.
+ *       The ELL part of HYB/HEC is stored the same way in blocks of 1024
+ *       rows (the Krylov/AMG page sets the ELL stride to "256 or other
+ *       multiples" of the SIMD width): slot (i, j) at
+ *       (i / 1024) * W * 1024 + j * 1024 + i % 1024.
  *     - SELL sort key (length descending, row ascending) -- unique, so the
  *       permutation is unique; slice s has width w_s = length of its first
  *       (longest) row; entry j of sorted row r sits at
@@ -169,20 +173,24 @@ int64_t oracle_max_len(int64_t n, const int64_t *rowptr)
 }
 
 /*
- * ELLPACK-R of width W (W >= every row length handled; entries j >= W of a
- * row are skipped, which is how the ELL part of HYB/HEC is built).
- * out_col/out_val hold W * S slots, out_len S lengths, S = pad64(n).
+ * ELLPACK arrays of width W (W >= every row length handled; entries j >= W
+ * of a row are skipped, which is how the ELL part of HYB/HEC is built),
+ * stored in column-major blocks of B rows: entry j of row i in slot
+ * (i / B) * W * B + j * B + i % B.  block <= 0 means one block of
+ * B = pad64(n) rows (ELLPACK-R's column-by-column layout).  Rows are padded
+ * to R = ceil(n / B) * B; out_col/out_val hold W * R slots, out_len R lengths.
  */
 void oracle_ell(int64_t n, const int64_t *rowptr, const int32_t *col,
-                const void *val, int vsize, int64_t W,
+                const void *val, int vsize, int64_t W, int64_t block,
                 int32_t *out_col, void *out_val, int32_t *out_len)
 {
-    int64_t S = pad64(n);
+    int64_t B = block > 0 ? block : pad64(n);
+    int64_t R = block > 0 ? (n + block - 1) / block * block : B;
     char *ov = (char *)out_val;
     const char *iv = (const char *)val;
-    memset(out_col, 0, (size_t)(W * S) * sizeof(int32_t));
-    memset(ov, 0, (size_t)(W * S) * (size_t)vsize);
-    for (int64_t i = 0; i < S; ++i)
+    memset(out_col, 0, (size_t)(W * R) * sizeof(int32_t));
+    memset(ov, 0, (size_t)(W * R) * (size_t)vsize);
+    for (int64_t i = 0; i < R; ++i)
         out_len[i] = 0;
     for (int64_t i = 0; i < n; ++i) {
         int64_t len = rowptr[i + 1] - rowptr[i];
@@ -190,7 +198,7 @@ void oracle_ell(int64_t n, const int64_t *rowptr, const int32_t *col,
             len = W;
         out_len[i] = (int32_t)len;
         for (int64_t j = 0; j < len; ++j) {
-            int64_t slot = j * S + i;
+            int64_t slot = (i / B) * W * B + j * B + i % B;
             int64_t k = rowptr[i] + j;
             out_col[slot] = col[k];
             memcpy(ov + slot * vsize, iv + k * vsize, (size_t)vsize);

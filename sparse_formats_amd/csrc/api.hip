@@ -18,7 +18,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/spmv_amd.h"
+#include "spmv_amd.h"
 #include "internal.h"
 
 using namespace spmv;
@@ -95,7 +95,7 @@ int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 struct Built {
     int format = SPMV_CSR;
     // ELL-R, or the ELL part of HYB / HEC
-    int64_t ell_width = 0, ell_stride = 0;
+    int64_t ell_width = 0, ell_bh = 0, ell_rows = 0;  // width, rows per block, padded rows
     DevBuf ell_col, ell_val, ell_len;
     // SELL-64
     int64_t nslices = 0, sell_slots = 0;
@@ -105,6 +105,9 @@ struct Built {
     // tail of HYB / HEC
     int64_t tail_nnz = 0, tail_chunks = 0;
     DevBuf tail_row, tail_ptr, tail_col, tail_val, chunk_row;
+    // x staged in LDS by the ELL / tail kernels
+    bool window = false;
+    double band_fraction = 0;
 
     size_t bytes() const {
         return ell_col.bytes + ell_val.bytes + ell_len.bytes + slice_ptr.bytes + sell_len.bytes +
@@ -207,25 +210,45 @@ __global__ void k_max_len(int64_t n, const int* __restrict__ rowptr, int* out) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
         m = max(m, rowptr[i + 1] - rowptr[i]);
-    if (m) atomicMax(out, m);
+    for (int d = 32; d > 0; d >>= 1) m = max(m, __shfl_xor(m, d));  // one atomic per wave
+    if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m);
 }
 
-__global__ void k_len_hist(int64_t n, const int* __restrict__ rowptr, int* __restrict__ hist) {
+// row-length histogram; short lengths are counted in LDS first because a
+// handful of bins would otherwise take an atomic from every row
+constexpr int kHistLds = 2048;
+__global__ __launch_bounds__(256) void k_len_hist(int64_t n, int W, const int* __restrict__ rowptr,
+                                                  int* __restrict__ hist) {
+    __shared__ int lh[kHistLds];
+    for (int b = threadIdx.x; b < kHistLds; b += blockDim.x) lh[b] = 0;
+    __syncthreads();
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        atomicAdd(hist + (rowptr[i + 1] - rowptr[i]), 1);
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int L = rowptr[i + 1] - rowptr[i];
+        if (L < kHistLds)
+            atomicAdd(lh + L, 1);
+        else
+            atomicAdd(hist + L, 1);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < kHistLds && b <= W; b += blockDim.x)
+        if (lh[b]) atomicAdd(hist + b, lh[b]);
 }
 
-// ELL slots: slot t = j * S + i holds entry j of row i (j < min(len_i, W)),
-// otherwise column 0 / value +0.  len[i] = min(len_i, W), 0 for padded rows.
+// ELL slots in blocks of bh rows, each block column by column: storage
+// position t holds entry j of row i (j < min(len_i, W)), otherwise column 0 /
+// value +0; len[i] = min(len_i, W), 0 for padded rows.
 template <typename V>
-__global__ void k_ell_fill(int64_t n, int64_t S, int64_t W, const int* __restrict__ rowptr,
-                           const int* __restrict__ col, const V* __restrict__ val,
-                           int* __restrict__ ecol, V* __restrict__ eval, int* __restrict__ elen) {
-    const int64_t total = S * W;
+__global__ void k_ell_fill(int64_t n, int64_t rows, int64_t bh, int64_t W,
+                           const int* __restrict__ rowptr, const int* __restrict__ col,
+                           const V* __restrict__ val, int* __restrict__ ecol,
+                           V* __restrict__ eval, int* __restrict__ elen) {
+    const int64_t total = rows * W;
+    const int64_t bstride = bh * W;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
          t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t j = t / S, i = t - j * S;
+        const int64_t blk = t / bstride, rem = t - blk * bstride;
+        const int64_t j = rem / bh, i = blk * bh + (rem - j * bh);
         int c = 0;
         V v = V(0);
         if (i < n) {
@@ -239,9 +262,23 @@ __global__ void k_ell_fill(int64_t n, int64_t S, int64_t W, const int* __restric
         ecol[t] = c;
         eval[t] = v;
     }
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows;
          i += (int64_t)gridDim.x * blockDim.x)
         elen[i] = i < n ? (int)std::min<int64_t>(rowptr[i + 1] - rowptr[i], W) : 0;
+}
+
+// entries within `lead` positions of their row (reach of the LDS window)
+__global__ void k_band_count(int64_t n, int64_t lead, const int* __restrict__ rowptr,
+                             const int* __restrict__ col, unsigned long long* out) {
+    unsigned long long cnt = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        for (int k = rowptr[i]; k < rowptr[i + 1]; ++k) {
+            const int64_t d = (int64_t)col[k] - i;
+            cnt += (d >= -lead && d <= lead) ? 1u : 0u;
+        }
+    for (int d = 32; d > 0; d >>= 1) cnt += __shfl_xor(cnt, d);
+    if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(out, cnt);
 }
 
 // sort key for SELL: rows by length descending; the radix sort is stable,
@@ -371,17 +408,22 @@ uint64_t budget_bytes(const spmv_convert_opts& o) {
     return (uint64_t)(0.75 * (double)tot);
 }
 
+// ELL arrays of width W: one column-major block of all rows (block = 0,
+// ELLPACK-R) or column-major blocks of `block` rows (ELL part of HYB/HEC)
 template <typename V>
-void build_ell_part(const spmv_handle* h, int64_t W, Built& b, hipStream_t s) {
-    const int64_t S = pad64(h->n);
+void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, Built& b, hipStream_t s) {
+    const int64_t bh = block > 0 ? block : pad64(h->n);
+    const int64_t rows = block > 0 ? (h->n + block - 1) / block * block : bh;
     b.ell_width = W;
-    b.ell_stride = S;
-    b.ell_col.alloc((size_t)(W * S) * 4);
-    b.ell_val.alloc((size_t)(W * S) * sizeof(V));
-    b.ell_len.alloc((size_t)S * 4);
-    hipLaunchKernelGGL(k_ell_fill<V>, dim3(grid_for(std::max<int64_t>(W * S, S))), dim3(256), 0,
-                       s, h->n, S, W, h->rowptr.as<int>(), h->col.as<int>(), h->val.as<V>(),
-                       b.ell_col.as<int>(), b.ell_val.as<V>(), b.ell_len.as<int>());
+    b.ell_bh = bh;
+    b.ell_rows = rows;
+    b.ell_col.alloc((size_t)(W * rows) * 4);
+    b.ell_val.alloc((size_t)(W * rows) * sizeof(V));
+    b.ell_len.alloc((size_t)rows * 4);
+    hipLaunchKernelGGL(k_ell_fill<V>, dim3(grid_for(std::max<int64_t>(W * rows, rows))), dim3(256),
+                       0, s, h->n, rows, std::max<int64_t>(bh, 1), W, h->rowptr.as<int>(),
+                       h->col.as<int>(), h->val.as<V>(), b.ell_col.as<int>(), b.ell_val.as<V>(),
+                       b.ell_len.as<int>());
     hip_check(hipGetLastError(), "ell fill");
 }
 
@@ -470,8 +512,8 @@ int64_t choose_width(const spmv_handle* h, int requested, std::vector<int>& hist
     DevBuf dh((size_t)(W + 1) * 4);
     hip_check(hipMemsetAsync(dh.p, 0, (size_t)(W + 1) * 4, s), "hipMemsetAsync");
     if (h->n > 0) {
-        hipLaunchKernelGGL(k_len_hist, dim3(grid_for(h->n)), dim3(256), 0, s, h->n,
-                           h->rowptr.as<int>(), dh.as<int>());
+        hipLaunchKernelGGL(k_len_hist, dim3(std::min<unsigned>(grid_for(h->n), 2048)), dim3(256), 0,
+                           s, h->n, W, h->rowptr.as<int>(), dh.as<int>());
         hip_check(hipGetLastError(), "histogram");
     }
     hip_check(hipMemcpyAsync(hist.data(), dh.p, (size_t)(W + 1) * 4, hipMemcpyDeviceToHost, s),
@@ -497,7 +539,7 @@ void build_split(const spmv_handle* h, int format, int requested, Built& b, hipS
     const int64_t K = choose_width(h, requested, hist, s);
     int64_t tail = 0;
     for (size_t l = (size_t)K + 1; l < hist.size(); ++l) tail += (int64_t)hist[l] * ((int64_t)l - K);
-    build_ell_part<V>(h, K, b, s);
+    build_ell_part<V>(h, K, kEllBlock, b, s);
     b.tail_nnz = tail;
     const int64_t n = h->n;
     b.tail_ptr.alloc((size_t)(n + 1) * 4);
@@ -543,6 +585,65 @@ void build_split(const spmv_handle* h, int format, int requested, Built& b, hipS
         b.tail_ptr.release();  // HYB keeps the COO rows only
     }
     sync(s);
+}
+
+// CSR sub-wave: time every candidate group size on the device and keep the
+// fastest (the apply does not depend on the values of x, so zeros are used)
+int tune_subwave(const spmv_handle* h, hipStream_t s) {
+    int rule = 1;  // smallest power of two >= the longest row, at most 64
+    while (rule < 64 && rule < h->max_len) rule <<= 1;
+    if (h->n == 0 || h->nnz == 0) return rule;
+    DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
+    hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
+    hipEvent_t e0, e1;
+    hip_check(hipEventCreate(&e0), "hipEventCreate");
+    hip_check(hipEventCreate(&e1), "hipEventCreate");
+    const CsrView v{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
+    const bool f64 = h->dtype == SPMV_F64;
+    int best = rule;
+    float best_ms = 1e30f;
+    hipError_t err = hipSuccess;
+    for (int sw = h->max_len <= 2 ? 1 : 2; sw <= 64 && err == hipSuccess; sw <<= 1) {
+        err = launch_csr(v, sw, f64, ys.p, xs.p, 1.0, 0.0, s);
+        if (err == hipSuccess) err = hipEventRecord(e0, s);
+        for (int r = 0; r < 2 && err == hipSuccess; ++r)
+            err = launch_csr(v, sw, f64, ys.p, xs.p, 1.0, 0.0, s);
+        if (err == hipSuccess) err = hipEventRecord(e1, s);
+        if (err == hipSuccess) err = hipEventSynchronize(e1);
+        float ms = 0;
+        if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+        if (err == hipSuccess && ms < best_ms) best_ms = ms, best = sw;
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    hip_check(err, "sub-wave tuning");
+    return best;
+}
+
+// share of the entries the LDS window reaches, and whether to use it
+void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s) {
+    const int64_t lead = h->dtype == SPMV_F64 ? EllWinLead<double>::value
+                                              : EllWinLead<float>::value;
+    DevBuf cnt(8);
+    hip_check(hipMemsetAsync(cnt.p, 0, 8, s), "hipMemsetAsync");
+    if (h->n > 0) {
+        hipLaunchKernelGGL(k_band_count, dim3(grid_for(h->n)), dim3(256), 0, s, h->n, lead,
+                           h->rowptr.as<int>(), h->col.as<int>(), cnt.as<unsigned long long>());
+        hip_check(hipGetLastError(), "band count");
+    }
+    const unsigned long long c = read_scalar<unsigned long long>(cnt.p, s);
+    b.band_fraction = h->nnz ? (double)c / (double)h->nnz : 0.0;
+    if (opt >= 0) {
+        // window offsets are computed in 32 bits: rows and columns plus the
+        // window length must stay below 2^31
+        b.window = opt == 1 && h->n < INT32_MAX - 2 * (int64_t)WinLen<float>::value;
+        return;
+    }
+    if (h->n >= INT32_MAX - 2 * (int64_t)WinLen<float>::value) {
+        b.window = false;
+        return;
+    }
+    b.window = b.band_fraction >= 0.5 && (format != SPMV_ELLR || h->max_len <= 128);
 }
 
 int run_guarded(const std::function<void()>& body) {
@@ -678,14 +779,13 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
     return run_guarded([&] {
         if (!h) fail(SPMV_ERR_STATE, "null handle");
         if (!valid_format(format)) fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
-        spmv_convert_opts o{-1, 0, 0};
+        spmv_convert_opts o{-1, 0, -1, 0, 0};
         if (opts) o = *opts;
+        if (o.x_window < -1 || o.x_window > 1 || o.reserved != 0)
+            fail(SPMV_ERR_INVALID_ARG, "x_window must be -1, 0 or 1 and reserved 0");
         if (format == SPMV_CSR) {
             int sw = o.subwave;
-            if (sw == 0) {
-                sw = 1;
-                while (sw < 64 && sw < h->max_len) sw <<= 1;
-            }
+            if (sw == 0) sw = tune_subwave(h, nullptr);
             if (sw < 1 || sw > 64 || (sw & (sw - 1)))
                 fail(SPMV_ERR_INVALID_ARG, "subwave must be a power of two in 1..64 (got %d)", sw);
             h->subwave = sw;
@@ -707,9 +807,10 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
                      "budget of %.3g bytes",
                      need, (long long)h->n, (long long)S, (long long)W, (double)budget);
             if (f64)
-                build_ell_part<double>(h, W, b, s);
+                build_ell_part<double>(h, W, 0, b, s);
             else
-                build_ell_part<float>(h, W, b, s);
+                build_ell_part<float>(h, W, 0, b, s);
+            decide_window(h, format, o.x_window, b, s);
             sync(s);
         } else if (format == SPMV_SELL64) {
             if (f64)
@@ -721,6 +822,7 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
                 build_split<double>(h, format, o.ell_width, b, s);
             else
                 build_split<float>(h, format, o.ell_width, b, s);
+            decide_window(h, format, o.x_window, b, s);
         }
         h->fmt = std::move(b);
         h->format = format;
@@ -755,11 +857,13 @@ int spmv_apply(spmv_t h, void* y, const void* x, double alpha, double beta, void
         case SPMV_ELLR:
         case SPMV_HYB:
         case SPMV_HEC: {
-            EllView a{(int)h->n, b.ell_stride, b.ell_len.as<int>(), b.ell_col.as<int>(), b.ell_val.p};
+            EllView a{(int)h->n, std::max<int64_t>(b.ell_bh, 1), b.ell_width * b.ell_bh,
+                      (int)b.ell_width, b.ell_len.as<int>(), b.ell_col.as<int>(), b.ell_val.p,
+                      b.window};
             e = launch_ell(a, f64, y, x, alpha, beta, s);
             if (e == hipSuccess && h->format != SPMV_ELLR && b.tail_nnz > 0) {
                 TailView t{(int)h->n, b.tail_nnz, b.tail_row.as<int>(), b.tail_ptr.as<int>(),
-                           b.chunk_row.as<int>(), b.tail_col.as<int>(), b.tail_val.p};
+                           b.chunk_row.as<int>(), b.tail_col.as<int>(), b.tail_val.p, b.window};
                 e = launch_tail(t, f64, y, x, alpha, s);
             }
             break;
@@ -811,8 +915,9 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
         case SPMV_CSR: i.slots = h->nnz; break;
         case SPMV_ELLR:
             i.ell_width = (int32_t)b.ell_width;
-            i.ell_stride = b.ell_stride;
-            i.slots = b.ell_width * b.ell_stride;
+            i.ell_stride = b.ell_bh;
+            i.ell_rows = b.ell_rows;
+            i.slots = b.ell_width * b.ell_rows;
             break;
         case SPMV_SELL64:
             i.nslices = (int32_t)b.nslices;
@@ -820,11 +925,14 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
             break;
         default:
             i.ell_width = (int32_t)b.ell_width;
-            i.ell_stride = b.ell_stride;
+            i.ell_stride = b.ell_bh;
+            i.ell_rows = b.ell_rows;
             i.tail_nnz = b.tail_nnz;
-            i.slots = b.ell_width * b.ell_stride + b.tail_nnz;
+            i.slots = b.ell_width * b.ell_rows + b.tail_nnz;
     }
     i.footprint_bytes = h->rowptr.bytes + h->col.bytes + h->val.bytes + b.bytes();
+    i.x_window = b.window ? 1 : 0;
+    i.band_fraction = b.band_fraction;
     *out = i;
     return SPMV_OK;
 }
@@ -843,9 +951,9 @@ int spmv_export(spmv_t h, int array, void* host_dst, int64_t capacity_bytes, int
             case SPMV_A_ROWPTR: src = h->rowptr.p, sz = (h->n + 1) * 4; break;
             case SPMV_A_COL: src = h->col.p, sz = h->nnz * 4; break;
             case SPMV_A_VAL: src = h->val.p, sz = h->nnz * vs; break;
-            case SPMV_A_ELL_COL: if (ell) src = b.ell_col.p, sz = b.ell_width * b.ell_stride * 4; break;
-            case SPMV_A_ELL_VAL: if (ell) src = b.ell_val.p, sz = b.ell_width * b.ell_stride * vs; break;
-            case SPMV_A_ELL_LEN: if (ell) src = b.ell_len.p, sz = b.ell_stride * 4; break;
+            case SPMV_A_ELL_COL: if (ell) src = b.ell_col.p, sz = b.ell_width * b.ell_rows * 4; break;
+            case SPMV_A_ELL_VAL: if (ell) src = b.ell_val.p, sz = b.ell_width * b.ell_rows * vs; break;
+            case SPMV_A_ELL_LEN: if (ell) src = b.ell_len.p, sz = b.ell_rows * 4; break;
             case SPMV_A_SELL_PERM: if (f == SPMV_SELL64) src = b.perm.p, sz = h->n * 4; break;
             case SPMV_A_SELL_SLICE_PTR: if (f == SPMV_SELL64) src = b.slice_ptr.p, sz = (b.nslices + 1) * 8; break;
             case SPMV_A_SELL_LEN: if (f == SPMV_SELL64) src = b.sell_len.p, sz = b.nslices * 64 * 4; break;

@@ -90,6 +90,33 @@ __device__ __forceinline__ T group_sum(T v) {
     return v;
 }
 
+// Workgroup barrier for LDS hand-offs that leaves global loads in flight:
+// waits only for this wave's LDS operations, then s_barrier.  A plain
+// __syncthreads() also waits for every outstanding global load, which would
+// drain the prefetch of the next step that the window kernels rely on.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Fill win with x[from, to) (element q at slot q mod WL): the loads of a
+// thread are all issued before its stores, so the fill costs one latency.
+template <typename T, int WL>
+__device__ __forceinline__ void window_fill(T* win, const T* __restrict__ x, int64_t from,
+                                            int64_t to) {
+    constexpr int kPer = (WL + 1023) / 1024;
+    T v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int64_t q = from + threadIdx.x + 1024 * u;
+        v[u] = q < to ? x[q] : T(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int64_t q = from + threadIdx.x + 1024 * u;
+        if (q < to) win[q % WL] = v[u];
+    }
+}
+
 // fp atomic add in L2 (device-scope, relaxed); hardware fp32/fp64 atomics
 // on coarse-grained device memory.
 __device__ __forceinline__ void atomic_add(double* p, double v) {

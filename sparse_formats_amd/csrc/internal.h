@@ -19,6 +19,33 @@ constexpr int kSellChunk = 128;
 constexpr int kTailPerLane = 8;
 constexpr int kTailChunk = 64 * kTailPerLane;
 
+// LDS window of x: one workgroup of 1024 threads per CU stages the x
+// entries near its rows in the whole 160 KiB of LDS, as a circular buffer
+// (element q at slot q mod WinLen) that slides forward with the rows.
+constexpr int kWinBytes = 160 * 1024;
+template <typename T>
+struct WinLen {
+    static constexpr int value = kWinBytes / (int)sizeof(T);
+};
+// ELL: row tiles of kEllWinTile rows (one per thread), the window centred
+// on the tile
+constexpr int kEllWinTile = 1024;
+template <typename T>
+struct EllWinLead {
+    static constexpr int value = (WinLen<T>::value - kEllWinTile) / 2;
+};
+// tail: a step's rows follow its first row, so the window leads by less
+template <typename T>
+struct WinLead {
+    static constexpr int value = WinLen<T>::value / 2 - 1024;
+};
+// tail window kernel: chunks per wave and per workgroup step (16 waves)
+constexpr int kTailChunksPerWave = 4;
+constexpr int kTailStepChunks = 16 * kTailChunksPerWave;
+// persistent workgroups launched for a window kernel: one per CU (the
+// window takes a CU's whole LDS), work spread evenly over them
+constexpr int kWinGroups = 256;
+
 struct CsrView {
     int n;
     const int* rowptr;
@@ -26,12 +53,23 @@ struct CsrView {
     const void* val;
 };
 
+// ELL arrays are stored in blocks of `bh` rows, each block column by column:
+// slot (i, j) at (i / bh) * bstride + j * bh + i % bh with bstride = width *
+// bh.  ELLPACK-R uses one block of all (padded) rows, i.e. the global
+// column-major layout; the ELL part of HYB/HEC uses blocks of kEllBlock rows
+// so that a tile of rows reads one contiguous slab (a few pages) instead of
+// `width` places a whole matrix height apart.
+constexpr int kEllBlock = 1024;
+
 struct EllView {
     int n;
-    int64_t stride;   // rows padded to a multiple of 64
-    const int* len;   // [stride]
-    const int* col;   // [width * stride], slot (i, j) at j * stride + i
+    int64_t bh;       // rows per block = distance between a row's slots
+    int64_t bstride;  // slots per block (width * bh)
+    int width;        // slots per row (every row's slots j < width exist)
+    const int* len;   // [padded rows]
+    const int* col;
     const void* val;
+    bool window;      // stage x in LDS (banded matrices)
 };
 
 struct SellView {
@@ -54,6 +92,7 @@ struct TailView {
     const int* chunk_row;  // HEC: row of the first entry of each wave chunk
     const int* col;
     const void* val;
+    bool window;           // stage x in LDS (banded matrices)
 };
 
 // kernel launchers (asynchronous on `stream`); fp64 when f64, else fp32

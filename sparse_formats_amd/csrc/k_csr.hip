@@ -7,6 +7,8 @@
 // group stride through the row (consecutive lanes read consecutive entries,
 // so a wave's loads of val/col are contiguous) and the partial sums are
 // combined with DPP / ds_swizzle moves inside the wave (no LDS traffic).
+// The loads allocate in the caches: with short rows a cache line is shared
+// by neighbouring groups, which would otherwise fetch it again.
 #include "common.h"
 #include "internal.h"
 
@@ -28,12 +30,12 @@ __global__ __launch_bounds__(256) void k_csr_vector(int n, const int* __restrict
     int k = k0 + sub;
     // two independent chains keep two loads of val/col in flight per lane
     for (; k + S < k1; k += 2 * S) {
-        const T v0 = ld_nt(val + k), v1 = ld_nt(val + k + S);
-        const int c0 = ld_nt(col + k), c1 = ld_nt(col + k + S);
+        const T v0 = val[k], v1 = val[k + S];
+        const int c0 = col[k], c1 = col[k + S];
         s0 = fma(v0, x[c0], s0);
         s1 = fma(v1, x[c1], s1);
     }
-    if (k < k1) s0 = fma(ld_nt(val + k), x[ld_nt(col + k)], s0);
+    if (k < k1) s0 = fma(val[k], x[col[k]], s0);
     T s = group_sum<S>(s0 + s1);
     if (sub == 0) y[row] = axpby(s, alpha, beta, y + row);
 }

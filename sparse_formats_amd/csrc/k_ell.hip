@@ -9,7 +9,11 @@
 // "Sparse Linear Algebra on AMD and NVIDIA GPUs -- The Race Is On" notes that
 // on AMD GPUs the column-major layout must be read with one lane per row (a
 // group of lanes on one row reads slots a whole stride apart); that is the
-// mapping kept here.
+// mapping kept here.  ELLPACK-R is one column-major block of all rows; the
+// ELL part of HYB/HEC is stored in column-major blocks of kEllBlock rows
+// (see internal.h).
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -19,46 +23,155 @@ namespace spmv {
 // ELLPACK-R (also the ELL part of HYB / HEC)
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void k_ell(int n, int64_t stride, const int* __restrict__ len,
+__global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
+                                             const int* __restrict__ len,
                                              const int* __restrict__ col,
                                              const T* __restrict__ val, const T* __restrict__ x,
                                              T* __restrict__ y, T alpha, T beta) {
     const int64_t i = xcd_tile(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
     if (i >= n) return;
     const int L = len[i];
-    const int* c = col + i;
-    const T* v = val + i;
+    const int64_t base = (i / bh) * bstride + i % bh;
+    const int* c = col + base;
+    const T* v = val + base;
     T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
     int j = 0;
     for (; j + 4 <= L; j += 4) {
-        const int64_t o = (int64_t)j * stride;
-        const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + stride);
-        const T v2 = ld_nt(v + o + 2 * stride), v3 = ld_nt(v + o + 3 * stride);
-        const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + stride);
-        const int c2 = ld_nt(c + o + 2 * stride), c3 = ld_nt(c + o + 3 * stride);
+        const int64_t o = (int64_t)j * bh;
+        const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + bh);
+        const T v2 = ld_nt(v + o + 2 * bh), v3 = ld_nt(v + o + 3 * bh);
+        const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + bh);
+        const int c2 = ld_nt(c + o + 2 * bh), c3 = ld_nt(c + o + 3 * bh);
         s0 = fma(v0, x[c0], s0);
         s1 = fma(v1, x[c1], s1);
         s2 = fma(v2, x[c2], s2);
         s3 = fma(v3, x[c3], s3);
     }
     for (; j < L; ++j) {
-        const int64_t o = (int64_t)j * stride;
+        const int64_t o = (int64_t)j * bh;
         s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
     }
     y[i] = axpby((s0 + s1) + (s2 + s3), alpha, beta, y + i);
+}
+
+// ELLPACK-R with x staged in LDS (banded matrices).  Workgroup g (1024
+// threads) runs a contiguous range of row tiles of kEllWinTile rows, each
+// thread taking rows r0 + tid + 1024 * h for h < kEllWinTile / 1024.  Tile t
+// sees the window [r0 - lead, r0 - lead + WL), so a row reads its x entries
+// within about +-lead of itself from LDS and any others from global memory.
+// The window takes the whole LDS, so only 16 waves share a CU: each thread
+// keeps 16 entries of each of its rows in flight per round (values,
+// columns, then the x reads), and the elements entering the window for the
+// next tile are loaded while the current tile computes.
+template <typename T>
+__global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bstride, int width,
+                                                  const int* __restrict__ len,
+                                                  const int* __restrict__ col,
+                                                  const T* __restrict__ val,
+                                                  const T* __restrict__ x, T* __restrict__ y,
+                                                  T alpha, T beta, int64_t ntiles) {
+    constexpr int WL = WinLen<T>::value;
+    constexpr int TILE = kEllWinTile;
+    constexpr int H = TILE / 1024;  // rows per thread per tile
+    constexpr int LEAD = (WL - TILE) / 2;
+    constexpr int B = 16;
+    __shared__ T win[WL];
+    const int64_t g = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t t0 = g * ntiles / gridDim.x, t1 = (g + 1) * ntiles / gridDim.x;
+    const int tid = threadIdx.x;
+    int64_t wlo = t0 * TILE - LEAD;
+    window_fill<T, WL>(win, x, max<int64_t>(wlo, 0), min<int64_t>(wlo + WL, n));
+    __syncthreads();
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t whi = wlo + WL;
+        // the next tile's window gains [whi, whi + TILE): H elements per thread
+        T pre[H];
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            const int64_t q = whi + tid + 1024 * h;
+            pre[h] = (t + 1 < t1 && q < n) ? x[q] : T(0);
+        }
+        const int wl = (int)wlo;
+        int L[H];
+        int64_t row[H];
+        int Lmax = 0;
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            row[h] = t * TILE + tid + 1024 * h;
+            L[h] = row[h] < n ? len[row[h]] : 0;
+            Lmax = max(Lmax, L[h]);
+        }
+        T sum[H][2] = {};
+        for (int j = 0; j < Lmax; j += B) {
+            // a full round without per-entry branches: slots past a row's
+            // end (up to the format width) hold column 0 / value 0 and are
+            // read but masked out of the sum
+            T vv[H][B];
+            int cc[H][B];
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                const int64_t i = row[h] < n ? row[h] : 0;
+                const int64_t base = (i / bh) * bstride + i % bh;
+#pragma unroll
+                for (int u = 0; u < B; ++u) {
+                    const int64_t jj = min(j + u, width - 1);
+                    vv[h][u] = ld_nt(val + base + jj * bh);
+                    cc[h][u] = ld_nt(col + base + jj * bh);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+#pragma unroll
+                for (int u = 0; u < B; ++u) {
+                    const bool in = j + u < L[h];
+                    // the slot read is always in range; global memory only
+                    // for entries outside the window
+                    T xv = win[cc[h][u] % WL];
+                    if (in && (uint32_t)(cc[h][u] - wl) >= (uint32_t)WL) xv = x[cc[h][u]];
+                    sum[h][u & 1] += in ? vv[h][u] * xv : T(0);
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+            if (row[h] < n) y[row[h]] = axpby(sum[h][0] + sum[h][1], alpha, beta, y + row[h]);
+        if (t + 1 >= t1) break;
+        lds_barrier();  // tile t is done with the slots reused now
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            const int64_t q = whi + tid + 1024 * h;
+            if (q < n) win[q % WL] = pre[h];
+        }
+        lds_barrier();
+        wlo += TILE;
+    }
+}
+
+template <typename T>
+static hipError_t run_ell_win(const EllView& a, void* y, const void* x, double alpha,
+                              double beta, hipStream_t stream) {
+    const int64_t ntiles = ((int64_t)a.n + kEllWinTile - 1) / kEllWinTile;
+    const int64_t g = std::min<int64_t>(ntiles, kWinGroups);
+    hipLaunchKernelGGL(k_ell_win<T>, dim3((unsigned)g), dim3(1024), 0, stream, a.n, a.bh,
+                       a.bstride, a.width, a.len, a.col, (const T*)a.val, (const T*)x, (T*)y, (T)alpha,
+                       (T)beta, ntiles);
+    return hipGetLastError();
 }
 
 hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double alpha,
                       double beta, hipStream_t stream) {
     const int64_t blocks = ((int64_t)a.n + 255) / 256;
     if (blocks == 0) return hipSuccess;
+    if (a.window)
+        return f64 ? run_ell_win<double>(a, y, x, alpha, beta, stream)
+                   : run_ell_win<float>(a, y, x, alpha, beta, stream);
     if (f64)
         hipLaunchKernelGGL(k_ell<double>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
-                           a.stride, a.len, a.col, (const double*)a.val, (const double*)x,
+                           a.bh, a.bstride, a.len, a.col, (const double*)a.val, (const double*)x,
                            (double*)y, alpha, beta);
     else
         hipLaunchKernelGGL(k_ell<float>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
-                           a.stride, a.len, a.col, (const float*)a.val, (const float*)x,
+                           a.bh, a.bstride, a.len, a.col, (const float*)a.val, (const float*)x,
                            (float*)y, (float)alpha, (float)beta);
     return hipGetLastError();
 }

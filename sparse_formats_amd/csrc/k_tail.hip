@@ -7,24 +7,32 @@
 // separate launch and combines partial results with atomic +=.  Here the
 // tail entries, ordered by row, are cut into chunks of 64 * E consecutive
 // entries, one chunk per wave and E consecutive entries per lane:
-//   1. each lane walks its E entries in order, finishing every row segment
-//      that starts and ends inside its run with a plain y += alpha * sum
-//      (no other lane or wave touches that row's tail);
+//   1. each lane walks its E entries in order and adds every row segment
+//      that starts and ends inside its run straight into y;
 //   2. the lane's first and last segments may continue in neighbouring
 //      lanes: a segmented inclusive scan over the lanes (keyed by row, which
 //      is non-decreasing along the chunk) sums them, and the lane that
-//      closes a row inside the wave writes it;
-//   3. only the chunk's first and last rows can be shared with other waves;
-//      they are added with device-scope atomics, every other row with a
-//      plain read-modify-write.
-// HYB reads the row of every entry; HEC finds rows by binary search in its
-// row pointer, starting from the row of each chunk's first entry (computed
-// once when the format is built).
+//      closes a row inside the wave adds it;
+//   3. every addition into y is a device-scope atomic without return value,
+//      so no lane ever waits for y (a plain read-modify-write would stall
+//      the wave on the load), and rows shared by neighbouring waves need no
+//      special case.
+// HYB reads the row of every entry.  HEC finds rows in its row pointer:
+// each lane binary-searches the row of its first entry between the rows of
+// its chunk's first and last entries (computed once when the format is
+// built), then reads the next eight row starts at once and places its
+// entries among them, searching again only if its run crosses more rows.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
 namespace spmv {
 
+// Each lane reads its run with 16-byte loads at a 64-byte lane stride, so one
+// load instruction touches every line of the wave's chunk partially and the
+// next three complete them: these loads must allocate in the caches (no
+// nontemporal hint), or each line is fetched from L2 four times.
 typedef double d2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef int i4_t __attribute__((ext_vector_type(4)));
@@ -34,7 +42,7 @@ __device__ __forceinline__ void load_run(const double* p, double (&v)[E]) {
     const d2_t* q = reinterpret_cast<const d2_t*>(p);
 #pragma unroll
     for (int k = 0; k < E / 2; ++k) {
-        const d2_t t = ld_nt(q + k);
+        const d2_t t = q[k];
         v[2 * k] = t.x;
         v[2 * k + 1] = t.y;
     }
@@ -45,7 +53,7 @@ __device__ __forceinline__ void load_run(const float* p, float (&v)[E]) {
     const f4_t* q = reinterpret_cast<const f4_t*>(p);
 #pragma unroll
     for (int k = 0; k < E / 4; ++k) {
-        const f4_t t = ld_nt(q + k);
+        const f4_t t = q[k];
         v[4 * k] = t.x;
         v[4 * k + 1] = t.y;
         v[4 * k + 2] = t.z;
@@ -58,7 +66,7 @@ __device__ __forceinline__ void load_run(const int* p, int (&v)[E]) {
     const i4_t* q = reinterpret_cast<const i4_t*>(p);
 #pragma unroll
     for (int k = 0; k < E / 4; ++k) {
-        const i4_t t = ld_nt(q + k);
+        const i4_t t = q[k];
         v[4 * k] = t.x;
         v[4 * k + 1] = t.y;
         v[4 * k + 2] = t.z;
@@ -79,65 +87,115 @@ __device__ __forceinline__ int row_of(const int* __restrict__ ptr, int lo, int h
     return lo;
 }
 
+// Registers of one lane's run: values, columns and (HYB) rows.
 template <typename T>
-__device__ __forceinline__ void add_row(T* y, int row, T v, bool shared) {
-    if (shared)
-        atomic_add(y + row, v);
-    else
-        y[row] += v;
-}
+struct TailRun {
+    T v[kTailPerLane];
+    int c[kTailPerLane];
+    int r[kTailPerLane];
+    int cnt;  // entries of this lane (0 for lanes past the end)
+};
 
+// Issue the loads of one wave's chunk of 64 * E tail entries (chunk index w).
 template <typename T, bool kCoo>
-__global__ __launch_bounds__(256) void k_tail(int n, int64_t nnz, const int* __restrict__ trow,
-                                              const int* __restrict__ tptr,
-                                              const int* __restrict__ chunk_row,
-                                              const int* __restrict__ col,
-                                              const T* __restrict__ val,
-                                              const T* __restrict__ x, T* __restrict__ y,
-                                              T alpha) {
+__device__ __forceinline__ void tail_fetch(int64_t w, int lane, int64_t nnz,
+                                           const int* __restrict__ trow,
+                                           const int* __restrict__ col,
+                                           const T* __restrict__ val, TailRun<T>& R) {
     constexpr int E = kTailPerLane;
     constexpr int kNone = 0x7fffffff;
-    const int64_t w = xcd_tile(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
-    const int64_t c0 = w * kTailChunk;
-    if (c0 >= nnz) return;  // the whole wave leaves together
-    const int lane = threadIdx.x & 63;
-    const int64_t e0 = c0 + (int64_t)lane * E;
-    const int cnt = e0 < nnz ? (int)min<int64_t>(E, nnz - e0) : 0;
-
-    T v[E];
-    int c[E];
-    int r[E];
-    if (cnt == E) {
-        load_run<E>(val + e0, v);
-        load_run<E>(col + e0, c);
-        if constexpr (kCoo) load_run<E>(trow + e0, r);
+    const int64_t e0 = w * kTailChunk + (int64_t)lane * E;
+    R.cnt = e0 < nnz ? (int)min<int64_t>(E, nnz - e0) : 0;
+    if (R.cnt == E) {
+        load_run<E>(val + e0, R.v);
+        load_run<E>(col + e0, R.c);
+        if constexpr (kCoo) load_run<E>(trow + e0, R.r);
     } else {
 #pragma unroll
         for (int k = 0; k < E; ++k) {
-            v[k] = k < cnt ? val[e0 + k] : T(0);
-            c[k] = k < cnt ? col[e0 + k] : 0;
-            if constexpr (kCoo) r[k] = k < cnt ? trow[e0 + k] : kNone;
+            R.v[k] = k < R.cnt ? val[e0 + k] : T(0);
+            R.c[k] = k < R.cnt ? col[e0 + k] : 0;
+            if constexpr (kCoo) R.r[k] = k < R.cnt ? trow[e0 + k] : kNone;
         }
     }
+}
+
+// Finish the chunk: rows (HEC), products, segmented sums and additions into
+// y.  With kWin, x entries inside [wlo, wlo + WinLen) come from the LDS
+// window `win` (element q at slot q mod WinLen), the rest from global memory.
+// Window path: issue the global loads of the x entries outside the window
+// (xg, flagged in far).  They must go out before the next chunk's loads:
+// loads complete in order, so waiting on them would drain that prefetch.
+template <typename T>
+__device__ __forceinline__ void tail_far_gather(const T* __restrict__ x, int64_t wlo,
+                                                const TailRun<T>& R, bool (&far)[kTailPerLane],
+                                                T (&xg)[kTailPerLane]) {
+#pragma unroll
+    for (int k = 0; k < kTailPerLane; ++k) {
+        far[k] = k < R.cnt && (uint32_t)(R.c[k] - (int)wlo) >= (uint32_t)WinLen<T>::value;
+        xg[k] = far[k] ? x[R.c[k]] : T(0);
+    }
+}
+
+template <typename T, bool kCoo, bool kWin>
+__device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
+                                            const int* __restrict__ tptr,
+                                            const int* __restrict__ chunk_row,
+                                            const T* __restrict__ x, T* __restrict__ y, T alpha,
+                                            const T* win, const bool (&far)[kTailPerLane],
+                                            const T (&xg)[kTailPerLane], TailRun<T>& R) {
+    constexpr int E = kTailPerLane;
+    constexpr int kNone = 0x7fffffff;
+    if (w * kTailChunk >= nnz) return;  // the whole wave leaves together
+    const int64_t e0 = w * kTailChunk + (int64_t)lane * E;
+    const int cnt = R.cnt;
+    int* r = R.r;
     if constexpr (!kCoo) {
         const int lo = chunk_row[w], hi = chunk_row[w + 1];
         int cur = cnt > 0 ? row_of(tptr, lo, hi, e0) : kNone;
-        int next_start = cnt > 0 ? tptr[cur + 1] : 0;
+        const int base = cnt > 0 ? cur : lo;  // inactive lanes read in-range rows
+        // starts of the next E rows (clamped to the chunk's last row)
+        int nxt[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) nxt[j] = tptr[min(base + 1 + j, hi + 1)];
 #pragma unroll
         for (int k = 0; k < E; ++k) {
-            if (k < cnt && e0 + k >= next_start) {
-                cur = row_of(tptr, cur + 1, hi, e0 + k);
-                next_start = tptr[cur + 1];
+            int adv = 0;
+#pragma unroll
+            for (int j = 0; j < E; ++j) adv += nxt[j] <= e0 + k;
+            r[k] = k < cnt ? cur + adv : kNone;
+        }
+        // a run crossing more than E row starts (rows with no tail entries
+        // in between): place the remaining entries by binary search
+        if (cnt > 0 && nxt[E - 1] <= e0 + cnt - 1) {
+            int c2 = cur + E;
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                if (k < cnt && e0 + k >= nxt[E - 1]) {
+                    if (e0 + k >= tptr[c2 + 1]) c2 = row_of(tptr, c2 + 1, hi, e0 + k);
+                    r[k] = c2;
+                }
             }
-            r[k] = k < cnt ? cur : kNone;
         }
     }
     T p[E];
 #pragma unroll
-    for (int k = 0; k < E; ++k) p[k] = k < cnt ? v[k] * x[c[k]] : T(0);
+    for (int k = 0; k < E; ++k) {
+        T xv = T(0);
+        if (k < cnt) {
+            if constexpr (kWin) {
+                // the slot read is always in range
+                const T xw = win[R.c[k] % WinLen<T>::value];
+                xv = far[k] ? xg[k] : xw;
+            } else {
+                xv = x[R.c[k]];
+            }
+        }
+        p[k] = R.v[k] * xv;
+    }
 
-    // 1. walk the run; rows that start and end inside it are exclusive
-    int head_row = r[0];
+    // 1. walk the run; rows that start and end inside it are added directly
+    const int head_row = r[0];
     T head_sum = 0;
     bool split = false;
     int cur = r[0];
@@ -150,7 +208,7 @@ __global__ __launch_bounds__(256) void k_tail(int n, int64_t nnz, const int* __r
                     head_sum = acc;
                     split = true;
                 } else {
-                    y[cur] += alpha * acc;
+                    atomic_add(y + cur, alpha * acc);
                 }
                 cur = r[k];
                 acc = 0;
@@ -168,20 +226,89 @@ __global__ __launch_bounds__(256) void k_tail(int n, int64_t nnz, const int* __r
         const T s2 = __shfl_up(sum, d);
         if (lane >= d && k2 == key) sum += s2;
     }
-    const int first_row = __shfl(head_row, 0);
-    const int last_lane = (int)min<int64_t>(63, (nnz - c0 - 1) / E);
-    const int last_row = __shfl(key, last_lane);
     const int prev_key = __shfl_up(key, 1);
     const T prev_sum = __shfl_up(sum, 1);
     const int next_first = __shfl_down(head_row, 1);
 
-    // 3. write what closes here
+    // 3. add what closes here
     if (split) {
         const T tot = head_sum + ((lane > 0 && prev_key == head_row) ? prev_sum : T(0));
-        add_row(y, head_row, alpha * tot, head_row == first_row);
+        atomic_add(y + head_row, alpha * tot);
     }
-    if (cnt > 0 && (lane == 63 || next_first != key))
-        add_row(y, key, alpha * sum, key == first_row || key == last_row);
+    if (cnt > 0 && (lane == 63 || next_first != key)) atomic_add(y + key, alpha * sum);
+}
+
+template <typename T, bool kCoo>
+__global__ __launch_bounds__(256) void k_tail(int n, int64_t nnz, const int* __restrict__ trow,
+                                              const int* __restrict__ tptr,
+                                              const int* __restrict__ chunk_row,
+                                              const int* __restrict__ col,
+                                              const T* __restrict__ val,
+                                              const T* __restrict__ x, T* __restrict__ y,
+                                              T alpha) {
+    const int64_t w = xcd_tile(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+    if (w * kTailChunk >= nnz) return;
+    TailRun<T> R;
+    tail_fetch<T, kCoo>(w, threadIdx.x & 63, nnz, trow, col, val, R);
+    bool far[kTailPerLane] = {};
+    T xg[kTailPerLane] = {};
+    tail_finish<T, kCoo, false>(w, threadIdx.x & 63, nnz, tptr, chunk_row, x, y, alpha, nullptr,
+                                far, xg, R);
+}
+
+// Tail with x staged in LDS.  Workgroup g (16 waves) runs a contiguous
+// share of the steps; a step is kTailStepChunks consecutive wave
+// chunks (kTailChunksPerWave per wave) and its window starts WinLead rows
+// before the step's first row.  Only the x elements entering the window are
+// loaded (rows only move forward, so each element is loaded about once per
+// workgroup).  Inside a step each wave runs its chunks back to back with the
+// next chunk's loads in flight while the current one is summed, so the
+// barriers that move the window are paid once per kTailChunksPerWave chunks.
+template <typename T, bool kCoo>
+__global__ __launch_bounds__(1024) void k_tail_win(int n, int64_t nnz,
+                                                   const int* __restrict__ trow,
+                                                   const int* __restrict__ tptr,
+                                                   const int* __restrict__ chunk_row,
+                                                   const int* __restrict__ col,
+                                                   const T* __restrict__ val,
+                                                   const T* __restrict__ x, T* __restrict__ y,
+                                                   T alpha, int64_t nsteps) {
+    constexpr int WL = WinLen<T>::value;
+    constexpr int LEAD = WinLead<T>::value;
+    constexpr int CPW = kTailChunksPerWave;
+    __shared__ T win[WL];
+    const int64_t g = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t s0 = g * nsteps / gridDim.x, s1 = (g + 1) * nsteps / gridDim.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t prev_whi = -1;
+    for (int64_t s = s0; s < s1; ++s) {
+        const int64_t r_first = kCoo ? trow[s * (int64_t)kTailStepChunks * kTailChunk]
+                                     : chunk_row[s * kTailStepChunks];
+        const int64_t wlo = r_first - LEAD, whi = wlo + WL;
+        lds_barrier();  // the previous step is done with the slots reused now
+        const int64_t from = max<int64_t>(max<int64_t>(prev_whi, wlo), 0);
+        const int64_t to = min<int64_t>(whi, n);
+        if (to - from > 2048) {
+            window_fill<T, WL>(win, x, from, to);
+        } else {
+            for (int64_t q = from + threadIdx.x; q < to; q += 1024) win[q % WL] = x[q];
+        }
+        lds_barrier();
+        prev_whi = whi;
+        const int64_t w0 = s * kTailStepChunks + (int64_t)wave * CPW;
+        TailRun<T> run[2];
+        tail_fetch<T, kCoo>(w0, lane, nnz, trow, col, val, run[0]);
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            bool far[kTailPerLane];
+            T xg[kTailPerLane];
+            tail_far_gather<T>(x, wlo, run[k & 1], far, xg);
+            if (k + 1 < CPW)
+                tail_fetch<T, kCoo>(w0 + k + 1, lane, nnz, trow, col, val, run[(k + 1) & 1]);
+            tail_finish<T, kCoo, true>(w0 + k, lane, nnz, tptr, chunk_row, x, y, alpha, win, far,
+                                       xg, run[k & 1]);
+        }
+    }
 }
 
 template <typename T>
@@ -189,6 +316,19 @@ static hipError_t run(const TailView& t, void* y, const void* x, double alpha,
                       hipStream_t stream) {
     if (t.nnz == 0) return hipSuccess;
     const int64_t waves = (t.nnz + kTailChunk - 1) / kTailChunk;
+    if (t.window) {
+        const int64_t nsteps = (waves + kTailStepChunks - 1) / kTailStepChunks;
+        const int64_t g = std::min<int64_t>(nsteps, kWinGroups);
+        if (t.row)
+            hipLaunchKernelGGL((k_tail_win<T, true>), dim3((unsigned)g), dim3(1024), 0, stream, t.n,
+                               t.nnz, t.row, t.ptr, t.chunk_row, t.col, (const T*)t.val,
+                               (const T*)x, (T*)y, (T)alpha, nsteps);
+        else
+            hipLaunchKernelGGL((k_tail_win<T, false>), dim3((unsigned)g), dim3(1024), 0, stream,
+                               t.n, t.nnz, t.row, t.ptr, t.chunk_row, t.col, (const T*)t.val,
+                               (const T*)x, (T*)y, (T)alpha, nsteps);
+        return hipGetLastError();
+    }
     const int64_t blocks = (waves + 3) / 4;
     if (t.row)
         hipLaunchKernelGGL((k_tail<T, true>), dim3((unsigned)blocks), dim3(256), 0, stream, t.n,

@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_header_compiles_as_c(tmp_path):
     c = tmp_path / "t.c"
-    c.write_text('#include "spmv_amd.h"\nint main(void){spmv_convert_opts o={-1,0,0};'
+    c.write_text('#include "spmv_amd.h"\nint main(void){spmv_convert_opts o={-1,0,-1,0,0};'
                  'spmv_info_t i; (void)o; (void)i; return SPMV_OK;}\n')
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
                         "-c", str(c), "-o", str(tmp_path / "t.o")], capture_output=True, text=True)

@@ -126,7 +126,8 @@ def test_layouts_bit_exact(name, dtype):
             M.convert(fmt, ell_width=req)
             K = oracle.hyb_width(a, req)
             assert M.info()["ell_width"] == K
-            oc, ov, ol = oracle.ell(a, K)
+            assert M.info()["ell_stride"] == oracle.ELL_BLOCK_SPLIT
+            oc, ov, ol = oracle.ell(a, K, block=oracle.ELL_BLOCK_SPLIT)
             assert np.array_equal(M.export("ell_col"), oc)
             assert M.export("ell_val").tobytes() == ov.tobytes()
             assert np.array_equal(M.export("ell_len"), ol)
@@ -294,3 +295,60 @@ def test_apply_on_side_stream():
         M.apply(y, x)
     s.synchronize()
     check(a, x_np, None, 1.0, 0.0, y.cpu().numpy(), torch.float64)
+
+
+def _banded():
+    # banded rows (|col - row| up to 12,000: partly beyond the LDS window),
+    # a few long rows and 5% far columns; enough rows and entries that the
+    # persistent window kernels slide over several tiles / steps
+    return gen_c5(n=1_200_000, lo=3, hi=12, frac_long=0.0005, long_len=3000, band=12_000,
+                  seed=47)
+
+
+from gen import c5_fem as gen_c5  # noqa: E402
+
+WINDOW_MATS = dict(MATS, banded=_banded)
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("name", ["c1", "ragged", "every_len", "long_spans", "box27", "nnz0",
+                                  "n1", "banded"])
+@pytest.mark.parametrize("fmt", ["ellr", "hyb", "hec"])
+@pytest.mark.parametrize("win", [1, 0])
+def test_x_window_forced(fmt, name, dtype, win):
+    a = WINDOW_MATS[name]()
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    x_np, y0_np = vectors(a.n, 16)
+    x_np, y0_np = x_np.astype(npdt), y0_np.astype(npdt)
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n)
+    kws = [dict()]
+    if fmt != "ellr":
+        kws.append(dict(ell_width=0))   # whole matrix in the tail
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    for kw in kws:
+        if fmt == "ellr" and name == "banded":
+            kw = dict(footprint_budget=1 << 40)
+        M.convert(fmt, x_window=win, **kw)
+        assert M.info()["x_window"] == win
+        for alpha, beta in AB[:2]:
+            y = apply(M, x, y0, alpha, beta)
+            rows = None if a.n < 100_000 else np.unique(np.concatenate(
+                [np.arange(0, a.n, 97), np.argsort(a.row_lengths())[-200:]]))
+            check(a, x_np, y0_np, alpha, beta, y, dtype, rows=rows,
+                  what="%s win=%d %s %s" % (fmt, win, kw, name))
+    M.close()
+
+
+def test_x_window_auto_choice():
+    a = _banded()
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("hec")
+    i = M.info()
+    assert i["x_window"] == 1 and 0.7 < i["band_fraction"] < 0.9
+    b = MATS["ragged"]()
+    M2 = sf.Matrix.from_csr(*to_dev(b), n=b.n).convert("hyb")
+    assert M2.info()["x_window"] == (1 if M2.info()["band_fraction"] >= 0.5 else 0)
+    with pytest.raises(sf.SpmvError):
+        M2.convert("hyb", x_window=2)

@@ -36,11 +36,12 @@ def one_full_row(N, full=0):
     return CSR(N, rowptr, col, np.arange(1, rowptr[-1] + 1, dtype=np.float64))
 
 
-def ell_to_csr(n, oc, ov, ol):
-    S = oracle.pad64(n)
+def ell_to_csr(n, oc, ov, ol, block=0):
+    B = oracle.pad64(n) if block <= 0 else block
+    W = oc.size // max(ol.size, 1)
     rows_c, rows_v = [], []
     for i in range(n):
-        idx = np.arange(ol[i]) * S + i
+        idx = (i // B) * W * B + np.arange(ol[i]) * B + i % B
         rows_c.append(oc[idx])
         rows_v.append(ov[idx])
     return rows_c, rows_v
@@ -132,6 +133,17 @@ def test_ell_round_trip(name, mk):
     assert ov[~used].tobytes() == np.zeros((~used).sum(), ov.dtype).tobytes()
 
 
+def test_blocked_ell_layout_small():
+    """Blocks of B rows, each column-major: hand-placed 5-row example, B = 2."""
+    a = CSR(5, np.array([0, 2, 3, 3, 6, 7], np.int64), np.array([4, 1, 0, 2, 3, 4, 1], np.int32),
+            np.arange(1.0, 8.0))
+    oc, ov, ol = oracle.ell(a, 3, block=2)
+    # padded rows R = 6, width 3: block k holds rows 2k, 2k+1, slot j*2 + r
+    assert list(ol) == [2, 1, 0, 3, 1, 0]
+    assert list(ov) == [1, 3, 2, 0, 0, 0,  0, 4, 0, 5, 0, 6,  7, 0, 0, 0, 0, 0]
+    assert list(oc) == [4, 0, 1, 0, 0, 0,  0, 2, 0, 3, 0, 4,  1, 0, 0, 0, 0, 0]
+
+
 @pytest.mark.parametrize("name,mk", MATS)
 def test_sell_round_trip(name, mk):
     a = mk()
@@ -174,14 +186,16 @@ def test_split_round_trip(name, mk, K):
     """ELL part (width K) + tail (COO and CSR) rebuild the input exactly."""
     a = mk()
     K = oracle.hyb_width(a) if K is None else oracle.hyb_width(a, K)
-    oc, ov, ol = oracle.ell(a, K)
+    B = oracle.ELL_BLOCK_SPLIT
+    oc, ov, ol = oracle.ell(a, K, block=B)
     L = a.row_lengths()
-    assert np.array_equal(ol[:a.n], np.minimum(L, K))
+    assert ol.size == -(-a.n // B) * B and oc.size == K * ol.size
+    assert np.array_equal(ol[:a.n], np.minimum(L, K)) and np.all(ol[a.n:] == 0)
     trow, tptr, tcol, tval = oracle.tail(a, K)
     assert trow.size == int(np.maximum(L - K, 0).sum())
     assert np.array_equal(np.diff(tptr), np.maximum(L - K, 0))
     assert np.all(np.diff(trow) >= 0)
-    ec, ev = ell_to_csr(a.n, oc, ov, ol)
+    ec, ev = ell_to_csr(a.n, oc, ov, ol, block=B)
     rows_c, rows_v = [], []
     for i in range(a.n):
         sel = slice(tptr[i], tptr[i + 1])
