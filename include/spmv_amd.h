@@ -90,10 +90,12 @@ typedef struct {
      * a value >= 0 is used as given, clamped to the longest row. */
     int32_t ell_width;
     /* CSR: lanes cooperating on one row, a power of two in 1..64.  0 times
-     * every candidate on the device during the conversion and keeps the
-     * fastest.  (The subwarp rule of "Sparse Linear Algebra on AMD and
-     * NVIDIA GPUs -- The Race Is On" -- threads per row follow the maximum
-     * row length -- is the value spmv_create starts with.) */
+     * every candidate (and 1 or 4 consecutive rows per lane group) on the
+     * device during the conversion and keeps the fastest; a fixed value
+     * only chooses the rows per group.  (The subwarp rule of "Sparse Linear
+     * Algebra on AMD and NVIDIA GPUs -- The Race Is On" -- threads per row
+     * follow the maximum row length -- is the value spmv_create starts
+     * with.) */
     int32_t subwave;
     /* ELL-R / HYB / HEC: stage x in LDS.  The workgroup keeps the x entries
      * within about +-9,700 (fp64) or +-19,900 (fp32) positions of its rows
@@ -103,7 +105,8 @@ typedef struct {
      * the entries fall inside the window, and for ELL-R only when the
      * longest row has at most 128 entries), 0 off, 1 on. */
     int32_t x_window;
-    int32_t reserved;      /* must be 0 */
+    /* CSR: consecutive rows per lane group, 0 (choose by timing), 1 or 4 */
+    int32_t csr_rows;
     /* Largest device footprint a padded format (ELL-R) may take, in bytes;
      * 0 means 75% of the device's memory. */
     uint64_t footprint_budget_bytes;
@@ -126,7 +129,7 @@ typedef struct {
     int32_t nslices;       /* SELL-64: slices */
     uint64_t footprint_bytes; /* device bytes held by the handle */
     int32_t x_window;      /* 1 when the active format stages x in LDS */
-    int32_t reserved;
+    int32_t csr_rows;      /* CSR: consecutive rows per lane group (1 or 4) */
     double band_fraction;  /* share of entries within the window's reach
                               (computed by ELL-R / HYB / HEC conversions) */
     int64_t ell_rows;      /* ELL-R / HYB / HEC: rows padded to whole blocks */

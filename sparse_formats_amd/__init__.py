@@ -48,7 +48,7 @@ class SpmvError(RuntimeError):
 
 class _ConvertOpts(ctypes.Structure):
     _fields_ = [("ell_width", ctypes.c_int32), ("subwave", ctypes.c_int32),
-                ("x_window", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("x_window", ctypes.c_int32), ("csr_rows", ctypes.c_int32),
                 ("footprint_budget_bytes", ctypes.c_uint64)]
 
 
@@ -59,7 +59,7 @@ class _Info(ctypes.Structure):
                 ("ell_stride", ctypes.c_int64), ("slots", ctypes.c_int64),
                 ("subwave", ctypes.c_int32), ("nslices", ctypes.c_int32),
                 ("footprint_bytes", ctypes.c_uint64), ("x_window", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("band_fraction", ctypes.c_double),
+                ("csr_rows", ctypes.c_int32), ("band_fraction", ctypes.c_double),
                 ("ell_rows", ctypes.c_int64)]
 
 
@@ -157,11 +157,12 @@ class Matrix:
         return cls(h, int(n), nnz, val.dtype)
 
     def convert(self, fmt: str, ell_width: int = -1, subwave: int = 0, x_window: int = -1,
-                footprint_budget: int = 0) -> "Matrix":
+                footprint_budget: int = 0, csr_rows: int = 0) -> "Matrix":
         """Build `fmt` on the device and make it active (options as in spmv_convert_opts)."""
         if fmt not in FORMATS:
             raise ValueError("unknown format %r (one of %s)" % (fmt, ", ".join(FORMATS)))
-        o = _ConvertOpts(int(ell_width), int(subwave), int(x_window), 0, int(footprint_budget))
+        o = _ConvertOpts(int(ell_width), int(subwave), int(x_window), int(csr_rows),
+                         int(footprint_budget))
         _check(_lib.spmv_convert(self._h, FORMATS[fmt], ctypes.byref(o)))
         return self
 

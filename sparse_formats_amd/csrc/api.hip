@@ -124,6 +124,7 @@ struct spmv_handle {
     size_t vsize = 8;
     int max_len = 0;
     int subwave = 1;
+    int csr_rows = 1;     // rows per lane group of the CSR kernel
     DevBuf rowptr, col, val;  // canonical CSR (int32 row pointer)
     Built fmt;                // active non-CSR format (format == CSR: none)
     int format = SPMV_CSR;
@@ -205,13 +206,20 @@ __global__ void k_rowptr_from_sorted(int64_t n, int64_t nnz, const unsigned* __r
     }
 }
 
-__global__ void k_max_len(int64_t n, const int* __restrict__ rowptr, int* out) {
+__global__ __launch_bounds__(256) void k_max_len(int64_t n, const int* __restrict__ rowptr,
+                                                 int* out) {
+    __shared__ int wmax[4];
     int m = 0;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
         m = max(m, rowptr[i + 1] - rowptr[i]);
-    for (int d = 32; d > 0; d >>= 1) m = max(m, __shfl_xor(m, d));  // one atomic per wave
-    if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m);
+    for (int d = 32; d > 0; d >>= 1) m = max(m, __shfl_xor(m, d));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {  // one atomic per block
+        m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+        if (m) atomicMax(out, m);
+    }
 }
 
 // row-length histogram; short lengths are counted in LDS first because a
@@ -587,12 +595,15 @@ void build_split(const spmv_handle* h, int format, int requested, Built& b, hipS
     sync(s);
 }
 
-// CSR sub-wave: time every candidate group size on the device and keep the
-// fastest (the apply does not depend on the values of x, so zeros are used)
-int tune_subwave(const spmv_handle* h, hipStream_t s) {
+// CSR kernel shape: time every candidate (lanes per row, rows per lane group)
+// on the device and keep the fastest (the apply does not depend on the
+// values of x, so zeros are used).  Fixed values are not tuned.
+void tune_csr(spmv_handle* h, int fixed_subwave, int fixed_rows, hipStream_t s) {
     int rule = 1;  // smallest power of two >= the longest row, at most 64
     while (rule < 64 && rule < h->max_len) rule <<= 1;
-    if (h->n == 0 || h->nnz == 0) return rule;
+    h->subwave = fixed_subwave ? fixed_subwave : rule;
+    h->csr_rows = fixed_rows ? fixed_rows : 1;
+    if (h->n == 0 || h->nnz == 0 || (fixed_subwave && fixed_rows)) return;
     DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
     hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
     hipEvent_t e0, e1;
@@ -600,24 +611,27 @@ int tune_subwave(const spmv_handle* h, hipStream_t s) {
     hip_check(hipEventCreate(&e1), "hipEventCreate");
     const CsrView v{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
     const bool f64 = h->dtype == SPMV_F64;
-    int best = rule;
     float best_ms = 1e30f;
     hipError_t err = hipSuccess;
-    for (int sw = h->max_len <= 2 ? 1 : 2; sw <= 64 && err == hipSuccess; sw <<= 1) {
-        err = launch_csr(v, sw, f64, ys.p, xs.p, 1.0, 0.0, s);
-        if (err == hipSuccess) err = hipEventRecord(e0, s);
-        for (int r = 0; r < 2 && err == hipSuccess; ++r)
-            err = launch_csr(v, sw, f64, ys.p, xs.p, 1.0, 0.0, s);
-        if (err == hipSuccess) err = hipEventRecord(e1, s);
-        if (err == hipSuccess) err = hipEventSynchronize(e1);
-        float ms = 0;
-        if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
-        if (err == hipSuccess && ms < best_ms) best_ms = ms, best = sw;
-    }
+    const int sw_lo = fixed_subwave ? fixed_subwave : (h->max_len <= 2 ? 1 : 2);
+    const int sw_hi = fixed_subwave ? fixed_subwave : 64;
+    for (int sw = sw_lo; sw <= sw_hi && err == hipSuccess; sw <<= 1)
+        for (int rows : {1, kCsrRowsMulti}) {
+            if (err != hipSuccess) break;
+            if (fixed_rows && rows != fixed_rows) continue;
+            err = launch_csr(v, sw, rows, f64, ys.p, xs.p, 1.0, 0.0, s);
+            if (err == hipSuccess) err = hipEventRecord(e0, s);
+            for (int r = 0; r < 2 && err == hipSuccess; ++r)
+                err = launch_csr(v, sw, rows, f64, ys.p, xs.p, 1.0, 0.0, s);
+            if (err == hipSuccess) err = hipEventRecord(e1, s);
+            if (err == hipSuccess) err = hipEventSynchronize(e1);
+            float ms = 0;
+            if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+            if (err == hipSuccess && ms < best_ms) best_ms = ms, h->subwave = sw, h->csr_rows = rows;
+        }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
-    hip_check(err, "sub-wave tuning");
-    return best;
+    hip_check(err, "CSR kernel tuning");
 }
 
 // share of the entries the LDS window reaches, and whether to use it
@@ -758,8 +772,8 @@ int spmv_create(spmv_t* out, int kind, int64_t n, int64_t nnz, const int64_t* ro
             }
             hip_check(hipMemsetAsync(flags.p, 0, 4, s), "hipMemsetAsync");
             if (n > 0) {
-                hipLaunchKernelGGL(k_max_len, dim3(grid_for(n)), dim3(256), 0, s, n,
-                                   h->rowptr.as<int>(), flags.as<int>());
+                hipLaunchKernelGGL(k_max_len, dim3(std::min<unsigned>(grid_for(n), 1024)), dim3(256),
+                                   0, s, n, h->rowptr.as<int>(), flags.as<int>());
                 hip_check(hipGetLastError(), "max length");
             }
             h->max_len = read_scalar<int>(flags.p, s);
@@ -781,14 +795,16 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
         if (!valid_format(format)) fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
         spmv_convert_opts o{-1, 0, -1, 0, 0};
         if (opts) o = *opts;
-        if (o.x_window < -1 || o.x_window > 1 || o.reserved != 0)
-            fail(SPMV_ERR_INVALID_ARG, "x_window must be -1, 0 or 1 and reserved 0");
+        if (o.x_window < -1 || o.x_window > 1)
+            fail(SPMV_ERR_INVALID_ARG, "x_window must be -1, 0 or 1");
+        if (o.csr_rows != 0 && o.csr_rows != 1 && o.csr_rows != kCsrRowsMulti)
+            fail(SPMV_ERR_INVALID_ARG, "csr_rows must be 0, 1 or %d", kCsrRowsMulti);
         if (format == SPMV_CSR) {
-            int sw = o.subwave;
-            if (sw == 0) sw = tune_subwave(h, nullptr);
-            if (sw < 1 || sw > 64 || (sw & (sw - 1)))
-                fail(SPMV_ERR_INVALID_ARG, "subwave must be a power of two in 1..64 (got %d)", sw);
-            h->subwave = sw;
+            const int sw = o.subwave;
+            if (sw < 0 || sw > 64 || (sw & (sw - 1)))
+                fail(SPMV_ERR_INVALID_ARG, "subwave must be 0 or a power of two in 1..64 (got %d)",
+                     sw);
+            tune_csr(h, sw, o.csr_rows, nullptr);
             h->fmt = Built{};
             h->format = SPMV_CSR;
             return;
@@ -851,7 +867,7 @@ int spmv_apply(spmv_t h, void* y, const void* x, double alpha, double beta, void
     switch (h->format) {
         case SPMV_CSR: {
             CsrView a{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
-            e = launch_csr(a, h->subwave, f64, y, x, alpha, beta, s);
+            e = launch_csr(a, h->subwave, h->csr_rows, f64, y, x, alpha, beta, s);
             break;
         }
         case SPMV_ELLR:
@@ -932,6 +948,7 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     }
     i.footprint_bytes = h->rowptr.bytes + h->col.bytes + h->val.bytes + b.bytes();
     i.x_window = b.window ? 1 : 0;
+    i.csr_rows = h->csr_rows;
     i.band_fraction = b.band_fraction;
     *out = i;
     return SPMV_OK;

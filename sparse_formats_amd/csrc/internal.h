@@ -96,8 +96,10 @@ struct TailView {
 };
 
 // kernel launchers (asynchronous on `stream`); fp64 when f64, else fp32
-hipError_t launch_csr(const CsrView& a, int subwave, bool f64, void* y, const void* x,
-                      double alpha, double beta, hipStream_t stream);
+// rows: rows per lane group, 1 or kCsrRowsMulti
+constexpr int kCsrRowsMulti = 4;
+hipError_t launch_csr(const CsrView& a, int subwave, int rows, bool f64, void* y,
+                      const void* x, double alpha, double beta, hipStream_t stream);
 hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double alpha,
                       double beta, hipStream_t stream);
 hipError_t launch_sell(const SellView& a, bool f64, void* y, const void* x, double alpha,

@@ -14,62 +14,97 @@
 
 namespace spmv {
 
-template <typename T, int S>
+// Each group of S lanes handles R consecutive rows.  A lone row costs three
+// dependent memory round trips (row pointer, then val/col, then x), so the
+// group first issues the row pointers, values and columns of all R rows
+// (two entries per lane and row) and only then the x reads and sums; longer
+// rows finish in a plain loop.  The first pass reads with clamped indices
+// and masks the products, so it has no per-entry branches.
+template <typename T, int S, int R>
 __global__ __launch_bounds__(256) void k_csr_vector(int n, const int* __restrict__ rowptr,
                                                     const int* __restrict__ col,
                                                     const T* __restrict__ val,
                                                     const T* __restrict__ x, T* __restrict__ y,
                                                     T alpha, T beta) {
-    constexpr int kRowsPerBlock = 256 / S;
+    constexpr int kGroups = 256 / S;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t row = tile * kRowsPerBlock + threadIdx.x / S;
+    const int64_t row0 = (tile * kGroups + threadIdx.x / S) * R;
     const int sub = threadIdx.x & (S - 1);
-    if (row >= n) return;  // whole groups leave together
-    const int k0 = rowptr[row], k1 = rowptr[row + 1];
-    T s0 = 0, s1 = 0;
-    int k = k0 + sub;
-    // two independent chains keep two loads of val/col in flight per lane
-    for (; k + S < k1; k += 2 * S) {
-        const T v0 = val[k], v1 = val[k + S];
-        const int c0 = col[k], c1 = col[k + S];
-        s0 = fma(v0, x[c0], s0);
-        s1 = fma(v1, x[c1], s1);
+    if (row0 >= n) return;  // whole groups leave together
+    int kb[R + 1];
+#pragma unroll
+    for (int r = 0; r <= R; ++r) kb[r] = rowptr[row0 + r < n ? row0 + r : (int64_t)n];
+    T v[R][2];
+    int c[R][2];
+    bool ok[R][2];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int k = kb[r] + sub + u * S;
+            ok[r][u] = k < kb[r + 1];
+            const int kc = max(min(k, kb[r + 1] - 1), 0);  // in bounds even when masked
+            v[r][u] = val[kc];
+            c[r][u] = col[kc];
+        }
+    T sum[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const T p0 = ok[r][0] ? v[r][0] * x[c[r][0]] : T(0);
+        const T p1 = ok[r][1] ? v[r][1] * x[c[r][1]] : T(0);
+        sum[r] = p0 + p1;
     }
-    if (k < k1) s0 = fma(val[k], x[col[k]], s0);
-    T s = group_sum<S>(s0 + s1);
-    if (sub == 0) y[row] = axpby(s, alpha, beta, y + row);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        for (int k = kb[r] + sub + 2 * S; k < kb[r + 1]; k += S) sum[r] = fma(val[k], x[col[k]], sum[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const T s_r = group_sum<S>(sum[r]);
+        if (sub == 0 && row0 + r < n) y[row0 + r] = axpby(s_r, alpha, beta, y + row0 + r);
+    }
 }
 
-template <typename T, int S>
+template <typename T, int S, int R>
 static hipError_t run(const CsrView& a, void* y, const void* x, double alpha, double beta,
                       hipStream_t stream) {
-    constexpr int kRowsPerBlock = 256 / S;
+    constexpr int kRowsPerBlock = 256 / S * R;
     const int64_t blocks = ((int64_t)a.n + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_csr_vector<T, S>), dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
-                       a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, (T)alpha, (T)beta);
+    hipLaunchKernelGGL((k_csr_vector<T, S, R>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       a.n, a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, (T)alpha,
+                       (T)beta);
     return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t dispatch(const CsrView& a, int subwave, void* y, const void* x, double alpha,
-                           double beta, hipStream_t stream) {
+template <typename T, int R>
+static hipError_t dispatch_s(const CsrView& a, int subwave, void* y, const void* x, double alpha,
+                             double beta, hipStream_t stream) {
     switch (subwave) {
-        case 1: return run<T, 1>(a, y, x, alpha, beta, stream);
-        case 2: return run<T, 2>(a, y, x, alpha, beta, stream);
-        case 4: return run<T, 4>(a, y, x, alpha, beta, stream);
-        case 8: return run<T, 8>(a, y, x, alpha, beta, stream);
-        case 16: return run<T, 16>(a, y, x, alpha, beta, stream);
-        case 32: return run<T, 32>(a, y, x, alpha, beta, stream);
-        case 64: return run<T, 64>(a, y, x, alpha, beta, stream);
+        case 1: return run<T, 1, R>(a, y, x, alpha, beta, stream);
+        case 2: return run<T, 2, R>(a, y, x, alpha, beta, stream);
+        case 4: return run<T, 4, R>(a, y, x, alpha, beta, stream);
+        case 8: return run<T, 8, R>(a, y, x, alpha, beta, stream);
+        case 16: return run<T, 16, R>(a, y, x, alpha, beta, stream);
+        case 32: return run<T, 32, R>(a, y, x, alpha, beta, stream);
+        case 64: return run<T, 64, R>(a, y, x, alpha, beta, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_csr(const CsrView& a, int subwave, bool f64, void* y, const void* x,
-                      double alpha, double beta, hipStream_t stream) {
-    return f64 ? dispatch<double>(a, subwave, y, x, alpha, beta, stream)
-               : dispatch<float>(a, subwave, y, x, alpha, beta, stream);
+template <typename T>
+static hipError_t dispatch(const CsrView& a, int subwave, int rows, void* y, const void* x,
+                           double alpha, double beta, hipStream_t stream) {
+    switch (rows) {
+        case 1: return dispatch_s<T, 1>(a, subwave, y, x, alpha, beta, stream);
+        case 4: return dispatch_s<T, 4>(a, subwave, y, x, alpha, beta, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_csr(const CsrView& a, int subwave, int rows, bool f64, void* y,
+                      const void* x, double alpha, double beta, hipStream_t stream) {
+    return f64 ? dispatch<double>(a, subwave, rows, y, x, alpha, beta, stream)
+               : dispatch<float>(a, subwave, rows, y, x, alpha, beta, stream);
 }
 
 }  // namespace spmv

@@ -74,15 +74,21 @@ def test_split_width_any(fmt, K):
               what="%s K=%d" % (fmt, K))
 
 
+@pytest.mark.parametrize("rows", [1, 4])
 @pytest.mark.parametrize("sw", [1, 2, 4, 8, 16, 32, 64])
-def test_csr_every_subwave(sw):
-    a = MATS["every_len"]()
+@pytest.mark.parametrize("name", ["every_len", "ragged", "nnz0", "n1", "c1"])
+def test_csr_every_shape(sw, rows, name):
+    a = MATS[name]()
     x_np, y0_np = vectors(a.n, 9)
-    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("csr", subwave=sw)
-    assert M.info()["subwave"] == sw
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("csr", subwave=sw, csr_rows=rows)
+    assert M.info()["subwave"] == sw and M.info()["csr_rows"] == rows
     x = torch.from_numpy(x_np).cuda()
     y0 = torch.from_numpy(y0_np).cuda()
-    check(a, x_np, y0_np, 1.5, -0.5, apply(M, x, y0, 1.5, -0.5), torch.float64)
+    for alpha, beta in AB[:2]:
+        check(a, x_np, y0_np, alpha, beta, apply(M, x, y0, alpha, beta), torch.float64,
+              what="csr S=%d R=%d %s" % (sw, rows, name))
+    with pytest.raises(sf.SpmvError):
+        M.convert("csr", csr_rows=3)
 
 
 def test_sell_split_slices():
