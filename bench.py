@@ -47,6 +47,17 @@ KERNELS = {
 }
 
 
+def kernels_of(fmt: str, info: dict) -> str:
+    """The kernels one apply of this handle launches."""
+    if fmt == "csr":
+        if info.get("csr_kernel") == "balanced":
+            return "k_scale + k_tail%s<CSR>" % ("_win" if info["x_window"] else "")
+        return "k_csr_vector<S=%d,R=%d>" % (info["subwave"], info["csr_rows"])
+    if fmt in ("ellr", "hyb", "hec") and info.get("x_window"):
+        return KERNELS[fmt].replace("k_ell", "k_ell_win").replace("k_tail", "k_tail_win")
+    return KERNELS[fmt]
+
+
 def row_info_bytes(fmt: str, n: int, tail_nnz: int = 0) -> int:
     """Bytes of row information an apply must read in each format."""
     if fmt == "csr":
@@ -238,7 +249,7 @@ def main(argv=None):
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "slots": info["slots"], "ell_width": info["ell_width"],
             "tail_nnz": info["tail_nnz"], "setup_ms": round(setup_ms[f], 1),
-            "kernels": KERNELS[f],
+            "kernels": kernels_of(f, info), "x_window": info["x_window"],
         }
     best = max(per, key=lambda f: per[f]["gflops"])
     dom = max(per, key=lambda f: per[f]["ms_median"])
@@ -247,7 +258,7 @@ def main(argv=None):
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_for("%s:%s:%s" % (args.workload, args.dtype, dom)),
-                "kernel": "%s apply (%s)" % (dom, KERNELS[dom]),
+                "kernel": "%s apply (%s)" % (dom, d["kernels"]),
                 "frac_of_stream": d["frac_stream"]}
     flops_step = 2.0 * a.nnz * len(fmts)
     out = {

@@ -26,8 +26,8 @@
  *             ("Development of Krylov...", Sect. 2.1, Fig. 3); the ELL part
  *             is applied first, then the irregular part.  The ELL part of
  *             HYB and HEC is stored column by column in blocks of 1024 rows
- *             (the same page sets the ELL stride to "256 or other multiples"
- *             of the SIMD width rather than to the matrix height).
+ *             (the same page sets the ELL stride to 256 or a multiple of it,
+ *             rather than to the matrix height).
  *
  * Conventions shared by all entry points
  *   - Every array argument is a DEVICE pointer (e.g. a torch tensor's
@@ -68,6 +68,16 @@ typedef enum {
     SPMV_HEC = 4
 } spmv_format;
 
+/* CSR apply kernels (spmv_convert_opts.csr_kernel, spmv_info_t.csr_kernel) */
+typedef enum {
+    SPMV_CSR_AUTO = 0,     /* time both on the device, keep the faster */
+    SPMV_CSR_VECTOR = 1,   /* a group of lanes per row (subwave, csr_rows) */
+    SPMV_CSR_BALANCED = 2  /* the same number of entries per wave, whatever
+                              the row lengths ("Load-balancing Sparse Matrix
+                              Vector Product Kernels on GPUs", abstract: a
+                              CSR kernel for unbalanced matrices) */
+} spmv_csr_kernel;
+
 /* input layout of spmv_create */
 typedef enum { SPMV_IN_CSR = 0, SPMV_IN_COO = 1 } spmv_input;
 
@@ -90,23 +100,29 @@ typedef struct {
      * a value >= 0 is used as given, clamped to the longest row. */
     int32_t ell_width;
     /* CSR: lanes cooperating on one row, a power of two in 1..64.  0 times
-     * every candidate (and 1 or 4 consecutive rows per lane group) on the
-     * device during the conversion and keeps the fastest; a fixed value
-     * only chooses the rows per group.  (The subwarp rule of "Sparse Linear
+     * every candidate (and 1, 2 or 4 rows per lane group) on the device
+     * during the conversion and keeps the fastest; a fixed value only
+     * chooses the rows per group.  (The subwarp rule of "Sparse Linear
      * Algebra on AMD and NVIDIA GPUs -- The Race Is On" -- threads per row
      * follow the maximum row length -- is the value spmv_create starts
      * with.) */
     int32_t subwave;
-    /* ELL-R / HYB / HEC: stage x in LDS.  The workgroup keeps the x entries
-     * within about +-9,700 (fp64) or +-19,900 (fp32) positions of its rows
-     * in a window that slides with the rows (the "banded" structure of FEM
-     * and stencil matrices); entries outside the window are read from
-     * global memory.  -1 decides from the matrix (on when at least half of
+    /* ELL-R / HYB / HEC / balanced CSR: stage x in LDS.  The workgroup
+     * keeps the x entries within about +-9,700 (fp64) or +-19,900 (fp32)
+     * positions of its rows in a window that slides with the rows (the
+     * banded structure of FEM and stencil matrices); entries outside the
+     * window are read from global memory.  -1 decides from the matrix (on when at least half of
      * the entries fall inside the window, and for ELL-R only when the
      * longest row has at most 128 entries), 0 off, 1 on. */
     int32_t x_window;
-    /* CSR: consecutive rows per lane group, 0 (choose by timing), 1 or 4 */
+    /* CSR: rows per lane group, 0 (choose by timing), 1, 2 or 4 */
     int32_t csr_rows;
+    /* CSR: apply kernel, a spmv_csr_kernel.  The balanced kernel cuts the
+     * entries into equal chunks of 512 per wave, sums the row segments of
+     * each chunk with a segmented scan over the lanes and adds rows that
+     * cross chunks with atomics after a pass that writes beta * y.  With
+     * x_window it stages x in LDS like the HEC tail. */
+    int32_t csr_kernel;
     /* Largest device footprint a padded format (ELL-R) may take, in bytes;
      * 0 means 75% of the device's memory. */
     uint64_t footprint_budget_bytes;
@@ -129,7 +145,8 @@ typedef struct {
     int32_t nslices;       /* SELL-64: slices */
     uint64_t footprint_bytes; /* device bytes held by the handle */
     int32_t x_window;      /* 1 when the active format stages x in LDS */
-    int32_t csr_rows;      /* CSR: consecutive rows per lane group (1 or 4) */
+    int32_t csr_rows;      /* CSR: rows per lane group (1, 2 or 4) */
+    int32_t csr_kernel;    /* CSR: SPMV_CSR_VECTOR or SPMV_CSR_BALANCED */
     double band_fraction;  /* share of entries within the window's reach
                               (computed by ELL-R / HYB / HEC conversions) */
     int64_t ell_rows;      /* ELL-R / HYB / HEC: rows padded to whole blocks */

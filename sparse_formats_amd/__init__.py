@@ -19,12 +19,13 @@ import os
 import numpy as np
 import torch
 
-__all__ = ["Matrix", "SpmvError", "FORMATS", "ARRAYS", "stream_copy", "lib_path", "version"]
+__all__ = ["Matrix", "SpmvError", "FORMATS", "CSR_KERNELS", "ARRAYS", "stream_copy", "lib_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspmv_amd.so")
 
 FORMATS = {"csr": 0, "ellr": 1, "sell64": 2, "hyb": 3, "hec": 4}
+CSR_KERNELS = {"auto": 0, "vector": 1, "balanced": 2}
 ARRAYS = {
     "rowptr": (0, np.int32), "col": (1, np.int32), "val": (2, None),
     "ell_col": (3, np.int32), "ell_val": (4, None), "ell_len": (5, np.int32),
@@ -49,7 +50,7 @@ class SpmvError(RuntimeError):
 class _ConvertOpts(ctypes.Structure):
     _fields_ = [("ell_width", ctypes.c_int32), ("subwave", ctypes.c_int32),
                 ("x_window", ctypes.c_int32), ("csr_rows", ctypes.c_int32),
-                ("footprint_budget_bytes", ctypes.c_uint64)]
+                ("csr_kernel", ctypes.c_int32), ("footprint_budget_bytes", ctypes.c_uint64)]
 
 
 class _Info(ctypes.Structure):
@@ -59,7 +60,8 @@ class _Info(ctypes.Structure):
                 ("ell_stride", ctypes.c_int64), ("slots", ctypes.c_int64),
                 ("subwave", ctypes.c_int32), ("nslices", ctypes.c_int32),
                 ("footprint_bytes", ctypes.c_uint64), ("x_window", ctypes.c_int32),
-                ("csr_rows", ctypes.c_int32), ("band_fraction", ctypes.c_double),
+                ("csr_rows", ctypes.c_int32), ("csr_kernel", ctypes.c_int32),
+                ("band_fraction", ctypes.c_double),
                 ("ell_rows", ctypes.c_int64)]
 
 
@@ -157,11 +159,14 @@ class Matrix:
         return cls(h, int(n), nnz, val.dtype)
 
     def convert(self, fmt: str, ell_width: int = -1, subwave: int = 0, x_window: int = -1,
-                footprint_budget: int = 0, csr_rows: int = 0) -> "Matrix":
-        """Build `fmt` on the device and make it active (options as in spmv_convert_opts)."""
+                footprint_budget: int = 0, csr_rows: int = 0,
+                csr_kernel: str = "auto") -> "Matrix":
+        """Build `fmt` on the device and make it active (options as in spmv_convert_opts;
+        csr_kernel is "auto", "vector" or "balanced")."""
         if fmt not in FORMATS:
             raise ValueError("unknown format %r (one of %s)" % (fmt, ", ".join(FORMATS)))
-        o = _ConvertOpts(int(ell_width), int(subwave), int(x_window), int(csr_rows),
+        ck = CSR_KERNELS.get(csr_kernel, csr_kernel)
+        o = _ConvertOpts(int(ell_width), int(subwave), int(x_window), int(csr_rows), int(ck),
                          int(footprint_budget))
         _check(_lib.spmv_convert(self._h, FORMATS[fmt], ctypes.byref(o)))
         return self
@@ -180,6 +185,7 @@ class Matrix:
         _check(_lib.spmv_info(self._h, ctypes.byref(i)))
         d = {k: getattr(i, k) for k, _ in _Info._fields_}
         d["format"] = [k for k, v in FORMATS.items() if v == d["format"]][0]
+        d["csr_kernel"] = [k for k, v in CSR_KERNELS.items() if v == d["csr_kernel"]][0]
         return d
 
     def export(self, name: str) -> np.ndarray:

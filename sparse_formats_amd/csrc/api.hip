@@ -105,6 +105,8 @@ struct Built {
     // tail of HYB / HEC
     int64_t tail_nnz = 0, tail_chunks = 0;
     DevBuf tail_row, tail_ptr, tail_col, tail_val, chunk_row;
+    // CSR: entry-balanced kernel (chunk_row over the whole matrix)
+    bool csr_balanced = false;
     // x staged in LDS by the ELL / tail kernels
     bool window = false;
     double band_fraction = 0;
@@ -595,43 +597,79 @@ void build_split(const spmv_handle* h, int format, int requested, Built& b, hipS
     sync(s);
 }
 
-// CSR kernel shape: time every candidate (lanes per row, rows per lane group)
-// on the device and keep the fastest (the apply does not depend on the
-// values of x, so zeros are used).  Fixed values are not tuned.
-void tune_csr(spmv_handle* h, int fixed_subwave, int fixed_rows, hipStream_t s) {
+void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s);
+
+// CSR kernel: time every shape of the vector kernel (lanes per row, rows
+// per lane group) and the entry-balanced kernel on the device and keep the
+// fastest (the apply does not depend on the values of x, so zeros are used).
+// Fixed values are not tuned.
+void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t s) {
     int rule = 1;  // smallest power of two >= the longest row, at most 64
     while (rule < 64 && rule < h->max_len) rule <<= 1;
-    h->subwave = fixed_subwave ? fixed_subwave : rule;
-    h->csr_rows = fixed_rows ? fixed_rows : 1;
-    if (h->n == 0 || h->nnz == 0 || (fixed_subwave && fixed_rows)) return;
+    h->subwave = o.subwave ? o.subwave : rule;
+    h->csr_rows = o.csr_rows ? o.csr_rows : 1;
+    b.csr_balanced = o.csr_kernel == SPMV_CSR_BALANCED;
+    const bool want_vec = o.csr_kernel != SPMV_CSR_BALANCED;
+    const bool want_bal = o.csr_kernel != SPMV_CSR_VECTOR && h->nnz > 0;
+    if (want_bal) {
+        // row of the first entry of every wave chunk, over the whole matrix
+        b.tail_chunks = (h->nnz + kTailChunk - 1) / kTailChunk;
+        b.chunk_row.alloc((size_t)(b.tail_chunks + 1) * 4);
+        hipLaunchKernelGGL(k_chunk_rows, dim3(grid_for(b.tail_chunks + 1)), dim3(256), 0, s, h->n,
+                           b.tail_chunks, (int64_t)kTailChunk, h->rowptr.as<int>(),
+                           b.chunk_row.as<int>());
+        hip_check(hipGetLastError(), "chunk rows");
+        decide_window(h, SPMV_CSR, o.x_window, b, s);
+    }
+    const bool tune_vec = want_vec && !(o.subwave && o.csr_rows);
+    if (h->n == 0 || h->nnz == 0 || (!tune_vec && !(want_vec && want_bal))) {
+        sync(s);
+        return;
+    }
     DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
     hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
     hipEvent_t e0, e1;
     hip_check(hipEventCreate(&e0), "hipEventCreate");
     hip_check(hipEventCreate(&e1), "hipEventCreate");
     const CsrView v{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
+    const TailView t{(int)h->n, h->nnz, nullptr, h->rowptr.as<int>(), b.chunk_row.as<int>(),
+                     h->col.as<int>(), h->val.p, b.window};
     const bool f64 = h->dtype == SPMV_F64;
     float best_ms = 1e30f;
     hipError_t err = hipSuccess;
-    const int sw_lo = fixed_subwave ? fixed_subwave : (h->max_len <= 2 ? 1 : 2);
-    const int sw_hi = fixed_subwave ? fixed_subwave : 64;
-    for (int sw = sw_lo; sw <= sw_hi && err == hipSuccess; sw <<= 1)
-        for (int rows : {1, kCsrRowsMulti}) {
-            if (err != hipSuccess) break;
-            if (fixed_rows && rows != fixed_rows) continue;
-            err = launch_csr(v, sw, rows, f64, ys.p, xs.p, 1.0, 0.0, s);
-            if (err == hipSuccess) err = hipEventRecord(e0, s);
-            for (int r = 0; r < 2 && err == hipSuccess; ++r)
-                err = launch_csr(v, sw, rows, f64, ys.p, xs.p, 1.0, 0.0, s);
-            if (err == hipSuccess) err = hipEventRecord(e1, s);
-            if (err == hipSuccess) err = hipEventSynchronize(e1);
-            float ms = 0;
-            if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
-            if (err == hipSuccess && ms < best_ms) best_ms = ms, h->subwave = sw, h->csr_rows = rows;
-        }
+    // one candidate: a warm-up launch, then two timed ones
+    auto time_it = [&](auto&& launch) -> float {
+        err = launch();
+        if (err == hipSuccess) err = hipEventRecord(e0, s);
+        for (int r = 0; r < 2 && err == hipSuccess; ++r) err = launch();
+        if (err == hipSuccess) err = hipEventRecord(e1, s);
+        if (err == hipSuccess) err = hipEventSynchronize(e1);
+        float ms = 1e30f;
+        if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+        return ms;
+    };
+    if (want_vec) {
+        const int sw_lo = o.subwave ? o.subwave : (h->max_len <= 2 ? 1 : 2);
+        const int sw_hi = o.subwave ? o.subwave : 64;
+        for (int sw = sw_lo; sw <= sw_hi && err == hipSuccess; sw <<= 1)
+            for (int rows = 1; rows <= kCsrRowsMax && err == hipSuccess; rows <<= 1) {
+                if (o.csr_rows && rows != o.csr_rows) continue;
+                const float ms = time_it(
+                    [&] { return launch_csr(v, sw, rows, f64, ys.p, xs.p, 1.0, 0.0, s); });
+                if (err == hipSuccess && ms < best_ms) best_ms = ms, h->subwave = sw, h->csr_rows = rows;
+            }
+    }
+    if (want_vec && want_bal && err == hipSuccess) {
+        const float ms = time_it([&] {
+            hipError_t e = launch_scale(h->n, f64, ys.p, 0.0, s);
+            return e == hipSuccess ? launch_tail(t, f64, ys.p, xs.p, 1.0, s) : e;
+        });
+        if (err == hipSuccess) b.csr_balanced = ms < best_ms;
+    }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     hip_check(err, "CSR kernel tuning");
+    if (!b.csr_balanced) b.chunk_row.release(), b.window = false, b.tail_chunks = 0;
 }
 
 // share of the entries the LDS window reaches, and whether to use it
@@ -793,19 +831,23 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
     return run_guarded([&] {
         if (!h) fail(SPMV_ERR_STATE, "null handle");
         if (!valid_format(format)) fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
-        spmv_convert_opts o{-1, 0, -1, 0, 0};
+        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, 0};
         if (opts) o = *opts;
         if (o.x_window < -1 || o.x_window > 1)
             fail(SPMV_ERR_INVALID_ARG, "x_window must be -1, 0 or 1");
-        if (o.csr_rows != 0 && o.csr_rows != 1 && o.csr_rows != kCsrRowsMulti)
-            fail(SPMV_ERR_INVALID_ARG, "csr_rows must be 0, 1 or %d", kCsrRowsMulti);
+        if (o.csr_rows < 0 || o.csr_rows > kCsrRowsMax || (o.csr_rows & (o.csr_rows - 1)))
+            fail(SPMV_ERR_INVALID_ARG, "csr_rows must be 0 or a power of two up to %d",
+                 kCsrRowsMax);
         if (format == SPMV_CSR) {
             const int sw = o.subwave;
             if (sw < 0 || sw > 64 || (sw & (sw - 1)))
                 fail(SPMV_ERR_INVALID_ARG, "subwave must be 0 or a power of two in 1..64 (got %d)",
                      sw);
-            tune_csr(h, sw, o.csr_rows, nullptr);
-            h->fmt = Built{};
+            if (o.csr_kernel < SPMV_CSR_AUTO || o.csr_kernel > SPMV_CSR_BALANCED)
+                fail(SPMV_ERR_INVALID_ARG, "csr_kernel must be 0, 1 or 2 (got %d)", o.csr_kernel);
+            Built b;
+            tune_csr(h, o, b, nullptr);
+            h->fmt = std::move(b);
             h->format = SPMV_CSR;
             return;
         }
@@ -866,6 +908,13 @@ int spmv_apply(spmv_t h, void* y, const void* x, double alpha, double beta, void
     hipError_t e = hipSuccess;
     switch (h->format) {
         case SPMV_CSR: {
+            if (b.csr_balanced) {
+                TailView t{(int)h->n, h->nnz, nullptr, h->rowptr.as<int>(), b.chunk_row.as<int>(),
+                           h->col.as<int>(), h->val.p, b.window};
+                e = launch_scale(h->n, f64, y, beta, s);
+                if (e == hipSuccess) e = launch_tail(t, f64, y, x, alpha, s);
+                break;
+            }
             CsrView a{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
             e = launch_csr(a, h->subwave, h->csr_rows, f64, y, x, alpha, beta, s);
             break;
@@ -949,6 +998,7 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.footprint_bytes = h->rowptr.bytes + h->col.bytes + h->val.bytes + b.bytes();
     i.x_window = b.window ? 1 : 0;
     i.csr_rows = h->csr_rows;
+    i.csr_kernel = h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED : SPMV_CSR_VECTOR;
     i.band_fraction = b.band_fraction;
     *out = i;
     return SPMV_OK;

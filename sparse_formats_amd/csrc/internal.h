@@ -96,8 +96,8 @@ struct TailView {
 };
 
 // kernel launchers (asynchronous on `stream`); fp64 when f64, else fp32
-// rows: rows per lane group, 1 or kCsrRowsMulti
-constexpr int kCsrRowsMulti = 4;
+// rows: rows per lane group, a power of two up to kCsrRowsMax
+constexpr int kCsrRowsMax = 4;
 hipError_t launch_csr(const CsrView& a, int subwave, int rows, bool f64, void* y,
                       const void* x, double alpha, double beta, hipStream_t stream);
 hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double alpha,
@@ -106,6 +106,8 @@ hipError_t launch_sell(const SellView& a, bool f64, void* y, const void* x, doub
                        double beta, hipStream_t stream);
 hipError_t launch_tail(const TailView& t, bool f64, void* y, const void* x, double alpha,
                        hipStream_t stream);
+// y = beta * y for n entries (beta == 0 writes zeros and never reads y)
+hipError_t launch_scale(int64_t n, bool f64, void* y, double beta, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
 }  // namespace spmv

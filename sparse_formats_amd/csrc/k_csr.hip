@@ -14,60 +14,80 @@
 
 namespace spmv {
 
-// Each group of S lanes handles R consecutive rows.  A lone row costs three
-// dependent memory round trips (row pointer, then val/col, then x), so the
-// group first issues the row pointers, values and columns of all R rows
-// (two entries per lane and row) and only then the x reads and sums; longer
-// rows finish in a plain loop.  The first pass reads with clamped indices
-// and masks the products, so it has no per-entry branches.
+// Each group of S lanes handles R rows.  A lone row costs three dependent
+// memory round trips (row pointer, then val/col, then x), so the group first
+// issues the row pointers, values and columns of all R rows (U entries per
+// lane and row, U = 16 / S for small groups so that the first pass covers 16
+// entries of every row) and only then the x reads and sums; longer rows
+// finish in a plain loop.  The R rows of a group are interleaved with those
+// of the other groups of its wave (row = wave base + r * groups + group), so
+// every load instruction covers consecutive rows: neighbouring rows share
+// cache lines of val/col and, for banded matrices, entry u of neighbouring
+// rows usually lies on the same diagonal, so their x reads share lines too.
+// The first pass reads with clamped indices and masks the products, so it
+// has no per-entry branches.
+template <int S, int R>
+struct CsrFirstPass {
+    static constexpr int a = 16 / S, b = 16 / R;
+    static constexpr int value = (a < b ? a : b) > 2 ? (a < b ? a : b) : 2;
+};
+
 template <typename T, int S, int R>
 __global__ __launch_bounds__(256) void k_csr_vector(int n, const int* __restrict__ rowptr,
                                                     const int* __restrict__ col,
                                                     const T* __restrict__ val,
                                                     const T* __restrict__ x, T* __restrict__ y,
                                                     T alpha, T beta) {
-    constexpr int kGroups = 256 / S;
+    constexpr int kGroups = kWave / S;  // groups per wave
+    constexpr int U = CsrFirstPass<S, R>::value;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t row0 = (tile * kGroups + threadIdx.x / S) * R;
+    const int64_t wave = tile * 4 + threadIdx.x / kWave;
+    const int64_t base = wave * (kGroups * R) + (threadIdx.x % kWave) / S;
     const int sub = threadIdx.x & (S - 1);
-    if (row0 >= n) return;  // whole groups leave together
-    int kb[R + 1];
+    if (base >= n) return;  // whole groups leave together
+    int kb[R], ke[R];
 #pragma unroll
-    for (int r = 0; r <= R; ++r) kb[r] = rowptr[row0 + r < n ? row0 + r : (int64_t)n];
-    T v[R][2];
-    int c[R][2];
-    bool ok[R][2];
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = base + r * kGroups;
+        kb[r] = row < n ? rowptr[row] : 0;
+        ke[r] = row < n ? rowptr[row + 1] : 0;
+    }
+    T v[R][U];
+    int c[R][U];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int k = kb[r] + sub + u * S;
-            ok[r][u] = k < kb[r + 1];
-            const int kc = max(min(k, kb[r + 1] - 1), 0);  // in bounds even when masked
+        for (int u = 0; u < U; ++u) {
+            const int kc = max(min(kb[r] + sub + u * S, ke[r] - 1), 0);  // in bounds even when masked
             v[r][u] = val[kc];
             c[r][u] = col[kc];
         }
     T sum[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const T p0 = ok[r][0] ? v[r][0] * x[c[r][0]] : T(0);
-        const T p1 = ok[r][1] ? v[r][1] * x[c[r][1]] : T(0);
-        sum[r] = p0 + p1;
+        T acc = T(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const T p = v[r][u] * x[c[r][u]];
+            acc += kb[r] + sub + u * S < ke[r] ? p : T(0);
+        }
+        sum[r] = acc;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        for (int k = kb[r] + sub + 2 * S; k < kb[r + 1]; k += S) sum[r] = fma(val[k], x[col[k]], sum[r]);
+        for (int k = kb[r] + sub + U * S; k < ke[r]; k += S) sum[r] = fma(val[k], x[col[k]], sum[r]);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const T s_r = group_sum<S>(sum[r]);
-        if (sub == 0 && row0 + r < n) y[row0 + r] = axpby(s_r, alpha, beta, y + row0 + r);
+        const int64_t row = base + r * kGroups;
+        if (sub == 0 && row < n) y[row] = axpby(s_r, alpha, beta, y + row);
     }
 }
 
 template <typename T, int S, int R>
 static hipError_t run(const CsrView& a, void* y, const void* x, double alpha, double beta,
                       hipStream_t stream) {
-    constexpr int kRowsPerBlock = 256 / S * R;
+    constexpr int kRowsPerBlock = 256 / S * R;  // 4 waves of 64 / S groups of R rows
     const int64_t blocks = ((int64_t)a.n + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_csr_vector<T, S, R>), dim3((unsigned)blocks), dim3(256), 0, stream,
@@ -96,6 +116,7 @@ static hipError_t dispatch(const CsrView& a, int subwave, int rows, void* y, con
                            double alpha, double beta, hipStream_t stream) {
     switch (rows) {
         case 1: return dispatch_s<T, 1>(a, subwave, y, x, alpha, beta, stream);
+        case 2: return dispatch_s<T, 2>(a, subwave, y, x, alpha, beta, stream);
         case 4: return dispatch_s<T, 4>(a, subwave, y, x, alpha, beta, stream);
         default: return hipErrorInvalidValue;
     }

@@ -341,6 +341,27 @@ static hipError_t run(const TailView& t, void* y, const void* x, double alpha,
     return hipGetLastError();
 }
 
+// y = beta * y before an entry-balanced pass over the whole matrix adds its
+// products with atomics (beta == 0 never reads y, so NaNs in y vanish).
+template <typename T>
+__global__ __launch_bounds__(256) void k_scale(int64_t n, T* __restrict__ y, T beta) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        y[i] = beta == T(0) ? T(0) : beta * y[i];
+}
+
+hipError_t launch_scale(int64_t n, bool f64, void* y, double beta, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+    if (f64)
+        hipLaunchKernelGGL(k_scale<double>, dim3((unsigned)blocks), dim3(256), 0, stream, n,
+                           (double*)y, beta);
+    else
+        hipLaunchKernelGGL(k_scale<float>, dim3((unsigned)blocks), dim3(256), 0, stream, n,
+                           (float*)y, (float)beta);
+    return hipGetLastError();
+}
+
 hipError_t launch_tail(const TailView& t, bool f64, void* y, const void* x, double alpha,
                        hipStream_t stream) {
     return f64 ? run<double>(t, y, x, alpha, stream) : run<float>(t, y, x, alpha, stream);

@@ -74,7 +74,7 @@ def test_split_width_any(fmt, K):
               what="%s K=%d" % (fmt, K))
 
 
-@pytest.mark.parametrize("rows", [1, 4])
+@pytest.mark.parametrize("rows", [1, 2, 4])
 @pytest.mark.parametrize("sw", [1, 2, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("name", ["every_len", "ragged", "nnz0", "n1", "c1"])
 def test_csr_every_shape(sw, rows, name):
@@ -89,6 +89,8 @@ def test_csr_every_shape(sw, rows, name):
               what="csr S=%d R=%d %s" % (sw, rows, name))
     with pytest.raises(sf.SpmvError):
         M.convert("csr", csr_rows=3)
+    with pytest.raises(sf.SpmvError):
+        M.convert("csr", csr_rows=8)
 
 
 def test_sell_split_slices():
@@ -358,3 +360,58 @@ def test_x_window_auto_choice():
     assert M2.info()["x_window"] == (1 if M2.info()["band_fraction"] >= 0.5 else 0)
     with pytest.raises(sf.SpmvError):
         M2.convert("hyb", x_window=2)
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("name", list(MATS) + ["banded"])
+@pytest.mark.parametrize("win", [0, 1])
+def test_csr_balanced(name, dtype, win):
+    """The entry-balanced CSR kernel (beta pass, then 512-entry wave chunks
+    with a segmented scan and atomics for rows that cross chunks)."""
+    a = WINDOW_MATS[name]()
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    x_np, y0_np = vectors(a.n, 17)
+    x_np, y0_np = x_np.astype(npdt), y0_np.astype(npdt)
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n).convert("csr", csr_kernel="balanced",
+                                                             x_window=win)
+    i = M.info()
+    assert i["csr_kernel"] == "balanced" and i["format"] == "csr"
+    assert i["x_window"] == (win if a.nnz > 0 else 0)
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    rows = None if a.n < 100_000 else np.unique(np.concatenate(
+        [np.arange(0, a.n, 97), np.argsort(a.row_lengths())[-200:]]))
+    for alpha, beta in AB:
+        y = apply(M, x, y0, alpha, beta)
+        check(a, x_np, y0_np, alpha, beta, y, dtype, rows=rows,
+              what="csr balanced win=%d %s a=%g b=%g" % (win, name, alpha, beta))
+    if a.n > 0:
+        # beta = 0 never reads y: NaNs in y must not survive
+        y = torch.full((a.n,), float("nan"), dtype=dtype, device="cuda")
+        M.apply(y, x)
+        torch.cuda.synchronize()
+        check(a, x_np, None, 1.0, 0.0, y.cpu().numpy(), dtype, rows=rows,
+              what="csr balanced NaN y %s" % name)
+    M.close()
+
+
+def test_csr_kernel_choice():
+    for name in ["c1", "ragged", "long_spans"]:
+        a = MATS[name]()
+        x_np, y0_np = vectors(a.n, 18)
+        M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("csr")
+        assert M.info()["csr_kernel"] in ("vector", "balanced")
+        y = apply(M, torch.from_numpy(x_np).cuda(), torch.from_numpy(y0_np).cuda(), 1.5, -0.5)
+        check(a, x_np, y0_np, 1.5, -0.5, y, torch.float64, what="csr auto %s" % name)
+        M.convert("csr", csr_kernel="vector")
+        assert M.info()["csr_kernel"] == "vector" and M.info()["x_window"] == 0
+        # converting to another format and back keeps the handle consistent
+        M.convert("hec").convert("csr", csr_kernel="balanced")
+        assert M.info()["csr_kernel"] == "balanced"
+        y = apply(M, torch.from_numpy(x_np).cuda(), torch.from_numpy(y0_np).cuda(), 1.0, 1.0)
+        check(a, x_np, y0_np, 1.0, 1.0, y, torch.float64, what="csr balanced %s" % name)
+        with pytest.raises(sf.SpmvError):
+            M.convert("csr", csr_kernel=3)
+        M.close()
