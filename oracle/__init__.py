@@ -11,7 +11,10 @@ Functions (each restates a definition from the pages; see oracle.c):
                     the per-row scale |alpha|*sum|a*x| + |beta*y|.
 * ``ell``        -- ELLPACK arrays: ELLPACK-R (column-major, stride a multiple of
                     64) or the HYB/HEC ELL part (column-major blocks of rows).
-* ``sell``       -- SELL-64 (sorted, sliced, padded) arrays and permutation.
+* ``sell``       -- SELL-64 (sorted, sliced, padded) arrays and permutation,
+                    optionally sorted only inside windows of sigma rows.
+* ``ell_pad_fraction`` -- share of padding slots a lane-per-row sweep of an
+                    unsorted ELL part reads (the windowed-sort decision).
 * ``hyb_width``  -- the ELL width of the HYB/HEC split.
 * ``tail``       -- the irregular part of the split as COO and CSR.
 * ``check``      -- the per-entry tolerance test |y - y_ref| <= tol * scale.
@@ -58,8 +61,10 @@ def _load():
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_len.argtypes = [I64, P]
         lib.oracle_max_len.restype = I64
-        lib.oracle_ell.argtypes = [I64, P, P, P, ctypes.c_int, I64, I64, P, P, P]
-        lib.oracle_sell_layout.argtypes = [I64, P, P, P, P]
+        lib.oracle_ell.argtypes = [I64, P, P, P, ctypes.c_int, I64, I64, I64, P, P, P, P]
+        lib.oracle_ell_pad_fraction.argtypes = [I64, P, I64]
+        lib.oracle_ell_pad_fraction.restype = ctypes.c_double
+        lib.oracle_sell_layout.argtypes = [I64, P, I64, P, P, P]
         lib.oracle_sell_layout.restype = I64
         lib.oracle_sell_fill.argtypes = [I64, P, P, P, ctypes.c_int, P, P, P, P]
         lib.oracle_hyb_width.argtypes = [I64, P, I64]
@@ -137,12 +142,15 @@ def max_len(a) -> int:
 ELL_BLOCK_SPLIT = 1024   # rows per column-major block of the HYB/HEC ELL part
 
 
-def ell(a, width: int | None = None, block: int = 0):
+def ell(a, width: int | None = None, block: int = 0, sigma: int = 0, with_perm: bool = False):
     """ELLPACK arrays of the given width (default: longest row).
 
     block == 0: ELLPACK-R, one column-major block of pad64(n) rows.
-    block > 0: column-major blocks of `block` rows (the HYB/HEC ELL part).
-    Returns (col[W*R] int32, val[W*R], len[R] int32), R the padded rows.
+    block > 0: column-major blocks of `block` rows (the HYB/HEC ELL part);
+    sigma > 0 (dividing block) orders the rows of each aligned window of
+    sigma positions by stored length descending, then row ascending.
+    Returns (col[W*R] int32, val[W*R], len[R] int32[, perm[R] int64]), R the
+    padded rows, lengths and perm by position.
     """
     lib = _load()
     rowptr = _c(a.rowptr, np.int64)
@@ -152,21 +160,29 @@ def ell(a, width: int | None = None, block: int = 0):
     oc = np.empty(W * R, dtype=np.int32)
     ov = np.empty(W * R, dtype=val.dtype)
     ol = np.empty(R, dtype=np.int32)
+    op = np.empty(R, dtype=np.int64)
     lib.oracle_ell(a.n, _p(rowptr), _p(_c(a.col, np.int32)), _p(val), val.itemsize,
-                   W, int(block), _p(oc), _p(ov), _p(ol))
-    return oc, ov, ol
+                   W, int(block), int(sigma), _p(oc), _p(ov), _p(ol), _p(op))
+    return (oc, ov, ol, op) if with_perm else (oc, ov, ol)
 
 
-def sell(a):
+def ell_pad_fraction(a, width: int) -> float:
+    """Share of the slots a lane-per-row sweep of the unsorted ELL part reads
+    past the rows' ends (waves of 64 consecutive rows run to their longest)."""
+    return float(_load().oracle_ell_pad_fraction(a.n, _p(_c(a.rowptr, np.int64)), int(width)))
+
+
+def sell(a, sigma: int = 0):
     """SELL-64: (perm[n] int64, slice_ptr[S/64+1] int64, len_sorted[S] int32,
-    col[slots] int32, val[slots])."""
+    col[slots] int32, val[slots]).  sigma > 0 sorts only inside aligned
+    windows of sigma rows (0: all rows at once)."""
     lib = _load()
     rowptr = _c(a.rowptr, np.int64)
     S = pad64(a.n)
     perm = np.empty(a.n, dtype=np.int64)
     sp = np.empty(S // 64 + 1, dtype=np.int64)
     ls = np.empty(S, dtype=np.int32)
-    total = lib.oracle_sell_layout(a.n, _p(rowptr), _p(perm), _p(sp), _p(ls))
+    total = lib.oracle_sell_layout(a.n, _p(rowptr), int(sigma), _p(perm), _p(sp), _p(ls))
     val = np.ascontiguousarray(a.val)
     oc = np.empty(total, dtype=np.int32)
     ov = np.empty(total, dtype=val.dtype)

@@ -44,12 +44,19 @@
  *     - ELL-R stride S = 64 * ceil(n / 64); slot (i, j) at j * S + i; pad
  *       slots hold column 0 and value +0.0; padded rows have length 0.
  *       The ELL part of HYB/HEC is stored the same way in blocks of 1024
- *       rows (the Krylov/AMG page sets the ELL stride to "256 or other
- *       multiples" of the SIMD width): slot (i, j) at
- *       (i / 1024) * W * 1024 + j * 1024 + i % 1024.
+ *       rows (the Krylov/AMG page sets the ELL stride to 256 or a multiple
+ *       of it): slot (i, j) at (i / 1024) * W * 1024 + j * 1024 + i % 1024.
+ *     - Windowed sorting (the sort of pJDS applied only inside aligned
+ *       windows of sigma rows, so rows move less than sigma and x locality
+ *       survives): SELL-64 sorts by (i / sigma, length desc, row asc) and
+ *       pads each slice to its longest row; sigma = 1 keeps the row order; the
+ *       ELL part of HYB/HEC may sort the rows of every 1024-row block by
+ *       (position / sigma, stored length desc, row asc), sigma dividing
+ *       1024, with out_perm[p] the row at position p.
  *     - SELL sort key (length descending, row ascending) -- unique, so the
- *       permutation is unique; slice s has width w_s = length of its first
- *       (longest) row; entry j of sorted row r sits at
+ *       permutation is unique; slice s has width w_s = length of its
+ *       longest row (the first one after a whole-matrix sort); entry j of
+ *       sorted row r sits at
  *       slice_ptr[r / 64] + 64 * j + r % 64.
  *     - HYB/HEC width K = max{k >= 0 : #{i : len_i >= k} >= ceil(n / 3)}
  *       unless a width is given (clamped to the longest row); the first K
@@ -172,45 +179,109 @@ int64_t oracle_max_len(int64_t n, const int64_t *rowptr)
     return w;
 }
 
+/* stored length of row i in an ELL part of width W */
+static int64_t ell_len(const int64_t *rowptr, int64_t i, int64_t W)
+{
+    int64_t len = rowptr[i + 1] - rowptr[i];
+    return len < W ? len : W;
+}
+
+/* windowed-sort comparator state: rows of one window, by stored length
+ * descending, then row ascending */
+static const int64_t *g_ell_rowptr;
+static int64_t g_ell_W;
+static int cmp_ell_rows(const void *pa, const void *pb)
+{
+    int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    int64_t la = ell_len(g_ell_rowptr, a, g_ell_W), lb = ell_len(g_ell_rowptr, b, g_ell_W);
+    if (la != lb)
+        return la > lb ? -1 : 1;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
 /*
  * ELLPACK arrays of width W (W >= every row length handled; entries j >= W
  * of a row are skipped, which is how the ELL part of HYB/HEC is built),
- * stored in column-major blocks of B rows: entry j of row i in slot
- * (i / B) * W * B + j * B + i % B.  block <= 0 means one block of
- * B = pad64(n) rows (ELLPACK-R's column-by-column layout).  Rows are padded
- * to R = ceil(n / B) * B; out_col/out_val hold W * R slots, out_len R lengths.
+ * stored in column-major blocks of B rows: the row at position p holds its
+ * entry j in slot (p / B) * W * B + j * B + p % B.  block <= 0 means one
+ * block of B = pad64(n) rows (ELLPACK-R's column-by-column layout).  Rows
+ * are padded to R = ceil(n / B) * B; out_col/out_val hold W * R slots,
+ * out_len R lengths (by position).
+ * sigma <= 0: position p holds row p.  sigma > 0 (block > 0, sigma divides
+ * B): the rows of each aligned window of sigma positions are ordered by
+ * stored length descending, then row ascending; padding rows (>= n) stay
+ * last.  out_perm (R entries, may be NULL) receives the row at each
+ * position (p itself for padding).
  */
 void oracle_ell(int64_t n, const int64_t *rowptr, const int32_t *col,
                 const void *val, int vsize, int64_t W, int64_t block,
-                int32_t *out_col, void *out_val, int32_t *out_len)
+                int64_t sigma, int32_t *out_col, void *out_val, int32_t *out_len,
+                int64_t *out_perm)
 {
     int64_t B = block > 0 ? block : pad64(n);
     int64_t R = block > 0 ? (n + block - 1) / block * block : B;
     char *ov = (char *)out_val;
     const char *iv = (const char *)val;
+    int64_t *row_at = (int64_t *)malloc((size_t)(R > 0 ? R : 1) * sizeof(int64_t));
+    for (int64_t p = 0; p < R; ++p)
+        row_at[p] = p;
+    if (sigma > 0 && block > 0) {
+        g_ell_rowptr = rowptr;
+        g_ell_W = W;
+        for (int64_t w0 = 0; w0 < n; w0 += sigma) {
+            int64_t w1 = w0 + sigma < n ? w0 + sigma : n;  /* real rows of the window */
+            qsort(row_at + w0, (size_t)(w1 - w0), sizeof(int64_t), cmp_ell_rows);
+        }
+    }
     memset(out_col, 0, (size_t)(W * R) * sizeof(int32_t));
     memset(ov, 0, (size_t)(W * R) * (size_t)vsize);
-    for (int64_t i = 0; i < R; ++i)
-        out_len[i] = 0;
-    for (int64_t i = 0; i < n; ++i) {
-        int64_t len = rowptr[i + 1] - rowptr[i];
-        if (len > W)
-            len = W;
-        out_len[i] = (int32_t)len;
+    for (int64_t p = 0; p < R; ++p) {
+        int64_t i = row_at[p];
+        int64_t len = i < n ? ell_len(rowptr, i, W) : 0;
+        out_len[p] = (int32_t)len;
+        if (out_perm)
+            out_perm[p] = i;
         for (int64_t j = 0; j < len; ++j) {
-            int64_t slot = (i / B) * W * B + j * B + i % B;
+            int64_t slot = (p / B) * W * B + j * B + p % B;
             int64_t k = rowptr[i] + j;
             out_col[slot] = col[k];
             memcpy(ov + slot * vsize, iv + k * vsize, (size_t)vsize);
         }
     }
+    free(row_at);
 }
 
-/* sort key: length descending, then row ascending */
+/*
+ * Share of the slots that a lane-per-row sweep of the (unsorted) ELL part
+ * of width W reads beyond the rows' ends: waves of 64 consecutive rows run
+ * to their longest stored row, so the padding read is
+ * 1 - sum_i len_i / sum_waves 64 * max len in the wave.
+ */
+double oracle_ell_pad_fraction(int64_t n, const int64_t *rowptr, int64_t W)
+{
+    double used = 0, read = 0;
+    for (int64_t w0 = 0; w0 < n; w0 += 64) {
+        int64_t mx = 0;
+        for (int64_t i = w0; i < w0 + 64 && i < n; ++i) {
+            int64_t l = ell_len(rowptr, i, W);
+            used += (double)l;
+            if (l > mx)
+                mx = l;
+        }
+        read += 64.0 * (double)mx;
+    }
+    return read > 0 ? 1.0 - used / read : 0.0;
+}
+
+/* sort key: window (sigma rows; 0 = one window), length descending, then
+ * row ascending */
 static const int64_t *g_rowptr;
+static int64_t g_sigma;
 static int cmp_rows(const void *pa, const void *pb)
 {
     int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    if (g_sigma > 0 && a / g_sigma != b / g_sigma)
+        return a / g_sigma < b / g_sigma ? -1 : 1;
     int64_t la = g_rowptr[a + 1] - g_rowptr[a];
     int64_t lb = g_rowptr[b + 1] - g_rowptr[b];
     if (la != lb)
@@ -222,21 +293,31 @@ static int cmp_rows(const void *pa, const void *pb)
  * SELL-64 layout sizes and permutation.  perm[r] (r < pad64(n)) is the
  * original row at sorted position r (rows >= n are padding, perm = -1 kept
  * out: perm has n entries); slice_ptr has nslices + 1 entries; len_sorted has
- * pad64(n) entries.  Returns the total number of slots.
+ * pad64(n) entries.  sigma <= 0 sorts all rows at once (pJDS); sigma > 0
+ * sorts only inside aligned windows of sigma rows.  Returns the total number
+ * of slots.
  */
-int64_t oracle_sell_layout(int64_t n, const int64_t *rowptr, int64_t *perm,
+int64_t oracle_sell_layout(int64_t n, const int64_t *rowptr, int64_t sigma, int64_t *perm,
                            int64_t *slice_ptr, int32_t *len_sorted)
 {
     int64_t S = pad64(n), ns = S / 64;
     for (int64_t i = 0; i < n; ++i)
         perm[i] = i;
     g_rowptr = rowptr;
+    g_sigma = sigma;
     qsort(perm, (size_t)n, sizeof(int64_t), cmp_rows);
     for (int64_t r = 0; r < S; ++r)
         len_sorted[r] = r < n ? (int32_t)(rowptr[perm[r] + 1] - rowptr[perm[r]]) : 0;
     slice_ptr[0] = 0;
-    for (int64_t s = 0; s < ns; ++s)
-        slice_ptr[s + 1] = slice_ptr[s] + 64 * (int64_t)len_sorted[64 * s];
+    for (int64_t s = 0; s < ns; ++s) {
+        /* width = longest row of the slice (its first row unless a window
+         * boundary falls inside the slice) */
+        int64_t w = 0;
+        for (int64_t r = 64 * s; r < 64 * s + 64; ++r)
+            if (len_sorted[r] > w)
+                w = len_sorted[r];
+        slice_ptr[s + 1] = slice_ptr[s] + 64 * w;
+    }
     return slice_ptr[ns];
 }
 

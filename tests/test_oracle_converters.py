@@ -203,3 +203,99 @@ def test_split_round_trip(name, mk, K):
         rows_c.append(np.concatenate([ec[i], tcol[sel]]))
         rows_v.append(np.concatenate([ev[i], tval[sel]]))
     same_rows(a, rows_c, rows_v)
+
+
+def _hand5():
+    # lengths 2, 1, 0, 3, 1
+    return CSR(5, np.array([0, 2, 3, 3, 6, 7], np.int64), np.array([4, 1, 0, 2, 3, 4, 1], np.int32),
+               np.arange(1.0, 8.0))
+
+
+def test_sorted_ell_layout_small():
+    """Windowed sort of the blocked ELL part, hand-placed: B = 4, W = 3."""
+    a = _hand5()
+    oc, ov, ol, op = oracle.ell(a, 3, block=4, sigma=4, with_perm=True)
+    # block 0 holds rows 0..3 ordered by length desc: 3, 0, 1, 2; block 1: row 4 + padding
+    assert list(op) == [3, 0, 1, 2, 4, 5, 6, 7]
+    assert list(ol) == [3, 2, 1, 0, 1, 0, 0, 0]
+    assert list(ov) == [4, 1, 3, 0, 5, 2, 0, 0, 6, 0, 0, 0,  7] + [0] * 11
+    assert list(oc) == [2, 4, 0, 0, 3, 1, 0, 0, 4, 0, 0, 0,  1] + [0] * 11
+    # windows of 2 positions: {0, 1} keeps rows 0, 1; {2, 3} puts row 3 first
+    oc, ov, ol, op = oracle.ell(a, 3, block=4, sigma=2, with_perm=True)
+    assert list(op[:4]) == [0, 1, 3, 2] and list(ol[:4]) == [2, 1, 3, 0]
+    assert list(ov[:12]) == [1, 3, 4, 0, 2, 0, 5, 0, 0, 0, 6, 0]
+    assert list(oc[:12]) == [4, 0, 2, 0, 1, 0, 3, 0, 0, 0, 4, 0]
+    # sigma 0 is the unsorted layout
+    u = oracle.ell(a, 3, block=4, with_perm=True)
+    assert list(u[3]) == list(range(8))
+
+
+@pytest.mark.parametrize("name,mk", MATS)
+@pytest.mark.parametrize("sigma", [64, 256, 1024])
+def test_sorted_ell_round_trip(name, mk, sigma):
+    a = mk()
+    B = oracle.ELL_BLOCK_SPLIT
+    K = oracle.hyb_width(a)
+    oc, ov, ol, op = oracle.ell(a, K, block=B, sigma=sigma, with_perm=True)
+    R = ol.size
+    assert np.array_equal(np.sort(op), np.arange(R))
+    assert np.array_equal(op[a.n:], np.arange(a.n, R))
+    L = np.minimum(a.row_lengths(), K)
+    assert np.array_equal(ol[:a.n], L[op[:a.n]])
+    # inside every window: stored length descending, then row ascending
+    for w0 in range(0, a.n, sigma):
+        rows = op[w0:min(w0 + sigma, a.n)]
+        assert np.all((rows >= w0) & (rows < w0 + sigma))
+        key = list(zip(-L[rows], rows))
+        assert key == sorted(key)
+    # decode by position, then undo the permutation
+    pc, pv = ell_to_csr(R, oc, ov, ol, block=B)
+    rows_c, rows_v = [None] * a.n, [None] * a.n
+    for p in range(a.n):
+        rows_c[op[p]], rows_v[op[p]] = pc[p], pv[p]
+    for i in range(a.n):
+        s = a.rowptr[i]
+        assert np.array_equal(rows_c[i], a.col[s:s + L[i]])
+        assert rows_v[i].tobytes() == a.val[s:s + L[i]].tobytes()
+
+
+def test_ell_pad_fraction():
+    a = _hand5()
+    # one wave of 64 rows runs to the longest stored row (3): 64 * 3 slots for 7 entries
+    assert oracle.ell_pad_fraction(a, 3) == pytest.approx(1 - 7 / 192)
+    assert oracle.ell_pad_fraction(a, 1) == pytest.approx(1 - 4 / 64)
+    # constant length over whole waves reads no padding
+    b = random_csr(256, seed=35, lens=np.full(256, 9))
+    assert oracle.ell_pad_fraction(b, 9) == 0.0
+    assert oracle.ell_pad_fraction(b, 20) == 0.0
+    # two waves: lengths 1 and 5 alternating in the first, all 2 in the second
+    lens = np.concatenate([np.tile([1, 5], 32), np.full(64, 2)])
+    c = random_csr(128, seed=36, lens=lens)
+    assert oracle.ell_pad_fraction(c, 8) == pytest.approx(1 - (32 * 6 + 128) / (64 * 5 + 64 * 2))
+
+
+def test_sell_windowed_sort():
+    a = _hand5()
+    perm, sp, ls, sc, sv = oracle.sell(a, sigma=2)
+    assert list(perm) == [0, 1, 3, 2, 4]
+    # one slice, padded to its longest row (3), not to its first row
+    assert list(sp) == [0, 192] and list(ls[:5]) == [2, 1, 3, 0, 1]
+    same_rows(a, *sell_to_csr(a.n, perm, sp, ls, sc, sv))
+    ident = oracle.sell(a, sigma=1)[0]
+    assert list(ident) == list(range(5))
+    b = random_csr(1000, seed=37, density=0.01, empty_frac=0.2, long_rows=3, long_len=700)
+    whole = oracle.sell(b)
+    for sigma in (b.n, 4096):
+        w = oracle.sell(b, sigma=sigma)
+        assert all(np.array_equal(u, v) for u, v in zip(whole, w))
+    perm, sp, ls, sc, sv = oracle.sell(b, sigma=128)
+    L = b.row_lengths()
+    for w0 in range(0, b.n, 128):
+        rows = perm[w0:w0 + 128]
+        assert np.all((rows >= w0) & (rows < w0 + 128))
+        key = list(zip(-L[rows], rows))
+        assert key == sorted(key)
+    widths = np.diff(sp) // 64
+    Lp = np.concatenate([L[perm], np.zeros(oracle.pad64(b.n) - b.n, np.int64)])
+    assert np.array_equal(widths, Lp.reshape(-1, 64).max(axis=1))
+    same_rows(b, *sell_to_csr(b.n, perm, sp, ls, sc, sv))
