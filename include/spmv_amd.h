@@ -123,6 +123,24 @@ typedef struct {
      * cross chunks with atomics after a pass that writes beta * y.  With
      * x_window it stages x in LDS like the HEC tail. */
     int32_t csr_kernel;
+    /* Windowed sorting: the pJDS sort of "Sparse matrix-vector multiplication
+     * on GPGPU clusters" (Sect. 2.2: rows ordered by length, longest first)
+     * applied only inside aligned windows of sort_window rows, so that rows
+     * move less than a window and neighbouring rows keep reading
+     * neighbouring x.
+     *   SELL-64: -1 (default) sorts inside windows of 8192 rows (64 KiB of
+     *            fp64 y: the y writes of a window stay within a few L2
+     *            lines per slice and banded matrices keep their x
+     *            locality); 0 keeps the row order; k >= 1 sorts inside
+     *            windows of k rows, k >= n sorts all rows at once (the
+     *            page's pJDS).  Each slice is padded to its longest row.
+     *   HYB/HEC: the rows of every 1024-row block of the ELL part;
+     *            -1 (default) sorts inside the whole block when waves of 64
+     *            unsorted rows would read more than 10% padding slots, 0 never,
+     *            k in {64, 128, 256, 512, 1024} inside windows of k rows.
+     *            The ELL part then keeps a position -> row permutation.
+     *   ELL-R / CSR: must be -1 or 0. */
+    int32_t sort_window;
     /* Largest device footprint a padded format (ELL-R) may take, in bytes;
      * 0 means 75% of the device's memory. */
     uint64_t footprint_budget_bytes;
@@ -147,6 +165,9 @@ typedef struct {
     int32_t x_window;      /* 1 when the active format stages x in LDS */
     int32_t csr_rows;      /* CSR: rows per lane group (1, 2 or 4) */
     int32_t csr_kernel;    /* CSR: SPMV_CSR_VECTOR or SPMV_CSR_BALANCED */
+    int32_t sort_window;   /* SELL-64 / HYB / HEC: rows per sort window in
+                              effect (0: rows kept in order; SELL-64 with
+                              all rows sorted at once reports n) */
     double band_fraction;  /* share of entries within the window's reach
                               (computed by ELL-R / HYB / HEC conversions) */
     int64_t ell_rows;      /* ELL-R / HYB / HEC: rows padded to whole blocks */
@@ -173,7 +194,9 @@ typedef enum {
     SPMV_A_TAIL_ROW = 11,  /* HYB: int32[tail_nnz] row of each tail entry */
     SPMV_A_TAIL_PTR = 12,  /* HEC: int32[n+1] start of each row's tail */
     SPMV_A_TAIL_COL = 13,  /* HYB/HEC: int32[tail_nnz] */
-    SPMV_A_TAIL_VAL = 14   /* HYB/HEC: dtype[tail_nnz] */
+    SPMV_A_TAIL_VAL = 14,  /* HYB/HEC: dtype[tail_nnz] */
+    SPMV_A_ELL_PERM = 15   /* HYB/HEC with a sorted ELL part: int32[ell_rows],
+                              row at each position (itself for padding) */
 } spmv_array;
 
 /*

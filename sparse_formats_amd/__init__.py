@@ -32,7 +32,7 @@ ARRAYS = {
     "sell_perm": (6, np.int32), "sell_slice_ptr": (7, np.int64), "sell_len": (8, np.int32),
     "sell_col": (9, np.int32), "sell_val": (10, None),
     "tail_row": (11, np.int32), "tail_ptr": (12, np.int32), "tail_col": (13, np.int32),
-    "tail_val": (14, None),
+    "tail_val": (14, None), "ell_perm": (15, np.int32),
 }
 _DTYPE = {torch.float32: 1, torch.float64: 2}
 _NP = {1: np.float32, 2: np.float64}
@@ -50,7 +50,8 @@ class SpmvError(RuntimeError):
 class _ConvertOpts(ctypes.Structure):
     _fields_ = [("ell_width", ctypes.c_int32), ("subwave", ctypes.c_int32),
                 ("x_window", ctypes.c_int32), ("csr_rows", ctypes.c_int32),
-                ("csr_kernel", ctypes.c_int32), ("footprint_budget_bytes", ctypes.c_uint64)]
+                ("csr_kernel", ctypes.c_int32), ("sort_window", ctypes.c_int32),
+                ("footprint_budget_bytes", ctypes.c_uint64)]
 
 
 class _Info(ctypes.Structure):
@@ -61,7 +62,7 @@ class _Info(ctypes.Structure):
                 ("subwave", ctypes.c_int32), ("nslices", ctypes.c_int32),
                 ("footprint_bytes", ctypes.c_uint64), ("x_window", ctypes.c_int32),
                 ("csr_rows", ctypes.c_int32), ("csr_kernel", ctypes.c_int32),
-                ("band_fraction", ctypes.c_double),
+                ("sort_window", ctypes.c_int32), ("band_fraction", ctypes.c_double),
                 ("ell_rows", ctypes.c_int64)]
 
 
@@ -160,14 +161,14 @@ class Matrix:
 
     def convert(self, fmt: str, ell_width: int = -1, subwave: int = 0, x_window: int = -1,
                 footprint_budget: int = 0, csr_rows: int = 0,
-                csr_kernel: str = "auto") -> "Matrix":
+                csr_kernel: str = "auto", sort_window: int = -1) -> "Matrix":
         """Build `fmt` on the device and make it active (options as in spmv_convert_opts;
         csr_kernel is "auto", "vector" or "balanced")."""
         if fmt not in FORMATS:
             raise ValueError("unknown format %r (one of %s)" % (fmt, ", ".join(FORMATS)))
         ck = CSR_KERNELS.get(csr_kernel, csr_kernel)
         o = _ConvertOpts(int(ell_width), int(subwave), int(x_window), int(csr_rows), int(ck),
-                         int(footprint_budget))
+                         int(sort_window), int(footprint_budget))
         _check(_lib.spmv_convert(self._h, FORMATS[fmt], ctypes.byref(o)))
         return self
 

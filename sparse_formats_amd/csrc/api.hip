@@ -97,6 +97,8 @@ struct Built {
     // ELL-R, or the ELL part of HYB / HEC
     int64_t ell_width = 0, ell_bh = 0, ell_rows = 0;  // width, rows per block, padded rows
     DevBuf ell_col, ell_val, ell_len;
+    DevBuf ell_perm;      // sorted ELL part: row at each position (else empty)
+    int sort_window = 0;  // rows per sort window in effect (0: none)
     // SELL-64
     int64_t nslices = 0, sell_slots = 0;
     DevBuf slice_ptr, sell_len, perm, sell_col, sell_val;
@@ -112,7 +114,8 @@ struct Built {
     double band_fraction = 0;
 
     size_t bytes() const {
-        return ell_col.bytes + ell_val.bytes + ell_len.bytes + slice_ptr.bytes + sell_len.bytes +
+        return ell_col.bytes + ell_val.bytes + ell_len.bytes + ell_perm.bytes + slice_ptr.bytes +
+               sell_len.bytes +
                perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + tail_row.bytes +
                tail_ptr.bytes + tail_col.bytes + tail_val.bytes + chunk_row.bytes;
     }
@@ -251,14 +254,15 @@ __global__ __launch_bounds__(256) void k_len_hist(int64_t n, int W, const int* _
 template <typename V>
 __global__ void k_ell_fill(int64_t n, int64_t rows, int64_t bh, int64_t W,
                            const int* __restrict__ rowptr, const int* __restrict__ col,
-                           const V* __restrict__ val, int* __restrict__ ecol,
-                           V* __restrict__ eval, int* __restrict__ elen) {
+                           const V* __restrict__ val, const int* __restrict__ perm,
+                           int* __restrict__ ecol, V* __restrict__ eval, int* __restrict__ elen) {
     const int64_t total = rows * W;
     const int64_t bstride = bh * W;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
          t += (int64_t)gridDim.x * blockDim.x) {
         const int64_t blk = t / bstride, rem = t - blk * bstride;
-        const int64_t j = rem / bh, i = blk * bh + (rem - j * bh);
+        const int64_t j = rem / bh, p = blk * bh + (rem - j * bh);
+        const int64_t i = perm && p < n ? perm[p] : p;  // row at position p
         int c = 0;
         V v = V(0);
         if (i < n) {
@@ -272,9 +276,63 @@ __global__ void k_ell_fill(int64_t n, int64_t rows, int64_t bh, int64_t W,
         ecol[t] = c;
         eval[t] = v;
     }
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows;
-         i += (int64_t)gridDim.x * blockDim.x)
-        elen[i] = i < n ? (int)std::min<int64_t>(rowptr[i + 1] - rowptr[i], W) : 0;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < rows;
+         p += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = perm && p < n ? perm[p] : p;
+        elen[p] = i < n ? (int)std::min<int64_t>(rowptr[i + 1] - rowptr[i], W) : 0;
+    }
+}
+
+// Windowed sort of one kEllBlock-row block of the ELL part (one workgroup
+// per block): positions ordered by (position / sigma, stored length
+// descending, row ascending).  The keys are unique, so a bitonic sort of
+// the block's keys in LDS gives the one ordering; padding rows (>= n) have
+// length 0 and the largest rows of their window, so they stay in place.
+__global__ __launch_bounds__(kEllBlock) void k_ell_block_sort(int64_t n, int64_t W, int sigma,
+                                                              const int* __restrict__ rowptr,
+                                                              int* __restrict__ perm) {
+    __shared__ unsigned long long key[kEllBlock];
+    const int p = threadIdx.x;
+    const int64_t pos = (int64_t)blockIdx.x * kEllBlock + p;  // also the row before sorting
+    int64_t len = 0;
+    if (pos < n) len = std::min<int64_t>(rowptr[pos + 1] - rowptr[pos], W);
+    // window (4 bits) | 2^32 - 1 - length (32 bits) | position in block (10 bits)
+    key[p] = ((unsigned long long)(p / sigma) << 42) |
+             ((unsigned long long)(0xFFFFFFFFu - (unsigned)len) << 10) | (unsigned)p;
+    __syncthreads();
+    for (int k = 2; k <= kEllBlock; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int q = p ^ j;
+            if (q > p) {
+                const unsigned long long a = key[p], b = key[q];
+                if ((a > b) == ((p & k) == 0)) key[p] = b, key[q] = a;
+            }
+            __syncthreads();
+        }
+    perm[pos] = (int)((int64_t)blockIdx.x * kEllBlock + (int)(key[p] & (kEllBlock - 1)));
+}
+
+// padding read by waves of 64 unsorted rows: out[0] += sum of stored
+// lengths, out[1] += 64 * longest stored length (one wave per 64 rows)
+__global__ __launch_bounds__(256) void k_ell_pad_count(int64_t n, int64_t W,
+                                                       const int* __restrict__ rowptr,
+                                                       unsigned long long* __restrict__ out) {
+    const int64_t waves = (n + 63) / 64;
+    const int lane = threadIdx.x & 63;
+    for (int64_t w = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64; w < waves;
+         w += (int64_t)gridDim.x * blockDim.x / 64) {
+        const int64_t i = w * 64 + lane;
+        int mx = i < n ? (int)std::min<int64_t>(rowptr[i + 1] - rowptr[i], W) : 0;
+        long long sum = mx;
+        for (int o = 32; o > 0; o >>= 1) {
+            mx = max(mx, __shfl_xor(mx, o));
+            sum += __shfl_xor(sum, o);
+        }
+        if (lane == 0) {
+            atomicAdd(out, (unsigned long long)sum);
+            atomicAdd(out + 1, 64ull * (unsigned long long)mx);
+        }
+    }
 }
 
 // entries within `lead` positions of their row (reach of the LDS window)
@@ -300,15 +358,38 @@ __global__ void k_sell_keys(int64_t n, int W, const int* __restrict__ rowptr,
         key[i] = (unsigned)(W - (rowptr[i + 1] - rowptr[i]));
 }
 
-// sorted lengths and per-slice slot counts 64 * width (width = first row)
+// windowed sort key: window << 32 | (W - length)
+__global__ void k_sell_keys_win(int64_t n, int64_t sigma, int W, const int* __restrict__ rowptr,
+                                unsigned long long* __restrict__ key) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        key[i] = ((unsigned long long)(i / sigma) << 32) |
+                 (unsigned)(W - (rowptr[i + 1] - rowptr[i]));
+}
+
+__global__ void k_iota(int64_t n, int* __restrict__ out) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        out[i] = (int)i;
+}
+
+// lengths in sorted order (0 for the padding rows)
 __global__ void k_sell_len(int64_t n, int64_t S, const int* __restrict__ rowptr,
-                           const int* __restrict__ perm, int* __restrict__ slen,
-                           int64_t* __restrict__ slots) {
+                           const int* __restrict__ perm, int* __restrict__ slen) {
     for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < S;
-         r += (int64_t)gridDim.x * blockDim.x) {
-        const int L = r < n ? rowptr[perm[r] + 1] - rowptr[perm[r]] : 0;
-        slen[r] = L;
-        if ((r & 63) == 0) slots[r >> 6] = 64 * (int64_t)L;
+         r += (int64_t)gridDim.x * blockDim.x)
+        slen[r] = r < n ? rowptr[perm[r] + 1] - rowptr[perm[r]] : 0;
+}
+
+// slots of each slice: 64 * its longest row (the first one unless a sort
+// window boundary or unsorted rows fall inside the slice)
+__global__ void k_sell_width(int64_t ns, const int* __restrict__ slen,
+                             int64_t* __restrict__ slots) {
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < ns;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        int w = 0;
+        for (int l = 0; l < 64; ++l) w = max(w, slen[q * 64 + l]);
+        slots[q] = 64 * (int64_t)w;
     }
 }
 
@@ -421,7 +502,8 @@ uint64_t budget_bytes(const spmv_convert_opts& o) {
 // ELL arrays of width W: one column-major block of all rows (block = 0,
 // ELLPACK-R) or column-major blocks of `block` rows (ELL part of HYB/HEC)
 template <typename V>
-void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, Built& b, hipStream_t s) {
+void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, int sigma, Built& b,
+                    hipStream_t s) {
     const int64_t bh = block > 0 ? block : pad64(h->n);
     const int64_t rows = block > 0 ? (h->n + block - 1) / block * block : bh;
     b.ell_width = W;
@@ -430,21 +512,77 @@ void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, Built& b, hi
     b.ell_col.alloc((size_t)(W * rows) * 4);
     b.ell_val.alloc((size_t)(W * rows) * sizeof(V));
     b.ell_len.alloc((size_t)rows * 4);
+    b.sort_window = 0;
+    if (sigma > 0 && rows > 0) {  // block == kEllBlock, sigma divides it
+        b.ell_perm.alloc((size_t)rows * 4);
+        hipLaunchKernelGGL(k_ell_block_sort, dim3((unsigned)(rows / kEllBlock)), dim3(kEllBlock), 0,
+                           s, h->n, W, sigma, h->rowptr.as<int>(), b.ell_perm.as<int>());
+        hip_check(hipGetLastError(), "ell block sort");
+        b.sort_window = sigma;
+    }
     hipLaunchKernelGGL(k_ell_fill<V>, dim3(grid_for(std::max<int64_t>(W * rows, rows))), dim3(256),
                        0, s, h->n, rows, std::max<int64_t>(bh, 1), W, h->rowptr.as<int>(),
-                       h->col.as<int>(), h->val.as<V>(), b.ell_col.as<int>(), b.ell_val.as<V>(),
-                       b.ell_len.as<int>());
+                       h->col.as<int>(), h->val.as<V>(), b.ell_perm.as<int>(), b.ell_col.as<int>(),
+                       b.ell_val.as<V>(), b.ell_len.as<int>());
     hip_check(hipGetLastError(), "ell fill");
 }
 
+// the ELL part of HYB/HEC is sorted inside its blocks (by default) when
+// waves of 64 unsorted rows would read more than this share of padding
+constexpr double kSortPadShare = 0.10;
+
+// share of padding slots that waves of 64 unsorted rows would read in an
+// ELL part of width W
+double ell_pad_fraction(const spmv_handle* h, int64_t W, hipStream_t s) {
+    if (h->n == 0 || W == 0) return 0.0;
+    DevBuf cnt(16);
+    hip_check(hipMemsetAsync(cnt.p, 0, 16, s), "hipMemsetAsync");
+    hipLaunchKernelGGL(k_ell_pad_count, dim3(std::min<unsigned>(grid_for(h->n), 4096)), dim3(256), 0,
+                       s, h->n, W, h->rowptr.as<int>(), cnt.as<unsigned long long>());
+    hip_check(hipGetLastError(), "padding count");
+    unsigned long long c[2];
+    hip_check(hipMemcpyAsync(c, cnt.p, 16, hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+    sync(s);
+    return c[1] ? 1.0 - (double)c[0] / (double)c[1] : 0.0;
+}
+
+// sort_window: -1 sorts inside windows of kSellSortWindow rows, 0 keeps
+// the row order, k >= 1 sorts inside aligned windows of k rows (k >= n: all
+// rows at once, the pJDS order)
 template <typename V>
-void build_sell(const spmv_handle* h, Built& b, hipStream_t s) {
+void build_sell(const spmv_handle* h, int sort_window, Built& b, hipStream_t s) {
     const int64_t n = h->n, S = pad64(n), ns = S / 64;
     b.nslices = ns;
     b.perm.alloc((size_t)std::max<int64_t>(n, 1) * 4);
     b.sell_len.alloc((size_t)S * 4);
     b.slice_ptr.alloc((size_t)(ns + 1) * 8);
-    if (n > 0) {
+    if (sort_window < 0) sort_window = kSellSortWindow;
+    int64_t sigma = sort_window >= n ? n : sort_window;
+    if (sort_window == 0) sigma = 1;  // every row its own window: row order kept
+    b.sort_window = sigma <= 1 ? 0 : (int)sigma;
+    if (n > 0 && sigma <= 1) {
+        hipLaunchKernelGGL(k_iota, dim3(grid_for(n)), dim3(256), 0, s, n, b.perm.as<int>());
+        hip_check(hipGetLastError(), "identity permutation");
+    } else if (n > 0 && sigma < n) {
+        // key = window << 32 | (W - length): 64-bit stable radix sort
+        DevBuf keys((size_t)n * 8), keys_out((size_t)n * 8);
+        hipLaunchKernelGGL(k_sell_keys_win, dim3(grid_for(n)), dim3(256), 0, s, n, sigma,
+                           h->max_len, h->rowptr.as<int>(), keys.as<unsigned long long>());
+        hip_check(hipGetLastError(), "sell keys");
+        size_t tmp = 0;
+        rocprim::counting_iterator<int> iota(0);
+        const unsigned nb = 32 + bits_for((uint64_t)((n - 1) / sigma));
+        hip_check(rocprim::radix_sort_pairs(nullptr, tmp, keys.as<unsigned long long>(),
+                                            keys_out.as<unsigned long long>(), iota,
+                                            b.perm.as<int>(), (size_t)n, 0, nb, s),
+                  "radix_sort_pairs");
+        DevBuf work(tmp);
+        hip_check(rocprim::radix_sort_pairs(work.p, tmp, keys.as<unsigned long long>(),
+                                            keys_out.as<unsigned long long>(), iota,
+                                            b.perm.as<int>(), (size_t)n, 0, nb, s),
+                  "radix_sort_pairs");
+        sync(s);  // before the temporaries are freed
+    } else if (n > 0) {
         DevBuf keys((size_t)n * 4), keys_out((size_t)n * 4);
         hipLaunchKernelGGL(k_sell_keys, dim3(grid_for(n)), dim3(256), 0, s, n, h->max_len,
                            h->rowptr.as<int>(), keys.as<unsigned>());
@@ -466,9 +604,11 @@ void build_sell(const spmv_handle* h, Built& b, hipStream_t s) {
     DevBuf slots((size_t)std::max<int64_t>(ns, 1) * 8);
     if (ns > 0) {
         hipLaunchKernelGGL(k_sell_len, dim3(grid_for(S)), dim3(256), 0, s, n, S,
-                           h->rowptr.as<int>(), b.perm.as<int>(), b.sell_len.as<int>(),
-                           slots.as<int64_t>());
+                           h->rowptr.as<int>(), b.perm.as<int>(), b.sell_len.as<int>());
         hip_check(hipGetLastError(), "sell lengths");
+        hipLaunchKernelGGL(k_sell_width, dim3(grid_for(ns)), dim3(256), 0, s, ns,
+                           b.sell_len.as<int>(), slots.as<int64_t>());
+        hip_check(hipGetLastError(), "sell widths");
         hip_check(hipMemsetAsync(b.slice_ptr.p, 0, 8, s), "hipMemsetAsync");
         size_t tmp = 0;
         hip_check(rocprim::inclusive_scan(nullptr, tmp, slots.as<int64_t>(),
@@ -544,12 +684,15 @@ int64_t choose_width(const spmv_handle* h, int requested, std::vector<int>& hist
 }
 
 template <typename V>
-void build_split(const spmv_handle* h, int format, int requested, Built& b, hipStream_t s) {
+void build_split(const spmv_handle* h, int format, int requested, int sort_window, Built& b,
+                 hipStream_t s) {
     std::vector<int> hist;
     const int64_t K = choose_width(h, requested, hist, s);
     int64_t tail = 0;
     for (size_t l = (size_t)K + 1; l < hist.size(); ++l) tail += (int64_t)hist[l] * ((int64_t)l - K);
-    build_ell_part<V>(h, K, kEllBlock, b, s);
+    int sigma = sort_window;
+    if (sigma < 0) sigma = ell_pad_fraction(h, K, s) > kSortPadShare ? kEllBlock : 0;
+    build_ell_part<V>(h, K, kEllBlock, sigma, b, s);
     b.tail_nnz = tail;
     const int64_t n = h->n;
     b.tail_ptr.alloc((size_t)(n + 1) * 4);
@@ -599,6 +742,70 @@ void build_split(const spmv_handle* h, int format, int requested, Built& b, hipS
 
 void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s);
 
+// launch the kernels of one apply of `format` built in `b`
+hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* y, const void* x,
+                        double alpha, double beta, hipStream_t s) {
+    const bool f64 = h->dtype == SPMV_F64;
+    hipError_t e = hipSuccess;
+    switch (format) {
+        case SPMV_CSR: {
+            if (b.csr_balanced) {
+                TailView t{(int)h->n, h->nnz, nullptr, h->rowptr.as<int>(), b.chunk_row.as<int>(),
+                           h->col.as<int>(), h->val.p, b.window};
+                e = launch_scale(h->n, f64, y, beta, s);
+                if (e == hipSuccess) e = launch_tail(t, f64, y, x, alpha, s);
+                break;
+            }
+            CsrView a{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
+            e = launch_csr(a, h->subwave, h->csr_rows, f64, y, x, alpha, beta, s);
+            break;
+        }
+        case SPMV_ELLR:
+        case SPMV_HYB:
+        case SPMV_HEC: {
+            EllView a{(int)h->n, std::max<int64_t>(b.ell_bh, 1), b.ell_width * b.ell_bh,
+                      (int)b.ell_width, b.ell_len.as<int>(), b.ell_perm.as<int>(),
+                      b.ell_col.as<int>(), b.ell_val.p, b.window};
+            e = launch_ell(a, f64, y, x, alpha, beta, s);
+            if (e == hipSuccess && format != SPMV_ELLR && b.tail_nnz > 0) {
+                TailView t{(int)h->n, b.tail_nnz, b.tail_row.as<int>(), b.tail_ptr.as<int>(),
+                           b.chunk_row.as<int>(), b.tail_col.as<int>(), b.tail_val.p, b.window};
+                e = launch_tail(t, f64, y, x, alpha, s);
+            }
+            break;
+        }
+        case SPMV_SELL64: {
+            SellView a{(int)h->n, (int)b.nslices, b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
+                       b.perm.as<int>(), b.sell_col.as<int>(), b.sell_val.p, (int)b.nchunks,
+                       b.chunks.as<int4>()};
+            e = launch_sell(a, f64, y, x, alpha, beta, s);
+            break;
+        }
+    }
+    return e;
+}
+
+// device time of `launch` (ms): one warm-up call, then two timed calls
+template <typename F>
+float time_launches(F&& launch, hipStream_t s) {
+    hipEvent_t e0, e1;
+    hip_check(hipEventCreate(&e0), "hipEventCreate");
+    hip_check(hipEventCreate(&e1), "hipEventCreate");
+    hipError_t err = launch();
+    if (err == hipSuccess) err = hipEventRecord(e0, s);
+    for (int r = 0; r < 2 && err == hipSuccess; ++r) err = launch();
+    if (err == hipSuccess) err = hipEventRecord(e1, s);
+    if (err == hipSuccess) err = hipEventSynchronize(e1);
+    float ms = 1e30f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    hip_check(err, "kernel timing");
+    return ms;
+}
+
+
+
 // CSR kernel: time every shape of the vector kernel (lanes per row, rows
 // per lane group) and the entry-balanced kernel on the device and keep the
 // fastest (the apply does not depend on the values of x, so zeros are used).
@@ -608,9 +815,9 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     while (rule < 64 && rule < h->max_len) rule <<= 1;
     h->subwave = o.subwave ? o.subwave : rule;
     h->csr_rows = o.csr_rows ? o.csr_rows : 1;
-    b.csr_balanced = o.csr_kernel == SPMV_CSR_BALANCED;
     const bool want_vec = o.csr_kernel != SPMV_CSR_BALANCED;
     const bool want_bal = o.csr_kernel != SPMV_CSR_VECTOR && h->nnz > 0;
+    b.csr_balanced = !want_vec;
     if (want_bal) {
         // row of the first entry of every wave chunk, over the whole matrix
         b.tail_chunks = (h->nnz + kTailChunk - 1) / kTailChunk;
@@ -619,7 +826,10 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
                            b.tail_chunks, (int64_t)kTailChunk, h->rowptr.as<int>(),
                            b.chunk_row.as<int>());
         hip_check(hipGetLastError(), "chunk rows");
+        const bool bal = b.csr_balanced;
+        b.csr_balanced = true;  // the window is timed on the balanced kernel
         decide_window(h, SPMV_CSR, o.x_window, b, s);
+        b.csr_balanced = bal;
     }
     const bool tune_vec = want_vec && !(o.subwave && o.csr_rows);
     if (h->n == 0 || h->nnz == 0 || (!tune_vec && !(want_vec && want_bal))) {
@@ -628,51 +838,35 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     }
     DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
     hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
-    hipEvent_t e0, e1;
-    hip_check(hipEventCreate(&e0), "hipEventCreate");
-    hip_check(hipEventCreate(&e1), "hipEventCreate");
     const CsrView v{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
-    const TailView t{(int)h->n, h->nnz, nullptr, h->rowptr.as<int>(), b.chunk_row.as<int>(),
-                     h->col.as<int>(), h->val.p, b.window};
     const bool f64 = h->dtype == SPMV_F64;
     float best_ms = 1e30f;
-    hipError_t err = hipSuccess;
-    // one candidate: a warm-up launch, then two timed ones
-    auto time_it = [&](auto&& launch) -> float {
-        err = launch();
-        if (err == hipSuccess) err = hipEventRecord(e0, s);
-        for (int r = 0; r < 2 && err == hipSuccess; ++r) err = launch();
-        if (err == hipSuccess) err = hipEventRecord(e1, s);
-        if (err == hipSuccess) err = hipEventSynchronize(e1);
-        float ms = 1e30f;
-        if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
-        return ms;
-    };
     if (want_vec) {
         const int sw_lo = o.subwave ? o.subwave : (h->max_len <= 2 ? 1 : 2);
         const int sw_hi = o.subwave ? o.subwave : 64;
-        for (int sw = sw_lo; sw <= sw_hi && err == hipSuccess; sw <<= 1)
-            for (int rows = 1; rows <= kCsrRowsMax && err == hipSuccess; rows <<= 1) {
+        for (int sw = sw_lo; sw <= sw_hi; sw <<= 1)
+            for (int rows = 1; rows <= kCsrRowsMax; rows <<= 1) {
                 if (o.csr_rows && rows != o.csr_rows) continue;
-                const float ms = time_it(
-                    [&] { return launch_csr(v, sw, rows, f64, ys.p, xs.p, 1.0, 0.0, s); });
-                if (err == hipSuccess && ms < best_ms) best_ms = ms, h->subwave = sw, h->csr_rows = rows;
+                const float ms = time_launches(
+                    [&] { return launch_csr(v, sw, rows, f64, ys.p, xs.p, 1.0, 0.0, s); }, s);
+                if (ms < best_ms) best_ms = ms, h->subwave = sw, h->csr_rows = rows;
             }
     }
-    if (want_vec && want_bal && err == hipSuccess) {
-        const float ms = time_it([&] {
-            hipError_t e = launch_scale(h->n, f64, ys.p, 0.0, s);
-            return e == hipSuccess ? launch_tail(t, f64, ys.p, xs.p, 1.0, s) : e;
-        });
-        if (err == hipSuccess) b.csr_balanced = ms < best_ms;
+    if (want_vec && want_bal) {
+        b.csr_balanced = true;
+        const float ms = time_launches(
+            [&] { return launch_built(h, b, SPMV_CSR, ys.p, xs.p, 1.0, 0.0, s); }, s);
+        b.csr_balanced = ms < best_ms;
     }
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
-    hip_check(err, "CSR kernel tuning");
     if (!b.csr_balanced) b.chunk_row.release(), b.window = false, b.tail_chunks = 0;
 }
 
-// share of the entries the LDS window reaches, and whether to use it
+// Share of the entries the LDS window reaches, and whether to use it.  On
+// its own the window is only a candidate when at least half of the entries
+// lie within its reach (and, for ELL-R, rows are at most 128 long); the
+// apply is then timed with and without it and the faster kept (stencils
+// whose x reads already coalesce gain nothing from it).  `b` must hold the
+// built format.
 void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s) {
     const int64_t lead = h->dtype == SPMV_F64 ? EllWinLead<double>::value
                                               : EllWinLead<float>::value;
@@ -685,17 +879,23 @@ void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStrea
     }
     const unsigned long long c = read_scalar<unsigned long long>(cnt.p, s);
     b.band_fraction = h->nnz ? (double)c / (double)h->nnz : 0.0;
+    // window offsets are computed in 32 bits: rows and columns plus the
+    // window length must stay below 2^31
+    const bool fits = h->n < INT32_MAX - 2 * (int64_t)WinLen<float>::value;
     if (opt >= 0) {
-        // window offsets are computed in 32 bits: rows and columns plus the
-        // window length must stay below 2^31
-        b.window = opt == 1 && h->n < INT32_MAX - 2 * (int64_t)WinLen<float>::value;
+        b.window = opt == 1 && fits;
         return;
     }
-    if (h->n >= INT32_MAX - 2 * (int64_t)WinLen<float>::value) {
-        b.window = false;
-        return;
-    }
-    b.window = b.band_fraction >= 0.5 && (format != SPMV_ELLR || h->max_len <= 128);
+    b.window = fits && h->nnz > 0 && b.band_fraction >= 0.5 &&
+               (format != SPMV_ELLR || h->max_len <= 128);
+    if (!b.window) return;
+    DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
+    hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
+    auto run = [&] { return launch_built(h, b, format, ys.p, xs.p, 1.0, 0.0, s); };
+    const float with = time_launches(run, s);
+    b.window = false;
+    const float without = time_launches(run, s);
+    b.window = with < without;
 }
 
 int run_guarded(const std::function<void()>& body) {
@@ -831,8 +1031,18 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
     return run_guarded([&] {
         if (!h) fail(SPMV_ERR_STATE, "null handle");
         if (!valid_format(format)) fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
-        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, 0};
+        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0};
         if (opts) o = *opts;
+        if (o.sort_window < -1)
+            fail(SPMV_ERR_INVALID_ARG, "sort_window must be -1, 0 or positive (got %d)",
+                 o.sort_window);
+        if ((format == SPMV_CSR || format == SPMV_ELLR) && o.sort_window > 0)
+            fail(SPMV_ERR_INVALID_ARG, "sort_window applies to SELL-64, HYB and HEC only");
+        if ((format == SPMV_HYB || format == SPMV_HEC) && o.sort_window > 0 &&
+            (o.sort_window < 64 || o.sort_window > kEllBlock || kEllBlock % o.sort_window))
+            fail(SPMV_ERR_INVALID_ARG,
+                 "sort_window for HYB/HEC must be -1, 0 or a power of two in 64..%d (got %d)",
+                 kEllBlock, o.sort_window);
         if (o.x_window < -1 || o.x_window > 1)
             fail(SPMV_ERR_INVALID_ARG, "x_window must be -1, 0 or 1");
         if (o.csr_rows < 0 || o.csr_rows > kCsrRowsMax || (o.csr_rows & (o.csr_rows - 1)))
@@ -865,21 +1075,21 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
                      "budget of %.3g bytes",
                      need, (long long)h->n, (long long)S, (long long)W, (double)budget);
             if (f64)
-                build_ell_part<double>(h, W, 0, b, s);
+                build_ell_part<double>(h, W, 0, 0, b, s);
             else
-                build_ell_part<float>(h, W, 0, b, s);
+                build_ell_part<float>(h, W, 0, 0, b, s);
             decide_window(h, format, o.x_window, b, s);
             sync(s);
         } else if (format == SPMV_SELL64) {
             if (f64)
-                build_sell<double>(h, b, s);
+                build_sell<double>(h, o.sort_window, b, s);
             else
-                build_sell<float>(h, b, s);
+                build_sell<float>(h, o.sort_window, b, s);
         } else {
             if (f64)
-                build_split<double>(h, format, o.ell_width, b, s);
+                build_split<double>(h, format, o.ell_width, o.sort_window, b, s);
             else
-                build_split<float>(h, format, o.ell_width, b, s);
+                build_split<float>(h, format, o.ell_width, o.sort_window, b, s);
             decide_window(h, format, o.x_window, b, s);
         }
         h->fmt = std::move(b);
@@ -902,45 +1112,7 @@ int spmv_apply(spmv_t h, void* y, const void* x, double alpha, double beta, void
         return SPMV_ERR_INVALID_ARG;
     }
     if (h->n == 0) return SPMV_OK;
-    hipStream_t s = (hipStream_t)stream;
-    const bool f64 = h->dtype == SPMV_F64;
-    const Built& b = h->fmt;
-    hipError_t e = hipSuccess;
-    switch (h->format) {
-        case SPMV_CSR: {
-            if (b.csr_balanced) {
-                TailView t{(int)h->n, h->nnz, nullptr, h->rowptr.as<int>(), b.chunk_row.as<int>(),
-                           h->col.as<int>(), h->val.p, b.window};
-                e = launch_scale(h->n, f64, y, beta, s);
-                if (e == hipSuccess) e = launch_tail(t, f64, y, x, alpha, s);
-                break;
-            }
-            CsrView a{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
-            e = launch_csr(a, h->subwave, h->csr_rows, f64, y, x, alpha, beta, s);
-            break;
-        }
-        case SPMV_ELLR:
-        case SPMV_HYB:
-        case SPMV_HEC: {
-            EllView a{(int)h->n, std::max<int64_t>(b.ell_bh, 1), b.ell_width * b.ell_bh,
-                      (int)b.ell_width, b.ell_len.as<int>(), b.ell_col.as<int>(), b.ell_val.p,
-                      b.window};
-            e = launch_ell(a, f64, y, x, alpha, beta, s);
-            if (e == hipSuccess && h->format != SPMV_ELLR && b.tail_nnz > 0) {
-                TailView t{(int)h->n, b.tail_nnz, b.tail_row.as<int>(), b.tail_ptr.as<int>(),
-                           b.chunk_row.as<int>(), b.tail_col.as<int>(), b.tail_val.p, b.window};
-                e = launch_tail(t, f64, y, x, alpha, s);
-            }
-            break;
-        }
-        case SPMV_SELL64: {
-            SellView a{(int)h->n, (int)b.nslices, b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
-                       b.perm.as<int>(), b.sell_col.as<int>(), b.sell_val.p, (int)b.nchunks,
-                       b.chunks.as<int4>()};
-            e = launch_sell(a, f64, y, x, alpha, beta, s);
-            break;
-        }
-    }
+    const hipError_t e = launch_built(h, h->fmt, h->format, y, x, alpha, beta, (hipStream_t)stream);
     if (e != hipSuccess) {
         g_err = std::string("kernel launch failed: ") + hipGetErrorString(e);
         return SPMV_ERR_HIP;
@@ -999,6 +1171,7 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.x_window = b.window ? 1 : 0;
     i.csr_rows = h->csr_rows;
     i.csr_kernel = h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED : SPMV_CSR_VECTOR;
+    i.sort_window = b.sort_window;
     i.band_fraction = b.band_fraction;
     *out = i;
     return SPMV_OK;
@@ -1030,6 +1203,7 @@ int spmv_export(spmv_t h, int array, void* host_dst, int64_t capacity_bytes, int
             case SPMV_A_TAIL_PTR: if (f == SPMV_HEC) src = b.tail_ptr.p, sz = (h->n + 1) * 4; break;
             case SPMV_A_TAIL_COL: if (f == SPMV_HYB || f == SPMV_HEC) src = b.tail_col.p, sz = b.tail_nnz * 4; break;
             case SPMV_A_TAIL_VAL: if (f == SPMV_HYB || f == SPMV_HEC) src = b.tail_val.p, sz = b.tail_nnz * vs; break;
+            case SPMV_A_ELL_PERM: if (ell && b.ell_perm.p) src = b.ell_perm.p, sz = b.ell_rows * 4; break;
             default: fail(SPMV_ERR_INVALID_ARG, "unknown array id %d", array);
         }
         if (sz < 0) fail(SPMV_ERR_STATE, "array %d does not belong to the active format", array);

@@ -13,6 +13,8 @@ namespace spmv {
 // very long rows would otherwise keep one wave busy for the whole apply.
 constexpr int kSellSplitWidth = 256;
 constexpr int kSellChunk = 128;
+// default SELL-64 sort window (rows): the sort moves rows less than this
+constexpr int kSellSortWindow = 8192;
 
 // Tail entries per lane of the load-balanced tail kernel (one wave takes
 // 64 * kTailPerLane consecutive entries).
@@ -66,7 +68,8 @@ struct EllView {
     int64_t bh;       // rows per block = distance between a row's slots
     int64_t bstride;  // slots per block (width * bh)
     int width;        // slots per row (every row's slots j < width exist)
-    const int* len;   // [padded rows]
+    const int* len;   // [padded rows], by position
+    const int* perm;  // row at each position, or nullptr (position = row)
     const int* col;
     const void* val;
     bool window;      // stage x in LDS (banded matrices)

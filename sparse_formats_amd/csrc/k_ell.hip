@@ -25,6 +25,7 @@ namespace spmv {
 template <typename T>
 __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
                                              const int* __restrict__ len,
+                                             const int* __restrict__ perm,
                                              const int* __restrict__ col,
                                              const T* __restrict__ val, const T* __restrict__ x,
                                              T* __restrict__ y, T alpha, T beta) {
@@ -51,21 +52,24 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
         const int64_t o = (int64_t)j * bh;
         s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
     }
-    y[i] = axpby((s0 + s1) + (s2 + s3), alpha, beta, y + i);
+    const int64_t row = perm ? perm[i] : i;  // positions < n hold rows < n
+    y[row] = axpby((s0 + s1) + (s2 + s3), alpha, beta, y + row);
 }
 
 // ELLPACK-R with x staged in LDS (banded matrices).  Workgroup g (1024
 // threads) runs a contiguous range of row tiles of kEllWinTile rows, each
-// thread taking rows r0 + tid + 1024 * h for h < kEllWinTile / 1024.  Tile t
-// sees the window [r0 - lead, r0 - lead + WL), so a row reads its x entries
-// within about +-lead of itself from LDS and any others from global memory.
-// The window takes the whole LDS, so only 16 waves share a CU: each thread
-// keeps 16 entries of each of its rows in flight per round (values,
-// columns, then the x reads), and the elements entering the window for the
-// next tile are loaded while the current tile computes.
+// thread taking positions r0 + tid + 1024 * h for h < kEllWinTile / 1024.
+// Tile t sees the window [r0 - lead, r0 - lead + WL), so a row reads its x
+// entries within about +-lead of itself from LDS and any others from global
+// memory (a sorted ELL part only permutes rows inside a tile, which the
+// window covers).  The window takes the whole LDS, so only 16 waves share a
+// CU: each thread keeps 16 entries of each of its rows in flight per round
+// (values, columns, then the x reads), and the elements entering the window
+// for the next tile are loaded while the current tile computes.
 template <typename T>
-__global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bstride, int width,
+__global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bstride,
                                                   const int* __restrict__ len,
+                                                  const int* __restrict__ perm,
                                                   const int* __restrict__ col,
                                                   const T* __restrict__ val,
                                                   const T* __restrict__ x, T* __restrict__ y,
@@ -103,9 +107,9 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
         }
         T sum[H][2] = {};
         for (int j = 0; j < Lmax; j += B) {
-            // a full round without per-entry branches: slots past a row's
-            // end (up to the format width) hold column 0 / value 0 and are
-            // read but masked out of the sum
+            // a round of B entries: every load of the round is issued before
+            // the first use; lanes past their row's end issue none (so a
+            // wave never touches lines holding only padding) and add zero
             T vv[H][B];
             int cc[H][B];
 #pragma unroll
@@ -114,9 +118,14 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
                 const int64_t base = (i / bh) * bstride + i % bh;
 #pragma unroll
                 for (int u = 0; u < B; ++u) {
-                    const int64_t jj = min(j + u, width - 1);
-                    vv[h][u] = ld_nt(val + base + jj * bh);
-                    cc[h][u] = ld_nt(col + base + jj * bh);
+                    const int64_t jj = j + u;
+                    if (j + u < L[h]) {
+                        vv[h][u] = ld_nt(val + base + jj * bh);
+                        cc[h][u] = ld_nt(col + base + jj * bh);
+                    } else {
+                        vv[h][u] = T(0);
+                        cc[h][u] = 0;
+                    }
                 }
             }
 #pragma unroll
@@ -134,7 +143,10 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
         }
 #pragma unroll
         for (int h = 0; h < H; ++h)
-            if (row[h] < n) y[row[h]] = axpby(sum[h][0] + sum[h][1], alpha, beta, y + row[h]);
+            if (row[h] < n) {
+                const int64_t r = perm ? perm[row[h]] : row[h];
+                y[r] = axpby(sum[h][0] + sum[h][1], alpha, beta, y + r);
+            }
         if (t + 1 >= t1) break;
         lds_barrier();  // tile t is done with the slots reused now
 #pragma unroll
@@ -153,8 +165,8 @@ static hipError_t run_ell_win(const EllView& a, void* y, const void* x, double a
     const int64_t ntiles = ((int64_t)a.n + kEllWinTile - 1) / kEllWinTile;
     const int64_t g = std::min<int64_t>(ntiles, kWinGroups);
     hipLaunchKernelGGL(k_ell_win<T>, dim3((unsigned)g), dim3(1024), 0, stream, a.n, a.bh,
-                       a.bstride, a.width, a.len, a.col, (const T*)a.val, (const T*)x, (T*)y, (T)alpha,
-                       (T)beta, ntiles);
+                       a.bstride, a.len, a.perm, a.col, (const T*)a.val, (const T*)x, (T*)y,
+                       (T)alpha, (T)beta, ntiles);
     return hipGetLastError();
 }
 
@@ -167,12 +179,12 @@ hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double
                    : run_ell_win<float>(a, y, x, alpha, beta, stream);
     if (f64)
         hipLaunchKernelGGL(k_ell<double>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
-                           a.bh, a.bstride, a.len, a.col, (const double*)a.val, (const double*)x,
-                           (double*)y, alpha, beta);
+                           a.bh, a.bstride, a.len, a.perm, a.col, (const double*)a.val,
+                           (const double*)x, (double*)y, alpha, beta);
     else
         hipLaunchKernelGGL(k_ell<float>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
-                           a.bh, a.bstride, a.len, a.col, (const float*)a.val, (const float*)x,
-                           (float*)y, (float)alpha, (float)beta);
+                           a.bh, a.bstride, a.len, a.perm, a.col, (const float*)a.val,
+                           (const float*)x, (float*)y, (float)alpha, (float)beta);
     return hipGetLastError();
 }
 

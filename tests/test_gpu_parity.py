@@ -100,11 +100,15 @@ def test_sell_split_slices():
     L[[5, 700, 701, 4000, 8999]] = [3000, 2900, 257, 8999, 1000]
     a = random_csr(n, seed=45, lens=L)
     x_np, y0_np = vectors(n, 10)
-    M = sf.Matrix.from_csr(*to_dev(a), n=n).convert("sell64")
     x = torch.from_numpy(x_np).cuda()
     y0 = torch.from_numpy(y0_np).cuda()
-    for alpha, beta in AB:
-        check(a, x_np, y0_np, alpha, beta, apply(M, x, y0, alpha, beta), torch.float64)
+    for sigma in (-1, n, 1024):   # default window (8192 rows), all rows, small windows
+        M = sf.Matrix.from_csr(*to_dev(a), n=n).convert("sell64", sort_window=sigma)
+        assert M.info()["sort_window"] == {-1: 8192, n: n, 1024: 1024}[sigma]
+        for alpha, beta in AB:
+            check(a, x_np, y0_np, alpha, beta, apply(M, x, y0, alpha, beta), torch.float64,
+                  what="sell split sigma=%d" % sigma)
+        M.close()
 
 
 @pytest.mark.parametrize("name", ["c1", "ragged", "dups_unsorted", "every_len", "nnz0", "n1"])
@@ -129,16 +133,35 @@ def test_layouts_bit_exact(name, dtype):
     assert np.array_equal(M.export("sell_len"), ls)
     assert np.array_equal(M.export("sell_col"), sc)
     assert M.export("sell_val").tobytes() == sv.tobytes()
+    for sigma in (0, 1, 64, 128, 1000):
+        # SELL-64 sorted inside windows of sigma rows (0 keeps the order)
+        M.convert("sell64", sort_window=sigma)
+        perm, sp, ls, sc, sv = oracle.sell(a, sigma=max(sigma, 1))
+        assert M.info()["sort_window"] == (0 if sigma <= 1 or a.n <= 1 else min(sigma, a.n))
+        assert np.array_equal(M.export("sell_perm"), perm.astype(np.int32))
+        assert np.array_equal(M.export("sell_slice_ptr"), sp)
+        assert np.array_equal(M.export("sell_len"), ls)
+        assert np.array_equal(M.export("sell_col"), sc)
+        assert M.export("sell_val").tobytes() == sv.tobytes()
     for fmt in ("hyb", "hec"):
-        for req in (-1, 0, 3):
-            M.convert(fmt, ell_width=req)
+        for req, sigma in ((-1, 0), (0, 0), (3, 0), (-1, 64), (-1, 1024), (3, 256), (-1, -1)):
+            M.convert(fmt, ell_width=req, sort_window=sigma)
             K = oracle.hyb_width(a, req)
             assert M.info()["ell_width"] == K
             assert M.info()["ell_stride"] == oracle.ELL_BLOCK_SPLIT
-            oc, ov, ol = oracle.ell(a, K, block=oracle.ELL_BLOCK_SPLIT)
+            if sigma < 0:   # sorted inside whole blocks when >10% padding would be read
+                sigma = oracle.ELL_BLOCK_SPLIT if oracle.ell_pad_fraction(a, K) > 0.1 else 0
+            assert M.info()["sort_window"] == (sigma if a.n > 0 else 0)
+            oc, ov, ol, op = oracle.ell(a, K, block=oracle.ELL_BLOCK_SPLIT, sigma=sigma,
+                                        with_perm=True)
             assert np.array_equal(M.export("ell_col"), oc)
             assert M.export("ell_val").tobytes() == ov.tobytes()
             assert np.array_equal(M.export("ell_len"), ol)
+            if sigma > 0 and a.n > 0:
+                assert np.array_equal(M.export("ell_perm"), op.astype(np.int32))
+            else:
+                with pytest.raises(sf.SpmvError):
+                    M.export("ell_perm")
             trow, tptr, tcol, tval = oracle.tail(a, K)
             assert M.info()["tail_nnz"] == tcol.size
             if fmt == "hyb":
@@ -247,17 +270,19 @@ def test_beta_zero_ignores_nan_y(fmt):
 
 
 def test_determinism():
+    """Kernels without atomics (vector CSR, ELL-R) repeat bit for bit; the
+    others add partial sums with atomics, so only the tolerance holds."""
     a = MATS["long_spans"]()
     x_np, _ = vectors(a.n, 14)
     x = torch.from_numpy(x_np).cuda()
-    for fmt in FORMATS:
-        M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt)
+    for fmt, kw in [(f, {}) for f in FORMATS] + [("csr", dict(csr_kernel="vector"))]:
+        M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt, **kw)
         y1 = torch.zeros(a.n, dtype=torch.float64, device="cuda")
         y2 = torch.zeros_like(y1)
         M.apply(y1, x)
         M.apply(y2, x)
         torch.cuda.synchronize()
-        if fmt in ("csr", "ellr"):
+        if fmt == "ellr" or (fmt == "csr" and M.info()["csr_kernel"] == "vector"):
             assert torch.equal(y1, y2), fmt
         else:
             ref, sc = oracle.spmv(a, x_np)
@@ -351,13 +376,17 @@ def test_x_window_forced(fmt, name, dtype, win):
 
 
 def test_x_window_auto_choice():
+    """Auto: a candidate when half the entries are within reach, then timed."""
     a = _banded()
     M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("hec")
     i = M.info()
-    assert i["x_window"] == 1 and 0.7 < i["band_fraction"] < 0.9
-    b = MATS["ragged"]()
-    M2 = sf.Matrix.from_csr(*to_dev(b), n=b.n).convert("hyb")
-    assert M2.info()["x_window"] == (1 if M2.info()["band_fraction"] >= 0.5 else 0)
+    assert 0.7 < i["band_fraction"] < 0.9 and i["x_window"] in (0, 1)
+    # far columns everywhere: never a candidate
+    far = random_csr(300_000, seed=48, density=2e-5)
+    M2 = sf.Matrix.from_csr(*to_dev(far), n=far.n).convert("hyb")
+    assert M2.info()["band_fraction"] < 0.5 and M2.info()["x_window"] == 0
+    M2.convert("csr", csr_kernel="balanced")
+    assert M2.info()["x_window"] == 0
     with pytest.raises(sf.SpmvError):
         M2.convert("hyb", x_window=2)
 
@@ -415,3 +444,43 @@ def test_csr_kernel_choice():
         with pytest.raises(sf.SpmvError):
             M.convert("csr", csr_kernel=3)
         M.close()
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("name", ["c1", "ragged", "every_len", "long_spans", "box27", "nnz0",
+                                  "n1", "dups_unsorted", "banded"])
+@pytest.mark.parametrize("fmt,sigma,win", [("sell64", 0, -1), ("sell64", 64, -1),
+                                           ("sell64", 4096, -1), ("hyb", 64, 0), ("hyb", 1024, 1),
+                                           ("hec", 1024, 0), ("hec", 256, 1)])
+def test_windowed_sort_parity(fmt, sigma, win, name, dtype):
+    """Formats whose rows are sorted only inside windows (y written through
+    the permutation; the LDS x window on or off for the sorted ELL part)."""
+    a = WINDOW_MATS[name]()
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    x_np, y0_np = vectors(a.n, 19)
+    x_np, y0_np = x_np.astype(npdt), y0_np.astype(npdt)
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n).convert(fmt, sort_window=sigma,
+                                                             x_window=win)
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    rows = None if a.n < 100_000 else np.unique(np.concatenate(
+        [np.arange(0, a.n, 97), np.argsort(a.row_lengths())[-200:]]))
+    for alpha, beta in AB[:3]:
+        y = apply(M, x, y0, alpha, beta)
+        check(a, x_np, y0_np, alpha, beta, y, dtype, rows=rows,
+              what="%s sort=%d win=%d %s a=%g b=%g" % (fmt, sigma, win, name, alpha, beta))
+    M.close()
+
+
+def test_sort_window_errors():
+    a = MATS["ragged"]()
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
+    for fmt, sigma in (("hyb", 100), ("hec", 2048), ("hyb", 32), ("ellr", 64), ("csr", 64),
+                       ("sell64", -2)):
+        with pytest.raises(sf.SpmvError):
+            M.convert(fmt, sort_window=sigma)
+    M.convert("sell64", sort_window=7)   # any window works for SELL-64
+    assert M.info()["sort_window"] == 7
+    M.close()
