@@ -1,27 +1,19 @@
-// Irregular part of HYB (COO) and HEC (CSR): y += alpha * A_tail * x with the
-// work split by entries, not by rows.
+// Irregular part of HYB (COO) and HEC (CSR), and CSR run by entries:
+// y += alpha * A_tail * x with the work split by entries, not by rows.
 //
 // "Load-balancing Sparse Matrix Vector Product Kernels on GPUs" (abstract)
 // balances COO/CSR work independently of the row lengths; the Trilinos
 // "unpackAndCombine" discussion (few long rows) puts the long rows in a
 // separate launch and combines partial results with atomic +=.  Here the
-// tail entries, ordered by row, are cut into chunks of 64 * E consecutive
-// entries, one chunk per wave and E consecutive entries per lane:
-//   1. each lane walks its E entries in order and adds every row segment
-//      that starts and ends inside its run straight into y;
-//   2. the lane's first and last segments may continue in neighbouring
-//      lanes: a segmented inclusive scan over the lanes (keyed by row, which
-//      is non-decreasing along the chunk) sums them, and the lane that
-//      closes a row inside the wave adds it;
-//   3. every addition into y is a device-scope atomic without return value,
-//      so no lane ever waits for y (a plain read-modify-write would stall
-//      the wave on the load), and rows shared by neighbouring waves need no
-//      special case.
-// HYB reads the row of every entry.  HEC finds rows in its row pointer:
-// each lane binary-searches the row of its first entry between the rows of
-// its chunk's first and last entries (computed once when the format is
-// built), then reads the next eight row starts at once and places its
-// entries among them, searching again only if its run crosses more rows.
+// tail entries, ordered by row, are cut into chunks of 512 consecutive
+// entries, one chunk per wave, each run in passes of 64 * E consecutive
+// entries with E per lane (HYB: E = 2 for fp64, 4 for fp32, so a pass is one
+// 16-byte load per lane; CSR tails: one pass of E = 8).  In every pass the
+// lanes add the row segments inside their runs, a segmented scan over the
+// lanes sums the segments that cross lanes, and every addition into y is a
+// device-scope atomic without return value (no lane ever waits for y, and
+// rows shared by passes or waves need no special case).  HYB reads the row
+// of every entry; the CSR forms search the row pointer.
 #include <algorithm>
 
 #include "common.h"
@@ -29,48 +21,57 @@
 
 namespace spmv {
 
-// Each lane reads its run with 16-byte loads at a 64-byte lane stride, so one
-// load instruction touches every line of the wave's chunk partially and the
-// next three complete them: these loads must allocate in the caches (no
-// nontemporal hint), or each line is fetched from L2 four times.
+// A wave's chunk of 64 * kTailPerLane consecutive entries is processed in
+// P passes of 64 * E consecutive entries, E = 16 / sizeof(T) per lane: one
+// 16-byte load per lane brings the values of a pass, so a load instruction
+// covers 1 KiB of contiguous values (whole cache lines) and the lanes of a
+// pass read the entries of neighbouring rows side by side (for banded
+// matrices their x reads share lines too).  All loads of a chunk are issued
+// before the first use.
 typedef double d2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int i2_t __attribute__((ext_vector_type(2)));
 typedef int i4_t __attribute__((ext_vector_type(4)));
 
+// COO tails (rows stored) run in passes of one 16-byte value load per lane;
+// CSR tails keep one pass of kTailPerLane entries per lane, which needs a
+// single row search per lane (the cross-lane work of a pass -- the scan and
+// the search -- would otherwise be paid P times).
+template <typename T, bool kCoo>
+struct TailShape {
+    static constexpr int E = kCoo ? 16 / (int)sizeof(T) : kTailPerLane;  // per lane and pass
+    static constexpr int P = kTailPerLane / E;                           // passes per chunk
+};
+
+// E consecutive elements with 16-byte loads (E * sizeof a multiple of 16
+// bytes, p 16-byte aligned)
 template <int E>
-__device__ __forceinline__ void load_run(const double* p, double (&v)[E]) {
-    const d2_t* q = reinterpret_cast<const d2_t*>(p);
+__device__ __forceinline__ void load_vec(const double* p, double (&v)[E]) {
 #pragma unroll
     for (int k = 0; k < E / 2; ++k) {
-        const d2_t t = q[k];
-        v[2 * k] = t.x;
-        v[2 * k + 1] = t.y;
+        const d2_t t = reinterpret_cast<const d2_t*>(p)[k];
+        v[2 * k] = t.x, v[2 * k + 1] = t.y;
     }
 }
-
 template <int E>
-__device__ __forceinline__ void load_run(const float* p, float (&v)[E]) {
-    const f4_t* q = reinterpret_cast<const f4_t*>(p);
+__device__ __forceinline__ void load_vec(const float* p, float (&v)[E]) {
 #pragma unroll
     for (int k = 0; k < E / 4; ++k) {
-        const f4_t t = q[k];
-        v[4 * k] = t.x;
-        v[4 * k + 1] = t.y;
-        v[4 * k + 2] = t.z;
-        v[4 * k + 3] = t.w;
+        const f4_t t = reinterpret_cast<const f4_t*>(p)[k];
+        v[4 * k] = t.x, v[4 * k + 1] = t.y, v[4 * k + 2] = t.z, v[4 * k + 3] = t.w;
     }
 }
-
 template <int E>
-__device__ __forceinline__ void load_run(const int* p, int (&v)[E]) {
-    const i4_t* q = reinterpret_cast<const i4_t*>(p);
+__device__ __forceinline__ void load_vec(const int* p, int (&v)[E]) {
+    if constexpr (E == 2) {
+        const i2_t t = *reinterpret_cast<const i2_t*>(p);
+        v[0] = t.x, v[1] = t.y;
+    } else {
 #pragma unroll
-    for (int k = 0; k < E / 4; ++k) {
-        const i4_t t = q[k];
-        v[4 * k] = t.x;
-        v[4 * k + 1] = t.y;
-        v[4 * k + 2] = t.z;
-        v[4 * k + 3] = t.w;
+        for (int k = 0; k < E / 4; ++k) {
+            const i4_t t = reinterpret_cast<const i4_t*>(p)[k];
+            v[4 * k] = t.x, v[4 * k + 1] = t.y, v[4 * k + 2] = t.z, v[4 * k + 3] = t.w;
+        }
     }
 }
 
@@ -87,114 +88,104 @@ __device__ __forceinline__ int row_of(const int* __restrict__ ptr, int lo, int h
     return lo;
 }
 
-// Registers of one lane's run: values, columns and (HYB) rows.
-template <typename T>
+// Registers of one lane's share of a chunk: values, columns and rows of its
+// E entries in each of the P passes.
+template <typename T, bool kCoo>
 struct TailRun {
-    T v[kTailPerLane];
-    int c[kTailPerLane];
-    int r[kTailPerLane];
-    int cnt;  // entries of this lane (0 for lanes past the end)
+    static constexpr int E = TailShape<T, kCoo>::E, P = TailShape<T, kCoo>::P;
+    T v[P][E];
+    int c[P][E];
+    int r[P][E];
+    int cnt[P];  // entries of this lane in each pass (0 past the end)
 };
 
-// Issue the loads of one wave's chunk of 64 * E tail entries (chunk index w).
+__device__ __forceinline__ int64_t pass_entry(int64_t w, int p, int lane, int E) {
+    return w * kTailChunk + (int64_t)p * 64 * E + (int64_t)lane * E;
+}
+
+// Issue the loads of chunk w (values, columns and, for HYB, rows).
 template <typename T, bool kCoo>
 __device__ __forceinline__ void tail_fetch(int64_t w, int lane, int64_t nnz,
                                            const int* __restrict__ trow,
                                            const int* __restrict__ col,
-                                           const T* __restrict__ val, TailRun<T>& R) {
-    constexpr int E = kTailPerLane;
+                                           const T* __restrict__ val, TailRun<T, kCoo>& R) {
+    constexpr int E = TailShape<T, kCoo>::E, P = TailShape<T, kCoo>::P;
     constexpr int kNone = 0x7fffffff;
-    const int64_t e0 = w * kTailChunk + (int64_t)lane * E;
-    R.cnt = e0 < nnz ? (int)min<int64_t>(E, nnz - e0) : 0;
-    if (R.cnt == E) {
-        load_run<E>(val + e0, R.v);
-        load_run<E>(col + e0, R.c);
-        if constexpr (kCoo) load_run<E>(trow + e0, R.r);
-    } else {
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
-            R.v[k] = k < R.cnt ? val[e0 + k] : T(0);
-            R.c[k] = k < R.cnt ? col[e0 + k] : 0;
-            if constexpr (kCoo) R.r[k] = k < R.cnt ? trow[e0 + k] : kNone;
-        }
-    }
-}
-
-// Finish the chunk: rows (HEC), products, segmented sums and additions into
-// y.  With kWin, x entries inside [wlo, wlo + WinLen) come from the LDS
-// window `win` (element q at slot q mod WinLen), the rest from global memory.
-// Window path: issue the global loads of the x entries outside the window
-// (xg, flagged in far).  They must go out before the next chunk's loads:
-// loads complete in order, so waiting on them would drain that prefetch.
-template <typename T>
-__device__ __forceinline__ void tail_far_gather(const T* __restrict__ x, int64_t wlo,
-                                                const TailRun<T>& R, bool (&far)[kTailPerLane],
-                                                T (&xg)[kTailPerLane]) {
-#pragma unroll
-    for (int k = 0; k < kTailPerLane; ++k) {
-        far[k] = k < R.cnt && (uint32_t)(R.c[k] - (int)wlo) >= (uint32_t)WinLen<T>::value;
-        xg[k] = far[k] ? x[R.c[k]] : T(0);
-    }
-}
-
-template <typename T, bool kCoo, bool kWin>
-__device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
-                                            const int* __restrict__ tptr,
-                                            const int* __restrict__ chunk_row,
-                                            const T* __restrict__ x, T* __restrict__ y, T alpha,
-                                            const T* win, const bool (&far)[kTailPerLane],
-                                            const T (&xg)[kTailPerLane], TailRun<T>& R) {
-    constexpr int E = kTailPerLane;
-    constexpr int kNone = 0x7fffffff;
-    if (w * kTailChunk >= nnz) return;  // the whole wave leaves together
-    const int64_t e0 = w * kTailChunk + (int64_t)lane * E;
-    const int cnt = R.cnt;
-    int* r = R.r;
-    if constexpr (!kCoo) {
-        const int lo = chunk_row[w], hi = chunk_row[w + 1];
-        int cur = cnt > 0 ? row_of(tptr, lo, hi, e0) : kNone;
-        const int base = cnt > 0 ? cur : lo;  // inactive lanes read in-range rows
-        // starts of the next E rows (clamped to the chunk's last row)
-        int nxt[E];
-#pragma unroll
-        for (int j = 0; j < E; ++j) nxt[j] = tptr[min(base + 1 + j, hi + 1)];
-#pragma unroll
-        for (int k = 0; k < E; ++k) {
-            int adv = 0;
-#pragma unroll
-            for (int j = 0; j < E; ++j) adv += nxt[j] <= e0 + k;
-            r[k] = k < cnt ? cur + adv : kNone;
-        }
-        // a run crossing more than E row starts (rows with no tail entries
-        // in between): place the remaining entries by binary search
-        if (cnt > 0 && nxt[E - 1] <= e0 + cnt - 1) {
-            int c2 = cur + E;
+    for (int p = 0; p < P; ++p) {
+        const int64_t e0 = pass_entry(w, p, lane, E);
+        R.cnt[p] = e0 < nnz ? (int)min<int64_t>(E, nnz - e0) : 0;
+        if (R.cnt[p] == E) {
+            load_vec<E>(val + e0, R.v[p]);
+            load_vec<E>(col + e0, R.c[p]);
+            if constexpr (kCoo) load_vec<E>(trow + e0, R.r[p]);
+        } else {
 #pragma unroll
             for (int k = 0; k < E; ++k) {
-                if (k < cnt && e0 + k >= nxt[E - 1]) {
-                    if (e0 + k >= tptr[c2 + 1]) c2 = row_of(tptr, c2 + 1, hi, e0 + k);
-                    r[k] = c2;
-                }
+                R.v[p][k] = k < R.cnt[p] ? val[e0 + k] : T(0);
+                R.c[p][k] = k < R.cnt[p] ? col[e0 + k] : 0;
+                if constexpr (kCoo) R.r[p][k] = k < R.cnt[p] ? trow[e0 + k] : kNone;
             }
         }
     }
-    T p[E];
+}
+
+// Rows of chunk w's entries from the CSR tail pointer (HEC, and CSR run by
+// entries; one pass of E entries per lane).  Each lane binary-searches the
+// row of its first entry between the rows of the chunk's first and last
+// entries (stored when the format is built), then reads the next E row
+// starts at once and places its entries among them, searching again only
+// if its run crosses more rows (rows without entries in between).
+template <typename T>
+__device__ __forceinline__ void tail_rows(int64_t w, int lane, const int* __restrict__ tptr,
+                                          const int* __restrict__ chunk_row,
+                                          TailRun<T, false>& R) {
+    constexpr int E = TailShape<T, false>::E;
+    constexpr int kNone = 0x7fffffff;
+    const int64_t e0 = pass_entry(w, 0, lane, E);
+    const int cnt = R.cnt[0];
+    int* r = R.r[0];
+    const int lo = chunk_row[w], hi = chunk_row[w + 1];
+    const int cur = cnt > 0 ? row_of(tptr, lo, hi, e0) : kNone;
+    const int base = cnt > 0 ? cur : lo;  // inactive lanes read in-range rows
+    int nxt[E];  // starts of the next E rows (clamped to the chunk's last row)
+#pragma unroll
+    for (int j = 0; j < E; ++j) nxt[j] = tptr[min(base + 1 + j, hi + 1)];
 #pragma unroll
     for (int k = 0; k < E; ++k) {
-        T xv = T(0);
-        if (k < cnt) {
-            if constexpr (kWin) {
-                // the slot read is always in range
-                const T xw = win[R.c[k] % WinLen<T>::value];
-                xv = far[k] ? xg[k] : xw;
-            } else {
-                xv = x[R.c[k]];
+        int adv = 0;
+#pragma unroll
+        for (int j = 0; j < E; ++j) adv += nxt[j] <= e0 + k;
+        r[k] = k < cnt ? cur + adv : kNone;
+    }
+    if (cnt > 0 && nxt[E - 1] <= e0 + cnt - 1) {
+        int c2 = cur + E;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            if (k < cnt && e0 + k >= nxt[E - 1]) {
+                if (e0 + k >= tptr[c2 + 1]) c2 = row_of(tptr, c2 + 1, hi, e0 + k);
+                r[k] = c2;
             }
         }
-        p[k] = R.v[k] * xv;
     }
+}
 
-    // 1. walk the run; rows that start and end inside it are added directly
+// Add the products p of one pass into y.  The lane's E entries are
+// consecutive and ordered by row; the wave's 64 * E entries too.
+//   1. each lane walks its entries and adds the rows that start and end
+//      inside its run;
+//   2. the lane's last segment may continue in the next lanes: a segmented
+//      inclusive scan over the lanes (keyed by row) sums it, and the lane
+//      where the row ends (or the last lane) adds it; a lane's first
+//      segment that began in an earlier lane is added with the earlier
+//      lanes' scan value;
+//   3. every addition into y is a device-scope atomic without return value,
+//      so no lane waits for y and rows shared with other passes or waves
+//      need no special case.
+template <typename T, int E>
+__device__ __forceinline__ void pass_sum(int lane, int cnt, const int (&r)[E], const T (&p)[E],
+                                         T* __restrict__ y, T alpha) {
+    constexpr int kNone = 0x7fffffff;
     const int head_row = r[0];
     T head_sum = 0;
     bool split = false;
@@ -218,8 +209,6 @@ __device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
     }
     const int key = cnt > 0 ? cur : kNone;  // row of the lane's last segment
     T sum = acc;
-
-    // 2. segmented inclusive scan of the last segments across the wave
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
         const int k2 = __shfl_up(key, d);
@@ -229,13 +218,65 @@ __device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
     const int prev_key = __shfl_up(key, 1);
     const T prev_sum = __shfl_up(sum, 1);
     const int next_first = __shfl_down(head_row, 1);
-
-    // 3. add what closes here
     if (split) {
         const T tot = head_sum + ((lane > 0 && prev_key == head_row) ? prev_sum : T(0));
         atomic_add(y + head_row, alpha * tot);
     }
     if (cnt > 0 && (lane == 63 || next_first != key)) atomic_add(y + key, alpha * sum);
+}
+
+// Window path: issue the global loads of the x entries outside the window
+// (xg, flagged in far).  They must go out before the next chunk's loads:
+// loads complete in order, so waiting on them would drain that prefetch.
+template <typename T, bool kCoo>
+__device__ __forceinline__ void tail_far_gather(const T* __restrict__ x, int64_t wlo,
+                                                const TailRun<T, kCoo>& R,
+                                                bool (&far)[TailShape<T, kCoo>::P][TailShape<T, kCoo>::E],
+                                                T (&xg)[TailShape<T, kCoo>::P][TailShape<T, kCoo>::E]) {
+    constexpr int E = TailShape<T, kCoo>::E, P = TailShape<T, kCoo>::P;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            far[p][k] = k < R.cnt[p] &&
+                        (uint32_t)(R.c[p][k] - (int)wlo) >= (uint32_t)WinLen<T>::value;
+            xg[p][k] = far[p][k] ? x[R.c[p][k]] : T(0);
+        }
+}
+
+// Finish chunk w: rows (CSR tail), products, sums into y.  With kWin, x
+// entries inside the window come from LDS (element q at slot q mod
+// WinLen), the others were gathered into xg.
+template <typename T, bool kCoo, bool kWin>
+__device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
+                                            const int* __restrict__ tptr,
+                                            const int* __restrict__ chunk_row,
+                                            const T* __restrict__ x, T* __restrict__ y, T alpha,
+                                            const T* win,
+                                            const bool (&far)[TailShape<T, kCoo>::P][TailShape<T, kCoo>::E],
+                                            const T (&xg)[TailShape<T, kCoo>::P][TailShape<T, kCoo>::E],
+                                            TailRun<T, kCoo>& R) {
+    constexpr int E = TailShape<T, kCoo>::E, P = TailShape<T, kCoo>::P;
+    if (w * kTailChunk >= nnz) return;  // the whole wave leaves together
+    if constexpr (!kCoo) tail_rows<T>(w, lane, tptr, chunk_row, R);
+    T pr[P][E];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            T xv = T(0);
+            if (k < R.cnt[p]) {
+                if constexpr (kWin) {
+                    const T xw = win[R.c[p][k] % WinLen<T>::value];  // slot always in range
+                    xv = far[p][k] ? xg[p][k] : xw;
+                } else {
+                    xv = x[R.c[p][k]];
+                }
+            }
+            pr[p][k] = R.v[p][k] * xv;
+        }
+#pragma unroll
+    for (int p = 0; p < P; ++p) pass_sum<T, E>(lane, R.cnt[p], R.r[p], pr[p], y, alpha);
 }
 
 template <typename T, bool kCoo>
@@ -246,12 +287,13 @@ __global__ __launch_bounds__(256) void k_tail(int n, int64_t nnz, const int* __r
                                               const T* __restrict__ val,
                                               const T* __restrict__ x, T* __restrict__ y,
                                               T alpha) {
+    constexpr int E = TailShape<T, kCoo>::E, P = TailShape<T, kCoo>::P;
     const int64_t w = xcd_tile(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
     if (w * kTailChunk >= nnz) return;
-    TailRun<T> R;
+    TailRun<T, kCoo> R;
     tail_fetch<T, kCoo>(w, threadIdx.x & 63, nnz, trow, col, val, R);
-    bool far[kTailPerLane] = {};
-    T xg[kTailPerLane] = {};
+    bool far[P][E] = {};
+    T xg[P][E] = {};
     tail_finish<T, kCoo, false>(w, threadIdx.x & 63, nnz, tptr, chunk_row, x, y, alpha, nullptr,
                                 far, xg, R);
 }
@@ -296,13 +338,13 @@ __global__ __launch_bounds__(1024) void k_tail_win(int n, int64_t nnz,
         lds_barrier();
         prev_whi = whi;
         const int64_t w0 = s * kTailStepChunks + (int64_t)wave * CPW;
-        TailRun<T> run[2];
+        TailRun<T, kCoo> run[2];
         tail_fetch<T, kCoo>(w0, lane, nnz, trow, col, val, run[0]);
 #pragma unroll
         for (int k = 0; k < CPW; ++k) {
-            bool far[kTailPerLane];
-            T xg[kTailPerLane];
-            tail_far_gather<T>(x, wlo, run[k & 1], far, xg);
+            bool far[TailShape<T, kCoo>::P][TailShape<T, kCoo>::E];
+            T xg[TailShape<T, kCoo>::P][TailShape<T, kCoo>::E];
+            tail_far_gather<T, kCoo>(x, wlo, run[k & 1], far, xg);
             if (k + 1 < CPW)
                 tail_fetch<T, kCoo>(w0 + k + 1, lane, nnz, trow, col, val, run[(k + 1) & 1]);
             tail_finish<T, kCoo, true>(w0 + k, lane, nnz, tptr, chunk_row, x, y, alpha, win, far,
