@@ -90,6 +90,55 @@ __device__ __forceinline__ T group_sum(T v) {
     return v;
 }
 
+// DPP moves with an explicit value for lanes that have no source: lanes
+// whose source lies outside the pattern (or whose row is not in ROWS) get
+// `old`.  Controls (gfx9): row_shr:d = 0x110 + d inside rows of 16 lanes,
+// row_bcast:15 = 0x142 (lane 15 of each row to the next row), row_bcast:31 =
+// 0x143 (lane 31 to rows 2 and 3), wave_shr:1 = 0x138 (lane i - 1 across the
+// wave), wave_shl:1 = 0x130 (lane i + 1).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_or(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or(float old, float v) {
+    return __int_as_float(dpp_or<CTRL, ROWS>(__float_as_int(old), __float_as_int(v)));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_or(double old, double v) {
+    const int64_t o = __double_as_longlong(old), b = __double_as_longlong(v);
+    const int lo = dpp_or<CTRL, ROWS>((int)(o & 0xffffffff), (int)(b & 0xffffffff));
+    const int hi = dpp_or<CTRL, ROWS>((int)(o >> 32), (int)(b >> 32));
+    return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+// Segmented inclusive scan over the wave: lanes with equal keys form the
+// segments (keys must be non-decreasing over the lanes and >= 0); each lane
+// gets the sum of v over its segment up to itself.  Hillis-Steele steps of
+// 1, 2, 4, 8 lanes inside rows of 16, then the last lane of row 0 (and 2)
+// into rows 1 (and 3), then lane 31 into rows 2 and 3.  With monotone keys a
+// source lane with the same key means every lane in between has it too, so
+// each conditional add joins two adjacent pieces of one segment.
+template <typename T>
+__device__ __forceinline__ T segmented_scan(int key, T v) {
+#define SPMV_SEG_STEP(CTRL, ROWS)                         \
+    {                                                     \
+        const int k2 = dpp_or<CTRL, ROWS>(-1, key);       \
+        const T s2 = dpp_or<CTRL, ROWS>(T(0), v);         \
+        if (k2 == key) v += s2;                           \
+    }
+    SPMV_SEG_STEP(0x111, 0xF)
+    SPMV_SEG_STEP(0x112, 0xF)
+    SPMV_SEG_STEP(0x114, 0xF)
+    SPMV_SEG_STEP(0x118, 0xF)
+    SPMV_SEG_STEP(0x142, 0xA)
+    SPMV_SEG_STEP(0x143, 0xC)
+#undef SPMV_SEG_STEP
+    return v;
+}
+
 // Workgroup barrier for LDS hand-offs that leaves global loads in flight:
 // waits only for this wave's LDS operations, then s_barrier.  A plain
 // __syncthreads() also waits for every outstanding global load, which would

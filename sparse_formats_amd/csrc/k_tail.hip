@@ -208,18 +208,12 @@ __device__ __forceinline__ void pass_sum(int lane, int cnt, const int (&r)[E], c
         }
     }
     const int key = cnt > 0 ? cur : kNone;  // row of the lane's last segment
-    T sum = acc;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int k2 = __shfl_up(key, d);
-        const T s2 = __shfl_up(sum, d);
-        if (lane >= d && k2 == key) sum += s2;
-    }
-    const int prev_key = __shfl_up(key, 1);
-    const T prev_sum = __shfl_up(sum, 1);
-    const int next_first = __shfl_down(head_row, 1);
+    const T sum = segmented_scan(key, acc);
+    const int prev_key = dpp_or<0x138, 0xF>(-1, key);    // lane - 1 (none for lane 0)
+    const T prev_sum = dpp_or<0x138, 0xF>(T(0), sum);
+    const int next_first = dpp_or<0x130, 0xF>(-1, head_row);  // lane + 1 (none for 63)
     if (split) {
-        const T tot = head_sum + ((lane > 0 && prev_key == head_row) ? prev_sum : T(0));
+        const T tot = head_sum + (prev_key == head_row ? prev_sum : T(0));
         atomic_add(y + head_row, alpha * tot);
     }
     if (cnt > 0 && (lane == 63 || next_first != key)) atomic_add(y + key, alpha * sum);
