@@ -105,8 +105,8 @@ struct Built {
     int64_t nchunks = 0;
     DevBuf chunks;
     // tail of HYB / HEC
-    int64_t tail_nnz = 0, tail_chunks = 0;
-    DevBuf tail_row, tail_ptr, tail_col, tail_val, chunk_row;
+    int64_t tail_nnz = 0, tail_runs = 0;
+    DevBuf tail_row, tail_ptr, tail_col, tail_val, run_row;
     // CSR: entry-balanced kernel (chunk_row over the whole matrix)
     bool csr_balanced = false;
     // x staged in LDS by the ELL / tail kernels
@@ -117,7 +117,7 @@ struct Built {
         return ell_col.bytes + ell_val.bytes + ell_len.bytes + ell_perm.bytes + slice_ptr.bytes +
                sell_len.bytes +
                perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + tail_row.bytes +
-               tail_ptr.bytes + tail_col.bytes + tail_val.bytes + chunk_row.bytes;
+               tail_ptr.bytes + tail_col.bytes + tail_val.bytes + run_row.bytes;
     }
 };
 
@@ -446,25 +446,17 @@ __global__ void k_tail_fill(int64_t n, int K, const int* __restrict__ rowptr,
     }
 }
 
-// chunk_row[k] = row holding tail entry k * chunk (k < nchunks); last = n - 1
-__global__ void k_chunk_rows(int64_t n, int64_t nchunks, int64_t chunk,
-                             const int* __restrict__ tptr, int* __restrict__ out) {
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k <= nchunks;
-         k += (int64_t)gridDim.x * blockDim.x) {
-        if (k == nchunks) {
-            out[k] = (int)(n - 1);
-            continue;
-        }
-        const int64_t e = k * chunk;
-        int64_t lo = 0, hi = n - 1;  // largest r with tptr[r] <= e
-        while (lo < hi) {
-            const int64_t m = (lo + hi + 1) >> 1;
-            if (tptr[m] <= e)
-                lo = m;
-            else
-                hi = m - 1;
-        }
-        out[k] = (int)lo;
+// run_row[k] = row holding entry k * kTailPerLane (the first entry of lane
+// run k) for k < nruns, and run_row[nruns] = n - 1; one thread per row
+// writes the runs that start inside the row
+__global__ void k_run_rows(int64_t n, int64_t nruns, const int* __restrict__ ptr,
+                           int* __restrict__ out) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t k0 = ((int64_t)ptr[i] + kTailPerLane - 1) / kTailPerLane;
+        const int64_t k1 = ((int64_t)ptr[i + 1] + kTailPerLane - 1) / kTailPerLane;
+        for (int64_t k = k0; k < k1; ++k) out[k] = (int)i;
+        if (i == 0) out[nruns] = (int)(n - 1);
     }
 }
 
@@ -725,14 +717,13 @@ void build_split(const spmv_handle* h, int format, int requested, int sort_windo
                            b.tail_col.as<int>(), b.tail_val.as<V>());
         hip_check(hipGetLastError(), "tail fill");
     }
-    b.tail_chunks = (tail + kTailChunk - 1) / kTailChunk;
+    b.tail_runs = (tail + kTailPerLane - 1) / kTailPerLane;
     if (format == SPMV_HEC) {
-        b.chunk_row.alloc((size_t)(b.tail_chunks + 1) * 4);
+        b.run_row.alloc((size_t)(b.tail_runs + 1) * 4);
         if (n > 0) {
-            hipLaunchKernelGGL(k_chunk_rows, dim3(grid_for(b.tail_chunks + 1)), dim3(256), 0, s, n,
-                               b.tail_chunks, (int64_t)kTailChunk, b.tail_ptr.as<int>(),
-                               b.chunk_row.as<int>());
-            hip_check(hipGetLastError(), "chunk rows");
+            hipLaunchKernelGGL(k_run_rows, dim3(grid_for(n)), dim3(256), 0, s, n, b.tail_runs,
+                               b.tail_ptr.as<int>(), b.run_row.as<int>());
+            hip_check(hipGetLastError(), "run rows");
         }
     } else {
         b.tail_ptr.release();  // HYB keeps the COO rows only
@@ -750,7 +741,7 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
     switch (format) {
         case SPMV_CSR: {
             if (b.csr_balanced) {
-                TailView t{(int)h->n, h->nnz, nullptr, h->rowptr.as<int>(), b.chunk_row.as<int>(),
+                TailView t{(int)h->n, h->nnz, nullptr, h->rowptr.as<int>(), b.run_row.as<int>(),
                            h->col.as<int>(), h->val.p, b.window};
                 e = launch_scale(h->n, f64, y, beta, s);
                 if (e == hipSuccess) e = launch_tail(t, f64, y, x, alpha, s);
@@ -769,7 +760,7 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
             e = launch_ell(a, f64, y, x, alpha, beta, s);
             if (e == hipSuccess && format != SPMV_ELLR && b.tail_nnz > 0) {
                 TailView t{(int)h->n, b.tail_nnz, b.tail_row.as<int>(), b.tail_ptr.as<int>(),
-                           b.chunk_row.as<int>(), b.tail_col.as<int>(), b.tail_val.p, b.window};
+                           b.run_row.as<int>(), b.tail_col.as<int>(), b.tail_val.p, b.window};
                 e = launch_tail(t, f64, y, x, alpha, s);
             }
             break;
@@ -819,13 +810,12 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     const bool want_bal = o.csr_kernel != SPMV_CSR_VECTOR && h->nnz > 0;
     b.csr_balanced = !want_vec;
     if (want_bal) {
-        // row of the first entry of every wave chunk, over the whole matrix
-        b.tail_chunks = (h->nnz + kTailChunk - 1) / kTailChunk;
-        b.chunk_row.alloc((size_t)(b.tail_chunks + 1) * 4);
-        hipLaunchKernelGGL(k_chunk_rows, dim3(grid_for(b.tail_chunks + 1)), dim3(256), 0, s, h->n,
-                           b.tail_chunks, (int64_t)kTailChunk, h->rowptr.as<int>(),
-                           b.chunk_row.as<int>());
-        hip_check(hipGetLastError(), "chunk rows");
+        // row of the first entry of every lane run, over the whole matrix
+        b.tail_runs = (h->nnz + kTailPerLane - 1) / kTailPerLane;
+        b.run_row.alloc((size_t)(b.tail_runs + 1) * 4);
+        hipLaunchKernelGGL(k_run_rows, dim3(grid_for(h->n)), dim3(256), 0, s, h->n, b.tail_runs,
+                           h->rowptr.as<int>(), b.run_row.as<int>());
+        hip_check(hipGetLastError(), "run rows");
         const bool bal = b.csr_balanced;
         b.csr_balanced = true;  // the window is timed on the balanced kernel
         decide_window(h, SPMV_CSR, o.x_window, b, s);
@@ -858,7 +848,7 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
             [&] { return launch_built(h, b, SPMV_CSR, ys.p, xs.p, 1.0, 0.0, s); }, s);
         b.csr_balanced = ms < best_ms;
     }
-    if (!b.csr_balanced) b.chunk_row.release(), b.window = false, b.tail_chunks = 0;
+    if (!b.csr_balanced) b.run_row.release(), b.window = false, b.tail_runs = 0;
 }
 
 // Share of the entries the LDS window reaches, and whether to use it.  On

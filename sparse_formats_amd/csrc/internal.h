@@ -92,7 +92,8 @@ struct TailView {
     int64_t nnz;
     const int* row;        // COO row ids (HYB) or nullptr
     const int* ptr;        // CSR tail pointer [n+1] (HEC) or nullptr
-    const int* chunk_row;  // HEC: row of the first entry of each wave chunk
+    const int* run_row;    // CSR tail: row of the first entry of each lane run
+                           // of kTailPerLane entries (+ n - 1 at the end)
     const int* col;
     const void* val;
     bool window;           // stage x in LDS (banded matrices)

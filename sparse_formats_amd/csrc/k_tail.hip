@@ -131,26 +131,26 @@ __device__ __forceinline__ void tail_fetch(int64_t w, int lane, int64_t nnz,
 }
 
 // Rows of chunk w's entries from the CSR tail pointer (HEC, and CSR run by
-// entries; one pass of E entries per lane).  Each lane binary-searches the
-// row of its first entry between the rows of the chunk's first and last
-// entries (stored when the format is built), then reads the next E row
-// starts at once and places its entries among them, searching again only
-// if its run crosses more rows (rows without entries in between).
+// entries; one pass of E entries per lane).  The row of every lane's first
+// entry is stored when the format is built (run_row, 4 bytes per 8
+// entries); the lane reads the next E row starts at once and places its
+// entries among them, searching (up to the next lane's row) only if its run
+// crosses more rows (rows without entries in between).
 template <typename T>
 __device__ __forceinline__ void tail_rows(int64_t w, int lane, const int* __restrict__ tptr,
-                                          const int* __restrict__ chunk_row,
+                                          const int* __restrict__ run_row,
                                           TailRun<T, false>& R) {
     constexpr int E = TailShape<T, false>::E;
     constexpr int kNone = 0x7fffffff;
-    const int64_t e0 = pass_entry(w, 0, lane, E);
     const int cnt = R.cnt[0];
     int* r = R.r[0];
-    const int lo = chunk_row[w], hi = chunk_row[w + 1];
-    const int cur = cnt > 0 ? row_of(tptr, lo, hi, e0) : kNone;
-    const int base = cnt > 0 ? cur : lo;  // inactive lanes read in-range rows
-    int nxt[E];  // starts of the next E rows (clamped to the chunk's last row)
+    const int64_t q = w * 64 + lane;  // lane run index
+    const int64_t e0 = q * E;
+    const int64_t qs = cnt > 0 ? q : 0;  // past the last run: any valid index
+    const int cur = run_row[qs], hi = run_row[qs + 1];
+    int nxt[E];  // starts of the next E rows (clamped to the next run's row)
 #pragma unroll
-    for (int j = 0; j < E; ++j) nxt[j] = tptr[min(base + 1 + j, hi + 1)];
+    for (int j = 0; j < E; ++j) nxt[j] = tptr[min(cur + 1 + j, hi + 1)];
 #pragma unroll
     for (int k = 0; k < E; ++k) {
         int adv = 0;
@@ -244,7 +244,7 @@ __device__ __forceinline__ void tail_far_gather(const T* __restrict__ x, int64_t
 template <typename T, bool kCoo, bool kWin>
 __device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
                                             const int* __restrict__ tptr,
-                                            const int* __restrict__ chunk_row,
+                                            const int* __restrict__ run_row,
                                             const T* __restrict__ x, T* __restrict__ y, T alpha,
                                             const T* win,
                                             const bool (&far)[TailShape<T, kCoo>::P][TailShape<T, kCoo>::E],
@@ -252,7 +252,9 @@ __device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
                                             TailRun<T, kCoo>& R) {
     constexpr int E = TailShape<T, kCoo>::E, P = TailShape<T, kCoo>::P;
     if (w * kTailChunk >= nnz) return;  // the whole wave leaves together
-    if constexpr (!kCoo) tail_rows<T>(w, lane, tptr, chunk_row, R);
+    if constexpr (!kCoo) tail_rows<T>(w, lane, tptr, run_row, R);
+    // every x read is issued before the first product (entries past the
+    // end read nothing and hold value 0)
     T pr[P][E];
 #pragma unroll
     for (int p = 0; p < P; ++p)
@@ -276,7 +278,7 @@ __device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
 template <typename T, bool kCoo>
 __global__ __launch_bounds__(256) void k_tail(int n, int64_t nnz, const int* __restrict__ trow,
                                               const int* __restrict__ tptr,
-                                              const int* __restrict__ chunk_row,
+                                              const int* __restrict__ run_row,
                                               const int* __restrict__ col,
                                               const T* __restrict__ val,
                                               const T* __restrict__ x, T* __restrict__ y,
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(256) void k_tail(int n, int64_t nnz, const int* __r
     tail_fetch<T, kCoo>(w, threadIdx.x & 63, nnz, trow, col, val, R);
     bool far[P][E] = {};
     T xg[P][E] = {};
-    tail_finish<T, kCoo, false>(w, threadIdx.x & 63, nnz, tptr, chunk_row, x, y, alpha, nullptr,
+    tail_finish<T, kCoo, false>(w, threadIdx.x & 63, nnz, tptr, run_row, x, y, alpha, nullptr,
                                 far, xg, R);
 }
 
@@ -304,7 +306,7 @@ template <typename T, bool kCoo>
 __global__ __launch_bounds__(1024) void k_tail_win(int n, int64_t nnz,
                                                    const int* __restrict__ trow,
                                                    const int* __restrict__ tptr,
-                                                   const int* __restrict__ chunk_row,
+                                                   const int* __restrict__ run_row,
                                                    const int* __restrict__ col,
                                                    const T* __restrict__ val,
                                                    const T* __restrict__ x, T* __restrict__ y,
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(1024) void k_tail_win(int n, int64_t nnz,
     int64_t prev_whi = -1;
     for (int64_t s = s0; s < s1; ++s) {
         const int64_t r_first = kCoo ? trow[s * (int64_t)kTailStepChunks * kTailChunk]
-                                     : chunk_row[s * kTailStepChunks];
+                                     : run_row[s * (int64_t)kTailStepChunks * 64];
         const int64_t wlo = r_first - LEAD, whi = wlo + WL;
         lds_barrier();  // the previous step is done with the slots reused now
         const int64_t from = max<int64_t>(max<int64_t>(prev_whi, wlo), 0);
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(1024) void k_tail_win(int n, int64_t nnz,
             tail_far_gather<T, kCoo>(x, wlo, run[k & 1], far, xg);
             if (k + 1 < CPW)
                 tail_fetch<T, kCoo>(w0 + k + 1, lane, nnz, trow, col, val, run[(k + 1) & 1]);
-            tail_finish<T, kCoo, true>(w0 + k, lane, nnz, tptr, chunk_row, x, y, alpha, win, far,
+            tail_finish<T, kCoo, true>(w0 + k, lane, nnz, tptr, run_row, x, y, alpha, win, far,
                                        xg, run[k & 1]);
         }
     }
@@ -357,22 +359,22 @@ static hipError_t run(const TailView& t, void* y, const void* x, double alpha,
         const int64_t g = std::min<int64_t>(nsteps, kWinGroups);
         if (t.row)
             hipLaunchKernelGGL((k_tail_win<T, true>), dim3((unsigned)g), dim3(1024), 0, stream, t.n,
-                               t.nnz, t.row, t.ptr, t.chunk_row, t.col, (const T*)t.val,
+                               t.nnz, t.row, t.ptr, t.run_row, t.col, (const T*)t.val,
                                (const T*)x, (T*)y, (T)alpha, nsteps);
         else
             hipLaunchKernelGGL((k_tail_win<T, false>), dim3((unsigned)g), dim3(1024), 0, stream,
-                               t.n, t.nnz, t.row, t.ptr, t.chunk_row, t.col, (const T*)t.val,
+                               t.n, t.nnz, t.row, t.ptr, t.run_row, t.col, (const T*)t.val,
                                (const T*)x, (T*)y, (T)alpha, nsteps);
         return hipGetLastError();
     }
     const int64_t blocks = (waves + 3) / 4;
     if (t.row)
         hipLaunchKernelGGL((k_tail<T, true>), dim3((unsigned)blocks), dim3(256), 0, stream, t.n,
-                           t.nnz, t.row, t.ptr, t.chunk_row, t.col, (const T*)t.val,
+                           t.nnz, t.row, t.ptr, t.run_row, t.col, (const T*)t.val,
                            (const T*)x, (T*)y, (T)alpha);
     else
         hipLaunchKernelGGL((k_tail<T, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                           t.n, t.nnz, t.row, t.ptr, t.chunk_row, t.col, (const T*)t.val,
+                           t.n, t.nnz, t.row, t.ptr, t.run_row, t.col, (const T*)t.val,
                            (const T*)x, (T*)y, (T)alpha);
     return hipGetLastError();
 }
