@@ -134,21 +134,38 @@ def cpu_baseline(a, x, target_s: float = 10.0):
                       "rows) in %.1f s" % (reps, a.n, t)}
 
 
-def traffic_for(kernel_key: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if the
-    kernel sources have not changed since they were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def kernel_bases(fmt: str, info: dict) -> set:
+    """Base names of the kernels one apply of this handle launches (SELL's
+    chunk kernel, present only with very long slices, is left out)."""
+    win = "_win" if info.get("x_window") else ""
+    if fmt == "csr":
+        if info.get("csr_kernel") == "balanced":
+            return {"k_scale", "k_tail" + win}
+        return {"k_csr_vector"}
+    if fmt == "sell64":
+        return {"k_sell"}
+    out = {"k_ell" + win}
+    if fmt in ("hyb", "hec") and info.get("tail_nnz", 0) > 0:
+        out.add("k_tail" + win)
+    return out
+
+
+def traffic_for(key: str, bases: set, path: str | None = None):
+    """HBM bytes of one apply from committed rocprofv3 counter runs
+    (profiles/traffic.json), if the kernel sources have not changed since
+    they were taken and the profiled apply ran the same kernels."""
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(kernel_key)
-    if not rec:
-        return None
-    h = hashlib.sha256()
-    for f in sorted(rec.get("sources", [])):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != rec.get("sha256"):
-        return None
-    return rec.get("bytes_per_launch")
+    recs = json.load(open(path)).get(key) or []
+    for rec in recs if isinstance(recs, list) else [recs]:
+        if {k.split("<")[0] for k in rec.get("kernels", [])} - {"k_sell_chunks"} != bases:
+            continue
+        h = hashlib.sha256()
+        for f in sorted(rec.get("sources", [])):
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        return rec.get("bytes_per_launch") if h.hexdigest() == rec.get("sha256") else None
+    return None
 
 
 def main(argv=None):
@@ -161,6 +178,8 @@ def main(argv=None):
     ap.add_argument("--formats", default=",".join(ALL_FORMATS))
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--csr-kernel", default="auto", choices=["auto", "vector", "balanced"],
+                    help="CSR apply kernel (default: timed at conversion)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: this SpMV path runs on a single MI355X and has no "
@@ -194,7 +213,7 @@ def main(argv=None):
         t1 = time.perf_counter()
         M = sf.Matrix.from_csr(rp, col, val, n=a.n)
         try:
-            M.convert(fmt)
+            M.convert(fmt, csr_kernel=args.csr_kernel)
         except sf.SpmvError as e:
             refused[fmt] = str(e)
             M.close()
@@ -234,10 +253,11 @@ def main(argv=None):
     total_ms = start.elapsed_time(end)
 
     per = {}
+    mats_info = {f: mats[f].info() for f in fmts}
     for f in fmts:
         ts = np.array([e0.elapsed_time(e1) for e0, e1 in ev[f]])
         med = float(np.median(ts))
-        info = mats[f].info()
+        info = mats_info[f]
         bm = bytes_model(f, a.n, a.nnz, s_v, info["tail_nnz"])
         gbs = bm / (med * 1e-3) / 1e9
         per[f] = {
@@ -257,7 +277,8 @@ def main(argv=None):
     achieved = d["bytes_model"] / (d["ms_median"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_for("%s:%s:%s" % (args.workload, args.dtype, dom)),
+                "traffic": traffic_for("%s:%s:%s" % (args.workload, args.dtype, dom),
+                                       kernel_bases(dom, mats_info[dom])),
                 "kernel": "%s apply (%s)" % (dom, d["kernels"]),
                 "frac_of_stream": d["frac_stream"]}
     flops_step = 2.0 * a.nnz * len(fmts)

@@ -1,0 +1,157 @@
+"""Summaries of the rocprofv3 runs behind the benchmark's roofline figures.
+
+Reads the output directories of the runs made by these commands (from the
+repository root on the MI355X machine, W the workload):
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d <out>/stats_W -o run \
+        -- python3 bench.py --workload W --steps 10 --warmup 2 --no-cpu
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/FETCH_SIZE_W_F -o run \
+        -- python3 bench.py --workload W --formats F --steps 2 --warmup 1 --no-cpu
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/WRITE_SIZE_W_F -o run \
+        -- python3 bench.py --workload W --formats F --steps 2 --warmup 1 --no-cpu
+
+(for CSR once per kernel: F = csr-vector / csr-balanced with
+--formats csr --csr-kernel vector / balanced)
+
+and writes profiles/spmv_<W>_<dtype>_kernel_stats.md, ..._fetch_write.md and the
+per-apply HBM bytes of every format into profiles/traffic.json (keyed by
+workload:dtype:format, with a hash of the kernel sources so that the bench
+drops the figure once a kernel changes).
+
+Usage: python profiles/summarize.py <out> <workload> [dtype]
+"""
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FORMATS = ["csr-vector", "csr-balanced", "ellr", "sell64", "hyb", "hec"]
+APPLY = ("k_csr_vector", "k_scale", "k_tail", "k_tail_win", "k_ell", "k_ell_win", "k_sell",
+         "k_sell_chunks")
+SOURCES = ["sparse_formats_amd/csrc/" + f for f in
+           ("api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "common.h", "internal.h")]
+
+
+def short(name):
+    n = name.replace("(anonymous namespace)::", "").replace("spmv::", "")
+    n = n[5:] if n.startswith("void ") else n
+    base = n.split("(")[0]
+    return base.split("<")[0], base
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(SOURCES):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def rows_of(d, suffix):
+    f = [x for x in os.listdir(d) if x.endswith(suffix)][0]
+    return list(csv.DictReader(open(os.path.join(d, f))))
+
+
+def split_apply(seq):
+    """Split a format's last apply off the end of a dispatch list [(short, full)]."""
+    out = []
+    seen = set()
+    for s, full in reversed(seq):
+        if s not in APPLY or full in seen:
+            break
+        # an apply launches at most one ELL, one tail, one scale, one SELL kernel
+        seen.add(full)
+        out.append((s, full))
+    return list(reversed(out))
+
+
+def main():
+    out_dir, workload = sys.argv[1], sys.argv[2]
+    dtype = sys.argv[3] if len(sys.argv) > 3 else "f64"
+    tag = "%s_%s" % (workload, dtype)
+    # ---- kernel statistics of the default bench
+    sd = os.path.join(out_dir, "stats_" + workload)
+    stats = rows_of(sd, "kernel_stats.csv")
+    trace = sorted(rows_of(sd, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    last_copy = max(i for i, r in enumerate(trace) if short(r["Kernel_Name"])[0] == "k_copy")
+    timed = [r for r in trace[last_copy + 1:] if short(r["Kernel_Name"])[0] in APPLY]
+    lines = ["# rocprofv3 kernel statistics: bench.py on %s (%s)" % (workload, dtype), "",
+             "Command (repository root, MI355X):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d <out>/stats_%s -o run "
+             "-- python3 bench.py --workload %s --steps 10 --warmup 2 --no-cpu" % (workload, workload),
+             "", "rocprofv3 statistics (all dispatches of the run, including the conversion-time "
+             "timing of kernel shapes and the stream copy):", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in stats[:14]:
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %.2f |" % (
+            short(r["Name"])[1], r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    # per kernel (full name) over the 12 bench steps after the stream copy
+    per = {}
+    for r in timed:
+        per.setdefault(short(r["Kernel_Name"])[1], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "Applies after the stream copy (2 warm-up + 10 timed steps), per kernel:", "",
+              "| kernel | dispatches | mean us | median us |", "|---|---|---|---|"]
+    for k, v in per.items():
+        lines.append("| %s | %d | %.1f | %.1f |" % (k, len(v), statistics.mean(v),
+                                                    statistics.median(v)))
+    open(os.path.join(ROOT, "profiles", "spmv_%s_kernel_stats.md" % tag), "w").write(
+        "\n".join(lines) + "\n")
+    # ---- traffic per format
+    tj = os.path.join(ROOT, "profiles", "traffic.json")
+    T = json.load(open(tj)) if os.path.exists(tj) else {}
+    T = {k: v for k, v in T.items() if not k.startswith("%s:%s:" % (workload, dtype))}
+    fw = ["# HBM traffic per apply: bench.py on %s (%s)" % (workload, dtype), "",
+          "Commands (repository root, MI355X; one counter per run, F the format):", "",
+          "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/FETCH_SIZE_%s_F -o run "
+          "-- python3 bench.py --workload %s --formats F --steps 2 --warmup 1 --no-cpu"
+          % (workload, workload),
+          "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/WRITE_SIZE_%s_F -o run "
+          "-- python3 bench.py --workload %s --formats F --steps 2 --warmup 1 --no-cpu"
+          % (workload, workload), ""]
+    table = ["| format | kernels of one apply | FETCH bytes | WRITE bytes | total |",
+             "|---|---|---|---|---|"]
+    src_hash = source_hash()
+    for f in FORMATS:
+        vals = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            d = os.path.join(out_dir, "%s_%s_%s" % (c, workload, f))
+            if not os.path.isdir(d):
+                break
+            rows = sorted(rows_of(d, "counter_collection.csv"), key=lambda r: int(r["Dispatch_Id"]))
+            copy = [float(r["Counter_Value"]) * 1024 for r in rows
+                    if short(r["Kernel_Name"])[0] == "k_copy"]
+            factor = 2.0 * (1 << 30) / statistics.mean(copy)   # copy: 2 GiB read, 2 GiB written
+            seq = [(short(r["Kernel_Name"])[0], short(r["Kernel_Name"])[1],
+                    float(r["Counter_Value"]) * 1024) for r in rows]
+            last = split_apply([(s, full) for s, full, _ in seq])
+            tail = seq[-len(last):]
+            vals[c] = (factor, [(full, v * factor) for _, full, v in tail])
+        if len(vals) < 2:
+            continue
+        kern = [k for k, _ in vals["FETCH_SIZE"][1]]
+        fb = sum(v for _, v in vals["FETCH_SIZE"][1])
+        wb = sum(v for _, v in vals["WRITE_SIZE"][1])
+        table.append("| %s | %s | %.4g | %.4g | %.4g |" % (f, " + ".join(kern), fb, wb, fb + wb))
+        T.setdefault("%s:%s:%s" % (workload, dtype, f.split("-")[0]), []).append({
+            "kernels": kern, "bytes_per_launch": round(fb + wb), "fetch_scaled": round(fb),
+            "write_scaled": round(wb), "fetch_factor": round(vals["FETCH_SIZE"][0], 5),
+            "write_factor": round(vals["WRITE_SIZE"][0], 5), "sources": SOURCES,
+            "sha256": src_hash})
+    ff = T.get("%s:%s:ellr" % (workload, dtype), [{}])[0]
+    fw.append("Calibration: the library's copy kernel k_copy reads and writes 2 GiB per "
+              "dispatch in every run; FETCH_SIZE is scaled by %.4f and WRITE_SIZE by %.4f "
+              "(KiB counters, factors from that run)." % (ff.get("fetch_factor", 0),
+                                                          ff.get("write_factor", 0)))
+    fw += ["", "Last apply of the timed loop (the run applies only format F):", ""] + table
+    open(os.path.join(ROOT, "profiles", "spmv_%s_fetch_write.md" % tag), "w").write(
+        "\n".join(fw) + "\n")
+    json.dump(T, open(tj, "w"), indent=1, sort_keys=True)
+    print("\n".join(fw))
+
+
+if __name__ == "__main__":
+    main()

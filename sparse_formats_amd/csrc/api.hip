@@ -519,6 +519,10 @@ void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, int sigma, B
     hip_check(hipGetLastError(), "ell fill");
 }
 
+// a timed alternative to the simpler kernel (no LDS window, no atomics) is
+// kept only when it is at least this much faster
+constexpr float kPreferMargin = 0.95f;
+
 // the ELL part of HYB/HEC is sorted inside its blocks (by default) when
 // waves of 64 unsorted rows would read more than this share of padding
 constexpr double kSortPadShare = 0.10;
@@ -846,7 +850,9 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
         b.csr_balanced = true;
         const float ms = time_launches(
             [&] { return launch_built(h, b, SPMV_CSR, ys.p, xs.p, 1.0, 0.0, s); }, s);
-        b.csr_balanced = ms < best_ms;
+        // the vector kernel adds no atomics (bit-reproducible results): the
+        // balanced one must be clearly faster to be kept
+        b.csr_balanced = ms < kPreferMargin * best_ms;
     }
     if (!b.csr_balanced) b.run_row.release(), b.window = false, b.tail_runs = 0;
 }
@@ -885,7 +891,7 @@ void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStrea
     const float with = time_launches(run, s);
     b.window = false;
     const float without = time_launches(run, s);
-    b.window = with < without;
+    b.window = with < kPreferMargin * without;
 }
 
 int run_guarded(const std::function<void()>& body) {

@@ -86,3 +86,32 @@ def test_bench_json_line():
     assert set(out["formats"]) == {"csr", "ellr", "sell64", "hyb", "hec"}
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in out["roofline"]
+
+
+def test_traffic_record_checks(tmp_path):
+    """The bench reports counter traffic only for the kernels it launched and
+    only while their sources are unchanged."""
+    import hashlib
+    srcs = ["sparse_formats_amd/csrc/k_tail.hip", "sparse_formats_amd/csrc/common.h"]
+    h = hashlib.sha256()
+    for f in sorted(srcs):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    rec = {"w:f64:csr": [{"kernels": ["k_scale<double>", "k_tail<double, false>"],
+                          "bytes_per_launch": 123, "sources": srcs, "sha256": h.hexdigest()},
+                         {"kernels": ["k_csr_vector<double, 8, 1>"], "bytes_per_launch": 99,
+                          "sources": srcs, "sha256": h.hexdigest()}],
+           "w:f64:hyb": {"kernels": ["k_ell<double>", "k_tail<double, true>"],
+                         "bytes_per_launch": 7, "sources": srcs, "sha256": "0" * 64}}
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps(rec))
+    bal = bench.kernel_bases("csr", {"csr_kernel": "balanced", "x_window": 0})
+    assert bal == {"k_scale", "k_tail"}
+    assert bench.traffic_for("w:f64:csr", bal, str(p)) == 123
+    vec = bench.kernel_bases("csr", {"csr_kernel": "vector", "x_window": 0})
+    assert bench.traffic_for("w:f64:csr", vec, str(p)) == 99            # the other record
+    win = bench.kernel_bases("csr", {"csr_kernel": "balanced", "x_window": 1})
+    assert bench.traffic_for("w:f64:csr", win, str(p)) is None          # window variant
+    hyb = bench.kernel_bases("hyb", {"x_window": 0, "tail_nnz": 5})
+    assert bench.traffic_for("w:f64:hyb", hyb, str(p)) is None          # stale sources
+    assert bench.traffic_for("w:f64:hec", hyb, str(p)) is None          # no record
+    assert bench.kernel_bases("hec", {"x_window": 1, "tail_nnz": 0}) == {"k_ell_win"}
