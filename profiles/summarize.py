@@ -67,6 +67,35 @@ def split_apply(seq):
     return list(reversed(out))
 
 
+def per_format_applies(timed, formats):
+    """Attribute the bench's apply dispatches to formats: every step applies
+    the formats in order, each with its own kernels (CSR: k_csr_vector, or
+    k_scale + a CSR tail; ELL-R: one ELL kernel; SELL-64: k_sell [+ chunks];
+    HYB / HEC: one ELL kernel [+ a COO / CSR tail])."""
+    out = {f: [] for f in formats}
+    i = 0
+    names = [(short(r["Kernel_Name"])[0], short(r["Kernel_Name"])[1],
+              (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in timed]
+    while i < len(names):
+        for f in formats:
+            if i >= len(names):
+                break
+            s, full, t = names[i]
+            ks, tot = [full], t
+            i += 1
+            follow = {"csr": ("k_tail", "k_tail_win") if s == "k_scale" else (),
+                      "sell64": ("k_sell_chunks",),
+                      "hyb": ("k_tail", "k_tail_win"), "hec": ("k_tail", "k_tail_win")}.get(f, ())
+            coo = {"hyb": "true", "hec": "false", "csr": "false"}.get(f)
+            if i < len(names) and names[i][0] in follow and (
+                    f == "sell64" or names[i][1].endswith(coo + ">")):
+                ks.append(names[i][1])
+                tot += names[i][2]
+                i += 1
+            out[f].append((" + ".join(ks), tot))
+    return out
+
+
 def main():
     out_dir, workload = sys.argv[1], sys.argv[2]
     dtype = sys.argv[3] if len(sys.argv) > 3 else "f64"
@@ -98,6 +127,25 @@ def main():
     for k, v in per.items():
         lines.append("| %s | %d | %.1f | %.1f |" % (k, len(v), statistics.mean(v),
                                                     statistics.median(v)))
+    js = [l for l in open(os.path.join(out_dir, "stats_%s.log" % workload))
+          if l.startswith('{"metric"')]
+    if js:
+        bench_line = json.loads(js[-1])
+        formats = bench_line["config"]["formats"]
+        applies = per_format_applies(timed, formats)
+        lines += ["", "One apply per format (the kernels of each format in the 2 warm-up + 10 "
+                  "timed steps, summed per apply), beside the bench's own median from HIP "
+                  "events in the same run:", "",
+                  "| format | kernels | applies | mean us | median us | bench median us |",
+                  "|---|---|---|---|---|---|"]
+        for f in formats:
+            v = applies[f]
+            if not v:
+                continue
+            ts = [t for _, t in v]
+            lines.append("| %s | %s | %d | %.1f | %.1f | %.1f |" % (
+                f, v[-1][0], len(v), statistics.mean(ts), statistics.median(ts),
+                bench_line["formats"][f]["ms_median"] * 1e3))
     open(os.path.join(ROOT, "profiles", "spmv_%s_kernel_stats.md" % tag), "w").write(
         "\n".join(lines) + "\n")
     # ---- traffic per format
