@@ -65,7 +65,16 @@ typedef enum {
     SPMV_ELLR = 1,
     SPMV_SELL64 = 2,
     SPMV_HYB = 3,
-    SPMV_HEC = 4
+    SPMV_HEC = 4,
+    /* spmv_convert only: build every eligible format in turn with the given
+     * options, time one apply of each on the device and keep the fastest
+     * (spmv_info then reports the format kept).  ELL-R is eligible while its
+     * padded slots are at most 1.5 times the stored entries; a format over
+     * the footprint budget is skipped.  The choice from the row-length
+     * statistics that "Load-balancing Sparse Matrix Vector Product Kernels
+     * on GPUs" (abstract) and "Development of Krylov...", Sect. 4, make per
+     * matrix is made here by measurement. */
+    SPMV_AUTO = 5
 } spmv_format;
 
 /* CSR apply kernels (spmv_convert_opts.csr_kernel, spmv_info_t.csr_kernel) */
@@ -229,8 +238,10 @@ int spmv_create(spmv_t *out, int kind, int64_t n, int64_t nnz,
  * spmv_convert -- build `format` on the device from the CSR copy and make it
  * the active format.  Synchronous (small size read-backs are needed).
  * The previous non-CSR format is released once the new one is built; on any
- * error the handle is left exactly as it was.  Converting to SPMV_CSR only
- * switches the active format (and applies opts->subwave).
+ * error the handle is left exactly as it was.  Converting to SPMV_CSR
+ * switches the active format and chooses its kernel (see csr_kernel).
+ * SPMV_AUTO releases the previous format before it starts and leaves CSR
+ * active if it fails.
  *   opts  may be NULL (defaults, see spmv_convert_opts)
  * Errors: STATE, INVALID_ARG (unknown format, bad subwave), FOOTPRINT (the
  * padded layout exceeds the budget; e.g. ELL-R of a matrix with a few very

@@ -24,7 +24,7 @@ __all__ = ["Matrix", "SpmvError", "FORMATS", "CSR_KERNELS", "ARRAYS", "stream_co
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspmv_amd.so")
 
-FORMATS = {"csr": 0, "ellr": 1, "sell64": 2, "hyb": 3, "hec": 4}
+FORMATS = {"csr": 0, "ellr": 1, "sell64": 2, "hyb": 3, "hec": 4, "auto": 5}
 CSR_KERNELS = {"auto": 0, "vector": 1, "balanced": 2}
 ARRAYS = {
     "rowptr": (0, np.int32), "col": (1, np.int32), "val": (2, None),

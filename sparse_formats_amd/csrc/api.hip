@@ -523,6 +523,10 @@ void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, int sigma, B
 // kept only when it is at least this much faster
 constexpr float kPreferMargin = 0.95f;
 
+// automatic format choice: ELL-R is a candidate only while its padded slots
+// are at most this many times the stored entries
+constexpr double kAutoEllPadding = 1.5;
+
 // the ELL part of HYB/HEC is sorted inside its blocks (by default) when
 // waves of 64 unsorted rows would read more than this share of padding
 constexpr double kSortPadShare = 0.10;
@@ -912,6 +916,94 @@ int run_guarded(const std::function<void()>& body) {
 
 bool valid_format(int f) { return f >= SPMV_CSR && f <= SPMV_HEC; }
 
+// Build `format` (options already validated) and make it the active format.
+void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
+    if (format == SPMV_CSR) {
+        Built b;
+        tune_csr(h, o, b, nullptr);
+        h->fmt = std::move(b);
+        h->format = SPMV_CSR;
+        return;
+    }
+    hipStream_t s = nullptr;
+    const bool f64 = h->dtype == SPMV_F64;
+    Built b;
+    b.format = format;
+    if (format == SPMV_ELLR) {
+        const int64_t S = pad64(h->n), W = h->max_len;
+        const double need = (double)W * (double)S * (4.0 + (double)h->vsize) + 4.0 * (double)S;
+        const uint64_t budget = budget_bytes(o);
+        if (need > (double)budget)
+            fail(SPMV_ERR_FOOTPRINT,
+                 "ELL-R needs %.3g bytes (%lld rows padded to %lld x width %lld) over the "
+                 "budget of %.3g bytes",
+                 need, (long long)h->n, (long long)S, (long long)W, (double)budget);
+        if (f64)
+            build_ell_part<double>(h, W, 0, 0, b, s);
+        else
+            build_ell_part<float>(h, W, 0, 0, b, s);
+        decide_window(h, format, o.x_window, b, s);
+        sync(s);
+    } else if (format == SPMV_SELL64) {
+        if (f64)
+            build_sell<double>(h, o.sort_window, b, s);
+        else
+            build_sell<float>(h, o.sort_window, b, s);
+    } else {
+        if (f64)
+            build_split<double>(h, format, o.ell_width, o.sort_window, b, s);
+        else
+            build_split<float>(h, format, o.ell_width, o.sort_window, b, s);
+        decide_window(h, format, o.x_window, b, s);
+    }
+    h->fmt = std::move(b);
+    h->format = format;
+}
+
+// Automatic format: build every eligible format in turn with the same
+// options, time one apply of each on the device (x = 0: the apply does not
+// depend on the values) and keep the fastest.  ELL-R is eligible only while
+// its padded slots stay within kAutoEllPadding times the stored entries
+// (its cost follows the slots, not the entries, once rows differ in length).
+void convert_auto(spmv_handle* h, const spmv_convert_opts& o) {
+    h->fmt = Built{};  // the previous format is released first
+    h->format = SPMV_CSR;
+    const double ell_slots = (double)pad64(h->n) * (double)h->max_len;
+    std::vector<int> cand = {SPMV_CSR, SPMV_SELL64, SPMV_HYB, SPMV_HEC};
+    if (ell_slots <= kAutoEllPadding * (double)std::max<int64_t>(h->nnz, 1))
+        cand.insert(cand.begin() + 1, SPMV_ELLR);
+    hipStream_t s = nullptr;
+    DevBuf xs((size_t)std::max<int64_t>(h->n, 1) * h->vsize);
+    DevBuf ys((size_t)std::max<int64_t>(h->n, 1) * h->vsize);
+    hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
+    Built best;
+    int best_fmt = -1;
+    float best_ms = 0;
+    for (int f : cand) {
+        spmv_convert_opts of = o;
+        if (f == SPMV_CSR || f == SPMV_ELLR) of.sort_window = -1;
+        try {
+            convert_into(h, f, of);
+        } catch (const Error& e) {
+            if (e.code != SPMV_ERR_FOOTPRINT) throw;
+            continue;  // too large for the budget: not a candidate
+        }
+        const float ms = h->n == 0 ? 0.0f : time_launches([&] {
+            return launch_built(h, h->fmt, f, ys.p, xs.p, 1.0, 0.0, s);
+        }, s);
+        if (best_fmt < 0 || ms < best_ms) {
+            best = std::move(h->fmt);
+            best_fmt = f;
+            best_ms = ms;
+        }
+        h->fmt = Built{};
+        h->format = SPMV_CSR;
+    }
+    h->fmt = std::move(best);
+    h->format = best_fmt;
+}
+
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1026,7 +1118,8 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
     g_err.clear();
     return run_guarded([&] {
         if (!h) fail(SPMV_ERR_STATE, "null handle");
-        if (!valid_format(format)) fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
+        if (!valid_format(format) && format != SPMV_AUTO)
+            fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
         spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0};
         if (opts) o = *opts;
         if (o.sort_window < -1)
@@ -1034,7 +1127,8 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
                  o.sort_window);
         if ((format == SPMV_CSR || format == SPMV_ELLR) && o.sort_window > 0)
             fail(SPMV_ERR_INVALID_ARG, "sort_window applies to SELL-64, HYB and HEC only");
-        if ((format == SPMV_HYB || format == SPMV_HEC) && o.sort_window > 0 &&
+        if ((format == SPMV_HYB || format == SPMV_HEC || format == SPMV_AUTO) &&
+            o.sort_window > 0 &&
             (o.sort_window < 64 || o.sort_window > kEllBlock || kEllBlock % o.sort_window))
             fail(SPMV_ERR_INVALID_ARG,
                  "sort_window for HYB/HEC must be -1, 0 or a power of two in 64..%d (got %d)",
@@ -1044,52 +1138,15 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
         if (o.csr_rows < 0 || o.csr_rows > kCsrRowsMax || (o.csr_rows & (o.csr_rows - 1)))
             fail(SPMV_ERR_INVALID_ARG, "csr_rows must be 0 or a power of two up to %d",
                  kCsrRowsMax);
-        if (format == SPMV_CSR) {
-            const int sw = o.subwave;
-            if (sw < 0 || sw > 64 || (sw & (sw - 1)))
-                fail(SPMV_ERR_INVALID_ARG, "subwave must be 0 or a power of two in 1..64 (got %d)",
-                     sw);
-            if (o.csr_kernel < SPMV_CSR_AUTO || o.csr_kernel > SPMV_CSR_BALANCED)
-                fail(SPMV_ERR_INVALID_ARG, "csr_kernel must be 0, 1 or 2 (got %d)", o.csr_kernel);
-            Built b;
-            tune_csr(h, o, b, nullptr);
-            h->fmt = std::move(b);
-            h->format = SPMV_CSR;
-            return;
-        }
-        hipStream_t s = nullptr;
-        const bool f64 = h->dtype == SPMV_F64;
-        Built b;
-        b.format = format;
-        if (format == SPMV_ELLR) {
-            const int64_t S = pad64(h->n), W = h->max_len;
-            const double need = (double)W * (double)S * (4.0 + (double)h->vsize) + 4.0 * (double)S;
-            const uint64_t budget = budget_bytes(o);
-            if (need > (double)budget)
-                fail(SPMV_ERR_FOOTPRINT,
-                     "ELL-R needs %.3g bytes (%lld rows padded to %lld x width %lld) over the "
-                     "budget of %.3g bytes",
-                     need, (long long)h->n, (long long)S, (long long)W, (double)budget);
-            if (f64)
-                build_ell_part<double>(h, W, 0, 0, b, s);
-            else
-                build_ell_part<float>(h, W, 0, 0, b, s);
-            decide_window(h, format, o.x_window, b, s);
-            sync(s);
-        } else if (format == SPMV_SELL64) {
-            if (f64)
-                build_sell<double>(h, o.sort_window, b, s);
-            else
-                build_sell<float>(h, o.sort_window, b, s);
-        } else {
-            if (f64)
-                build_split<double>(h, format, o.ell_width, o.sort_window, b, s);
-            else
-                build_split<float>(h, format, o.ell_width, o.sort_window, b, s);
-            decide_window(h, format, o.x_window, b, s);
-        }
-        h->fmt = std::move(b);
-        h->format = format;
+        if (o.subwave < 0 || o.subwave > 64 || (o.subwave & (o.subwave - 1)))
+            fail(SPMV_ERR_INVALID_ARG, "subwave must be 0 or a power of two in 1..64 (got %d)",
+                 o.subwave);
+        if (o.csr_kernel < SPMV_CSR_AUTO || o.csr_kernel > SPMV_CSR_BALANCED)
+            fail(SPMV_ERR_INVALID_ARG, "csr_kernel must be 0, 1 or 2 (got %d)", o.csr_kernel);
+        if (format == SPMV_AUTO)
+            convert_auto(h, o);
+        else
+            convert_into(h, format, o);
     });
 }
 

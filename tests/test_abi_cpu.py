@@ -64,6 +64,7 @@ def test_enum_values_match_binding():
     fm = {"csr": ev["SPMV_CSR"], "ellr": ev["SPMV_ELLR"], "sell64": ev["SPMV_SELL64"],
           "hyb": ev["SPMV_HYB"], "hec": ev["SPMV_HEC"]}
     assert fm == {"csr": 0, "ellr": 1, "sell64": 2, "hyb": 3, "hec": 4}
+    assert ev["SPMV_AUTO"] == 5 and ev["SPMV_CSR_BALANCED"] == 2 and ev["SPMV_A_ELL_PERM"] == 15
     assert ev["SPMV_A_TAIL_VAL"] == 14 and ev["SPMV_A_SELL_SLICE_PTR"] == 7
 
 

@@ -484,3 +484,29 @@ def test_sort_window_errors():
     M.convert("sell64", sort_window=7)   # any window works for SELL-64
     assert M.info()["sort_window"] == 7
     M.close()
+
+
+@pytest.mark.parametrize("name", ["c1", "ragged", "every_len", "long_spans", "box27", "n1", "nnz0",
+                                  "banded"])
+def test_auto_format(name):
+    """SPMV_AUTO keeps one of the five formats (ELL-R only when its padding is
+    at most 1.5x the entries) and applies it exactly like that format."""
+    a = WINDOW_MATS[name]()
+    x_np, y0_np = vectors(a.n, 20)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("hec").convert("auto")
+    fmt = M.info()["format"]
+    assert fmt in FORMATS
+    if oracle.pad64(a.n) * oracle.max_len(a) > 1.5 * max(a.nnz, 1):
+        assert fmt != "ellr"
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    rows = None if a.n < 100_000 else np.arange(0, a.n, 61)
+    for alpha, beta in AB[:2]:
+        check(a, x_np, y0_np, alpha, beta, apply(M, x, y0, alpha, beta), torch.float64, rows=rows,
+              what="auto -> %s on %s" % (fmt, name))
+    # a budget that refuses ELL-R still leaves a choice
+    M.convert("auto", footprint_budget=1)
+    assert M.info()["format"] != "ellr"
+    with pytest.raises(sf.SpmvError):
+        M.convert("auto", sort_window=100)
+    M.close()
