@@ -107,6 +107,10 @@ struct Built {
     // tail of HYB / HEC
     int64_t tail_nnz = 0, tail_runs = 0;
     DevBuf tail_row, tail_ptr, tail_col, tail_val, run_row;
+    // HEC: the tail pointer over the rows that have tail entries only
+    // (tail_rows: those rows; tail_cptr: their starts + the end)
+    int64_t tail_nrows = 0;
+    DevBuf tail_rows, tail_cptr;
     // CSR: entry-balanced kernel (chunk_row over the whole matrix)
     bool csr_balanced = false;
     // x staged in LDS by the ELL / tail kernels
@@ -117,7 +121,8 @@ struct Built {
         return ell_col.bytes + ell_val.bytes + ell_len.bytes + ell_perm.bytes + slice_ptr.bytes +
                sell_len.bytes +
                perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + tail_row.bytes +
-               tail_ptr.bytes + tail_col.bytes + tail_val.bytes + run_row.bytes;
+               tail_ptr.bytes + tail_col.bytes + tail_val.bytes + run_row.bytes + tail_rows.bytes +
+               tail_cptr.bytes;
     }
 };
 
@@ -428,6 +433,25 @@ __global__ void k_tail_len(int64_t n, int K, const int* __restrict__ rowptr,
         tlen[i] = max(rowptr[i + 1] - rowptr[i] - K, 0);
 }
 
+__global__ void k_tail_flags(int64_t n, const int* __restrict__ tptr, int* __restrict__ flag) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        flag[i] = tptr[i + 1] > tptr[i] ? 1 : 0;
+}
+
+// rows with tail entries: rows[pos[i]] = i and cptr[pos[i]] = tptr[i] for
+// every row i with tptr[i + 1] > tptr[i] (pos = exclusive count of such rows)
+__global__ void k_compact_rows(int64_t n, const int* __restrict__ tptr,
+                               const int* __restrict__ pos, int* __restrict__ rows,
+                               int* __restrict__ cptr) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        if (tptr[i + 1] > tptr[i]) {
+            rows[pos[i]] = (int)i;
+            cptr[pos[i]] = tptr[i];
+        }
+}
+
 // one wave per row: entries K.. of row i go to tail slots tptr[i]..
 template <typename V>
 __global__ void k_tail_fill(int64_t n, int K, const int* __restrict__ rowptr,
@@ -727,11 +751,41 @@ void build_split(const spmv_handle* h, int format, int requested, int sort_windo
     }
     b.tail_runs = (tail + kTailPerLane - 1) / kTailPerLane;
     if (format == SPMV_HEC) {
-        b.run_row.alloc((size_t)(b.tail_runs + 1) * 4);
-        if (n > 0) {
-            hipLaunchKernelGGL(k_run_rows, dim3(grid_for(n)), dim3(256), 0, s, n, b.tail_runs,
-                               b.tail_ptr.as<int>(), b.run_row.as<int>());
+        // compress the tail pointer to the rows that have tail entries, so a
+        // lane run of 8 entries crosses at most 8 (compressed) rows
+        b.tail_nrows = 0;
+        if (tail > 0) {
+            DevBuf flag((size_t)n * 4), pos((size_t)n * 4);
+            hipLaunchKernelGGL(k_tail_flags, dim3(grid_for(n)), dim3(256), 0, s, n,
+                               b.tail_ptr.as<int>(), flag.as<int>());
+            hip_check(hipGetLastError(), "tail flags");
+            size_t tmp = 0;
+            hip_check(rocprim::exclusive_scan(nullptr, tmp, flag.as<int>(), pos.as<int>(), 0,
+                                              (size_t)n, rocprim::plus<int>(), s),
+                      "exclusive_scan");
+            DevBuf work(tmp);
+            hip_check(rocprim::exclusive_scan(work.p, tmp, flag.as<int>(), pos.as<int>(), 0,
+                                              (size_t)n, rocprim::plus<int>(), s),
+                      "exclusive_scan");
+            const int last_pos = read_scalar<int>(pos.as<int>() + (n - 1), s);
+            const int last_flag = read_scalar<int>(flag.as<int>() + (n - 1), s);
+            b.tail_nrows = (int64_t)last_pos + last_flag;
+            b.tail_rows.alloc((size_t)b.tail_nrows * 4);
+            b.tail_cptr.alloc((size_t)(b.tail_nrows + 1) * 4);
+            hipLaunchKernelGGL(k_compact_rows, dim3(grid_for(n)), dim3(256), 0, s, n,
+                               b.tail_ptr.as<int>(), pos.as<int>(), b.tail_rows.as<int>(),
+                               b.tail_cptr.as<int>());
+            hip_check(hipGetLastError(), "compact rows");
+            const int tail_end = (int)tail;
+            hip_check(hipMemcpyAsync(b.tail_cptr.as<int>() + b.tail_nrows, &tail_end, 4,
+                                     hipMemcpyHostToDevice, s),
+                      "hipMemcpyAsync");
+            b.run_row.alloc((size_t)(b.tail_runs + 1) * 4);
+            hipLaunchKernelGGL(k_run_rows, dim3(grid_for(b.tail_nrows)), dim3(256), 0, s,
+                               b.tail_nrows, b.tail_runs, b.tail_cptr.as<int>(),
+                               b.run_row.as<int>());
             hip_check(hipGetLastError(), "run rows");
+            sync(s);  // before the temporaries are freed
         }
     } else {
         b.tail_ptr.release();  // HYB keeps the COO rows only
@@ -750,7 +804,7 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
         case SPMV_CSR: {
             if (b.csr_balanced) {
                 TailView t{(int)h->n, h->nnz, nullptr, h->rowptr.as<int>(), b.run_row.as<int>(),
-                           h->col.as<int>(), h->val.p, b.window};
+                           nullptr, h->col.as<int>(), h->val.p, b.window};
                 e = launch_scale(h->n, f64, y, beta, s);
                 if (e == hipSuccess) e = launch_tail(t, f64, y, x, alpha, s);
                 break;
@@ -767,8 +821,11 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
                       b.ell_col.as<int>(), b.ell_val.p, b.window};
             e = launch_ell(a, f64, y, x, alpha, beta, s);
             if (e == hipSuccess && format != SPMV_ELLR && b.tail_nnz > 0) {
-                TailView t{(int)h->n, b.tail_nnz, b.tail_row.as<int>(), b.tail_ptr.as<int>(),
-                           b.run_row.as<int>(), b.tail_col.as<int>(), b.tail_val.p, b.window};
+                const bool hec = format == SPMV_HEC;
+                TailView t{(int)h->n, b.tail_nnz, hec ? nullptr : b.tail_row.as<int>(),
+                           hec ? b.tail_cptr.as<int>() : nullptr, b.run_row.as<int>(),
+                           hec ? b.tail_rows.as<int>() : nullptr, b.tail_col.as<int>(),
+                           b.tail_val.p, b.window};
                 e = launch_tail(t, f64, y, x, alpha, s);
             }
             break;

@@ -91,9 +91,12 @@ struct TailView {
     int n;
     int64_t nnz;
     const int* row;        // COO row ids (HYB) or nullptr
-    const int* ptr;        // CSR tail pointer [n+1] (HEC) or nullptr
-    const int* run_row;    // CSR tail: row of the first entry of each lane run
-                           // of kTailPerLane entries (+ n - 1 at the end)
+    const int* ptr;        // CSR tail pointer over the tail's rows or nullptr
+                           // (HEC: only the rows with tail entries)
+    const int* run_row;    // CSR tail: row (index into ptr) of the first entry of
+                           // each lane run of kTailPerLane entries, plus the
+                           // last row at the end
+    const int* row_map;    // HEC: matrix row of each tail row; nullptr: identity
     const int* col;
     const void* val;
     bool window;           // stage x in LDS (banded matrices)

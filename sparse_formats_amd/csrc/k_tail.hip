@@ -139,6 +139,7 @@ __device__ __forceinline__ void tail_fetch(int64_t w, int lane, int64_t nnz,
 template <typename T>
 __device__ __forceinline__ void tail_rows(int64_t w, int lane, const int* __restrict__ tptr,
                                           const int* __restrict__ run_row,
+                                          const int* __restrict__ row_map,
                                           TailRun<T, false>& R) {
     constexpr int E = TailShape<T, false>::E;
     constexpr int kNone = 0x7fffffff;
@@ -167,6 +168,10 @@ __device__ __forceinline__ void tail_rows(int64_t w, int lane, const int* __rest
                 r[k] = c2;
             }
         }
+    }
+    if (row_map) {  // HEC: tail rows -> matrix rows
+#pragma unroll
+        for (int k = 0; k < E; ++k) r[k] = k < cnt ? row_map[r[k]] : kNone;
     }
 }
 
@@ -245,6 +250,7 @@ template <typename T, bool kCoo, bool kWin>
 __device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
                                             const int* __restrict__ tptr,
                                             const int* __restrict__ run_row,
+                                            const int* __restrict__ row_map,
                                             const T* __restrict__ x, T* __restrict__ y, T alpha,
                                             const T* win,
                                             const bool (&far)[TailShape<T, kCoo>::P][TailShape<T, kCoo>::E],
@@ -252,7 +258,7 @@ __device__ __forceinline__ void tail_finish(int64_t w, int lane, int64_t nnz,
                                             TailRun<T, kCoo>& R) {
     constexpr int E = TailShape<T, kCoo>::E, P = TailShape<T, kCoo>::P;
     if (w * kTailChunk >= nnz) return;  // the whole wave leaves together
-    if constexpr (!kCoo) tail_rows<T>(w, lane, tptr, run_row, R);
+    if constexpr (!kCoo) tail_rows<T>(w, lane, tptr, run_row, row_map, R);
     // every x read is issued before the first product (entries past the
     // end read nothing and hold value 0)
     T pr[P][E];
@@ -279,6 +285,7 @@ template <typename T, bool kCoo>
 __global__ __launch_bounds__(256) void k_tail(int n, int64_t nnz, const int* __restrict__ trow,
                                               const int* __restrict__ tptr,
                                               const int* __restrict__ run_row,
+                                              const int* __restrict__ row_map,
                                               const int* __restrict__ col,
                                               const T* __restrict__ val,
                                               const T* __restrict__ x, T* __restrict__ y,
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(256) void k_tail(int n, int64_t nnz, const int* __r
     tail_fetch<T, kCoo>(w, threadIdx.x & 63, nnz, trow, col, val, R);
     bool far[P][E] = {};
     T xg[P][E] = {};
-    tail_finish<T, kCoo, false>(w, threadIdx.x & 63, nnz, tptr, run_row, x, y, alpha, nullptr,
+    tail_finish<T, kCoo, false>(w, threadIdx.x & 63, nnz, tptr, run_row, row_map, x, y, alpha, nullptr,
                                 far, xg, R);
 }
 
@@ -307,6 +314,7 @@ __global__ __launch_bounds__(1024) void k_tail_win(int n, int64_t nnz,
                                                    const int* __restrict__ trow,
                                                    const int* __restrict__ tptr,
                                                    const int* __restrict__ run_row,
+                                                   const int* __restrict__ row_map,
                                                    const int* __restrict__ col,
                                                    const T* __restrict__ val,
                                                    const T* __restrict__ x, T* __restrict__ y,
@@ -320,8 +328,13 @@ __global__ __launch_bounds__(1024) void k_tail_win(int n, int64_t nnz,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int64_t prev_whi = -1;
     for (int64_t s = s0; s < s1; ++s) {
-        const int64_t r_first = kCoo ? trow[s * (int64_t)kTailStepChunks * kTailChunk]
-                                     : run_row[s * (int64_t)kTailStepChunks * 64];
+        int64_t r_first;
+        if constexpr (kCoo) {
+            r_first = trow[s * (int64_t)kTailStepChunks * kTailChunk];
+        } else {
+            const int tr = run_row[s * (int64_t)kTailStepChunks * 64];
+            r_first = row_map ? row_map[tr] : tr;
+        }
         const int64_t wlo = r_first - LEAD, whi = wlo + WL;
         lds_barrier();  // the previous step is done with the slots reused now
         const int64_t from = max<int64_t>(max<int64_t>(prev_whi, wlo), 0);
@@ -343,7 +356,7 @@ __global__ __launch_bounds__(1024) void k_tail_win(int n, int64_t nnz,
             tail_far_gather<T, kCoo>(x, wlo, run[k & 1], far, xg);
             if (k + 1 < CPW)
                 tail_fetch<T, kCoo>(w0 + k + 1, lane, nnz, trow, col, val, run[(k + 1) & 1]);
-            tail_finish<T, kCoo, true>(w0 + k, lane, nnz, tptr, run_row, x, y, alpha, win, far,
+            tail_finish<T, kCoo, true>(w0 + k, lane, nnz, tptr, run_row, row_map, x, y, alpha, win, far,
                                        xg, run[k & 1]);
         }
     }
@@ -359,22 +372,22 @@ static hipError_t run(const TailView& t, void* y, const void* x, double alpha,
         const int64_t g = std::min<int64_t>(nsteps, kWinGroups);
         if (t.row)
             hipLaunchKernelGGL((k_tail_win<T, true>), dim3((unsigned)g), dim3(1024), 0, stream, t.n,
-                               t.nnz, t.row, t.ptr, t.run_row, t.col, (const T*)t.val,
+                               t.nnz, t.row, t.ptr, t.run_row, t.row_map, t.col, (const T*)t.val,
                                (const T*)x, (T*)y, (T)alpha, nsteps);
         else
             hipLaunchKernelGGL((k_tail_win<T, false>), dim3((unsigned)g), dim3(1024), 0, stream,
-                               t.n, t.nnz, t.row, t.ptr, t.run_row, t.col, (const T*)t.val,
+                               t.n, t.nnz, t.row, t.ptr, t.run_row, t.row_map, t.col, (const T*)t.val,
                                (const T*)x, (T*)y, (T)alpha, nsteps);
         return hipGetLastError();
     }
     const int64_t blocks = (waves + 3) / 4;
     if (t.row)
         hipLaunchKernelGGL((k_tail<T, true>), dim3((unsigned)blocks), dim3(256), 0, stream, t.n,
-                           t.nnz, t.row, t.ptr, t.run_row, t.col, (const T*)t.val,
+                           t.nnz, t.row, t.ptr, t.run_row, t.row_map, t.col, (const T*)t.val,
                            (const T*)x, (T*)y, (T)alpha);
     else
         hipLaunchKernelGGL((k_tail<T, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                           t.n, t.nnz, t.row, t.ptr, t.run_row, t.col, (const T*)t.val,
+                           t.n, t.nnz, t.row, t.ptr, t.run_row, t.row_map, t.col, (const T*)t.val,
                            (const T*)x, (T*)y, (T)alpha);
     return hipGetLastError();
 }
