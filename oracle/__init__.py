@@ -66,7 +66,7 @@ def _load():
         lib.oracle_ell_pad_fraction.restype = ctypes.c_double
         lib.oracle_sell_layout.argtypes = [I64, P, I64, P, P, P]
         lib.oracle_sell_layout.restype = I64
-        lib.oracle_sell_fill.argtypes = [I64, P, P, P, ctypes.c_int, P, P, P, P]
+        lib.oracle_sell_fill.argtypes = [I64, P, P, P, ctypes.c_int, P, P, ctypes.c_int, P, P]
         lib.oracle_hyb_width.argtypes = [I64, P, I64]
         lib.oracle_hyb_width.restype = I64
         lib.oracle_tail_nnz.argtypes = [I64, P, I64]
@@ -172,10 +172,11 @@ def ell_pad_fraction(a, width: int) -> float:
     return float(_load().oracle_ell_pad_fraction(a.n, _p(_c(a.rowptr, np.int64)), int(width)))
 
 
-def sell(a, sigma: int = 0):
+def sell(a, sigma: int = 0, permuted: bool = False):
     """SELL-64: (perm[n] int64, slice_ptr[S/64+1] int64, len_sorted[S] int32,
     col[slots] int32, val[slots]).  sigma > 0 sorts only inside aligned
-    windows of sigma rows (0: all rows at once)."""
+    windows of sigma rows (0: all rows at once).  permuted: the columns of the
+    permuted basis P A P^T ((P v)[r] = v[perm[r]])."""
     lib = _load()
     rowptr = _c(a.rowptr, np.int64)
     S = pad64(a.n)
@@ -187,7 +188,7 @@ def sell(a, sigma: int = 0):
     oc = np.empty(total, dtype=np.int32)
     ov = np.empty(total, dtype=val.dtype)
     lib.oracle_sell_fill(a.n, _p(rowptr), _p(_c(a.col, np.int32)), _p(val), val.itemsize,
-                         _p(perm), _p(sp), _p(oc), _p(ov))
+                         _p(perm), _p(sp), int(bool(permuted)), _p(oc), _p(ov))
     return perm, sp, ls, oc, ov
 
 

@@ -321,15 +321,28 @@ int64_t oracle_sell_layout(int64_t n, const int64_t *rowptr, int64_t sigma, int6
     return slice_ptr[ns];
 }
 
-/* SELL-64 fill given the layout from oracle_sell_layout */
+/*
+ * SELL-64 fill given the layout from oracle_sell_layout.  permuted != 0
+ * stores the matrix of the permuted basis, P A P^T with (P v)[r] =
+ * v[perm[r]] (the form in which "Sparse matrix-vector multiplication on
+ * GPGPU clusters", Sect. 2.2, runs a whole solve): column c becomes the
+ * sorted position of row c, inv[c] with perm[inv[c]] = c.  Pads stay 0.
+ */
 void oracle_sell_fill(int64_t n, const int64_t *rowptr, const int32_t *col,
                       const void *val, int vsize, const int64_t *perm,
-                      const int64_t *slice_ptr, int32_t *out_col, void *out_val)
+                      const int64_t *slice_ptr, int permuted, int32_t *out_col,
+                      void *out_val)
 {
     int64_t S = pad64(n), ns = S / 64;
     int64_t total = slice_ptr[ns];
     char *ov = (char *)out_val;
     const char *iv = (const char *)val;
+    int64_t *inv = NULL;
+    if (permuted) {
+        inv = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+        for (int64_t r = 0; r < n; ++r)
+            inv[perm[r]] = r;
+    }
     memset(out_col, 0, (size_t)total * sizeof(int32_t));
     memset(ov, 0, (size_t)total * (size_t)vsize);
     for (int64_t r = 0; r < n; ++r) {
@@ -338,10 +351,11 @@ void oracle_sell_fill(int64_t n, const int64_t *rowptr, const int32_t *col,
         for (int64_t j = 0; j < len; ++j) {
             int64_t slot = slice_ptr[r / 64] + 64 * j + r % 64;
             int64_t k = rowptr[i] + j;
-            out_col[slot] = col[k];
+            out_col[slot] = permuted ? (int32_t)inv[col[k]] : col[k];
             memcpy(ov + slot * vsize, iv + k * vsize, (size_t)vsize);
         }
     }
+    free(inv);
 }
 
 /* HYB/HEC ELL width: the ceil(n/3) rule, or the requested width clamped */

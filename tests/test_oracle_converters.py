@@ -299,3 +299,32 @@ def test_sell_windowed_sort():
     Lp = np.concatenate([L[perm], np.zeros(oracle.pad64(b.n) - b.n, np.int64)])
     assert np.array_equal(widths, Lp.reshape(-1, 64).max(axis=1))
     same_rows(b, *sell_to_csr(b.n, perm, sp, ls, sc, sv))
+
+
+def test_sell_permuted_basis():
+    """Permuted basis: row r of P A P^T is row perm[r] of A with every column c
+    replaced by its sorted position (hand example, then a round trip)."""
+    a = _hand5()   # lengths 2, 1, 0, 3, 1; sorted: 3, 0, 1, 4, 2
+    perm, sp, ls, sc, sv = oracle.sell(a, permuted=True)
+    assert list(perm) == [3, 0, 1, 4, 2]
+    inv = {int(p): r for r, p in enumerate(perm)}
+    # sorted positions: row 3 -> 0, 0 -> 1, 1 -> 2, 4 -> 3, 2 -> 4
+    assert inv == {3: 0, 0: 1, 1: 2, 4: 3, 2: 4}
+    # row 3 of A (lane 0): cols 2, 3, 4 -> 4, 0, 3 in columns 0..2 of the slice
+    assert [sc[0], sc[64], sc[128]] == [4, 0, 3]
+    # row 0 (lane 1): cols 4, 1 -> 3, 2; row 1 (lane 2): col 0 -> 1; row 4 (lane 3): col 1 -> 2
+    assert [sc[1], sc[65], sc[2], sc[3]] == [3, 2, 1, 2]
+    plain = oracle.sell(a)
+    assert sv.tobytes() == plain[4].tobytes() and np.array_equal(sp, plain[1])
+    b = random_csr(1000, seed=38, density=0.01, empty_frac=0.2, long_rows=3, long_len=700)
+    perm, sp, ls, sc, sv = oracle.sell(b, sigma=128, permuted=True)
+    rows_c, rows_v = sell_to_csr(b.n, perm, sp, ls, sc, sv)
+    # undo the renumbering: sorted position -> original row
+    same_rows(b, [perm[c] for c in rows_c], rows_v)
+    # the permuted product equals the permuted original product
+    x = np.random.default_rng(3).standard_normal(b.n)
+    y = oracle.spmv(b, x)[0]
+    A_perm = CSR(b.n, np.concatenate([[0], np.cumsum(b.row_lengths()[perm])]).astype(np.int64),
+                 np.concatenate(rows_c).astype(np.int32), np.concatenate(rows_v))
+    yp = oracle.spmv(A_perm, x[perm])[0]
+    assert np.allclose(yp, y[perm], rtol=0, atol=1e-12 * np.abs(y).max())
