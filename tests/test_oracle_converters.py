@@ -324,7 +324,9 @@ def test_sell_permuted_basis():
     # the permuted product equals the permuted original product
     x = np.random.default_rng(3).standard_normal(b.n)
     y = oracle.spmv(b, x)[0]
+    # rows_c / rows_v are indexed by original row: row r of P A P^T is row perm[r]
     A_perm = CSR(b.n, np.concatenate([[0], np.cumsum(b.row_lengths()[perm])]).astype(np.int64),
-                 np.concatenate(rows_c).astype(np.int32), np.concatenate(rows_v))
+                 np.concatenate([rows_c[p] for p in perm]).astype(np.int32),
+                 np.concatenate([rows_v[p] for p in perm]))
     yp = oracle.spmv(A_perm, x[perm])[0]
     assert np.allclose(yp, y[perm], rtol=0, atol=1e-12 * np.abs(y).max())
