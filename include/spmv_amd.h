@@ -150,6 +150,14 @@ typedef struct {
      *            The ELL part then keeps a position -> row permutation.
      *   ELL-R / CSR: must be -1 or 0. */
     int32_t sort_window;
+    /* SELL-64: 1 stores the matrix of the permuted basis, P A P^T with
+     * (P v)[r] = v[perm[r]] (perm = spmv_export SPMV_A_SELL_PERM): spmv_apply
+     * then takes x and y in sorted row order (x'[r] = x[perm[r]]) and writes y
+     * without the scatter through the permutation -- the form in which
+     * "Sparse matrix-vector multiplication on GPGPU clusters" (Sect. 2.2) runs
+     * a whole solve.  spmv_permute moves vectors between the bases.  0: the
+     * caller's basis.  Must be 0 for the other formats. */
+    int32_t permuted_basis;
     /* Largest device footprint a padded format (ELL-R) may take, in bytes;
      * 0 means 75% of the device's memory. */
     uint64_t footprint_budget_bytes;
@@ -174,6 +182,7 @@ typedef struct {
     int32_t x_window;      /* 1 when the active format stages x in LDS */
     int32_t csr_rows;      /* CSR: rows per lane group (1, 2 or 4) */
     int32_t csr_kernel;    /* CSR: SPMV_CSR_VECTOR or SPMV_CSR_BALANCED */
+    int32_t permuted_basis; /* SELL-64: 1 when apply works in the sorted basis */
     int32_t sort_window;   /* SELL-64 / HYB / HEC: rows per sort window in
                               effect (0: rows kept in order; SELL-64 with
                               all rows sorted at once reports n) */
@@ -262,6 +271,19 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts *opts);
  */
 int spmv_apply(spmv_t h, void *y, const void *x, double alpha, double beta,
                void *stream);
+
+/*
+ * spmv_permute -- move a vector between the caller's basis and the sorted
+ * basis of the active SELL-64 format (the permutation of its rows, with or
+ * without permuted_basis):
+ *   direction 0: dst[r] = src[perm[r]]   (caller's basis -> sorted)
+ *   direction 1: dst[perm[r]] = src[r]   (sorted -> caller's basis)
+ *   dst, src  device dtype[n], must not overlap
+ * Asynchronous on `stream`; moves the values exactly.
+ * Errors: STATE (null handle, active format not SELL-64), INVALID_ARG
+ * (null pointer, overlap, bad direction), HIP.
+ */
+int spmv_permute(spmv_t h, void *dst, const void *src, int direction, void *stream);
 
 /* spmv_destroy -- free every device buffer of the handle (synchronises the
  * device first).  A NULL handle is accepted.  Errors: HIP. */

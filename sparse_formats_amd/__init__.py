@@ -51,7 +51,7 @@ class _ConvertOpts(ctypes.Structure):
     _fields_ = [("ell_width", ctypes.c_int32), ("subwave", ctypes.c_int32),
                 ("x_window", ctypes.c_int32), ("csr_rows", ctypes.c_int32),
                 ("csr_kernel", ctypes.c_int32), ("sort_window", ctypes.c_int32),
-                ("footprint_budget_bytes", ctypes.c_uint64)]
+                ("permuted_basis", ctypes.c_int32), ("footprint_budget_bytes", ctypes.c_uint64)]
 
 
 class _Info(ctypes.Structure):
@@ -62,7 +62,8 @@ class _Info(ctypes.Structure):
                 ("subwave", ctypes.c_int32), ("nslices", ctypes.c_int32),
                 ("footprint_bytes", ctypes.c_uint64), ("x_window", ctypes.c_int32),
                 ("csr_rows", ctypes.c_int32), ("csr_kernel", ctypes.c_int32),
-                ("sort_window", ctypes.c_int32), ("band_fraction", ctypes.c_double),
+                ("permuted_basis", ctypes.c_int32), ("sort_window", ctypes.c_int32),
+                ("band_fraction", ctypes.c_double),
                 ("ell_rows", ctypes.c_int64)]
 
 
@@ -74,6 +75,7 @@ def _load():
     lib.spmv_create.argtypes = [ctypes.POINTER(P), I, I64, I64, P, P, P, I, P]
     lib.spmv_convert.argtypes = [P, I, ctypes.POINTER(_ConvertOpts)]
     lib.spmv_apply.argtypes = [P, P, P, D, D, P]
+    lib.spmv_permute.argtypes = [P, P, P, I, P]
     lib.spmv_destroy.argtypes = [P]
     lib.spmv_info.argtypes = [P, ctypes.POINTER(_Info)]
     lib.spmv_export.argtypes = [P, I, P, I64, ctypes.POINTER(I64)]
@@ -161,14 +163,15 @@ class Matrix:
 
     def convert(self, fmt: str, ell_width: int = -1, subwave: int = 0, x_window: int = -1,
                 footprint_budget: int = 0, csr_rows: int = 0,
-                csr_kernel: str = "auto", sort_window: int = -1) -> "Matrix":
+                csr_kernel: str = "auto", sort_window: int = -1,
+                permuted_basis: int = 0) -> "Matrix":
         """Build `fmt` on the device and make it active (options as in spmv_convert_opts;
         csr_kernel is "auto", "vector" or "balanced")."""
         if fmt not in FORMATS:
             raise ValueError("unknown format %r (one of %s)" % (fmt, ", ".join(FORMATS)))
         ck = CSR_KERNELS.get(csr_kernel, csr_kernel)
         o = _ConvertOpts(int(ell_width), int(subwave), int(x_window), int(csr_rows), int(ck),
-                         int(sort_window), int(footprint_budget))
+                         int(sort_window), int(permuted_basis), int(footprint_budget))
         _check(_lib.spmv_convert(self._h, FORMATS[fmt], ctypes.byref(o)))
         return self
 
@@ -180,6 +183,18 @@ class Matrix:
         _check(_lib.spmv_apply(self._h, _dev(y, self.dtype, "y"), _dev(x, self.dtype, "x"),
                                float(alpha), float(beta), _stream(stream)))
         return y
+
+    def permute(self, dst, src, inverse: bool = False, stream=None):
+        """Move a vector between the caller's basis and the sorted basis of the
+        active SELL-64 format: dst[r] = src[perm[r]], or dst[perm[r]] = src[r]
+        when inverse."""
+        for t, nm in ((dst, "dst"), (src, "src")):
+            if t.numel() != self.n:
+                raise ValueError("%s must have n = %d entries" % (nm, self.n))
+        _check(_lib.spmv_permute(self._h, _dev(dst, self.dtype, "dst"),
+                                 _dev(src, self.dtype, "src"), 1 if inverse else 0,
+                                 _stream(stream)))
+        return dst
 
     def info(self) -> dict:
         i = _Info()

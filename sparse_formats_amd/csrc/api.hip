@@ -111,8 +111,10 @@ struct Built {
     // (tail_rows: those rows; tail_cptr: their starts + the end)
     int64_t tail_nrows = 0;
     DevBuf tail_rows, tail_cptr;
-    // CSR: entry-balanced kernel (chunk_row over the whole matrix)
+    // CSR: entry-balanced kernel (run rows over the whole matrix)
     bool csr_balanced = false;
+    // SELL-64 in the permuted basis (x and y in sorted row order)
+    bool permuted = false;
     // x staged in LDS by the ELL / tail kernels
     bool window = false;
     double band_fraction = 0;
@@ -378,6 +380,13 @@ __global__ void k_iota(int64_t n, int* __restrict__ out) {
         out[i] = (int)i;
 }
 
+// inv[perm[r]] = r
+__global__ void k_invert_perm(int64_t n, const int* __restrict__ perm, int* __restrict__ inv) {
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < n;
+         r += (int64_t)gridDim.x * blockDim.x)
+        inv[perm[r]] = (int)r;
+}
+
 // lengths in sorted order (0 for the padding rows)
 __global__ void k_sell_len(int64_t n, int64_t S, const int* __restrict__ rowptr,
                            const int* __restrict__ perm, int* __restrict__ slen) {
@@ -402,9 +411,9 @@ __global__ void k_sell_width(int64_t ns, const int* __restrict__ slen,
 template <typename V>
 __global__ void k_sell_fill(int64_t n, int64_t nslices, const int* __restrict__ rowptr,
                             const int* __restrict__ col, const V* __restrict__ val,
-                            const int* __restrict__ perm, const int64_t* __restrict__ sp,
-                            const int* __restrict__ slen, int* __restrict__ scol,
-                            V* __restrict__ sval) {
+                            const int* __restrict__ perm, const int* __restrict__ inv,
+                            const int64_t* __restrict__ sp, const int* __restrict__ slen,
+                            int* __restrict__ scol, V* __restrict__ sval) {
     const int64_t s = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (s >= nslices) return;
     const int lane = threadIdx.x & 63;
@@ -416,7 +425,8 @@ __global__ void k_sell_fill(int64_t n, int64_t nslices, const int* __restrict__ 
     for (int64_t j = 0; j < w; ++j) {
         const int64_t slot = base + 64 * j + lane;
         if (j < L) {
-            scol[slot] = col[k0 + j];
+            // permuted basis: column c becomes the sorted position of row c
+            scol[slot] = inv ? inv[col[k0 + j]] : col[k0 + j];
             sval[slot] = val[k0 + j];
         } else {
             scol[slot] = 0;
@@ -572,11 +582,13 @@ double ell_pad_fraction(const spmv_handle* h, int64_t W, hipStream_t s) {
 
 // sort_window: -1 sorts inside windows of kSellSortWindow rows, 0 keeps
 // the row order, k >= 1 sorts inside aligned windows of k rows (k >= n: all
-// rows at once, the pJDS order)
+// rows at once, the pJDS order).  permuted: store P A P^T (columns renumbered
+// to sorted positions; apply works in the sorted basis).
 template <typename V>
-void build_sell(const spmv_handle* h, int sort_window, Built& b, hipStream_t s) {
+void build_sell(const spmv_handle* h, int sort_window, bool permuted, Built& b, hipStream_t s) {
     const int64_t n = h->n, S = pad64(n), ns = S / 64;
     b.nslices = ns;
+    b.permuted = permuted;
     b.perm.alloc((size_t)std::max<int64_t>(n, 1) * 4);
     b.sell_len.alloc((size_t)S * 4);
     b.slice_ptr.alloc((size_t)(ns + 1) * 8);
@@ -670,11 +682,20 @@ void build_sell(const spmv_handle* h, int sort_window, Built& b, hipStream_t s) 
     b.sell_col.alloc((size_t)b.sell_slots * 4);
     b.sell_val.alloc((size_t)b.sell_slots * sizeof(V));
     if (ns > 0) {
+        DevBuf inv;
+        if (permuted) {
+            inv.alloc((size_t)std::max<int64_t>(n, 1) * 4);
+            hipLaunchKernelGGL(k_invert_perm, dim3(grid_for(n)), dim3(256), 0, s, n,
+                               b.perm.as<int>(), inv.as<int>());
+            hip_check(hipGetLastError(), "invert permutation");
+        }
         hipLaunchKernelGGL(k_sell_fill<V>, dim3((unsigned)((ns + 3) / 4)), dim3(256), 0, s, n,
                            ns, h->rowptr.as<int>(), h->col.as<int>(), h->val.as<V>(),
-                           b.perm.as<int>(), b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
-                           b.sell_col.as<int>(), b.sell_val.as<V>());
+                           b.perm.as<int>(), permuted ? inv.as<int>() : nullptr,
+                           b.slice_ptr.as<int64_t>(),
+                           b.sell_len.as<int>(), b.sell_col.as<int>(), b.sell_val.as<V>());
         hip_check(hipGetLastError(), "sell fill");
+        sync(s);  // before the temporaries are freed
     }
     sync(s);
 }
@@ -833,7 +854,7 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
         case SPMV_SELL64: {
             SellView a{(int)h->n, (int)b.nslices, b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
                        b.perm.as<int>(), b.sell_col.as<int>(), b.sell_val.p, (int)b.nchunks,
-                       b.chunks.as<int4>()};
+                       b.chunks.as<int4>(), b.permuted};
             e = launch_sell(a, f64, y, x, alpha, beta, s);
             break;
         }
@@ -1003,9 +1024,9 @@ void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
         sync(s);
     } else if (format == SPMV_SELL64) {
         if (f64)
-            build_sell<double>(h, o.sort_window, b, s);
+            build_sell<double>(h, o.sort_window, o.permuted_basis != 0, b, s);
         else
-            build_sell<float>(h, o.sort_window, b, s);
+            build_sell<float>(h, o.sort_window, o.permuted_basis != 0, b, s);
     } else {
         if (f64)
             build_split<double>(h, format, o.ell_width, o.sort_window, b, s);
@@ -1177,8 +1198,12 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
         if (!h) fail(SPMV_ERR_STATE, "null handle");
         if (!valid_format(format) && format != SPMV_AUTO)
             fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
-        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0};
+        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0, 0};
         if (opts) o = *opts;
+        if (o.permuted_basis != 0 && o.permuted_basis != 1)
+            fail(SPMV_ERR_INVALID_ARG, "permuted_basis must be 0 or 1");
+        if (o.permuted_basis && format != SPMV_SELL64)
+            fail(SPMV_ERR_INVALID_ARG, "permuted_basis applies to SELL-64 only");
         if (o.sort_window < -1)
             fail(SPMV_ERR_INVALID_ARG, "sort_window must be -1, 0 or positive (got %d)",
                  o.sort_window);
@@ -1223,6 +1248,40 @@ int spmv_apply(spmv_t h, void* y, const void* x, double alpha, double beta, void
     }
     if (h->n == 0) return SPMV_OK;
     const hipError_t e = launch_built(h, h->fmt, h->format, y, x, alpha, beta, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        g_err = std::string("kernel launch failed: ") + hipGetErrorString(e);
+        return SPMV_ERR_HIP;
+    }
+    return SPMV_OK;
+}
+
+int spmv_permute(spmv_t h, void* dst, const void* src, int direction, void* stream) {
+    g_err.clear();
+    if (!h) {
+        g_err = "null handle";
+        return SPMV_ERR_STATE;
+    }
+    if (h->format != SPMV_SELL64) {
+        g_err = "spmv_permute needs SELL-64 as the active format";
+        return SPMV_ERR_STATE;
+    }
+    if (direction != 0 && direction != 1) {
+        g_err = "direction must be 0 (to the sorted basis) or 1 (back)";
+        return SPMV_ERR_INVALID_ARG;
+    }
+    if (h->n == 0) return SPMV_OK;
+    if (!dst || !src) {
+        g_err = "dst or src is NULL";
+        return SPMV_ERR_INVALID_ARG;
+    }
+    const uintptr_t d = (uintptr_t)dst, q = (uintptr_t)src, len = (uintptr_t)(h->n * h->vsize);
+    if (d < q + len && q < d + len) {
+        g_err = "dst and src overlap";
+        return SPMV_ERR_INVALID_ARG;
+    }
+    const hipError_t e = launch_permute(h->n, h->dtype == SPMV_F64, dst, src,
+                                        h->fmt.perm.as<int>(), direction == 1,
+                                        (hipStream_t)stream);
     if (e != hipSuccess) {
         g_err = std::string("kernel launch failed: ") + hipGetErrorString(e);
         return SPMV_ERR_HIP;
@@ -1282,6 +1341,7 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.csr_rows = h->csr_rows;
     i.csr_kernel = h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED : SPMV_CSR_VECTOR;
     i.sort_window = b.sort_window;
+    i.permuted_basis = h->format == SPMV_SELL64 && b.permuted ? 1 : 0;
     i.band_fraction = b.band_fraction;
     *out = i;
     return SPMV_OK;

@@ -85,6 +85,7 @@ struct SellView {
     const void* val;
     int nchunks;               // column chunks of split slices
     const int4* chunks;        // (slice, j0, j1, 0)
+    bool permuted;             // y in sorted order (permuted basis)
 };
 
 struct TailView {
@@ -113,6 +114,9 @@ hipError_t launch_sell(const SellView& a, bool f64, void* y, const void* x, doub
                        double beta, hipStream_t stream);
 hipError_t launch_tail(const TailView& t, bool f64, void* y, const void* x, double alpha,
                        hipStream_t stream);
+// dst[r] = src[perm[r]] (inverse == false) or dst[perm[r]] = src[r]
+hipError_t launch_permute(int64_t n, bool f64, void* dst, const void* src, const int* perm,
+                          bool inverse, hipStream_t stream);
 // y = beta * y for n entries (beta == 0 writes zeros and never reads y)
 hipError_t launch_scale(int64_t n, bool f64, void* y, double beta, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);

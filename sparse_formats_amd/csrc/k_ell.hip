@@ -190,8 +190,9 @@ hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double
 
 // ---------------------------------------------------------------------------
 // SELL-64: wave s runs slice s; lane l runs sorted row 64 s + l and writes
-// y[perm[row]].  Slices wider than kSellSplitWidth only get beta * y here;
-// their columns are added by k_sell_chunks.
+// y[perm[row]] (in the permuted basis y[row]).  Slices wider than
+// kSellSplitWidth only get beta * y here; their columns are added by
+// k_sell_chunks.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_sell(int n, int nslices,
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256) void k_sell(int n, int nslices,
                                               const int* __restrict__ perm,
                                               const int* __restrict__ col,
                                               const T* __restrict__ val, const T* __restrict__ x,
-                                              T* __restrict__ y, T alpha, T beta) {
+                                              T* __restrict__ y, T alpha, T beta, bool permuted) {
     const int64_t s = xcd_tile(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
     if (s >= nslices) return;
     const int lane = threadIdx.x & 63;
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(256) void k_sell(int n, int nslices,
         s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
     }
     if (r < n) {
-        const int row = perm[r];
+        const int64_t row = permuted ? r : perm[r];
         y[row] = axpby((s0 + s1) + (s2 + s3), alpha, beta, y + row);
     }
 }
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(256) void k_sell_chunks(int n, int nchunks,
                                                      const int* __restrict__ col,
                                                      const T* __restrict__ val,
                                                      const T* __restrict__ x, T* __restrict__ y,
-                                                     T alpha) {
+                                                     T alpha, bool permuted) {
     const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w >= nchunks) return;
     const int4 ch = chunks[w];
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(256) void k_sell_chunks(int n, int nchunks,
         const int64_t o = (int64_t)j * 64;
         s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
     }
-    if (r < n && ch.y < L) atomic_add(y + perm[r], alpha * ((s0 + s1) + (s2 + s3)));
+    if (r < n && ch.y < L) atomic_add(y + (permuted ? r : perm[r]), alpha * ((s0 + s1) + (s2 + s3)));
 }
 
 template <typename T>
@@ -280,12 +281,12 @@ static hipError_t run_sell(const SellView& a, void* y, const void* x, double alp
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(k_sell<T>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n, a.nslices,
                        a.slice_ptr, a.len, a.perm, a.col, (const T*)a.val, (const T*)x, (T*)y,
-                       (T)alpha, (T)beta);
+                       (T)alpha, (T)beta, a.permuted);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nchunks == 0) return e;
     hipLaunchKernelGGL(k_sell_chunks<T>, dim3((unsigned)((a.nchunks + 3) / 4)), dim3(256), 0,
                        stream, a.n, a.nchunks, a.chunks, a.slice_ptr, a.len, a.perm, a.col,
-                       (const T*)a.val, (const T*)x, (T*)y, (T)alpha);
+                       (const T*)a.val, (const T*)x, (T*)y, (T)alpha, a.permuted);
     return hipGetLastError();
 }
 
@@ -293,6 +294,34 @@ hipError_t launch_sell(const SellView& a, bool f64, void* y, const void* x, doub
                        double beta, hipStream_t stream) {
     return f64 ? run_sell<double>(a, y, x, alpha, beta, stream)
                : run_sell<float>(a, y, x, alpha, beta, stream);
+}
+
+// dst[r] = src[perm[r]] or dst[perm[r]] = src[r] (vectors between the
+// caller's basis and the sorted one)
+template <typename T>
+__global__ __launch_bounds__(256) void k_permute(int64_t n, T* __restrict__ dst,
+                                                 const T* __restrict__ src,
+                                                 const int* __restrict__ perm, bool inverse) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < n; r += stride) {
+        if (inverse)
+            dst[perm[r]] = src[r];
+        else
+            dst[r] = src[perm[r]];
+    }
+}
+
+hipError_t launch_permute(int64_t n, bool f64, void* dst, const void* src, const int* perm,
+                          bool inverse, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+    if (f64)
+        hipLaunchKernelGGL(k_permute<double>, dim3((unsigned)blocks), dim3(256), 0, stream, n,
+                           (double*)dst, (const double*)src, perm, inverse);
+    else
+        hipLaunchKernelGGL(k_permute<float>, dim3((unsigned)blocks), dim3(256), 0, stream, n,
+                           (float*)dst, (const float*)src, perm, inverse);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -103,6 +103,8 @@ def test_null_handle_errors(lib):
     assert lib.spmv_apply(None, None, None, 1.0, 0.0, None) == -6
     assert lib.spmv_info(None, None) == -6
     assert lib.spmv_export(None, 0, None, 0, None) == -6
+    lib.spmv_permute.argtypes = [P, P, P, ctypes.c_int, P]
+    assert lib.spmv_permute(None, None, None, 0, None) == -6
     assert lib.spmv_destroy(None) == 0
     # copy: misaligned, negative, overlapping
     assert lib.spmv_stream_copy(P(0x1008), P(0x2000), 16, None) == -1

@@ -133,10 +133,14 @@ def test_layouts_bit_exact(name, dtype):
     assert np.array_equal(M.export("sell_len"), ls)
     assert np.array_equal(M.export("sell_col"), sc)
     assert M.export("sell_val").tobytes() == sv.tobytes()
-    for sigma in (0, 1, 64, 128, 1000):
-        # SELL-64 sorted inside windows of sigma rows (0 keeps the order)
-        M.convert("sell64", sort_window=sigma)
-        perm, sp, ls, sc, sv = oracle.sell(a, sigma=max(sigma, 1))
+    for sigma, pb in ((0, 0), (1, 0), (64, 0), (128, 0), (1000, 0), (128, 1), (-1, 1)):
+        # SELL-64 sorted inside windows of sigma rows (0 keeps the order),
+        # in the caller's basis or the permuted one
+        M.convert("sell64", sort_window=sigma, permuted_basis=pb)
+        assert M.info()["permuted_basis"] == pb
+        if sigma < 0:
+            sigma = 8192
+        perm, sp, ls, sc, sv = oracle.sell(a, sigma=max(sigma, 1), permuted=bool(pb))
         assert M.info()["sort_window"] == (0 if sigma <= 1 or a.n <= 1 else min(sigma, a.n))
         assert np.array_equal(M.export("sell_perm"), perm.astype(np.int32))
         assert np.array_equal(M.export("sell_slice_ptr"), sp)
@@ -509,4 +513,52 @@ def test_auto_format(name):
     assert M.info()["format"] != "ellr"
     with pytest.raises(sf.SpmvError):
         M.convert("auto", sort_window=100)
+    M.close()
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("name", ["c1", "ragged", "every_len", "long_spans", "dups_unsorted", "n1",
+                                  "nnz0", "banded"])
+@pytest.mark.parametrize("sigma", [-1, 64, 10 ** 9])
+def test_sell_permuted_basis(name, dtype, sigma):
+    """apply in the sorted basis: y' = P A P^T x' + beta y' with (P v)[r] =
+    v[perm[r]], checked against the oracle in the caller's basis; spmv_permute
+    moves vectors there and back exactly."""
+    a = WINDOW_MATS[name]()
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    x_np, y0_np = vectors(a.n, 21)
+    x_np, y0_np = x_np.astype(npdt), y0_np.astype(npdt)
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n).convert("sell64", sort_window=sigma,
+                                                             permuted_basis=1)
+    if a.n == 0:
+        return
+    perm = M.export("sell_perm").astype(np.int64)
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    xp = torch.empty_like(x)
+    y0p = torch.empty_like(y0)
+    M.permute(xp, x)
+    M.permute(y0p, y0)
+    torch.cuda.synchronize()
+    assert np.array_equal(xp.cpu().numpy(), x_np[perm])     # moves values exactly
+    back = torch.empty_like(x)
+    M.permute(back, xp, inverse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy(), x_np)
+    rows = None if a.n < 100_000 else np.arange(0, a.n, 53)
+    for alpha, beta in AB[:3]:
+        yp = apply(M, xp, y0p, alpha, beta)          # sorted basis
+        y = np.empty_like(yp)
+        y[perm] = yp                                 # back to the caller's basis
+        check(a, x_np, y0_np, alpha, beta, y, dtype, rows=rows,
+              what="sell permuted sigma=%d %s a=%g b=%g" % (sigma, name, alpha, beta))
+    with pytest.raises(sf.SpmvError):
+        M.permute(xp, xp)                            # overlap
+    M.convert("hyb")
+    with pytest.raises(sf.SpmvError):
+        M.permute(xp, x)                             # no permutation active
+    with pytest.raises(sf.SpmvError):
+        M.convert("hyb", permuted_basis=1)
     M.close()
