@@ -158,6 +158,13 @@ typedef struct {
      * a whole solve.  spmv_permute moves vectors between the bases.  0: the
      * caller's basis.  Must be 0 for the other formats. */
     int32_t permuted_basis;
+    /* ELL-R / HYB / HEC without the LDS window: wave groups per tile of 64
+     * rows ("Sparse Linear Algebra on AMD and NVIDIA GPUs -- The Race Is On":
+     * the lanes of a group read one column of consecutive rows, several
+     * groups share the rows).  0 chooses: 16 below 128 tiles of 64 rows
+     * (rows of at least 256 entries), 4 below 512 tiles (rows of at least 16
+     * entries), else 1; or 1, 4, 16. */
+    int32_t ell_groups;
     /* Largest device footprint a padded format (ELL-R) may take, in bytes;
      * 0 means 75% of the device's memory. */
     uint64_t footprint_budget_bytes;
@@ -183,6 +190,7 @@ typedef struct {
     int32_t csr_rows;      /* CSR: rows per lane group (1, 2 or 4) */
     int32_t csr_kernel;    /* CSR: SPMV_CSR_VECTOR or SPMV_CSR_BALANCED */
     int32_t permuted_basis; /* SELL-64: 1 when apply works in the sorted basis */
+    int32_t ell_groups;    /* ELL-R / HYB / HEC: wave groups per 64-row tile */
     int32_t sort_window;   /* SELL-64 / HYB / HEC: rows per sort window in
                               effect (0: rows kept in order; SELL-64 with
                               all rows sorted at once reports n) */

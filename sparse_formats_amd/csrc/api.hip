@@ -98,6 +98,7 @@ struct Built {
     int64_t ell_width = 0, ell_bh = 0, ell_rows = 0;  // width, rows per block, padded rows
     DevBuf ell_col, ell_val, ell_len;
     DevBuf ell_perm;      // sorted ELL part: row at each position (else empty)
+    int ell_groups = 1;   // wave groups per 64-row tile
     int sort_window = 0;  // rows per sort window in effect (0: none)
     // SELL-64
     int64_t nslices = 0, sell_slots = 0;
@@ -816,6 +817,26 @@ void build_split(const spmv_handle* h, int format, int requested, int sort_windo
 
 void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s);
 
+// wave groups per 64-row tile of the ELL kernel (without the LDS window):
+// several groups only when the matrix has too few tiles to fill the GPU and
+// rows long enough to share
+void choose_groups(const spmv_handle* h, int opt, Built& b) {
+    if (b.window) {
+        b.ell_groups = 1;
+        return;
+    }
+    if (opt > 0) {
+        b.ell_groups = opt;
+        return;
+    }
+    const int64_t tiles = (h->n + 63) / 64;  // one wave of 64 rows each
+    const int64_t W = b.ell_width;
+    b.ell_groups = tiles >= kEllGroupTiles               ? 1
+                   : tiles < kEllGroupTiles / 4 && W >= 256 ? 16
+                   : W >= 16                                ? 4
+                                                            : 1;
+}
+
 // launch the kernels of one apply of `format` built in `b`
 hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* y, const void* x,
                         double alpha, double beta, hipStream_t s) {
@@ -839,7 +860,7 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
         case SPMV_HEC: {
             EllView a{(int)h->n, std::max<int64_t>(b.ell_bh, 1), b.ell_width * b.ell_bh,
                       (int)b.ell_width, b.ell_len.as<int>(), b.ell_perm.as<int>(),
-                      b.ell_col.as<int>(), b.ell_val.p, b.window};
+                      b.ell_col.as<int>(), b.ell_val.p, b.window, b.ell_groups};
             e = launch_ell(a, f64, y, x, alpha, beta, s);
             if (e == hipSuccess && format != SPMV_ELLR && b.tail_nnz > 0) {
                 const bool hec = format == SPMV_HEC;
@@ -1021,6 +1042,7 @@ void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
         else
             build_ell_part<float>(h, W, 0, 0, b, s);
         decide_window(h, format, o.x_window, b, s);
+        choose_groups(h, o.ell_groups, b);
         sync(s);
     } else if (format == SPMV_SELL64) {
         if (f64)
@@ -1033,6 +1055,7 @@ void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
         else
             build_split<float>(h, format, o.ell_width, o.sort_window, b, s);
         decide_window(h, format, o.x_window, b, s);
+        choose_groups(h, o.ell_groups, b);
     }
     h->fmt = std::move(b);
     h->format = format;
@@ -1198,8 +1221,10 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
         if (!h) fail(SPMV_ERR_STATE, "null handle");
         if (!valid_format(format) && format != SPMV_AUTO)
             fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
-        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0, 0};
+        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0, 0, 0};
         if (opts) o = *opts;
+        if (o.ell_groups != 0 && o.ell_groups != 1 && o.ell_groups != 4 && o.ell_groups != 16)
+            fail(SPMV_ERR_INVALID_ARG, "ell_groups must be 0, 1, 4 or 16 (got %d)", o.ell_groups);
         if (o.permuted_basis != 0 && o.permuted_basis != 1)
             fail(SPMV_ERR_INVALID_ARG, "permuted_basis must be 0 or 1");
         if (o.permuted_basis && format != SPMV_SELL64)
@@ -1341,6 +1366,9 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.csr_rows = h->csr_rows;
     i.csr_kernel = h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED : SPMV_CSR_VECTOR;
     i.sort_window = b.sort_window;
+    i.ell_groups = (h->format == SPMV_ELLR || h->format == SPMV_HYB || h->format == SPMV_HEC)
+                       ? b.ell_groups
+                       : 0;
     i.permuted_basis = h->format == SPMV_SELL64 && b.permuted ? 1 : 0;
     i.band_fraction = b.band_fraction;
     *out = i;

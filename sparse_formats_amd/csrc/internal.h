@@ -62,6 +62,12 @@ struct CsrView {
 // so that a tile of rows reads one contiguous slab (a few pages) instead of
 // `width` places a whole matrix height apart.
 constexpr int kEllBlock = 1024;
+// ELL with several wave groups per row tile is used (by default) when the
+// matrix has too few 64-row tiles to fill the GPU: 4 groups below
+// kEllGroupTiles tiles, 16 below kEllGroupTiles / 4 (measured on rows of
+// hundreds of entries: 64 tiles 4.3x faster with 16 groups, 313 tiles 1.7x
+// with 4, 1024 tiles best with one)
+constexpr int64_t kEllGroupTiles = 512;
 
 struct EllView {
     int n;
@@ -73,6 +79,7 @@ struct EllView {
     const int* col;
     const void* val;
     bool window;      // stage x in LDS (banded matrices)
+    int groups;       // wave groups per 64-row tile (1, 4 or 16; without the window)
 };
 
 struct SellView {

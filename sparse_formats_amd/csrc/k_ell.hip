@@ -159,6 +159,74 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
     }
 }
 
+// ELLPACK with G wave groups per tile of 64 rows.  "Sparse Linear Algebra on
+// AMD and NVIDIA GPUs -- The Race Is On" keeps the lanes of a group on one
+// column of consecutive rows (coalesced, as in the one-lane-per-row kernel)
+// and gives a row several groups to raise the parallelism of matrices with
+// few, long rows.  Wave g takes the columns g, g + G, g + 2G, ... of its
+// lanes' rows (four in flight); the G partial sums of a row meet in LDS.
+template <typename T, int G>
+__global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bstride,
+                                                   const int* __restrict__ len,
+                                                   const int* __restrict__ perm,
+                                                   const int* __restrict__ col,
+                                                   const T* __restrict__ val,
+                                                   const T* __restrict__ x, T* __restrict__ y,
+                                                   T alpha, T beta) {
+    __shared__ T part[G][kWave];
+    const int lane = threadIdx.x & (kWave - 1), g = threadIdx.x / kWave;
+    const int64_t i = xcd_tile(blockIdx.x, gridDim.x) * kWave + lane;
+    T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    if (i < n) {
+        const int L = len[i];
+        const int64_t base = (i / bh) * bstride + i % bh;
+        const int* c = col + base;
+        const T* v = val + base;
+        int j = g;
+        for (; j + 3 * G < L; j += 4 * G) {
+            const int64_t o = (int64_t)j * bh, d = (int64_t)G * bh;
+            const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + d);
+            const T v2 = ld_nt(v + o + 2 * d), v3 = ld_nt(v + o + 3 * d);
+            const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + d);
+            const int c2 = ld_nt(c + o + 2 * d), c3 = ld_nt(c + o + 3 * d);
+            s0 = fma(v0, x[c0], s0);
+            s1 = fma(v1, x[c1], s1);
+            s2 = fma(v2, x[c2], s2);
+            s3 = fma(v3, x[c3], s3);
+        }
+        for (; j < L; j += G) {
+            const int64_t o = (int64_t)j * bh;
+            s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
+        }
+    }
+    part[g][lane] = (s0 + s1) + (s2 + s3);
+    __syncthreads();
+    if (g == 0 && i < n) {
+        T s = part[0][lane];
+#pragma unroll
+        for (int q = 1; q < G; ++q) s += part[q][lane];
+        const int64_t row = perm ? perm[i] : i;
+        y[row] = axpby(s, alpha, beta, y + row);
+    }
+}
+
+template <typename T>
+static hipError_t run_ell_mg(const EllView& a, void* y, const void* x, double alpha,
+                             double beta, hipStream_t stream) {
+    const int64_t blocks = ((int64_t)a.n + kWave - 1) / kWave;
+    if (a.groups == 16)
+        hipLaunchKernelGGL((k_ell_mg<T, 16>), dim3((unsigned)blocks), dim3(64 * 16), 0, stream,
+                           a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
+                           (const T*)x, (T*)y, (T)alpha, (T)beta);
+    else if (a.groups == 4)
+        hipLaunchKernelGGL((k_ell_mg<T, 4>), dim3((unsigned)blocks), dim3(64 * 4), 0, stream,
+                           a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
+                           (const T*)x, (T*)y, (T)alpha, (T)beta);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t run_ell_win(const EllView& a, void* y, const void* x, double alpha,
                               double beta, hipStream_t stream) {
@@ -177,6 +245,9 @@ hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double
     if (a.window)
         return f64 ? run_ell_win<double>(a, y, x, alpha, beta, stream)
                    : run_ell_win<float>(a, y, x, alpha, beta, stream);
+    if (a.groups > 1)
+        return f64 ? run_ell_mg<double>(a, y, x, alpha, beta, stream)
+                   : run_ell_mg<float>(a, y, x, alpha, beta, stream);
     if (f64)
         hipLaunchKernelGGL(k_ell<double>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
                            a.bh, a.bstride, a.len, a.perm, a.col, (const double*)a.val,

@@ -562,3 +562,41 @@ def test_sell_permuted_basis(name, dtype, sigma):
     with pytest.raises(sf.SpmvError):
         M.convert("hyb", permuted_basis=1)
     M.close()
+
+
+def _short_wide():
+    # few rows (under one tile per CU), long rows of mixed length
+    rng = np.random.default_rng(49)
+    return random_csr(1500, seed=49, lens=rng.integers(200, 3000, 1500))
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("name", ["short_wide", "c1", "ragged", "every_len", "long_spans", "n1",
+                                  "nnz0"])
+@pytest.mark.parametrize("fmt,kw", [("ellr", {}), ("hyb", dict(ell_width=10 ** 6)),
+                                    ("hec", {}), ("hyb", dict(sort_window=1024))])
+@pytest.mark.parametrize("groups", [0, 4, 16])
+def test_ell_wave_groups(fmt, kw, groups, name, dtype):
+    """ELL kernel with several wave groups per 64-row tile (each group every
+    G-th column, partial sums joined in LDS)."""
+    a = _short_wide() if name == "short_wide" else MATS[name]()
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    x_np, y0_np = vectors(a.n, 22)
+    x_np, y0_np = x_np.astype(npdt), y0_np.astype(npdt)
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n).convert(fmt, ell_groups=groups, x_window=0,
+                                                             **kw)
+    g = M.info()["ell_groups"]
+    if groups:
+        assert g == groups
+    elif name == "short_wide" and fmt == "ellr":
+        assert g == 16          # 24 tiles of 64 rows, rows of hundreds of entries
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    for alpha, beta in AB[:3]:
+        check(a, x_np, y0_np, alpha, beta, apply(M, x, y0, alpha, beta), dtype,
+              what="%s %s groups=%d %s" % (fmt, kw, g, name))
+    with pytest.raises(sf.SpmvError):
+        M.convert(fmt, ell_groups=8)
+    M.close()
