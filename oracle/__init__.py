@@ -18,6 +18,7 @@ Functions (each restates a definition from the pages; see oracle.c):
 * ``hyb_width``  -- the ELL width of the HYB/HEC split.
 * ``tail``       -- the irregular part of the split as COO and CSR.
 * ``check``      -- the per-entry tolerance test |y - y_ref| <= tol * scale.
+* ``cg``, ``bicgstab`` -- textbook Krylov solvers over the product (fp64).
 """
 from __future__ import annotations
 
@@ -72,6 +73,9 @@ def _load():
         lib.oracle_tail_nnz.argtypes = [I64, P, I64]
         lib.oracle_tail_nnz.restype = I64
         lib.oracle_tail.argtypes = [I64, P, P, P, ctypes.c_int, I64, P, P, P, P]
+        for f in (lib.oracle_cg, lib.oracle_bicgstab):
+            f.argtypes = [I64, P, P, P, P, P, ctypes.c_double, ctypes.c_int, P]
+            f.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -209,3 +213,25 @@ def tail(a, K: int):
     lib.oracle_tail(a.n, _p(rowptr), _p(_c(a.col, np.int32)), _p(val), val.itemsize, int(K),
                     _p(orow), _p(optr), _p(oc), _p(ov))
     return orow, optr, oc, ov
+
+
+def _solve(fn, a, b, x0, rtol, max_iter):
+    rowptr = _c(a.rowptr, np.int64)
+    val = _c(a.val, np.float64)
+    bb = _c(b, np.float64)
+    x = np.array(np.zeros(a.n) if x0 is None else x0, dtype=np.float64)
+    rel = ctypes.c_double()
+    it = fn(a.n, _p(rowptr), _p(_c(a.col, np.int32)), _p(val), _p(bb), _p(x), float(rtol),
+            int(max_iter), ctypes.byref(rel))
+    return x, int(it), rel.value
+
+
+def cg(a, b, x0=None, rtol: float = 1e-10, max_iter: int = 1000):
+    """Conjugate gradients (A symmetric positive definite): (x, iterations,
+    ||r|| / ||b|| of the recurred residual)."""
+    return _solve(_load().oracle_cg, a, b, x0, rtol, max_iter)
+
+
+def bicgstab(a, b, x0=None, rtol: float = 1e-10, max_iter: int = 1000):
+    """BiCGSTAB (general A): (x, iterations, ||r|| / ||b||)."""
+    return _solve(_load().oracle_bicgstab, a, b, x0, rtol, max_iter)

@@ -418,3 +418,118 @@ void oracle_tail(int64_t n, const int64_t *rowptr, const int32_t *col,
             out_ptr[i + 1] = (int32_t)t;
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* Krylov solvers over the product: the consumers sparse mat-vec serves in */
+/* "Development of Krylov and AMG linear solvers for large-scale sparse   */
+/* matrices on GPUs" (Sect. 3).  Textbook forms: conjugate gradients      */
+/* (Hestenes and Stiefel 1952) for symmetric positive definite A, and     */
+/* BiCGSTAB (van der Vorst 1992) for general A.  Stop when the recurred    */
+/* residual satisfies ||r|| <= rtol * ||b|| (2-norms) or after max_iter    */
+/* iterations.  Products use the Dot2 rows above; inner products are plain */
+/* fp64 sums in index order.                                               */
+/* ---------------------------------------------------------------------- */
+
+static void solver_matvec(int64_t n, const int64_t *rowptr, const int32_t *col,
+                          const double *val, const double *x, double *y)
+{
+    double ab;
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = row_dot2(rowptr[i], rowptr[i + 1], col, val, x, &ab);
+}
+
+static double solver_dot(int64_t n, const double *a, const double *b)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        s += a[i] * b[i];
+    return s;
+}
+
+/* x holds the initial guess on entry and the solution on return.  Returns
+ * the iterations taken; *rel_res = ||r|| / ||b|| of the last residual. */
+int oracle_cg(int64_t n, const int64_t *rowptr, const int32_t *col, const double *val,
+              const double *b, double *x, double rtol, int max_iter, double *rel_res)
+{
+    double *r = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double *p = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double *q = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double bnorm = sqrt(solver_dot(n, b, b));
+    int k = 0;
+    solver_matvec(n, rowptr, col, val, x, q);
+    for (int64_t i = 0; i < n; ++i) {
+        r[i] = b[i] - q[i];
+        p[i] = r[i];
+    }
+    double rr = solver_dot(n, r, r);
+    while (sqrt(rr) > rtol * bnorm && k < max_iter) {
+        solver_matvec(n, rowptr, col, val, p, q);
+        double alpha = rr / solver_dot(n, p, q);
+        for (int64_t i = 0; i < n; ++i) {
+            x[i] += alpha * p[i];
+            r[i] -= alpha * q[i];
+        }
+        double rr_new = solver_dot(n, r, r);
+        double beta = rr_new / rr;
+        for (int64_t i = 0; i < n; ++i)
+            p[i] = r[i] + beta * p[i];
+        rr = rr_new;
+        ++k;
+    }
+    *rel_res = bnorm > 0 ? sqrt(rr) / bnorm : sqrt(rr);
+    free(r);
+    free(p);
+    free(q);
+    return k;
+}
+
+int oracle_bicgstab(int64_t n, const int64_t *rowptr, const int32_t *col, const double *val,
+                    const double *b, double *x, double rtol, int max_iter, double *rel_res)
+{
+    size_t sz = (size_t)(n > 0 ? n : 1) * sizeof(double);
+    double *r = (double *)malloc(sz), *rh = (double *)malloc(sz), *p = (double *)malloc(sz);
+    double *v = (double *)malloc(sz), *s = (double *)malloc(sz), *t = (double *)malloc(sz);
+    double bnorm = sqrt(solver_dot(n, b, b));
+    int k = 0;
+    solver_matvec(n, rowptr, col, val, x, t);
+    for (int64_t i = 0; i < n; ++i) {
+        r[i] = b[i] - t[i];
+        rh[i] = r[i];
+        p[i] = 0.0;
+        v[i] = 0.0;
+    }
+    double rho = 1.0, alpha = 1.0, omega = 1.0;
+    double rr = solver_dot(n, r, r);
+    while (sqrt(rr) > rtol * bnorm && k < max_iter) {
+        double rho_new = solver_dot(n, rh, r);
+        if (rho_new == 0.0)
+            break; /* breakdown */
+        double beta = (rho_new / rho) * (alpha / omega);
+        for (int64_t i = 0; i < n; ++i)
+            p[i] = r[i] + beta * (p[i] - omega * v[i]);
+        solver_matvec(n, rowptr, col, val, p, v);
+        alpha = rho_new / solver_dot(n, rh, v);
+        for (int64_t i = 0; i < n; ++i)
+            s[i] = r[i] - alpha * v[i];
+        solver_matvec(n, rowptr, col, val, s, t);
+        double tt = solver_dot(n, t, t);
+        omega = tt > 0 ? solver_dot(n, t, s) / tt : 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            x[i] += alpha * p[i] + omega * s[i];
+            r[i] = s[i] - omega * t[i];
+        }
+        rr = solver_dot(n, r, r);
+        rho = rho_new;
+        ++k;
+        if (omega == 0.0)
+            break; /* s was already the residual of x + alpha p */
+    }
+    *rel_res = bnorm > 0 ? sqrt(rr) / bnorm : sqrt(rr);
+    free(r);
+    free(rh);
+    free(p);
+    free(v);
+    free(s);
+    free(t);
+    return k;
+}
