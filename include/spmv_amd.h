@@ -293,6 +293,44 @@ int spmv_apply(spmv_t h, void *y, const void *x, double alpha, double beta,
  */
 int spmv_permute(spmv_t h, void *dst, const void *src, int direction, void *stream);
 
+/* Krylov solvers over spmv_apply ("Development of Krylov and AMG linear
+ * solvers for large-scale sparse matrices on GPUs", Sect. 3: the solvers the
+ * sparse product serves) */
+typedef enum {
+    SPMV_SOLVE_CG = 0,       /* conjugate gradients: A symmetric positive definite */
+    SPMV_SOLVE_BICGSTAB = 1  /* BiCGSTAB (van der Vorst): general A */
+} spmv_solve_method;
+
+typedef struct {
+    int32_t method;     /* spmv_solve_method */
+    int32_t max_iter;   /* iteration cap (> 0) */
+    double rtol;        /* stop when ||r|| <= rtol * ||b|| (2-norms, recurred
+                           residual r) */
+} spmv_solve_opts;
+
+typedef struct {
+    int32_t iterations;   /* iterations taken */
+    int32_t converged;    /* 1 when ||r|| <= rtol * ||b|| */
+    double rel_residual;  /* ||r|| / ||b|| (||r|| when b = 0) */
+} spmv_solve_info;
+
+/*
+ * spmv_solve -- solve A x = b with the active format's apply.
+ *   x     device dtype[n]: the initial guess on entry, the solution on return
+ *   b     device dtype[n], must not overlap x
+ *   opts  method, iteration cap, relative tolerance
+ *   info  host out-parameter (may be NULL)
+ * Vector updates are fused kernels; inner products are fp64 sums in a fixed
+ * order.  The host drives the iteration (it reads back two scalars per
+ * iteration), so the call is synchronous on `stream`.  Work vectors (3 n for
+ * CG, 6 n for BiCGSTAB) are allocated for the call.  Not reaching the
+ * tolerance is not an error (info->converged = 0).
+ * Errors: STATE, INVALID_ARG (null pointer, overlap, bad method / cap /
+ * tolerance), NO_MEMORY, HIP.
+ */
+int spmv_solve(spmv_t h, void *x, const void *b, const spmv_solve_opts *opts,
+               spmv_solve_info *info, void *stream);
+
 /* spmv_destroy -- free every device buffer of the handle (synchronises the
  * device first).  A NULL handle is accepted.  Errors: HIP. */
 int spmv_destroy(spmv_t h);

@@ -55,6 +55,15 @@ class _ConvertOpts(ctypes.Structure):
                 ("footprint_budget_bytes", ctypes.c_uint64)]
 
 
+class _SolveOpts(ctypes.Structure):
+    _fields_ = [("method", ctypes.c_int32), ("max_iter", ctypes.c_int32), ("rtol", ctypes.c_double)]
+
+
+class _SolveInfo(ctypes.Structure):
+    _fields_ = [("iterations", ctypes.c_int32), ("converged", ctypes.c_int32),
+                ("rel_residual", ctypes.c_double)]
+
+
 class _Info(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("nnz", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("format", ctypes.c_int32), ("max_len", ctypes.c_int32),
@@ -78,6 +87,7 @@ def _load():
     lib.spmv_convert.argtypes = [P, I, ctypes.POINTER(_ConvertOpts)]
     lib.spmv_apply.argtypes = [P, P, P, D, D, P]
     lib.spmv_permute.argtypes = [P, P, P, I, P]
+    lib.spmv_solve.argtypes = [P, P, P, ctypes.POINTER(_SolveOpts), ctypes.POINTER(_SolveInfo), P]
     lib.spmv_destroy.argtypes = [P]
     lib.spmv_info.argtypes = [P, ctypes.POINTER(_Info)]
     lib.spmv_export.argtypes = [P, I, P, I64, ctypes.POINTER(I64)]
@@ -198,6 +208,23 @@ class Matrix:
                                  _dev(src, self.dtype, "src"), 1 if inverse else 0,
                                  _stream(stream)))
         return dst
+
+    def solve(self, b, x=None, method: str = "cg", rtol: float = 1e-10, max_iter: int = 1000,
+              stream=None):
+        """Solve A x = b with the active format (method "cg" for symmetric
+        positive definite A, "bicgstab" otherwise).  x: initial guess, updated
+        in place (zeros when None).  Returns (x, info dict)."""
+        import torch
+        if b.numel() != self.n:
+            raise ValueError("b must have n = %d entries" % self.n)
+        if x is None:
+            x = torch.zeros_like(b)
+        o = _SolveOpts({"cg": 0, "bicgstab": 1}[method], int(max_iter), float(rtol))
+        info = _SolveInfo()
+        _check(_lib.spmv_solve(self._h, _dev(x, self.dtype, "x"), _dev(b, self.dtype, "b"),
+                               ctypes.byref(o), ctypes.byref(info), _stream(stream)))
+        return x, {"iterations": info.iterations, "converged": bool(info.converged),
+                   "rel_residual": info.rel_residual}
 
     def info(self) -> dict:
         i = _Info()

@@ -11,6 +11,7 @@
 #include <rocprim/iterator/counting_iterator.hpp>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <functional>
@@ -1105,6 +1106,93 @@ void convert_auto(spmv_handle* h, const spmv_convert_opts& o) {
 }
 
 
+// Krylov solvers driven from the host: every product is the active format's
+// apply; the scalars of an iteration are two fp64 inner products read back
+// (the textbook forms of conjugate gradients and BiCGSTAB, stopping on the
+// recurred residual).
+spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_opts& o,
+                      hipStream_t s) {
+    const int64_t n = h->n;
+    const bool f64 = h->dtype == SPMV_F64;
+    const size_t vb = (size_t)n * h->vsize;
+    const int nvec = o.method == SPMV_SOLVE_CG ? 3 : 6;
+    DevBuf work(vb * nvec), partial((size_t)2 * kSolveBlocks * 8), scal(16);
+    char* w = work.as<char>();
+    void *r = w, *p = w + vb, *q = w + 2 * vb;           // CG: r, p, q = A p
+    void *rh = w + 2 * vb, *v = w + 3 * vb, *sv = w + 4 * vb, *t = w + 5 * vb;  // BiCGSTAB
+    double* pd = partial.as<double>();
+    double* out = scal.as<double>();
+    auto chk = [](hipError_t e, const char* what) { hip_check(e, what); };
+    auto apply = [&](void* yy, const void* xx, double alpha, double beta) {
+        chk(launch_built(h, h->fmt, h->format, yy, xx, alpha, beta, s), "apply");
+    };
+    auto fetch = [&](double* d) {
+        chk(hipMemcpyAsync(d, out, 16, hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+        sync(s);
+    };
+    double d2[2];
+    // b . b and r = b - A x
+    chk(launch_dot2(n, f64, b, b, nullptr, nullptr, pd, out, s), "dot");
+    fetch(d2);
+    const double bnorm = std::sqrt(d2[0]);
+    chk(hipMemcpyAsync(r, b, vb, hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
+    apply(r, x, -1.0, 1.0);
+    chk(launch_dot2(n, f64, r, r, nullptr, nullptr, pd, out, s), "dot");
+    fetch(d2);
+    double rr = d2[0];
+    const double goal = o.rtol * bnorm;
+    int k = 0;
+    if (o.method == SPMV_SOLVE_CG) {
+        chk(hipMemcpyAsync(p, r, vb, hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
+        while (std::sqrt(rr) > goal && k < o.max_iter) {
+            apply(q, p, 1.0, 0.0);
+            chk(launch_dot2(n, f64, p, q, nullptr, nullptr, pd, out, s), "dot");
+            fetch(d2);
+            const double alpha = rr / d2[0];
+            chk(launch_cg_xr(n, f64, x, r, p, q, alpha, pd, out, s), "cg update");
+            fetch(d2);
+            const double beta = d2[0] / rr;
+            chk(launch_update_p(n, f64, p, r, nullptr, beta, 0.0, s), "cg direction");
+            rr = d2[0];
+            ++k;
+        }
+    } else {
+        chk(hipMemcpyAsync(rh, r, vb, hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
+        chk(hipMemsetAsync(p, 0, vb, s), "hipMemsetAsync");
+        chk(hipMemsetAsync(v, 0, vb, s), "hipMemsetAsync");
+        double rho = 1.0, alpha = 1.0, omega = 1.0;
+        while (std::sqrt(rr) > goal && k < o.max_iter) {
+            chk(launch_dot2(n, f64, rh, r, nullptr, nullptr, pd, out, s), "dot");
+            fetch(d2);
+            const double rho_new = d2[0];
+            if (rho_new == 0.0) break;  // breakdown
+            const double beta = (rho_new / rho) * (alpha / omega);
+            chk(launch_update_p(n, f64, p, r, v, beta, omega, s), "bicgstab direction");
+            apply(v, p, 1.0, 0.0);
+            chk(launch_dot2(n, f64, rh, v, nullptr, nullptr, pd, out, s), "dot");
+            fetch(d2);
+            alpha = rho_new / d2[0];
+            chk(launch_axmy(n, f64, sv, r, v, alpha, s), "bicgstab s");
+            apply(t, sv, 1.0, 0.0);
+            chk(launch_dot2(n, f64, t, sv, t, t, pd, out, s), "dot");
+            fetch(d2);
+            omega = d2[1] > 0 ? d2[0] / d2[1] : 0.0;
+            chk(launch_bicg_xr(n, f64, x, r, p, sv, t, alpha, omega, pd, out, s), "bicgstab update");
+            fetch(d2);
+            rr = d2[0];
+            rho = rho_new;
+            ++k;
+            if (omega == 0.0) break;  // s was already the residual of x + alpha p
+        }
+    }
+    sync(s);  // before the work vectors are freed
+    spmv_solve_info res;
+    res.iterations = k;
+    res.rel_residual = bnorm > 0 ? std::sqrt(rr) / bnorm : std::sqrt(rr);
+    res.converged = std::sqrt(rr) <= goal ? 1 : 0;
+    return res;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1312,6 +1400,29 @@ int spmv_permute(spmv_t h, void* dst, const void* src, int direction, void* stre
         return SPMV_ERR_HIP;
     }
     return SPMV_OK;
+}
+
+int spmv_solve(spmv_t h, void* x, const void* b, const spmv_solve_opts* opts,
+               spmv_solve_info* info, void* stream) {
+    g_err.clear();
+    return run_guarded([&] {
+        if (!h) fail(SPMV_ERR_STATE, "null handle");
+        if (!opts) fail(SPMV_ERR_INVALID_ARG, "opts is NULL");
+        const spmv_solve_opts o = *opts;
+        if (o.method != SPMV_SOLVE_CG && o.method != SPMV_SOLVE_BICGSTAB)
+            fail(SPMV_ERR_INVALID_ARG, "unknown method %d", o.method);
+        if (o.max_iter <= 0) fail(SPMV_ERR_INVALID_ARG, "max_iter must be positive");
+        if (!(o.rtol >= 0)) fail(SPMV_ERR_INVALID_ARG, "rtol must be >= 0");
+        const int64_t n = h->n;
+        spmv_solve_info res{0, 1, 0.0};
+        if (n > 0) {
+            if (!x || !b) fail(SPMV_ERR_INVALID_ARG, "x or b is NULL");
+            const uintptr_t xb = (uintptr_t)x, bb = (uintptr_t)b, len = (uintptr_t)(n * h->vsize);
+            if (xb < bb + len && bb < xb + len) fail(SPMV_ERR_INVALID_ARG, "x and b overlap");
+            res = solve(h, x, b, o, (hipStream_t)stream);
+        }
+        if (info) *info = res;
+    });
 }
 
 int spmv_destroy(spmv_t h) {
