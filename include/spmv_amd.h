@@ -168,6 +168,13 @@ typedef struct {
     /* Largest device footprint a padded format (ELL-R) may take, in bytes;
      * 0 means 75% of the device's memory. */
     uint64_t footprint_budget_bytes;
+    /* CSR vector kernel: copy the entries of each wave's rows into LDS with
+     * whole-line loads before the group sums (subwave 2..16, one row per
+     * group).  The LDS slice of a wave holds the entries of 99.5 % of the
+     * waves (at most 1,280 fp64 / 2,048 fp32 entries); the other waves read
+     * directly.  The sums are the same either way.  -1 times both, 0 off,
+     * 1 on. */
+    int32_t csr_stage;
 } spmv_convert_opts;
 
 /* description of a handle (spmv_info) */
@@ -197,6 +204,8 @@ typedef struct {
     double band_fraction;  /* share of entries within the window's reach
                               (computed by ELL-R / HYB / HEC conversions) */
     int64_t ell_rows;      /* ELL-R / HYB / HEC: rows padded to whole blocks */
+    int32_t csr_stage_slots; /* CSR vector kernel staged in LDS: entries one wave
+                                can stage (0: the kernel reads directly) */
 } spmv_info_t;
 
 /* arrays readable with spmv_export */

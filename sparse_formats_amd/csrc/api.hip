@@ -139,7 +139,10 @@ struct spmv_handle {
     int max_len = 0;
     int subwave = 1;
     int csr_rows = 1;     // rows per lane group of the CSR kernel
-    DevBuf rowptr, col, val;  // canonical CSR (int32 row pointer)
+    int csr_stage_slots = 0;  // CSR: LDS slots per wave of the staged kernel (0: direct)
+    bool csr_stage_col_nt = false;  // staged CSR: col read without caching
+    DevBuf rowptr, col, val;  // canonical CSR (int32 row pointer); col and val
+                              // end with 16 zero bytes (whole 16-byte loads)
     Built fmt;                // active non-CSR format (format == CSR: none)
     int format = SPMV_CSR;
 };
@@ -493,6 +496,20 @@ __global__ void k_run_rows(int64_t n, int64_t nruns, const int* __restrict__ ptr
         const int64_t k1 = ((int64_t)ptr[i + 1] + kTailPerLane - 1) / kTailPerLane;
         for (int64_t k = k0; k < k1; ++k) out[k] = (int)i;
         if (i == 0) out[nruns] = (int)(n - 1);
+    }
+}
+
+// Histogram of the LDS slots the staged CSR kernel needs per wave (entries
+// of its rw rows from the 16-byte aligned start), in buckets of 64; the last
+// bucket collects everything above.
+__global__ void k_stage_hist(int64_t n, int rw, const int* __restrict__ ptr, int nb,
+                             unsigned* __restrict__ hist) {
+    const int64_t waves = (n + rw - 1) / rw;
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < waves;
+         w += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r0 = w * rw, r1 = std::min<int64_t>(r0 + rw, n);
+        const int need = ptr[r1] - (ptr[r0] & -4);
+        atomicAdd(&hist[std::min(need / 64, nb - 1)], 1u);
     }
 }
 
@@ -852,8 +869,9 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
                 if (e == hipSuccess) e = launch_tail(t, f64, y, x, alpha, s);
                 break;
             }
-            CsrView a{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
-            e = launch_csr(a, h->subwave, h->csr_rows, f64, y, x, alpha, beta, s);
+            CsrView a{(int)h->n, (int)h->nnz, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
+            e = launch_csr(a, h->subwave, h->csr_rows, h->csr_stage_slots, h->csr_stage_col_nt,
+                           f64, y, x, alpha, beta, s);
             break;
         }
         case SPMV_ELLR:
@@ -905,15 +923,49 @@ float time_launches(F&& launch, hipStream_t s) {
 
 
 
+// LDS slots per wave of the staged CSR kernel with `sw` lanes per row: the
+// fewest multiples of 64 that hold the entries of 99.5 % of the waves (one
+// outlier wave would otherwise set the LDS of all and lower the occupancy;
+// waves that do not fit read directly), at least 256, at most what four
+// slices per workgroup allow.
+int stage_slots_for(const spmv_handle* h, int sw, hipStream_t s) {
+    const int max_slots = csr_stage_max_slots(h->dtype == SPMV_F64);
+    const int rw = 64 / sw, nb = max_slots / 64 + 1;
+    const int64_t waves = (h->n + rw - 1) / rw;
+    if (waves == 0) return 256;
+    DevBuf hist((size_t)nb * 4);
+    hip_check(hipMemsetAsync(hist.p, 0, hist.bytes, s), "hipMemsetAsync");
+    hipLaunchKernelGGL(k_stage_hist, dim3(grid_for(waves)), dim3(256), 0, s, h->n, rw,
+                       h->rowptr.as<int>(), nb, hist.as<unsigned>());
+    hip_check(hipGetLastError(), "stage histogram");
+    std::vector<unsigned> c(nb);
+    hip_check(hipMemcpyAsync(c.data(), hist.p, hist.bytes, hipMemcpyDeviceToHost, s),
+              "hipMemcpyAsync");
+    sync(s);
+    int64_t cum = 0;
+    int slots = max_slots;
+    for (int b = 0; b < nb - 1; ++b) {
+        cum += c[b];
+        if ((double)cum >= 0.995 * (double)waves) {
+            slots = (b + 1) * 64;
+            break;
+        }
+    }
+    return std::min(std::max(slots, 256), max_slots);
+}
+
 // CSR kernel: time every shape of the vector kernel (lanes per row, rows
-// per lane group) and the entry-balanced kernel on the device and keep the
-// fastest (the apply does not depend on the values of x, so zeros are used).
-// Fixed values are not tuned.
+// per lane group, direct or staged through LDS) and the entry-balanced kernel
+// on the device and keep the fastest (the apply does not depend on the
+// values of x, so zeros are used).  Fixed values are not tuned.
 void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t s) {
     int rule = 1;  // smallest power of two >= the longest row, at most 64
     while (rule < 64 && rule < h->max_len) rule <<= 1;
+    if (o.csr_stage == 1) rule = std::min(std::max(rule, kCsrStageMin), kCsrStageMax);
     h->subwave = o.subwave ? o.subwave : rule;
     h->csr_rows = o.csr_rows ? o.csr_rows : 1;
+    h->csr_stage_slots = 0;
+    h->csr_stage_col_nt = false;
     const bool want_vec = o.csr_kernel != SPMV_CSR_BALANCED;
     const bool want_bal = o.csr_kernel != SPMV_CSR_VECTOR && h->nnz > 0;
     b.csr_balanced = !want_vec;
@@ -929,26 +981,45 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
         decide_window(h, SPMV_CSR, o.x_window, b, s);
         b.csr_balanced = bal;
     }
-    const bool tune_vec = want_vec && !(o.subwave && o.csr_rows);
+    const bool tune_vec = want_vec && !(o.subwave && o.csr_rows && o.csr_stage >= 0);
+    if (o.csr_stage == 1) h->csr_stage_slots = stage_slots_for(h, h->subwave, s);
     if (h->n == 0 || h->nnz == 0 || (!tune_vec && !(want_vec && want_bal))) {
         sync(s);
         return;
     }
     DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
     hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
-    const CsrView v{(int)h->n, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
+    const CsrView v{(int)h->n, (int)h->nnz, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
     const bool f64 = h->dtype == SPMV_F64;
     float best_ms = 1e30f;
     if (want_vec) {
         const int sw_lo = o.subwave ? o.subwave : (h->max_len <= 2 ? 1 : 2);
         const int sw_hi = o.subwave ? o.subwave : 64;
         for (int sw = sw_lo; sw <= sw_hi; sw <<= 1)
-            for (int rows = 1; rows <= kCsrRowsMax; rows <<= 1) {
-                if (o.csr_rows && rows != o.csr_rows) continue;
-                const float ms = time_launches(
-                    [&] { return launch_csr(v, sw, rows, f64, ys.p, xs.p, 1.0, 0.0, s); }, s);
-                if (ms < best_ms) best_ms = ms, h->subwave = sw, h->csr_rows = rows;
-            }
+            for (int rows = 1; rows <= kCsrRowsMax; rows <<= 1)
+                for (int st = 0; st <= 1; ++st) {
+                    if (o.csr_rows && rows != o.csr_rows) continue;
+                    if (o.csr_stage >= 0 && st != o.csr_stage) continue;
+                    if (st && (rows != 1 || sw < kCsrStageMin || sw > kCsrStageMax)) continue;
+                    const int slots = st ? stage_slots_for(h, sw, s) : 0;
+                    const float ms = time_launches([&] {
+                        return launch_csr(v, sw, rows, slots, false, f64, ys.p, xs.p, 1.0, 0.0,
+                                          s);
+                    }, s);
+                    if (ms < best_ms)
+                        best_ms = ms, h->subwave = sw, h->csr_rows = rows,
+                        h->csr_stage_slots = slots;
+                }
+        if (h->csr_stage_slots > 0) {
+            // the copy streams val past the caches; col too only if that is
+            // faster (a matrix whose col fits the last-level cache beside x
+            // gains from keeping it there over repeated applies)
+            const float ms = time_launches([&] {
+                return launch_csr(v, h->subwave, 1, h->csr_stage_slots, true, f64, ys.p, xs.p,
+                                  1.0, 0.0, s);
+            }, s);
+            if (ms < best_ms) best_ms = ms, h->csr_stage_col_nt = true;
+        }
     }
     if (want_vec && want_bal) {
         b.csr_balanced = true;
@@ -1228,8 +1299,12 @@ int spmv_create(spmv_t* out, int kind, int64_t n, int64_t nnz, const int64_t* ro
             h->dtype = dtype;
             h->vsize = dtype == SPMV_F64 ? 8 : 4;
             h->rowptr.alloc((size_t)(n + 1) * 4);
-            h->col.alloc((size_t)nnz * 4);
-            h->val.alloc((size_t)nnz * h->vsize);
+            h->col.alloc((size_t)nnz * 4 + 16);
+            h->val.alloc((size_t)nnz * h->vsize + 16);
+            hip_check(hipMemsetAsync((char*)h->col.p + (size_t)nnz * 4, 0, 16, s),
+                      "hipMemsetAsync");
+            hip_check(hipMemsetAsync((char*)h->val.p + (size_t)nnz * h->vsize, 0, 16, s),
+                      "hipMemsetAsync");
             DevBuf flags(8);
             hip_check(hipMemsetAsync(flags.p, 0, 8, s), "hipMemsetAsync");
             if (kind == SPMV_IN_CSR) {
@@ -1309,7 +1384,7 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
         if (!h) fail(SPMV_ERR_STATE, "null handle");
         if (!valid_format(format) && format != SPMV_AUTO)
             fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
-        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0, 0, 0};
+        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0, 0, 0, -1};
         if (opts) o = *opts;
         if (o.ell_groups != 0 && o.ell_groups != 1 && o.ell_groups != 4 && o.ell_groups != 16)
             fail(SPMV_ERR_INVALID_ARG, "ell_groups must be 0, 1, 4 or 16 (got %d)", o.ell_groups);
@@ -1338,6 +1413,14 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
                  o.subwave);
         if (o.csr_kernel < SPMV_CSR_AUTO || o.csr_kernel > SPMV_CSR_BALANCED)
             fail(SPMV_ERR_INVALID_ARG, "csr_kernel must be 0, 1 or 2 (got %d)", o.csr_kernel);
+        if (o.csr_stage < -1 || o.csr_stage > 1)
+            fail(SPMV_ERR_INVALID_ARG, "csr_stage must be -1, 0 or 1 (got %d)", o.csr_stage);
+        if (o.csr_stage == 1 &&
+            ((o.subwave && (o.subwave < kCsrStageMin || o.subwave > kCsrStageMax)) ||
+             o.csr_rows > 1 || o.csr_kernel == SPMV_CSR_BALANCED))
+            fail(SPMV_ERR_INVALID_ARG,
+                 "csr_stage = 1 needs the vector kernel with subwave 0 or %d..%d and csr_rows 0 "
+                 "or 1", kCsrStageMin, kCsrStageMax);
         if (format == SPMV_AUTO)
             convert_auto(h, o);
         else
@@ -1475,6 +1558,7 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.footprint_bytes = h->rowptr.bytes + h->col.bytes + h->val.bytes + b.bytes();
     i.x_window = b.window ? 1 : 0;
     i.csr_rows = h->csr_rows;
+    i.csr_stage_slots = h->format == SPMV_CSR && !b.csr_balanced ? h->csr_stage_slots : 0;
     i.csr_kernel = h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED : SPMV_CSR_VECTOR;
     i.sort_window = b.sort_window;
     i.ell_groups = (h->format == SPMV_ELLR || h->format == SPMV_HYB || h->format == SPMV_HEC)

@@ -8,6 +8,8 @@
 namespace spmv {
 
 constexpr int kWave = 64;
+// cache-policy bits of a memory instruction on gfx950: nontemporal
+constexpr int kCachePolicyNT = 2;
 
 // MI355X dispatches workgroup b of a grid to XCD (b mod 8).  Each XCD has its
 // own L2, so neighbouring tiles (which share x entries of a banded matrix)
@@ -143,6 +145,33 @@ __device__ __forceinline__ T segmented_scan(int key, T v) {
 // waits only for this wave's LDS operations, then s_barrier.  A plain
 // __syncthreads() also waits for every outstanding global load, which would
 // drain the prefetch of the next step that the window kernels rely on.
+// Orders a wave's LDS stores before its later LDS loads from other lanes of
+// the same wave (data staged in a slice only that wave touches).  LDS
+// operations of one wave complete in issue order, so no wait is needed; the
+// fences keep the compiler from moving the loads above the stores.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 16 bytes per lane straight from global memory into LDS (no registers):
+// lane i's bytes land at lds + 16 * i, with `lds` the same for the whole wave.
+// The copy is counted by vmcnt; wait_vm() waits for it.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// the same, without keeping the lines in the caches (data read once)
+__device__ __forceinline__ void load_lds16_nt(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0,
+                                     kCachePolicyNT);
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

@@ -50,6 +50,7 @@ constexpr int kWinGroups = 256;
 
 struct CsrView {
     int n;
+    int nnz;               // col and val hold 16 bytes past entry nnz - 1
     const int* rowptr;
     const int* col;
     const void* val;
@@ -111,10 +112,18 @@ struct TailView {
 };
 
 // kernel launchers (asynchronous on `stream`); fp64 when f64, else fp32
-// rows: rows per lane group, a power of two up to kCsrRowsMax
+// rows: rows per lane group, a power of two up to kCsrRowsMax; stage_slots >
+// 0: copy each wave's entries into LDS first when they fit in that many slots
+// (subwave 2..16 with one row per group; four slices per workgroup within
+// kCsrStageLds bytes, the default dynamic LDS limit).  The staged copy reads
+// val without keeping it in the caches, and col too when stage_col_nt.
 constexpr int kCsrRowsMax = 4;
-hipError_t launch_csr(const CsrView& a, int subwave, int rows, bool f64, void* y,
-                      const void* x, double alpha, double beta, hipStream_t stream);
+constexpr int kCsrStageMin = 2, kCsrStageMax = 16;
+constexpr size_t kCsrStageLds = 64 * 1024;
+hipError_t launch_csr(const CsrView& a, int subwave, int rows, int stage_slots, bool stage_col_nt,
+                      bool f64, void* y, const void* x, double alpha, double beta,
+                      hipStream_t stream);
+int csr_stage_max_slots(bool f64);
 hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double alpha,
                       double beta, hipStream_t stream);
 hipError_t launch_sell(const SellView& a, bool f64, void* y, const void* x, double alpha,

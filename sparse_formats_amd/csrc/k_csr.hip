@@ -84,6 +84,131 @@ __global__ __launch_bounds__(256) void k_csr_vector(int n, const int* __restrict
     }
 }
 
+// Staged variant (one row per group, rows base .. base + 64/S - 1 per wave).
+// The wave's rows hold the contiguous entries [k0, k1) of val/col; when they
+// fit its LDS slice, the wave first copies them there with direct
+// global-to-LDS loads of 16 bytes per lane on consecutive addresses (every
+// instruction reads whole cache lines, once), then runs the group sums on
+// the copy.  Without the copy each load instruction of a group touches the
+// lines of 64/S separate row segments and a line is requested again by the
+// next instruction, which raises the L1 to L2 request count, the limiter of
+// short-row matrices.  The x reads keep the group layout (entry u of
+// neighbouring rows on neighbouring lanes).  A wave whose rows do not fit
+// reads val/col directly; both give the same sums.
+// LDS per wave: `slots` entries of val (rounded up to whole passes of
+// 64 * 16 / sizeof(T) values) and of col (whole passes of 256 columns).
+template <typename T>
+struct CsrStage {
+    static constexpr int V = 16 / sizeof(T);  // values per 16-byte load
+    static __host__ __device__ int val_slots(int slots) {
+        return (slots + kWave * V - 1) / (kWave * V) * (kWave * V);
+    }
+    static __host__ __device__ int col_slots(int slots) { return (slots + 255) / 256 * 256; }
+    static __host__ __device__ int wave_bytes(int slots) {
+        return val_slots(slots) * (int)sizeof(T) + col_slots(slots) * 4;
+    }
+};
+
+// Sum of the entries kb + sub, kb + sub + S, ... below ke; ld(k, v, c) reads
+// entry k, which is clamped to ke - 1 for the masked loads of the first pass.
+template <typename T, int S, int U, typename Load>
+__device__ __forceinline__ T group_row_sum(int kb, int ke, int sub, const T* __restrict__ x,
+                                           Load ld) {
+    T v[U];
+    int c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ld(min(kb + sub + u * S, ke - 1), v[u], c[u]);
+    T acc = T(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const T p = v[u] * x[c[u]];
+        acc += kb + sub + u * S < ke ? p : T(0);
+    }
+    for (int k = kb + sub + U * S; k < ke; k += S) {
+        T vk;
+        int ck;
+        ld(k, vk, ck);
+        acc = fma(vk, x[ck], acc);
+    }
+    return acc;
+}
+
+template <typename T, int S>
+__global__ __launch_bounds__(256) void k_csr_staged(int n, const int* __restrict__ rowptr,
+                                                    const int* __restrict__ col,
+                                                    const T* __restrict__ val,
+                                                    const T* __restrict__ x, T* __restrict__ y,
+                                                    T alpha, T beta, int slots, int col_nt) {
+    using St = CsrStage<T>;
+    constexpr int V = St::V;
+    constexpr int U = CsrFirstPass<S, 1>::value;
+    extern __shared__ __align__(16) char s_stage[];
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t base = (xcd_tile(blockIdx.x, gridDim.x) * 4 + w) * (kWave / S);
+    if (base >= n) return;  // whole waves leave together
+    const int sub = lane & (S - 1);
+    const int64_t row = base + lane / S;
+    const int kb = rowptr[row < n ? row : n];
+    const int ke = rowptr[row < n ? row + 1 : n];
+    const int k0 = __builtin_amdgcn_readfirstlane(kb);       // lane 0: row base < n
+    const int k1 = __builtin_amdgcn_readlane(ke, kWave - 1);  // end of the last row
+    const int kA = k0 & -4;                                  // 16-byte aligned for both
+    T sum;
+    if (k1 > kA && k1 - kA <= St::val_slots(slots)) {
+        // slots [0, k1 - kA) are all written below, and every read stays
+        // there; a lane's last 16 bytes may pass k1 (col/val are padded by 16
+        // bytes) and the last pass stays inside the rounded-up slices
+        T* sv = reinterpret_cast<T*>(s_stage + w * St::wave_bytes(slots));
+        int* sc = reinterpret_cast<int*>(sv + St::val_slots(slots));
+        const int npv = (k1 - kA + kWave * V - 1) / (kWave * V);
+        const int npc = (k1 - kA + kWave * 4 - 1) / (kWave * 4);
+        for (int p = 0; p < npv; ++p) {
+            const int k = kA + (p * kWave + lane) * V;
+            if (k < k1) load_lds16_nt(val + k, sv + p * kWave * V);
+        }
+        if (col_nt) {
+            for (int p = 0; p < npc; ++p) {
+                const int k = kA + (p * kWave + lane) * 4;
+                if (k < k1) load_lds16_nt(col + k, sc + p * kWave * 4);
+            }
+        } else {
+            for (int p = 0; p < npc; ++p) {
+                const int k = kA + (p * kWave + lane) * 4;
+                if (k < k1) load_lds16(col + k, sc + p * kWave * 4);
+            }
+        }
+        wait_vm();
+        wave_lds_sync();
+        sum = group_row_sum<T, S, U>(kb, ke, sub, x, [&](int k, T& v, int& c) {
+            const int i = max(k - kA, 0);
+            v = sv[i];
+            c = sc[i];
+        });
+    } else {
+        sum = group_row_sum<T, S, U>(kb, ke, sub, x, [&](int k, T& v, int& c) {
+            const int i = max(k, 0);  // entry 0 exists: col/val are padded
+            v = val[i];
+            c = col[i];
+        });
+    }
+    sum = group_sum<S>(sum);
+    if (sub == 0 && row < n) y[row] = axpby(sum, alpha, beta, y + row);
+}
+
+template <typename T, int S>
+static hipError_t run_staged(const CsrView& a, int slots, bool col_nt, void* y, const void* x,
+                             double alpha, double beta, hipStream_t stream) {
+    constexpr int kRowsPerBlock = 256 / S;
+    const int64_t blocks = ((int64_t)a.n + kRowsPerBlock - 1) / kRowsPerBlock;
+    if (blocks == 0) return hipSuccess;
+    const size_t lds = 4 * (size_t)CsrStage<T>::wave_bytes(slots);
+    if (slots < 1 || lds > kCsrStageLds) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_csr_staged<T, S>), dim3((unsigned)blocks), dim3(256), lds, stream, a.n,
+                       a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, (T)alpha, (T)beta,
+                       slots, col_nt ? 1 : 0);
+    return hipGetLastError();
+}
+
 template <typename T, int S, int R>
 static hipError_t run(const CsrView& a, void* y, const void* x, double alpha, double beta,
                       hipStream_t stream) {
@@ -112,8 +237,19 @@ static hipError_t dispatch_s(const CsrView& a, int subwave, void* y, const void*
 }
 
 template <typename T>
-static hipError_t dispatch(const CsrView& a, int subwave, int rows, void* y, const void* x,
-                           double alpha, double beta, hipStream_t stream) {
+static hipError_t dispatch(const CsrView& a, int subwave, int rows, int slots, bool col_nt,
+                           void* y, const void* x, double alpha, double beta,
+                           hipStream_t stream) {
+    if (slots > 0) {
+        if (rows != 1) return hipErrorInvalidValue;
+        switch (subwave) {
+            case 2: return run_staged<T, 2>(a, slots, col_nt, y, x, alpha, beta, stream);
+            case 4: return run_staged<T, 4>(a, slots, col_nt, y, x, alpha, beta, stream);
+            case 8: return run_staged<T, 8>(a, slots, col_nt, y, x, alpha, beta, stream);
+            case 16: return run_staged<T, 16>(a, slots, col_nt, y, x, alpha, beta, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (rows) {
         case 1: return dispatch_s<T, 1>(a, subwave, y, x, alpha, beta, stream);
         case 2: return dispatch_s<T, 2>(a, subwave, y, x, alpha, beta, stream);
@@ -122,10 +258,21 @@ static hipError_t dispatch(const CsrView& a, int subwave, int rows, void* y, con
     }
 }
 
-hipError_t launch_csr(const CsrView& a, int subwave, int rows, bool f64, void* y,
-                      const void* x, double alpha, double beta, hipStream_t stream) {
-    return f64 ? dispatch<double>(a, subwave, rows, y, x, alpha, beta, stream)
-               : dispatch<float>(a, subwave, rows, y, x, alpha, beta, stream);
+hipError_t launch_csr(const CsrView& a, int subwave, int rows, int stage_slots, bool stage_col_nt,
+                      bool f64, void* y, const void* x, double alpha, double beta,
+                      hipStream_t stream) {
+    return f64 ? dispatch<double>(a, subwave, rows, stage_slots, stage_col_nt, y, x, alpha, beta,
+                                  stream)
+               : dispatch<float>(a, subwave, rows, stage_slots, stage_col_nt, y, x, alpha, beta,
+                                 stream);
+}
+
+int csr_stage_max_slots(bool f64) {
+    int s = 256;  // largest multiple of 256 whose four wave slices fit
+    while (4 * (size_t)(f64 ? CsrStage<double>::wave_bytes(s + 256)
+                            : CsrStage<float>::wave_bytes(s + 256)) <= kCsrStageLds)
+        s += 256;
+    return s;
 }
 
 }  // namespace spmv

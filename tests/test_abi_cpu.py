@@ -56,6 +56,36 @@ def test_header_compiles_as_c(tmp_path):
     assert r.returncode == 0, r.stderr
 
 
+def test_struct_layouts_match_binding(tmp_path):
+    """Sizes and field offsets of the option and info structs as gcc lays them
+    out agree with the Python binding's ctypes mirrors."""
+    sys.path.insert(0, ROOT)
+    import sparse_formats_amd as sf
+    mirrors = {"spmv_convert_opts": sf._ConvertOpts, "spmv_info_t": sf._Info,
+               "spmv_solve_opts": sf._SolveOpts, "spmv_solve_info": sf._SolveInfo}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "spmv_amd.h"',
+             'int main(void){']
+    for cname, py in mirrors.items():
+        lines.append('printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in py._fields_:
+            lines.append('printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines.append('return 0;}')
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    r = subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(c), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines():
+        a, b, v = line.split()
+        got[(a, b)] = int(v)
+    for cname, py in mirrors.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
 def test_enum_values_match_binding():
     sys.path.insert(0, ROOT)
     ev = enum_values()

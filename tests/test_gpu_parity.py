@@ -93,6 +93,59 @@ def test_csr_every_shape(sw, rows, name):
         M.convert("csr", csr_rows=8)
 
 
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("sw", [2, 4, 8, 16])
+@pytest.mark.parametrize("name", ["short", "every_len", "ragged", "dups_unsorted", "nnz0", "n1",
+                                  "c1", "box27"])
+def test_csr_staged(sw, name, dtype):
+    """The LDS-staged vector kernel against the oracle, and bit for bit against
+    the direct kernel of the same shape (same per-lane order).  "every_len"
+    and "ragged" have waves too long for the slice, which read directly."""
+    if name == "short":
+        a = random_csr(20011, seed=45, lens=(np.arange(20011) * 7919) % 41)
+    else:
+        a = MATS[name]()
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    x_np, y0_np = (v.astype(npdt) for v in vectors(a.n, 19))
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n)
+    M.convert("csr", csr_kernel="vector", subwave=sw, csr_rows=1, csr_stage=1)
+    inf = M.info()
+    assert inf["csr_stage_slots"] >= 256 and inf["subwave"] == sw and inf["csr_kernel"] == "vector"
+    ys = []
+    for alpha, beta in AB:
+        y = apply(M, x, y0, alpha, beta)
+        check(a, x_np, y0_np, alpha, beta, y, dtype, what="csr staged S=%d %s a=%g b=%g" % (
+            sw, name, alpha, beta))
+        ys.append(y)
+    M.convert("csr", csr_kernel="vector", subwave=sw, csr_rows=1, csr_stage=0)
+    assert M.info()["csr_stage_slots"] == 0
+    for (alpha, beta), y_st in zip(AB, ys):
+        assert np.array_equal(apply(M, x, y0, alpha, beta), y_st), (sw, name, alpha, beta)
+    M.close()
+
+
+def test_csr_stage_errors():
+    a = MATS["c1"]()
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
+    for kw in (dict(csr_stage=2), dict(csr_stage=-2), dict(csr_stage=1, subwave=32),
+               dict(csr_stage=1, subwave=1), dict(csr_stage=1, csr_rows=2),
+               dict(csr_stage=1, csr_kernel="balanced")):
+        with pytest.raises(sf.SpmvError):
+            M.convert("csr", **kw)
+    # auto shape with staging forced stays in the staged range
+    M.convert("csr", csr_kernel="vector", csr_stage=1)
+    inf = M.info()
+    assert inf["csr_stage_slots"] >= 256 and 2 <= inf["subwave"] <= 16 and inf["csr_rows"] == 1
+    # the balanced kernel reports no staging
+    M.convert("csr", csr_kernel="balanced")
+    assert M.info()["csr_stage_slots"] == 0
+    M.close()
+
+
 def test_sell_split_slices():
     """Slices wider than the split width go through column chunks + atomics."""
     n = 9000
