@@ -77,7 +77,9 @@ typedef enum {
     SPMV_AUTO = 5
 } spmv_format;
 
-/* CSR apply kernels (spmv_convert_opts.csr_kernel, spmv_info_t.csr_kernel) */
+/* CSR apply kernels (spmv_convert_opts.csr_kernel, spmv_info_t.csr_kernel);
+ * for HEC the same option picks the kernel of the CSR tail
+ * (spmv_info_t.tail_kernel) */
 typedef enum {
     SPMV_CSR_AUTO = 0,     /* time both on the device, keep the faster */
     SPMV_CSR_VECTOR = 1,   /* a group of lanes per row (subwave, csr_rows) */
@@ -130,7 +132,10 @@ typedef struct {
      * entries into equal chunks of 512 per wave, sums the row segments of
      * each chunk with a segmented scan over the lanes and adds rows that
      * cross chunks with atomics after a pass that writes beta * y.  With
-     * x_window it stages x in LDS like the HEC tail. */
+     * x_window it stages x in LDS like the HEC tail.  HEC: the kernel of
+     * the tail -- balanced as above, or the vector kernel over the rows that
+     * hold tail entries (each adds its sum onto the ELL part's result, no
+     * atomics); auto keeps the balanced one when the LDS window is on. */
     int32_t csr_kernel;
     /* Windowed sorting: the pJDS sort of "Sparse matrix-vector multiplication
      * on GPGPU clusters" (Sect. 2.2: rows ordered by length, longest first)
@@ -206,6 +211,8 @@ typedef struct {
     int64_t ell_rows;      /* ELL-R / HYB / HEC: rows padded to whole blocks */
     int32_t csr_stage_slots; /* CSR vector kernel staged in LDS: entries one wave
                                 can stage (0: the kernel reads directly) */
+    int32_t tail_kernel;   /* HYB / HEC with tail entries: SPMV_CSR_BALANCED or
+                              (HEC only) SPMV_CSR_VECTOR; otherwise 0 */
 } spmv_info_t;
 
 /* arrays readable with spmv_export */

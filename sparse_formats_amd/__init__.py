@@ -75,7 +75,8 @@ class _Info(ctypes.Structure):
                 ("permuted_basis", ctypes.c_int32), ("ell_groups", ctypes.c_int32),
                 ("sort_window", ctypes.c_int32),
                 ("band_fraction", ctypes.c_double),
-                ("ell_rows", ctypes.c_int64), ("csr_stage_slots", ctypes.c_int32)]
+                ("ell_rows", ctypes.c_int64), ("csr_stage_slots", ctypes.c_int32),
+                ("tail_kernel", ctypes.c_int32)]
 
 
 def _load():
@@ -232,6 +233,7 @@ class Matrix:
         d = {k: getattr(i, k) for k, _ in _Info._fields_}
         d["format"] = [k for k, v in FORMATS.items() if v == d["format"]][0]
         d["csr_kernel"] = [k for k, v in CSR_KERNELS.items() if v == d["csr_kernel"]][0]
+        d["tail_kernel"] = [k for k, v in CSR_KERNELS.items() if v == d["tail_kernel"]][0]
         return d
 
     def export(self, name: str) -> np.ndarray:

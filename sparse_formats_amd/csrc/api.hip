@@ -92,6 +92,13 @@ struct DevBuf {
 
 int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 
+// a shape of the vector CSR kernel: lanes per row, rows per lane group,
+// LDS slots per wave when staged (0: direct), col read without caching
+struct VecShape {
+    int subwave = 1, rows = 1, slots = 0;
+    bool col_nt = false;
+};
+
 // the arrays of one converted (non-CSR) format
 struct Built {
     int format = SPMV_CSR;
@@ -113,6 +120,10 @@ struct Built {
     // (tail_rows: those rows; tail_cptr: their starts + the end)
     int64_t tail_nrows = 0;
     DevBuf tail_rows, tail_cptr;
+    // HEC: the tail runs as the vector CSR kernel over the compressed rows
+    // (added onto the ELL part, no atomics) instead of the balanced kernel
+    bool tail_vector = false;
+    VecShape tail_vec;
     // CSR: entry-balanced kernel (run rows over the whole matrix)
     bool csr_balanced = false;
     // SELL-64 in the permuted basis (x and y in sorted row order)
@@ -780,8 +791,12 @@ void build_split(const spmv_handle* h, int format, int requested, int sort_windo
         sync(s);
     }
     if (format == SPMV_HYB) b.tail_row.alloc((size_t)std::max<int64_t>(tail, 1) * 4);
-    b.tail_col.alloc((size_t)std::max<int64_t>(tail, 1) * 4);
-    b.tail_val.alloc((size_t)std::max<int64_t>(tail, 1) * sizeof(V));
+    // 16 zero bytes past the end: the vector kernel's whole 16-byte loads
+    b.tail_col.alloc((size_t)tail * 4 + 16);
+    b.tail_val.alloc((size_t)tail * sizeof(V) + 16);
+    hip_check(hipMemsetAsync((char*)b.tail_col.p + (size_t)tail * 4, 0, 16, s), "hipMemsetAsync");
+    hip_check(hipMemsetAsync((char*)b.tail_val.p + (size_t)tail * sizeof(V), 0, 16, s),
+              "hipMemsetAsync");
     if (tail > 0) {
         hipLaunchKernelGGL(k_tail_fill<V>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, n,
                            (int)K, h->rowptr.as<int>(), h->col.as<int>(), h->val.as<V>(),
@@ -881,7 +896,12 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
                       (int)b.ell_width, b.ell_len.as<int>(), b.ell_perm.as<int>(),
                       b.ell_col.as<int>(), b.ell_val.p, b.window, b.ell_groups};
             e = launch_ell(a, f64, y, x, alpha, beta, s);
-            if (e == hipSuccess && format != SPMV_ELLR && b.tail_nnz > 0) {
+            if (e == hipSuccess && format == SPMV_HEC && b.tail_nnz > 0 && b.tail_vector) {
+                const CsrView t{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
+                                b.tail_col.as<int>(), b.tail_val.p, b.tail_rows.as<int>()};
+                const VecShape& v = b.tail_vec;
+                e = launch_csr(t, v.subwave, v.rows, v.slots, v.col_nt, f64, y, x, alpha, 1.0, s);
+            } else if (e == hipSuccess && format != SPMV_ELLR && b.tail_nnz > 0) {
                 const bool hec = format == SPMV_HEC;
                 TailView t{(int)h->n, b.tail_nnz, hec ? nullptr : b.tail_row.as<int>(),
                            hec ? b.tail_cptr.as<int>() : nullptr, b.run_row.as<int>(),
@@ -928,15 +948,15 @@ float time_launches(F&& launch, hipStream_t s) {
 // outlier wave would otherwise set the LDS of all and lower the occupancy;
 // waves that do not fit read directly), at least 256, at most what four
 // slices per workgroup allow.
-int stage_slots_for(const spmv_handle* h, int sw, hipStream_t s) {
-    const int max_slots = csr_stage_max_slots(h->dtype == SPMV_F64);
+int stage_slots_for(const CsrView& v, bool f64, int sw, hipStream_t s) {
+    const int max_slots = csr_stage_max_slots(f64);
     const int rw = 64 / sw, nb = max_slots / 64 + 1;
-    const int64_t waves = (h->n + rw - 1) / rw;
+    const int64_t waves = ((int64_t)v.n + rw - 1) / rw;
     if (waves == 0) return 256;
     DevBuf hist((size_t)nb * 4);
     hip_check(hipMemsetAsync(hist.p, 0, hist.bytes, s), "hipMemsetAsync");
-    hipLaunchKernelGGL(k_stage_hist, dim3(grid_for(waves)), dim3(256), 0, s, h->n, rw,
-                       h->rowptr.as<int>(), nb, hist.as<unsigned>());
+    hipLaunchKernelGGL(k_stage_hist, dim3(grid_for(waves)), dim3(256), 0, s, (int64_t)v.n, rw,
+                       v.rowptr, nb, hist.as<unsigned>());
     hip_check(hipGetLastError(), "stage histogram");
     std::vector<unsigned> c(nb);
     hip_check(hipMemcpyAsync(c.data(), hist.p, hist.bytes, hipMemcpyDeviceToHost, s),
@@ -954,10 +974,39 @@ int stage_slots_for(const spmv_handle* h, int sw, hipStream_t s) {
     return std::min(std::max(slots, 256), max_slots);
 }
 
-// CSR kernel: time every shape of the vector kernel (lanes per row, rows
-// per lane group, direct or staged through LDS) and the entry-balanced kernel
-// on the device and keep the fastest (the apply does not depend on the
-// values of x, so zeros are used).  Fixed values are not tuned.
+// Time the shapes of the vector CSR kernel on `v` (lanes per row from sw_lo
+// to sw_hi, rows per lane group, direct or staged through LDS; a value >= 0
+// or > 0 in rows / stage fixes that choice) with x = 0 and the result added
+// to ys with `beta`, and return the fastest and its time.  The staged copy
+// streams val past the caches; col too only when that is faster (a col array
+// that fits the last-level cache beside x stays there over repeated applies).
+float tune_vector(const CsrView& v, bool f64, int sw_lo, int sw_hi, int fix_rows, int fix_stage,
+                  void* ys, const void* xs, double beta, VecShape& best, hipStream_t s) {
+    float best_ms = 1e30f;
+    for (int sw = sw_lo; sw <= sw_hi; sw <<= 1)
+        for (int rows = 1; rows <= kCsrRowsMax; rows <<= 1)
+            for (int st = 0; st <= 1; ++st) {
+                if (fix_rows && rows != fix_rows) continue;
+                if (fix_stage >= 0 && st != fix_stage) continue;
+                if (st && (rows != 1 || sw < kCsrStageMin || sw > kCsrStageMax)) continue;
+                const int slots = st ? stage_slots_for(v, f64, sw, s) : 0;
+                const float ms = time_launches([&] {
+                    return launch_csr(v, sw, rows, slots, false, f64, ys, xs, 1.0, beta, s);
+                }, s);
+                if (ms < best_ms) best_ms = ms, best = VecShape{sw, rows, slots, false};
+            }
+    if (best.slots > 0) {
+        const float ms = time_launches([&] {
+            return launch_csr(v, best.subwave, 1, best.slots, true, f64, ys, xs, 1.0, beta, s);
+        }, s);
+        if (ms < best_ms) best_ms = ms, best.col_nt = true;
+    }
+    return best_ms;
+}
+
+// CSR kernel: time every shape of the vector kernel and the entry-balanced
+// kernel on the device and keep the fastest (the apply does not depend on
+// the values of x, so zeros are used).  Fixed values are not tuned.
 void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t s) {
     int rule = 1;  // smallest power of two >= the longest row, at most 64
     while (rule < 64 && rule < h->max_len) rule <<= 1;
@@ -966,6 +1015,8 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     h->csr_rows = o.csr_rows ? o.csr_rows : 1;
     h->csr_stage_slots = 0;
     h->csr_stage_col_nt = false;
+    const bool f64 = h->dtype == SPMV_F64;
+    const CsrView v{(int)h->n, (int)h->nnz, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
     const bool want_vec = o.csr_kernel != SPMV_CSR_BALANCED;
     const bool want_bal = o.csr_kernel != SPMV_CSR_VECTOR && h->nnz > 0;
     b.csr_balanced = !want_vec;
@@ -982,44 +1033,21 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
         b.csr_balanced = bal;
     }
     const bool tune_vec = want_vec && !(o.subwave && o.csr_rows && o.csr_stage >= 0);
-    if (o.csr_stage == 1) h->csr_stage_slots = stage_slots_for(h, h->subwave, s);
+    if (o.csr_stage == 1) h->csr_stage_slots = stage_slots_for(v, f64, h->subwave, s);
     if (h->n == 0 || h->nnz == 0 || (!tune_vec && !(want_vec && want_bal))) {
         sync(s);
         return;
     }
     DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
     hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
-    const CsrView v{(int)h->n, (int)h->nnz, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
-    const bool f64 = h->dtype == SPMV_F64;
     float best_ms = 1e30f;
     if (want_vec) {
-        const int sw_lo = o.subwave ? o.subwave : (h->max_len <= 2 ? 1 : 2);
-        const int sw_hi = o.subwave ? o.subwave : 64;
-        for (int sw = sw_lo; sw <= sw_hi; sw <<= 1)
-            for (int rows = 1; rows <= kCsrRowsMax; rows <<= 1)
-                for (int st = 0; st <= 1; ++st) {
-                    if (o.csr_rows && rows != o.csr_rows) continue;
-                    if (o.csr_stage >= 0 && st != o.csr_stage) continue;
-                    if (st && (rows != 1 || sw < kCsrStageMin || sw > kCsrStageMax)) continue;
-                    const int slots = st ? stage_slots_for(h, sw, s) : 0;
-                    const float ms = time_launches([&] {
-                        return launch_csr(v, sw, rows, slots, false, f64, ys.p, xs.p, 1.0, 0.0,
-                                          s);
-                    }, s);
-                    if (ms < best_ms)
-                        best_ms = ms, h->subwave = sw, h->csr_rows = rows,
-                        h->csr_stage_slots = slots;
-                }
-        if (h->csr_stage_slots > 0) {
-            // the copy streams val past the caches; col too only if that is
-            // faster (a matrix whose col fits the last-level cache beside x
-            // gains from keeping it there over repeated applies)
-            const float ms = time_launches([&] {
-                return launch_csr(v, h->subwave, 1, h->csr_stage_slots, true, f64, ys.p, xs.p,
-                                  1.0, 0.0, s);
-            }, s);
-            if (ms < best_ms) best_ms = ms, h->csr_stage_col_nt = true;
-        }
+        VecShape best;
+        best_ms = tune_vector(v, f64, o.subwave ? o.subwave : (h->max_len <= 2 ? 1 : 2),
+                              o.subwave ? o.subwave : 64, o.csr_rows, o.csr_stage, ys.p, xs.p, 0.0,
+                              best, s);
+        h->subwave = best.subwave, h->csr_rows = best.rows;
+        h->csr_stage_slots = best.slots, h->csr_stage_col_nt = best.col_nt;
     }
     if (want_vec && want_bal) {
         b.csr_balanced = true;
@@ -1030,6 +1058,39 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
         b.csr_balanced = ms < kPreferMargin * best_ms;
     }
     if (!b.csr_balanced) b.run_row.release(), b.window = false, b.tail_runs = 0;
+}
+
+// HEC tail kernel: the balanced kernel (atomics) or the vector CSR kernel
+// over the rows that hold tail entries (each row added once onto the ELL
+// part's result: no atomics, bit-reproducible).  `kernel` (a
+// spmv_csr_kernel) fixes the choice; SPMV_CSR_AUTO keeps the faster on the
+// device, the balanced one only when clearly faster, and keeps the balanced
+// one with the LDS window (the vector kernel has no window).
+void tune_hec_tail(const spmv_handle* h, int kernel, Built& b, hipStream_t s) {
+    b.tail_vector = false;
+    if (b.tail_nnz == 0 || kernel == SPMV_CSR_BALANCED ||
+        (kernel == SPMV_CSR_AUTO && b.window))
+        return;
+    const bool f64 = h->dtype == SPMV_F64;
+    DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
+    hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
+    hip_check(hipMemsetAsync(ys.p, 0, ys.bytes, s), "hipMemsetAsync");
+    const TailView t{(int)h->n, b.tail_nnz, nullptr, b.tail_cptr.as<int>(), b.run_row.as<int>(),
+                     b.tail_rows.as<int>(), b.tail_col.as<int>(), b.tail_val.p, false};
+    const float bal_ms = kernel == SPMV_CSR_VECTOR
+                             ? 1e30f
+                             : time_launches([&] { return launch_tail(t, f64, ys.p, xs.p, 1.0, s); },
+                                             s);
+    const CsrView v{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
+                    b.tail_col.as<int>(), b.tail_val.p, b.tail_rows.as<int>()};
+    VecShape best;
+    const float vec_ms = tune_vector(v, f64, 1, 64, 0, -1, ys.p, xs.p, 1.0, best, s);
+    sync(s);
+    if (!(bal_ms < kPreferMargin * vec_ms)) {
+        b.tail_vector = true;
+        b.tail_vec = best;
+        b.run_row.release();
+    }
 }
 
 // Share of the entries the LDS window reaches, and whether to use it.  On
@@ -1128,6 +1189,7 @@ void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
             build_split<float>(h, format, o.ell_width, o.sort_window, b, s);
         decide_window(h, format, o.x_window, b, s);
         choose_groups(h, o.ell_groups, b);
+        if (format == SPMV_HEC) tune_hec_tail(h, o.csr_kernel, b, s);
     }
     h->fmt = std::move(b);
     h->format = format;
@@ -1559,6 +1621,9 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.x_window = b.window ? 1 : 0;
     i.csr_rows = h->csr_rows;
     i.csr_stage_slots = h->format == SPMV_CSR && !b.csr_balanced ? h->csr_stage_slots : 0;
+    i.tail_kernel = (h->format == SPMV_HYB || h->format == SPMV_HEC) && b.tail_nnz > 0
+                        ? (b.tail_vector ? SPMV_CSR_VECTOR : SPMV_CSR_BALANCED)
+                        : SPMV_CSR_AUTO;
     i.csr_kernel = h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED : SPMV_CSR_VECTOR;
     i.sort_window = b.sort_window;
     i.ell_groups = (h->format == SPMV_ELLR || h->format == SPMV_HYB || h->format == SPMV_HEC)

@@ -54,6 +54,7 @@ struct CsrView {
     const int* rowptr;
     const int* col;
     const void* val;
+    const int* row_map = nullptr;  // output row of each row (nullptr: itself)
 };
 
 // ELL arrays are stored in blocks of `bh` rows, each block column by column:

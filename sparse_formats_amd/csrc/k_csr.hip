@@ -1,4 +1,6 @@
-// CSR apply with a sub-wave of S lanes per row.
+// CSR apply with a sub-wave of S lanes per row.  Row r's result goes to
+// y[row_map[r]] when a row map is given (the HEC tail: rows that hold tail
+// entries, added onto the ELL part's result with beta = 1), else to y[r].
 //
 // "Sparse Linear Algebra on AMD and NVIDIA GPUs -- The Race Is On" assigns a
 // group of threads to each row and reduces their partial sums across the
@@ -37,7 +39,8 @@ __global__ __launch_bounds__(256) void k_csr_vector(int n, const int* __restrict
                                                     const int* __restrict__ col,
                                                     const T* __restrict__ val,
                                                     const T* __restrict__ x, T* __restrict__ y,
-                                                    T alpha, T beta) {
+                                                    const int* __restrict__ row_map, T alpha,
+                                                    T beta) {
     constexpr int kGroups = kWave / S;  // groups per wave
     constexpr int U = CsrFirstPass<S, R>::value;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -80,7 +83,10 @@ __global__ __launch_bounds__(256) void k_csr_vector(int n, const int* __restrict
     for (int r = 0; r < R; ++r) {
         const T s_r = group_sum<S>(sum[r]);
         const int64_t row = base + r * kGroups;
-        if (sub == 0 && row < n) y[row] = axpby(s_r, alpha, beta, y + row);
+        if (sub == 0 && row < n) {
+            const int64_t out = row_map ? row_map[row] : row;
+            y[out] = axpby(s_r, alpha, beta, y + out);
+        }
     }
 }
 
@@ -138,7 +144,8 @@ __global__ __launch_bounds__(256) void k_csr_staged(int n, const int* __restrict
                                                     const int* __restrict__ col,
                                                     const T* __restrict__ val,
                                                     const T* __restrict__ x, T* __restrict__ y,
-                                                    T alpha, T beta, int slots, int col_nt) {
+                                                    const int* __restrict__ row_map, T alpha,
+                                                    T beta, int slots, int col_nt) {
     using St = CsrStage<T>;
     constexpr int V = St::V;
     constexpr int U = CsrFirstPass<S, 1>::value;
@@ -192,7 +199,10 @@ __global__ __launch_bounds__(256) void k_csr_staged(int n, const int* __restrict
         });
     }
     sum = group_sum<S>(sum);
-    if (sub == 0 && row < n) y[row] = axpby(sum, alpha, beta, y + row);
+    if (sub == 0 && row < n) {
+        const int64_t out = row_map ? row_map[row] : row;
+        y[out] = axpby(sum, alpha, beta, y + out);
+    }
 }
 
 template <typename T, int S>
@@ -204,8 +214,8 @@ static hipError_t run_staged(const CsrView& a, int slots, bool col_nt, void* y, 
     const size_t lds = 4 * (size_t)CsrStage<T>::wave_bytes(slots);
     if (slots < 1 || lds > kCsrStageLds) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_csr_staged<T, S>), dim3((unsigned)blocks), dim3(256), lds, stream, a.n,
-                       a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, (T)alpha, (T)beta,
-                       slots, col_nt ? 1 : 0);
+                       a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, a.row_map, (T)alpha,
+                       (T)beta, slots, col_nt ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -216,7 +226,8 @@ static hipError_t run(const CsrView& a, void* y, const void* x, double alpha, do
     const int64_t blocks = ((int64_t)a.n + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_csr_vector<T, S, R>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       a.n, a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, (T)alpha,
+                       a.n, a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, a.row_map,
+                       (T)alpha,
                        (T)beta);
     return hipGetLastError();
 }

@@ -128,6 +128,32 @@ def test_csr_staged(sw, name, dtype):
     M.close()
 
 
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("name", ["c1", "ragged", "every_len", "long_spans", "box27", "nnz0",
+                                  "dups_unsorted", "n1"])
+@pytest.mark.parametrize("kernel", ["vector", "balanced", "auto"])
+def test_hec_tail_kernels(kernel, name, dtype):
+    """HEC with either tail kernel (and the timed choice) against the oracle,
+    at the default split and at K = 1 (almost everything in the tail)."""
+    a = MATS[name]()
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    x_np, y0_np = (v.astype(npdt) for v in vectors(a.n, 23))
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n)
+    for K in (-1, 1):
+        M.convert("hec", ell_width=K, csr_kernel=kernel)
+        inf = M.info()
+        if inf["tail_nnz"] > 0 and kernel != "auto":
+            assert inf["tail_kernel"] == kernel
+        for alpha, beta in AB:
+            check(a, x_np, y0_np, alpha, beta, apply(M, x, y0, alpha, beta), dtype,
+                  what="hec tail %s K=%d %s a=%g b=%g" % (kernel, K, name, alpha, beta))
+    M.close()
+
+
 def test_csr_stage_errors():
     a = MATS["c1"]()
     M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
