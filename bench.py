@@ -52,10 +52,20 @@ def kernels_of(fmt: str, info: dict) -> str:
     if fmt == "csr":
         if info.get("csr_kernel") == "balanced":
             return "k_scale + k_tail%s<CSR>" % ("_win" if info["x_window"] else "")
-        return "k_csr_vector<S=%d,R=%d>" % (info["subwave"], info["csr_rows"])
+        return _vector_kernel(info["subwave"], info["csr_rows"], info.get("csr_stage_slots", 0))
+    k = KERNELS[fmt]
+    if fmt == "hec" and info.get("tail_kernel") == "vector":
+        k = k.replace("k_tail<CSR>", _vector_kernel(info["tail_subwave"], info["tail_rows"],
+                                                    info["tail_stage_slots"]))
     if fmt in ("ellr", "hyb", "hec") and info.get("x_window"):
-        return KERNELS[fmt].replace("k_ell", "k_ell_win").replace("k_tail", "k_tail_win")
-    return KERNELS[fmt]
+        k = k.replace("k_ell", "k_ell_win").replace("k_tail", "k_tail_win")
+    return k
+
+
+def _vector_kernel(sw: int, rows: int, slots: int) -> str:
+    if slots > 0:
+        return "k_csr_staged<S=%d>" % sw
+    return "k_csr_vector<S=%d,R=%d>" % (sw, rows)
 
 
 def row_info_bytes(fmt: str, n: int, tail_nnz: int = 0) -> int:
@@ -141,11 +151,13 @@ def kernel_bases(fmt: str, info: dict) -> set:
     if fmt == "csr":
         if info.get("csr_kernel") == "balanced":
             return {"k_scale", "k_tail" + win}
-        return {"k_csr_vector"}
+        return {"k_csr_staged" if info.get("csr_stage_slots", 0) > 0 else "k_csr_vector"}
     if fmt == "sell64":
         return {"k_sell"}
     out = {"k_ell" + win}
-    if fmt in ("hyb", "hec") and info.get("tail_nnz", 0) > 0:
+    if fmt == "hec" and info.get("tail_nnz", 0) > 0 and info.get("tail_kernel") == "vector":
+        out.add("k_csr_staged" if info.get("tail_stage_slots", 0) > 0 else "k_csr_vector")
+    elif fmt in ("hyb", "hec") and info.get("tail_nnz", 0) > 0:
         out.add("k_tail" + win)
     return out
 

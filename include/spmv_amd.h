@@ -213,6 +213,9 @@ typedef struct {
                                 can stage (0: the kernel reads directly) */
     int32_t tail_kernel;   /* HYB / HEC with tail entries: SPMV_CSR_BALANCED or
                               (HEC only) SPMV_CSR_VECTOR; otherwise 0 */
+    int32_t tail_subwave;  /* HEC vector tail: lanes per row, rows per lane */
+    int32_t tail_rows;     /* group and LDS slots per wave (0: direct); */
+    int32_t tail_stage_slots; /* all 0 otherwise */
 } spmv_info_t;
 
 /* arrays readable with spmv_export */

@@ -76,7 +76,8 @@ class _Info(ctypes.Structure):
                 ("sort_window", ctypes.c_int32),
                 ("band_fraction", ctypes.c_double),
                 ("ell_rows", ctypes.c_int64), ("csr_stage_slots", ctypes.c_int32),
-                ("tail_kernel", ctypes.c_int32)]
+                ("tail_kernel", ctypes.c_int32), ("tail_subwave", ctypes.c_int32),
+                ("tail_rows", ctypes.c_int32), ("tail_stage_slots", ctypes.c_int32)]
 
 
 def _load():

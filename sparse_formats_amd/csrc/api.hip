@@ -1624,6 +1624,10 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.tail_kernel = (h->format == SPMV_HYB || h->format == SPMV_HEC) && b.tail_nnz > 0
                         ? (b.tail_vector ? SPMV_CSR_VECTOR : SPMV_CSR_BALANCED)
                         : SPMV_CSR_AUTO;
+    const bool tv = h->format == SPMV_HEC && b.tail_nnz > 0 && b.tail_vector;
+    i.tail_subwave = tv ? b.tail_vec.subwave : 0;
+    i.tail_rows = tv ? b.tail_vec.rows : 0;
+    i.tail_stage_slots = tv ? b.tail_vec.slots : 0;
     i.csr_kernel = h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED : SPMV_CSR_VECTOR;
     i.sort_window = b.sort_window;
     i.ell_groups = (h->format == SPMV_ELLR || h->format == SPMV_HYB || h->format == SPMV_HEC)

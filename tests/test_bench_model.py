@@ -115,3 +115,14 @@ def test_traffic_record_checks(tmp_path):
     assert bench.traffic_for("w:f64:hyb", hyb, str(p)) is None          # stale sources
     assert bench.traffic_for("w:f64:hec", hyb, str(p)) is None          # no record
     assert bench.kernel_bases("hec", {"x_window": 1, "tail_nnz": 0}) == {"k_ell_win"}
+    staged = bench.kernel_bases("csr", {"csr_kernel": "vector", "x_window": 0,
+                                        "csr_stage_slots": 512})
+    assert staged == {"k_csr_staged"}
+    assert bench.traffic_for("w:f64:csr", staged, str(p)) is None       # no staged record
+    hec_vec = {"x_window": 0, "tail_nnz": 9, "tail_kernel": "vector", "tail_subwave": 2,
+               "tail_rows": 1, "tail_stage_slots": 256}
+    assert bench.kernel_bases("hec", hec_vec) == {"k_ell", "k_csr_staged"}
+    assert bench.kernels_of("hec", hec_vec) == "k_ell + k_csr_staged<S=2>"
+    hec_vec.update(tail_stage_slots=0, tail_subwave=4, tail_rows=2)
+    assert bench.kernel_bases("hec", hec_vec) == {"k_ell", "k_csr_vector"}
+    assert bench.kernels_of("hec", hec_vec) == "k_ell + k_csr_vector<S=4,R=2>"
