@@ -29,7 +29,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FORMATS = ["csr-vector", "csr-balanced", "ellr", "sell64", "hyb", "hec"]
-APPLY = ("k_csr_vector", "k_scale", "k_tail", "k_tail_win", "k_ell", "k_ell_win", "k_sell",
+APPLY = ("k_csr_vector", "k_csr_staged", "k_scale", "k_tail", "k_tail_win", "k_ell", "k_ell_win", "k_sell",
          "k_sell_chunks")
 SOURCES = ["sparse_formats_amd/csrc/" + f for f in
            ("api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "common.h", "internal.h")]
@@ -70,8 +70,9 @@ def split_apply(seq):
 def per_format_applies(timed, formats):
     """Attribute the bench's apply dispatches to formats: every step applies
     the formats in order, each with its own kernels (CSR: k_csr_vector, or
-    k_scale + a CSR tail; ELL-R: one ELL kernel; SELL-64: k_sell [+ chunks];
-    HYB / HEC: one ELL kernel [+ a COO / CSR tail])."""
+    k_csr_staged or k_scale + a CSR tail; ELL-R: one ELL kernel; SELL-64: k_sell
+    [+ chunks]; HYB / HEC: one ELL kernel [+ a COO / CSR tail, for HEC possibly
+    the vector CSR kernel])."""
     out = {f: [] for f in formats}
     i = 0
     names = [(short(r["Kernel_Name"])[0], short(r["Kernel_Name"])[1],
@@ -85,10 +86,11 @@ def per_format_applies(timed, formats):
             i += 1
             follow = {"csr": ("k_tail", "k_tail_win") if s == "k_scale" else (),
                       "sell64": ("k_sell_chunks",),
-                      "hyb": ("k_tail", "k_tail_win"), "hec": ("k_tail", "k_tail_win")}.get(f, ())
+                      "hyb": ("k_tail", "k_tail_win"),
+                      "hec": ("k_tail", "k_tail_win", "k_csr_vector", "k_csr_staged")}.get(f, ())
             coo = {"hyb": "true", "hec": "false", "csr": "false"}.get(f)
             if i < len(names) and names[i][0] in follow and (
-                    f == "sell64" or names[i][1].endswith(coo + ">")):
+                    not names[i][0].startswith("k_tail") or names[i][1].endswith(coo + ">")):
                 ks.append(names[i][1])
                 tot += names[i][2]
                 i += 1
