@@ -15,7 +15,8 @@ Functions (each restates a definition from the pages; see oracle.c):
                     optionally sorted only inside windows of sigma rows.
 * ``ell_pad_fraction`` -- share of padding slots a lane-per-row sweep of an
                     unsorted ELL part reads (the windowed-sort decision).
-* ``hyb_width``  -- the ELL width of the HYB/HEC split.
+* ``hyb_width``  -- the ELL width of the HYB/HEC split (the ceil(n/3) rule).
+* ``regular_width`` -- the other width candidate (99 % of rows fit whole).
 * ``tail``       -- the irregular part of the split as COO and CSR.
 * ``check``      -- the per-entry tolerance test |y - y_ref| <= tol * scale.
 * ``cg``, ``bicgstab`` -- textbook Krylov solvers over the product (fp64).
@@ -70,6 +71,8 @@ def _load():
         lib.oracle_sell_fill.argtypes = [I64, P, P, P, ctypes.c_int, P, P, ctypes.c_int, P, P]
         lib.oracle_hyb_width.argtypes = [I64, P, I64]
         lib.oracle_hyb_width.restype = I64
+        lib.oracle_regular_width.argtypes = [I64, P]
+        lib.oracle_regular_width.restype = I64
         lib.oracle_tail_nnz.argtypes = [I64, P, I64]
         lib.oracle_tail_nnz.restype = I64
         lib.oracle_tail.argtypes = [I64, P, P, P, ctypes.c_int, I64, P, P, P, P]
@@ -198,6 +201,12 @@ def sell(a, sigma: int = 0, permuted: bool = False):
 
 def hyb_width(a, requested: int = -1) -> int:
     return int(_load().oracle_hyb_width(a.n, _p(_c(a.rowptr, np.int64)), int(requested)))
+
+
+def regular_width(a) -> int:
+    """The second HYB/HEC width candidate: the smallest k with at most 1 % of
+    the rows longer than k."""
+    return int(_load().oracle_regular_width(a.n, _p(_c(a.rowptr, np.int64))))
 
 
 def tail(a, K: int):

@@ -379,6 +379,23 @@ int64_t oracle_hyb_width(int64_t n, const int64_t *rowptr, int64_t requested)
     return K;
 }
 
+/* the other HYB/HEC width candidate: the smallest k such that at most 1 % of
+ * the rows are longer than k (100 * #{i : len_i > k} <= n), so that the ELL
+ * part holds the regular rows whole and the tail only the few long ones */
+int64_t oracle_regular_width(int64_t n, const int64_t *rowptr)
+{
+    int64_t W = oracle_max_len(n, rowptr);
+    for (int64_t k = 0; k <= W; ++k) {
+        int64_t longer = 0;
+        for (int64_t i = 0; i < n; ++i)
+            if (rowptr[i + 1] - rowptr[i] > k)
+                ++longer;
+        if (100 * longer <= n)
+            return k;
+    }
+    return W;
+}
+
 /* number of tail entries for width K */
 int64_t oracle_tail_nnz(int64_t n, const int64_t *rowptr, int64_t K)
 {

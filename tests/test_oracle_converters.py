@@ -170,6 +170,25 @@ def test_hyb_width_fixture():
         assert oracle.hyb_width(a) == int(k), (k, lens)
 
 
+def test_regular_width_examples():
+    """Hand-counted: the smallest k with at most 1 % of the rows longer."""
+    def mk(lens):
+        lens = np.asarray(lens, np.int64)
+        rp = np.concatenate([[0], np.cumsum(lens)])
+        return CSR(len(lens), rp, np.zeros(rp[-1], np.int32), np.ones(rp[-1]))
+    assert oracle.regular_width(mk([1] * 99 + [50])) == 1       # one row of 100 may be longer
+    assert oracle.regular_width(mk([1] * 98 + [50, 50])) == 50  # two may not
+    assert oracle.regular_width(mk([3] * 100)) == 3
+    assert oracle.regular_width(mk([0] * 10)) == 0
+    assert oracle.regular_width(mk([])) == 0
+    assert oracle.regular_width(mk([5, 1, 1])) == 5             # n < 100: no row may be longer
+    lens = [20 + i % 21 for i in range(2000)]                   # 20..40, as in the FEM block
+    for i in range(0, 2000, 100):
+        lens[i] = 2000                                          # exactly 1 % long rows
+    assert oracle.regular_width(mk(lens)) == 40
+    assert oracle.hyb_width(mk(lens)) < 40
+
+
 def test_hyb_width_stencils_and_override():
     a = c1_laplace2d()
     assert oracle.hyb_width(a) == 5
