@@ -731,6 +731,10 @@ void build_sell(const spmv_handle* h, int sort_window, bool permuted, Built& b, 
 }
 
 // row-length histogram -> HYB/HEC width K (ceil(n/3) rule unless requested)
+// requested >= 0: that width (clamped to the longest row); -1: the
+// ceil(n/3) rule; kRegularWidth: the width that holds 99 % of the rows whole
+constexpr int kRegularWidth = -2;
+
 int64_t choose_width(const spmv_handle* h, int requested, std::vector<int>& hist, hipStream_t s) {
     const int W = h->max_len;
     hist.assign((size_t)W + 1, 0);
@@ -745,6 +749,15 @@ int64_t choose_width(const spmv_handle* h, int requested, std::vector<int>& hist
               "hipMemcpyAsync");
     sync(s);
     if (requested >= 0) return std::min<int64_t>(requested, W);
+    if (requested == kRegularWidth) {
+        // the smallest k with at most 1 % of the rows longer than k
+        int64_t longer = h->n;  // rows longer than k, starting at k = -1
+        for (int64_t k = 0; k <= W; ++k) {
+            longer -= hist[(size_t)k];
+            if (100 * longer <= h->n) return k;
+        }
+        return W;
+    }
     const int64_t need = (h->n + 2) / 3;
     int64_t at_least = h->n;  // rows with length >= k, starting at k = 0
     int64_t K = 0;
@@ -1148,6 +1161,20 @@ int run_guarded(const std::function<void()>& body) {
 
 bool valid_format(int f) { return f >= SPMV_CSR && f <= SPMV_HEC; }
 
+// HYB/HEC at ELL width `width` (as choose_width takes it): the split, the
+// window and group choices, and HEC's tail kernel
+void build_split_tuned(spmv_handle* h, int format, const spmv_convert_opts& o, int width,
+                       Built& b, hipStream_t s) {
+    b.format = format;
+    if (h->dtype == SPMV_F64)
+        build_split<double>(h, format, width, o.sort_window, b, s);
+    else
+        build_split<float>(h, format, width, o.sort_window, b, s);
+    decide_window(h, format, o.x_window, b, s);
+    choose_groups(h, o.ell_groups, b);
+    if (format == SPMV_HEC) tune_hec_tail(h, o.csr_kernel, b, s);
+}
+
 // Build `format` (options already validated) and make it the active format.
 void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
     if (format == SPMV_CSR) {
@@ -1183,13 +1210,28 @@ void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
         else
             build_sell<float>(h, o.sort_window, o.permuted_basis != 0, b, s);
     } else {
-        if (f64)
-            build_split<double>(h, format, o.ell_width, o.sort_window, b, s);
-        else
-            build_split<float>(h, format, o.ell_width, o.sort_window, b, s);
-        decide_window(h, format, o.x_window, b, s);
-        choose_groups(h, o.ell_groups, b);
-        if (format == SPMV_HEC) tune_hec_tail(h, o.csr_kernel, b, s);
+        build_split_tuned(h, format, o, o.ell_width, b, s);
+        if (o.ell_width < 0 && h->n > 0) {
+            // second width candidate: the rows of regular length whole in the
+            // ELL part (with a sorted ELL part its padding costs storage more
+            // than reads), if it differs, fits the budget and applies faster
+            std::vector<int> hist;
+            const int64_t K2 = choose_width(h, kRegularWidth, hist, s);
+            const double need = (double)K2 * (double)((h->n + kEllBlock - 1) / kEllBlock) *
+                                (double)kEllBlock * (4.0 + (double)h->vsize);
+            if (K2 > b.ell_width && need <= (double)budget_bytes(o)) {
+                Built b2;
+                build_split_tuned(h, format, o, (int)K2, b2, s);
+                DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
+                hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
+                const float t1 = time_launches(
+                    [&] { return launch_built(h, b, format, ys.p, xs.p, 1.0, 0.0, s); }, s);
+                const float t2 = time_launches(
+                    [&] { return launch_built(h, b2, format, ys.p, xs.p, 1.0, 0.0, s); }, s);
+                sync(s);
+                if (t2 < t1) b = std::move(b2);
+            }
+        }
     }
     h->fmt = std::move(b);
     h->format = format;

@@ -229,8 +229,11 @@ def test_layouts_bit_exact(name, dtype):
     for fmt in ("hyb", "hec"):
         for req, sigma in ((-1, 0), (0, 0), (3, 0), (-1, 64), (-1, 1024), (3, 256), (-1, -1)):
             M.convert(fmt, ell_width=req, sort_window=sigma)
-            K = oracle.hyb_width(a, req)
-            assert M.info()["ell_width"] == K
+            K = M.info()["ell_width"]
+            if req >= 0:
+                assert K == oracle.hyb_width(a, req)
+            else:   # the faster of the two width candidates
+                assert K in (oracle.hyb_width(a), max(oracle.hyb_width(a), oracle.regular_width(a)))
             assert M.info()["ell_stride"] == oracle.ELL_BLOCK_SPLIT
             if sigma < 0:   # sorted inside whole blocks when >10% padding would be read
                 sigma = oracle.ELL_BLOCK_SPLIT if oracle.ell_pad_fraction(a, K) > 0.1 else 0
