@@ -416,6 +416,52 @@ def test_apply_on_side_stream():
     check(a, x_np, None, 1.0, 0.0, y.cpu().numpy(), torch.float64)
 
 
+GRAPH_CASES = [("csr", dict(csr_kernel="vector", csr_stage=1)),
+               ("csr", dict(csr_kernel="vector", csr_stage=0)),
+               ("csr", dict(csr_kernel="balanced", x_window=0)),
+               ("csr", dict(csr_kernel="balanced", x_window=1)),
+               ("ellr", dict(x_window=0)), ("ellr", dict(x_window=1)), ("ellr", dict(ell_groups=4)),
+               ("sell64", {}),
+               ("hyb", dict(x_window=0)), ("hyb", dict(x_window=1)),
+               ("hec", dict(csr_kernel="vector", x_window=0)),
+               ("hec", dict(csr_kernel="balanced", x_window=1))]
+
+
+@pytest.mark.parametrize("fmt,kw", GRAPH_CASES)
+def test_apply_in_hip_graph(fmt, kw):
+    """apply captured in a HIP graph: every replay, with new x and y written
+    by eager work in between, matches the oracle (and the eager apply)."""
+    a = _banded() if kw.get("x_window") == 1 else MATS["long_spans"]()
+    xs = [vectors(a.n, 60 + r)[0] for r in range(4)]
+    _, y0_np = vectors(a.n, 59)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt, **kw)
+    x = torch.from_numpy(xs[0]).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    y = y0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        M.apply(y, x, 1.5, -0.5)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.apply(y, x, 1.5, -0.5)
+    for r in range(4):
+        x.copy_(torch.from_numpy(xs[r]))
+        y.copy_(y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        yg = y.cpu().numpy()
+        check(a, xs[r], y0_np, 1.5, -0.5, yg, torch.float64,
+              what="graph %s %s replay %d" % (fmt, kw, r))
+        ye = apply(M, x, y0, 1.5, -0.5)
+        check(a, xs[r], y0_np, 1.5, -0.5, ye, torch.float64, what="eager %s %s" % (fmt, kw))
+    del g
+    M.close()
+
+
 def _banded():
     # banded rows (|col - row| up to 12,000: partly beyond the LDS window),
     # a few long rows and 5% far columns; enough rows and entries that the
