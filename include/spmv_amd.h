@@ -340,8 +340,9 @@ typedef struct {
  *   opts  method, iteration cap, relative tolerance
  *   info  host out-parameter (may be NULL)
  * Vector updates are fused kernels; inner products are fp64 sums in a fixed
- * order.  The host drives the iteration (it reads back two scalars per
- * iteration), so the call is synchronous on `stream`.  Work vectors (3 n for
+ * order.  The iteration's scalars stay on the device and batches of eight
+ * iterations are replayed from a HIP graph on a private stream (ordered
+ * after `stream`'s earlier work); the call returns when the solve is done.  Work vectors (3 n for
  * CG, 6 n for BiCGSTAB) are allocated for the call.  Not reaching the
  * tolerance is not an error (info->converged = 0).
  * Errors: STATE, INVALID_ARG (null pointer, overlap, bad method / cap /

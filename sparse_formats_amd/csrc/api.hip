@@ -1285,84 +1285,133 @@ void convert_auto(spmv_handle* h, const spmv_convert_opts& o) {
 // apply; the scalars of an iteration are two fp64 inner products read back
 // (the textbook forms of conjugate gradients and BiCGSTAB, stopping on the
 // recurred residual).
+// Iterations enqueued per graph replay: the host reads the state back once
+// per replay, so a solve ends at most kSolveGraphIters - 1 idle iterations
+// (whose kernels leave at once, applies aside) after convergence.
+constexpr int kSolveGraphIters = 8;
+
+// RAII holders for the solve's private stream and graph
+struct StreamHolder {
+    hipStream_t s = nullptr;
+    ~StreamHolder() {
+        if (s) (void)hipStreamDestroy(s);
+    }
+};
+struct GraphHolder {
+    hipGraph_t g = nullptr;
+    hipGraphExec_t e = nullptr;
+    ~GraphHolder() {
+        if (e) (void)hipGraphExecDestroy(e);
+        if (g) (void)hipGraphDestroy(g);
+    }
+};
+
+// Krylov solve driven from the device: the iteration's scalars stay in
+// device memory (st) and kSolveGraphIters iterations are captured once in a
+// HIP graph and replayed; the host only reads the done flag after each
+// replay.  The recurrences are the textbook ones (see the kernels in
+// k_vec.hip); the setup (b.b, r = b - A x, r.r) runs before the capture.
 spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_opts& o,
-                      hipStream_t s) {
+                      hipStream_t caller) {
     const int64_t n = h->n;
     const bool f64 = h->dtype == SPMV_F64;
     const size_t vb = (size_t)n * h->vsize;
     const int nvec = o.method == SPMV_SOLVE_CG ? 3 : 6;
-    DevBuf work(vb * nvec), partial((size_t)2 * kSolveBlocks * 8), scal(16);
+    auto chk = [](hipError_t e, const char* what) { hip_check(e, what); };
+    // the caller's stream may be the null stream, which cannot be captured:
+    // work on a private stream ordered after the caller's work
+    sync(caller);
+    StreamHolder sh;
+    chk(hipStreamCreateWithFlags(&sh.s, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+    hipStream_t s = sh.s;
+    DevBuf work(vb * nvec), partial((size_t)2 * kSolveBlocks * 8), state(kStCount * 8);
     char* w = work.as<char>();
     void *r = w, *p = w + vb, *q = w + 2 * vb;           // CG: r, p, q = A p
     void *rh = w + 2 * vb, *v = w + 3 * vb, *sv = w + 4 * vb, *t = w + 5 * vb;  // BiCGSTAB
     double* pd = partial.as<double>();
-    double* out = scal.as<double>();
-    auto chk = [](hipError_t e, const char* what) { hip_check(e, what); };
+    double* st = state.as<double>();
     auto apply = [&](void* yy, const void* xx, double alpha, double beta) {
         chk(launch_built(h, h->fmt, h->format, yy, xx, alpha, beta, s), "apply");
     };
-    auto fetch = [&](double* d) {
-        chk(hipMemcpyAsync(d, out, 16, hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
-        sync(s);
-    };
     double d2[2];
-    // b . b and r = b - A x
-    chk(launch_dot2(n, f64, b, b, nullptr, nullptr, pd, out, s), "dot");
-    fetch(d2);
-    const double bnorm = std::sqrt(d2[0]);
+    auto dot = [&](const void* a0, const void* b0) {
+        chk(launch_dot2(n, f64, a0, b0, nullptr, nullptr, pd, st + kStPQ, s), "dot");
+        chk(hipMemcpyAsync(d2, st + kStPQ, 8, hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+        sync(s);
+        return d2[0];
+    };
+    // setup: ||b||, r = b - A x, r.r, the state
+    const double bnorm = std::sqrt(dot(b, b));
     chk(hipMemcpyAsync(r, b, vb, hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
     apply(r, x, -1.0, 1.0);
-    chk(launch_dot2(n, f64, r, r, nullptr, nullptr, pd, out, s), "dot");
-    fetch(d2);
-    double rr = d2[0];
+    const double rr0 = dot(r, r);
     const double goal = o.rtol * bnorm;
-    int k = 0;
+    double st0[kStCount] = {};
+    st0[kStRR] = rr0;
+    st0[kStGoal] = goal;
+    st0[kStMaxIt] = (double)o.max_iter;
+    st0[kStDone] = std::sqrt(rr0) > goal ? 0.0 : 1.0;
+    st0[kStRho] = st0[kStAlpha] = st0[kStOmega] = 1.0;
+    chk(hipMemcpyAsync(st, st0, sizeof st0, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
     if (o.method == SPMV_SOLVE_CG) {
         chk(hipMemcpyAsync(p, r, vb, hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
-        while (std::sqrt(rr) > goal && k < o.max_iter) {
-            apply(q, p, 1.0, 0.0);
-            chk(launch_dot2(n, f64, p, q, nullptr, nullptr, pd, out, s), "dot");
-            fetch(d2);
-            const double alpha = rr / d2[0];
-            chk(launch_cg_xr(n, f64, x, r, p, q, alpha, pd, out, s), "cg update");
-            fetch(d2);
-            const double beta = d2[0] / rr;
-            chk(launch_update_p(n, f64, p, r, nullptr, beta, 0.0, s), "cg direction");
-            rr = d2[0];
-            ++k;
-        }
     } else {
         chk(hipMemcpyAsync(rh, r, vb, hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
         chk(hipMemsetAsync(p, 0, vb, s), "hipMemsetAsync");
         chk(hipMemsetAsync(v, 0, vb, s), "hipMemsetAsync");
-        double rho = 1.0, alpha = 1.0, omega = 1.0;
-        while (std::sqrt(rr) > goal && k < o.max_iter) {
-            chk(launch_dot2(n, f64, rh, r, nullptr, nullptr, pd, out, s), "dot");
-            fetch(d2);
-            const double rho_new = d2[0];
-            if (rho_new == 0.0) break;  // breakdown
-            const double beta = (rho_new / rho) * (alpha / omega);
-            chk(launch_update_p(n, f64, p, r, v, beta, omega, s), "bicgstab direction");
+    }
+    sync(s);
+    // one iteration, enqueued on s (captured below, never run eagerly)
+    auto iteration = [&] {
+        if (o.method == SPMV_SOLVE_CG) {
+            apply(q, p, 1.0, 0.0);
+            chk(launch_dot2(n, f64, p, q, nullptr, nullptr, pd, nullptr, s), "dot");
+            chk(launch_solve_step(pd, st, kStepCgPQ, s), "step");
+            chk(launch_cg_xr(n, f64, x, r, p, q, st, pd, s), "cg update");
+            chk(launch_solve_step(pd, st, kStepCgRR, s), "step");
+            chk(launch_update_p(n, f64, p, r, nullptr, st, s), "cg direction");
+        } else {
+            chk(launch_dot2(n, f64, rh, r, nullptr, nullptr, pd, nullptr, s), "dot");
+            chk(launch_solve_step(pd, st, kStepBiRho, s), "step");
+            chk(launch_update_p(n, f64, p, r, v, st, s), "bicgstab direction");
             apply(v, p, 1.0, 0.0);
-            chk(launch_dot2(n, f64, rh, v, nullptr, nullptr, pd, out, s), "dot");
-            fetch(d2);
-            alpha = rho_new / d2[0];
-            chk(launch_axmy(n, f64, sv, r, v, alpha, s), "bicgstab s");
+            chk(launch_dot2(n, f64, rh, v, nullptr, nullptr, pd, nullptr, s), "dot");
+            chk(launch_solve_step(pd, st, kStepBiRV, s), "step");
+            chk(launch_axmy(n, f64, sv, r, v, st, s), "bicgstab s");
             apply(t, sv, 1.0, 0.0);
-            chk(launch_dot2(n, f64, t, sv, t, t, pd, out, s), "dot");
-            fetch(d2);
-            omega = d2[1] > 0 ? d2[0] / d2[1] : 0.0;
-            chk(launch_bicg_xr(n, f64, x, r, p, sv, t, alpha, omega, pd, out, s), "bicgstab update");
-            fetch(d2);
-            rr = d2[0];
-            rho = rho_new;
-            ++k;
-            if (omega == 0.0) break;  // s was already the residual of x + alpha p
+            chk(launch_dot2(n, f64, t, sv, t, t, pd, nullptr, s), "dot");
+            chk(launch_solve_step(pd, st, kStepBiOmega, s), "step");
+            chk(launch_bicg_xr(n, f64, x, r, p, sv, t, st, pd, s), "bicgstab update");
+            chk(launch_solve_step(pd, st, kStepBiRR, s), "step");
+        }
+    };
+    if (st0[kStDone] == 0.0) {
+        GraphHolder gh;
+        chk(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+        try {
+            for (int i = 0; i < kSolveGraphIters; ++i) iteration();
+        } catch (...) {
+            hipGraph_t g = nullptr;
+            (void)hipStreamEndCapture(s, &g);
+            if (g) (void)hipGraphDestroy(g);
+            throw;
+        }
+        chk(hipStreamEndCapture(s, &gh.g), "hipStreamEndCapture");
+        chk(hipGraphInstantiate(&gh.e, gh.g, nullptr, nullptr, 0), "hipGraphInstantiate");
+        double flag = 0.0;
+        const int64_t replays = ((int64_t)o.max_iter + kSolveGraphIters - 1) / kSolveGraphIters;
+        for (int64_t k = 0; k < replays && flag == 0.0; ++k) {
+            chk(hipGraphLaunch(gh.e, s), "hipGraphLaunch");
+            chk(hipMemcpyAsync(&flag, st + kStDone, 8, hipMemcpyDeviceToHost, s),
+                "hipMemcpyAsync");
+            sync(s);
         }
     }
+    chk(hipMemcpyAsync(st0, st, sizeof st0, hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
     sync(s);  // before the work vectors are freed
+    const double rr = st0[kStRR];
     spmv_solve_info res;
-    res.iterations = k;
+    res.iterations = (int)st0[kStK];
     res.rel_residual = bnorm > 0 ? std::sqrt(rr) / bnorm : std::sqrt(rr);
     res.converged = std::sqrt(rr) <= goal ? 1 : 0;
     return res;

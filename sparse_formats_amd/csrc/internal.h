@@ -137,22 +137,31 @@ hipError_t launch_permute(int64_t n, bool f64, void* dst, const void* src, const
 // Krylov solver vector kernels (k_vec.hip).  partial: device double[2 *
 // kSolveBlocks]; out: device double[2].  Inner products in fp64.
 constexpr int kSolveBlocks = 1024;
-// out[0] = a0 . b0, out[1] = a1 . b1 (0 when a1 is nullptr)
+// out[0] = a0 . b0, out[1] = a1 . b1 (0 when a1 is nullptr); out == nullptr
+// leaves the sums in partial only (for launch_solve_step)
 hipError_t launch_dot2(int64_t n, bool f64, const void* a0, const void* b0, const void* a1,
                        const void* b1, double* partial, double* out, hipStream_t s);
-// x += alpha p, r -= alpha q, out[0] = r . r
+// Device-resident scalars of a solve (double st[kStCount]); the kernels below
+// read them and do nothing once st[kStDone] is set.
+enum SolveState : int {
+    kStRR, kStGoal, kStK, kStMaxIt, kStDone, kStPQ, kStAlpha, kStBeta, kStOmega, kStRho,
+    kStRhoNew, kStCount
+};
+enum SolveStep : int { kStepCgPQ, kStepCgRR, kStepBiRho, kStepBiRV, kStepBiOmega, kStepBiRR };
+// reduce partial (as launch_dot2 leaves it) and advance st by `step`
+hipError_t launch_solve_step(const double* partial, double* st, int step, hipStream_t s);
+// x += alpha p, r -= alpha q (alpha = rr / p.q), partial sums of r . r
 hipError_t launch_cg_xr(int64_t n, bool f64, void* x, void* r, const void* p, const void* q,
-                        double alpha, double* partial, double* out, hipStream_t s);
+                        const double* st, double* partial, hipStream_t s);
 // p = r + beta (p - omega v)  (v == nullptr: p = r + beta p)
 hipError_t launch_update_p(int64_t n, bool f64, void* p, const void* r, const void* v,
-                           double beta, double omega, hipStream_t s);
+                           const double* st, hipStream_t s);
 // s = r - alpha v
 hipError_t launch_axmy(int64_t n, bool f64, void* s_out, const void* r, const void* v,
-                       double alpha, hipStream_t s);
-// x += alpha p + omega s, r = s - omega t, out[0] = r . r
+                       const double* st, hipStream_t s);
+// x += alpha p + omega s, r = s - omega t, partial sums of r . r
 hipError_t launch_bicg_xr(int64_t n, bool f64, void* x, void* r, const void* p, const void* s_in,
-                          const void* t, double alpha, double omega, double* partial,
-                          double* out, hipStream_t s);
+                          const void* t, const double* st, double* partial, hipStream_t s);
 // y = beta * y for n entries (beta == 0 writes zeros and never reads y)
 hipError_t launch_scale(int64_t n, bool f64, void* y, double beta, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);

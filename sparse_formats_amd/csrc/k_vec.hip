@@ -64,12 +64,23 @@ __global__ __launch_bounds__(256) void k_dot_finish(const double* __restrict__ p
     }
 }
 
-// x += alpha p; r -= alpha q; partial sums of r . r
+// The scalars of an iteration live in device memory (st, indexed by
+// SolveState): the step kernel computes them from the inner products and the
+// vector kernels read them, so an iteration needs no host round trip and can
+// be replayed from a HIP graph.  Once st[kStDone] is set every kernel below
+// leaves without writing, so iterations enqueued past convergence change
+// nothing.
+__device__ __forceinline__ bool solve_done(const double* st) { return st[kStDone] != 0.0; }
+
+// x += alpha p; r -= alpha q; partial sums of r . r   (alpha = rr / p.q)
 template <typename T>
 __global__ __launch_bounds__(256) void k_cg_xr(int64_t n, T* __restrict__ x, T* __restrict__ r,
                                                const T* __restrict__ p, const T* __restrict__ q,
-                                               T alpha, double* __restrict__ partial) {
+                                               const double* __restrict__ st,
+                                               double* __restrict__ partial) {
     __shared__ double sh[4];
+    if (solve_done(st)) return;
+    const T alpha = (T)(st[kStPQ] != 0.0 ? st[kStRR] / st[kStPQ] : 0.0);
     double s = 0;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         x[i] += alpha * p[i];
@@ -81,11 +92,13 @@ __global__ __launch_bounds__(256) void k_cg_xr(int64_t n, T* __restrict__ x, T* 
     if (threadIdx.x == 0) partial[2 * blockIdx.x] = t, partial[2 * blockIdx.x + 1] = 0;
 }
 
-// p = r + beta (p - omega v)   (conjugate gradients: omega = 0, v unused)
+// p = r + beta (p - omega v)   (conjugate gradients: v == nullptr, p = r + beta p)
 template <typename T>
 __global__ __launch_bounds__(256) void k_update_p(int64_t n, T* __restrict__ p,
                                                   const T* __restrict__ r, const T* __restrict__ v,
-                                                  T beta, T omega) {
+                                                  const double* __restrict__ st) {
+    if (solve_done(st)) return;
+    const T beta = (T)st[kStBeta], omega = (T)(v ? st[kStOmega] : 0.0);
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
         p[i] = r[i] + beta * (v ? p[i] - omega * v[i] : p[i]);
 }
@@ -94,7 +107,9 @@ __global__ __launch_bounds__(256) void k_update_p(int64_t n, T* __restrict__ p,
 template <typename T>
 __global__ __launch_bounds__(256) void k_axmy(int64_t n, T* __restrict__ s,
                                               const T* __restrict__ r, const T* __restrict__ v,
-                                              T alpha) {
+                                              const double* __restrict__ st) {
+    if (solve_done(st)) return;
+    const T alpha = (T)st[kStAlpha];
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
         s[i] = r[i] - alpha * v[i];
 }
@@ -103,9 +118,12 @@ __global__ __launch_bounds__(256) void k_axmy(int64_t n, T* __restrict__ s,
 template <typename T>
 __global__ __launch_bounds__(256) void k_bicg_xr(int64_t n, T* __restrict__ x, T* __restrict__ r,
                                                  const T* __restrict__ p, const T* __restrict__ s,
-                                                 const T* __restrict__ t, T alpha, T omega,
+                                                 const T* __restrict__ t,
+                                                 const double* __restrict__ st,
                                                  double* __restrict__ partial) {
     __shared__ double sh[4];
+    if (solve_done(st)) return;
+    const T alpha = (T)st[kStAlpha], omega = (T)st[kStOmega];
     double acc = 0;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         x[i] += alpha * p[i] + omega * s[i];
@@ -115,6 +133,65 @@ __global__ __launch_bounds__(256) void k_bicg_xr(int64_t n, T* __restrict__ x, T
     }
     const double tt = block_sum(acc, sh);
     if (threadIdx.x == 0) partial[2 * blockIdx.x] = tt, partial[2 * blockIdx.x + 1] = 0;
+}
+
+// Sum the partial products in block order (as k_dot_finish), then one
+// thread advances the iteration's scalars:
+//   kStepCgPQ     p.q
+//   kStepCgRR     r.r of the new residual: beta = rr_new / rr, rr = rr_new,
+//                 k += 1, done when ||r|| <= goal or k == max_iter
+//   kStepBiRho    rho_new = rhat.r (done on breakdown rho_new == 0),
+//                 beta = (rho_new / rho) (alpha / omega) with the last alpha
+//   kStepBiRV     alpha = rho_new / rhat.v
+//   kStepBiOmega  omega = t.s / t.t (0 when t = 0)
+//   kStepBiRR     rr = r.r, rho = rho_new, k += 1, done as for CG or when
+//                 omega == 0 (s was already the residual of x + alpha p)
+__global__ __launch_bounds__(256) void k_solve_step(const double* __restrict__ partial, int blocks,
+                                                    double* __restrict__ st, int step) {
+    __shared__ double sh[4];
+    if (solve_done(st)) return;
+    double t[2];
+    for (int k = 0; k < 2; ++k) {
+        double s = 0;
+        for (int b = threadIdx.x; b < blocks; b += 256) s += partial[2 * b + k];
+        t[k] = block_sum(s, sh);
+        __syncthreads();
+    }
+    if (threadIdx.x != 0) return;
+    auto advance = [&](double rr) {
+        st[kStRR] = rr;
+        const double k = st[kStK] + 1.0;
+        st[kStK] = k;
+        if (!(sqrt(rr) > st[kStGoal]) || k >= st[kStMaxIt]) st[kStDone] = 1.0;
+    };
+    switch (step) {
+        case kStepCgPQ:
+            st[kStPQ] = t[0];
+            break;
+        case kStepCgRR:
+            st[kStBeta] = st[kStRR] != 0.0 ? t[0] / st[kStRR] : 0.0;
+            advance(t[0]);
+            break;
+        case kStepBiRho:
+            if (t[0] == 0.0) {
+                st[kStDone] = 1.0;
+                break;
+            }
+            st[kStBeta] = (t[0] / st[kStRho]) * (st[kStAlpha] / st[kStOmega]);
+            st[kStRhoNew] = t[0];
+            break;
+        case kStepBiRV:
+            st[kStAlpha] = st[kStRhoNew] / t[0];
+            break;
+        case kStepBiOmega:
+            st[kStOmega] = t[1] > 0 ? t[0] / t[1] : 0.0;
+            break;
+        case kStepBiRR:
+            st[kStRho] = st[kStRhoNew];
+            advance(t[0]);
+            if (st[kStOmega] == 0.0) st[kStDone] = 1.0;
+            break;
+    }
 }
 
 static unsigned grid_of(int64_t n) {
@@ -130,58 +207,59 @@ hipError_t launch_dot2(int64_t n, bool f64, const void* a0, const void* b0, cons
     else
         hipLaunchKernelGGL(k_dot2<float>, dim3(g), dim3(256), 0, s, n, (const float*)a0,
                            (const float*)b0, (const float*)a1, (const float*)b1, partial);
-    hipLaunchKernelGGL(k_dot_finish, dim3(1), dim3(256), 0, s, partial, (int)g, out);
+    if (out) hipLaunchKernelGGL(k_dot_finish, dim3(1), dim3(256), 0, s, partial, (int)g, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_solve_step(const double* partial, double* st, int step, hipStream_t s) {
+    hipLaunchKernelGGL(k_solve_step, dim3(1), dim3(256), 0, s, partial, (int)kDotBlocks, st, step);
     return hipGetLastError();
 }
 
 hipError_t launch_cg_xr(int64_t n, bool f64, void* x, void* r, const void* p, const void* q,
-                        double alpha, double* partial, double* out, hipStream_t s) {
+                        const double* st, double* partial, hipStream_t s) {
     const unsigned g = kDotBlocks;
     if (f64)
         hipLaunchKernelGGL(k_cg_xr<double>, dim3(g), dim3(256), 0, s, n, (double*)x, (double*)r,
-                           (const double*)p, (const double*)q, alpha, partial);
+                           (const double*)p, (const double*)q, st, partial);
     else
         hipLaunchKernelGGL(k_cg_xr<float>, dim3(g), dim3(256), 0, s, n, (float*)x, (float*)r,
-                           (const float*)p, (const float*)q, (float)alpha, partial);
-    hipLaunchKernelGGL(k_dot_finish, dim3(1), dim3(256), 0, s, partial, (int)g, out);
+                           (const float*)p, (const float*)q, st, partial);
     return hipGetLastError();
 }
 
 hipError_t launch_update_p(int64_t n, bool f64, void* p, const void* r, const void* v,
-                           double beta, double omega, hipStream_t s) {
+                           const double* st, hipStream_t s) {
     if (f64)
         hipLaunchKernelGGL(k_update_p<double>, dim3(grid_of(n)), dim3(256), 0, s, n, (double*)p,
-                           (const double*)r, (const double*)v, beta, omega);
+                           (const double*)r, (const double*)v, st);
     else
         hipLaunchKernelGGL(k_update_p<float>, dim3(grid_of(n)), dim3(256), 0, s, n, (float*)p,
-                           (const float*)r, (const float*)v, (float)beta, (float)omega);
+                           (const float*)r, (const float*)v, st);
     return hipGetLastError();
 }
 
 hipError_t launch_axmy(int64_t n, bool f64, void* s_out, const void* r, const void* v,
-                       double alpha, hipStream_t s) {
+                       const double* st, hipStream_t s) {
     if (f64)
         hipLaunchKernelGGL(k_axmy<double>, dim3(grid_of(n)), dim3(256), 0, s, n, (double*)s_out,
-                           (const double*)r, (const double*)v, alpha);
+                           (const double*)r, (const double*)v, st);
     else
         hipLaunchKernelGGL(k_axmy<float>, dim3(grid_of(n)), dim3(256), 0, s, n, (float*)s_out,
-                           (const float*)r, (const float*)v, (float)alpha);
+                           (const float*)r, (const float*)v, st);
     return hipGetLastError();
 }
 
 hipError_t launch_bicg_xr(int64_t n, bool f64, void* x, void* r, const void* p, const void* s_in,
-                          const void* t, double alpha, double omega, double* partial,
-                          double* out, hipStream_t s) {
+                          const void* t, const double* st, double* partial, hipStream_t s) {
     const unsigned g = kDotBlocks;
     if (f64)
         hipLaunchKernelGGL(k_bicg_xr<double>, dim3(g), dim3(256), 0, s, n, (double*)x,
                            (double*)r, (const double*)p, (const double*)s_in, (const double*)t,
-                           alpha, omega, partial);
+                           st, partial);
     else
         hipLaunchKernelGGL(k_bicg_xr<float>, dim3(g), dim3(256), 0, s, n, (float*)x, (float*)r,
-                           (const float*)p, (const float*)s_in, (const float*)t, (float)alpha,
-                           (float)omega, partial);
-    hipLaunchKernelGGL(k_dot_finish, dim3(1), dim3(256), 0, s, partial, (int)g, out);
+                           (const float*)p, (const float*)s_in, (const float*)t, st, partial);
     return hipGetLastError();
 }
 
