@@ -342,9 +342,9 @@ typedef struct {
  * Vector updates are fused kernels; inner products are fp64 sums in a fixed
  * order.  The iteration's scalars stay on the device and batches of eight
  * iterations are replayed from a HIP graph on a private stream (ordered
- * after `stream`'s earlier work); the call returns when the solve is done.  Work vectors (3 n for
- * CG, 6 n for BiCGSTAB) are allocated for the call.  Not reaching the
- * tolerance is not an error (info->converged = 0).
+ * after `stream`'s earlier work); the call returns when the solve is done.
+ * Work vectors (3 n for CG, 6 n for BiCGSTAB) are allocated for the call.
+ * Not reaching the tolerance is not an error (info->converged = 0).
  * Errors: STATE, INVALID_ARG (null pointer, overlap, bad method / cap /
  * tolerance), NO_MEMORY, HIP.
  */
