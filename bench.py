@@ -54,6 +54,8 @@ def kernels_of(fmt: str, info: dict) -> str:
             return "k_scale + k_tail%s<CSR>" % ("_win" if info["x_window"] else "")
         return _vector_kernel(info["subwave"], info["csr_rows"], info.get("csr_stage_slots", 0))
     k = KERNELS[fmt]
+    if fmt in ("hyb", "hec") and info.get("tail_nnz", 1) == 0:
+        k = "k_ell"
     if fmt == "hec" and info.get("tail_kernel") == "vector":
         k = k.replace("k_tail<CSR>", _vector_kernel(info["tail_subwave"], info["tail_rows"],
                                                     info["tail_stage_slots"]))

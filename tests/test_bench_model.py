@@ -126,3 +126,5 @@ def test_traffic_record_checks(tmp_path):
     hec_vec.update(tail_stage_slots=0, tail_subwave=4, tail_rows=2)
     assert bench.kernel_bases("hec", hec_vec) == {"k_ell", "k_csr_vector"}
     assert bench.kernels_of("hec", hec_vec) == "k_ell + k_csr_vector<S=4,R=2>"
+    assert bench.kernels_of("hyb", {"x_window": 1, "tail_nnz": 0}) == "k_ell_win"
+    assert bench.kernels_of("hyb", {"x_window": 0, "tail_nnz": 3}) == "k_ell + k_tail<COO>"
