@@ -993,9 +993,15 @@ int stage_slots_for(const CsrView& v, bool f64, int sw, hipStream_t s) {
 // to ys with `beta`, and return the fastest and its time.  The staged copy
 // streams val past the caches; col too only when that is faster (a col array
 // that fits the last-level cache beside x stays there over repeated applies).
-float tune_vector(const CsrView& v, bool f64, int sw_lo, int sw_hi, int fix_rows, int fix_stage,
-                  void* ys, const void* xs, double beta, VecShape& best, hipStream_t s) {
+float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw_hi, int fix_rows,
+                  int fix_stage, void* ys, const void* xs, double beta, VecShape& best,
+                  hipStream_t s) {
     float best_ms = 1e30f;
+    // a group that would loop more than kVecMaxPasses times over the longest
+    // row serialises the launch on it: such shapes are not timed (the widest
+    // one in range always is)
+    const int cap = fix_stage == 1 ? std::min(sw_hi, kCsrStageMax) : sw_hi;
+    while (sw_lo < cap && (max_len + sw_lo - 1) / sw_lo > kVecMaxPasses) sw_lo <<= 1;
     for (int sw = sw_lo; sw <= sw_hi; sw <<= 1)
         for (int rows = 1; rows <= kCsrRowsMax; rows <<= 1)
             for (int st = 0; st <= 1; ++st) {
@@ -1056,7 +1062,7 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     float best_ms = 1e30f;
     if (want_vec) {
         VecShape best;
-        best_ms = tune_vector(v, f64, o.subwave ? o.subwave : (h->max_len <= 2 ? 1 : 2),
+        best_ms = tune_vector(v, f64, h->max_len, o.subwave ? o.subwave : (h->max_len <= 2 ? 1 : 2),
                               o.subwave ? o.subwave : 64, o.csr_rows, o.csr_stage, ys.p, xs.p, 0.0,
                               best, s);
         h->subwave = best.subwave, h->csr_rows = best.rows;
@@ -1097,7 +1103,8 @@ void tune_hec_tail(const spmv_handle* h, int kernel, Built& b, hipStream_t s) {
     const CsrView v{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
                     b.tail_col.as<int>(), b.tail_val.p, b.tail_rows.as<int>()};
     VecShape best;
-    const float vec_ms = tune_vector(v, f64, 1, 64, 0, -1, ys.p, xs.p, 1.0, best, s);
+    const float vec_ms =
+        tune_vector(v, f64, h->max_len - b.ell_width, 1, 64, 0, -1, ys.p, xs.p, 1.0, best, s);
     sync(s);
     if (!(bal_ms < kPreferMargin * vec_ms)) {
         b.tail_vector = true;

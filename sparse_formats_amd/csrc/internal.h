@@ -120,6 +120,9 @@ struct TailView {
 // val without keeping it in the caches, and col too when stage_col_nt.
 constexpr int kCsrRowsMax = 4;
 constexpr int kCsrStageMin = 2, kCsrStageMax = 16;
+// vector shapes whose groups would loop more often over the longest row are
+// not tried when a kernel is chosen by timing
+constexpr int kVecMaxPasses = 4096;
 constexpr size_t kCsrStageLds = 64 * 1024;
 hipError_t launch_csr(const CsrView& a, int subwave, int rows, int stage_slots, bool stage_col_nt,
                       bool f64, void* y, const void* x, double alpha, double beta,

@@ -462,6 +462,65 @@ def test_apply_in_hip_graph(fmt, kw):
     M.close()
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_concurrent_applies_on_two_streams(fmt):
+    """One handle applied on two streams at once (different x and y): apply
+    keeps no scratch of its own, so neither result depends on the other."""
+    a = MATS["long_spans"]()
+    x1, y01 = vectors(a.n, 71)
+    x2, y02 = vectors(a.n, 72)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    xa, xb = torch.from_numpy(x1).cuda(), torch.from_numpy(x2).cuda()
+    ya, yb = torch.from_numpy(y01).cuda(), torch.from_numpy(y02).cuda()
+    torch.cuda.synchronize()
+    for _ in range(3):   # several rounds, each adding onto y (beta = 1)
+        with torch.cuda.stream(s1):
+            M.apply(ya, xa, 0.5, 1.0)
+        with torch.cuda.stream(s2):
+            M.apply(yb, xb, -0.25, 1.0)
+    torch.cuda.synchronize()
+    # three applies of alpha A x onto y0 equal one apply of 3 alpha
+    check(a, x1, y01, 1.5, 1.0, ya.cpu().numpy(), torch.float64, what="stream 1 " + fmt)
+    check(a, x2, y02, -0.75, 1.0, yb.cpu().numpy(), torch.float64, what="stream 2 " + fmt)
+    M.close()
+
+
+def _arrow(n=3_000_000, seed=81):
+    """Row 0 holds every column; every other row its diagonal and column 0."""
+    rng = np.random.default_rng(seed)
+    lens = np.full(n, 2, np.int64)
+    lens[0] = n
+    rowptr = np.concatenate([[0], np.cumsum(lens)])
+    col = np.empty(rowptr[-1], np.int32)
+    col[:n] = np.arange(n)
+    rest = np.arange(1, n, dtype=np.int32)
+    col[n::2] = 0
+    col[n + 1::2] = rest
+    return CSR(n, rowptr, col, rng.standard_normal(rowptr[-1]))
+
+
+def test_arrow_matrix_every_format():
+    """A row as long as the matrix (3 M entries) beside rows of 2: the long row
+    goes to the tail, to column chunks or to wide groups, and the conversion
+    does not time shapes that would crawl along it.  ELL-R is refused."""
+    a = _arrow()
+    x_np, y0_np = vectors(a.n, 82)
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
+    for fmt, kw in (("csr", {}), ("csr", dict(csr_kernel="vector")),
+                    ("csr", dict(csr_kernel="vector", csr_stage=1)), ("sell64", {}),
+                    ("hyb", {}), ("hec", {}), ("hec", dict(csr_kernel="vector")), ("auto", {})):
+        M.convert(fmt, **kw)
+        check(a, x_np, y0_np, 0.5, 2.0, apply(M, x, y0, 0.5, 2.0), torch.float64,
+              what="arrow %s %s" % (fmt, kw))
+    with pytest.raises(sf.SpmvError) as e:
+        M.convert("ellr")
+    assert e.value.code == -4
+    M.close()
+
+
 def _banded():
     # banded rows (|col - row| up to 12,000: partly beyond the LDS window),
     # a few long rows and 5% far columns; enough rows and entries that the
