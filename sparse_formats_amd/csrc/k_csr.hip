@@ -21,9 +21,10 @@ namespace spmv {
 // issues the row pointers, values and columns of all R rows (U entries per
 // lane and row, U = 16 / S for small groups so that the first pass covers 16
 // entries of every row) and only then the x reads and sums; longer rows
-// finish in a plain loop.  The R rows of a group are interleaved with those
-// of the other groups of its wave (row = wave base + r * groups + group), so
-// every load instruction covers consecutive rows: neighbouring rows share
+// continue in further passes of U entries.  The R rows of a group are
+// interleaved with those of the other groups of its wave (row = wave base +
+// r * groups + group), so every load instruction covers consecutive rows:
+// neighbouring rows share
 // cache lines of val/col and, for banded matrices, entry u of neighbouring
 // rows usually lies on the same diagonal, so their x reads share lines too.
 // The first pass reads with clamped indices and masks the products, so it
@@ -76,9 +77,25 @@ __global__ __launch_bounds__(256) void k_csr_vector(int n, const int* __restrict
         }
         sum[r] = acc;
     }
+    // longer rows: further passes of U entries per lane, each with all of its
+    // loads issued before the first product (one round trip per pass)
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        for (int k = kb[r] + sub + U * S; k < ke[r]; k += S) sum[r] = fma(val[k], x[col[k]], sum[r]);
+        for (int k0 = kb[r] + sub + U * S; k0 < ke[r]; k0 += U * S) {
+            T vv[U];
+            int cc[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int kc = min(k0 + u * S, ke[r] - 1);
+                vv[u] = val[kc];
+                cc[u] = col[kc];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const T p = vv[u] * x[cc[u]];
+                sum[r] += k0 + u * S < ke[r] ? p : T(0);
+            }
+        }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const T s_r = group_sum<S>(sum[r]);
@@ -115,26 +132,25 @@ struct CsrStage {
     }
 };
 
-// Sum of the entries kb + sub, kb + sub + S, ... below ke; ld(k, v, c) reads
-// entry k, which is clamped to ke - 1 for the masked loads of the first pass.
+// Sum of the entries kb + sub, kb + sub + S, ... below ke in passes of U per
+// lane (every load of a pass issued before its first product); ld(k, v, c)
+// reads entry k, which is clamped to ke - 1 for the masked loads past the
+// row.  The additions happen in the order of k_csr_vector<T, S, 1>, so both
+// kernels give the same sums.
 template <typename T, int S, int U, typename Load>
 __device__ __forceinline__ T group_row_sum(int kb, int ke, int sub, const T* __restrict__ x,
                                            Load ld) {
-    T v[U];
-    int c[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) ld(min(kb + sub + u * S, ke - 1), v[u], c[u]);
     T acc = T(0);
+    for (int k0 = kb + sub; k0 < ke; k0 += U * S) {
+        T v[U];
+        int c[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const T p = v[u] * x[c[u]];
-        acc += kb + sub + u * S < ke ? p : T(0);
-    }
-    for (int k = kb + sub + U * S; k < ke; k += S) {
-        T vk;
-        int ck;
-        ld(k, vk, ck);
-        acc = fma(vk, x[ck], acc);
+        for (int u = 0; u < U; ++u) ld(min(k0 + u * S, ke - 1), v[u], c[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const T p = v[u] * x[c[u]];
+            acc += k0 + u * S < ke ? p : T(0);
+        }
     }
     return acc;
 }
