@@ -180,6 +180,11 @@ typedef struct {
      * directly.  The sums are the same either way.  -1 times both, 0 off,
      * 1 on. */
     int32_t csr_stage;
+    /* Cache policy of the column indices (ELL-R, SELL-64, the ELL part of
+     * HYB/HEC, the staged CSR copy): 0 streams them past the caches like the
+     * values, 1 keeps them in the caches (when they fit the last-level cache
+     * beside x they stay there over repeated applies), -1 times both. */
+    int32_t col_cache;
 } spmv_convert_opts;
 
 /* description of a handle (spmv_info) */
@@ -216,6 +221,7 @@ typedef struct {
     int32_t tail_subwave;  /* HEC vector tail: lanes per row, rows per lane */
     int32_t tail_rows;     /* group and LDS slots per wave (0: direct); */
     int32_t tail_stage_slots; /* all 0 otherwise */
+    int32_t col_cached;    /* 1 when the active kernels keep col in the caches */
 } spmv_info_t;
 
 /* arrays readable with spmv_export */

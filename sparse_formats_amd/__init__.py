@@ -52,7 +52,8 @@ class _ConvertOpts(ctypes.Structure):
                 ("x_window", ctypes.c_int32), ("csr_rows", ctypes.c_int32),
                 ("csr_kernel", ctypes.c_int32), ("sort_window", ctypes.c_int32),
                 ("permuted_basis", ctypes.c_int32), ("ell_groups", ctypes.c_int32),
-                ("footprint_budget_bytes", ctypes.c_uint64), ("csr_stage", ctypes.c_int32)]
+                ("footprint_budget_bytes", ctypes.c_uint64), ("csr_stage", ctypes.c_int32),
+                ("col_cache", ctypes.c_int32)]
 
 
 class _SolveOpts(ctypes.Structure):
@@ -77,7 +78,8 @@ class _Info(ctypes.Structure):
                 ("band_fraction", ctypes.c_double),
                 ("ell_rows", ctypes.c_int64), ("csr_stage_slots", ctypes.c_int32),
                 ("tail_kernel", ctypes.c_int32), ("tail_subwave", ctypes.c_int32),
-                ("tail_rows", ctypes.c_int32), ("tail_stage_slots", ctypes.c_int32)]
+                ("tail_rows", ctypes.c_int32), ("tail_stage_slots", ctypes.c_int32),
+                ("col_cached", ctypes.c_int32)]
 
 
 def _load():
@@ -178,7 +180,8 @@ class Matrix:
     def convert(self, fmt: str, ell_width: int = -1, subwave: int = 0, x_window: int = -1,
                 footprint_budget: int = 0, csr_rows: int = 0,
                 csr_kernel: str = "auto", sort_window: int = -1,
-                permuted_basis: int = 0, ell_groups: int = 0, csr_stage: int = -1) -> "Matrix":
+                permuted_basis: int = 0, ell_groups: int = 0, csr_stage: int = -1,
+                col_cache: int = -1) -> "Matrix":
         """Build `fmt` on the device and make it active (options as in spmv_convert_opts;
         csr_kernel is "auto", "vector" or "balanced")."""
         if fmt not in FORMATS:
@@ -186,7 +189,7 @@ class Matrix:
         ck = CSR_KERNELS.get(csr_kernel, csr_kernel)
         o = _ConvertOpts(int(ell_width), int(subwave), int(x_window), int(csr_rows), int(ck),
                          int(sort_window), int(permuted_basis), int(ell_groups),
-                         int(footprint_budget), int(csr_stage))
+                         int(footprint_budget), int(csr_stage), int(col_cache))
         _check(_lib.spmv_convert(self._h, FORMATS[fmt], ctypes.byref(o)))
         return self
 

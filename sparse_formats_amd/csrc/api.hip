@@ -130,6 +130,8 @@ struct Built {
     bool permuted = false;
     // x staged in LDS by the ELL / tail kernels
     bool window = false;
+    // ELL-R / SELL-64 / ELL part: col read without caching (else cached)
+    bool col_nt = true;
     double band_fraction = 0;
 
     size_t bytes() const {
@@ -907,7 +909,7 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
         case SPMV_HEC: {
             EllView a{(int)h->n, std::max<int64_t>(b.ell_bh, 1), b.ell_width * b.ell_bh,
                       (int)b.ell_width, b.ell_len.as<int>(), b.ell_perm.as<int>(),
-                      b.ell_col.as<int>(), b.ell_val.p, b.window, b.ell_groups};
+                      b.ell_col.as<int>(), b.ell_val.p, b.window, b.ell_groups, b.col_nt};
             e = launch_ell(a, f64, y, x, alpha, beta, s);
             if (e == hipSuccess && format == SPMV_HEC && b.tail_nnz > 0 && b.tail_vector) {
                 const CsrView t{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
@@ -927,7 +929,7 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
         case SPMV_SELL64: {
             SellView a{(int)h->n, (int)b.nslices, b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
                        b.perm.as<int>(), b.sell_col.as<int>(), b.sell_val.p, (int)b.nchunks,
-                       b.chunks.as<int4>(), b.permuted};
+                       b.chunks.as<int4>(), b.permuted, b.col_nt};
             e = launch_sell(a, f64, y, x, alpha, beta, s);
             break;
         }
@@ -994,8 +996,8 @@ int stage_slots_for(const CsrView& v, bool f64, int sw, hipStream_t s) {
 // streams val past the caches; col too only when that is faster (a col array
 // that fits the last-level cache beside x stays there over repeated applies).
 float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw_hi, int fix_rows,
-                  int fix_stage, void* ys, const void* xs, double beta, VecShape& best,
-                  hipStream_t s) {
+                  int fix_stage, int col_cache, void* ys, const void* xs, double beta,
+                  VecShape& best, hipStream_t s) {
     float best_ms = 1e30f;
     // a group that would loop more than kVecMaxPasses times over the longest
     // row serialises the launch on it: such shapes are not timed (the widest
@@ -1014,12 +1016,13 @@ float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw
                 }, s);
                 if (ms < best_ms) best_ms = ms, best = VecShape{sw, rows, slots, false};
             }
-    if (best.slots > 0) {
+    if (best.slots > 0 && col_cache < 0) {
         const float ms = time_launches([&] {
             return launch_csr(v, best.subwave, 1, best.slots, true, f64, ys, xs, 1.0, beta, s);
         }, s);
         if (ms < best_ms) best_ms = ms, best.col_nt = true;
     }
+    if (col_cache >= 0) best.col_nt = col_cache == 0;
     return best_ms;
 }
 
@@ -1033,7 +1036,7 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     h->subwave = o.subwave ? o.subwave : rule;
     h->csr_rows = o.csr_rows ? o.csr_rows : 1;
     h->csr_stage_slots = 0;
-    h->csr_stage_col_nt = false;
+    h->csr_stage_col_nt = o.col_cache == 0;
     const bool f64 = h->dtype == SPMV_F64;
     const CsrView v{(int)h->n, (int)h->nnz, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
     const bool want_vec = o.csr_kernel != SPMV_CSR_BALANCED;
@@ -1063,8 +1066,8 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     if (want_vec) {
         VecShape best;
         best_ms = tune_vector(v, f64, h->max_len, o.subwave ? o.subwave : (h->max_len <= 2 ? 1 : 2),
-                              o.subwave ? o.subwave : 64, o.csr_rows, o.csr_stage, ys.p, xs.p, 0.0,
-                              best, s);
+                              o.subwave ? o.subwave : 64, o.csr_rows, o.csr_stage, o.col_cache, ys.p,
+                              xs.p, 0.0, best, s);
         h->subwave = best.subwave, h->csr_rows = best.rows;
         h->csr_stage_slots = best.slots, h->csr_stage_col_nt = best.col_nt;
     }
@@ -1085,7 +1088,7 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
 // spmv_csr_kernel) fixes the choice; SPMV_CSR_AUTO keeps the faster on the
 // device, the balanced one only when clearly faster, and keeps the balanced
 // one with the LDS window (the vector kernel has no window).
-void tune_hec_tail(const spmv_handle* h, int kernel, Built& b, hipStream_t s) {
+void tune_hec_tail(const spmv_handle* h, int kernel, int col_cache, Built& b, hipStream_t s) {
     b.tail_vector = false;
     if (b.tail_nnz == 0 || kernel == SPMV_CSR_BALANCED ||
         (kernel == SPMV_CSR_AUTO && b.window))
@@ -1104,7 +1107,8 @@ void tune_hec_tail(const spmv_handle* h, int kernel, Built& b, hipStream_t s) {
                     b.tail_col.as<int>(), b.tail_val.p, b.tail_rows.as<int>()};
     VecShape best;
     const float vec_ms =
-        tune_vector(v, f64, h->max_len - b.ell_width, 1, 64, 0, -1, ys.p, xs.p, 1.0, best, s);
+        tune_vector(v, f64, h->max_len - b.ell_width, 1, 64, 0, -1, col_cache, ys.p, xs.p, 1.0,
+                    best, s);
     sync(s);
     if (!(bal_ms < kPreferMargin * vec_ms)) {
         b.tail_vector = true;
@@ -1168,6 +1172,23 @@ int run_guarded(const std::function<void()>& body) {
 
 bool valid_format(int f) { return f >= SPMV_CSR && f <= SPMV_HEC; }
 
+// Column-index cache policy of the ELL-family kernels: streamed past the
+// caches (the default) or cached, whichever applies faster.  Cached indices
+// pay when they fit the last-level cache beside x over repeated applies.
+void choose_col_policy(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s) {
+    b.col_nt = opt != 1;
+    if (opt >= 0 || h->n == 0 || h->nnz == 0) return;
+    DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
+    hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
+    const float t_nt =
+        time_launches([&] { return launch_built(h, b, format, ys.p, xs.p, 1.0, 0.0, s); }, s);
+    b.col_nt = false;
+    const float t_c =
+        time_launches([&] { return launch_built(h, b, format, ys.p, xs.p, 1.0, 0.0, s); }, s);
+    sync(s);
+    b.col_nt = !(t_c < t_nt);
+}
+
 // HYB/HEC at ELL width `width` (as choose_width takes it): the split, the
 // window and group choices, and HEC's tail kernel
 void build_split_tuned(spmv_handle* h, int format, const spmv_convert_opts& o, int width,
@@ -1179,7 +1200,8 @@ void build_split_tuned(spmv_handle* h, int format, const spmv_convert_opts& o, i
         build_split<float>(h, format, width, o.sort_window, b, s);
     decide_window(h, format, o.x_window, b, s);
     choose_groups(h, o.ell_groups, b);
-    if (format == SPMV_HEC) tune_hec_tail(h, o.csr_kernel, b, s);
+    if (format == SPMV_HEC) tune_hec_tail(h, o.csr_kernel, o.col_cache, b, s);
+    choose_col_policy(h, format, o.col_cache, b, s);
 }
 
 // Build `format` (options already validated) and make it the active format.
@@ -1210,12 +1232,14 @@ void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
             build_ell_part<float>(h, W, 0, 0, b, s);
         decide_window(h, format, o.x_window, b, s);
         choose_groups(h, o.ell_groups, b);
+        choose_col_policy(h, format, o.col_cache, b, s);
         sync(s);
     } else if (format == SPMV_SELL64) {
         if (f64)
             build_sell<double>(h, o.sort_window, o.permuted_basis != 0, b, s);
         else
             build_sell<float>(h, o.sort_window, o.permuted_basis != 0, b, s);
+        choose_col_policy(h, format, o.col_cache, b, s);
     } else {
         build_split_tuned(h, format, o, o.ell_width, b, s);
         if (o.ell_width < 0 && h->n > 0) {
@@ -1544,7 +1568,7 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
         if (!h) fail(SPMV_ERR_STATE, "null handle");
         if (!valid_format(format) && format != SPMV_AUTO)
             fail(SPMV_ERR_INVALID_ARG, "unknown format %d", format);
-        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0, 0, 0, -1};
+        spmv_convert_opts o{-1, 0, -1, 0, SPMV_CSR_AUTO, -1, 0, 0, 0, -1, -1};
         if (opts) o = *opts;
         if (o.ell_groups != 0 && o.ell_groups != 1 && o.ell_groups != 4 && o.ell_groups != 16)
             fail(SPMV_ERR_INVALID_ARG, "ell_groups must be 0, 1, 4 or 16 (got %d)", o.ell_groups);
@@ -1573,6 +1597,8 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
                  o.subwave);
         if (o.csr_kernel < SPMV_CSR_AUTO || o.csr_kernel > SPMV_CSR_BALANCED)
             fail(SPMV_ERR_INVALID_ARG, "csr_kernel must be 0, 1 or 2 (got %d)", o.csr_kernel);
+        if (o.col_cache < -1 || o.col_cache > 1)
+            fail(SPMV_ERR_INVALID_ARG, "col_cache must be -1, 0 or 1 (got %d)", o.col_cache);
         if (o.csr_stage < -1 || o.csr_stage > 1)
             fail(SPMV_ERR_INVALID_ARG, "csr_stage must be -1, 0 or 1 (got %d)", o.csr_stage);
         if (o.csr_stage == 1 &&
@@ -1726,6 +1752,10 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.tail_subwave = tv ? b.tail_vec.subwave : 0;
     i.tail_rows = tv ? b.tail_vec.rows : 0;
     i.tail_stage_slots = tv ? b.tail_vec.slots : 0;
+    if (h->format == SPMV_CSR)
+        i.col_cached = !b.csr_balanced && h->csr_stage_slots > 0 && !h->csr_stage_col_nt;
+    else
+        i.col_cached = !b.col_nt;
     i.csr_kernel = h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED : SPMV_CSR_VECTOR;
     i.sort_window = b.sort_window;
     i.ell_groups = (h->format == SPMV_ELLR || h->format == SPMV_HYB || h->format == SPMV_HEC)

@@ -28,6 +28,17 @@ __device__ __forceinline__ T ld_nt(const T* p) {
     return __builtin_nontemporal_load(p);
 }
 
+// Column indices: streamed like the values (kNT), or kept in the caches --
+// when the index array fits the last-level cache beside x, it stays there
+// over repeated applies (the format times both and keeps the faster).
+template <bool kNT>
+__device__ __forceinline__ int ld_col(const int* p) {
+    if constexpr (kNT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
 // ---------------------------------------------------------------------------
 // cross-lane moves.  DPP controls (gfx9 encoding):
 //   quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2)

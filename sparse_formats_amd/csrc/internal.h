@@ -82,6 +82,7 @@ struct EllView {
     const void* val;
     bool window;      // stage x in LDS (banded matrices)
     int groups;       // wave groups per 64-row tile (1, 4 or 16; without the window)
+    bool col_nt = true;  // col read without caching (else kept in the caches)
 };
 
 struct SellView {
@@ -95,6 +96,7 @@ struct SellView {
     int nchunks;               // column chunks of split slices
     const int4* chunks;        // (slice, j0, j1, 0)
     bool permuted;             // y in sorted order (permuted basis)
+    bool col_nt = true;        // col read without caching (else kept in the caches)
 };
 
 struct TailView {

@@ -22,7 +22,7 @@ namespace spmv {
 // ---------------------------------------------------------------------------
 // ELLPACK-R (also the ELL part of HYB / HEC)
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool kColNT>
 __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
                                              const int* __restrict__ len,
                                              const int* __restrict__ perm,
@@ -41,8 +41,8 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
         const int64_t o = (int64_t)j * bh;
         const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + bh);
         const T v2 = ld_nt(v + o + 2 * bh), v3 = ld_nt(v + o + 3 * bh);
-        const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + bh);
-        const int c2 = ld_nt(c + o + 2 * bh), c3 = ld_nt(c + o + 3 * bh);
+        const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + bh);
+        const int c2 = ld_col<kColNT>(c + o + 2 * bh), c3 = ld_col<kColNT>(c + o + 3 * bh);
         s0 = fma(v0, x[c0], s0);
         s1 = fma(v1, x[c1], s1);
         s2 = fma(v2, x[c2], s2);
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
     }
     for (; j < L; ++j) {
         const int64_t o = (int64_t)j * bh;
-        s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
+        s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
     }
     const int64_t row = perm ? perm[i] : i;  // positions < n hold rows < n
     y[row] = axpby((s0 + s1) + (s2 + s3), alpha, beta, y + row);
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
 // CU: each thread keeps 16 entries of each of its rows in flight per round
 // (values, columns, then the x reads), and the elements entering the window
 // for the next tile are loaded while the current tile computes.
-template <typename T>
+template <typename T, bool kColNT>
 __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bstride,
                                                   const int* __restrict__ len,
                                                   const int* __restrict__ perm,
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
                     const int64_t jj = j + u;
                     if (j + u < L[h]) {
                         vv[h][u] = ld_nt(val + base + jj * bh);
-                        cc[h][u] = ld_nt(col + base + jj * bh);
+                        cc[h][u] = ld_col<kColNT>(col + base + jj * bh);
                     } else {
                         vv[h][u] = T(0);
                         cc[h][u] = 0;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
 // and gives a row several groups to raise the parallelism of matrices with
 // few, long rows.  Wave g takes the columns g, g + G, g + 2G, ... of its
 // lanes' rows (four in flight); the G partial sums of a row meet in LDS.
-template <typename T, int G>
+template <typename T, int G, bool kColNT>
 __global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bstride,
                                                    const int* __restrict__ len,
                                                    const int* __restrict__ perm,
@@ -187,8 +187,8 @@ __global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bs
             const int64_t o = (int64_t)j * bh, d = (int64_t)G * bh;
             const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + d);
             const T v2 = ld_nt(v + o + 2 * d), v3 = ld_nt(v + o + 3 * d);
-            const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + d);
-            const int c2 = ld_nt(c + o + 2 * d), c3 = ld_nt(c + o + 3 * d);
+            const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + d);
+            const int c2 = ld_col<kColNT>(c + o + 2 * d), c3 = ld_col<kColNT>(c + o + 3 * d);
             s0 = fma(v0, x[c0], s0);
             s1 = fma(v1, x[c1], s1);
             s2 = fma(v2, x[c2], s2);
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bs
         }
         for (; j < L; j += G) {
             const int64_t o = (int64_t)j * bh;
-            s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
+            s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
         }
     }
     part[g][lane] = (s0 + s1) + (s2 + s3);
@@ -210,53 +210,50 @@ __global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bs
     }
 }
 
-template <typename T>
+template <typename T, bool kColNT>
 static hipError_t run_ell_mg(const EllView& a, void* y, const void* x, double alpha,
                              double beta, hipStream_t stream) {
     const int64_t blocks = ((int64_t)a.n + kWave - 1) / kWave;
     if (a.groups == 16)
-        hipLaunchKernelGGL((k_ell_mg<T, 16>), dim3((unsigned)blocks), dim3(64 * 16), 0, stream,
-                           a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
+        hipLaunchKernelGGL((k_ell_mg<T, 16, kColNT>), dim3((unsigned)blocks), dim3(64 * 16), 0,
+                           stream, a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
                            (const T*)x, (T*)y, (T)alpha, (T)beta);
     else if (a.groups == 4)
-        hipLaunchKernelGGL((k_ell_mg<T, 4>), dim3((unsigned)blocks), dim3(64 * 4), 0, stream,
-                           a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
+        hipLaunchKernelGGL((k_ell_mg<T, 4, kColNT>), dim3((unsigned)blocks), dim3(64 * 4), 0,
+                           stream, a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
                            (const T*)x, (T*)y, (T)alpha, (T)beta);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t run_ell_win(const EllView& a, void* y, const void* x, double alpha,
-                              double beta, hipStream_t stream) {
-    const int64_t ntiles = ((int64_t)a.n + kEllWinTile - 1) / kEllWinTile;
-    const int64_t g = std::min<int64_t>(ntiles, kWinGroups);
-    hipLaunchKernelGGL(k_ell_win<T>, dim3((unsigned)g), dim3(1024), 0, stream, a.n, a.bh,
+template <typename T, bool kColNT>
+static hipError_t run_ell(const EllView& a, void* y, const void* x, double alpha, double beta,
+                          hipStream_t stream) {
+    if (a.window) {
+        const int64_t ntiles = ((int64_t)a.n + kEllWinTile - 1) / kEllWinTile;
+        const int64_t g = std::min<int64_t>(ntiles, kWinGroups);
+        hipLaunchKernelGGL((k_ell_win<T, kColNT>), dim3((unsigned)g), dim3(1024), 0, stream, a.n,
+                           a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val, (const T*)x,
+                           (T*)y, (T)alpha, (T)beta, ntiles);
+        return hipGetLastError();
+    }
+    if (a.groups > 1) return run_ell_mg<T, kColNT>(a, y, x, alpha, beta, stream);
+    const int64_t blocks = ((int64_t)a.n + 255) / 256;
+    hipLaunchKernelGGL((k_ell<T, kColNT>), dim3((unsigned)blocks), dim3(256), 0, stream, a.n, a.bh,
                        a.bstride, a.len, a.perm, a.col, (const T*)a.val, (const T*)x, (T*)y,
-                       (T)alpha, (T)beta, ntiles);
+                       (T)alpha, (T)beta);
     return hipGetLastError();
 }
 
 hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double alpha,
                       double beta, hipStream_t stream) {
-    const int64_t blocks = ((int64_t)a.n + 255) / 256;
-    if (blocks == 0) return hipSuccess;
-    if (a.window)
-        return f64 ? run_ell_win<double>(a, y, x, alpha, beta, stream)
-                   : run_ell_win<float>(a, y, x, alpha, beta, stream);
-    if (a.groups > 1)
-        return f64 ? run_ell_mg<double>(a, y, x, alpha, beta, stream)
-                   : run_ell_mg<float>(a, y, x, alpha, beta, stream);
+    if (a.n <= 0) return hipSuccess;
     if (f64)
-        hipLaunchKernelGGL(k_ell<double>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
-                           a.bh, a.bstride, a.len, a.perm, a.col, (const double*)a.val,
-                           (const double*)x, (double*)y, alpha, beta);
-    else
-        hipLaunchKernelGGL(k_ell<float>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
-                           a.bh, a.bstride, a.len, a.perm, a.col, (const float*)a.val,
-                           (const float*)x, (float*)y, (float)alpha, (float)beta);
-    return hipGetLastError();
+        return a.col_nt ? run_ell<double, true>(a, y, x, alpha, beta, stream)
+                        : run_ell<double, false>(a, y, x, alpha, beta, stream);
+    return a.col_nt ? run_ell<float, true>(a, y, x, alpha, beta, stream)
+                    : run_ell<float, false>(a, y, x, alpha, beta, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -265,7 +262,7 @@ hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double
 // kSellSplitWidth only get beta * y here; their columns are added by
 // k_sell_chunks.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool kColNT>
 __global__ __launch_bounds__(256) void k_sell(int n, int nslices,
                                               const int64_t* __restrict__ slice_ptr,
                                               const int* __restrict__ len,
@@ -289,8 +286,8 @@ __global__ __launch_bounds__(256) void k_sell(int n, int nslices,
         const int64_t o = (int64_t)j * 64;
         const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + 64);
         const T v2 = ld_nt(v + o + 128), v3 = ld_nt(v + o + 192);
-        const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + 64);
-        const int c2 = ld_nt(c + o + 128), c3 = ld_nt(c + o + 192);
+        const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + 64);
+        const int c2 = ld_col<kColNT>(c + o + 128), c3 = ld_col<kColNT>(c + o + 192);
         s0 = fma(v0, x[c0], s0);
         s1 = fma(v1, x[c1], s1);
         s2 = fma(v2, x[c2], s2);
@@ -298,7 +295,7 @@ __global__ __launch_bounds__(256) void k_sell(int n, int nslices,
     }
     for (; j < L; ++j) {
         const int64_t o = (int64_t)j * 64;
-        s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
+        s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
     }
     if (r < n) {
         const int64_t row = permuted ? r : perm[r];
@@ -307,7 +304,7 @@ __global__ __launch_bounds__(256) void k_sell(int n, int nslices,
 }
 
 // one wave per column chunk (slice, j0, j1) of a split slice
-template <typename T>
+template <typename T, bool kColNT>
 __global__ __launch_bounds__(256) void k_sell_chunks(int n, int nchunks,
                                                      const int4* __restrict__ chunks,
                                                      const int64_t* __restrict__ slice_ptr,
@@ -331,8 +328,8 @@ __global__ __launch_bounds__(256) void k_sell_chunks(int n, int nchunks,
         const int64_t o = (int64_t)j * 64;
         const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + 64);
         const T v2 = ld_nt(v + o + 128), v3 = ld_nt(v + o + 192);
-        const int c0 = ld_nt(c + o), c1 = ld_nt(c + o + 64);
-        const int c2 = ld_nt(c + o + 128), c3 = ld_nt(c + o + 192);
+        const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + 64);
+        const int c2 = ld_col<kColNT>(c + o + 128), c3 = ld_col<kColNT>(c + o + 192);
         s0 = fma(v0, x[c0], s0);
         s1 = fma(v1, x[c1], s1);
         s2 = fma(v2, x[c2], s2);
@@ -340,31 +337,34 @@ __global__ __launch_bounds__(256) void k_sell_chunks(int n, int nchunks,
     }
     for (; j < L; ++j) {
         const int64_t o = (int64_t)j * 64;
-        s0 = fma(ld_nt(v + o), x[ld_nt(c + o)], s0);
+        s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
     }
     if (r < n && ch.y < L) atomic_add(y + (permuted ? r : perm[r]), alpha * ((s0 + s1) + (s2 + s3)));
 }
 
-template <typename T>
+template <typename T, bool kColNT>
 static hipError_t run_sell(const SellView& a, void* y, const void* x, double alpha, double beta,
                            hipStream_t stream) {
     const int64_t blocks = ((int64_t)a.nslices + 3) / 4;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sell<T>, dim3((unsigned)blocks), dim3(256), 0, stream, a.n, a.nslices,
-                       a.slice_ptr, a.len, a.perm, a.col, (const T*)a.val, (const T*)x, (T*)y,
-                       (T)alpha, (T)beta, a.permuted);
+    hipLaunchKernelGGL((k_sell<T, kColNT>), dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
+                       a.nslices, a.slice_ptr, a.len, a.perm, a.col, (const T*)a.val,
+                       (const T*)x, (T*)y, (T)alpha, (T)beta, a.permuted);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nchunks == 0) return e;
-    hipLaunchKernelGGL(k_sell_chunks<T>, dim3((unsigned)((a.nchunks + 3) / 4)), dim3(256), 0,
-                       stream, a.n, a.nchunks, a.chunks, a.slice_ptr, a.len, a.perm, a.col,
-                       (const T*)a.val, (const T*)x, (T*)y, (T)alpha, a.permuted);
+    hipLaunchKernelGGL((k_sell_chunks<T, kColNT>), dim3((unsigned)((a.nchunks + 3) / 4)),
+                       dim3(256), 0, stream, a.n, a.nchunks, a.chunks, a.slice_ptr, a.len, a.perm,
+                       a.col, (const T*)a.val, (const T*)x, (T*)y, (T)alpha, a.permuted);
     return hipGetLastError();
 }
 
 hipError_t launch_sell(const SellView& a, bool f64, void* y, const void* x, double alpha,
                        double beta, hipStream_t stream) {
-    return f64 ? run_sell<double>(a, y, x, alpha, beta, stream)
-               : run_sell<float>(a, y, x, alpha, beta, stream);
+    if (f64)
+        return a.col_nt ? run_sell<double, true>(a, y, x, alpha, beta, stream)
+                        : run_sell<double, false>(a, y, x, alpha, beta, stream);
+    return a.col_nt ? run_sell<float, true>(a, y, x, alpha, beta, stream)
+                    : run_sell<float, false>(a, y, x, alpha, beta, stream);
 }
 
 // dst[r] = src[perm[r]] or dst[perm[r]] = src[r] (vectors between the

@@ -154,6 +154,29 @@ def test_hec_tail_kernels(kernel, name, dtype):
     M.close()
 
 
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("fmt,kw", [("ellr", {}), ("ellr", dict(ell_groups=4)),
+                                    ("ellr", dict(x_window=1)), ("sell64", {}),
+                                    ("hyb", dict(x_window=0)), ("hyb", dict(x_window=1)),
+                                    ("hec", dict(csr_kernel="balanced")),
+                                    ("csr", dict(csr_kernel="vector", csr_stage=1))])
+@pytest.mark.parametrize("cache", [0, 1])
+def test_col_cache_policies(fmt, kw, cache, dtype):
+    """Column indices streamed (0) or cached (1): same results, both reported."""
+    a = _banded() if kw.get("x_window") == 1 else MATS["long_spans"]()
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    x_np, y0_np = (v.astype(npdt) for v in vectors(a.n, 91))
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n).convert(fmt, col_cache=cache, **kw)
+    assert M.info()["col_cached"] == cache
+    y = apply(M, torch.from_numpy(x_np).cuda(), torch.from_numpy(y0_np).cuda(), -1.25, 0.5)
+    check(a, x_np, y0_np, -1.25, 0.5, y, dtype, what="col_cache=%d %s %s" % (cache, fmt, kw))
+    with pytest.raises(sf.SpmvError):
+        M.convert(fmt, col_cache=2)
+    M.close()
+
+
 def test_csr_stage_errors():
     a = MATS["c1"]()
     M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
