@@ -44,32 +44,41 @@ struct TailShape {
 };
 
 // E consecutive elements with 16-byte loads (E * sizeof a multiple of 16
-// bytes, p 16-byte aligned)
-template <int E>
+// bytes, p 16-byte aligned).  kNT streams them past the caches: right for
+// the COO passes, whose load instructions read whole lines once; the CSR
+// tails' runs read a line in several instructions, which must find it cached.
+template <bool kNT, typename V>
+__device__ __forceinline__ V load16(const V* p) {
+    if constexpr (kNT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+template <int E, bool kNT>
 __device__ __forceinline__ void load_vec(const double* p, double (&v)[E]) {
 #pragma unroll
     for (int k = 0; k < E / 2; ++k) {
-        const d2_t t = reinterpret_cast<const d2_t*>(p)[k];
+        const d2_t t = load16<kNT>(reinterpret_cast<const d2_t*>(p) + k);
         v[2 * k] = t.x, v[2 * k + 1] = t.y;
     }
 }
-template <int E>
+template <int E, bool kNT>
 __device__ __forceinline__ void load_vec(const float* p, float (&v)[E]) {
 #pragma unroll
     for (int k = 0; k < E / 4; ++k) {
-        const f4_t t = reinterpret_cast<const f4_t*>(p)[k];
+        const f4_t t = load16<kNT>(reinterpret_cast<const f4_t*>(p) + k);
         v[4 * k] = t.x, v[4 * k + 1] = t.y, v[4 * k + 2] = t.z, v[4 * k + 3] = t.w;
     }
 }
-template <int E>
+template <int E, bool kNT>
 __device__ __forceinline__ void load_vec(const int* p, int (&v)[E]) {
     if constexpr (E == 2) {
-        const i2_t t = *reinterpret_cast<const i2_t*>(p);
+        const i2_t t = load16<kNT>(reinterpret_cast<const i2_t*>(p));
         v[0] = t.x, v[1] = t.y;
     } else {
 #pragma unroll
         for (int k = 0; k < E / 4; ++k) {
-            const i4_t t = reinterpret_cast<const i4_t*>(p)[k];
+            const i4_t t = load16<kNT>(reinterpret_cast<const i4_t*>(p) + k);
             v[4 * k] = t.x, v[4 * k + 1] = t.y, v[4 * k + 2] = t.z, v[4 * k + 3] = t.w;
         }
     }
@@ -116,9 +125,9 @@ __device__ __forceinline__ void tail_fetch(int64_t w, int lane, int64_t nnz,
         const int64_t e0 = pass_entry(w, p, lane, E);
         R.cnt[p] = e0 < nnz ? (int)min<int64_t>(E, nnz - e0) : 0;
         if (R.cnt[p] == E) {
-            load_vec<E>(val + e0, R.v[p]);
-            load_vec<E>(col + e0, R.c[p]);
-            if constexpr (kCoo) load_vec<E>(trow + e0, R.r[p]);
+            load_vec<E, kCoo>(val + e0, R.v[p]);
+            load_vec<E, kCoo>(col + e0, R.c[p]);
+            if constexpr (kCoo) load_vec<E, true>(trow + e0, R.r[p]);
         } else {
 #pragma unroll
             for (int k = 0; k < E; ++k) {
