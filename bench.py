@@ -194,6 +194,8 @@ def main(argv=None):
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--csr-kernel", default="auto", choices=["auto", "vector", "balanced"],
                     help="CSR apply kernel (default: timed at conversion)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the whole steps eagerly instead of replaying a HIP graph of one")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: this SpMV path runs on a single MI355X and has no "
@@ -265,6 +267,34 @@ def main(argv=None):
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    step_timing = "eager"
+    if not args.no_graph:
+        # the step rate without host launch gaps: the same applies, captured
+        # once as a HIP graph of one step and replayed
+        cur = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            for f in fmts:
+                mats[f].apply(y, x)
+        cur.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for f in fmts:
+                mats[f].apply(y, x)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        eager_ms = total_ms
+        start.record()
+        for _ in range(args.steps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+        step_timing = "hip_graph (eager steps: %.5f ms)" % (eager_ms / args.steps)
+        del graph
 
     per = {}
     mats_info = {f: mats[f].info() for f in fmts}
@@ -307,6 +337,7 @@ def main(argv=None):
         "config": {"workload": args.workload, "n": a.n, "nnz": a.nnz,
                    "formats": fmts, "refused": refused,
                    "step": "one apply y = A x in each listed format",
+                   "step_timing": step_timing,
                    "value": "2 nnz x formats per step / step time"},
         "best_format": {"format": best, "gflops": per[best]["gflops"],
                         "eff_gbs": per[best]["eff_gbs"],

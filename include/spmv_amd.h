@@ -183,7 +183,8 @@ typedef struct {
     /* Cache policy of the column indices (ELL-R, SELL-64, the ELL part of
      * HYB/HEC, the staged CSR copy): 0 streams them past the caches like the
      * values, 1 keeps them in the caches (when they fit the last-level cache
-     * beside x they stay there over repeated applies), -1 times both. */
+     * beside x they stay there over repeated applies), -1 times both and
+     * keeps them cached only when that is at least 5 % faster. */
     int32_t col_cache;
 } spmv_convert_opts;
 

@@ -124,7 +124,8 @@ def main():
     for r in timed:
         per.setdefault(short(r["Kernel_Name"])[1], []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines += ["", "Applies after the stream copy (2 warm-up + 10 timed steps), per kernel:", "",
+    lines += ["", "Applies after the stream copy (the warm-up and timed steps, eager and replayed "
+              "from the step's HIP graph), per kernel:", "",
               "| kernel | dispatches | mean us | median us |", "|---|---|---|---|"]
     for k, v in per.items():
         lines.append("| %s | %d | %.1f | %.1f |" % (k, len(v), statistics.mean(v),
@@ -135,8 +136,8 @@ def main():
         bench_line = json.loads(js[-1])
         formats = bench_line["config"]["formats"]
         applies = per_format_applies(timed, formats)
-        lines += ["", "One apply per format (the kernels of each format in the 2 warm-up + 10 "
-                  "timed steps, summed per apply), beside the bench's own median from HIP "
+        lines += ["", "One apply per format (the kernels of each format in the warm-up and timed "
+                  "steps, summed per apply), beside the bench's own median from HIP "
                   "events in the same run:", "",
                   "| format | kernels | applies | mean us | median us | bench median us |",
                   "|---|---|---|---|---|---|"]

@@ -1020,7 +1020,8 @@ float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw
         const float ms = time_launches([&] {
             return launch_csr(v, best.subwave, 1, best.slots, true, f64, ys, xs, 1.0, beta, s);
         }, s);
-        if (ms < best_ms) best_ms = ms, best.col_nt = true;
+        // streamed unless keeping col cached is clearly faster
+        if (!(best_ms < kPreferMargin * ms)) best_ms = std::min(best_ms, ms), best.col_nt = true;
     }
     if (col_cache >= 0) best.col_nt = col_cache == 0;
     return best_ms;
@@ -1186,7 +1187,9 @@ void choose_col_policy(const spmv_handle* h, int format, int opt, Built& b, hipS
     const float t_c =
         time_launches([&] { return launch_built(h, b, format, ys.p, xs.p, 1.0, 0.0, s); }, s);
     sync(s);
-    b.col_nt = !(t_c < t_nt);
+    // cached only when clearly faster: over interleaved work (other matrices
+    // between two applies) the cached indices do not survive anyway
+    b.col_nt = !(t_c < kPreferMargin * t_nt);
 }
 
 // HYB/HEC at ELL width `width` (as choose_width takes it): the split, the

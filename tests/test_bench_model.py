@@ -84,6 +84,7 @@ def test_bench_json_line():
         assert k in out, k
     assert out["config"]["workload"] == "c1_laplace2d_64"
     assert set(out["formats"]) == {"csr", "ellr", "sell64", "hyb", "hec"}
+    assert out["config"]["step_timing"].startswith("hip_graph")
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in out["roofline"]
 
