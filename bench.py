@@ -138,7 +138,7 @@ def cpu_baseline(a, x, target_s: float = 10.0):
         oracle.spmv(a, x, nthreads=cores)
         reps += 1
         t = time.perf_counter() - t0
-        if t >= target_s or reps >= 200:
+        if t >= target_s or reps >= 2000:
             break
     gflops = 2.0 * a.nnz * reps / t / 1e9
     return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
