@@ -28,10 +28,12 @@ namespace spmv {
 // cache lines of val/col and, for banded matrices, entry u of neighbouring
 // rows usually lies on the same diagonal, so their x reads share lines too.
 // The first pass reads with clamped indices and masks the products, so it
-// has no per-entry branches.
+// has no per-entry branches.  Pairs of lanes take 12 entries each per pass
+// (24 per row: the rows of about 15-22 entries that make such a shape the
+// fastest then finish in one pass); other groups cover 16 entries per pass.
 template <int S, int R>
 struct CsrFirstPass {
-    static constexpr int a = 16 / S, b = 16 / R;
+    static constexpr int a = (S == 2 ? 24 : 16) / S, b = 16 / R;
     static constexpr int value = (a < b ? a : b) > 2 ? (a < b ? a : b) : 2;
 };
 
