@@ -30,7 +30,11 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names a library built from a modified copy of oracle.c: the
+# tests that check that the pins catch planted mistakes run the pin suite
+# against it.  It is loaded as it is, never rebuilt.
+_PLANTED = os.environ.get("ORACLE_LIB")
+_SO = _PLANTED or os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
 _lib = None
 
@@ -40,6 +44,8 @@ TOL_F32 = 1e-5
 
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (no fast-math, no FMA contraction)."""
+    if _PLANTED:
+        return _SO
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
         tmp = _SO + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",

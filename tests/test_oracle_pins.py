@@ -86,6 +86,22 @@ def test_alpha_beta_exact():
                 Fraction(1, 10 ** 300), (alpha, beta, i)
 
 
+def test_scale_definition_hand_example():
+    """The tolerance scale is |alpha| * sum |a x| + |beta * y0| (hand-computed):
+    row [1, -2, 4] against x = [1, 1, 0.5] has sum |a x| = 1 + 2 + 2 = 5 and
+    sum a x = 1; alpha = -3, beta = 0.5, y0 = -8 give y = -3 - 4 = -7 and a
+    scale of 15 + 4 = 19."""
+    a = CSR(3, np.array([0, 3, 3, 3], np.int64), np.array([0, 1, 2], np.int32),
+            np.array([1.0, -2.0, 4.0]))
+    x = np.array([1.0, 1.0, 0.5])
+    y0 = np.array([-8.0, 6.0, 0.0])
+    y, sc = oracle.spmv(a, x, y0, -3.0, 0.5)
+    assert y.tolist() == [-7.0, 3.0, 0.0]
+    assert sc.tolist() == [19.0, 3.0, 0.0]
+    y, sc = oracle.spmv(a, x, None, 2.0, 0.0)   # beta = 0: y0 is not read
+    assert y.tolist() == [2.0, 0.0, 0.0] and sc.tolist() == [10.0, 0.0, 0.0]
+
+
 @pytest.mark.parametrize("kw", [
     dict(n=150, seed=11, density=0.05),
     dict(n=200, seed=12, density=0.03, empty_frac=0.3, unsorted=True),
