@@ -486,15 +486,16 @@ __global__ void k_tail_fill(int64_t n, int K, const int* __restrict__ rowptr,
                             const int* __restrict__ col, const V* __restrict__ val,
                             const int* __restrict__ tptr, int* __restrict__ trow,
                             int* __restrict__ tcol, V* __restrict__ tval) {
-    const int64_t i = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (i >= n) return;
     const int lane = threadIdx.x & 63;
-    const int t0 = tptr[i], t1 = tptr[i + 1];
-    const int k0 = rowptr[i] + K;
-    for (int t = t0 + lane; t < t1; t += 64) {
-        tcol[t] = col[k0 + (t - t0)];
-        tval[t] = val[k0 + (t - t0)];
-        if (trow) trow[t] = (int)i;
+    for (int64_t i = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); i < n;
+         i += (int64_t)gridDim.x * (blockDim.x >> 6)) {  // one wave per row
+        const int t0 = tptr[i], t1 = tptr[i + 1];
+        const int k0 = rowptr[i] + K;
+        for (int t = t0 + lane; t < t1; t += 64) {
+            tcol[t] = col[k0 + (t - t0)];
+            tval[t] = val[k0 + (t - t0)];
+            if (trow) trow[t] = (int)i;
+        }
     }
 }
 
@@ -813,7 +814,7 @@ void build_split(const spmv_handle* h, int format, int requested, int sort_windo
     hip_check(hipMemsetAsync((char*)b.tail_val.p + (size_t)tail * sizeof(V), 0, 16, s),
               "hipMemsetAsync");
     if (tail > 0) {
-        hipLaunchKernelGGL(k_tail_fill<V>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, n,
+        hipLaunchKernelGGL(k_tail_fill<V>, dim3(grid_for(n, 4)), dim3(256), 0, s, n,
                            (int)K, h->rowptr.as<int>(), h->col.as<int>(), h->val.as<V>(),
                            b.tail_ptr.as<int>(), format == SPMV_HYB ? b.tail_row.as<int>() : nullptr,
                            b.tail_col.as<int>(), b.tail_val.as<V>());

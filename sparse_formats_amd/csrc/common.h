@@ -8,6 +8,10 @@
 namespace spmv {
 
 constexpr int kWave = 64;
+// A dispatch covers fewer than 2^32 work-items; launches of kernels whose
+// grids grow with the row count are split into pieces of at most this many
+// work-items (each piece passes its first tile).
+constexpr int64_t kMaxLaunchItems = int64_t(1) << 31;
 // cache-policy bits of a memory instruction on gfx950: nontemporal
 constexpr int kCachePolicyNT = 2;
 

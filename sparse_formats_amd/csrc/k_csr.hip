@@ -43,10 +43,10 @@ __global__ __launch_bounds__(256) void k_csr_vector(int n, const int* __restrict
                                                     const T* __restrict__ val,
                                                     const T* __restrict__ x, T* __restrict__ y,
                                                     const int* __restrict__ row_map, T alpha,
-                                                    T beta) {
+                                                    T beta, int64_t tile0) {
     constexpr int kGroups = kWave / S;  // groups per wave
     constexpr int U = CsrFirstPass<S, R>::value;
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t tile = tile0 + xcd_tile(blockIdx.x, gridDim.x);
     const int64_t wave = tile * 4 + threadIdx.x / kWave;
     const int64_t base = wave * (kGroups * R) + (threadIdx.x % kWave) / S;
     const int sub = threadIdx.x & (S - 1);
@@ -163,13 +163,13 @@ __global__ __launch_bounds__(256) void k_csr_staged(int n, const int* __restrict
                                                     const T* __restrict__ val,
                                                     const T* __restrict__ x, T* __restrict__ y,
                                                     const int* __restrict__ row_map, T alpha,
-                                                    T beta, int slots, int col_nt) {
+                                                    T beta, int slots, int col_nt, int64_t tile0) {
     using St = CsrStage<T>;
     constexpr int V = St::V;
     constexpr int U = CsrFirstPass<S, 1>::value;
     extern __shared__ __align__(16) char s_stage[];
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int64_t base = (xcd_tile(blockIdx.x, gridDim.x) * 4 + w) * (kWave / S);
+    const int64_t base = ((tile0 + xcd_tile(blockIdx.x, gridDim.x)) * 4 + w) * (kWave / S);
     if (base >= n) return;  // whole waves leave together
     const int sub = lane & (S - 1);
     const int64_t row = base + lane / S;
@@ -231,9 +231,12 @@ static hipError_t run_staged(const CsrView& a, int slots, bool col_nt, void* y, 
     if (blocks == 0) return hipSuccess;
     const size_t lds = 4 * (size_t)CsrStage<T>::wave_bytes(slots);
     if (slots < 1 || lds > kCsrStageLds) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_csr_staged<T, S>), dim3((unsigned)blocks), dim3(256), lds, stream, a.n,
-                       a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, a.row_map, (T)alpha,
-                       (T)beta, slots, col_nt ? 1 : 0);
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxLaunchItems / 256) {
+        const int64_t nb = std::min<int64_t>(blocks - b0, kMaxLaunchItems / 256);
+        hipLaunchKernelGGL((k_csr_staged<T, S>), dim3((unsigned)nb), dim3(256), lds, stream, a.n,
+                           a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, a.row_map,
+                           (T)alpha, (T)beta, slots, col_nt ? 1 : 0, b0);
+    }
     return hipGetLastError();
 }
 
@@ -243,10 +246,12 @@ static hipError_t run(const CsrView& a, void* y, const void* x, double alpha, do
     constexpr int kRowsPerBlock = 256 / S * R;  // 4 waves of 64 / S groups of R rows
     const int64_t blocks = ((int64_t)a.n + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_csr_vector<T, S, R>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       a.n, a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, a.row_map,
-                       (T)alpha,
-                       (T)beta);
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxLaunchItems / 256) {
+        const int64_t nb = std::min<int64_t>(blocks - b0, kMaxLaunchItems / 256);
+        hipLaunchKernelGGL((k_csr_vector<T, S, R>), dim3((unsigned)nb), dim3(256), 0, stream,
+                           a.n, a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, a.row_map,
+                           (T)alpha, (T)beta, b0);
+    }
     return hipGetLastError();
 }
 

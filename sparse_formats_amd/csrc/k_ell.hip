@@ -172,10 +172,10 @@ __global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bs
                                                    const int* __restrict__ col,
                                                    const T* __restrict__ val,
                                                    const T* __restrict__ x, T* __restrict__ y,
-                                                   T alpha, T beta) {
+                                                   T alpha, T beta, int64_t tile0) {
     __shared__ T part[G][kWave];
     const int lane = threadIdx.x & (kWave - 1), g = threadIdx.x / kWave;
-    const int64_t i = xcd_tile(blockIdx.x, gridDim.x) * kWave + lane;
+    const int64_t i = (tile0 + xcd_tile(blockIdx.x, gridDim.x)) * kWave + lane;
     T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
     if (i < n) {
         const int L = len[i];
@@ -214,16 +214,19 @@ template <typename T, bool kColNT>
 static hipError_t run_ell_mg(const EllView& a, void* y, const void* x, double alpha,
                              double beta, hipStream_t stream) {
     const int64_t blocks = ((int64_t)a.n + kWave - 1) / kWave;
-    if (a.groups == 16)
-        hipLaunchKernelGGL((k_ell_mg<T, 16, kColNT>), dim3((unsigned)blocks), dim3(64 * 16), 0,
-                           stream, a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
-                           (const T*)x, (T*)y, (T)alpha, (T)beta);
-    else if (a.groups == 4)
-        hipLaunchKernelGGL((k_ell_mg<T, 4, kColNT>), dim3((unsigned)blocks), dim3(64 * 4), 0,
-                           stream, a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
-                           (const T*)x, (T*)y, (T)alpha, (T)beta);
-    else
-        return hipErrorInvalidValue;
+    if (a.groups != 16 && a.groups != 4) return hipErrorInvalidValue;
+    const int64_t per = kMaxLaunchItems / (64 * a.groups);  // blocks per launch
+    for (int64_t b0 = 0; b0 < blocks; b0 += per) {
+        const int64_t nb = std::min<int64_t>(blocks - b0, per);
+        if (a.groups == 16)
+            hipLaunchKernelGGL((k_ell_mg<T, 16, kColNT>), dim3((unsigned)nb), dim3(64 * 16), 0,
+                               stream, a.n, a.bh, a.bstride, a.len, a.perm, a.col,
+                               (const T*)a.val, (const T*)x, (T*)y, (T)alpha, (T)beta, b0);
+        else
+            hipLaunchKernelGGL((k_ell_mg<T, 4, kColNT>), dim3((unsigned)nb), dim3(64 * 4), 0,
+                               stream, a.n, a.bh, a.bstride, a.len, a.perm, a.col,
+                               (const T*)a.val, (const T*)x, (T*)y, (T)alpha, (T)beta, b0);
+    }
     return hipGetLastError();
 }
 

@@ -1,0 +1,90 @@
+"""Row counts large enough that the grids of the per-row kernels would pass
+HIP's 2^32 work-item limit (a group of S lanes per row, G wave groups per
+64-row tile): launches are split, and every format still matches the oracle.
+
+The matrix has n = 300,000,000 rows, at most three entries in a row, and its
+entries in a few hundred rows spread over the whole range (columns up to
+n - 1).  It is built from COO triples on the device; x is drawn on the device
+and only the entries the matrix reads are copied back, so the oracle runs on
+the touched rows alone (a compact CSR over the columns used) and every other
+row must come out as exactly beta * y0."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gen import CSR
+
+from gpu_util import TOL
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import sparse_formats_amd as sf
+
+N = 300_000_000
+
+
+def _triples(seed=101):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([
+        [0, 1, 2, 63, 64, 65, N // 2, N - 65, N - 64, N - 2, N - 1],
+        rng.integers(0, N, 400)])).astype(np.int64)
+    lens = rng.integers(1, 4, rows.size)
+    r = np.repeat(rows, lens)
+    c = rng.integers(0, N, r.size).astype(np.int64)
+    c[::7] = N - 1
+    c[1::11] = 0
+    c[2::13] = r[2::13]                       # some diagonal entries
+    v = rng.standard_normal(r.size)
+    return r, c.astype(np.int32), v
+
+
+@pytest.fixture(scope="module")
+def large():
+    r, c, v = _triples()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    x = torch.rand(N, dtype=torch.float64, device="cuda", generator=g) * 2 - 1
+    M = sf.Matrix.from_coo(torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda(),
+                           torch.from_numpy(v).cuda(), n=N)
+    # compact reference: the touched rows, columns renumbered into x_used
+    used = np.unique(c)
+    x_used = x[torch.from_numpy(used.astype(np.int64)).cuda()].cpu().numpy()
+    order = np.lexsort((np.arange(r.size), r))          # by row, then input order
+    rs, cs, vs = r[order], c[order], v[order]
+    rows, counts = np.unique(rs, return_counts=True)
+    rp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    compact = CSR(rows.size, rp, np.searchsorted(used, cs).astype(np.int32), vs)
+    yield M, x, rows, compact, x_used
+    M.close()
+
+
+def _check(M, x, rows, compact, x_used, what):
+    alpha, beta = 1.5, 0.5
+    y = torch.full((N,), 2.0, dtype=torch.float64, device="cuda")
+    M.apply(y, x, alpha, beta)
+    torch.cuda.synchronize()
+    touched = torch.from_numpy(rows).cuda()
+    got = y[touched].cpu().numpy()
+    ref, scale = oracle.spmv(compact, x_used, np.full(rows.size, 2.0), alpha, beta)
+    ok, worst, k = oracle.check(got, ref, scale, TOL[torch.float64])
+    assert ok, "%s: worst %.3g at row %d" % (what, worst, rows[k])
+    y[touched] = 1.0
+    assert int((y != 1.0).sum()) == 0, what   # untouched rows: beta * y0 = 1 exactly
+
+
+@pytest.mark.parametrize("fmt,kw", [
+    ("csr", dict(csr_kernel="vector", subwave=64, csr_rows=1, csr_stage=0)),
+    ("csr", dict(csr_kernel="vector", subwave=16, csr_rows=1, csr_stage=1)),
+    ("csr", dict(csr_kernel="balanced")),
+    ("ellr", dict(ell_groups=16)),
+    ("ellr", dict(ell_groups=1)),
+    ("sell64", {}),
+    ("hyb", {}),
+    ("hec", {}),
+])
+def test_many_rows(large, fmt, kw):
+    M, x, rows, compact, x_used = large
+    M.convert(fmt, **kw)
+    _check(M, x, rows, compact, x_used, "%s %s" % (fmt, kw))
