@@ -33,8 +33,9 @@
  *   - Every array argument is a DEVICE pointer (e.g. a torch tensor's
  *     data_ptr()), never a host pointer.  Host pointers appear only in
  *     spmv_export (destination buffer) and in the out-parameters.
- *   - Indices are 0-based.  Rows and columns lie in [0, n).  n < 2^31 and
- *     nnz < 2^31.
+ *   - Indices are 0-based.  Rows and columns lie in [0, n).  n < 2^31 - 1
+ *     and nnz <= 2^31 - 65537 (the kernels' 32-bit entry indices keep that
+ *     headroom).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   - Functions return 0 (SPMV_OK) or a negative spmv_status; nothing is
  *     thrown across the ABI.  After a non-zero return spmv_last_error()
@@ -259,7 +260,8 @@ typedef enum {
  *              SPMV_IN_COO: `rowidx` is the row of every entry, int64[nnz]
  *              (any order; entries are ordered by (row, input position),
  *              which keeps the input order inside a row)
- *   n, nnz     matrix size and stored entries (0 <= n, nnz < 2^31)
+ *   n, nnz     matrix size and stored entries (0 <= n < 2^31 - 1,
+ *              0 <= nnz <= 2^31 - 65537)
  *   rowidx     device pointer as above (may be NULL only if COO and nnz == 0)
  *   col        device int32[nnz], may be NULL when nnz == 0
  *   val        device dtype[nnz], may be NULL when nnz == 0
@@ -359,7 +361,9 @@ int spmv_solve(spmv_t h, void *x, const void *b, const spmv_solve_opts *opts,
                spmv_solve_info *info, void *stream);
 
 /* spmv_destroy -- free every device buffer of the handle (synchronises the
- * device first).  A NULL handle is accepted.  Errors: HIP. */
+ * device first).  A NULL handle is accepted.  The handle is released even
+ * when HIP is returned (an earlier asynchronous error reported by the
+ * synchronisation); it must not be used again.  Errors: HIP. */
 int spmv_destroy(spmv_t h);
 
 /*

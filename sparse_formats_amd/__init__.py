@@ -252,9 +252,10 @@ class Matrix:
         return out
 
     def close(self):
-        if getattr(self, "_h", None):
-            _check(_lib.spmv_destroy(self._h))
-            self._h = None
+        h = getattr(self, "_h", None)
+        if h:
+            self._h = None   # released even when destroy reports an earlier device error
+            _check(_lib.spmv_destroy(h))
 
     def __del__(self):
         try:

@@ -589,6 +589,9 @@ void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, int sigma, B
 // a timed alternative to the simpler kernel (no LDS window, no atomics) is
 // kept only when it is at least this much faster
 constexpr float kPreferMargin = 0.95f;
+// entry indices are 32-bit in the kernels, which step past a row's end by up
+// to a few hundred entries before masking: keep that headroom below 2^31
+constexpr int64_t kMaxNnz = INT32_MAX - 65536;
 
 // automatic format choice: ELL-R is a candidate only while its padded slots
 // are at most this many times the stored entries
@@ -1474,8 +1477,8 @@ int spmv_create(spmv_t* out, int kind, int64_t n, int64_t nnz, const int64_t* ro
             fail(SPMV_ERR_INVALID_ARG, "unknown dtype %d", dtype);
         if (n < 0 || nnz < 0) fail(SPMV_ERR_INVALID_ARG, "negative size (n=%lld nnz=%lld)",
                                    (long long)n, (long long)nnz);
-        if (n >= INT32_MAX || nnz >= INT32_MAX)
-            fail(SPMV_ERR_INVALID_ARG, "n and nnz must be below 2^31-1");
+        if (n >= INT32_MAX || nnz > kMaxNnz)
+            fail(SPMV_ERR_INVALID_ARG, "n must be below 2^31-1 and nnz at most 2^31-65537");
         if (kind == SPMV_IN_CSR && !rowidx) fail(SPMV_ERR_INVALID_ARG, "rowptr is NULL");
         if (nnz > 0 && (!rowidx || !col || !val))
             fail(SPMV_ERR_INVALID_ARG, "row/col/val pointer is NULL");

@@ -88,7 +88,7 @@ __device__ __forceinline__ void load_vec(const int* p, int (&v)[E]) {
 // ptr[lo] <= e < ptr[hi + 1])
 __device__ __forceinline__ int row_of(const int* __restrict__ ptr, int lo, int hi, int64_t e) {
     while (lo < hi) {
-        const int m = (lo + hi + 1) >> 1;
+        const int m = lo + ((hi - lo + 1) >> 1);  // lo + hi may pass 2^31
         if (ptr[m] <= e)
             lo = m;
         else
@@ -158,9 +158,10 @@ __device__ __forceinline__ void tail_rows(int64_t w, int lane, const int* __rest
     const int64_t e0 = q * E;
     const int64_t qs = cnt > 0 ? q : 0;  // past the last run: any valid index
     const int cur = run_row[qs], hi = run_row[qs + 1];
-    int nxt[E];  // starts of the next E rows (clamped to the next run's row)
+    int nxt[E];  // starts of the next E rows (clamped to the next run's row;
+                 // cur + 1 + j itself may pass 2^31 near the last rows)
 #pragma unroll
-    for (int j = 0; j < E; ++j) nxt[j] = tptr[min(cur + 1 + j, hi + 1)];
+    for (int j = 0; j < E; ++j) nxt[j] = tptr[cur + 1 + min(j, hi - cur)];
 #pragma unroll
     for (int k = 0; k < E; ++k) {
         int adv = 0;

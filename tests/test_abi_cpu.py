@@ -114,6 +114,9 @@ def test_create_argument_errors(lib):
     assert _create(lib, ctypes.byref(h), n=-1) == -1
     assert _create(lib, ctypes.byref(h), nnz=-5) == -1
     assert _create(lib, ctypes.byref(h), nnz=2 ** 31, rowidx=fake, col=fake, val=fake) == -1
+    assert _create(lib, ctypes.byref(h), nnz=2 ** 31 - 65536, rowidx=fake, col=fake,
+                   val=fake) == -1                      # past the headroom of the entry indices
+    assert _create(lib, ctypes.byref(h), n=2 ** 31 - 1, rowidx=fake) == -1
     assert _create(lib, ctypes.byref(h), n=2 ** 31, rowidx=fake) == -1
     assert _create(lib, ctypes.byref(h), rowidx=None, col=fake, val=fake) == -1
     assert _create(lib, ctypes.byref(h), rowidx=fake, col=None, val=fake) == -1

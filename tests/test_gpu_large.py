@@ -1,8 +1,11 @@
 """Row counts large enough that the grids of the per-row kernels would pass
 HIP's 2^32 work-item limit (a group of S lanes per row, G wave groups per
 64-row tile): launches are split, and every format still matches the oracle.
+The largest case is the largest n the library takes, 2^31 - 2 (row and column
+indices up to 2^31 - 3, padded row counts of 2^31).
 
-The matrix has n = 300,000,000 rows, at most three entries in a row, and its
+The matrix has n rows (300,000,000, then 2^31 - 2), at most three entries in
+a row, and its
 entries in a few hundred rows spread over the whole range (columns up to
 n - 1).  It is built from COO triples on the device; x is drawn on the device
 and only the entries the matrix reads are copied back, so the oracle runs on
@@ -22,10 +25,10 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import sparse_formats_amd as sf
 
-N = 300_000_000
+SIZES = [300_000_000, 2 ** 31 - 2]
 
 
-def _triples(seed=101):
+def _triples(N, seed=101):
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([
         [0, 1, 2, 63, 64, 65, N // 2, N - 65, N - 64, N - 2, N - 1],
@@ -40,9 +43,10 @@ def _triples(seed=101):
     return r, c.astype(np.int32), v
 
 
-@pytest.fixture(scope="module")
-def large():
-    r, c, v = _triples()
+@pytest.fixture(scope="module", params=SIZES, ids=["300M", "2^31-2"])
+def large(request):
+    N = request.param
+    r, c, v = _triples(N)
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
     x = torch.rand(N, dtype=torch.float64, device="cuda", generator=g) * 2 - 1
@@ -56,11 +60,13 @@ def large():
     rows, counts = np.unique(rs, return_counts=True)
     rp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     compact = CSR(rows.size, rp, np.searchsorted(used, cs).astype(np.int32), vs)
-    yield M, x, rows, compact, x_used
+    yield N, M, x, rows, compact, x_used
     M.close()
+    del x
+    torch.cuda.empty_cache()
 
 
-def _check(M, x, rows, compact, x_used, what):
+def _check(N, M, x, rows, compact, x_used, what):
     alpha, beta = 1.5, 0.5
     y = torch.full((N,), 2.0, dtype=torch.float64, device="cuda")
     M.apply(y, x, alpha, beta)
@@ -85,6 +91,12 @@ def _check(M, x, rows, compact, x_used, what):
     ("hec", {}),
 ])
 def test_many_rows(large, fmt, kw):
-    M, x, rows, compact, x_used = large
+    N, M, x, rows, compact, x_used = large
+    if fmt == "ellr" and N > 2 ** 30:
+        # 3 x 2^31 slots (77 GB) exceed a 1 GiB budget: refused, handle kept
+        with pytest.raises(sf.SpmvError) as e:
+            M.convert(fmt, footprint_budget=1 << 30, **kw)
+        assert e.value.code == -4
+        return
     M.convert(fmt, **kw)
-    _check(M, x, rows, compact, x_used, "%s %s" % (fmt, kw))
+    _check(N, M, x, rows, compact, x_used, "n=%d %s %s" % (N, fmt, kw))
