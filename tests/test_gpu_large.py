@@ -100,3 +100,70 @@ def test_many_rows(large, fmt, kw):
         return
     M.convert(fmt, **kw)
     _check(N, M, x, rows, compact, x_used, "n=%d %s %s" % (N, fmt, kw))
+
+
+# -- the largest entry count the library takes ---------------------------------
+
+NNZ_MAX = 2 ** 31 - 65537
+N_WIDE = 100_000_000
+
+
+@pytest.fixture(scope="module")
+def many_entries():
+    """n = 10^8 rows of 21 or 22 entries, nnz = 2^31 - 65537 exactly, built on
+    the device (random columns, N(0,1) values); the oracle checks sampled rows."""
+    n = N_WIDE
+    extra = NNZ_MAX - 21 * n
+    lens = torch.full((n,), 21, dtype=torch.int64, device="cuda")
+    lens[:extra] += 1
+    rowptr = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+    rowptr[1:] = torch.cumsum(lens, 0)
+    del lens
+    assert int(rowptr[-1]) == NNZ_MAX
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    col = torch.randint(0, n, (NNZ_MAX,), dtype=torch.int32, device="cuda", generator=g)
+    val = torch.randn(NNZ_MAX, dtype=torch.float64, device="cuda", generator=g)
+    x = torch.rand(n, dtype=torch.float64, device="cuda", generator=g) * 2 - 1
+    M = sf.Matrix.from_csr(rowptr, col, val, n=n)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, extra - 1, extra, n // 2, n - 2, n - 1],
+                                     rng.integers(0, n, 3000)])).astype(np.int64)
+    rp = rowptr.cpu().numpy()
+    idx = np.concatenate([np.arange(rp[r], rp[r + 1]) for r in rows])
+    idx_t = torch.from_numpy(idx).cuda()
+    cs = col[idx_t].cpu().numpy()
+    vs = val[idx_t].cpu().numpy()
+    used = np.unique(cs)
+    x_used = x[torch.from_numpy(used.astype(np.int64)).cuda()].cpu().numpy()
+    lens_s = (rp[rows + 1] - rp[rows]).astype(np.int64)
+    crp = np.concatenate([[0], np.cumsum(lens_s)]).astype(np.int64)
+    compact = CSR(rows.size, crp, np.searchsorted(used, cs).astype(np.int32), vs)
+    del rowptr, col, val, idx_t
+    torch.cuda.empty_cache()
+    yield n, M, x, rows, compact, x_used
+    M.close()
+    del x
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt,kw", [
+    ("csr", dict(csr_kernel="vector", subwave=16, csr_rows=1, csr_stage=1)),
+    ("csr", dict(csr_kernel="vector", subwave=16, csr_rows=2, csr_stage=0)),
+    ("csr", dict(csr_kernel="balanced")),
+    ("ellr", {}),
+    ("sell64", {}),
+    ("hyb", dict(ell_width=10)),
+    ("hec", dict(ell_width=10)),
+])
+def test_most_entries(many_entries, fmt, kw):
+    n, M, x, rows, compact, x_used = many_entries
+    M.convert(fmt, **kw)
+    alpha, beta = -0.75, 0.5
+    y = torch.full((n,), 2.0, dtype=torch.float64, device="cuda")
+    M.apply(y, x, alpha, beta)
+    torch.cuda.synchronize()
+    got = y[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref, scale = oracle.spmv(compact, x_used, np.full(rows.size, 2.0), alpha, beta)
+    ok, worst, k = oracle.check(got, ref, scale, TOL[torch.float64])
+    assert ok, "nnz=%d %s %s: worst %.3g at row %d" % (NNZ_MAX, fmt, kw, worst, rows[k])
