@@ -241,6 +241,9 @@ def main(argv=None):
         log("%s built in %.0f ms: %s" % (fmt, setup_ms[fmt], M.info()))
     del rp, col, val
     torch.cuda.empty_cache()
+    if not mats:
+        log("every requested format was refused: %s" % refused)
+        return 2
 
     stream_gbs = None if args.no_stream else measure_stream_copy(torch, sf)
     if stream_gbs:
