@@ -50,6 +50,8 @@ KERNELS = {
 def kernels_of(fmt: str, info: dict) -> str:
     """The kernels one apply of this handle launches."""
     if fmt == "csr":
+        if info.get("csr_kernel") == "xblock":
+            return "k_xblk + k_xblk_carry + k_xblk_sum"
         if info.get("csr_kernel") == "balanced":
             return "k_scale + k_tail%s<CSR>" % ("_win" if info["x_window"] else "")
         return _vector_kernel(info["subwave"], info["csr_rows"], info.get("csr_stage_slots", 0))
@@ -151,6 +153,8 @@ def kernel_bases(fmt: str, info: dict) -> set:
     chunk kernel, present only with very long slices, is left out)."""
     win = "_win" if info.get("x_window") else ""
     if fmt == "csr":
+        if info.get("csr_kernel") == "xblock":
+            return {"k_xblk", "k_xblk_carry", "k_xblk_sum"}
         if info.get("csr_kernel") == "balanced":
             return {"k_scale", "k_tail" + win}
         return {"k_csr_staged" if info.get("csr_stage_slots", 0) > 0 else "k_csr_vector"}
@@ -192,7 +196,7 @@ def main(argv=None):
     ap.add_argument("--formats", default=",".join(ALL_FORMATS))
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
-    ap.add_argument("--csr-kernel", default="auto", choices=["auto", "vector", "balanced"],
+    ap.add_argument("--csr-kernel", default="auto", choices=["auto", "vector", "balanced", "xblock"],
                     help="CSR apply kernel (default: timed at conversion)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the whole steps eagerly instead of replaying a HIP graph of one")

@@ -43,8 +43,11 @@
  *     spmv_apply surface at the caller's next synchronisation, since apply
  *     is asynchronous.
  *   - A handle may be used by several threads for spmv_apply at once (on
- *     different streams); spmv_convert / spmv_destroy must not overlap any
- *     other call on the same handle.
+ *     different streams), except with the column-slice CSR kernel
+ *     (SPMV_CSR_XBLOCK, spmv_info_t.csr_kernel), whose applies share the
+ *     handle's partial-product buffer and must not overlap one another;
+ *     spmv_convert / spmv_destroy must not overlap any other call on the
+ *     same handle.
  */
 #ifndef SPMV_AMD_H
 #define SPMV_AMD_H
@@ -82,12 +85,25 @@ typedef enum {
  * for HEC the same option picks the kernel of the CSR tail
  * (spmv_info_t.tail_kernel) */
 typedef enum {
-    SPMV_CSR_AUTO = 0,     /* time both on the device, keep the faster */
+    SPMV_CSR_AUTO = 0,     /* time the kernels on the device, keep the faster */
     SPMV_CSR_VECTOR = 1,   /* a group of lanes per row (subwave, csr_rows) */
-    SPMV_CSR_BALANCED = 2  /* the same number of entries per wave, whatever
+    SPMV_CSR_BALANCED = 2, /* the same number of entries per wave, whatever
                               the row lengths ("Load-balancing Sparse Matrix
                               Vector Product Kernels on GPUs", abstract: a
                               CSR kernel for unbalanced matrices) */
+    SPMV_CSR_XBLOCK = 3    /* CSR format only: the columns cut into 8 slices,
+                              one per XCD, each slice's entries balanced as
+                              above and its x reads kept in that XCD's L2
+                              (for x reads scattered over an x larger than
+                              one L2: "Sparse matrix-vector multiplication on
+                              GPGPU clusters", Sect. 2.3, right-hand-side
+                              reuse).  Stores a second, column-sliced copy of
+                              the entries plus 8 partial products per row;
+                              needs 8 n < 2^31 - 16.  SPMV_CSR_AUTO
+                              times it as well when x is over 4 MiB and
+                              at least half the entries lie outside the
+                              diagonal band of the LDS window, and keeps
+                              it only when clearly faster. */
 } spmv_csr_kernel;
 
 /* input layout of spmv_create */
@@ -300,9 +316,9 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts *opts);
  *   x      device dtype[n]; must not overlap y
  *   alpha, beta  scalars (rounded to float for SPMV_F32 handles)
  *   stream the kernels are enqueued on this stream; no host synchronisation
- * Accumulation is in the handle's dtype with fused multiply-adds; HYB/HEC
- * and split SELL slices add partial sums with atomics, so their last bits
- * may vary between runs.  Errors: STATE, INVALID_ARG (null or overlapping
+ * Accumulation is in the handle's dtype with fused multiply-adds; HYB/HEC,
+ * split SELL slices and the balanced and column-slice CSR kernels add
+ * partial sums with atomics, so their last bits may vary between runs.  Errors: STATE, INVALID_ARG (null or overlapping
  * vectors), HIP (launch failure).
  */
 int spmv_apply(spmv_t h, void *y, const void *x, double alpha, double beta,

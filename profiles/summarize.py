@@ -10,8 +10,8 @@ repository root on the MI355X machine, W the workload):
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/WRITE_SIZE_W_F -o run \
         -- python3 bench.py --workload W --formats F --steps 2 --warmup 1 --no-cpu
 
-(for CSR once per kernel: F = csr-vector / csr-balanced with
---formats csr --csr-kernel vector / balanced)
+(for CSR once per kernel: F = csr-vector / csr-balanced / csr-xblock with
+--formats csr --csr-kernel vector / balanced / xblock)
 
 and writes profiles/spmv_<W>_<dtype>_kernel_stats.md, ..._fetch_write.md and the
 per-apply HBM bytes of every format into profiles/traffic.json (keyed by
@@ -28,11 +28,11 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-FORMATS = ["csr-vector", "csr-balanced", "ellr", "sell64", "hyb", "hec"]
+FORMATS = ["csr-vector", "csr-balanced", "csr-xblock", "ellr", "sell64", "hyb", "hec"]
 APPLY = ("k_csr_vector", "k_csr_staged", "k_scale", "k_tail", "k_tail_win", "k_ell", "k_ell_win", "k_sell",
-         "k_sell_chunks")
+         "k_sell_chunks", "k_xblk", "k_xblk_carry", "k_xblk_sum")
 SOURCES = ["sparse_formats_amd/csrc/" + f for f in
-           ("api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "common.h", "internal.h")]
+           ("api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "k_xblk.hip", "common.h", "internal.h")]
 
 
 def short(name):

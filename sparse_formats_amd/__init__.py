@@ -25,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspmv_amd.so")
 
 FORMATS = {"csr": 0, "ellr": 1, "sell64": 2, "hyb": 3, "hec": 4, "auto": 5}
-CSR_KERNELS = {"auto": 0, "vector": 1, "balanced": 2}
+CSR_KERNELS = {"auto": 0, "vector": 1, "balanced": 2, "xblock": 3}
 ARRAYS = {
     "rowptr": (0, np.int32), "col": (1, np.int32), "val": (2, None),
     "ell_col": (3, np.int32), "ell_val": (4, None), "ell_len": (5, np.int32),
@@ -183,7 +183,7 @@ class Matrix:
                 permuted_basis: int = 0, ell_groups: int = 0, csr_stage: int = -1,
                 col_cache: int = -1) -> "Matrix":
         """Build `fmt` on the device and make it active (options as in spmv_convert_opts;
-        csr_kernel is "auto", "vector" or "balanced")."""
+        csr_kernel is "auto", "vector", "balanced" or "xblock")."""
         if fmt not in FORMATS:
             raise ValueError("unknown format %r (one of %s)" % (fmt, ", ".join(FORMATS)))
         ck = CSR_KERNELS.get(csr_kernel, csr_kernel)

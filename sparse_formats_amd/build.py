@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libspmv_amd.so")
-SOURCES = ["api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "k_vec.hip"]
+SOURCES = ["api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "k_vec.hip", "k_xblk.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -126,6 +126,10 @@ struct Built {
     VecShape tail_vec;
     // CSR: entry-balanced kernel (run rows over the whole matrix)
     bool csr_balanced = false;
+    // CSR by column slices, one per XCD (the view holds the pointers below)
+    bool csr_xblock = false;
+    DevBuf xb_ptr, xb_col, xb_val, xb_lane_row, xb_part, xb_carry_row, xb_carry_val;
+    XblkView xb{};
     // SELL-64 in the permuted basis (x and y in sorted row order)
     bool permuted = false;
     // x staged in LDS by the ELL / tail kernels
@@ -139,7 +143,8 @@ struct Built {
                sell_len.bytes +
                perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + tail_row.bytes +
                tail_ptr.bytes + tail_col.bytes + tail_val.bytes + run_row.bytes + tail_rows.bytes +
-               tail_cptr.bytes;
+               tail_cptr.bytes + xb_ptr.bytes + xb_col.bytes + xb_val.bytes + xb_lane_row.bytes +
+               xb_part.bytes + xb_carry_row.bytes + xb_carry_val.bytes;
     }
 };
 
@@ -589,6 +594,8 @@ void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, int sigma, B
 // a timed alternative to the simpler kernel (no LDS window, no atomics) is
 // kept only when it is at least this much faster
 constexpr float kPreferMargin = 0.95f;
+// the column-slice CSR kernel is a candidate only for x above one XCD's L2
+constexpr int64_t kXbMinX = 4 << 20;
 // entry indices are 32-bit in the kernels, which step past a row's end by up
 // to a few hundred entries before masking: keep that headroom below 2^31
 constexpr int64_t kMaxNnz = INT32_MAX - 65536;
@@ -896,6 +903,10 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
     hipError_t e = hipSuccess;
     switch (format) {
         case SPMV_CSR: {
+            if (b.csr_xblock) {
+                e = launch_xblk(b.xb, f64, y, x, alpha, beta, s);
+                break;
+            }
             if (b.csr_balanced) {
                 TailView t{(int)h->n, h->nnz, nullptr, h->rowptr.as<int>(), b.run_row.as<int>(),
                            nullptr, h->col.as<int>(), h->val.p, b.window};
@@ -1034,7 +1045,87 @@ float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw
 // CSR kernel: time every shape of the vector kernel and the entry-balanced
 // kernel on the device and keep the fastest (the apply does not depend on
 // the values of x, so zeros are used).  Fixed values are not tuned.
+// CSR by column slices (SPMV_CSR_XBLOCK): the tall row pointer from the
+// per-slice row lengths, the entries copied in tall order, the merged-item
+// start of every slice and the row of every lane's first item.
+void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
+    const int64_t n = h->n, R = (int64_t)kXbBlocks * n;
+    if (R > (int64_t)INT32_MAX - 16)
+        fail(SPMV_ERR_INVALID_ARG, "csr_kernel 3 (column slices) takes n <= %lld rows (got %lld)",
+             (long long)(((int64_t)INT32_MAX - 16) / kXbBlocks), (long long)n);
+    b.csr_xblock = true;
+    XblkView& v = b.xb;
+    v.n = n;
+    v.width = std::max<int64_t>((n + kXbBlocks - 1) / kXbBlocks, 1);
+    if (n == 0) return;
+    // the row pointer holds kXbItems copies of nnz past its end, the entry
+    // arrays kXbItems zero entries (a lane reads kXbItems of each unchecked)
+    b.xb_ptr.alloc((size_t)(R + 1 + kXbItems) * 4);
+    {
+        const std::vector<int> pad(kXbItems, (int)h->nnz);
+        hip_check(hipMemcpyAsync(b.xb_ptr.as<int>() + R + 1, pad.data(), pad.size() * 4,
+                                 hipMemcpyHostToDevice, s),
+                  "hipMemcpyAsync");
+        DevBuf cnt((size_t)R * 4);
+        hip_check(launch_xblk_count(n, v.width, h->rowptr.as<int>(), h->col.as<int>(),
+                                    cnt.as<int>(), s),
+                  "column-slice counts");
+        hip_check(hipMemsetAsync(b.xb_ptr.p, 0, 4, s), "hipMemsetAsync");
+        size_t tmp = 0;
+        hip_check(rocprim::inclusive_scan(nullptr, tmp, cnt.as<int>(), b.xb_ptr.as<int>() + 1,
+                                          (size_t)R, rocprim::plus<int>(), s),
+                  "inclusive_scan");
+        DevBuf work(tmp);
+        hip_check(rocprim::inclusive_scan(work.p, tmp, cnt.as<int>(), b.xb_ptr.as<int>() + 1,
+                                          (size_t)R, rocprim::plus<int>(), s),
+                  "inclusive_scan");
+        sync(s);
+    }
+    int64_t waves = 0, tiles = 0;
+    for (int k = 0; k <= kXbBlocks; ++k)
+        v.item0[k] = (int64_t)k * n + read_scalar<int>(b.xb_ptr.as<int>() + (size_t)k * n, s);
+    for (int k = 0; k < kXbBlocks; ++k) {
+        const int64_t w = (v.item0[k + 1] - v.item0[k] + kXbChunk - 1) / kXbChunk;
+        v.wave_base[k] = waves;
+        waves += w;
+        tiles = std::max<int64_t>(tiles, (w + 3) / 4);
+    }
+    v.wave_base[kXbBlocks] = waves;
+    v.waves = waves;
+    v.tiles = tiles;
+    const int64_t nnz = h->nnz;
+    b.xb_col.alloc((size_t)(nnz + kXbItems) * 4);
+    b.xb_val.alloc((size_t)(nnz + kXbItems) * h->vsize);
+    hip_check(hipMemsetAsync(b.xb_col.as<int>() + nnz, 0, kXbItems * 4, s), "hipMemsetAsync");
+    hip_check(hipMemsetAsync((char*)b.xb_val.p + (size_t)nnz * h->vsize, 0, kXbItems * h->vsize, s),
+              "hipMemsetAsync");
+    hip_check(launch_xblk_fill(n, v.width, h->dtype == SPMV_F64, h->rowptr.as<int>(),
+                               h->col.as<int>(), h->val.p, b.xb_ptr.as<int>(), b.xb_col.as<int>(),
+                               b.xb_val.p, s),
+              "column-slice fill");
+    v.ptr = b.xb_ptr.as<int>();
+    v.col = b.xb_col.as<int>();
+    v.val = b.xb_val.p;
+    // lanes past a slice's last item read row 0 (any valid row)
+    b.xb_lane_row.alloc((size_t)waves * 64 * 4);
+    hip_check(hipMemsetAsync(b.xb_lane_row.p, 0, b.xb_lane_row.bytes, s), "hipMemsetAsync");
+    hip_check(launch_xblk_lane_rows(v, b.xb_lane_row.as<int>(), s), "column-slice lane rows");
+    v.lane_row = b.xb_lane_row.as<int>();
+    b.xb_part.alloc((size_t)R * h->vsize);
+    b.xb_carry_row.alloc((size_t)waves * 4);
+    b.xb_carry_val.alloc((size_t)waves * h->vsize);
+    v.part = b.xb_part.p;
+    v.carry_row = b.xb_carry_row.as<int>();
+    v.carry_val = b.xb_carry_val.p;
+    sync(s);
+}
+
 void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t s) {
+    if (o.csr_kernel == SPMV_CSR_XBLOCK) {
+        h->subwave = 1, h->csr_rows = 1, h->csr_stage_slots = 0, h->csr_stage_col_nt = false;
+        build_xblock(h, b, s);
+        return;
+    }
     int rule = 1;  // smallest power of two >= the longest row, at most 64
     while (rule < 64 && rule < h->max_len) rule <<= 1;
     if (o.csr_stage == 1) rule = std::min(std::max(rule, kCsrStageMin), kCsrStageMax);
@@ -1083,8 +1174,28 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
         // the vector kernel adds no atomics (bit-reproducible results): the
         // balanced one must be clearly faster to be kept
         b.csr_balanced = ms < kPreferMargin * best_ms;
+        if (b.csr_balanced) best_ms = ms;
     }
     if (!b.csr_balanced) b.run_row.release(), b.window = false, b.tail_runs = 0;
+    // third candidate: column slices, for x reads scattered over an x larger
+    // than one XCD's L2 (most entries outside the diagonal band the LDS
+    // window would cover), when its copy of the entries fits the budget
+    const double xb_bytes = (double)h->nnz * (4.0 + (double)h->vsize) +
+                            (double)kXbBlocks * (double)h->n * (8.0 + (double)h->vsize);
+    if (o.csr_kernel == SPMV_CSR_AUTO && want_bal && !b.window &&
+        (double)h->n * (double)h->vsize > (double)kXbMinX && b.band_fraction < 0.5 &&
+        (int64_t)kXbBlocks * h->n <= (int64_t)INT32_MAX - 16 &&
+        xb_bytes <= (double)budget_bytes(o)) {
+        Built xb;
+        build_xblock(h, xb, s);
+        const float ms = time_launches(
+            [&] { return launch_built(h, xb, SPMV_CSR, ys.p, xs.p, 1.0, 0.0, s); }, s);
+        if (ms < kPreferMargin * best_ms) {
+            xb.band_fraction = b.band_fraction;
+            b = std::move(xb);
+        }
+    }
+    sync(s);
 }
 
 // HEC tail kernel: the balanced kernel (atomics) or the vector CSR kernel
@@ -1602,8 +1713,14 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
         if (o.subwave < 0 || o.subwave > 64 || (o.subwave & (o.subwave - 1)))
             fail(SPMV_ERR_INVALID_ARG, "subwave must be 0 or a power of two in 1..64 (got %d)",
                  o.subwave);
-        if (o.csr_kernel < SPMV_CSR_AUTO || o.csr_kernel > SPMV_CSR_BALANCED)
-            fail(SPMV_ERR_INVALID_ARG, "csr_kernel must be 0, 1 or 2 (got %d)", o.csr_kernel);
+        if (o.csr_kernel < SPMV_CSR_AUTO || o.csr_kernel > SPMV_CSR_XBLOCK)
+            fail(SPMV_ERR_INVALID_ARG, "csr_kernel must be 0, 1, 2 or 3 (got %d)", o.csr_kernel);
+        if (o.csr_kernel == SPMV_CSR_XBLOCK && format != SPMV_CSR)
+            fail(SPMV_ERR_INVALID_ARG, "csr_kernel 3 (column slices) applies to the CSR format only");
+        if (o.csr_kernel == SPMV_CSR_XBLOCK &&
+            (o.subwave || o.csr_rows > 1 || o.csr_stage == 1 || o.x_window == 1))
+            fail(SPMV_ERR_INVALID_ARG,
+                 "csr_kernel 3 (column slices) takes no subwave, csr_rows, csr_stage or x_window");
         if (o.col_cache < -1 || o.col_cache > 1)
             fail(SPMV_ERR_INVALID_ARG, "col_cache must be -1, 0 or 1 (got %d)", o.col_cache);
         if (o.csr_stage < -1 || o.csr_stage > 1)
@@ -1751,7 +1868,8 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.footprint_bytes = h->rowptr.bytes + h->col.bytes + h->val.bytes + b.bytes();
     i.x_window = b.window ? 1 : 0;
     i.csr_rows = h->csr_rows;
-    i.csr_stage_slots = h->format == SPMV_CSR && !b.csr_balanced ? h->csr_stage_slots : 0;
+    i.csr_stage_slots =
+        h->format == SPMV_CSR && !b.csr_balanced && !b.csr_xblock ? h->csr_stage_slots : 0;
     i.tail_kernel = (h->format == SPMV_HYB || h->format == SPMV_HEC) && b.tail_nnz > 0
                         ? (b.tail_vector ? SPMV_CSR_VECTOR : SPMV_CSR_BALANCED)
                         : SPMV_CSR_AUTO;
@@ -1760,10 +1878,13 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.tail_rows = tv ? b.tail_vec.rows : 0;
     i.tail_stage_slots = tv ? b.tail_vec.slots : 0;
     if (h->format == SPMV_CSR)
-        i.col_cached = !b.csr_balanced && h->csr_stage_slots > 0 && !h->csr_stage_col_nt;
+        i.col_cached =
+            !b.csr_balanced && !b.csr_xblock && h->csr_stage_slots > 0 && !h->csr_stage_col_nt;
     else
         i.col_cached = !b.col_nt;
-    i.csr_kernel = h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED : SPMV_CSR_VECTOR;
+    i.csr_kernel = h->format == SPMV_CSR && b.csr_xblock     ? SPMV_CSR_XBLOCK
+                   : h->format == SPMV_CSR && b.csr_balanced ? SPMV_CSR_BALANCED
+                                                             : SPMV_CSR_VECTOR;
     i.sort_window = b.sort_window;
     i.ell_groups = (h->format == SPMV_ELLR || h->format == SPMV_HYB || h->format == SPMV_HEC)
                        ? b.ell_groups

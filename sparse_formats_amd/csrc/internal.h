@@ -114,6 +114,42 @@ struct TailView {
     bool window;           // stage x in LDS (banded matrices)
 };
 
+// CSR by column blocks: the columns cut into kXbBlocks slices of `width`
+// columns (one per XCD), slice b's entries stored as a tall CSR matrix of n
+// rows (tall row b * n + i: row i's entries in slice b, original order).
+// Work is split into merged items (entries and one end marker per row): a
+// wave takes kXbChunk consecutive items of one slice, kXbItems per lane.
+constexpr int kXbBlocks = 8;
+constexpr int kXbItems = 8;
+constexpr int kXbChunk = 64 * kXbItems;
+struct XblkView {
+    int64_t n;            // matrix rows (tall rows: kXbBlocks * n < 2^31 - 16)
+    int64_t width;        // columns per slice
+    const int* ptr;       // [kXbBlocks * n + 1] tall row pointer
+    const int* col;       // [nnz] tall order
+    const void* val;      // [nnz]
+    const int* lane_row;  // [64 * waves] tall row of each lane's first item
+    void* part;           // [kXbBlocks * n] partial products per slice
+    int* carry_row;       // [waves] row open at the wave's end, or -1
+    void* carry_val;      // [waves] its sum within the wave
+    int64_t waves;        // all slices
+    int64_t tiles;        // workgroups (4 waves each) per slice, the most of any slice
+    int64_t wave_base[kXbBlocks + 1];  // first wave of each slice
+    int64_t item0[kXbBlocks + 1];      // first merged item of each slice (b * n + ptr[b * n])
+};
+hipError_t launch_xblk(const XblkView& a, bool f64, void* y, const void* x, double alpha,
+                       double beta, hipStream_t stream);
+// setup: cnt[b * n + i] = entries of row i in slice b
+hipError_t launch_xblk_count(int64_t n, int64_t width, const int* rowptr, const int* col,
+                             int* cnt, hipStream_t stream);
+// setup: tall col / val from the CSR arrays and the tall row pointer
+hipError_t launch_xblk_fill(int64_t n, int64_t width, bool f64, const int* rowptr, const int* col,
+                            const void* val, const int* ptr, int* ocol, void* oval,
+                            hipStream_t stream);
+// setup: lane_row (every lane of every slice's waves; lanes past a slice's
+// last item are left as they are)
+hipError_t launch_xblk_lane_rows(const XblkView& a, int* lane_row, hipStream_t stream);
+
 // kernel launchers (asynchronous on `stream`); fp64 when f64, else fp32
 // rows: rows per lane group, a power of two up to kCsrRowsMax; stage_slots >
 // 0: copy each wave's entries into LDS first when they fit in that many slots

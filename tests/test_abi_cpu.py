@@ -96,6 +96,9 @@ def test_enum_values_match_binding():
     assert fm == {"csr": 0, "ellr": 1, "sell64": 2, "hyb": 3, "hec": 4}
     assert ev["SPMV_AUTO"] == 5 and ev["SPMV_CSR_BALANCED"] == 2 and ev["SPMV_A_ELL_PERM"] == 15
     assert ev["SPMV_A_TAIL_VAL"] == 14 and ev["SPMV_A_SELL_SLICE_PTR"] == 7
+    import sparse_formats_amd as sf
+    assert sf.CSR_KERNELS == {"auto": ev["SPMV_CSR_AUTO"], "vector": ev["SPMV_CSR_VECTOR"],
+                              "balanced": ev["SPMV_CSR_BALANCED"], "xblock": ev["SPMV_CSR_XBLOCK"]}
 
 
 def _create(lib, out, kind=0, n=4, nnz=4, rowidx=None, col=None, val=None, dtype=2):

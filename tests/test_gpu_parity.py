@@ -443,6 +443,7 @@ GRAPH_CASES = [("csr", dict(csr_kernel="vector", csr_stage=1)),
                ("csr", dict(csr_kernel="vector", csr_stage=0)),
                ("csr", dict(csr_kernel="balanced", x_window=0)),
                ("csr", dict(csr_kernel="balanced", x_window=1)),
+               ("csr", dict(csr_kernel="xblock")),
                ("ellr", dict(x_window=0)), ("ellr", dict(x_window=1)), ("ellr", dict(ell_groups=4)),
                ("sell64", {}),
                ("hyb", dict(x_window=0)), ("hyb", dict(x_window=1)),
@@ -656,8 +657,75 @@ def test_csr_kernel_choice():
         y = apply(M, torch.from_numpy(x_np).cuda(), torch.from_numpy(y0_np).cuda(), 1.0, 1.0)
         check(a, x_np, y0_np, 1.0, 1.0, y, torch.float64, what="csr balanced %s" % name)
         with pytest.raises(sf.SpmvError):
-            M.convert("csr", csr_kernel=3)
+            M.convert("csr", csr_kernel=4)
         M.close()
+
+
+def _scattered():
+    # random columns over the whole row range (the x reads the column slices
+    # are for), lognormal lengths, a few rows spanning many waves, empty rows
+    rng = np.random.default_rng(47)
+    n = 50_000
+    lens = np.minimum(np.rint(rng.lognormal(np.log(6.0), 1.0, n)).astype(np.int64), n)
+    lens[rng.choice(n, 5000, replace=False)] = 0
+    lens[rng.choice(n, 4, replace=False)] = [n, 20_000, 4_097, 513]
+    return random_csr(n, seed=48, lens=lens)
+
+
+XBLOCK_MATS = dict(WINDOW_MATS, scattered=_scattered,
+                   n7=lambda: random_csr(7, seed=49, lens=np.array([0, 7, 1, 0, 3, 7, 2])))
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("name", list(XBLOCK_MATS))
+def test_csr_xblock(name, dtype):
+    """CSR by column slices (one per XCD; merged items of entries and row
+    ends, rows finished inside a wave stored plainly, rows open at a wave's
+    end carried) against the oracle, and NaNs in y dropped when beta = 0."""
+    a = XBLOCK_MATS[name]()
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    x_np, y0_np = vectors(a.n, 21)
+    x_np, y0_np = x_np.astype(npdt), y0_np.astype(npdt)
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n).convert("csr", csr_kernel="xblock")
+    i = M.info()
+    assert i["csr_kernel"] == "xblock" and i["format"] == "csr" and i["x_window"] == 0
+    assert i["csr_stage_slots"] == 0
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    for alpha, beta in AB:
+        y = apply(M, x, y0, alpha, beta)
+        check(a, x_np, y0_np, alpha, beta, y, dtype,
+              what="csr xblock %s a=%g b=%g" % (name, alpha, beta))
+    if a.n > 0:
+        y = torch.full((a.n,), float("nan"), dtype=dtype, device="cuda")
+        M.apply(y, x)
+        torch.cuda.synchronize()
+        check(a, x_np, None, 1.0, 0.0, y.cpu().numpy(), dtype, what="csr xblock NaN y %s" % name)
+        # repeated applies: the partial products are rewritten every time
+        for _ in range(2):
+            y = apply(M, x, y0, 1.0, 1.0)
+            check(a, x_np, y0_np, 1.0, 1.0, y, dtype, what="csr xblock again %s" % name)
+    # back to another kernel and format and again: the handle stays consistent
+    M.convert("hec").convert("csr", csr_kernel="xblock")
+    y = apply(M, x, y0, 0.5, 2.0)
+    check(a, x_np, y0_np, 0.5, 2.0, y, dtype, what="csr xblock again %s" % name)
+    M.close()
+
+
+def test_csr_xblock_errors():
+    a = MATS["c1"]()
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
+    for fmt, kw in [("hec", {}), ("hyb", {}), ("ellr", {}), ("sell64", {}), ("auto", {}),
+                    ("csr", dict(subwave=4)), ("csr", dict(csr_rows=2)),
+                    ("csr", dict(csr_stage=1)), ("csr", dict(x_window=1))]:
+        with pytest.raises(sf.SpmvError) as e:
+            M.convert(fmt, csr_kernel="xblock", **kw)
+        assert e.value.code == -1, (fmt, kw)
+    M.convert("csr", csr_kernel="xblock")  # the failed calls left it usable
+    assert M.info()["csr_kernel"] == "xblock"
+    M.close()
 
 
 @pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
