@@ -102,6 +102,7 @@ def main():
     out_dir, workload = sys.argv[1], sys.argv[2]
     dtype = sys.argv[3] if len(sys.argv) > 3 else "f64"
     tag = "%s_%s" % (workload, dtype)
+    dt_flag = "" if dtype == "f64" else " --dtype " + dtype
     # ---- kernel statistics of the default bench
     sd = os.path.join(out_dir, "stats_" + workload)
     stats = rows_of(sd, "kernel_stats.csv")
@@ -111,7 +112,8 @@ def main():
     lines = ["# rocprofv3 kernel statistics: bench.py on %s (%s)" % (workload, dtype), "",
              "Command (repository root, MI355X):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d <out>/stats_%s -o run "
-             "-- python3 bench.py --workload %s --steps 10 --warmup 2 --no-cpu" % (workload, workload),
+             "-- python3 bench.py --workload %s%s --steps 10 --warmup 2 --no-cpu"
+             % (workload, workload, dt_flag),
              "", "rocprofv3 statistics (all dispatches of the run, including the conversion-time "
              "timing of kernel shapes and the stream copy):", "",
              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
@@ -158,11 +160,12 @@ def main():
     fw = ["# HBM traffic per apply: bench.py on %s (%s)" % (workload, dtype), "",
           "Commands (repository root, MI355X; one counter per run, F the format):", "",
           "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/FETCH_SIZE_%s_F -o run "
-          "-- python3 bench.py --workload %s --formats F --steps 2 --warmup 1 --no-cpu"
-          % (workload, workload),
+          "-- python3 bench.py --workload %s%s --formats F --steps 2 --warmup 1 --no-cpu"
+          % (workload, workload, dt_flag),
           "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/WRITE_SIZE_%s_F -o run "
-          "-- python3 bench.py --workload %s --formats F --steps 2 --warmup 1 --no-cpu"
-          % (workload, workload), ""]
+          "-- python3 bench.py --workload %s%s --formats F --steps 2 --warmup 1 --no-cpu"
+          % (workload, workload, dt_flag),
+          "", "(F = csr-K stands for --formats csr --csr-kernel K.)", ""]
     table = ["| format | kernels of one apply | FETCH bytes | WRITE bytes | total |",
              "|---|---|---|---|---|"]
     src_hash = source_hash()
