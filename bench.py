@@ -107,26 +107,29 @@ def _stream_handle(torch):
     return torch.cuda.current_stream()
 
 
-def measure_stream_copy(torch, sf, gib: float = 2.0, reps: int = 20) -> float:
-    """Median GB/s of the library's copy kernel over two 2 GiB buffers."""
+def measure_stream_copy(torch, sf, gib: float = 2.0, reps: int = 20,
+                        read_only: bool = False) -> float:
+    """Median GB/s of the library's copy kernel over two 2 GiB buffers (or of
+    its read-only stream over one)."""
     nbytes = int(gib * (1 << 30))
     src = torch.empty(nbytes // 8, dtype=torch.float64, device="cuda").fill_(1.0)
-    dst = torch.empty_like(src)
+    dst = None if read_only else torch.empty_like(src)
+    run = (lambda: sf.stream_read(src)) if read_only else (lambda: sf.stream_copy(dst, src))
     for _ in range(3):
-        sf.stream_copy(dst, src)
+        run()
     ts = []
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        sf.stream_copy(dst, src)
+        run()
         e1.record()
         ts.append((e0, e1))
     torch.cuda.synchronize()
     ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
     del src, dst
     torch.cuda.empty_cache()
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+    return (1 if read_only else 2) * nbytes / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(a, x, target_s: float = 10.0):
@@ -250,8 +253,9 @@ def main(argv=None):
         return 2
 
     stream_gbs = None if args.no_stream else measure_stream_copy(torch, sf)
+    read_gbs = None if args.no_stream else measure_stream_copy(torch, sf, read_only=True)
     if stream_gbs:
-        log("stream copy %.1f GB/s" % stream_gbs)
+        log("stream copy %.1f GB/s, read-only stream %.1f GB/s" % (stream_gbs, read_gbs))
 
     fmts = list(mats)
     for _ in range(args.warmup):
@@ -331,7 +335,8 @@ def main(argv=None):
                 "traffic": traffic_for("%s:%s:%s" % (args.workload, args.dtype, dom),
                                        kernel_bases(dom, mats_info[dom])),
                 "kernel": "%s apply (%s)" % (dom, d["kernels"]),
-                "frac_of_stream": d["frac_stream"]}
+                "frac_of_stream": d["frac_stream"],
+                "frac_of_read_stream": round(achieved / read_gbs, 4) if read_gbs else None}
     flops_step = 2.0 * a.nnz * len(fmts)
     out = {
         "metric": "SpMV GFLOP/s and effective HBM GB/s (% of roofline) per format, " + args.dtype,
@@ -350,6 +355,7 @@ def main(argv=None):
                         "eff_gbs": per[best]["eff_gbs"],
                         "frac_stream": per[best]["frac_stream"]},
         "stream_copy_gbs": round(stream_gbs, 1) if stream_gbs else None,
+        "stream_read_gbs": round(read_gbs, 1) if read_gbs else None,
         "formats": per,
         "roofline": roofline,
     }

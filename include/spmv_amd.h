@@ -399,9 +399,12 @@ int spmv_export(spmv_t h, int array, void *host_dst, int64_t capacity_bytes,
                 int64_t *bytes);
 
 /*
- * spmv_stream_copy -- dst[0..bytes) = src[0..bytes) with the same load/store
- * style as the SpMV kernels (16-byte nontemporal loads, grid-stride); the
- * reference bandwidth that the SpMV kernels are compared with.  Both device
+ * spmv_stream_copy -- dst[0..bytes) = src[0..bytes) with 16-byte
+ * nontemporal loads and stores, one per thread over a grid that covers the
+ * buffer (the fastest copy shape measured on MI355X); the reference
+ * bandwidth that the SpMV kernels are compared with.  dst == NULL reads
+ * src only (the whole 16-byte words of it) and writes nothing: the
+ * bandwidth of loads alone, for read-dominated kernels.  Both device
  * pointers must be 16-byte aligned and not overlap.  Asynchronous on stream.
  * Errors: INVALID_ARG, HIP.
  */

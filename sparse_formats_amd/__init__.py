@@ -19,7 +19,8 @@ import os
 import numpy as np
 import torch
 
-__all__ = ["Matrix", "SpmvError", "FORMATS", "CSR_KERNELS", "ARRAYS", "stream_copy", "lib_path", "version"]
+__all__ = ["Matrix", "SpmvError", "FORMATS", "CSR_KERNELS", "ARRAYS", "stream_copy", "stream_read",
+           "lib_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspmv_amd.so")
@@ -268,6 +269,12 @@ class Matrix:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def stream_read(src, stream=None):
+    """Read src with the library's read-only streaming kernel (nothing written)."""
+    _check(_lib.spmv_stream_copy(None, _dev(src, None, "src"), src.numel() * src.element_size(),
+                                 _stream(stream)))
 
 
 def stream_copy(dst, src, stream=None):

@@ -1938,12 +1938,13 @@ int spmv_export(spmv_t h, int array, void* host_dst, int64_t capacity_bytes, int
 
 int spmv_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) {
     g_err.clear();
-    if (bytes < 0 || (bytes > 0 && (!dst || !src)) || ((uintptr_t)dst | (uintptr_t)src) % 16) {
-        g_err = "bad copy arguments (null, negative or not 16-byte aligned)";
+    // dst == NULL: read src only
+    if (bytes < 0 || (bytes > 0 && !src) || ((uintptr_t)dst | (uintptr_t)src) % 16) {
+        g_err = "bad copy arguments (null src, negative or not 16-byte aligned)";
         return SPMV_ERR_INVALID_ARG;
     }
     const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
-    if (bytes > 0 && d < s + (uintptr_t)bytes && s < d + (uintptr_t)bytes) {
+    if (dst && bytes > 0 && d < s + (uintptr_t)bytes && s < d + (uintptr_t)bytes) {
         g_err = "copy buffers overlap";
         return SPMV_ERR_INVALID_ARG;
     }

@@ -147,6 +147,9 @@ def test_null_handle_errors(lib):
     assert lib.spmv_stream_copy(P(0x1000), P(0x2000), -1, None) == -1
     assert lib.spmv_stream_copy(P(0x1000), P(0x1010), 64, None) == -1
     assert b"overlap" in lib.spmv_last_error()
+    # read-only stream (dst NULL): src still required and aligned
+    assert lib.spmv_stream_copy(None, None, 16, None) == -1
+    assert lib.spmv_stream_copy(None, P(0x1008), 16, None) == -1
 
 
 def test_version(lib):

@@ -423,6 +423,12 @@ def test_stream_copy():
     sf.stream_copy(d2, s2)
     torch.cuda.synchronize()
     assert torch.equal(d2, s2)
+    # the read-only stream (dst NULL) leaves its source as it was
+    keep = src.clone()
+    sf.stream_read(src)
+    sf.stream_read(s2)
+    torch.cuda.synchronize()
+    assert torch.equal(src, keep) and torch.equal(d2, s2)
 
 
 def test_apply_on_side_stream():
