@@ -195,11 +195,12 @@ def main():
             "write_scaled": round(wb), "fetch_factor": round(vals["FETCH_SIZE"][0], 5),
             "write_factor": round(vals["WRITE_SIZE"][0], 5), "sources": SOURCES,
             "sha256": src_hash})
-    ff = T.get("%s:%s:ellr" % (workload, dtype), [{}])[0]
+    recs = [r for k, v in T.items() if k.startswith("%s:%s:" % (workload, dtype)) for r in v]
+    ffs = sorted({r["fetch_factor"] for r in recs}) or [0]
+    wfs = sorted({r["write_factor"] for r in recs}) or [0]
     fw.append("Calibration: the library's copy kernel k_copy reads and writes 2 GiB per "
-              "dispatch in every run; FETCH_SIZE is scaled by %.4f and WRITE_SIZE by %.4f "
-              "(KiB counters, factors from that run)." % (ff.get("fetch_factor", 0),
-                                                          ff.get("write_factor", 0)))
+              "dispatch in every run; FETCH_SIZE is scaled by %.4f-%.4f and WRITE_SIZE by "
+              "%.4f-%.4f (KiB counters, each run's own factor)." % (ffs[0], ffs[-1], wfs[0], wfs[-1]))
     fw += ["", "Last apply of the timed loop (the run applies only format F):", ""] + table
     open(os.path.join(ROOT, "profiles", "spmv_%s_fetch_write.md" % tag), "w").write(
         "\n".join(fw) + "\n")
