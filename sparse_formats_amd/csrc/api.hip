@@ -1501,6 +1501,9 @@ spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_o
     st0[kStMaxIt] = (double)o.max_iter;
     st0[kStDone] = std::sqrt(rr0) > goal ? 0.0 : 1.0;
     st0[kStRho] = st0[kStAlpha] = st0[kStOmega] = 1.0;
+    // BiCGSTAB's first rho = rhat . r with rhat = r, and the first beta from
+    // rho = alpha = omega = 1 (p = v = 0 makes the first direction r)
+    st0[kStRhoNew] = st0[kStBeta] = rr0;
     chk(hipMemcpyAsync(st, st0, sizeof st0, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
     if (o.method == SPMV_SOLVE_CG) {
         chk(hipMemcpyAsync(p, r, vb, hipMemcpyDeviceToDevice, s), "hipMemcpyAsync");
@@ -1520,8 +1523,6 @@ spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_o
             chk(launch_solve_step(pd, st, kStepCgRR, s), "step");
             chk(launch_update_p(n, f64, p, r, nullptr, st, s), "cg direction");
         } else {
-            chk(launch_dot2(n, f64, rh, r, nullptr, nullptr, pd, nullptr, s), "dot");
-            chk(launch_solve_step(pd, st, kStepBiRho, s), "step");
             chk(launch_update_p(n, f64, p, r, v, st, s), "bicgstab direction");
             apply(v, p, 1.0, 0.0);
             chk(launch_dot2(n, f64, rh, v, nullptr, nullptr, pd, nullptr, s), "dot");
@@ -1530,7 +1531,7 @@ spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_o
             apply(t, sv, 1.0, 0.0);
             chk(launch_dot2(n, f64, t, sv, t, t, pd, nullptr, s), "dot");
             chk(launch_solve_step(pd, st, kStepBiOmega, s), "step");
-            chk(launch_bicg_xr(n, f64, x, r, p, sv, t, st, pd, s), "bicgstab update");
+            chk(launch_bicg_xr(n, f64, x, r, p, sv, t, rh, st, pd, s), "bicgstab update");
             chk(launch_solve_step(pd, st, kStepBiRR, s), "step");
         }
     };

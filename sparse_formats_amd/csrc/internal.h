@@ -188,7 +188,7 @@ enum SolveState : int {
     kStRR, kStGoal, kStK, kStMaxIt, kStDone, kStPQ, kStAlpha, kStBeta, kStOmega, kStRho,
     kStRhoNew, kStCount
 };
-enum SolveStep : int { kStepCgPQ, kStepCgRR, kStepBiRho, kStepBiRV, kStepBiOmega, kStepBiRR };
+enum SolveStep : int { kStepCgPQ, kStepCgRR, kStepBiRV, kStepBiOmega, kStepBiRR };
 // reduce partial (as launch_dot2 leaves it) and advance st by `step`
 hipError_t launch_solve_step(const double* partial, double* st, int step, hipStream_t s);
 // x += alpha p, r -= alpha q (alpha = rr / p.q), partial sums of r . r
@@ -200,9 +200,11 @@ hipError_t launch_update_p(int64_t n, bool f64, void* p, const void* r, const vo
 // s = r - alpha v
 hipError_t launch_axmy(int64_t n, bool f64, void* s_out, const void* r, const void* v,
                        const double* st, hipStream_t s);
-// x += alpha p + omega s, r = s - omega t, partial sums of r . r
+// x += alpha p + omega s, r = s - omega t, partial sums of r . r and of
+// rhat . r (for kStepBiRR)
 hipError_t launch_bicg_xr(int64_t n, bool f64, void* x, void* r, const void* p, const void* s_in,
-                          const void* t, const double* st, double* partial, hipStream_t s);
+                          const void* t, const void* rh, const double* st, double* partial,
+                          hipStream_t s);
 // y = beta * y for n entries (beta == 0 writes zeros and never reads y)
 hipError_t launch_scale(int64_t n, bool f64, void* y, double beta, hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);

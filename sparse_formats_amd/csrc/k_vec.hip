@@ -29,6 +29,79 @@ __device__ __forceinline__ double block_sum(double v, double* sh) {
     return s;
 }
 
+// The scalars of an iteration live in device memory (st, indexed by
+// SolveState): a one-workgroup step kernel computes them from the inner
+// products and the vector kernels read them, so an iteration needs no host
+// round trip and can be replayed from a HIP graph.  Once st[kStDone] is set every kernel below
+// leaves without writing, so iterations enqueued past convergence change
+// nothing.
+__device__ __forceinline__ bool solve_done(const double* st) { return st[kStDone] != 0.0; }
+
+// Sum the partial products in block order (as k_dot_finish), then one
+// thread advances the iteration's scalars:
+//   kStepCgPQ     p.q
+//   kStepCgRR     r.r of the new residual: beta = rr_new / rr, rr = rr_new,
+//                 k += 1, done when ||r|| <= goal or k == max_iter
+//   kStepBiRV     alpha = rho_new / rhat.v
+//   kStepBiOmega  omega = t.s / t.t (0 when t = 0)
+//   kStepBiRR     rr = r.r, rho = rho_new, k += 1, done as for CG or when
+//                 omega == 0 (s was already the residual of x + alpha p);
+//                 then for the next iteration rho_new = rhat.r (done on
+//                 breakdown rho_new == 0) and beta = (rho_new / rho)
+//                 (alpha / omega)
+__device__ void solve_step(const double* __restrict__ partial, int blocks,
+                           double* __restrict__ st, int step) {
+    __shared__ double sh[4];
+    double t[2];
+    for (int k = 0; k < 2; ++k) {
+        double s = 0;
+        for (int b = threadIdx.x; b < blocks; b += 256) s += partial[2 * b + k];
+        t[k] = block_sum(s, sh);
+        __syncthreads();
+    }
+    if (threadIdx.x != 0) return;
+    auto advance = [&](double rr) {
+        st[kStRR] = rr;
+        const double k = st[kStK] + 1.0;
+        st[kStK] = k;
+        if (!(sqrt(rr) > st[kStGoal]) || k >= st[kStMaxIt]) st[kStDone] = 1.0;
+    };
+    switch (step) {
+        case kStepCgPQ:
+            st[kStPQ] = t[0];
+            break;
+        case kStepCgRR:
+            st[kStBeta] = st[kStRR] != 0.0 ? t[0] / st[kStRR] : 0.0;
+            advance(t[0]);
+            break;
+        case kStepBiRV:
+            st[kStAlpha] = st[kStRhoNew] / t[0];
+            break;
+        case kStepBiOmega:
+            st[kStOmega] = t[1] > 0 ? t[0] / t[1] : 0.0;
+            break;
+        case kStepBiRR:
+            st[kStRho] = st[kStRhoNew];
+            advance(t[0]);
+            if (st[kStOmega] == 0.0) st[kStDone] = 1.0;
+            if (st[kStDone] != 0.0) break;
+            if (t[1] == 0.0) {
+                st[kStDone] = 1.0;
+                break;
+            }
+            st[kStBeta] = (t[1] / st[kStRho]) * (st[kStAlpha] / st[kStOmega]);
+            st[kStRhoNew] = t[1];
+            break;
+    }
+}
+
+// one workgroup: the step on the partial sums of the reduction kernel before
+__global__ __launch_bounds__(256) void k_solve_step(const double* __restrict__ partial, int blocks,
+                                                    double* __restrict__ st, int step) {
+    if (solve_done(st)) return;
+    solve_step(partial, blocks, st, step);
+}
+
 // partial[2 * b + k] = block b's share of a_k . b_k (k = 0, 1; the second
 // product only when a1 != nullptr)
 template <typename T>
@@ -63,14 +136,6 @@ __global__ __launch_bounds__(256) void k_dot_finish(const double* __restrict__ p
         if (threadIdx.x == 0) out[k] = t;
     }
 }
-
-// The scalars of an iteration live in device memory (st, indexed by
-// SolveState): the step kernel computes them from the inner products and the
-// vector kernels read them, so an iteration needs no host round trip and can
-// be replayed from a HIP graph.  Once st[kStDone] is set every kernel below
-// leaves without writing, so iterations enqueued past convergence change
-// nothing.
-__device__ __forceinline__ bool solve_done(const double* st) { return st[kStDone] != 0.0; }
 
 // x += alpha p; r -= alpha q; partial sums of r . r   (alpha = rr / p.q)
 template <typename T>
@@ -114,84 +179,29 @@ __global__ __launch_bounds__(256) void k_axmy(int64_t n, T* __restrict__ s,
         s[i] = r[i] - alpha * v[i];
 }
 
-// x += alpha p + omega s; r = s - omega t; partial sums of r . r
+// x += alpha p + omega s; r = s - omega t; partial sums of r . r and of
+// rhat . r (the next iteration's rho)
 template <typename T>
 __global__ __launch_bounds__(256) void k_bicg_xr(int64_t n, T* __restrict__ x, T* __restrict__ r,
                                                  const T* __restrict__ p, const T* __restrict__ s,
-                                                 const T* __restrict__ t,
+                                                 const T* __restrict__ t, const T* __restrict__ rh,
                                                  const double* __restrict__ st,
                                                  double* __restrict__ partial) {
     __shared__ double sh[4];
     if (solve_done(st)) return;
     const T alpha = (T)st[kStAlpha], omega = (T)st[kStOmega];
-    double acc = 0;
+    double acc = 0, acc_h = 0;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         x[i] += alpha * p[i] + omega * s[i];
         const T ri = s[i] - omega * t[i];
         r[i] = ri;
         acc += (double)ri * (double)ri;
+        acc_h += (double)rh[i] * (double)ri;
     }
     const double tt = block_sum(acc, sh);
-    if (threadIdx.x == 0) partial[2 * blockIdx.x] = tt, partial[2 * blockIdx.x + 1] = 0;
-}
-
-// Sum the partial products in block order (as k_dot_finish), then one
-// thread advances the iteration's scalars:
-//   kStepCgPQ     p.q
-//   kStepCgRR     r.r of the new residual: beta = rr_new / rr, rr = rr_new,
-//                 k += 1, done when ||r|| <= goal or k == max_iter
-//   kStepBiRho    rho_new = rhat.r (done on breakdown rho_new == 0),
-//                 beta = (rho_new / rho) (alpha / omega) with the last alpha
-//   kStepBiRV     alpha = rho_new / rhat.v
-//   kStepBiOmega  omega = t.s / t.t (0 when t = 0)
-//   kStepBiRR     rr = r.r, rho = rho_new, k += 1, done as for CG or when
-//                 omega == 0 (s was already the residual of x + alpha p)
-__global__ __launch_bounds__(256) void k_solve_step(const double* __restrict__ partial, int blocks,
-                                                    double* __restrict__ st, int step) {
-    __shared__ double sh[4];
-    if (solve_done(st)) return;
-    double t[2];
-    for (int k = 0; k < 2; ++k) {
-        double s = 0;
-        for (int b = threadIdx.x; b < blocks; b += 256) s += partial[2 * b + k];
-        t[k] = block_sum(s, sh);
-        __syncthreads();
-    }
-    if (threadIdx.x != 0) return;
-    auto advance = [&](double rr) {
-        st[kStRR] = rr;
-        const double k = st[kStK] + 1.0;
-        st[kStK] = k;
-        if (!(sqrt(rr) > st[kStGoal]) || k >= st[kStMaxIt]) st[kStDone] = 1.0;
-    };
-    switch (step) {
-        case kStepCgPQ:
-            st[kStPQ] = t[0];
-            break;
-        case kStepCgRR:
-            st[kStBeta] = st[kStRR] != 0.0 ? t[0] / st[kStRR] : 0.0;
-            advance(t[0]);
-            break;
-        case kStepBiRho:
-            if (t[0] == 0.0) {
-                st[kStDone] = 1.0;
-                break;
-            }
-            st[kStBeta] = (t[0] / st[kStRho]) * (st[kStAlpha] / st[kStOmega]);
-            st[kStRhoNew] = t[0];
-            break;
-        case kStepBiRV:
-            st[kStAlpha] = st[kStRhoNew] / t[0];
-            break;
-        case kStepBiOmega:
-            st[kStOmega] = t[1] > 0 ? t[0] / t[1] : 0.0;
-            break;
-        case kStepBiRR:
-            st[kStRho] = st[kStRhoNew];
-            advance(t[0]);
-            if (st[kStOmega] == 0.0) st[kStDone] = 1.0;
-            break;
-    }
+    __syncthreads();
+    const double th = block_sum(acc_h, sh);
+    if (threadIdx.x == 0) partial[2 * blockIdx.x] = tt, partial[2 * blockIdx.x + 1] = th;
 }
 
 static unsigned grid_of(int64_t n) {
@@ -251,15 +261,17 @@ hipError_t launch_axmy(int64_t n, bool f64, void* s_out, const void* r, const vo
 }
 
 hipError_t launch_bicg_xr(int64_t n, bool f64, void* x, void* r, const void* p, const void* s_in,
-                          const void* t, const double* st, double* partial, hipStream_t s) {
+                          const void* t, const void* rh, const double* st, double* partial,
+                          hipStream_t s) {
     const unsigned g = kDotBlocks;
     if (f64)
         hipLaunchKernelGGL(k_bicg_xr<double>, dim3(g), dim3(256), 0, s, n, (double*)x,
                            (double*)r, (const double*)p, (const double*)s_in, (const double*)t,
-                           st, partial);
+                           (const double*)rh, st, partial);
     else
         hipLaunchKernelGGL(k_bicg_xr<float>, dim3(g), dim3(256), 0, s, n, (float*)x, (float*)r,
-                           (const float*)p, (const float*)s_in, (const float*)t, st, partial);
+                           (const float*)p, (const float*)s_in, (const float*)t, (const float*)rh,
+                           st, partial);
     return hipGetLastError();
 }
 
