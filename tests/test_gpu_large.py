@@ -2,7 +2,9 @@
 HIP's 2^32 work-item limit (a group of S lanes per row, G wave groups per
 64-row tile): launches are split, and every format still matches the oracle.
 The largest case is the largest n the library takes, 2^31 - 2 (row and column
-indices up to 2^31 - 3, padded row counts of 2^31).
+indices up to 2^31 - 3, padded row counts of 2^31); the column-slice CSR
+kernel, whose tall matrix has 8 n rows, is refused there and run at the most
+rows it takes.
 
 The matrix has n rows (300,000,000, then 2^31 - 2), at most three entries in
 a row, and its
@@ -43,9 +45,21 @@ def _triples(N, seed=101):
     return r, c.astype(np.int32), v
 
 
+# the most rows the column-slice CSR kernel takes (its tall matrix has 8 n rows)
+XB_MAX = (2 ** 31 - 1 - 16) // 8
+
+
 @pytest.fixture(scope="module", params=SIZES, ids=["300M", "2^31-2"])
 def large(request):
-    N = request.param
+    yield from _large(request.param)
+
+
+@pytest.fixture(scope="module")
+def xb_largest():
+    yield from _large(XB_MAX)
+
+
+def _large(N):
     r, c, v = _triples(N)
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
@@ -89,9 +103,18 @@ def _check(N, M, x, rows, compact, x_used, what):
     ("sell64", {}),
     ("hyb", {}),
     ("hec", {}),
+    ("csr", dict(csr_kernel="xblock")),
 ])
 def test_many_rows(large, fmt, kw):
     N, M, x, rows, compact, x_used = large
+    if kw.get("csr_kernel") == "xblock":
+        # 8 n tall rows would pass 2^31: refused, handle kept
+        with pytest.raises(sf.SpmvError) as e:
+            M.convert(fmt, **kw)
+        assert e.value.code == -1
+        M.convert("csr", csr_kernel="balanced")
+        _check(N, M, x, rows, compact, x_used, "n=%d after a refused xblock" % N)
+        return
     if fmt == "ellr" and N > 2 ** 30:
         # 3 x 2^31 slots (77 GB) exceed a 1 GiB budget: refused, handle kept
         with pytest.raises(sf.SpmvError) as e:
@@ -100,6 +123,15 @@ def test_many_rows(large, fmt, kw):
         return
     M.convert(fmt, **kw)
     _check(N, M, x, rows, compact, x_used, "n=%d %s %s" % (N, fmt, kw))
+
+
+def test_xblock_most_rows(xb_largest):
+    """The column-slice CSR kernel at the most rows it takes: tall rows up to
+    2^31 - 17, merged items past 2^31."""
+    N, M, x, rows, compact, x_used = xb_largest
+    M.convert("csr", csr_kernel="xblock")
+    assert M.info()["csr_kernel"] == "xblock"
+    _check(N, M, x, rows, compact, x_used, "n=%d xblock" % N)
 
 
 # -- the largest entry count the library takes ---------------------------------
@@ -155,6 +187,7 @@ def many_entries():
     ("sell64", {}),
     ("hyb", dict(ell_width=10)),
     ("hec", dict(ell_width=10)),
+    ("csr", dict(csr_kernel="xblock")),
 ])
 def test_most_entries(many_entries, fmt, kw):
     n, M, x, rows, compact, x_used = many_entries
