@@ -1187,12 +1187,20 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
         (int64_t)kXbBlocks * h->n <= (int64_t)INT32_MAX - 16 &&
         xb_bytes <= (double)budget_bytes(o)) {
         Built xb;
-        build_xblock(h, xb, s);
-        const float ms = time_launches(
-            [&] { return launch_built(h, xb, SPMV_CSR, ys.p, xs.p, 1.0, 0.0, s); }, s);
-        if (ms < kPreferMargin * best_ms) {
-            xb.band_fraction = b.band_fraction;
-            b = std::move(xb);
+        bool built = true;
+        try {
+            build_xblock(h, xb, s);
+        } catch (const Error& e) {
+            if (e.code != SPMV_ERR_NO_MEMORY) throw;
+            built = false;  // no room for the optional copy: not a candidate
+        }
+        if (built) {
+            const float ms = time_launches(
+                [&] { return launch_built(h, xb, SPMV_CSR, ys.p, xs.p, 1.0, 0.0, s); }, s);
+            if (ms < kPreferMargin * best_ms) {
+                xb.band_fraction = b.band_fraction;
+                b = std::move(xb);
+            }
         }
     }
     sync(s);
