@@ -18,8 +18,11 @@ nominal 8 TB/s.  The CPU oracle (Dot2 CSR, OpenMP over the host cores) is
 timed on the same matrix as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--dtype f64|f32] [--formats csr,hyb] [--no-cpu]
-Prints one JSON line.
+                       [--dtype f64|f32] [--formats csr,hyb] [--no-cpu] [--cold]
+Prints one JSON line.  Per format also: the rate on the CSR bytes model (one
+byte count for every format); a matrix of under 1 MiB of values gets at least
+1,000 timed applies per format; --cold adds medians of applies that each
+follow a 1 GiB scratch read (nothing of the matrix or x left in the caches).
 """
 from __future__ import annotations
 
@@ -132,23 +135,33 @@ def measure_stream_copy(torch, sf, gib: float = 2.0, reps: int = 20,
     return (1 if read_only else 2) * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(a, x, target_s: float = 10.0):
-    """Time the CPU oracle (Dot2 CSR) on the full matrix over all host cores."""
+def cpu_baseline(a, x, s_v: int, target_s: float = 10.0, target_1core_s: float = 5.0):
+    """Time the CPU oracle (Dot2 CSR) on the full matrix over all host cores,
+    and on one core."""
     import oracle
     cores = len(os.sched_getaffinity(0))
-    oracle.spmv(a, x, nthreads=cores)              # warm caches / threads
-    reps, t = 0, 0.0
-    t0 = time.perf_counter()
-    while True:
-        oracle.spmv(a, x, nthreads=cores)
-        reps += 1
-        t = time.perf_counter() - t0
-        if t >= target_s or reps >= 2000:
-            break
-    gflops = 2.0 * a.nnz * reps / t / 1e9
-    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+
+    def timed(threads, budget):
+        oracle.spmv(a, x, nthreads=threads)        # warm caches / threads
+        reps, t = 0, 0.0
+        t0 = time.perf_counter()
+        while True:
+            oracle.spmv(a, x, nthreads=threads)
+            reps += 1
+            t = time.perf_counter() - t0
+            if t >= budget or reps >= 2000:
+                return reps, t
+
+    reps, t = timed(cores, target_s)
+    reps1, t1 = timed(1, target_1core_s)
+    bm = bytes_model("csr", a.n, a.nnz, s_v)
+    return {"value": round(2.0 * a.nnz * reps / t / 1e9, 3), "unit": "GFLOP/s", "cores": cores,
+            "kind": "oracle",
             "sample": "%d full applies of the same %d-row matrix (Dot2 fp64, OpenMP static "
-                      "rows) in %.1f s" % (reps, a.n, t)}
+                      "rows) in %.1f s; one core: %d in %.1f s" % (reps, a.n, t, reps1, t1),
+            "gbs_csr_model": round(bm * reps / t / 1e9, 2),
+            "value_1core": round(2.0 * a.nnz * reps1 / t1 / 1e9, 3),
+            "gbs_csr_model_1core": round(bm * reps1 / t1 / 1e9, 2)}
 
 
 def kernel_bases(fmt: str, info: dict) -> set:
@@ -199,6 +212,8 @@ def main(argv=None):
     ap.add_argument("--formats", default=",".join(ALL_FORMATS))
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time every format with a 1 GiB scratch read before each apply")
     ap.add_argument("--csr-kernel", default="auto", choices=["auto", "vector", "balanced", "xblock"],
                     help="CSR apply kernel (default: timed at conversion)")
     ap.add_argument("--no-graph", action="store_true",
@@ -278,6 +293,38 @@ def main(argv=None):
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    # a launch-bound matrix (a few hundred KB) gets at least 1,000 timed
+    # applies per format for its medians
+    reps = args.steps if a.nnz * s_v >= (1 << 20) else max(args.steps, 1000)
+    for f in fmts:
+        for _ in range(reps - args.steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            mats[f].apply(y, x)
+            e1.record()
+            ev[f].append((e0, e1))
+    torch.cuda.synchronize()
+    # cold: reading 1 GiB of scratch through the caches before each apply
+    # empties the Infinity Cache of the matrix and x (a read leaves no dirty
+    # lines, so the apply pays for no write-backs of the flush; the library's
+    # read stream would not do: its nontemporal loads leave the caches as
+    # they are).  Only the apply is timed.
+    cold = {f: [] for f in fmts} if args.cold else None
+    if args.cold:
+        scratch = torch.ones(1 << 27, dtype=torch.float64, device="cuda")
+        for f in fmts:
+            for r in range(args.steps):
+                scratch.sum()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                mats[f].apply(y, x)
+                e1.record()
+                cold[f].append((e0, e1))
+        torch.cuda.synchronize()
+        del scratch
+        torch.cuda.empty_cache()
     step_timing = "eager"
     if not args.no_graph:
         # the step rate without host launch gaps: the same applies, captured
@@ -309,6 +356,7 @@ def main(argv=None):
 
     per = {}
     mats_info = {f: mats[f].info() for f in fmts}
+    bm_csr = bytes_model("csr", a.n, a.nnz, s_v)  # one byte count for every format
     for f in fmts:
         ts = np.array([e0.elapsed_time(e1) for e0, e1 in ev[f]])
         med = float(np.median(ts))
@@ -317,15 +365,21 @@ def main(argv=None):
         gbs = bm / (med * 1e-3) / 1e9
         per[f] = {
             "ms_median": round(med, 5), "ms_min": round(float(ts.min()), 5),
-            "ms_p90": round(float(np.percentile(ts, 90)), 5),
+            "ms_p90": round(float(np.percentile(ts, 90)), 5), "timed_applies": int(ts.size),
             "gflops": round(2 * a.nnz / (med * 1e-3) / 1e9, 2),
             "eff_gbs": round(gbs, 1), "bytes_model": int(bm),
+            "eff_gbs_csr_model": round(bm_csr / (med * 1e-3) / 1e9, 1),
             "frac_stream": round(gbs / stream_gbs, 4) if stream_gbs else None,
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "slots": info["slots"], "ell_width": info["ell_width"],
             "tail_nnz": info["tail_nnz"], "setup_ms": round(setup_ms[f], 1),
             "kernels": kernels_of(f, info), "x_window": info["x_window"],
         }
+        if cold is not None:
+            tc = float(np.median([e0.elapsed_time(e1) for e0, e1 in cold[f]]))
+            per[f]["cold_ms_median"] = round(tc, 5)
+            per[f]["cold_frac_stream"] = (round(bm / (tc * 1e-3) / 1e9 / stream_gbs, 4)
+                                          if stream_gbs else None)
     best = max(per, key=lambda f: per[f]["gflops"])
     dom = max(per, key=lambda f: per[f]["ms_median"])
     d = per[dom]
@@ -361,7 +415,7 @@ def main(argv=None):
     }
     if not args.no_cpu:
         log("timing the CPU oracle ...")
-        out["cpu_baseline"] = cpu_baseline(a, x_np)
+        out["cpu_baseline"] = cpu_baseline(a, x_np, s_v)
     for M in mats.values():
         M.close()
     print(json.dumps(out), flush=True)
