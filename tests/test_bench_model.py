@@ -129,3 +129,12 @@ def test_traffic_record_checks(tmp_path):
     assert bench.kernels_of("hec", hec_vec) == "k_ell + k_csr_vector<S=4,R=2>"
     assert bench.kernels_of("hyb", {"x_window": 1, "tail_nnz": 0}) == "k_ell_win"
     assert bench.kernels_of("hyb", {"x_window": 0, "tail_nnz": 3}) == "k_ell + k_tail<COO>"
+    # the column-slice CSR kernel and its traffic record
+    xb = {"csr_kernel": "xblock", "x_window": 0, "subwave": 1, "csr_rows": 1}
+    assert bench.kernel_bases("csr", xb) == {"k_xblk", "k_xblk_carry", "k_xblk_sum"}
+    assert bench.kernels_of("csr", xb) == "k_xblk + k_xblk_carry + k_xblk_sum"
+    rec["w:f64:csr"].append({"kernels": ["k_xblk<double>", "k_xblk_carry<double>",
+                                         "k_xblk_sum<double>"], "bytes_per_launch": 55,
+                             "sources": srcs, "sha256": h.hexdigest()})
+    p.write_text(json.dumps(rec))
+    assert bench.traffic_for("w:f64:csr", bench.kernel_bases("csr", xb), str(p)) == 55
