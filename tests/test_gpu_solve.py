@@ -24,12 +24,12 @@ def _system(a, seed):
     return x_true, b
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
-def test_cg_laplacian(fmt):
+@pytest.mark.parametrize("fmt,kw", [(f, {}) for f in FORMATS] + [("csr", dict(csr_kernel="xblock"))])
+def test_cg_laplacian(fmt, kw):
     a = c1_laplace2d()
     x_true, b = _system(a, 1)
     xo, it_o, rel_o = oracle.cg(a, b, rtol=1e-10, max_iter=2000)
-    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt, **kw)
     x, info = M.solve(torch.from_numpy(b).cuda(), rtol=1e-10, max_iter=2000)
     xg = x.cpu().numpy()
     assert info["converged"] and info["rel_residual"] <= 1e-10
@@ -69,8 +69,9 @@ def test_cg_exact_cases():
     M.close()
 
 
-@pytest.mark.parametrize("fmt", ["csr", "sell64", "hec"])
-def test_bicgstab_nonsymmetric_stencil(fmt):
+@pytest.mark.parametrize("fmt,kw", [("csr", {}), ("sell64", {}), ("hec", {}),
+                                    ("csr", dict(csr_kernel="xblock"))])
+def test_bicgstab_nonsymmetric_stencil(fmt, kw):
     # 27-point stencil with independent noise per entry: not symmetric
     a = stencil((13, 11, 9), "box", 26.0, -1.0, noise=1e-2, seed=3)
     x_true, b = _system(a, 4)
@@ -80,7 +81,7 @@ def test_bicgstab_nonsymmetric_stencil(fmt):
         np.add.at(D[i], a.col[s:e], a.val[s:e])
     assert not np.allclose(D, D.T)
     xo, it_o, rel_o = oracle.bicgstab(a, b, rtol=1e-11)
-    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt, **kw)
     x, info = M.solve(torch.from_numpy(b).cuda(), method="bicgstab", rtol=1e-11)
     xg = x.cpu().numpy()
     assert info["converged"] and abs(info["iterations"] - it_o) <= 3, (info, it_o)
