@@ -200,8 +200,10 @@ typedef struct {
     /* Cache policy of the column indices (ELL-R, SELL-64, the ELL part of
      * HYB/HEC, the staged CSR copy): 0 streams them past the caches like the
      * values, 1 keeps them in the caches (when they fit the last-level cache
-     * beside x they stay there over repeated applies), -1 times both and
-     * keeps them cached only when that is at least 5 % faster. */
+     * beside x they stay there over applies that follow one another with
+     * nothing else in between), -1 (default) streams them: with other work
+     * between two applies (a solver's vector updates, other matrices) the
+     * cached indices do not survive, and streaming is then the faster. */
     int32_t col_cache;
 } spmv_convert_opts;
 

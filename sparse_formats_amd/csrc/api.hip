@@ -1014,6 +1014,7 @@ float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw
                   int fix_stage, int col_cache, void* ys, const void* xs, double beta,
                   VecShape& best, hipStream_t s) {
     float best_ms = 1e30f;
+    const bool col_nt = col_cache != 1;  // the staged copy streams col unless asked
     // a group that would loop more than kVecMaxPasses times over the longest
     // row serialises the launch on it: such shapes are not timed (the widest
     // one in range always is)
@@ -1027,18 +1028,10 @@ float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw
                 if (st && (rows != 1 || sw < kCsrStageMin || sw > kCsrStageMax)) continue;
                 const int slots = st ? stage_slots_for(v, f64, sw, s) : 0;
                 const float ms = time_launches([&] {
-                    return launch_csr(v, sw, rows, slots, false, f64, ys, xs, 1.0, beta, s);
+                    return launch_csr(v, sw, rows, slots, col_nt, f64, ys, xs, 1.0, beta, s);
                 }, s);
-                if (ms < best_ms) best_ms = ms, best = VecShape{sw, rows, slots, false};
+                if (ms < best_ms) best_ms = ms, best = VecShape{sw, rows, slots, col_nt};
             }
-    if (best.slots > 0 && col_cache < 0) {
-        const float ms = time_launches([&] {
-            return launch_csr(v, best.subwave, 1, best.slots, true, f64, ys, xs, 1.0, beta, s);
-        }, s);
-        // streamed unless keeping col cached is clearly faster
-        if (!(best_ms < kPreferMargin * ms)) best_ms = std::min(best_ms, ms), best.col_nt = true;
-    }
-    if (col_cache >= 0) best.col_nt = col_cache == 0;
     return best_ms;
 }
 
@@ -1132,7 +1125,7 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     h->subwave = o.subwave ? o.subwave : rule;
     h->csr_rows = o.csr_rows ? o.csr_rows : 1;
     h->csr_stage_slots = 0;
-    h->csr_stage_col_nt = o.col_cache == 0;
+    h->csr_stage_col_nt = o.col_cache != 1;
     const bool f64 = h->dtype == SPMV_F64;
     const CsrView v{(int)h->n, (int)h->nnz, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
     const bool want_vec = o.csr_kernel != SPMV_CSR_BALANCED;
@@ -1299,21 +1292,7 @@ bool valid_format(int f) { return f >= SPMV_CSR && f <= SPMV_HEC; }
 // Column-index cache policy of the ELL-family kernels: streamed past the
 // caches (the default) or cached, whichever applies faster.  Cached indices
 // pay when they fit the last-level cache beside x over repeated applies.
-void choose_col_policy(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s) {
-    b.col_nt = opt != 1;
-    if (opt >= 0 || h->n == 0 || h->nnz == 0) return;
-    DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
-    hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
-    const float t_nt =
-        time_launches([&] { return launch_built(h, b, format, ys.p, xs.p, 1.0, 0.0, s); }, s);
-    b.col_nt = false;
-    const float t_c =
-        time_launches([&] { return launch_built(h, b, format, ys.p, xs.p, 1.0, 0.0, s); }, s);
-    sync(s);
-    // cached only when clearly faster: over interleaved work (other matrices
-    // between two applies) the cached indices do not survive anyway
-    b.col_nt = !(t_c < kPreferMargin * t_nt);
-}
+void choose_col_policy(int opt, Built& b) { b.col_nt = opt != 1; }
 
 // HYB/HEC at ELL width `width` (as choose_width takes it): the split, the
 // window and group choices, and HEC's tail kernel
@@ -1327,7 +1306,7 @@ void build_split_tuned(spmv_handle* h, int format, const spmv_convert_opts& o, i
     decide_window(h, format, o.x_window, b, s);
     choose_groups(h, o.ell_groups, b);
     if (format == SPMV_HEC) tune_hec_tail(h, o.csr_kernel, o.col_cache, b, s);
-    choose_col_policy(h, format, o.col_cache, b, s);
+    choose_col_policy(o.col_cache, b);
 }
 
 // Build `format` (options already validated) and make it the active format.
@@ -1358,14 +1337,14 @@ void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
             build_ell_part<float>(h, W, 0, 0, b, s);
         decide_window(h, format, o.x_window, b, s);
         choose_groups(h, o.ell_groups, b);
-        choose_col_policy(h, format, o.col_cache, b, s);
+        choose_col_policy(o.col_cache, b);
         sync(s);
     } else if (format == SPMV_SELL64) {
         if (f64)
             build_sell<double>(h, o.sort_window, o.permuted_basis != 0, b, s);
         else
             build_sell<float>(h, o.sort_window, o.permuted_basis != 0, b, s);
-        choose_col_policy(h, format, o.col_cache, b, s);
+        choose_col_policy(o.col_cache, b);
     } else {
         build_split_tuned(h, format, o, o.ell_width, b, s);
         if (o.ell_width < 0 && h->n > 0) {
