@@ -18,7 +18,16 @@ per-apply HBM bytes of every format into profiles/traffic.json (keyed by
 workload:dtype:format, with a hash of the kernel sources so that the bench
 drops the figure once a kernel changes).
 
-Usage: python profiles/summarize.py <out> <workload> [dtype]
+Usage: python profile_summary.py <out> <workload> [dtype]
+       python profile_summary.py counters <out> <workload> <format> [dtype]
+
+The second form summarizes counter passes of one format (each pass a
+directory <out>/PMC<k>_<workload>_<format> made by
+    rocprofv3 --pmc <counters> --output-format csv -d <dir> -o run \
+        -- python3 bench.py --workload W --formats F [--csr-kernel K] --steps 2 --warmup 1 --no-cpu
+with the counters listed in <dir>.txt) into
+profiles/spmv_<W>_<dtype>_<format>_counters.md: the counters of the last
+dispatch of every kernel of the apply.
 """
 import csv
 import hashlib
@@ -27,7 +36,7 @@ import os
 import statistics
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 FORMATS = ["csr-vector", "csr-balanced", "csr-xblock", "ellr", "sell64", "hyb", "hec"]
 APPLY = ("k_csr_vector", "k_csr_staged", "k_scale", "k_tail", "k_tail_win", "k_ell", "k_ell_win", "k_sell",
          "k_sell_chunks", "k_xblk", "k_xblk_carry", "k_xblk_sum")
@@ -208,5 +217,60 @@ def main():
     print("\n".join(fw))
 
 
+def counters_main():
+    """Counter passes of one format: the counters of the last dispatch of each
+    kernel of its apply, one table row per kernel."""
+    out_dir, workload, fmt = sys.argv[2], sys.argv[3], sys.argv[4]
+    dtype = sys.argv[5] if len(sys.argv) > 5 else "f64"
+    fmt_base, _, kernel = fmt.partition("-")
+    dt_flag = "" if dtype == "f64" else " --dtype " + dtype
+    ck_flag = " --csr-kernel " + kernel if kernel else ""
+    passes = sorted(d for d in os.listdir(out_dir)
+                    if d.startswith("PMC") and d.endswith("_%s_%s" % (workload, fmt))
+                    and os.path.isdir(os.path.join(out_dir, d)))
+    kern_order, vals, cmds = [], {}, []
+    for d in passes:
+        names = open(os.path.join(out_dir, d + ".txt")).read().split()
+        cmds.append("    rocprofv3 --pmc %s --output-format csv -d <out>/%s -o run -- python3 bench.py "
+                    "--workload %s%s --formats %s%s --steps 2 --warmup 1 --no-cpu"
+                    % (" ".join(names), d, workload, dt_flag, fmt_base, ck_flag))
+        rows = sorted(rows_of(os.path.join(out_dir, d), "counter_collection.csv"),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        seq, seen_ids = [], set()  # one entry per dispatch (a row per counter)
+        for r in rows:
+            if r["Dispatch_Id"] not in seen_ids:
+                seen_ids.add(r["Dispatch_Id"])
+                seq.append((short(r["Kernel_Name"])[0], short(r["Kernel_Name"])[1]))
+        dispatch = {}
+        for r in rows:  # keep each kernel's last dispatch (the last apply)
+            if short(r["Kernel_Name"])[0] in APPLY:
+                dispatch[short(r["Kernel_Name"])[1]] = r["Dispatch_Id"]
+        last = {full for _, full in split_apply(seq)}
+        for r in rows:
+            full = short(r["Kernel_Name"])[1]
+            if full in last and r["Dispatch_Id"] == dispatch.get(full):
+                if full not in kern_order:
+                    kern_order.append(full)
+                vals.setdefault(full, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    cols = []
+    for k in kern_order:
+        for c in vals[k]:
+            if c not in cols:
+                cols.append(c)
+    lines = ["# rocprofv3 counters of one apply: bench.py on %s (%s), format %s" % (workload, dtype, fmt),
+             "", "Commands (repository root, MI355X; one pass per counter set):", ""] + cmds + [
+             "", "The last dispatch of each kernel of the apply (the run applies only this format):", "",
+             "| kernel | " + " | ".join(cols) + " |", "|---|" + "---|" * len(cols)]
+    for k in kern_order:
+        lines.append("| %s | %s |" % (k, " | ".join(
+            "%.4g" % vals[k][c] if c in vals[k] else "" for c in cols)))
+    path = os.path.join(ROOT, "profiles", "spmv_%s_%s_%s_counters.md" % (workload, dtype, fmt))
+    open(path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        counters_main()
+    else:
+        main()
