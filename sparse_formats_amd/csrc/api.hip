@@ -963,23 +963,31 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
 // spmv_convert call (FlushScope); without room for it the launches are timed
 // back to back.
 constexpr size_t kFlushBytes = size_t(512) << 20;
-thread_local const DevBuf* t_flush = nullptr;
 
+struct FlushScope;
+thread_local FlushScope* t_flush = nullptr;
+
+// allocated at the first timed launch of the convert call (conversions with
+// every choice given time nothing and allocate nothing)
 struct FlushScope {
     DevBuf buf;
-    const DevBuf* prev;
-    FlushScope() : prev(t_flush) {
-        void* q = nullptr;
-        if (hipMalloc(&q, kFlushBytes) == hipSuccess) {
-            buf.p = q, buf.bytes = kFlushBytes;
-            t_flush = &buf;
-        } else {
-            (void)hipGetLastError();
-        }
-    }
+    bool tried = false;
+    FlushScope* prev;
+    FlushScope() : prev(t_flush) { t_flush = this; }
     ~FlushScope() { t_flush = prev; }
     FlushScope(const FlushScope&) = delete;
     FlushScope& operator=(const FlushScope&) = delete;
+    const DevBuf* get() {
+        if (!tried) {
+            tried = true;
+            void* q = nullptr;
+            if (hipMalloc(&q, kFlushBytes) == hipSuccess)
+                buf.p = q, buf.bytes = kFlushBytes;
+            else
+                (void)hipGetLastError();
+        }
+        return buf.p ? &buf : nullptr;
+    }
 };
 
 __device__ int g_flush_sink;
@@ -997,9 +1005,9 @@ __global__ __launch_bounds__(256) void k_flush(const int4* __restrict__ p, int64
 }
 
 hipError_t flush_caches(hipStream_t s) {
-    if (!t_flush) return hipSuccess;
-    hipLaunchKernelGGL(k_flush, dim3(8192), dim3(256), 0, s, t_flush->as<int4>(),
-                       (int64_t)(t_flush->bytes / 16));
+    const DevBuf* f = t_flush ? t_flush->get() : nullptr;
+    if (!f) return hipSuccess;
+    hipLaunchKernelGGL(k_flush, dim3(8192), dim3(256), 0, s, f->as<int4>(), (int64_t)(f->bytes / 16));
     return hipGetLastError();
 }
 
