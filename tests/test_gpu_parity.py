@@ -417,6 +417,24 @@ def test_convert_twice_same_arrays():
         assert first == [M.export(n).tobytes() for n in arrays]
 
 
+def test_convert_releases_its_scratch():
+    """Timed conversions borrow a 512 MiB buffer (the cache flush between timed
+    launches) and the column-slice candidate's arrays; repeated conversions
+    leave the device's free memory where it was."""
+    a = MATS["long_spans"]()
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
+    M.convert("hec")
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    for fmt in ["csr", "hec", "hyb", "sell64", "auto", "csr"] * 2:
+        M.convert(fmt)
+    torch.cuda.synchronize()
+    M.convert("hec")
+    torch.cuda.synchronize()
+    assert abs(torch.cuda.mem_get_info()[0] - free0) < (64 << 20)
+    M.close()
+
+
 def test_stream_copy():
     src = torch.randn(1 << 20, dtype=torch.float64, device="cuda")
     dst = torch.empty_like(src)
