@@ -138,3 +138,32 @@ def test_traffic_record_checks(tmp_path):
                              "sources": srcs, "sha256": h.hexdigest()})
     p.write_text(json.dumps(rec))
     assert bench.traffic_for("w:f64:csr", bench.kernel_bases("csr", xb), str(p)) == 55
+
+
+def test_counter_summary(tmp_path, monkeypatch):
+    """profile_summary.py counters: the counters of the last dispatch of each
+    kernel of the last apply, with several counter rows per dispatch."""
+    import profile_summary as ps
+    out = tmp_path / "pmc"
+    d = out / "PMC1_w_csr-xblock"
+    d.mkdir(parents=True)
+    (out / "PMC1_w_csr-xblock.txt").write_text("A B\n")
+    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    disp = 0
+    for rep in range(3):       # three applies, then the last one is kept
+        for k in ("spmv::k_xblk<double>(x)", "spmv::k_xblk_carry<double>(x)",
+                  "spmv::k_xblk_sum<double>(x)"):
+            disp += 1
+            for c in ("A", "B"):
+                rows.append('%d,"%s",%s,%d' % (disp, k, c, 10 * rep + (c == "B")))
+    (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(ps, "ROOT", str(tmp_path))
+    monkeypatch.setattr(sys, "argv", ["x", "counters", str(out), "w", "csr-xblock"])
+    ps.counters_main()
+    text = (tmp_path / "profiles" / "spmv_w_f64_csr-xblock_counters.md").read_text()
+    body = [l for l in text.splitlines() if l.startswith("| k_")]
+    assert [l.split(" | ")[0] for l in body] == ["| k_xblk<double>", "| k_xblk_carry<double>",
+                                               "| k_xblk_sum<double>"]
+    assert all(l.endswith("| 20 | 21 |") for l in body)      # the last apply's values
+    assert "--formats csr --csr-kernel xblock" in text
