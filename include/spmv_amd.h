@@ -43,11 +43,9 @@
  *     spmv_apply surface at the caller's next synchronisation, since apply
  *     is asynchronous.
  *   - A handle may be used by several threads for spmv_apply at once (on
- *     different streams), except with the column-slice CSR kernel
- *     (SPMV_CSR_XBLOCK, spmv_info_t.csr_kernel), whose applies share the
- *     handle's partial-product buffer and must not overlap one another;
- *     spmv_convert / spmv_destroy must not overlap any other call on the
- *     same handle.
+ *     different streams), whatever its format and kernels: an apply writes
+ *     only y and keeps no buffer of its own.  spmv_convert / spmv_destroy
+ *     must not overlap any other call on the same handle.
  */
 #ifndef SPMV_AMD_H
 #define SPMV_AMD_H
@@ -97,9 +95,11 @@ typedef enum {
                               (for x reads scattered over an x larger than
                               one L2: "Sparse matrix-vector multiplication on
                               GPGPU clusters", Sect. 2.3, right-hand-side
-                              reuse).  Stores a second, column-sliced copy of
-                              the entries plus 8 partial products per row;
-                              needs 8 n < 2^31 - 16.  SPMV_CSR_AUTO
+                              reuse).  A pass writes beta * y, then each
+                              slice adds alpha times its row sums into y
+                              with atomics.  Stores a second, column-sliced
+                              copy of the entries; needs 8 n < 2^31 - 16.
+                              SPMV_CSR_AUTO
                               times it as well when x is over 4 MiB and
                               at least half the entries lie outside the
                               diagonal band of the LDS window, and keeps

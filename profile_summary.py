@@ -39,7 +39,7 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 FORMATS = ["csr-vector", "csr-balanced", "csr-xblock", "ellr", "sell64", "hyb", "hec"]
 APPLY = ("k_csr_vector", "k_csr_staged", "k_scale", "k_tail", "k_tail_win", "k_ell", "k_ell_win", "k_sell",
-         "k_sell_chunks", "k_xblk", "k_xblk_carry", "k_xblk_sum")
+         "k_sell_chunks", "k_xblk")
 SOURCES = ["sparse_formats_amd/csrc/" + f for f in
            ("api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "k_xblk.hip", "common.h", "internal.h")]
 
@@ -76,34 +76,60 @@ def split_apply(seq):
     return list(reversed(out))
 
 
-def per_format_applies(timed, formats):
-    """Attribute the bench's apply dispatches to formats: every step applies
-    the formats in order, each with its own kernels (CSR: k_csr_vector, or
-    k_csr_staged or k_scale + a CSR tail; ELL-R: one ELL kernel; SELL-64: k_sell
-    [+ chunks]; HYB / HEC: one ELL kernel [+ a COO / CSR tail, for HEC possibly
-    the vector CSR kernel])."""
+def signature(kernels):
+    """[(base name, COO tail?)] of one apply from the bench's kernel string of a
+    format (e.g. "k_ell_win + k_tail_win<COO>", "k_scale + k_xblk"); SELL's
+    optional chunk kernel is left out."""
+    sig = []
+    for part in kernels.replace("(+ k_sell_chunks)", "").split("+"):
+        part = part.strip()
+        if part:
+            coo = True if "<COO>" in part else False if "<CSR>" in part else None
+            sig.append((part.split("<")[0], coo))
+    return sig
+
+
+def _matches(disp, entry):
+    base, coo = entry
+    if disp[0] != base:
+        return False
+    return coo is None or disp[1].endswith("true>" if coo else "false>")
+
+
+def per_format_applies(timed, formats, kernels):
+    """Attribute the bench's apply dispatches to formats.  `kernels` maps each
+    format to the bench line's kernel string for it; every step applies the
+    formats in order.  At each dispatch the next format of the step is tried
+    first, then the others (a trace may begin inside a step); a dispatch that
+    starts no format's apply is skipped.  SELL-64's chunk kernel joins its
+    apply when it follows."""
     out = {f: [] for f in formats}
-    i = 0
+    sigs = {f: signature(kernels[f]) for f in formats}
     names = [(short(r["Kernel_Name"])[0], short(r["Kernel_Name"])[1],
               (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in timed]
+
+    def match_at(i, f):
+        sig = sigs[f]
+        return i + len(sig) <= len(names) and all(
+            _matches(names[i + j], sig[j]) for j in range(len(sig)))
+
+    i, k = 0, 0
     while i < len(names):
-        for f in formats:
-            if i >= len(names):
-                break
-            s, full, t = names[i]
-            ks, tot = [full], t
+        order = [formats[(k + d) % len(formats)] for d in range(len(formats))]
+        f = next((g for g in order if match_at(i, g)), None)
+        if f is None:
             i += 1
-            follow = {"csr": ("k_tail", "k_tail_win") if s == "k_scale" else (),
-                      "sell64": ("k_sell_chunks",),
-                      "hyb": ("k_tail", "k_tail_win"),
-                      "hec": ("k_tail", "k_tail_win", "k_csr_vector", "k_csr_staged")}.get(f, ())
-            coo = {"hyb": "true", "hec": "false", "csr": "false"}.get(f)
-            if i < len(names) and names[i][0] in follow and (
-                    not names[i][0].startswith("k_tail") or names[i][1].endswith(coo + ">")):
-                ks.append(names[i][1])
-                tot += names[i][2]
-                i += 1
-            out[f].append((" + ".join(ks), tot))
+            continue
+        m = len(sigs[f])
+        ks = [n[1] for n in names[i:i + m]]
+        tot = sum(n[2] for n in names[i:i + m])
+        i += m
+        if f == "sell64" and i < len(names) and names[i][0] == "k_sell_chunks":
+            ks.append(names[i][1])
+            tot += names[i][2]
+            i += 1
+        out[f].append((" + ".join(ks), tot))
+        k = (formats.index(f) + 1) % len(formats)
     return out
 
 
@@ -146,7 +172,8 @@ def main():
     if js:
         bench_line = json.loads(js[-1])
         formats = bench_line["config"]["formats"]
-        applies = per_format_applies(timed, formats)
+        applies = per_format_applies(
+            timed, formats, {f: bench_line["formats"][f]["kernels"] for f in formats})
         lines += ["", "One apply per format (the kernels of each format in the warm-up and timed "
                   "steps, summed per apply), beside the bench's own median from HIP "
                   "events in the same run:", "",

@@ -100,7 +100,7 @@ def _load():
     lib.spmv_last_error.restype = ctypes.c_char_p
     lib.spmv_version.restype = ctypes.c_char_p
     for f in ("spmv_create", "spmv_convert", "spmv_apply", "spmv_destroy", "spmv_info",
-              "spmv_export", "spmv_stream_copy"):
+              "spmv_export", "spmv_stream_copy", "spmv_permute", "spmv_solve"):
         getattr(lib, f).restype = I
     return lib
 

@@ -128,7 +128,7 @@ struct Built {
     bool csr_balanced = false;
     // CSR by column slices, one per XCD (the view holds the pointers below)
     bool csr_xblock = false;
-    DevBuf xb_ptr, xb_col, xb_val, xb_lane_row, xb_part, xb_carry_row, xb_carry_val;
+    DevBuf xb_ptr, xb_col, xb_val, xb_lane_row;
     XblkView xb{};
     // SELL-64 in the permuted basis (x and y in sorted row order)
     bool permuted = false;
@@ -143,8 +143,7 @@ struct Built {
                sell_len.bytes +
                perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + tail_row.bytes +
                tail_ptr.bytes + tail_col.bytes + tail_val.bytes + run_row.bytes + tail_rows.bytes +
-               tail_cptr.bytes + xb_ptr.bytes + xb_col.bytes + xb_val.bytes + xb_lane_row.bytes +
-               xb_part.bytes + xb_carry_row.bytes + xb_carry_val.bytes;
+               tail_cptr.bytes + xb_ptr.bytes + xb_col.bytes + xb_val.bytes + xb_lane_row.bytes;
     }
 };
 
@@ -1171,12 +1170,6 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
     hip_check(hipMemsetAsync(b.xb_lane_row.p, 0, b.xb_lane_row.bytes, s), "hipMemsetAsync");
     hip_check(launch_xblk_lane_rows(v, b.xb_lane_row.as<int>(), s), "column-slice lane rows");
     v.lane_row = b.xb_lane_row.as<int>();
-    b.xb_part.alloc((size_t)R * h->vsize);
-    b.xb_carry_row.alloc((size_t)waves * 4);
-    b.xb_carry_val.alloc((size_t)waves * h->vsize);
-    v.part = b.xb_part.p;
-    v.carry_row = b.xb_carry_row.as<int>();
-    v.carry_val = b.xb_carry_val.p;
     sync(s);
 }
 
@@ -1240,8 +1233,9 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     // third candidate: column slices, for x reads scattered over an x larger
     // than one XCD's L2 (most entries outside the diagonal band the LDS
     // window would cover), when its copy of the entries fits the budget
-    const double xb_bytes = (double)h->nnz * (4.0 + (double)h->vsize) +
-                            (double)kXbBlocks * (double)h->n * (8.0 + (double)h->vsize);
+    const double xb_bytes = (double)h->nnz * (4.0 + (double)h->vsize) +  // entries
+                            (double)kXbBlocks * (double)h->n * 4.0 +        // tall row pointer
+                            ((double)kXbBlocks * (double)h->n + (double)h->nnz) / 2.0;  // lane rows
     if (o.csr_kernel == SPMV_CSR_AUTO && want_bal && !b.window &&
         (double)h->n * (double)h->vsize > (double)kXbMinX && b.band_fraction < 0.5 &&
         (int64_t)kXbBlocks * h->n <= (int64_t)INT32_MAX - 16 &&
@@ -1800,6 +1794,7 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
 }
 
 int spmv_apply(spmv_t h, void* y, const void* x, double alpha, double beta, void* stream) {
+    g_err.clear();
     if (!h) {
         g_err = "null handle";
         return SPMV_ERR_STATE;

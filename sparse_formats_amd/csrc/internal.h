@@ -129,9 +129,6 @@ struct XblkView {
     const int* col;       // [nnz] tall order
     const void* val;      // [nnz]
     const int* lane_row;  // [64 * waves] tall row of each lane's first item
-    void* part;           // [kXbBlocks * n] partial products per slice
-    int* carry_row;       // [waves] row open at the wave's end, or -1
-    void* carry_val;      // [waves] its sum within the wave
     int64_t waves;        // all slices
     int64_t tiles;        // workgroups (4 waves each) per slice, the most of any slice
     int64_t wave_base[kXbBlocks + 1];  // first wave of each slice

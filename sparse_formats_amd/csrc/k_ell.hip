@@ -22,6 +22,26 @@ namespace spmv {
 // ---------------------------------------------------------------------------
 // ELLPACK-R (also the ELL part of HYB / HEC)
 // ---------------------------------------------------------------------------
+// A wave whose longest row is much longer than the others (a few long rows
+// among short ones, the case the pages give against ELLPACK) would leave one
+// lane reading that row's slots one by one, each slot in its own cache line
+// of the column-major layout.  Once at most kEllCoopLanes lanes of a wave
+// still have entries and the longest has at least kEllCoopMin left, the
+// whole wave takes the remaining rows one after the other: lane k reads
+// slots j0 + k, j0 + k + 64, ... of the row (kEllCoopUnroll in flight), and
+// a wave sum adds the result to the row's lane.  Waves whose rows all stay
+// within kEllCoopMin entries run the plain lane-per-row loop.
+constexpr int kEllCoopLanes = 16;
+constexpr int kEllCoopMin = 64;
+constexpr int kEllCoopUnroll = 8;
+
+template <typename T>
+__device__ __forceinline__ T wave_max_len(T v) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) v = max(v, __shfl_xor(v, d));
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
 template <typename T, bool kColNT>
 __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
                                              const int* __restrict__ len,
@@ -30,28 +50,87 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
                                              const T* __restrict__ val, const T* __restrict__ x,
                                              T* __restrict__ y, T alpha, T beta) {
     const int64_t i = xcd_tile(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
-    if (i >= n) return;
-    const int L = len[i];
+    const bool valid = i < n;
+    const int L = valid ? len[i] : 0;
     const int64_t base = (i / bh) * bstride + i % bh;
     const int* c = col + base;
     const T* v = val + base;
     T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    const int M = wave_max_len(L);  // wave-uniform
     int j = 0;
-    for (; j + 4 <= L; j += 4) {
-        const int64_t o = (int64_t)j * bh;
-        const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + bh);
-        const T v2 = ld_nt(v + o + 2 * bh), v3 = ld_nt(v + o + 3 * bh);
-        const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + bh);
-        const int c2 = ld_col<kColNT>(c + o + 2 * bh), c3 = ld_col<kColNT>(c + o + 3 * bh);
-        s0 = fma(v0, x[c0], s0);
-        s1 = fma(v1, x[c1], s1);
-        s2 = fma(v2, x[c2], s2);
-        s3 = fma(v3, x[c3], s3);
+    if (M <= kEllCoopMin) {
+        for (; j + 4 <= L; j += 4) {
+            const int64_t o = (int64_t)j * bh;
+            const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + bh);
+            const T v2 = ld_nt(v + o + 2 * bh), v3 = ld_nt(v + o + 3 * bh);
+            const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + bh);
+            const int c2 = ld_col<kColNT>(c + o + 2 * bh), c3 = ld_col<kColNT>(c + o + 3 * bh);
+            s0 = fma(v0, x[c0], s0);
+            s1 = fma(v1, x[c1], s1);
+            s2 = fma(v2, x[c2], s2);
+            s3 = fma(v3, x[c3], s3);
+        }
+        for (; j < L; ++j) {
+            const int64_t o = (int64_t)j * bh;
+            s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
+        }
+    } else {
+        // lane per row in rounds of 4 while many lanes are busy (j is the
+        // same in every lane)
+        for (;;) {
+            const uint64_t act = __ballot(j < L);
+            if (act == 0 || (__popcll(act) <= kEllCoopLanes && M - j >= kEllCoopMin)) break;
+            if (j + 4 <= L) {
+                const int64_t o = (int64_t)j * bh;
+                const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + bh);
+                const T v2 = ld_nt(v + o + 2 * bh), v3 = ld_nt(v + o + 3 * bh);
+                const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + bh);
+                const int c2 = ld_col<kColNT>(c + o + 2 * bh), c3 = ld_col<kColNT>(c + o + 3 * bh);
+                s0 = fma(v0, x[c0], s0);
+                s1 = fma(v1, x[c1], s1);
+                s2 = fma(v2, x[c2], s2);
+                s3 = fma(v3, x[c3], s3);
+            } else {
+                for (int u = j; u < L; ++u) {
+                    const int64_t o = (int64_t)u * bh;
+                    s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
+                }
+            }
+            j += 4;
+        }
+        // the rows still open, one at a time across the whole wave
+        const int lane = threadIdx.x & 63;
+        uint64_t open = __ballot(j < L);
+        while (open) {
+            const int l = __builtin_ctzll(open);
+            open &= open - 1;
+            const int Ll = __builtin_amdgcn_readlane(L, l);
+            const int64_t il = i - lane + l;  // the wave's rows are consecutive
+            const int64_t bl = (il / bh) * bstride + il % bh;
+            T p0 = 0, p1 = 0;
+            for (int q0 = j + lane; q0 - lane < Ll; q0 += 64 * kEllCoopUnroll) {
+                T vv[kEllCoopUnroll];
+                int cc[kEllCoopUnroll];
+#pragma unroll
+                for (int u = 0; u < kEllCoopUnroll; ++u) {
+                    const int q = q0 + 64 * u;
+                    vv[u] = q < Ll ? ld_nt(val + bl + (int64_t)q * bh) : T(0);
+                    cc[u] = q < Ll ? ld_col<kColNT>(col + bl + (int64_t)q * bh) : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < kEllCoopUnroll; ++u) {
+                    const T xv = q0 + 64 * u < Ll ? x[cc[u]] : T(0);
+                    if (u & 1)
+                        p1 = fma(vv[u], xv, p1);
+                    else
+                        p0 = fma(vv[u], xv, p0);
+                }
+            }
+            const T tot = lane_read(group_sum<64>(p0 + p1), 0);
+            if (lane == l) s0 += tot;
+        }
     }
-    for (; j < L; ++j) {
-        const int64_t o = (int64_t)j * bh;
-        s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
-    }
+    if (!valid) return;
     const int64_t row = perm ? perm[i] : i;  // positions < n hold rows < n
     y[row] = axpby((s0 + s1) + (s2 + s3), alpha, beta, y + row);
 }

@@ -131,11 +131,11 @@ def test_traffic_record_checks(tmp_path):
     assert bench.kernels_of("hyb", {"x_window": 0, "tail_nnz": 3}) == "k_ell + k_tail<COO>"
     # the column-slice CSR kernel and its traffic record
     xb = {"csr_kernel": "xblock", "x_window": 0, "subwave": 1, "csr_rows": 1}
-    assert bench.kernel_bases("csr", xb) == {"k_xblk", "k_xblk_carry", "k_xblk_sum"}
-    assert bench.kernels_of("csr", xb) == "k_xblk + k_xblk_carry + k_xblk_sum"
-    rec["w:f64:csr"].append({"kernels": ["k_xblk<double>", "k_xblk_carry<double>",
-                                         "k_xblk_sum<double>"], "bytes_per_launch": 55,
-                             "sources": srcs, "sha256": h.hexdigest()})
+    assert bench.kernel_bases("csr", xb) == {"k_scale", "k_xblk"}
+    assert bench.kernels_of("csr", xb) == "k_scale + k_xblk"
+    rec["w:f64:csr"][0]["kernels"] = ["k_scale<double>", "k_tail_win<double, false>"]
+    rec["w:f64:csr"].append({"kernels": ["k_scale<double>", "k_xblk<double>"],
+                             "bytes_per_launch": 55, "sources": srcs, "sha256": h.hexdigest()})
     p.write_text(json.dumps(rec))
     assert bench.traffic_for("w:f64:csr", bench.kernel_bases("csr", xb), str(p)) == 55
 
@@ -151,8 +151,7 @@ def test_counter_summary(tmp_path, monkeypatch):
     rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
     disp = 0
     for rep in range(3):       # three applies, then the last one is kept
-        for k in ("spmv::k_xblk<double>(x)", "spmv::k_xblk_carry<double>(x)",
-                  "spmv::k_xblk_sum<double>(x)"):
+        for k in ("spmv::k_scale<double>(x)", "spmv::k_xblk<double>(x)"):
             disp += 1
             for c in ("A", "B"):
                 rows.append('%d,"%s",%s,%d' % (disp, k, c, 10 * rep + (c == "B")))
@@ -163,7 +162,63 @@ def test_counter_summary(tmp_path, monkeypatch):
     ps.counters_main()
     text = (tmp_path / "profiles" / "spmv_w_f64_csr-xblock_counters.md").read_text()
     body = [l for l in text.splitlines() if l.startswith("| k_")]
-    assert [l.split(" | ")[0] for l in body] == ["| k_xblk<double>", "| k_xblk_carry<double>",
-                                               "| k_xblk_sum<double>"]
+    assert [l.split(" | ")[0] for l in body] == ["| k_scale<double>", "| k_xblk<double>"]
     assert all(l.endswith("| 20 | 21 |") for l in body)      # the last apply's values
     assert "--formats csr --csr-kernel xblock" in text
+
+
+def _trace(names):
+    """rocprofv3 kernel-trace rows: dispatch i runs 10 * (i + 1) us."""
+    rows, t = [], 0
+    for i, k in enumerate(names):
+        d = 10_000 * (i + 1)
+        rows.append({"Kernel_Name": "void spmv::%s(int)" % k, "Start_Timestamp": str(t),
+                     "End_Timestamp": str(t + d)})
+        t += d + 1000
+    return rows
+
+
+C4_KERNELS = {"csr": "k_scale + k_xblk", "sell64": "k_sell (+ k_sell_chunks)",
+              "hyb": "k_ell + k_tail<COO>", "hec": "k_ell + k_tail<CSR>"}
+C4_STEP = ["k_scale<double>", "k_xblk<double>", "k_sell<double, true>",
+           "k_sell_chunks<double, true>", "k_ell<double, true>", "k_tail<double, true>",
+           "k_ell<double, true>", "k_tail<double, false>"]
+
+
+def test_profile_attribution_c4_step_with_stray_dispatch():
+    """Each format gets its own kernels: the column-slice CSR apply (two
+    kernels), SELL with its chunk kernel, HYB's COO and HEC's CSR tail; a stray
+    dispatch before the first step is skipped, not counted as an apply."""
+    import profile_summary as ps
+    fmts = ["csr", "sell64", "hyb", "hec"]
+    trace = _trace(["k_tail<double, false>"] + C4_STEP * 3)
+    out = ps.per_format_applies(trace, fmts, C4_KERNELS)
+    assert [len(out[f]) for f in fmts] == [3, 3, 3, 3]
+    assert out["csr"][0][0] == "k_scale<double> + k_xblk<double>"
+    assert out["sell64"][0][0] == "k_sell<double, true> + k_sell_chunks<double, true>"
+    assert out["hyb"][0][0] == "k_ell<double, true> + k_tail<double, true>"
+    assert out["hec"][0][0] == "k_ell<double, true> + k_tail<double, false>"
+    # durations: dispatch i takes 10 (i + 1) us; the stray one is dispatch 0
+    assert out["csr"][0][1] == 20 + 30 and out["hec"][0][1] == 80 + 90
+
+
+def test_profile_attribution_trace_from_mid_step():
+    """A trace that begins inside a step (here at HYB's apply) is attributed
+    from its first whole apply on; the half apply before it is dropped."""
+    import profile_summary as ps
+    fmts = ["csr", "sell64", "hyb", "hec"]
+    trace = _trace(["k_sell_chunks<double, true>"] + C4_STEP[4:] + C4_STEP * 2)
+    out = ps.per_format_applies(trace, fmts, C4_KERNELS)
+    assert [len(out[f]) for f in fmts] == [2, 2, 3, 3]
+    assert all(k == "k_ell<double, true> + k_tail<double, true>" for k, _ in out["hyb"])
+    assert all(k == "k_scale<double> + k_xblk<double>" for k, _ in out["csr"])
+    # the C3 case: ELL-R, HYB and HEC all launch k_ell alone; step order decides
+    c3 = {"csr": "k_csr_staged<S=4>", "ellr": "k_ell", "sell64": "k_sell (+ k_sell_chunks)",
+          "hyb": "k_ell", "hec": "k_ell"}
+    f5 = list(c3)
+    step = ["k_csr_staged<double, 4>", "k_ell<double, true>", "k_sell<double, true>",
+            "k_ell<double, true>", "k_ell<double, true>"]
+    out = ps.per_format_applies(_trace(step * 2), f5, c3)
+    assert [len(out[f]) for f in f5] == [2] * 5
+    assert out["csr"][0][0] == "k_csr_staged<double, 4>"
+    assert out["hec"][1][1] == 100
