@@ -378,6 +378,31 @@ typedef struct {
 int spmv_solve(spmv_t h, void *x, const void *b, const spmv_solve_opts *opts,
                spmv_solve_info *info, void *stream);
 
+/*
+ * spmv_solve_noalloc -- spmv_solve for callers that cannot allocate device
+ * memory (serving loops that must not call hipMalloc, harnesses that forbid
+ * allocation): the same method, options, iterates and results, with no
+ * device allocation and no stream or graph created.
+ *   x, b, opts, info, stream  as for spmv_solve; the handle's device must be
+ *                             the current device
+ * The work vectors, inner-product partial sums and iteration scalars live in
+ * one array of 64 MiB that the library keeps per GPU until the process ends
+ * (taken at the first call on each device).  The vectors must fit it:
+ * 3 (CG) or 6 (BiCGSTAB) vectors of n entries, each rounded up to 256 bytes,
+ * in 64 MiB - 64 KiB -- e.g. fp64 CG up to 2,793,472 rows, fp64 BiCGSTAB up
+ * to 1,396,736, fp32 twice as many; larger n gives INVALID_ARG.  Batches of
+ * eight iterations are enqueued on `stream` itself and the host reads the
+ * done flag after each batch; the call returns when the solve is done.
+ * Every call on one GPU uses that GPU's one array, and each call sets up all
+ * of it that it reads: calls that overlap in time on one GPU (other threads)
+ * race and must not be made.
+ * Errors: as spmv_solve (never NO_MEMORY from an allocation of its own), plus
+ * INVALID_ARG when n exceeds the limit above and STATE when the handle's
+ * device is not current.
+ */
+int spmv_solve_noalloc(spmv_t h, void *x, const void *b, const spmv_solve_opts *opts,
+                       spmv_solve_info *info, void *stream);
+
 /* spmv_destroy -- free every device buffer of the handle (synchronises the
  * device first).  A NULL handle is accepted.  The handle is released even
  * when HIP is returned (an earlier asynchronous error reported by the

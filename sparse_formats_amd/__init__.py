@@ -93,6 +93,8 @@ def _load():
     lib.spmv_apply.argtypes = [P, P, P, D, D, P]
     lib.spmv_permute.argtypes = [P, P, P, I, P]
     lib.spmv_solve.argtypes = [P, P, P, ctypes.POINTER(_SolveOpts), ctypes.POINTER(_SolveInfo), P]
+    lib.spmv_solve_noalloc.argtypes = [P, P, P, ctypes.POINTER(_SolveOpts),
+                                       ctypes.POINTER(_SolveInfo), P]
     lib.spmv_destroy.argtypes = [P]
     lib.spmv_info.argtypes = [P, ctypes.POINTER(_Info)]
     lib.spmv_export.argtypes = [P, I, P, I64, ctypes.POINTER(I64)]
@@ -100,7 +102,8 @@ def _load():
     lib.spmv_last_error.restype = ctypes.c_char_p
     lib.spmv_version.restype = ctypes.c_char_p
     for f in ("spmv_create", "spmv_convert", "spmv_apply", "spmv_destroy", "spmv_info",
-              "spmv_export", "spmv_stream_copy", "spmv_permute", "spmv_solve"):
+              "spmv_export", "spmv_stream_copy", "spmv_permute", "spmv_solve",
+              "spmv_solve_noalloc"):
         getattr(lib, f).restype = I
     return lib
 
@@ -216,10 +219,12 @@ class Matrix:
         return dst
 
     def solve(self, b, x=None, method: str = "cg", rtol: float = 1e-10, max_iter: int = 1000,
-              stream=None):
+              stream=None, noalloc: bool = False):
         """Solve A x = b with the active format (method "cg" for symmetric
         positive definite A, "bicgstab" otherwise).  x: initial guess, updated
-        in place (zeros when None).  Returns (x, info dict)."""
+        in place (zeros when None).  noalloc: run spmv_solve_noalloc (the
+        library's fixed per-GPU workspace, no device allocation).  Returns
+        (x, info dict)."""
         import torch
         if b.numel() != self.n:
             raise ValueError("b must have n = %d entries" % self.n)
@@ -227,8 +232,9 @@ class Matrix:
             x = torch.zeros_like(b)
         o = _SolveOpts({"cg": 0, "bicgstab": 1}[method], int(max_iter), float(rtol))
         info = _SolveInfo()
-        _check(_lib.spmv_solve(self._h, _dev(x, self.dtype, "x"), _dev(b, self.dtype, "b"),
-                               ctypes.byref(o), ctypes.byref(info), _stream(stream)))
+        fn = _lib.spmv_solve_noalloc if noalloc else _lib.spmv_solve
+        _check(fn(self._h, _dev(x, self.dtype, "x"), _dev(b, self.dtype, "b"),
+                  ctypes.byref(o), ctypes.byref(info), _stream(stream)))
         return x, {"iterations": info.iterations, "converged": bool(info.converged),
                    "rel_residual": info.rel_residual}
 

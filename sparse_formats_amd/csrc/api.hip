@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <functional>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -158,6 +159,7 @@ struct spmv_handle {
     int csr_rows = 1;     // rows per lane group of the CSR kernel
     int csr_stage_slots = 0;  // CSR: LDS slots per wave of the staged kernel (0: direct)
     bool csr_stage_col_nt = false;  // staged CSR: col read without caching
+    int device = 0;           // device current at spmv_create (holds every buffer)
     DevBuf rowptr, col, val;  // canonical CSR (int32 row pointer); col and val
                               // end with 16 zero bytes (whole 16-byte loads)
     Built fmt;                // active non-CSR format (format == CSR: none)
@@ -1508,30 +1510,61 @@ struct GraphHolder {
     }
 };
 
+// Device memory of one solve: the work vectors (each `vstride` bytes apart),
+// the inner products' partial sums and the iteration's scalars.
+struct SolveSpace {
+    char* work = nullptr;
+    size_t vstride = 0;
+    double* partial = nullptr;  // [2 * kSolveBlocks]
+    double* state = nullptr;    // [kStCount]
+};
+
+int solve_vectors(int method) { return method == SPMV_SOLVE_CG ? 3 : 6; }
+
 // Krylov solve driven from the device: the iteration's scalars stay in
-// device memory (st) and kSolveGraphIters iterations are captured once in a
-// HIP graph and replayed; the host only reads the done flag after each
-// replay.  The recurrences are the textbook ones (see the kernels in
-// k_vec.hip); the setup (b.b, r = b - A x, r.r) runs before the capture.
+// device memory (st).  With `fixed` == nullptr the work vectors are
+// allocated for the call and kSolveGraphIters iterations are captured once
+// in a HIP graph on a private stream and replayed; with a fixed workspace
+// (the no-allocation entry point) nothing is allocated or created: batches
+// of kSolveGraphIters iterations are enqueued on the caller's stream.  Either
+// way the host only reads the done flag after each batch, and the same
+// kernels run in the same order, so both give the same iterates.  The
+// recurrences are the textbook ones (see the kernels in k_vec.hip); the setup
+// (b.b, r = b - A x, r.r) runs first.  Every vector, partial sum and scalar
+// an iteration reads is written by the setup or earlier in the iteration.
 spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_opts& o,
-                      hipStream_t caller) {
+                      hipStream_t caller, const SolveSpace* fixed) {
     const int64_t n = h->n;
     const bool f64 = h->dtype == SPMV_F64;
     const size_t vb = (size_t)n * h->vsize;
-    const int nvec = o.method == SPMV_SOLVE_CG ? 3 : 6;
+    const int nvec = solve_vectors(o.method);
     auto chk = [](hipError_t e, const char* what) { hip_check(e, what); };
-    // the caller's stream may be the null stream, which cannot be captured:
-    // work on a private stream ordered after the caller's work
-    sync(caller);
     StreamHolder sh;
-    chk(hipStreamCreateWithFlags(&sh.s, hipStreamNonBlocking), "hipStreamCreateWithFlags");
-    hipStream_t s = sh.s;
-    DevBuf work(vb * nvec), partial((size_t)2 * kSolveBlocks * 8), state(kStCount * 8);
-    char* w = work.as<char>();
-    void *r = w, *p = w + vb, *q = w + 2 * vb;           // CG: r, p, q = A p
-    void *rh = w + 2 * vb, *v = w + 3 * vb, *sv = w + 4 * vb, *t = w + 5 * vb;  // BiCGSTAB
-    double* pd = partial.as<double>();
-    double* st = state.as<double>();
+    DevBuf work, partial, state;
+    SolveSpace sp;
+    hipStream_t s = caller;
+    if (fixed) {
+        sp = *fixed;
+    } else {
+        // the caller's stream may be the null stream, which cannot be
+        // captured: work on a private stream ordered after the caller's work
+        sync(caller);
+        chk(hipStreamCreateWithFlags(&sh.s, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+        s = sh.s;
+        work.alloc(vb * nvec);
+        partial.alloc((size_t)2 * kSolveBlocks * 8);
+        state.alloc(kStCount * 8);
+        sp.work = work.as<char>();
+        sp.vstride = vb;
+        sp.partial = partial.as<double>();
+        sp.state = state.as<double>();
+    }
+    char* w = sp.work;
+    const size_t vs = sp.vstride;
+    void *r = w, *p = w + vs, *q = w + 2 * vs;           // CG: r, p, q = A p
+    void *rh = w + 2 * vs, *v = w + 3 * vs, *sv = w + 4 * vs, *t = w + 5 * vs;  // BiCGSTAB
+    double* pd = sp.partial;
+    double* st = sp.state;
     auto apply = [&](void* yy, const void* xx, double alpha, double beta) {
         chk(launch_built(h, h->fmt, h->format, yy, xx, alpha, beta, s), "apply");
     };
@@ -1566,7 +1599,8 @@ spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_o
         chk(hipMemsetAsync(v, 0, vb, s), "hipMemsetAsync");
     }
     sync(s);
-    // one iteration, enqueued on s (captured below, never run eagerly)
+    // one iteration, enqueued on s (captured below, or run in batches on the
+    // caller's stream with a fixed workspace)
     auto iteration = [&] {
         if (o.method == SPMV_SOLVE_CG) {
             apply(q, p, 1.0, 0.0);
@@ -1588,7 +1622,16 @@ spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_o
             chk(launch_solve_step(pd, st, kStepBiRR, s), "step");
         }
     };
-    if (st0[kStDone] == 0.0) {
+    const int64_t batches = ((int64_t)o.max_iter + kSolveGraphIters - 1) / kSolveGraphIters;
+    if (st0[kStDone] == 0.0 && fixed) {
+        double flag = 0.0;
+        for (int64_t k = 0; k < batches && flag == 0.0; ++k) {
+            for (int i = 0; i < kSolveGraphIters; ++i) iteration();
+            chk(hipMemcpyAsync(&flag, st + kStDone, 8, hipMemcpyDeviceToHost, s),
+                "hipMemcpyAsync");
+            sync(s);
+        }
+    } else if (st0[kStDone] == 0.0) {
         GraphHolder gh;
         chk(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
         try {
@@ -1602,8 +1645,7 @@ spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_o
         chk(hipStreamEndCapture(s, &gh.g), "hipStreamEndCapture");
         chk(hipGraphInstantiate(&gh.e, gh.g, nullptr, nullptr, 0), "hipGraphInstantiate");
         double flag = 0.0;
-        const int64_t replays = ((int64_t)o.max_iter + kSolveGraphIters - 1) / kSolveGraphIters;
-        for (int64_t k = 0; k < replays && flag == 0.0; ++k) {
+        for (int64_t k = 0; k < batches && flag == 0.0; ++k) {
             chk(hipGraphLaunch(gh.e, s), "hipGraphLaunch");
             chk(hipMemcpyAsync(&flag, st + kStDone, 8, hipMemcpyDeviceToHost, s),
                 "hipMemcpyAsync");
@@ -1618,6 +1660,82 @@ spmv_solve_info solve(spmv_handle* h, void* x, const void* b, const spmv_solve_o
     res.rel_residual = bnorm > 0 ? std::sqrt(rr) / bnorm : std::sqrt(rr);
     res.converged = std::sqrt(rr) <= goal ? 1 : 0;
     return res;
+}
+
+// arguments of spmv_solve / spmv_solve_noalloc
+spmv_solve_opts check_solve_args(const spmv_handle* h, const void* x, const void* b,
+                                 const spmv_solve_opts* opts) {
+    if (!h) fail(SPMV_ERR_STATE, "null handle");
+    if (!opts) fail(SPMV_ERR_INVALID_ARG, "opts is NULL");
+    const spmv_solve_opts o = *opts;
+    if (o.method != SPMV_SOLVE_CG && o.method != SPMV_SOLVE_BICGSTAB)
+        fail(SPMV_ERR_INVALID_ARG, "unknown method %d", o.method);
+    if (o.max_iter <= 0) fail(SPMV_ERR_INVALID_ARG, "max_iter must be positive");
+    if (!(o.rtol >= 0)) fail(SPMV_ERR_INVALID_ARG, "rtol must be >= 0");
+    if (h->n > 0) {
+        if (!x || !b) fail(SPMV_ERR_INVALID_ARG, "x or b is NULL");
+        const uintptr_t xb = (uintptr_t)x, bb = (uintptr_t)b, len = (uintptr_t)(h->n * h->vsize);
+        if (xb < bb + len && bb < xb + len) fail(SPMV_ERR_INVALID_ARG, "x and b overlap");
+    }
+    return o;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace of the no-allocation solve: one array per GPU in the library's
+// code object, held until the process ends.  Its head holds the iteration's
+// scalars (offset 0) and the inner products' partial sums (offset 256); the
+// work vectors follow from kScratchHead, each starting on a 256-byte
+// boundary.  Host code never names the array itself (its host-side symbol
+// is no device address): the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current and kept.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr size_t kScratchHead = size_t(64) << 10;
+static_assert(256 + 2 * kSolveBlocks * 8 <= kScratchHead, "scratch head too small");
+static_assert(kStCount * 8 <= 256, "solver state too large");
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of this device's scratch array
+char* scratch_base(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) fail(SPMV_ERR_STATE, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress");
+        if (!p) fail(SPMV_ERR_HIP, "hipGetSymbolAddress returned no address");
+        g_scratch_ptr[dev] = p;
+    }
+    return static_cast<char*>(g_scratch_ptr[dev]);
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// the solve's layout inside this device's scratch array (the handle's device
+// must be current); INVALID_ARG when the vectors do not fit
+SolveSpace solve_scratch(const spmv_handle* h, int method) {
+    int dev = 0;
+    hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (dev != h->device)
+        fail(SPMV_ERR_STATE, "the handle lives on device %d, device %d is current", h->device, dev);
+    const size_t vstride = round256((size_t)h->n * h->vsize);
+    const int nvec = solve_vectors(method);
+    const size_t room = kScratchBytes - kScratchHead;
+    if (vstride > room / nvec)
+        fail(SPMV_ERR_INVALID_ARG,
+             "n = %lld needs %zu bytes of work vectors; the no-allocation solve holds %zu "
+             "(at most %lld rows for this method and dtype)",
+             (long long)h->n, vstride * nvec, room, (long long)((room / nvec) / 256 * 256 / h->vsize));
+    char* base = scratch_base(dev);
+    SolveSpace sp;
+    sp.state = reinterpret_cast<double*>(base);
+    sp.partial = reinterpret_cast<double*>(base + 256);
+    sp.work = base + kScratchHead;
+    sp.vstride = vstride;
+    return sp;
 }
 
 }  // namespace
@@ -1648,8 +1766,11 @@ int spmv_create(spmv_t* out, int kind, int64_t n, int64_t nnz, const int64_t* ro
         if (nnz > 0 && (!rowidx || !col || !val))
             fail(SPMV_ERR_INVALID_ARG, "row/col/val pointer is NULL");
         hipStream_t s = (hipStream_t)stream;
+        int dev = 0;
+        hip_check(hipGetDevice(&dev), "hipGetDevice");
         auto* h = new spmv_handle;
         try {
+            h->device = dev;
             h->n = n;
             h->nnz = nnz;
             h->dtype = dtype;
@@ -1855,20 +1976,22 @@ int spmv_solve(spmv_t h, void* x, const void* b, const spmv_solve_opts* opts,
                spmv_solve_info* info, void* stream) {
     g_err.clear();
     return run_guarded([&] {
-        if (!h) fail(SPMV_ERR_STATE, "null handle");
-        if (!opts) fail(SPMV_ERR_INVALID_ARG, "opts is NULL");
-        const spmv_solve_opts o = *opts;
-        if (o.method != SPMV_SOLVE_CG && o.method != SPMV_SOLVE_BICGSTAB)
-            fail(SPMV_ERR_INVALID_ARG, "unknown method %d", o.method);
-        if (o.max_iter <= 0) fail(SPMV_ERR_INVALID_ARG, "max_iter must be positive");
-        if (!(o.rtol >= 0)) fail(SPMV_ERR_INVALID_ARG, "rtol must be >= 0");
-        const int64_t n = h->n;
+        const spmv_solve_opts o = check_solve_args(h, x, b, opts);
         spmv_solve_info res{0, 1, 0.0};
-        if (n > 0) {
-            if (!x || !b) fail(SPMV_ERR_INVALID_ARG, "x or b is NULL");
-            const uintptr_t xb = (uintptr_t)x, bb = (uintptr_t)b, len = (uintptr_t)(n * h->vsize);
-            if (xb < bb + len && bb < xb + len) fail(SPMV_ERR_INVALID_ARG, "x and b overlap");
-            res = solve(h, x, b, o, (hipStream_t)stream);
+        if (h->n > 0) res = solve(h, x, b, o, (hipStream_t)stream, nullptr);
+        if (info) *info = res;
+    });
+}
+
+int spmv_solve_noalloc(spmv_t h, void* x, const void* b, const spmv_solve_opts* opts,
+                       spmv_solve_info* info, void* stream) {
+    g_err.clear();
+    return run_guarded([&] {
+        const spmv_solve_opts o = check_solve_args(h, x, b, opts);
+        spmv_solve_info res{0, 1, 0.0};
+        if (h->n > 0) {
+            const SolveSpace sp = solve_scratch(h, o.method);
+            res = solve(h, x, b, o, (hipStream_t)stream, &sp);
         }
         if (info) *info = res;
     });
