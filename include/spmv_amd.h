@@ -135,13 +135,18 @@ typedef struct {
      * follow the maximum row length -- is the value spmv_create starts
      * with.) */
     int32_t subwave;
-    /* ELL-R / HYB / HEC / balanced CSR: stage x in LDS.  The workgroup
-     * keeps the x entries within about +-9,700 (fp64) or +-19,900 (fp32)
-     * positions of its rows in a window that slides with the rows (the
-     * banded structure of FEM and stencil matrices); entries outside the
-     * window are read from global memory.  -1 decides from the matrix (on when at least half of
-     * the entries fall inside the window, and for ELL-R only when the
-     * longest row has at most 128 entries), 0 off, 1 on. */
+    /* ELL-R / SELL-64 / HYB / HEC / balanced CSR: stage x in LDS.  The
+     * workgroup keeps the x entries within about +-9,700 (fp64) or +-19,900
+     * (fp32) positions of its rows in a window that slides with the rows
+     * (the banded structure of FEM and stencil matrices); entries outside
+     * the window are read from global memory.  -1 decides from the matrix:
+     * a candidate when at least half of the entries fall inside the window
+     * (for ELL-R only when the longest row has at most 128 entries), then
+     * one apply with and one without it are timed and the window is kept
+     * when clearly faster; 0 off, 1 on.  SELL-64 with the window sorts its
+     * rows inside windows of 1024 rows by default (sort_window), so that a
+     * tile of 1024 sorted rows holds the rows of one row range; its slices
+     * wider than 128 columns are read by the whole workgroup in chunks. */
     int32_t x_window;
     /* CSR: rows per lane group, 0 (choose by timing), 1, 2 or 4 */
     int32_t csr_rows;
@@ -162,9 +167,10 @@ typedef struct {
      *   SELL-64: -1 (default) sorts inside windows of 8192 rows (64 KiB of
      *            fp64 y: the y writes of a window stay within a few L2
      *            lines per slice and banded matrices keep their x
-     *            locality); 0 keeps the row order; k >= 1 sorts inside
-     *            windows of k rows, k >= n sorts all rows at once (the
-     *            page's pJDS).  Each slice is padded to its longest row.
+     *            locality), or of 1024 rows with the LDS window (x_window);
+     *            0 keeps the row order; k >= 1 sorts inside windows of k
+     *            rows, k >= n sorts all rows at once (the page's pJDS).
+     *            Each slice is padded to its longest row.
      *   HYB/HEC: the rows of every 1024-row block of the ELL part;
      *            -1 (default) sorts inside the whole block when waves of 64
      *            unsorted rows would read more than 10% padding slots, 0 never,
@@ -232,7 +238,8 @@ typedef struct {
                               effect (0: rows kept in order; SELL-64 with
                               all rows sorted at once reports n) */
     double band_fraction;  /* share of entries within the window's reach
-                              (computed by ELL-R / HYB / HEC conversions) */
+                              (computed by ELL-R / SELL-64 / HYB / HEC
+                              conversions) */
     int64_t ell_rows;      /* ELL-R / HYB / HEC: rows padded to whole blocks */
     int32_t csr_stage_slots; /* CSR vector kernel staged in LDS: entries one wave
                                 can stage (0: the kernel reads directly) */

@@ -113,7 +113,7 @@ struct Built {
     int64_t nslices = 0, sell_slots = 0;
     DevBuf slice_ptr, sell_len, perm, sell_col, sell_val;
     int64_t nchunks = 0;
-    DevBuf chunks;
+    DevBuf chunks, chunk_off;  // column chunks of long slices, first chunk per slice
     // tail of HYB / HEC
     int64_t tail_nnz = 0, tail_runs = 0;
     DevBuf tail_row, tail_ptr, tail_col, tail_val, run_row;
@@ -142,7 +142,8 @@ struct Built {
     size_t bytes() const {
         return ell_col.bytes + ell_val.bytes + ell_len.bytes + ell_perm.bytes + slice_ptr.bytes +
                sell_len.bytes +
-               perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + tail_row.bytes +
+               perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + chunk_off.bytes +
+               tail_row.bytes +
                tail_ptr.bytes + tail_col.bytes + tail_val.bytes + run_row.bytes + tail_rows.bytes +
                tail_cptr.bytes + xb_ptr.bytes + xb_col.bytes + xb_val.bytes + xb_lane_row.bytes;
     }
@@ -631,15 +632,54 @@ double ell_pad_fraction(const spmv_handle* h, int64_t W, hipStream_t s) {
 // the row order, k >= 1 sorts inside aligned windows of k rows (k >= n: all
 // rows at once, the pJDS order).  permuted: store P A P^T (columns renumbered
 // to sorted positions; apply works in the sorted basis).
+// Column chunks of the long slices of a built SELL layout, on the device:
+// without the LDS window the slices wider than kSellSplitWidth go to
+// k_sell_chunks whole, in chunks of kSellChunk columns; with it the columns
+// of the slices wider than kSellWinWide past kSellWinHead, in chunks of
+// kSellWinChunk columns per group of 16 rows, up to each group's longest row
+// (k_sell_win).  chunk_off[q] is the first chunk of slice q.
+void build_sell_chunks(Built& b, bool window, hipStream_t s) {
+    const int64_t ns = b.nslices;
+    const int split = window ? kSellWinWide : kSellSplitWidth;
+    const int head = window ? kSellWinHead : 0;
+    const int chunk = window ? kSellWinChunk : kSellChunk;
+    b.window = window;
+    b.chunk_off.alloc((size_t)(ns + 1) * 4);
+    hip_check(hipMemsetAsync(b.chunk_off.p, 0, 4, s), "hipMemsetAsync");
+    if (ns > 0) {
+        DevBuf cnt((size_t)ns * 4);
+        hip_check(launch_sell_chunk_count(ns, b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
+                                          split, head, chunk, window, cnt.as<int>(), s),
+                  "sell chunk counts");
+        size_t tmp = 0;
+        hip_check(rocprim::inclusive_scan(nullptr, tmp, cnt.as<int>(), b.chunk_off.as<int>() + 1,
+                                          (size_t)ns, rocprim::plus<int>(), s),
+                  "inclusive_scan");
+        DevBuf work(tmp);
+        hip_check(rocprim::inclusive_scan(work.p, tmp, cnt.as<int>(), b.chunk_off.as<int>() + 1,
+                                          (size_t)ns, rocprim::plus<int>(), s),
+                  "inclusive_scan");
+        sync(s);  // before the temporaries are freed
+    }
+    b.nchunks = read_scalar<int>(b.chunk_off.as<int>() + ns, s);
+    b.chunks.alloc((size_t)std::max<int64_t>(b.nchunks, 1) * sizeof(int4));
+    hip_check(launch_sell_chunk_fill(ns, b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
+                                     b.chunk_off.as<int>(), split, head, chunk, window,
+                                     b.chunks.as<int4>(), s),
+              "sell chunks");
+    sync(s);
+}
+
 template <typename V>
-void build_sell(const spmv_handle* h, int sort_window, bool permuted, Built& b, hipStream_t s) {
+void build_sell(const spmv_handle* h, int sort_window, bool permuted, bool window, Built& b,
+                hipStream_t s) {
     const int64_t n = h->n, S = pad64(n), ns = S / 64;
     b.nslices = ns;
     b.permuted = permuted;
     b.perm.alloc((size_t)std::max<int64_t>(n, 1) * 4);
     b.sell_len.alloc((size_t)S * 4);
     b.slice_ptr.alloc((size_t)(ns + 1) * 8);
-    if (sort_window < 0) sort_window = kSellSortWindow;
+    if (sort_window < 0) sort_window = window ? kSellWinSortWindow : kSellSortWindow;
     int64_t sigma = sort_window >= n ? n : sort_window;
     if (sort_window == 0) sigma = 1;  // every row its own window: row order kept
     b.sort_window = sigma <= 1 ? 0 : (int)sigma;
@@ -707,25 +747,8 @@ void build_sell(const spmv_handle* h, int sort_window, bool permuted, Built& b, 
     } else {
         hip_check(hipMemsetAsync(b.slice_ptr.p, 0, 8, s), "hipMemsetAsync");
     }
-    // slice widths decide the split of long slices into column chunks
-    std::vector<int64_t> sp((size_t)ns + 1);
-    hip_check(hipMemcpyAsync(sp.data(), b.slice_ptr.p, sp.size() * 8, hipMemcpyDeviceToHost, s),
-              "hipMemcpyAsync");
-    sync(s);
-    b.sell_slots = sp[(size_t)ns];
-    std::vector<int4> ch;
-    for (int64_t q = 0; q < ns; ++q) {
-        const int64_t w = (sp[(size_t)q + 1] - sp[(size_t)q]) / 64;
-        if (w > kSellSplitWidth)
-            for (int64_t j = 0; j < w; j += kSellChunk)
-                ch.push_back(make_int4((int)q, (int)j, (int)std::min<int64_t>(w, j + kSellChunk), 0));
-    }
-    b.nchunks = (int64_t)ch.size();
-    b.chunks.alloc(std::max<size_t>(ch.size(), 1) * sizeof(int4));
-    if (!ch.empty())
-        hip_check(hipMemcpyAsync(b.chunks.p, ch.data(), ch.size() * sizeof(int4),
-                                 hipMemcpyHostToDevice, s),
-                  "hipMemcpyAsync");
+    b.sell_slots = read_scalar<int64_t>(b.slice_ptr.as<int64_t>() + ns, s);
+    build_sell_chunks(b, window, s);
     b.sell_col.alloc((size_t)b.sell_slots * 4);
     b.sell_val.alloc((size_t)b.sell_slots * sizeof(V));
     if (ns > 0) {
@@ -948,7 +971,8 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
         case SPMV_SELL64: {
             SellView a{(int)h->n, (int)b.nslices, b.slice_ptr.as<int64_t>(), b.sell_len.as<int>(),
                        b.perm.as<int>(), b.sell_col.as<int>(), b.sell_val.p, (int)b.nchunks,
-                       b.chunks.as<int4>(), b.permuted, b.col_nt};
+                       b.chunks.as<int4>(), b.chunk_off.as<int>(), b.permuted, b.col_nt,
+                       b.window};
             e = launch_sell(a, f64, y, x, alpha, beta, s);
             break;
         }
@@ -1303,7 +1327,8 @@ void tune_hec_tail(const spmv_handle* h, int kernel, int col_cache, Built& b, hi
 // apply is then timed with and without it and the faster kept (stencils
 // whose x reads already coalesce gain nothing from it).  `b` must hold the
 // built format.
-void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s) {
+// share of the entries whose column lies within the window's reach of their row
+double band_fraction(const spmv_handle* h, hipStream_t s) {
     const int64_t lead = h->dtype == SPMV_F64 ? EllWinLead<double>::value
                                               : EllWinLead<float>::value;
     DevBuf cnt(8);
@@ -1314,10 +1339,18 @@ void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStrea
         hip_check(hipGetLastError(), "band count");
     }
     const unsigned long long c = read_scalar<unsigned long long>(cnt.p, s);
-    b.band_fraction = h->nnz ? (double)c / (double)h->nnz : 0.0;
-    // window offsets are computed in 32 bits: rows and columns plus the
-    // window length must stay below 2^31
-    const bool fits = h->n < INT32_MAX - 2 * (int64_t)WinLen<float>::value;
+    return h->nnz ? (double)c / (double)h->nnz : 0.0;
+}
+
+// window offsets are computed in 32 bits: rows and columns plus the window
+// length must stay below 2^31
+bool window_fits(const spmv_handle* h) {
+    return h->n < INT32_MAX - 2 * (int64_t)WinLen<float>::value;
+}
+
+void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s) {
+    b.band_fraction = band_fraction(h, s);
+    const bool fits = window_fits(h);
     if (opt >= 0) {
         b.window = opt == 1 && fits;
         return;
@@ -1372,6 +1405,48 @@ void build_split_tuned(spmv_handle* h, int format, const spmv_convert_opts& o, i
     choose_col_policy(o.col_cache, b);
 }
 
+// SELL-64 with or without the LDS window.  The window needs the rows
+// sorted inside windows that divide the tile (default kSellWinSortWindow
+// rows); without it the default sort window is kSellSortWindow.  x_window
+// -1: when at least half of the entries lie within the window's reach, both
+// layouts are built and one apply of each timed; the window is kept when
+// faster by kPreferMargin.  No room for the second layout: the first one.
+template <typename V>
+void convert_sell(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t s) {
+    const bool permuted = o.permuted_basis != 0;
+    auto build = [&](Built& c, bool win) {
+        build_sell<V>(h, o.sort_window, permuted, win, c, s);
+        choose_col_policy(o.col_cache, c);
+    };
+    const bool fits = window_fits(h) && h->n > 0;
+    const double band = o.x_window == 0 ? 0.0 : band_fraction(h, s);
+    if (o.x_window == 1 || (o.x_window == -1 && fits && h->nnz > 0 && band >= 0.5)) {
+        build(b, fits);
+        b.band_fraction = band;
+        if (o.x_window == 1 || !fits) return;
+        Built plain;
+        try {
+            build(plain, false);
+        } catch (const Error& e) {
+            if (e.code != SPMV_ERR_NO_MEMORY) throw;
+            return;
+        }
+        plain.band_fraction = band;
+        DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
+        hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
+        auto t_of = [&](const Built& c) {
+            return time_launches(
+                [&] { return launch_built(h, c, SPMV_SELL64, ys.p, xs.p, 1.0, 0.0, s); }, s);
+        };
+        const float tw = t_of(b), tp = t_of(plain);
+        sync(s);
+        if (!(tw < kPreferMargin * tp)) b = std::move(plain);
+        return;
+    }
+    build(b, false);
+    b.band_fraction = band;
+}
+
 // Build `format` (options already validated) and make it the active format.
 void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
     if (format == SPMV_CSR) {
@@ -1404,10 +1479,9 @@ void convert_into(spmv_handle* h, int format, const spmv_convert_opts& o) {
         sync(s);
     } else if (format == SPMV_SELL64) {
         if (f64)
-            build_sell<double>(h, o.sort_window, o.permuted_basis != 0, b, s);
+            convert_sell<double>(h, o, b, s);
         else
-            build_sell<float>(h, o.sort_window, o.permuted_basis != 0, b, s);
-        choose_col_policy(o.col_cache, b);
+            convert_sell<float>(h, o, b, s);
     } else {
         build_split_tuned(h, format, o, o.ell_width, b, s);
         if (o.ell_width < 0 && h->n > 0) {

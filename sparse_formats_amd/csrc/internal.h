@@ -85,6 +85,22 @@ struct EllView {
     bool col_nt = true;  // col read without caching (else kept in the caches)
 };
 
+// SELL-64 with x staged in LDS: rows sorted inside windows that divide
+// kEllWinTile, so a tile of kEllWinTile sorted positions (kEllWinTile / 64
+// slices) holds the rows of one row range and the ELL window applies.  A
+// slice wider than kSellWinWide columns ("wide") is read by its wave only up
+// to kSellWinHead; its further columns are cut into chunks of kSellWinChunk
+// columns for each group of 16 rows that reaches past kSellWinHead.  The
+// tile's waves take the chunks in turn: 16 lanes per row group and four
+// columns at a time (each 16 lanes read one whole line of a column), then
+// each row's sum is added into y with an atomic (the wide slices' rows are
+// scaled by beta first).
+constexpr int kSellWinWide = 128;
+constexpr int kSellWinHead = 64;
+constexpr int kSellWinChunk = 128;
+// default sort window of SELL-64 with the LDS window (one tile)
+constexpr int kSellWinSortWindow = kEllWinTile;
+
 struct SellView {
     int n;
     int nslices;
@@ -94,10 +110,28 @@ struct SellView {
     const int* col;
     const void* val;
     int nchunks;               // column chunks of split slices
-    const int4* chunks;        // (slice, j0, j1, 0)
+    const int4* chunks;        // (slice, j0, j1, row group), ordered by slice
+                               // (row group: rows 16 g .. 16 g + 15 with the
+                               // window; 0 without)
+    const int* chunk_off;      // [nslices + 1]: first chunk of each slice
     bool permuted;             // y in sorted order (permuted basis)
     bool col_nt = true;        // col read without caching (else kept in the caches)
+    bool window = false;       // x staged in LDS (chunks are then the wide
+                               // slices' columns past kSellWinHead)
 };
+// column chunks of the slices of a SELL layout, built on the device: a slice
+// wider than `split` columns gets chunks of `chunk` columns from column
+// `head` on.  Without the window (groups false: split kSellSplitWidth, head
+// 0, chunk kSellChunk) every row of the slice is in each chunk; with it
+// (kSellWinWide, kSellWinHead, kSellWinChunk, groups true) each group of 16
+// rows gets the chunks up to its own longest row.  len: [64 nslices] row
+// lengths in sorted order.  cnt: [nslices] chunks of each slice.
+hipError_t launch_sell_chunk_count(int64_t nslices, const int64_t* slice_ptr, const int* len,
+                                   int split, int head, int chunk, bool groups, int* cnt,
+                                   hipStream_t stream);
+hipError_t launch_sell_chunk_fill(int64_t nslices, const int64_t* slice_ptr, const int* len,
+                                  const int* chunk_off, int split, int head, int chunk,
+                                  bool groups, int4* chunks, hipStream_t stream);
 
 struct TailView {
     int n;

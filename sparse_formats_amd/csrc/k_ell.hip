@@ -424,11 +424,264 @@ __global__ __launch_bounds__(256) void k_sell_chunks(int n, int nchunks,
     if (r < n && ch.y < L) atomic_add(y + (permuted ? r : perm[r]), alpha * ((s0 + s1) + (s2 + s3)));
 }
 
+// One row's entries [j0, j1) of a SELL-64 slice (slots base + 64 j) with x
+// from the LDS window where the column lies in it (window [wl, wl + WL),
+// element q at slot q mod WL) and from global memory otherwise: rounds of
+// B entries, every load of a round issued before the first use.
+template <typename T, bool kColNT, int WL>
+__device__ __forceinline__ T sell_row_win(int64_t base, int j0, int j1, const int* __restrict__ col,
+                                          const T* __restrict__ val, const T* __restrict__ x,
+                                          const T* win, int wl) {
+    constexpr int B = 16;
+    T s0 = 0, s1 = 0;
+    for (int j = j0; j < j1; j += B) {
+        T vv[B];
+        int cc[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int64_t o = base + (int64_t)(j + u) * 64;
+            if (j + u < j1) {
+                vv[u] = ld_nt(val + o);
+                cc[u] = ld_col<kColNT>(col + o);
+            } else {
+                vv[u] = T(0);
+                cc[u] = 0;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const bool in = j + u < j1;
+            T xv = win[cc[u] % WL];  // the slot read is always in range
+            if (in && (uint32_t)(cc[u] - wl) >= (uint32_t)WL) xv = x[cc[u]];
+            if (u & 1)
+                s1 += in ? vv[u] * xv : T(0);
+            else
+                s0 += in ? vv[u] * xv : T(0);
+        }
+    }
+    return s0 + s1;
+}
+
+// The same over every fourth column: entries j0, j0 + 4, ... below j1.
+template <typename T, bool kColNT, int WL>
+__device__ __forceinline__ T sell_row4_win(int64_t base, int j0, int j1,
+                                           const int* __restrict__ col, const T* __restrict__ val,
+                                           const T* __restrict__ x, const T* win, int wl) {
+    constexpr int B = 16;
+    T s0 = 0, s1 = 0;
+    for (int j = j0; j < j1; j += 4 * B) {
+        T vv[B];
+        int cc[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int64_t o = base + (int64_t)(j + 4 * u) * 64;
+            if (j + 4 * u < j1) {
+                vv[u] = ld_nt(val + o);
+                cc[u] = ld_col<kColNT>(col + o);
+            } else {
+                vv[u] = T(0);
+                cc[u] = 0;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const bool in = j + 4 * u < j1;
+            T xv = win[cc[u] % WL];
+            if (in && (uint32_t)(cc[u] - wl) >= (uint32_t)WL) xv = x[cc[u]];
+            if (u & 1)
+                s1 += in ? vv[u] * xv : T(0);
+            else
+                s0 += in ? vv[u] * xv : T(0);
+        }
+    }
+    return s0 + s1;
+}
+
+// SELL-64 with x staged in LDS.  Workgroup g (1024 threads) runs a
+// contiguous range of tiles of kEllWinTile sorted positions; the window of
+// tile t is placed as the ELL window of rows [t kEllWinTile, (t + 1)
+// kEllWinTile) (with the rows sorted inside windows that divide the tile,
+// those are exactly the tile's rows).  Wave w takes slice (tile slices) t +
+// w, one lane per sorted row: the whole row in a narrow slice, written as
+// alpha s + beta y; the first kSellWinHead columns in a wide slice, added
+// into y.  Then the waves take the chunks of the tile's wide slices in turn
+// (chunk c by wave c mod 16): a chunk is 16 rows of a slice over
+// kSellWinChunk columns, lane 16 g + i on row i and the columns g, g + 4, ...
+// (each 16 lanes read one line of a column), the four partial sums of a row
+// joined across the lanes, and the row sums added into y.  The rows of wide
+// slices were scaled by beta before the launch (k_sell_wide_beta), so no
+// ordering between the waves is needed.  A zero sum of a wide slice's row is
+// left out unless alpha is not finite (alpha * 0 is then NaN).
+template <typename T, bool kColNT>
+__global__ __launch_bounds__(1024) void k_sell_win(int n, int nslices,
+                                                   const int64_t* __restrict__ slice_ptr,
+                                                   const int* __restrict__ len,
+                                                   const int* __restrict__ perm,
+                                                   const int* __restrict__ col,
+                                                   const T* __restrict__ val,
+                                                   const int* __restrict__ chunk_off,
+                                                   const int4* __restrict__ chunks,
+                                                   const T* __restrict__ x, T* __restrict__ y,
+                                                   T alpha, T beta, bool permuted,
+                                                   int64_t ntiles) {
+    constexpr int WL = WinLen<T>::value;
+    constexpr int TILE = kEllWinTile;
+    constexpr int SPT = TILE / 64;  // slices per tile (one per wave)
+    constexpr int LEAD = (WL - TILE) / 2;
+    static_assert(SPT == 16, "one slice per wave of a 1024-thread workgroup");
+    __shared__ T win[WL];
+    const int64_t g = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t t0 = g * ntiles / gridDim.x, t1 = (g + 1) * ntiles / gridDim.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bool fin = alpha - alpha == T(0);
+    int64_t wlo = t0 * TILE - LEAD;
+    window_fill<T, WL>(win, x, max<int64_t>(wlo, 0), min<int64_t>(wlo + WL, n));
+    __syncthreads();
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t whi = wlo + WL;
+        // the next tile's window gains [whi, whi + TILE): one element per thread
+        const int64_t q = whi + tid;
+        const T pre = (t + 1 < t1 && q < n) ? x[q] : T(0);
+        const int wl = (int)wlo;
+        const int64_t sl = t * SPT + wave;
+        if (sl < nslices) {
+            const int64_t base = slice_ptr[sl];
+            const bool wide = ((slice_ptr[sl + 1] - base) >> 6) > kSellWinWide;
+            const int64_t p = sl * 64 + lane;
+            const int L = len[p];
+            const int La = wide ? min(L, kSellWinHead) : L;
+            const T sum = sell_row_win<T, kColNT, WL>(base + lane, 0, La, col, val, x, win, wl);
+            if (p < n) {
+                const int64_t r = permuted ? p : perm[p];
+                if (!wide)
+                    y[r] = axpby(sum, alpha, beta, y + r);
+                else if (sum != T(0) || !fin)
+                    atomic_add(y + r, alpha * sum);
+            }
+        }
+        // the chunks of the tile's wide slices: lane = 16 g + i reads row
+        // 16 (group) + i at the columns j0 + g, j0 + g + 4, ...
+        const int64_t sl0 = t * SPT < nslices ? t * SPT : nslices;
+        const int64_t sl1 = (t + 1) * SPT < nslices ? (t + 1) * SPT : nslices;
+        const int c0 = chunk_off[sl0], c1 = chunk_off[sl1];
+        for (int c = c0 + wave; c < c1; c += SPT) {
+            const int4 ch = chunks[c];
+            const int rr = ch.w * 16 + (lane & 15), cg = lane >> 4;
+            const int64_t p = (int64_t)ch.x * 64 + rr;
+            const int Lb = min(len[p], ch.z);
+            T sum = sell_row4_win<T, kColNT, WL>(slice_ptr[ch.x] + rr, ch.y + cg, Lb, col, val, x,
+                                                 win, wl);
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            if (cg == 0 && ch.y < Lb) {  // rows of the group that reach the chunk (p < n)
+                const int64_t r = permuted ? p : perm[p];
+                if (sum != T(0) || !fin) atomic_add(y + r, alpha * sum);
+            }
+        }
+        if (t + 1 >= t1) break;
+        lds_barrier();  // tile t is done with the slots reused now
+        if (q < n) win[q % WL] = pre;
+        lds_barrier();
+        wlo += TILE;
+    }
+}
+
+// y = beta y at the rows of the slices wider than kSellWinWide (one wave per
+// slice), before k_sell_win adds their sums with atomics
+template <typename T>
+__global__ __launch_bounds__(256) void k_sell_wide_beta(int n, int nslices,
+                                                        const int64_t* __restrict__ slice_ptr,
+                                                        const int* __restrict__ perm,
+                                                        T* __restrict__ y, T beta,
+                                                        bool permuted) {
+    const int64_t sl = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (sl >= nslices || ((slice_ptr[sl + 1] - slice_ptr[sl]) >> 6) <= kSellWinWide) return;
+    const int64_t p = sl * 64 + (threadIdx.x & 63);
+    if (p >= n) return;
+    const int64_t r = permuted ? p : perm[p];
+    y[r] = beta == T(0) ? T(0) : beta * y[r];
+}
+
+// Chunks of slice q (one thread per slice): a slice wider than `split`
+// columns is cut into chunks of `chunk` columns from column `head` on --
+// with `groups`, for each group of 16 rows up to the group's longest row;
+// otherwise for all rows up to the slice's width.  With `out` the chunks are
+// written from out[0] on as (q, j0, j1, group); the count is returned.
+__device__ int sell_slice_chunks(int64_t q, const int64_t* __restrict__ slice_ptr,
+                                 const int* __restrict__ len, int split, int head, int chunk,
+                                 bool groups, int4* out) {
+    const int w = (int)((slice_ptr[q + 1] - slice_ptr[q]) >> 6);
+    if (w <= split) return 0;
+    int c = 0;
+    for (int g = 0; g < (groups ? 4 : 1); ++g) {
+        int reach = w;  // columns this group of rows needs
+        if (groups) {
+            reach = 0;
+            for (int i = 0; i < 16; ++i) reach = max(reach, len[q * 64 + g * 16 + i]);
+        }
+        for (int j0 = head; j0 < reach; j0 += chunk, ++c)
+            if (out) out[c] = make_int4((int)q, j0, min(reach, j0 + chunk), g);
+    }
+    return c;
+}
+
+__global__ void k_sell_chunk_count(int64_t nslices, const int64_t* __restrict__ slice_ptr,
+                                   const int* __restrict__ len, int split, int head, int chunk,
+                                   bool groups, int* __restrict__ cnt) {
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nslices;
+         q += (int64_t)gridDim.x * blockDim.x)
+        cnt[q] = sell_slice_chunks(q, slice_ptr, len, split, head, chunk, groups, nullptr);
+}
+
+__global__ void k_sell_chunk_fill(int64_t nslices, const int64_t* __restrict__ slice_ptr,
+                                  const int* __restrict__ len, const int* __restrict__ chunk_off,
+                                  int split, int head, int chunk, bool groups,
+                                  int4* __restrict__ chunks) {
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nslices;
+         q += (int64_t)gridDim.x * blockDim.x)
+        sell_slice_chunks(q, slice_ptr, len, split, head, chunk, groups, chunks + chunk_off[q]);
+}
+
+hipError_t launch_sell_chunk_count(int64_t nslices, const int64_t* slice_ptr, const int* len,
+                                   int split, int head, int chunk, bool groups, int* cnt,
+                                   hipStream_t stream) {
+    if (nslices <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((nslices + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_sell_chunk_count, dim3((unsigned)blocks), dim3(256), 0, stream, nslices,
+                       slice_ptr, len, split, head, chunk, groups, cnt);
+    return hipGetLastError();
+}
+
+hipError_t launch_sell_chunk_fill(int64_t nslices, const int64_t* slice_ptr, const int* len,
+                                  const int* chunk_off, int split, int head, int chunk,
+                                  bool groups, int4* chunks, hipStream_t stream) {
+    if (nslices <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((nslices + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_sell_chunk_fill, dim3((unsigned)blocks), dim3(256), 0, stream, nslices,
+                       slice_ptr, len, chunk_off, split, head, chunk, groups, chunks);
+    return hipGetLastError();
+}
+
 template <typename T, bool kColNT>
 static hipError_t run_sell(const SellView& a, void* y, const void* x, double alpha, double beta,
                            hipStream_t stream) {
     const int64_t blocks = ((int64_t)a.nslices + 3) / 4;
     if (blocks == 0) return hipSuccess;
+    if (a.window) {
+        if (a.nchunks > 0) {
+            hipLaunchKernelGGL(k_sell_wide_beta<T>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                               a.n, a.nslices, a.slice_ptr, a.perm, (T*)y, (T)beta, a.permuted);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        const int64_t ntiles = ((int64_t)a.nslices * 64 + kEllWinTile - 1) / kEllWinTile;
+        const int64_t g = std::min<int64_t>(ntiles, kWinGroups);
+        hipLaunchKernelGGL((k_sell_win<T, kColNT>), dim3((unsigned)g), dim3(1024), 0, stream, a.n,
+                           a.nslices, a.slice_ptr, a.len, a.perm, a.col, (const T*)a.val,
+                           a.chunk_off, a.chunks, (const T*)x, (T*)y, (T)alpha, (T)beta,
+                           a.permuted, ntiles);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_sell<T, kColNT>), dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
                        a.nslices, a.slice_ptr, a.len, a.perm, a.col, (const T*)a.val,
                        (const T*)x, (T*)y, (T)alpha, (T)beta, a.permuted);

@@ -937,3 +937,85 @@ def test_ell_wave_groups(fmt, kw, groups, name, dtype):
     with pytest.raises(sf.SpmvError):
         M.convert(fmt, ell_groups=8)
     M.close()
+
+
+def _banded_wide():
+    # the FEM block's shape at 300,000 rows: rows of 20-40 within +-10,000
+    # of the diagonal (5 % uniform), 1 % of rows with 2,000 entries (slices
+    # wider than the window kernel's head, cut into chunks), sorted columns
+    return gen_c5(n=300_000, seed=51)
+
+
+SELL_WIN_MATS = dict(WINDOW_MATS, banded_wide=_banded_wide)
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
+@pytest.mark.parametrize("name", ["c1", "ragged", "every_len", "long_spans", "box27", "nnz0",
+                                  "n1", "dups_unsorted", "banded", "banded_wide"])
+@pytest.mark.parametrize("sigma,permuted", [(-1, 0), (64, 0), (8192, 0), (0, 0), (-1, 1)])
+def test_sell_window(name, dtype, sigma, permuted):
+    """SELL-64 with x in the LDS window (forced): narrow slices written with
+    alpha s + beta y, the columns of slices wider than 128 past the first 64
+    taken as chunks by the tile's waves and added with atomics after a beta
+    pass over their rows.  Any sort window works (the window's reach only
+    decides how many x reads go to global memory); -1 takes 1,024 rows."""
+    a = SELL_WIN_MATS[name]()
+    if dtype == torch.float32:
+        a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
+    npdt = np.float64 if dtype == torch.float64 else np.float32
+    x_np, y0_np = vectors(a.n, 23)
+    x_np, y0_np = x_np.astype(npdt), y0_np.astype(npdt)
+    M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n).convert(
+        "sell64", x_window=1, sort_window=sigma, permuted_basis=permuted)
+    i = M.info()
+    assert i["x_window"] == (1 if a.n > 0 else 0)
+    if sigma == -1 and a.n > 1024:
+        assert i["sort_window"] == 1024
+    x = torch.from_numpy(x_np).cuda()
+    y0 = torch.from_numpy(y0_np).cuda()
+    perm = M.export("sell_perm").astype(np.int64) if a.n else np.zeros(0, np.int64)
+    for alpha, beta in AB:
+        if permuted:
+            xp, y0p = torch.empty_like(x), torch.empty_like(y0)
+            M.permute(xp, x)
+            M.permute(y0p, y0)
+            yp = apply(M, xp, y0p, alpha, beta)
+            y = np.empty_like(yp)
+            y[perm] = yp
+        else:
+            y = apply(M, x, y0, alpha, beta)
+        check(a, x_np, y0_np, alpha, beta, y, dtype,
+              what="sell window sigma=%d perm=%d %s a=%g b=%g" % (sigma, permuted, name, alpha,
+                                                                  beta))
+    if a.n > 0 and not permuted:
+        y = torch.full((a.n,), float("nan"), dtype=dtype, device="cuda")
+        M.apply(y, x)
+        torch.cuda.synchronize()
+        check(a, x_np, None, 1.0, 0.0, y.cpu().numpy(), dtype, what="sell window NaN y " + name)
+    M.close()
+
+
+def test_sell_window_layout_and_choice():
+    """The window's SELL layout is the oracle's SELL-64 with 1,024-row sort
+    windows, byte for byte; the automatic choice takes the window for the
+    banded FEM-like matrix only when it is faster, and never for far columns."""
+    a = _banded_wide()
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("sell64", x_window=1)
+    perm, sp, ls, sc, sv = oracle.sell(a, sigma=1024)
+    assert np.array_equal(M.export("sell_perm"), perm.astype(np.int32))
+    assert np.array_equal(M.export("sell_slice_ptr"), sp)
+    assert np.array_equal(M.export("sell_len"), ls)
+    assert np.array_equal(M.export("sell_col"), sc)
+    assert M.export("sell_val").tobytes() == sv.tobytes()
+    M.convert("sell64")       # auto: either layout, always correct
+    i = M.info()
+    assert i["x_window"] in (0, 1) and i["band_fraction"] > 0.8
+    assert i["sort_window"] == (1024 if i["x_window"] else 8192)
+    x_np, y0_np = vectors(a.n, 24)
+    y = apply(M, torch.from_numpy(x_np).cuda(), torch.from_numpy(y0_np).cuda(), 1.5, -0.5)
+    check(a, x_np, y0_np, 1.5, -0.5, y, torch.float64, what="sell auto window")
+    far = random_csr(300_000, seed=48, density=2e-5)
+    M2 = sf.Matrix.from_csr(*to_dev(far), n=far.n).convert("sell64")
+    assert M2.info()["x_window"] == 0 and M2.info()["sort_window"] == 8192
+    M.close()
+    M2.close()
