@@ -41,7 +41,8 @@ FORMATS = ["csr-vector", "csr-balanced", "csr-xblock", "ellr", "sell64", "hyb", 
 APPLY = ("k_csr_vector", "k_csr_staged", "k_scale", "k_tail", "k_tail_win", "k_ell", "k_ell_win", "k_sell",
          "k_sell_chunks", "k_xblk")
 SOURCES = ["sparse_formats_amd/csrc/" + f for f in
-           ("api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "k_xblk.hip", "common.h", "internal.h")]
+           ("api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "k_xblk.hip", "common.h", "internal.h",
+            "index_math.h")]
 
 
 def short(name):

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "index_math.h"
+
 namespace spmv {
 
 constexpr int kWave = 64;
@@ -14,16 +16,6 @@ constexpr int kWave = 64;
 constexpr int64_t kMaxLaunchItems = int64_t(1) << 31;
 // cache-policy bits of a memory instruction on gfx950: nontemporal
 constexpr int kCachePolicyNT = 2;
-
-// MI355X dispatches workgroup b of a grid to XCD (b mod 8).  Each XCD has its
-// own L2, so neighbouring tiles (which share x entries of a banded matrix)
-// should run on the same XCD.  This maps dispatch order to a logical tile
-// index such that XCD k works on the k-th contiguous eighth of the tiles.
-__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t grid) {
-    const int64_t xcd = b & 7, idx = b >> 3;
-    const int64_t per = grid >> 3, rem = grid & 7;
-    return xcd * per + (xcd < rem ? xcd : rem) + idx;
-}
 
 // Streaming (non-temporal) loads for matrix data that is read exactly once
 // per apply, so it does not evict x from the caches.

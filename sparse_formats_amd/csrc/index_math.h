@@ -1,0 +1,115 @@
+// Index arithmetic of the SpMV kernels, written as host-and-device functions:
+// the kernels call these, and the host tests run the same code at the
+// boundaries of the 32-bit and 64-bit ranges (rows and entries near 2^31,
+// slot offsets past 2^32, grids at the dispatch limit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spmv {
+
+// MI355X dispatches workgroup b of a grid to XCD (b mod 8).  Each XCD has its
+// own L2, so neighbouring tiles (which share x entries of a banded matrix)
+// should run on the same XCD.  This maps dispatch order to a logical tile
+// index such that XCD k works on the k-th contiguous eighth of the tiles (a
+// bijection of [0, grid)).
+__host__ __device__ inline int64_t xcd_tile(int64_t b, int64_t grid) {
+    const int64_t xcd = b & 7, idx = b >> 3;
+    const int64_t per = grid >> 3, rem = grid & 7;
+    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// First slot of the row at position i of an ELL array stored in column-major
+// blocks of bh rows (bstride = width * bh slots per block); entry j of the
+// row is at that slot + j * bh.
+__host__ __device__ inline int64_t ell_row_base(int64_t i, int64_t bh, int64_t bstride) {
+    return (i / bh) * bstride + i % bh;
+}
+
+// Largest r in [lo, hi] with ptr[r] <= e, given ptr[lo] <= e < ptr[hi + 1]
+// (the row holding entry e).  The midpoint is taken without lo + hi, which
+// passes 2^31 for the last rows of the largest matrices.  `ptr` is a pointer
+// or anything indexable.
+template <typename Ptr>
+__host__ __device__ inline int row_of(const Ptr& ptr, int lo, int hi, int64_t e) {
+    while (lo < hi) {
+        const int m = lo + ((hi - lo + 1) >> 1);
+        if ((int64_t)ptr[m] <= e)
+            lo = m;
+        else
+            hi = m - 1;
+    }
+    return lo;
+}
+
+// A lane run of entries starts in row `cur`; the next run starts in row
+// `hi`.  The index of the start of row cur + 1 + j, clamped to row hi + 1
+// (cur + 1 + j itself may pass 2^31 near the last rows).
+__host__ __device__ inline int run_next_start(int cur, int hi, int j) {
+    return cur + 1 + (j < hi - cur ? j : hi - cur);
+}
+
+// Column-slice CSR: a lane holds `items` merged items (entries and one end
+// marker per row) starting at entry e0 of tall row r0; next_end[s] =
+// ptr[r0 + 1 + s] is the end of row r0 + s.  Returns the nibble prefix sums
+// of the rows ending at each of the lane's I entry offsets: the entry at
+// offset kk belongs to tall row r0 + ((result >> 4 kk) & 15).  *closed gets
+// the rows that end inside the lane's items.  I <= 8 (four-bit fields).
+template <int I, typename Ptr>
+__host__ __device__ inline uint32_t xblk_row_offsets(const Ptr& next_end, int e0, int items,
+                                                     int* closed) {
+    static_assert(I <= 8, "four-bit counters of at most 8 rows, 8 offsets");
+    uint32_t cnt = 0;
+    int c = 0;
+#pragma unroll
+    for (int s = 0; s < I; ++s) {
+        const int d = (int)next_end[s] - e0;
+        const int re = d < I ? d : I;
+        c += s + re < items;
+        cnt += re < I ? 1u << (4 * re) : 0u;
+    }
+    *closed = items == 0 ? 0 : c;
+    return cnt * 0x11111111u;  // field kk: rows ending at offsets <= kk
+}
+
+// LDS window of x: element q at slot q mod WL; q lies in the window
+// [wl, wl + WL).  Both need wl > -WL and q < 2^31 - WL (the window
+// conversions take only n < 2^31 - 1 - 2 WL), so q - wl cannot overflow.
+__host__ __device__ inline bool in_window(int q, int wl, int WL) {
+    return (uint32_t)(q - wl) < (uint32_t)WL;
+}
+
+// Column chunks of SELL-64 slice q: a slice wider than `split` columns is
+// cut into chunks of `chunk` columns from column `head` on -- with `groups`,
+// for each group of 16 rows up to the group's longest row; otherwise for all
+// rows up to the slice's width.  With `out` the chunks are written from
+// out[0] on as (q, j0, j1, group); the count is returned.
+__host__ __device__ inline int sell_slice_chunks(int64_t q, const int64_t* slice_ptr,
+                                                 const int* len, int split, int head, int chunk,
+                                                 bool groups, int4* out) {
+    const int w = (int)((slice_ptr[q + 1] - slice_ptr[q]) >> 6);
+    if (w <= split) return 0;
+    int c = 0;
+    for (int g = 0; g < (groups ? 4 : 1); ++g) {
+        int reach = w;  // columns this group of rows needs
+        if (groups) {
+            reach = 0;
+            for (int i = 0; i < 16; ++i) {
+                const int l = len[q * 64 + g * 16 + i];
+                reach = l > reach ? l : reach;
+            }
+        }
+        for (int j0 = head; j0 < reach; j0 += chunk, ++c)
+            if (out) out[c] = make_int4((int)q, j0, j0 + chunk < reach ? j0 + chunk : reach, g);
+    }
+    return c;
+}
+
+// Launches whose grid grows with the rows are split into pieces of at most
+// max_items work-items: the blocks per piece, for blocks of `threads`.
+__host__ __device__ inline int64_t blocks_per_piece(int64_t max_items, int threads) {
+    return max_items / threads;
+}
+
+}  // namespace spmv

@@ -231,8 +231,9 @@ static hipError_t run_staged(const CsrView& a, int slots, bool col_nt, void* y, 
     if (blocks == 0) return hipSuccess;
     const size_t lds = 4 * (size_t)CsrStage<T>::wave_bytes(slots);
     if (slots < 1 || lds > kCsrStageLds) return hipErrorInvalidValue;
-    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxLaunchItems / 256) {
-        const int64_t nb = std::min<int64_t>(blocks - b0, kMaxLaunchItems / 256);
+    const int64_t per = blocks_per_piece(kMaxLaunchItems, 256);
+    for (int64_t b0 = 0; b0 < blocks; b0 += per) {
+        const int64_t nb = std::min<int64_t>(blocks - b0, per);
         hipLaunchKernelGGL((k_csr_staged<T, S>), dim3((unsigned)nb), dim3(256), lds, stream, a.n,
                            a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, a.row_map,
                            (T)alpha, (T)beta, slots, col_nt ? 1 : 0, b0);
@@ -246,8 +247,9 @@ static hipError_t run(const CsrView& a, void* y, const void* x, double alpha, do
     constexpr int kRowsPerBlock = 256 / S * R;  // 4 waves of 64 / S groups of R rows
     const int64_t blocks = ((int64_t)a.n + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks == 0) return hipSuccess;
-    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxLaunchItems / 256) {
-        const int64_t nb = std::min<int64_t>(blocks - b0, kMaxLaunchItems / 256);
+    const int64_t per = blocks_per_piece(kMaxLaunchItems, 256);
+    for (int64_t b0 = 0; b0 < blocks; b0 += per) {
+        const int64_t nb = std::min<int64_t>(blocks - b0, per);
         hipLaunchKernelGGL((k_csr_vector<T, S, R>), dim3((unsigned)nb), dim3(256), 0, stream,
                            a.n, a.rowptr, a.col, (const T*)a.val, (const T*)x, (T*)y, a.row_map,
                            (T)alpha, (T)beta, b0);

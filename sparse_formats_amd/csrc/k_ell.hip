@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
     const int64_t i = xcd_tile(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
     const bool valid = i < n;
     const int L = valid ? len[i] : 0;
-    const int64_t base = (i / bh) * bstride + i % bh;
+    const int64_t base = ell_row_base(i, bh, bstride);
     const int* c = col + base;
     const T* v = val + base;
     T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
             open &= open - 1;
             const int Ll = __builtin_amdgcn_readlane(L, l);
             const int64_t il = i - lane + l;  // the wave's rows are consecutive
-            const int64_t bl = (il / bh) * bstride + il % bh;
+            const int64_t bl = ell_row_base(il, bh, bstride);
             T p0 = 0, p1 = 0;
             for (int q0 = j + lane; q0 - lane < Ll; q0 += 64 * kEllCoopUnroll) {
                 T vv[kEllCoopUnroll];
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
 #pragma unroll
             for (int h = 0; h < H; ++h) {
                 const int64_t i = row[h] < n ? row[h] : 0;
-                const int64_t base = (i / bh) * bstride + i % bh;
+                const int64_t base = ell_row_base(i, bh, bstride);
 #pragma unroll
                 for (int u = 0; u < B; ++u) {
                     const int64_t jj = j + u;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
                     // the slot read is always in range; global memory only
                     // for entries outside the window
                     T xv = win[cc[h][u] % WL];
-                    if (in && (uint32_t)(cc[h][u] - wl) >= (uint32_t)WL) xv = x[cc[h][u]];
+                    if (in && !in_window(cc[h][u], wl, WL)) xv = x[cc[h][u]];
                     sum[h][u & 1] += in ? vv[h][u] * xv : T(0);
                 }
             }
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bs
     T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
     if (i < n) {
         const int L = len[i];
-        const int64_t base = (i / bh) * bstride + i % bh;
+        const int64_t base = ell_row_base(i, bh, bstride);
         const int* c = col + base;
         const T* v = val + base;
         int j = g;
@@ -294,7 +294,7 @@ static hipError_t run_ell_mg(const EllView& a, void* y, const void* x, double al
                              double beta, hipStream_t stream) {
     const int64_t blocks = ((int64_t)a.n + kWave - 1) / kWave;
     if (a.groups != 16 && a.groups != 4) return hipErrorInvalidValue;
-    const int64_t per = kMaxLaunchItems / (64 * a.groups);  // blocks per launch
+    const int64_t per = blocks_per_piece(kMaxLaunchItems, 64 * a.groups);
     for (int64_t b0 = 0; b0 < blocks; b0 += per) {
         const int64_t nb = std::min<int64_t>(blocks - b0, per);
         if (a.groups == 16)
@@ -452,7 +452,7 @@ __device__ __forceinline__ T sell_row_win(int64_t base, int j0, int j1, const in
         for (int u = 0; u < B; ++u) {
             const bool in = j + u < j1;
             T xv = win[cc[u] % WL];  // the slot read is always in range
-            if (in && (uint32_t)(cc[u] - wl) >= (uint32_t)WL) xv = x[cc[u]];
+            if (in && !in_window(cc[u], wl, WL)) xv = x[cc[u]];
             if (u & 1)
                 s1 += in ? vv[u] * xv : T(0);
             else
@@ -487,7 +487,7 @@ __device__ __forceinline__ T sell_row4_win(int64_t base, int j0, int j1,
         for (int u = 0; u < B; ++u) {
             const bool in = j + 4 * u < j1;
             T xv = win[cc[u] % WL];
-            if (in && (uint32_t)(cc[u] - wl) >= (uint32_t)WL) xv = x[cc[u]];
+            if (in && !in_window(cc[u], wl, WL)) xv = x[cc[u]];
             if (u & 1)
                 s1 += in ? vv[u] * xv : T(0);
             else
@@ -602,29 +602,7 @@ __global__ __launch_bounds__(256) void k_sell_wide_beta(int n, int nslices,
     y[r] = beta == T(0) ? T(0) : beta * y[r];
 }
 
-// Chunks of slice q (one thread per slice): a slice wider than `split`
-// columns is cut into chunks of `chunk` columns from column `head` on --
-// with `groups`, for each group of 16 rows up to the group's longest row;
-// otherwise for all rows up to the slice's width.  With `out` the chunks are
-// written from out[0] on as (q, j0, j1, group); the count is returned.
-__device__ int sell_slice_chunks(int64_t q, const int64_t* __restrict__ slice_ptr,
-                                 const int* __restrict__ len, int split, int head, int chunk,
-                                 bool groups, int4* out) {
-    const int w = (int)((slice_ptr[q + 1] - slice_ptr[q]) >> 6);
-    if (w <= split) return 0;
-    int c = 0;
-    for (int g = 0; g < (groups ? 4 : 1); ++g) {
-        int reach = w;  // columns this group of rows needs
-        if (groups) {
-            reach = 0;
-            for (int i = 0; i < 16; ++i) reach = max(reach, len[q * 64 + g * 16 + i]);
-        }
-        for (int j0 = head; j0 < reach; j0 += chunk, ++c)
-            if (out) out[c] = make_int4((int)q, j0, min(reach, j0 + chunk), g);
-    }
-    return c;
-}
-
+// setup: chunks of each slice (sell_slice_chunks)
 __global__ void k_sell_chunk_count(int64_t nslices, const int64_t* __restrict__ slice_ptr,
                                    const int* __restrict__ len, int split, int head, int chunk,
                                    bool groups, int* __restrict__ cnt) {

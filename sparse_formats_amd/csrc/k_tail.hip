@@ -84,19 +84,6 @@ __device__ __forceinline__ void load_vec(const int* p, int (&v)[E]) {
     }
 }
 
-// largest r in [lo, hi] with ptr[r] <= e (the row holding entry e, given
-// ptr[lo] <= e < ptr[hi + 1])
-__device__ __forceinline__ int row_of(const int* __restrict__ ptr, int lo, int hi, int64_t e) {
-    while (lo < hi) {
-        const int m = lo + ((hi - lo + 1) >> 1);  // lo + hi may pass 2^31
-        if (ptr[m] <= e)
-            lo = m;
-        else
-            hi = m - 1;
-    }
-    return lo;
-}
-
 // Registers of one lane's share of a chunk: values, columns and rows of its
 // E entries in each of the P passes.
 template <typename T, bool kCoo>
@@ -161,7 +148,7 @@ __device__ __forceinline__ void tail_rows(int64_t w, int lane, const int* __rest
     int nxt[E];  // starts of the next E rows (clamped to the next run's row;
                  // cur + 1 + j itself may pass 2^31 near the last rows)
 #pragma unroll
-    for (int j = 0; j < E; ++j) nxt[j] = tptr[cur + 1 + min(j, hi - cur)];
+    for (int j = 0; j < E; ++j) nxt[j] = tptr[run_next_start(cur, hi, j)];
 #pragma unroll
     for (int k = 0; k < E; ++k) {
         int adv = 0;
@@ -247,8 +234,7 @@ __device__ __forceinline__ void tail_far_gather(const T* __restrict__ x, int64_t
     for (int p = 0; p < P; ++p)
 #pragma unroll
         for (int k = 0; k < E; ++k) {
-            far[p][k] = k < R.cnt[p] &&
-                        (uint32_t)(R.c[p][k] - (int)wlo) >= (uint32_t)WinLen<T>::value;
+            far[p][k] = k < R.cnt[p] && !in_window(R.c[p][k], (int)wlo, WinLen<T>::value);
             xg[p][k] = far[p][k] ? x[R.c[p][k]] : T(0);
         }
 }

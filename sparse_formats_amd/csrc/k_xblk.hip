@@ -59,18 +59,9 @@ __global__ __launch_bounds__(256) void k_xblk(XblkView a, const T* __restrict__ 
     // ends of rows r0 .. r0 + I - 1 (the pointer holds I copies of nnz past
     // its end); a row ending at entry offset re < I of the lane is counted
     // in four-bit field re; rows r0 .. r0 + c - 1 end inside the lane's items
-    const int* __restrict__ ptr = a.ptr + r0 + 1;
-    uint32_t cnt = 0;
-    int c = 0;
-#pragma unroll
-    for (int s = 0; s < I; ++s) {
-        const int re = min(ptr[s] - e0, I);
-        c += s + re < items;
-        cnt += re < I ? 1u << (4 * re) : 0u;
-    }
-    if (items == 0) c = 0;
+    int c;
+    const uint32_t pre = xblk_row_offsets<I>(a.ptr + r0 + 1, e0, items, &c);
     const int m = items - c;  // entries e0 .. e0 + m - 1
-    const uint32_t pre = cnt * 0x11111111u;  // field kk: rows ending at offsets <= kk
     // the entry arrays hold I - 1 padding entries past nnz
     const T* __restrict__ val = static_cast<const T*>(a.val) + e0;
     const int* __restrict__ col = a.col + e0;

@@ -39,13 +39,3 @@ def check(a, x_np, y0_np, alpha, beta, y_gpu, dtype, rows=None, what=""):
     assert ok, "%s: worst |err|/(tol*scale) = %.3g at %s (gpu %r ref %r scale %r)" % (
         what, worst, k if rows is None else rows[k], float(yg[k]), float(ref[k]), float(scale[k]))
     return worst
-
-
-def sample_rows(a, k=20000, seed=0):
-    """Random rows plus the longest rows and both ends."""
-    rng = np.random.default_rng(seed)
-    L = a.row_lengths()
-    longest = np.argsort(L)[-256:]
-    pick = rng.choice(a.n, min(k, a.n), replace=False)
-    ends = np.array([0, 1, a.n - 2, a.n - 1])
-    return np.unique(np.concatenate([pick, longest, ends[(ends >= 0) & (ends < a.n)]]))

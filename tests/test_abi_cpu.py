@@ -11,7 +11,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spmv_amd.h")
-LIB = os.path.join(ROOT, "sparse_formats_amd", "libspmv_amd.so")
+# SPMV_ABI_LIB: a build of the same sources with the host code under the
+# sanitizers (tests/test_host_sanitizers.py runs this file against it)
+LIB = os.environ.get("SPMV_ABI_LIB") or os.path.join(ROOT, "sparse_formats_amd", "libspmv_amd.so")
 
 
 def declared_functions():
