@@ -215,7 +215,7 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
                     // the slot read is always in range; global memory only
                     // for entries outside the window
                     T xv = win[cc[h][u] % WL];
-                    if (in && !in_window(cc[h][u], wl, WL)) xv = x[cc[h][u]];
+                    if (in && (uint32_t)(cc[h][u] - wl) >= (uint32_t)WL) xv = x[cc[h][u]];
                     sum[h][u & 1] += in ? vv[h][u] * xv : T(0);
                 }
             }
@@ -452,7 +452,7 @@ __device__ __forceinline__ T sell_row_win(int64_t base, int j0, int j1, const in
         for (int u = 0; u < B; ++u) {
             const bool in = j + u < j1;
             T xv = win[cc[u] % WL];  // the slot read is always in range
-            if (in && !in_window(cc[u], wl, WL)) xv = x[cc[u]];
+            if (in && (uint32_t)(cc[u] - wl) >= (uint32_t)WL) xv = x[cc[u]];
             if (u & 1)
                 s1 += in ? vv[u] * xv : T(0);
             else
@@ -487,7 +487,7 @@ __device__ __forceinline__ T sell_row4_win(int64_t base, int j0, int j1,
         for (int u = 0; u < B; ++u) {
             const bool in = j + 4 * u < j1;
             T xv = win[cc[u] % WL];
-            if (in && !in_window(cc[u], wl, WL)) xv = x[cc[u]];
+            if (in && (uint32_t)(cc[u] - wl) >= (uint32_t)WL) xv = x[cc[u]];
             if (u & 1)
                 s1 += in ? vv[u] * xv : T(0);
             else

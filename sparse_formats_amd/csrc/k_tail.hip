@@ -234,7 +234,8 @@ __device__ __forceinline__ void tail_far_gather(const T* __restrict__ x, int64_t
     for (int p = 0; p < P; ++p)
 #pragma unroll
         for (int k = 0; k < E; ++k) {
-            far[p][k] = k < R.cnt[p] && !in_window(R.c[p][k], (int)wlo, WinLen<T>::value);
+            far[p][k] = k < R.cnt[p] &&
+                        (uint32_t)(R.c[p][k] - (int)wlo) >= (uint32_t)WinLen<T>::value;
             xg[p][k] = far[p][k] ? x[R.c[p][k]] : T(0);
         }
 }
