@@ -40,6 +40,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# launched by some applies only (SELL-64's chunk kernel and wide-slice beta pass)
+OPTIONAL_KERNELS = {"k_sell_chunks", "k_sell_wide_beta"}
 ALL_FORMATS = ["csr", "ellr", "sell64", "hyb", "hec"]
 KERNELS = {
     "csr": "k_csr_vector",
@@ -66,6 +68,8 @@ def kernels_of(fmt: str, info: dict) -> str:
                                                     info["tail_stage_slots"]))
     if fmt in ("ellr", "hyb", "hec") and info.get("x_window"):
         k = k.replace("k_ell", "k_ell_win").replace("k_tail", "k_tail_win")
+    if fmt == "sell64" and info.get("x_window"):
+        k = "(k_sell_wide_beta +) k_sell_win"
     return k
 
 
@@ -176,7 +180,8 @@ def cpu_baseline(a, x, s_v: int, target_s: float = 10.0, target_1core_s: float =
 
 def kernel_bases(fmt: str, info: dict) -> set:
     """Base names of the kernels one apply of this handle launches (SELL's
-    chunk kernel, present only with very long slices, is left out)."""
+    chunk kernel and wide-slice beta pass, present only with long slices, are
+    left out)."""
     win = "_win" if info.get("x_window") else ""
     if fmt == "csr":
         if info.get("csr_kernel") == "xblock":
@@ -185,7 +190,7 @@ def kernel_bases(fmt: str, info: dict) -> set:
             return {"k_scale", "k_tail" + win}
         return {"k_csr_staged" if info.get("csr_stage_slots", 0) > 0 else "k_csr_vector"}
     if fmt == "sell64":
-        return {"k_sell"}
+        return {"k_sell_win"} if info.get("x_window") else {"k_sell"}
     out = {"k_ell" + win}
     if fmt == "hec" and info.get("tail_nnz", 0) > 0 and info.get("tail_kernel") == "vector":
         out.add("k_csr_staged" if info.get("tail_stage_slots", 0) > 0 else "k_csr_vector")
@@ -203,7 +208,7 @@ def traffic_for(key: str, bases: set, path: str | None = None):
         return None
     recs = json.load(open(path)).get(key) or []
     for rec in recs if isinstance(recs, list) else [recs]:
-        if {k.split("<")[0] for k in rec.get("kernels", [])} - {"k_sell_chunks"} != bases:
+        if {k.split("<")[0] for k in rec.get("kernels", [])} - OPTIONAL_KERNELS != bases:
             continue
         h = hashlib.sha256()
         for f in sorted(rec.get("sources", [])):

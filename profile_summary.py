@@ -39,7 +39,11 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 FORMATS = ["csr-vector", "csr-balanced", "csr-xblock", "ellr", "sell64", "hyb", "hec"]
 APPLY = ("k_csr_vector", "k_csr_staged", "k_scale", "k_tail", "k_tail_win", "k_ell", "k_ell_win", "k_sell",
-         "k_sell_chunks", "k_xblk")
+         "k_sell_chunks", "k_sell_win", "k_sell_wide_beta", "k_xblk")
+# kernels an apply launches only for some matrices: SELL-64's chunk kernel
+# after k_sell, and its beta pass over the wide slices before k_sell_win
+OPTIONAL_AFTER = {"k_sell": "k_sell_chunks"}
+OPTIONAL_BEFORE = {"k_sell_win": "k_sell_wide_beta"}
 SOURCES = ["sparse_formats_amd/csrc/" + f for f in
            ("api.hip", "k_csr.hip", "k_ell.hip", "k_tail.hip", "k_xblk.hip", "common.h", "internal.h",
             "index_math.h")]
@@ -74,15 +78,17 @@ def split_apply(seq):
         # an apply launches at most one ELL, one tail, one scale, one SELL kernel
         seen.add(full)
         out.append((s, full))
+    assert out, "the run ends with no apply kernel (last: %s)" % (seq[-1:] or "none")
     return list(reversed(out))
 
 
 def signature(kernels):
     """[(base name, COO tail?)] of one apply from the bench's kernel string of a
     format (e.g. "k_ell_win + k_tail_win<COO>", "k_scale + k_xblk"); SELL's
-    optional chunk kernel is left out."""
+    optional kernels (in parentheses) are left out."""
     sig = []
-    for part in kernels.replace("(+ k_sell_chunks)", "").split("+"):
+    for part in kernels.replace("(+ k_sell_chunks)", "").replace("(k_sell_wide_beta +)",
+                                                                 "").split("+"):
         part = part.strip()
         if part:
             coo = True if "<COO>" in part else False if "<CSR>" in part else None
@@ -114,18 +120,29 @@ def per_format_applies(timed, formats, kernels):
         return i + len(sig) <= len(names) and all(
             _matches(names[i + j], sig[j]) for j in range(len(sig)))
 
+    def match_with_prefix(i, f):
+        """Length of the optional kernel before f's apply at i (0 or 1), or None."""
+        if match_at(i, f):
+            return 0
+        first = sigs[f][0][0] if sigs[f] else None
+        if (i < len(names) and first in OPTIONAL_BEFORE
+                and names[i][0] == OPTIONAL_BEFORE[first] and match_at(i + 1, f)):
+            return 1
+        return None
+
     i, k = 0, 0
     while i < len(names):
         order = [formats[(k + d) % len(formats)] for d in range(len(formats))]
-        f = next((g for g in order if match_at(i, g)), None)
+        f = next((g for g in order if match_with_prefix(i, g) is not None), None)
         if f is None:
             i += 1
             continue
-        m = len(sigs[f])
+        m = len(sigs[f]) + match_with_prefix(i, f)
         ks = [n[1] for n in names[i:i + m]]
         tot = sum(n[2] for n in names[i:i + m])
         i += m
-        if f == "sell64" and i < len(names) and names[i][0] == "k_sell_chunks":
+        last = sigs[f][-1][0] if sigs[f] else None
+        if last in OPTIONAL_AFTER and i < len(names) and names[i][0] == OPTIONAL_AFTER[last]:
             ks.append(names[i][1])
             tot += names[i][2]
             i += 1

@@ -222,3 +222,31 @@ def test_profile_attribution_trace_from_mid_step():
     assert [len(out[f]) for f in f5] == [2] * 5
     assert out["csr"][0][0] == "k_csr_staged<double, 4>"
     assert out["hec"][1][1] == 100
+
+
+def test_profile_attribution_sell_window():
+    """SELL-64 with the LDS window: its apply is k_sell_win, preceded by the
+    beta pass over the wide slices when the matrix has some; both variants are
+    one apply, and the bench names the kernels and traffic bases alike."""
+    import profile_summary as ps
+    info = {"x_window": 1}
+    assert bench.kernels_of("sell64", info) == "(k_sell_wide_beta +) k_sell_win"
+    assert bench.kernel_bases("sell64", info) == {"k_sell_win"}
+    assert bench.kernel_bases("sell64", {"x_window": 0}) == {"k_sell"}
+    kern = {"csr": "k_scale + k_tail_win<CSR>", "sell64": bench.kernels_of("sell64", info),
+            "hyb": "k_ell_win + k_tail_win<COO>"}
+    fmts = list(kern)
+    step_wide = ["k_scale<double>", "k_tail_win<double, false>", "k_sell_wide_beta<double>",
+                 "k_sell_win<double, true>", "k_ell_win<double, true>", "k_tail_win<double, true>"]
+    step_plain = ["k_scale<double>", "k_tail_win<double, false>", "k_sell_win<double, true>",
+                  "k_ell_win<double, true>", "k_tail_win<double, true>"]
+    out = ps.per_format_applies(_trace(step_wide + step_plain), fmts, kern)
+    assert [len(out[f]) for f in fmts] == [2, 2, 2]
+    assert out["sell64"][0][0] == "k_sell_wide_beta<double> + k_sell_win<double, true>"
+    assert out["sell64"][1][0] == "k_sell_win<double, true>"
+    assert out["sell64"][0][1] == 30 + 40     # dispatches 2 and 3 (10 (i + 1) us)
+    # the counter summary's last apply of a SELL-window run
+    seq = [("k_sell_wide_beta", "k_sell_wide_beta<double>"), ("k_sell_win", "k_sell_win<double, true>")]
+    assert ps.split_apply([("k_copy", "k_copy")] + seq) == seq
+    with pytest.raises(AssertionError):
+        ps.split_apply([("k_copy", "k_copy")])
