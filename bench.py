@@ -56,7 +56,7 @@ def kernels_of(fmt: str, info: dict) -> str:
     """The kernels one apply of this handle launches."""
     if fmt == "csr":
         if info.get("csr_kernel") == "xblock":
-            return "k_scale + k_xblk"
+            return "k_xblk"
         if info.get("csr_kernel") == "balanced":
             return "k_scale + k_tail%s<CSR>" % ("_win" if info["x_window"] else "")
         return _vector_kernel(info["subwave"], info["csr_rows"], info.get("csr_stage_slots", 0))
@@ -185,7 +185,7 @@ def kernel_bases(fmt: str, info: dict) -> set:
     win = "_win" if info.get("x_window") else ""
     if fmt == "csr":
         if info.get("csr_kernel") == "xblock":
-            return {"k_scale", "k_xblk"}
+            return {"k_xblk"}
         if info.get("csr_kernel") == "balanced":
             return {"k_scale", "k_tail" + win}
         return {"k_csr_staged" if info.get("csr_stage_slots", 0) > 0 else "k_csr_vector"}

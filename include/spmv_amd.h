@@ -89,16 +89,18 @@ typedef enum {
                               the row lengths ("Load-balancing Sparse Matrix
                               Vector Product Kernels on GPUs", abstract: a
                               CSR kernel for unbalanced matrices) */
-    SPMV_CSR_XBLOCK = 3    /* CSR format only: the columns cut into 8 slices,
-                              one per XCD, each slice's entries balanced as
-                              above and its x reads kept in that XCD's L2
-                              (for x reads scattered over an x larger than
-                              one L2: "Sparse matrix-vector multiplication on
+    SPMV_CSR_XBLOCK = 3    /* CSR format only: the columns cut into 8 slices
+                              and the rows into ranges of about equal entry
+                              counts (at most 20,480 rows in fp64, 40,960
+                              in fp32); one workgroup sums a range in LDS,
+                              slice by slice, starting with the slice of its
+                              XCD, so each XCD's x reads stay in its L2 (for
+                              x reads scattered over an x larger than one
+                              L2: "Sparse matrix-vector multiplication on
                               GPGPU clusters", Sect. 2.3, right-hand-side
-                              reuse).  A pass writes beta * y, then each
-                              slice adds alpha times its row sums into y
-                              with atomics.  Stores a second, column-sliced
-                              copy of the entries; needs 8 n < 2^31 - 16.
+                              reuse), then writes the range's y once.
+                              Stores a second copy of the entries, by tile,
+                              with 2-byte row offsets; needs 8 n < 2^31 - 16.
                               SPMV_CSR_AUTO
                               times it as well when x is over 4 MiB and
                               at least half the entries lie outside the
@@ -326,8 +328,9 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts *opts);
  *   alpha, beta  scalars (rounded to float for SPMV_F32 handles)
  *   stream the kernels are enqueued on this stream; no host synchronisation
  * Accumulation is in the handle's dtype with fused multiply-adds; HYB/HEC,
- * split SELL slices and the balanced and column-slice CSR kernels add
- * partial sums with atomics, so their last bits may vary between runs.  Errors: STATE, INVALID_ARG (null or overlapping
+ * split SELL slices and the balanced CSR kernel add partial sums with
+ * atomics in global memory, and the column-slice CSR kernel adds them with
+ * atomics in LDS, so their last bits may vary between runs.  Errors: STATE, INVALID_ARG (null or overlapping
  * vectors), HIP (launch failure).
  */
 int spmv_apply(spmv_t h, void *y, const void *x, double alpha, double beta,

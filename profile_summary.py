@@ -84,7 +84,7 @@ def split_apply(seq):
 
 def signature(kernels):
     """[(base name, COO tail?)] of one apply from the bench's kernel string of a
-    format (e.g. "k_ell_win + k_tail_win<COO>", "k_scale + k_xblk"); SELL's
+    format (e.g. "k_ell_win + k_tail_win<COO>", "k_xblk"); SELL's
     optional kernels (in parentheses) are left out."""
     sig = []
     for part in kernels.replace("(+ k_sell_chunks)", "").replace("(k_sell_wide_beta +)",

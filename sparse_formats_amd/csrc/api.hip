@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "spmv_amd.h"
+#include "index_math.h"
 #include "internal.h"
 
 using namespace spmv;
@@ -127,9 +128,9 @@ struct Built {
     VecShape tail_vec;
     // CSR: entry-balanced kernel (run rows over the whole matrix)
     bool csr_balanced = false;
-    // CSR by column slices, one per XCD (the view holds the pointers below)
+    // CSR by column slices (the view holds the pointers below)
     bool csr_xblock = false;
-    DevBuf xb_ptr, xb_col, xb_val, xb_lane_row;
+    DevBuf xb_rows, xb_tiles, xb_col, xb_val, xb_lrow;
     XblkView xb{};
     // SELL-64 in the permuted basis (x and y in sorted row order)
     bool permuted = false;
@@ -145,7 +146,8 @@ struct Built {
                perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + chunk_off.bytes +
                tail_row.bytes +
                tail_ptr.bytes + tail_col.bytes + tail_val.bytes + run_row.bytes + tail_rows.bytes +
-               tail_cptr.bytes + xb_ptr.bytes + xb_col.bytes + xb_val.bytes + xb_lane_row.bytes;
+               tail_cptr.bytes + xb_rows.bytes + xb_tiles.bytes + xb_col.bytes + xb_val.bytes +
+               xb_lrow.bytes;
     }
 };
 
@@ -1130,72 +1132,76 @@ float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw
 // CSR kernel: time every shape of the vector kernel and the entry-balanced
 // kernel on the device and keep the fastest (the apply does not depend on
 // the values of x, so zeros are used).  Fixed values are not tuned.
-// CSR by column slices (SPMV_CSR_XBLOCK): the tall row pointer from the
-// per-slice row lengths, the entries copied in tall order, the merged-item
-// start of every slice and the row of every lane's first item.
+// CSR by column slices (SPMV_CSR_XBLOCK): row ranges of about equal entry
+// counts (at most kXbCap rows, one pass of kXbGroups workgroups when the
+// rows allow), the entry counts of every row in every slice at their
+// xblk_slot positions, their scan (every entry's place), the tile starts and
+// the entries in tile order with their row offsets.
 void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
-    const int64_t n = h->n, R = (int64_t)kXbBlocks * n;
-    if (R > (int64_t)INT32_MAX - 16)
+    const int64_t n = h->n, nnz = h->nnz;
+    if ((int64_t)kXbBlocks * n > (int64_t)INT32_MAX - 16)
         fail(SPMV_ERR_INVALID_ARG, "csr_kernel 3 (column slices) takes n <= %lld rows (got %lld)",
              (long long)(((int64_t)INT32_MAX - 16) / kXbBlocks), (long long)n);
     b.csr_xblock = true;
     XblkView& v = b.xb;
+    v = XblkView{};
     v.n = n;
     v.width = std::max<int64_t>((n + kXbBlocks - 1) / kXbBlocks, 1);
     if (n == 0) return;
-    // the row pointer holds kXbItems copies of nnz past its end, the entry
-    // arrays kXbItems zero entries (a lane reads kXbItems of each unchecked)
-    b.xb_ptr.alloc((size_t)(R + 1 + kXbItems) * 4);
+    const int cap = h->dtype == SPMV_F64 ? kXbCap<double> : kXbCap<float>;
+    const int64_t passes = std::max<int64_t>(1, (n + (int64_t)kXbGroups * cap - 1) /
+                                                    ((int64_t)kXbGroups * cap));
+    const int64_t R0 = passes * kXbGroups;
+    std::vector<int> cand((size_t)R0 + 1);
     {
-        const std::vector<int> pad(kXbItems, (int)h->nnz);
-        hip_check(hipMemcpyAsync(b.xb_ptr.as<int>() + R + 1, pad.data(), pad.size() * 4,
-                                 hipMemcpyHostToDevice, s),
+        DevBuf dc(cand.size() * 4);
+        hip_check(launch_xblk_bounds(n, nnz, h->rowptr.as<int>(), R0, dc.as<int>(), s),
+                  "column-slice range bounds");
+        hip_check(hipMemcpyAsync(cand.data(), dc.p, dc.bytes, hipMemcpyDeviceToHost, s),
                   "hipMemcpyAsync");
-        DevBuf cnt((size_t)R * 4);
-        hip_check(launch_xblk_count(n, v.width, h->rowptr.as<int>(), h->col.as<int>(),
-                                    cnt.as<int>(), s),
+        sync(s);
+    }
+    v.ranges = xblk_split_ranges(cand.data(), R0, cap, nullptr);
+    std::vector<int> rows((size_t)v.ranges + 1);
+    xblk_split_ranges(cand.data(), R0, cap, rows.data());
+    b.xb_rows.alloc(rows.size() * 4);
+    hip_check(hipMemcpyAsync(b.xb_rows.p, rows.data(), rows.size() * 4, hipMemcpyHostToDevice, s),
+              "hipMemcpyAsync");
+    v.row_begin = b.xb_rows.as<int>();
+    const int64_t slots = (int64_t)kXbBlocks * n;
+    DevBuf pos((size_t)(slots + 1) * 4);
+    {
+        DevBuf cnt((size_t)slots * 4);
+        hip_check(launch_xblk_count(v, h->rowptr.as<int>(), h->col.as<int>(), cnt.as<int>(), s),
                   "column-slice counts");
-        hip_check(hipMemsetAsync(b.xb_ptr.p, 0, 4, s), "hipMemsetAsync");
+        hip_check(hipMemsetAsync(pos.p, 0, 4, s), "hipMemsetAsync");
         size_t tmp = 0;
-        hip_check(rocprim::inclusive_scan(nullptr, tmp, cnt.as<int>(), b.xb_ptr.as<int>() + 1,
-                                          (size_t)R, rocprim::plus<int>(), s),
+        hip_check(rocprim::inclusive_scan(nullptr, tmp, cnt.as<int>(), pos.as<int>() + 1,
+                                          (size_t)slots, rocprim::plus<int>(), s),
                   "inclusive_scan");
         DevBuf work(tmp);
-        hip_check(rocprim::inclusive_scan(work.p, tmp, cnt.as<int>(), b.xb_ptr.as<int>() + 1,
-                                          (size_t)R, rocprim::plus<int>(), s),
+        hip_check(rocprim::inclusive_scan(work.p, tmp, cnt.as<int>(), pos.as<int>() + 1,
+                                          (size_t)slots, rocprim::plus<int>(), s),
                   "inclusive_scan");
         sync(s);
     }
-    int64_t waves = 0, tiles = 0;
-    for (int k = 0; k <= kXbBlocks; ++k)
-        v.item0[k] = (int64_t)k * n + read_scalar<int>(b.xb_ptr.as<int>() + (size_t)k * n, s);
-    for (int k = 0; k < kXbBlocks; ++k) {
-        const int64_t w = (v.item0[k + 1] - v.item0[k] + kXbChunk - 1) / kXbChunk;
-        v.wave_base[k] = waves;
-        waves += w;
-        tiles = std::max<int64_t>(tiles, (w + 3) / 4);
-    }
-    v.wave_base[kXbBlocks] = waves;
-    v.waves = waves;
-    v.tiles = tiles;
-    const int64_t nnz = h->nnz;
-    b.xb_col.alloc((size_t)(nnz + kXbItems) * 4);
-    b.xb_val.alloc((size_t)(nnz + kXbItems) * h->vsize);
-    hip_check(hipMemsetAsync(b.xb_col.as<int>() + nnz, 0, kXbItems * 4, s), "hipMemsetAsync");
-    hip_check(hipMemsetAsync((char*)b.xb_val.p + (size_t)nnz * h->vsize, 0, kXbItems * h->vsize, s),
-              "hipMemsetAsync");
-    hip_check(launch_xblk_fill(n, v.width, h->dtype == SPMV_F64, h->rowptr.as<int>(),
-                               h->col.as<int>(), h->val.p, b.xb_ptr.as<int>(), b.xb_col.as<int>(),
-                               b.xb_val.p, s),
+    const int64_t ntiles = v.ranges * kXbBlocks;
+    b.xb_tiles.alloc((size_t)(ntiles + 1) * 4);
+    hip_check(launch_xblk_tiles(v, pos.as<int>(), b.xb_tiles.as<int>(), s), "column-slice tiles");
+    hip_check(hipMemcpyAsync(b.xb_tiles.as<int>() + ntiles, pos.as<int>() + slots, 4,
+                             hipMemcpyDeviceToDevice, s),
+              "hipMemcpyAsync");
+    v.tile_ptr = b.xb_tiles.as<int>();
+    b.xb_col.alloc((size_t)std::max<int64_t>(nnz, 1) * 4);
+    b.xb_val.alloc((size_t)std::max<int64_t>(nnz, 1) * h->vsize);
+    b.xb_lrow.alloc((size_t)std::max<int64_t>(nnz, 1) * 2);
+    hip_check(launch_xblk_fill(v, h->dtype == SPMV_F64, h->rowptr.as<int>(), h->col.as<int>(),
+                               h->val.p, pos.as<int>(), b.xb_col.as<int>(), b.xb_val.p,
+                               b.xb_lrow.as<uint16_t>(), s),
               "column-slice fill");
-    v.ptr = b.xb_ptr.as<int>();
     v.col = b.xb_col.as<int>();
     v.val = b.xb_val.p;
-    // lanes past a slice's last item read row 0 (any valid row)
-    b.xb_lane_row.alloc((size_t)waves * 64 * 4);
-    hip_check(hipMemsetAsync(b.xb_lane_row.p, 0, b.xb_lane_row.bytes, s), "hipMemsetAsync");
-    hip_check(launch_xblk_lane_rows(v, b.xb_lane_row.as<int>(), s), "column-slice lane rows");
-    v.lane_row = b.xb_lane_row.as<int>();
+    v.lrow = b.xb_lrow.as<uint16_t>();
     sync(s);
 }
 
@@ -1259,9 +1265,8 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     // third candidate: column slices, for x reads scattered over an x larger
     // than one XCD's L2 (most entries outside the diagonal band the LDS
     // window would cover), when its copy of the entries fits the budget
-    const double xb_bytes = (double)h->nnz * (4.0 + (double)h->vsize) +  // entries
-                            (double)kXbBlocks * (double)h->n * 4.0 +        // tall row pointer
-                            ((double)kXbBlocks * (double)h->n + (double)h->nnz) / 2.0;  // lane rows
+    const double xb_bytes = (double)h->nnz * (6.0 + (double)h->vsize) +  // entries, row offsets
+                            (double)kXbBlocks * (double)h->n * 8.0;         // counts and their scan
     if (o.csr_kernel == SPMV_CSR_AUTO && want_bal && !b.window &&
         (double)h->n * (double)h->vsize > (double)kXbMinX && b.band_fraction < 0.5 &&
         (int64_t)kXbBlocks * h->n <= (int64_t)INT32_MAX - 16 &&

@@ -50,27 +50,45 @@ __host__ __device__ __forceinline__ int run_next_start(int cur, int hi, int j) {
     return cur + 1 + (j < hi - cur ? j : hi - cur);
 }
 
-// Column-slice CSR: a lane holds `items` merged items (entries and one end
-// marker per row) starting at entry e0 of tall row r0; next_end[s] =
-// ptr[r0 + 1 + s] is the end of row r0 + s.  Returns the nibble prefix sums
-// of the rows ending at each of the lane's I entry offsets: the entry at
-// offset kk belongs to tall row r0 + ((result >> 4 kk) & 15).  *closed gets
-// the rows that end inside the lane's items.  I <= 8 (four-bit fields).
-template <int I, typename Ptr>
-__host__ __device__ __forceinline__ uint32_t xblk_row_offsets(const Ptr& next_end, int e0, int items,
-                                                     int* closed) {
-    static_assert(I <= 8, "four-bit counters of at most 8 rows, 8 offsets");
-    uint32_t cnt = 0;
-    int c = 0;
-#pragma unroll
-    for (int s = 0; s < I; ++s) {
-        const int d = (int)next_end[s] - e0;
-        const int re = d < I ? d : I;
-        c += s + re < items;
-        cnt += re < I ? 1u << (4 * re) : 0u;
+// Column-slice CSR.  Rows are cut into ranges, each summed by one workgroup
+// in LDS; the entries of range r with columns in slice b form tile (r, b).
+// Candidate range start for target r of R0: the row holding entry
+// r * nnz / R0 (ranges of about equal entry counts); 0 for r = 0, n for r >=
+// R0.  Needs n >= 1 and nnz < 2^31; r * nnz stays below 2^63 for r < 2^32.
+template <typename Ptr>
+__host__ __device__ __forceinline__ int xblk_bound(const Ptr& ptr, int n, int64_t nnz, int64_t r,
+                                                   int64_t R0) {
+    if (r >= R0) return n;
+    if (r == 0) return 0;
+    return row_of(ptr, 0, n - 1, r * nnz / R0);
+}
+
+// The ranges from the candidate starts cand[0..m] (non-decreasing, cand[0] =
+// 0, cand[m] = n): every stretch between distinct candidates is cut into
+// equal pieces of at most `cap` rows.  Writes the range starts and n to
+// out[0..R] when out is given; returns R.
+__host__ __device__ __forceinline__ int64_t xblk_split_ranges(const int* cand, int64_t m, int cap,
+                                                              int* out) {
+    int64_t R = 0;
+    for (int64_t k = 0; k < m; ++k) {
+        const int lo = cand[k], hi = cand[k + 1];
+        if (hi <= lo) continue;
+        const int64_t rows = (int64_t)hi - lo, pieces = (rows + cap - 1) / cap;
+        for (int64_t p = 0; p < pieces; ++p, ++R)
+            if (out) out[R] = lo + (int)(rows * p / pieces);
     }
-    *closed = items == 0 ? 0 : c;
-    return cnt * 0x11111111u;  // field kk: rows ending at offsets <= kk
+    if (out) out[R] = m > 0 ? cand[m] : 0;
+    return R;
+}
+
+// Position of the count of row i in slice b (kS slices) inside the count
+// array, whose scan gives every entry's place: range r of rows [rb, rb + nr)
+// owns kS * nr consecutive counts, slice-major (slice b's counts of the
+// range's rows in row order).  The tile (r, b) therefore starts at position
+// xblk_slot(rb, nr, b, rb, kS).
+__host__ __device__ __forceinline__ int64_t xblk_slot(int64_t rb, int64_t nr, int b, int64_t i,
+                                                      int kS) {
+    return (int64_t)kS * rb + (int64_t)b * nr + (i - rb);
 }
 
 // LDS window of x: element q at slot q mod WL; q lies in the window

@@ -148,38 +148,41 @@ struct TailView {
     bool window;           // stage x in LDS (banded matrices)
 };
 
-// CSR by column blocks: the columns cut into kXbBlocks slices of `width`
-// columns (one per XCD), slice b's entries stored as a tall CSR matrix of n
-// rows (tall row b * n + i: row i's entries in slice b, original order).
-// Work is split into merged items (entries and one end marker per row): a
-// wave takes kXbChunk consecutive items of one slice, kXbItems per lane.
+// CSR by column slices: the columns cut into kXbBlocks slices of `width`
+// columns, the rows into ranges of at most kXbCap<T> rows (about equal
+// entry counts).  One workgroup of kXbThreads sums a range in LDS, slice by
+// slice; the entries of range r in slice b (tile (r, b)) are stored
+// together, by row, with each entry's row offset inside its range.
 constexpr int kXbBlocks = 8;
-constexpr int kXbItems = 8;
-constexpr int kXbChunk = 64 * kXbItems;
+constexpr int kXbThreads = 1024;
+constexpr int kXbGroups = 256;            // persistent workgroups, one per CU
+constexpr int kXbLdsBytes = 160 * 1024;   // the range's partial sums
+template <typename T>
+constexpr int kXbCap = kXbLdsBytes / (int)sizeof(T);
 struct XblkView {
-    int64_t n;            // matrix rows (tall rows: kXbBlocks * n < 2^31 - 16)
-    int64_t width;        // columns per slice
-    const int* ptr;       // [kXbBlocks * n + 1] tall row pointer
-    const int* col;       // [nnz] tall order
-    const void* val;      // [nnz]
-    const int* lane_row;  // [64 * waves] tall row of each lane's first item
-    int64_t waves;        // all slices
-    int64_t tiles;        // workgroups (4 waves each) per slice, the most of any slice
-    int64_t wave_base[kXbBlocks + 1];  // first wave of each slice
-    int64_t item0[kXbBlocks + 1];      // first merged item of each slice (b * n + ptr[b * n])
+    int64_t n;             // matrix rows
+    int64_t width;         // columns per slice
+    int64_t ranges;        // row ranges
+    const int* row_begin;  // [ranges + 1] first row of each range, then n
+    const int* tile_ptr;   // [ranges * kXbBlocks + 1] first entry of tile (r, b), then nnz
+    const int* col;        // [nnz] tile order
+    const uint16_t* lrow;  // [nnz] row - row_begin[r]
+    const void* val;       // [nnz]
 };
 hipError_t launch_xblk(const XblkView& a, bool f64, void* y, const void* x, double alpha,
                        double beta, hipStream_t stream);
-// setup: cnt[b * n + i] = entries of row i in slice b
-hipError_t launch_xblk_count(int64_t n, int64_t width, const int* rowptr, const int* col,
-                             int* cnt, hipStream_t stream);
-// setup: tall col / val from the CSR arrays and the tall row pointer
-hipError_t launch_xblk_fill(int64_t n, int64_t width, bool f64, const int* rowptr, const int* col,
-                            const void* val, const int* ptr, int* ocol, void* oval,
-                            hipStream_t stream);
-// setup: lane_row (every lane of every slice's waves; lanes past a slice's
-// last item are left as they are)
-hipError_t launch_xblk_lane_rows(const XblkView& a, int* lane_row, hipStream_t stream);
+// setup: cand[r] = start of range r of R0 by entry count (xblk_bound), r in [0, R0]
+hipError_t launch_xblk_bounds(int64_t n, int64_t nnz, const int* rowptr, int64_t R0, int* cand,
+                              hipStream_t stream);
+// setup: the entry counts of every row in every slice at xblk_slot positions
+hipError_t launch_xblk_count(const XblkView& a, const int* rowptr, const int* col, int* cnt,
+                             hipStream_t stream);
+// setup: tile_ptr from the scanned counts (pos[k] = counts before position k)
+hipError_t launch_xblk_tiles(const XblkView& a, const int* pos, int* tile_ptr, hipStream_t stream);
+// setup: col / val / lrow in tile order from the CSR arrays and pos
+hipError_t launch_xblk_fill(const XblkView& a, bool f64, const int* rowptr, const int* col,
+                            const void* val, const int* pos, int* ocol, void* oval,
+                            uint16_t* olrow, hipStream_t stream);
 
 // kernel launchers (asynchronous on `stream`); fp64 when f64, else fp32
 // rows: rows per lane group, a power of two up to kCsrRowsMax; stage_slots >

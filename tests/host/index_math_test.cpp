@@ -128,33 +128,99 @@ static void test_run_next_start() {
             }
 }
 
-static void test_xblk_row_offsets() {
-    // against the plain count: entry kk of the lane belongs to row r0 + #{s :
-    // end of row r0 + s <= e0 + kk}; rows whose end marker falls within the
-    // lane's items are closed there (merged position of row t's end: t +
-    // ptr[t + 1])
+static void test_xblk_ranges() {
+    // candidate starts: the row holding entry r * nnz / R0, against a linear
+    // search, on random row pointers (empty rows too) and at n near 2^31
     std::mt19937_64 rng(11);
-    constexpr int I = 8;
-    for (int trial = 0; trial < 200000; ++trial) {
-        const int e0 = (int)(rng() % 1000) + (trial & 1 ? (INT_MAX - 70000) : 0);
-        int ends[I];
-        int e = e0 + (int)(rng() % 3);
-        for (int s = 0; s < I; ++s) {
-            e += (int)(rng() % 4 == 0 ? 0 : rng() % 4);  // empty rows too
-            ends[s] = e;
+    for (int trial = 0; trial < 2000; ++trial) {
+        const int n = 1 + (int)(rng() % 300);
+        std::vector<int> ptr(n + 1, 0);
+        for (int i = 0; i < n; ++i) ptr[i + 1] = ptr[i] + (rng() % 3 == 0 ? 0 : (int)(rng() % 9));
+        const int64_t nnz = ptr[n], R0 = 1 + (int64_t)(rng() % 40);
+        std::vector<int> cand(R0 + 1);
+        for (int64_t r = 0; r <= R0; ++r) {
+            cand[r] = xblk_bound(ptr.data(), n, nnz, r, R0);
+            if (r == 0) CHECK(cand[r] == 0, "first start");
+            else if (r == R0) CHECK(cand[r] == n, "last start");
+            else if (nnz > 0) {
+                const int64_t e = r * nnz / R0;
+                int ref = 0;
+                for (int i = 0; i < n; ++i)
+                    if (ptr[i] <= e) ref = i;
+                CHECK(cand[r] == ref, "trial %d r %lld: %d vs %d", trial, (long long)r, cand[r], ref);
+            }
+            if (r > 0) CHECK(cand[r] >= cand[r - 1], "candidates non-decreasing");
         }
-        const int items = (int)(rng() % (I + 1));
-        int closed = -1;
-        const uint32_t pre = xblk_row_offsets<I>(ends, e0, items, &closed);
-        int ref_closed = 0;
-        for (int s = 0; s < I; ++s)
-            if (s + (ends[s] - e0) < items) ++ref_closed;
-        CHECK(closed == ref_closed, "trial %d closed %d vs %d", trial, closed, ref_closed);
-        for (int kk = 0; kk < items - closed; ++kk) {
-            int ref = 0;
-            for (int s = 0; s < I; ++s) ref += ends[s] <= e0 + kk;
-            CHECK((int)((pre >> (4 * kk)) & 15) == ref, "trial %d kk %d", trial, kk);
+        // ranges: strictly increasing starts from 0 to n, at most cap rows,
+        // every distinct candidate kept as a start
+        const int cap = 1 + (int)(rng() % 50);
+        const int64_t R = xblk_split_ranges(cand.data(), R0, cap, nullptr);
+        std::vector<int> out(R + 1, -1);
+        CHECK(xblk_split_ranges(cand.data(), R0, cap, out.data()) == R, "count twice");
+        CHECK(out[0] == 0 && out[R] == n, "ranges cover [0, n)");
+        for (int64_t k = 0; k < R; ++k)
+            CHECK(out[k] < out[k + 1] && out[k + 1] - out[k] <= cap, "range %lld", (long long)k);
+        for (int64_t r = 0; r < R0; ++r) {
+            bool found = false;
+            for (int64_t k = 0; k <= R; ++k) found |= out[k] == cand[r];
+            CHECK(found, "candidate %lld kept", (long long)r);
         }
+    }
+    // n near 2^31 (the column-slice kernel takes fewer rows, the helpers not):
+    // every row one entry but the first, which holds nnz - (n - 1)
+    {
+        const int n = INT_MAX - 1;
+        const int64_t nnz = (int64_t)INT_MAX - 65536;
+        struct P {
+            int n;
+            int64_t nnz;
+            int64_t operator[](int64_t i) const { return i == 0 ? 0 : nnz - (n - i); }
+        } ptr{n, nnz};
+        const int64_t R0 = 256 * 410;
+        int prev = 0;
+        for (int64_t r = 0; r <= R0; r += 997) {
+            const int c = xblk_bound(ptr, n, nnz, r, R0);
+            CHECK(c >= prev && c <= n, "r %lld -> %d", (long long)r, c);
+            if (r > 0 && r < R0) {
+                const int64_t e = r * nnz / R0;
+                CHECK(ptr[c] <= e && e < ptr[c + 1], "row of entry %lld", (long long)e);
+            }
+            prev = c;
+        }
+        // one stretch of n rows in pieces of at most 20480
+        const int cand[2] = {0, n};
+        const int64_t R = xblk_split_ranges(cand, 1, 20480, nullptr);
+        CHECK(R == ((int64_t)n + 20479) / 20480, "pieces %lld", (long long)R);
+        std::vector<int> out(R + 1);
+        xblk_split_ranges(cand, 1, 20480, out.data());
+        for (int64_t k = 0; k < R; ++k)
+            CHECK(out[k] < out[k + 1] && out[k + 1] - out[k] <= 20480, "piece %lld", (long long)k);
+    }
+    // count positions: a bijection of [0, kS n) onto the counts of (row, slice),
+    // slice-major inside each range, tiles starting at xblk_slot(rb, nr, b, rb)
+    for (int trial = 0; trial < 200; ++trial) {
+        const int n = 1 + (int)(rng() % 500), kS = 8;
+        std::vector<int> starts = {0};
+        while (starts.back() < n) starts.push_back(std::min(n, starts.back() + 1 + (int)(rng() % 60)));
+        std::vector<char> seen((size_t)kS * n, 0);
+        for (size_t r = 0; r + 1 < starts.size(); ++r) {
+            const int rb = starts[r], nr = starts[r + 1] - rb;
+            for (int b = 0; b < kS; ++b)
+                for (int i = rb; i < rb + nr; ++i) {
+                    const int64_t s = xblk_slot(rb, nr, b, i, kS);
+                    CHECK(s >= 0 && s < (int64_t)kS * n && !seen[s], "slot of row %d slice %d", i, b);
+                    seen[s] = 1;
+                    CHECK(s == xblk_slot(rb, nr, b, rb, kS) + (i - rb), "tile order");
+                    if (i == rb && b > 0)
+                        CHECK(s == xblk_slot(rb, nr, b - 1, rb + nr - 1, kS) + 1, "tiles adjacent");
+                }
+        }
+    }
+    // the largest slot: kS n - 1 < 2^31 for n up to (2^31 - 17) / 8
+    {
+        const int64_t n = ((int64_t)INT_MAX - 16) / 8, rb = n - 20480, nr = 20480;
+        CHECK(xblk_slot(rb, nr, 7, n - 1, 8) == 8 * n - 1, "last slot");
+        CHECK(8 * n - 1 <= (int64_t)INT_MAX, "fits int");
     }
 }
 
@@ -242,7 +308,7 @@ int main() {
     test_ell_row_base();
     test_row_of();
     test_run_next_start();
-    test_xblk_row_offsets();
+    test_xblk_ranges();
     test_in_window();
     test_sell_chunks();
     test_launch_pieces();

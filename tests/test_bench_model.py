@@ -131,10 +131,10 @@ def test_traffic_record_checks(tmp_path):
     assert bench.kernels_of("hyb", {"x_window": 0, "tail_nnz": 3}) == "k_ell + k_tail<COO>"
     # the column-slice CSR kernel and its traffic record
     xb = {"csr_kernel": "xblock", "x_window": 0, "subwave": 1, "csr_rows": 1}
-    assert bench.kernel_bases("csr", xb) == {"k_scale", "k_xblk"}
-    assert bench.kernels_of("csr", xb) == "k_scale + k_xblk"
+    assert bench.kernel_bases("csr", xb) == {"k_xblk"}
+    assert bench.kernels_of("csr", xb) == "k_xblk"
     rec["w:f64:csr"][0]["kernels"] = ["k_scale<double>", "k_tail_win<double, false>"]
-    rec["w:f64:csr"].append({"kernels": ["k_scale<double>", "k_xblk<double>"],
+    rec["w:f64:csr"].append({"kernels": ["k_xblk<double>"],
                              "bytes_per_launch": 55, "sources": srcs, "sha256": h.hexdigest()})
     p.write_text(json.dumps(rec))
     assert bench.traffic_for("w:f64:csr", bench.kernel_bases("csr", xb), str(p)) == 55
@@ -145,26 +145,26 @@ def test_counter_summary(tmp_path, monkeypatch):
     kernel of the last apply, with several counter rows per dispatch."""
     import profile_summary as ps
     out = tmp_path / "pmc"
-    d = out / "PMC1_w_csr-xblock"
+    d = out / "PMC1_w_csr-balanced"
     d.mkdir(parents=True)
-    (out / "PMC1_w_csr-xblock.txt").write_text("A B\n")
+    (out / "PMC1_w_csr-balanced.txt").write_text("A B\n")
     rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
     disp = 0
     for rep in range(3):       # three applies, then the last one is kept
-        for k in ("spmv::k_scale<double>(x)", "spmv::k_xblk<double>(x)"):
+        for k in ("spmv::k_scale<double>(x)", "spmv::k_tail<double, false>(x)"):
             disp += 1
             for c in ("A", "B"):
                 rows.append('%d,"%s",%s,%d' % (disp, k, c, 10 * rep + (c == "B")))
     (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
     (tmp_path / "profiles").mkdir()
     monkeypatch.setattr(ps, "ROOT", str(tmp_path))
-    monkeypatch.setattr(sys, "argv", ["x", "counters", str(out), "w", "csr-xblock"])
+    monkeypatch.setattr(sys, "argv", ["x", "counters", str(out), "w", "csr-balanced"])
     ps.counters_main()
-    text = (tmp_path / "profiles" / "spmv_w_f64_csr-xblock_counters.md").read_text()
+    text = (tmp_path / "profiles" / "spmv_w_f64_csr-balanced_counters.md").read_text()
     body = [l for l in text.splitlines() if l.startswith("| k_")]
-    assert [l.split(" | ")[0] for l in body] == ["| k_scale<double>", "| k_xblk<double>"]
+    assert [l.split(" | ")[0] for l in body] == ["| k_scale<double>", "| k_tail<double, false>"]
     assert all(l.endswith("| 20 | 21 |") for l in body)      # the last apply's values
-    assert "--formats csr --csr-kernel xblock" in text
+    assert "--formats csr --csr-kernel balanced" in text
 
 
 def _trace(names):
@@ -178,28 +178,28 @@ def _trace(names):
     return rows
 
 
-C4_KERNELS = {"csr": "k_scale + k_xblk", "sell64": "k_sell (+ k_sell_chunks)",
+C4_KERNELS = {"csr": "k_xblk", "sell64": "k_sell (+ k_sell_chunks)",
               "hyb": "k_ell + k_tail<COO>", "hec": "k_ell + k_tail<CSR>"}
-C4_STEP = ["k_scale<double>", "k_xblk<double>", "k_sell<double, true>",
+C4_STEP = ["k_xblk<double>", "k_sell<double, true>",
            "k_sell_chunks<double, true>", "k_ell<double, true>", "k_tail<double, true>",
            "k_ell<double, true>", "k_tail<double, false>"]
 
 
 def test_profile_attribution_c4_step_with_stray_dispatch():
-    """Each format gets its own kernels: the column-slice CSR apply (two
-    kernels), SELL with its chunk kernel, HYB's COO and HEC's CSR tail; a stray
+    """Each format gets its own kernels: the column-slice CSR apply, SELL with
+    its chunk kernel, HYB's COO and HEC's CSR tail; a stray
     dispatch before the first step is skipped, not counted as an apply."""
     import profile_summary as ps
     fmts = ["csr", "sell64", "hyb", "hec"]
     trace = _trace(["k_tail<double, false>"] + C4_STEP * 3)
     out = ps.per_format_applies(trace, fmts, C4_KERNELS)
     assert [len(out[f]) for f in fmts] == [3, 3, 3, 3]
-    assert out["csr"][0][0] == "k_scale<double> + k_xblk<double>"
+    assert out["csr"][0][0] == "k_xblk<double>"
     assert out["sell64"][0][0] == "k_sell<double, true> + k_sell_chunks<double, true>"
     assert out["hyb"][0][0] == "k_ell<double, true> + k_tail<double, true>"
     assert out["hec"][0][0] == "k_ell<double, true> + k_tail<double, false>"
     # durations: dispatch i takes 10 (i + 1) us; the stray one is dispatch 0
-    assert out["csr"][0][1] == 20 + 30 and out["hec"][0][1] == 80 + 90
+    assert out["csr"][0][1] == 20 and out["hec"][0][1] == 70 + 80
 
 
 def test_profile_attribution_trace_from_mid_step():
@@ -207,11 +207,11 @@ def test_profile_attribution_trace_from_mid_step():
     from its first whole apply on; the half apply before it is dropped."""
     import profile_summary as ps
     fmts = ["csr", "sell64", "hyb", "hec"]
-    trace = _trace(["k_sell_chunks<double, true>"] + C4_STEP[4:] + C4_STEP * 2)
+    trace = _trace(["k_sell_chunks<double, true>"] + C4_STEP[3:] + C4_STEP * 2)
     out = ps.per_format_applies(trace, fmts, C4_KERNELS)
     assert [len(out[f]) for f in fmts] == [2, 2, 3, 3]
     assert all(k == "k_ell<double, true> + k_tail<double, true>" for k, _ in out["hyb"])
-    assert all(k == "k_scale<double> + k_xblk<double>" for k, _ in out["csr"])
+    assert all(k == "k_xblk<double>" for k, _ in out["csr"])
     # the C3 case: ELL-R, HYB and HEC all launch k_ell alone; step order decides
     c3 = {"csr": "k_csr_staged<S=4>", "ellr": "k_ell", "sell64": "k_sell (+ k_sell_chunks)",
           "hyb": "k_ell", "hec": "k_ell"}

@@ -738,9 +738,9 @@ XBLOCK_MATS = dict(WINDOW_MATS, scattered=_scattered,
 @pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
 @pytest.mark.parametrize("name", list(XBLOCK_MATS))
 def test_csr_xblock(name, dtype):
-    """CSR by column slices (one per XCD; merged items of entries and row
-    ends, each wave's row sums added into y with atomics after a beta pass)
-    against the oracle, and NaNs in y dropped when beta = 0."""
+    """CSR by column slices (row ranges summed in LDS slice by slice, each
+    range's y written once) against the oracle, and NaNs in y dropped when
+    beta = 0."""
     a = XBLOCK_MATS[name]()
     if dtype == torch.float32:
         a = CSR(a.n, a.rowptr, a.col, a.val.astype(np.float32))
