@@ -94,18 +94,16 @@ typedef enum {
                               counts (at most 20,480 rows in fp64, 40,960
                               in fp32); one workgroup sums a range in LDS,
                               slice by slice, starting with the slice of its
-                              XCD, so each XCD's x reads stay in its L2 (for
-                              x reads scattered over an x larger than one
-                              L2: "Sparse matrix-vector multiplication on
-                              GPGPU clusters", Sect. 2.3, right-hand-side
-                              reuse), then writes the range's y once.
-                              Stores a second copy of the entries, by tile,
-                              with 2-byte row offsets; needs 8 n < 2^31 - 16.
-                              SPMV_CSR_AUTO
-                              times it as well when x is over 4 MiB and
-                              at least half the entries lie outside the
-                              diagonal band of the LDS window, and keeps
-                              it only when clearly faster. */
+                              XCD, so each XCD's x reads stay in its L2
+                              ("Sparse matrix-vector multiplication on GPGPU
+                              clusters", Sect. 2.3, right-hand-side reuse),
+                              then writes the range's y once.  Stores a
+                              second copy of the entries, by tile and by
+                              column inside a tile, with 2-byte row offsets;
+                              needs 8 n < 2^31 - 16.  SPMV_CSR_AUTO times it
+                              as well when x is over 4 MiB and the copy fits
+                              the footprint budget, and keeps it only when
+                              clearly faster. */
 } spmv_csr_kernel;
 
 /* input layout of spmv_create */

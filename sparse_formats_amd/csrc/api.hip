@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <rocprim/device/device_radix_sort.hpp>
 #include <rocprim/device/device_scan.hpp>
+#include <rocprim/device/device_segmented_radix_sort.hpp>
 #include <rocprim/iterator/counting_iterator.hpp>
 
 #include <algorithm>
@@ -1199,6 +1200,41 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
                                h->val.p, pos.as<int>(), b.xb_col.as<int>(), b.xb_val.p,
                                b.xb_lrow.as<uint16_t>(), s),
               "column-slice fill");
+    if (nnz > 0) {
+        // every tile's entries in column order (a stable sort keeps a row's
+        // equal columns in their order): the workgroups of an XCD then sweep
+        // their slice of x together, so each x line is read from that XCD's
+        // L2 by all of them within a short time
+        DevBuf kcol((size_t)nnz * 4), idx((size_t)nnz * 4), src((size_t)nnz * 4);
+        hipLaunchKernelGGL(k_iota, dim3(grid_for(nnz)), dim3(256), 0, s, nnz, idx.as<int>());
+        hip_check(hipGetLastError(), "column-slice sort");
+        unsigned bits = 1;
+        while (bits < 31 && ((int64_t)1 << bits) < n) ++bits;
+        size_t tmp = 0;
+        hip_check(rocprim::segmented_radix_sort_pairs(
+                      nullptr, tmp, b.xb_col.as<unsigned>(), kcol.as<unsigned>(), idx.as<int>(),
+                      src.as<int>(), (unsigned)nnz, (unsigned)ntiles, b.xb_tiles.as<int>(),
+                      b.xb_tiles.as<int>() + 1, 0, bits, s),
+                  "segmented_radix_sort_pairs");
+        {
+            DevBuf work(tmp);
+            hip_check(rocprim::segmented_radix_sort_pairs(
+                          work.p, tmp, b.xb_col.as<unsigned>(), kcol.as<unsigned>(),
+                          idx.as<int>(), src.as<int>(), (unsigned)nnz, (unsigned)ntiles,
+                          b.xb_tiles.as<int>(), b.xb_tiles.as<int>() + 1, 0, bits, s),
+                      "segmented_radix_sort_pairs");
+            sync(s);
+        }
+        idx.release();
+        DevBuf oval((size_t)nnz * h->vsize), olrow((size_t)nnz * 2);
+        hip_check(launch_xblk_gather(nnz, h->dtype == SPMV_F64, src.as<int>(), b.xb_val.p,
+                                     b.xb_lrow.as<uint16_t>(), oval.p, olrow.as<uint16_t>(), s),
+                  "column-slice sort");
+        sync(s);
+        b.xb_col = std::move(kcol);
+        b.xb_val = std::move(oval);
+        b.xb_lrow = std::move(olrow);
+    }
     v.col = b.xb_col.as<int>();
     v.val = b.xb_val.p;
     v.lrow = b.xb_lrow.as<uint16_t>();
@@ -1262,13 +1298,12 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
         if (b.csr_balanced) best_ms = ms;
     }
     if (!b.csr_balanced) b.run_row.release(), b.window = false, b.tail_runs = 0;
-    // third candidate: column slices, for x reads scattered over an x larger
-    // than one XCD's L2 (most entries outside the diagonal band the LDS
-    // window would cover), when its copy of the entries fits the budget
+    // third candidate: column slices, for an x larger than one XCD's L2,
+    // when its copy of the entries fits the budget
     const double xb_bytes = (double)h->nnz * (6.0 + (double)h->vsize) +  // entries, row offsets
                             (double)kXbBlocks * (double)h->n * 8.0;         // counts and their scan
-    if (o.csr_kernel == SPMV_CSR_AUTO && want_bal && !b.window &&
-        (double)h->n * (double)h->vsize > (double)kXbMinX && b.band_fraction < 0.5 &&
+    if (o.csr_kernel == SPMV_CSR_AUTO && want_bal &&
+        (double)h->n * (double)h->vsize > (double)kXbMinX &&
         (int64_t)kXbBlocks * h->n <= (int64_t)INT32_MAX - 16 &&
         xb_bytes <= (double)budget_bytes(o)) {
         Built xb;

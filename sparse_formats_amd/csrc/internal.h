@@ -152,7 +152,7 @@ struct TailView {
 // columns, the rows into ranges of at most kXbCap<T> rows (about equal
 // entry counts).  One workgroup of kXbThreads sums a range in LDS, slice by
 // slice; the entries of range r in slice b (tile (r, b)) are stored
-// together, by row, with each entry's row offset inside its range.
+// together, by column, with each entry's row offset inside its range.
 constexpr int kXbBlocks = 8;
 constexpr int kXbThreads = 1024;
 constexpr int kXbGroups = 256;            // persistent workgroups, one per CU
@@ -165,7 +165,7 @@ struct XblkView {
     int64_t ranges;        // row ranges
     const int* row_begin;  // [ranges + 1] first row of each range, then n
     const int* tile_ptr;   // [ranges * kXbBlocks + 1] first entry of tile (r, b), then nnz
-    const int* col;        // [nnz] tile order
+    const int* col;        // [nnz] tile order, by column inside a tile
     const uint16_t* lrow;  // [nnz] row - row_begin[r]
     const void* val;       // [nnz]
 };
@@ -183,6 +183,9 @@ hipError_t launch_xblk_tiles(const XblkView& a, const int* pos, int* tile_ptr, h
 hipError_t launch_xblk_fill(const XblkView& a, bool f64, const int* rowptr, const int* col,
                             const void* val, const int* pos, int* ocol, void* oval,
                             uint16_t* olrow, hipStream_t stream);
+// setup: oval[k] = val[src[k]], olrow[k] = lrow[src[k]]
+hipError_t launch_xblk_gather(int64_t nnz, bool f64, const int* src, const void* val,
+                              const uint16_t* lrow, void* oval, uint16_t* olrow, hipStream_t stream);
 
 // kernel launchers (asynchronous on `stream`); fp64 when f64, else fp32
 // rows: rows per lane group, a power of two up to kCsrRowsMax; stage_slots >
