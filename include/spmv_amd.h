@@ -97,10 +97,15 @@ typedef enum {
                               XCD, so each XCD's x reads stay in its L2
                               ("Sparse matrix-vector multiplication on GPGPU
                               clusters", Sect. 2.3, right-hand-side reuse),
-                              then writes the range's y once.  Stores a
-                              second copy of the entries, by tile and by
-                              column inside a tile, with 2-byte row offsets;
-                              needs 8 n < 2^31 - 16.  SPMV_CSR_AUTO times it
+                              then writes the range's y once.  When most
+                              entries lie near the diagonal, those within
+                              55,296 (fp64) or 12,288 (fp32) columns of
+                              their range form a ninth tile, summed last,
+                              whose column and row offset share 4 bytes.
+                              Stores a second copy of the entries, by tile
+                              and by column inside a tile, with 2-byte row
+                              offsets outside the band tile; needs 9 n <
+                              2^31 - 16.  SPMV_CSR_AUTO times it
                               as well when x is over 4 MiB and the copy fits
                               the footprint budget, and keeps it only when
                               clearly faster. */

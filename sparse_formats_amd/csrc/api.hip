@@ -1138,11 +1138,13 @@ float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw
 // rows allow), the entry counts of every row in every slice at their
 // xblk_slot positions, their scan (every entry's place), the tile starts and
 // the entries in tile order with their row offsets.
+double entries_within(const spmv_handle* h, int64_t lead, hipStream_t s);
+
 void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
     const int64_t n = h->n, nnz = h->nnz;
-    if ((int64_t)kXbBlocks * n > (int64_t)INT32_MAX - 16)
+    if ((int64_t)kXbTiles * n > (int64_t)INT32_MAX - 16)
         fail(SPMV_ERR_INVALID_ARG, "csr_kernel 3 (column slices) takes n <= %lld rows (got %lld)",
-             (long long)(((int64_t)INT32_MAX - 16) / kXbBlocks), (long long)n);
+             (long long)(((int64_t)INT32_MAX - 16) / kXbTiles), (long long)n);
     b.csr_xblock = true;
     XblkView& v = b.xb;
     v = XblkView{};
@@ -1150,6 +1152,12 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
     v.width = std::max<int64_t>((n + kXbBlocks - 1) / kXbBlocks, 1);
     if (n == 0) return;
     const int cap = h->dtype == SPMV_F64 ? kXbCap<double> : kXbCap<float>;
+    // a range's band tile: columns within `band` of its rows, packed with
+    // the row offsets (band + cap + band columns fit the column bits); none
+    // (band -1) unless most entries lie that close to their row
+    v.lbits = h->dtype == SPMV_F64 ? kXbRowBits<double> : kXbRowBits<float>;
+    v.band = xblk_band(v.lbits, cap);
+    if (entries_within(h, v.band, s) < 0.5) v.band = -1;
     const int64_t passes = std::max<int64_t>(1, (n + (int64_t)kXbGroups * cap - 1) /
                                                     ((int64_t)kXbGroups * cap));
     const int64_t R0 = passes * kXbGroups;
@@ -1169,7 +1177,7 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
     hip_check(hipMemcpyAsync(b.xb_rows.p, rows.data(), rows.size() * 4, hipMemcpyHostToDevice, s),
               "hipMemcpyAsync");
     v.row_begin = b.xb_rows.as<int>();
-    const int64_t slots = (int64_t)kXbBlocks * n;
+    const int64_t slots = (int64_t)kXbTiles * n;
     DevBuf pos((size_t)(slots + 1) * 4);
     {
         DevBuf cnt((size_t)slots * 4);
@@ -1186,7 +1194,7 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
                   "inclusive_scan");
         sync(s);
     }
-    const int64_t ntiles = v.ranges * kXbBlocks;
+    const int64_t ntiles = v.ranges * kXbTiles;
     b.xb_tiles.alloc((size_t)(ntiles + 1) * 4);
     hip_check(launch_xblk_tiles(v, pos.as<int>(), b.xb_tiles.as<int>(), s), "column-slice tiles");
     hip_check(hipMemcpyAsync(b.xb_tiles.as<int>() + ntiles, pos.as<int>() + slots, 4,
@@ -1208,8 +1216,7 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
         DevBuf kcol((size_t)nnz * 4), idx((size_t)nnz * 4), src((size_t)nnz * 4);
         hipLaunchKernelGGL(k_iota, dim3(grid_for(nnz)), dim3(256), 0, s, nnz, idx.as<int>());
         hip_check(hipGetLastError(), "column-slice sort");
-        unsigned bits = 1;
-        while (bits < 31 && ((int64_t)1 << bits) < n) ++bits;
+        const unsigned bits = 32;  // band tiles hold packed words
         size_t tmp = 0;
         hip_check(rocprim::segmented_radix_sort_pairs(
                       nullptr, tmp, b.xb_col.as<unsigned>(), kcol.as<unsigned>(), idx.as<int>(),
@@ -1301,10 +1308,10 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     // third candidate: column slices, for an x larger than one XCD's L2,
     // when its copy of the entries fits the budget
     const double xb_bytes = (double)h->nnz * (6.0 + (double)h->vsize) +  // entries, row offsets
-                            (double)kXbBlocks * (double)h->n * 8.0;         // counts and their scan
+                            (double)kXbTiles * (double)h->n * 8.0;          // counts and their scan
     if (o.csr_kernel == SPMV_CSR_AUTO && want_bal &&
         (double)h->n * (double)h->vsize > (double)kXbMinX &&
-        (int64_t)kXbBlocks * h->n <= (int64_t)INT32_MAX - 16 &&
+        (int64_t)kXbTiles * h->n <= (int64_t)INT32_MAX - 16 &&
         xb_bytes <= (double)budget_bytes(o)) {
         Built xb;
         bool built = true;
@@ -1367,10 +1374,8 @@ void tune_hec_tail(const spmv_handle* h, int kernel, int col_cache, Built& b, hi
 // apply is then timed with and without it and the faster kept (stencils
 // whose x reads already coalesce gain nothing from it).  `b` must hold the
 // built format.
-// share of the entries whose column lies within the window's reach of their row
-double band_fraction(const spmv_handle* h, hipStream_t s) {
-    const int64_t lead = h->dtype == SPMV_F64 ? EllWinLead<double>::value
-                                              : EllWinLead<float>::value;
+// share of the entries whose column lies within `lead` of their row
+double entries_within(const spmv_handle* h, int64_t lead, hipStream_t s) {
     DevBuf cnt(8);
     hip_check(hipMemsetAsync(cnt.p, 0, 8, s), "hipMemsetAsync");
     if (h->n > 0) {
@@ -1380,6 +1385,12 @@ double band_fraction(const spmv_handle* h, hipStream_t s) {
     }
     const unsigned long long c = read_scalar<unsigned long long>(cnt.p, s);
     return h->nnz ? (double)c / (double)h->nnz : 0.0;
+}
+
+// share of the entries whose column lies within the window's reach of their row
+double band_fraction(const spmv_handle* h, hipStream_t s) {
+    return entries_within(h, h->dtype == SPMV_F64 ? EllWinLead<double>::value
+                                                  : EllWinLead<float>::value, s);
 }
 
 // window offsets are computed in 32 bits: rows and columns plus the window

@@ -81,6 +81,32 @@ __host__ __device__ __forceinline__ int64_t xblk_split_ranges(const int* cand, i
     return R;
 }
 
+// Tile of an entry of column c in the range of rows [rb, rb + nr): the
+// range's band tile kS when c lies within `band` columns of those rows (none
+// when band < 0), else its column slice c / width (< kS).
+__host__ __device__ __forceinline__ int xblk_tile(int64_t c, int64_t rb, int64_t nr, int64_t band,
+                                                  int64_t width, int kS) {
+    return band >= 0 && c >= rb - band && c < rb + nr + band ? kS : (int)(c / width);
+}
+
+// Half-width of a band tile whose entries pack their column, less the
+// band's first column rb - band, above a row offset of lbits bits into one
+// 32-bit word: rb - band .. rb + nr + band spans at most 2^(32 - lbits)
+// columns for ranges of nr <= cap rows.
+__host__ __device__ constexpr int64_t xblk_band(int lbits, int64_t cap) {
+    return (((int64_t)1 << (32 - lbits)) - cap) / 2;
+}
+// The packed word of a band entry (column c, row offset lr) of the range
+// starting at row rb, and its column back.
+__host__ __device__ __forceinline__ uint32_t xblk_pack(int64_t c, int64_t rb, int64_t band, int lr,
+                                                       int lbits) {
+    return ((uint32_t)(c - (rb - band)) << lbits) | (uint32_t)lr;
+}
+__host__ __device__ __forceinline__ int64_t xblk_unpack_col(uint32_t w, int64_t rb, int64_t band,
+                                                            int lbits) {
+    return rb - band + (int64_t)(w >> lbits);
+}
+
 // Position of the count of row i in slice b (kS slices) inside the count
 // array, whose scan gives every entry's place: range r of rows [rb, rb + nr)
 // owns kS * nr consecutive counts, slice-major (slice b's counts of the

@@ -150,22 +150,34 @@ struct TailView {
 
 // CSR by column slices: the columns cut into kXbBlocks slices of `width`
 // columns, the rows into ranges of at most kXbCap<T> rows (about equal
-// entry counts).  One workgroup of kXbThreads sums a range in LDS, slice by
-// slice; the entries of range r in slice b (tile (r, b)) are stored
-// together, by column, with each entry's row offset inside its range.
+// entry counts).  One workgroup of kXbThreads sums a range in LDS, tile by
+// tile: tile (r, b) holds the entries of range r with columns in slice b,
+// except those within `band` columns of the range's rows, which form its
+// last tile (r, kXbBlocks); each tile is stored together, by column, with
+// each entry's row offset inside its range (a band tile packs both into its
+// column word: band + nr + band < 2^(32 - kXbRowBits) columns).
 constexpr int kXbBlocks = 8;
+constexpr int kXbTiles = kXbBlocks + 1;  // the slices, then the range's band
 constexpr int kXbThreads = 1024;
 constexpr int kXbGroups = 256;            // persistent workgroups, one per CU
 constexpr int kXbLdsBytes = 160 * 1024;   // the range's partial sums
 template <typename T>
 constexpr int kXbCap = kXbLdsBytes / (int)sizeof(T);
+// a band tile stores each entry's column (less the band's first column) and
+// row offset in one 32-bit word, the row offset in the low kXbRowBits bits
+template <typename T>
+constexpr int kXbRowBits = sizeof(T) == 8 ? 15 : 16;
+static_assert(kXbCap<double> <= (1 << kXbRowBits<double>), "row offsets fit");
+static_assert(kXbCap<float> <= (1 << kXbRowBits<float>), "row offsets fit");
 struct XblkView {
     int64_t n;             // matrix rows
     int64_t width;         // columns per slice
     int64_t ranges;        // row ranges
     const int* row_begin;  // [ranges + 1] first row of each range, then n
-    const int* tile_ptr;   // [ranges * kXbBlocks + 1] first entry of tile (r, b), then nnz
-    const int* col;        // [nnz] tile order, by column inside a tile
+    int64_t band;          // entries within band columns of their range form its tile kXbBlocks
+    int lbits;             // kXbRowBits of the dtype
+    const int* tile_ptr;   // [ranges * kXbTiles + 1] first entry of tile (r, b), then nnz
+    const int* col;        // [nnz] tile order, by column inside a tile (band tiles packed)
     const uint16_t* lrow;  // [nnz] row - row_begin[r]
     const void* val;       // [nnz]
 };

@@ -20,11 +20,16 @@
 // lanes of a packet read neighbouring columns (one or two lines for a
 // diagonal band, where several entries share a column), and the workgroups
 // of an XCD, with equal shares of every slice, read each x line within a
-// short time of each other.  Measured on the power-law matrix (4 M rows,
-// 42 M entries): 0.31 ms per apply against 0.40 ms with the entries of a tile
-// in row order (products summed per row by a segmented scan over the lanes);
-// on the FEM block (8 M rows, 398 M entries, 95 % of columns within +-10,000
-// of the diagonal): 1.16 against 3.02 ms.
+// short time of each other.  When most entries lie near the diagonal, those
+// within `band` columns of their range's rows form a ninth tile, summed
+// after the slices, whose entries pack column and row offset into one 4-byte
+// word (12 bytes per fp64 entry instead of 14).
+//
+// Measured per apply (fp64): power-law matrix (4 M rows, 42 M entries) 0.31
+// ms against 0.40 ms with the entries of a tile in row order (products summed
+// per row by a segmented scan over the lanes); FEM block (8 M rows, 398 M
+// entries, 95 % of columns within +-10,000 of the diagonal) 1.05 ms with the
+// packed band tile, 1.16 without it, 3.02 in row order.
 #include "common.h"
 #include "internal.h"
 
@@ -58,8 +63,9 @@ __device__ __forceinline__ T ld_nt_at(const T* base, uint32_t off) {
 // would make the compiler wait for each earlier load before the next gather,
 // and so would a select on a loaded value here: the row offsets are masked
 // when they are used.  The wave's entries are addressed from pb = min(p, e1
-// - 1), so every offset is below 64 U.
-template <typename T, int U>
+// - 1), so every offset is below 64 U.  A packed (band) tile has no row
+// offset array: c holds column and row offset.
+template <typename T, int U, bool kPk>
 __device__ __forceinline__ void xb_load(const XblkView& a, int p, int e1, int lane,
                                         XbPackets<T, U>& q) {
     const int pb = min(p, e1 - 1);  // wave-uniform
@@ -74,60 +80,81 @@ __device__ __forceinline__ void xb_load(const XblkView& a, int p, int e1, int la
     for (int u = 0; u < U; ++u) q.c[u] = ld_nt_at(col, o[u] * 4);
 #pragma unroll
     for (int u = 0; u < U; ++u) q.v[u] = ld_nt_at(val, o[u] * (uint32_t)sizeof(T));
+    if constexpr (!kPk) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) q.lr[u] = ld_nt_at(lrow, o[u] * 2);
+        for (int u = 0; u < U; ++u) q.lr[u] = ld_nt_at(lrow, o[u] * 2);
+    }
 }
 
 // One round: gather x for the packets in q (at p), load the packets one
 // stride on into nq (past the tile's end they read its last entry again),
 // then add each of q's products into its row's LDS slot.  Columns are below
-// n < 2^28, so their byte offsets in x fit 32 bits.
-template <typename T, int U>
+// n < 2^28, so their byte offsets in x fit 32 bits.  cb: the first column of
+// a packed tile's band.
+template <typename T, int U, bool kPk>
 __device__ __forceinline__ void xb_round(const XblkView& a, const T* __restrict__ x, T* part,
-                                         int p, int e1, int lane, const XbPackets<T, U>& q,
-                                         XbPackets<T, U>& nq) {
+                                         int p, int e1, int lane, int cb,
+                                         const XbPackets<T, U>& q, XbPackets<T, U>& nq) {
     constexpr int kStride = kXbThreads * U;
+    constexpr int LB = kXbRowBits<T>;
     T xv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) xv[u] = ld_at(x, (uint32_t)q.c[u] * (uint32_t)sizeof(T));
-    xb_load(a, p + kStride, e1, lane, nq);
+    for (int u = 0; u < U; ++u) {
+        const uint32_t c = kPk ? (uint32_t)(cb + (int)((uint32_t)q.c[u] >> LB)) : (uint32_t)q.c[u];
+        xv[u] = ld_at(x, c * (uint32_t)sizeof(T));
+    }
+    xb_load<T, U, kPk>(a, p + kStride, e1, lane, nq);
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (p + u * 64 + lane < e1)
-            __hip_atomic_fetch_add(part + q.lr[u], q.v[u] * xv[u], __ATOMIC_RELAXED,
+        if (p + u * 64 + lane < e1) {
+            const int lr = kPk ? (int)((uint32_t)q.c[u] & ((1u << LB) - 1)) : q.lr[u];
+            __hip_atomic_fetch_add(part + lr, q.v[u] * xv[u], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+}
+
+// The sets of packets of one tile: two sets in turn (no register copies
+// between rounds, which would wait for every load in flight): a round
+// gathers x for one set, loads the other, then sums the first.
+template <typename T, int U, bool kPk>
+__device__ __forceinline__ void xb_tile(const XblkView& a, const T* __restrict__ x, T* part,
+                                        int p, int e1, int lane, int cb) {
+    constexpr int kStride = kXbThreads * U;
+    XbPackets<T, U> qa, qb;
+    xb_load<T, U, kPk>(a, p, e1, lane, qa);
+    for (;;) {
+        xb_round<T, U, kPk>(a, x, part, p, e1, lane, cb, qa, qb);
+        p += kStride;
+        if (p >= e1) break;
+        xb_round<T, U, kPk>(a, x, part, p, e1, lane, cb, qb, qa);
+        p += kStride;
+        if (p >= e1) break;
+    }
 }
 
 template <typename T, int U>
 __global__ __launch_bounds__(kXbThreads) void k_xblk(XblkView a, const T* __restrict__ x,
                                                      T* __restrict__ y, T alpha, T beta) {
     __shared__ T part[kXbCap<T>];
-    constexpr int kStride = kXbThreads * U;  // the workgroup's packets of one round
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int first = (int)(blockIdx.x & 7) * (kXbBlocks / 8);  // this XCD's first slice
     for (int64_t r = blockIdx.x; r < a.ranges; r += gridDim.x) {
         const int rb = a.row_begin[r], nr = a.row_begin[r + 1] - rb;
         for (int i = threadIdx.x; i < nr; i += kXbThreads) part[i] = T(0);
         __syncthreads();
-        for (int s = 0; s < kXbBlocks; ++s) {
-            const int b = (first + s) % kXbBlocks;
-            const int e1 = a.tile_ptr[r * kXbBlocks + b + 1];
-            int p = a.tile_ptr[r * kXbBlocks + b] + wv * 64 * U;
-            if (p < e1) {  // wave-uniform, as is the loop below
-                // two sets of packets in turn (no register copies between
-                // rounds, which would wait for every load in flight): a
-                // round gathers x for one set, loads the other, then sums
-                // the first
-                XbPackets<T, U> qa, qb;
-                xb_load(a, p, e1, lane, qa);
-                for (;;) {
-                    xb_round(a, x, part, p, e1, lane, qa, qb);
-                    p += kStride;
-                    if (p >= e1) break;
-                    xb_round(a, x, part, p, e1, lane, qb, qa);
-                    p += kStride;
-                    if (p >= e1) break;
-                }
+        // the slices from this XCD's own on (the workgroups of an XCD, with
+        // equal shares of each slice, read the same slice of x at the same
+        // time), then the range's band
+        for (int s = 0; s < kXbTiles; ++s) {
+            const int b = s < kXbBlocks ? (first + s) % kXbBlocks : kXbBlocks;
+            const int e0 = a.tile_ptr[r * kXbTiles + b], e1 = a.tile_ptr[r * kXbTiles + b + 1];
+            if (e0 == e1) continue;  // an empty tile (uniform): no barrier either
+            const int p = e0 + wv * 64 * U;
+            if (p < e1) {  // wave-uniform
+                if (b < kXbBlocks)
+                    xb_tile<T, U, false>(a, x, part, p, e1, lane, 0);
+                else
+                    xb_tile<T, U, true>(a, x, part, p, e1, lane, rb - (int)a.band);
             }
             // the waves move to the next slice together, so that the x
             // reads of the workgroup stay within one slice
@@ -175,20 +202,18 @@ __global__ __launch_bounds__(256) void k_xblk_count(XblkView a, const int* __res
     for (int64_t i = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); i < a.n;
          i += waves) {
         const int e1 = rowptr[i + 1];
-        int c = 0;  // lane b: entries in slice b
+        const int r = row_of(a.row_begin, 0, (int)a.ranges - 1, i);
+        const int rb = a.row_begin[r], nr = a.row_begin[r + 1] - rb;
+        int c = 0;  // lane b: entries in tile b
         for (int e = rowptr[i] + lane; e - lane < e1; e += 64) {
-            const int b = e < e1 ? (int)(col[e] / a.width) : -1;
+            const int b = e < e1 ? xblk_tile(col[e], rb, nr, a.band, a.width, kXbBlocks) : -1;
 #pragma unroll
-            for (int bb = 0; bb < kXbBlocks; ++bb) {
+            for (int bb = 0; bb < kXbTiles; ++bb) {
                 const int k = __popcll(__ballot(b == bb));
                 c += lane == bb ? k : 0;
             }
         }
-        if (lane < kXbBlocks) {
-            const int r = row_of(a.row_begin, 0, (int)a.ranges - 1, i);
-            const int rb = a.row_begin[r];
-            cnt[xblk_slot(rb, a.row_begin[r + 1] - rb, lane, i, kXbBlocks)] = c;
-        }
+        if (lane < kXbTiles) cnt[xblk_slot(rb, nr, lane, i, kXbTiles)] = c;
     }
 }
 
@@ -196,11 +221,11 @@ __global__ __launch_bounds__(256) void k_xblk_count(XblkView a, const int* __res
 __global__ __launch_bounds__(256) void k_xblk_tiles(XblkView a, const int* __restrict__ pos,
                                                     int* __restrict__ tile_ptr) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= a.ranges * kXbBlocks) return;
-    const int64_t r = t / kXbBlocks;
-    const int b = (int)(t % kXbBlocks);
+    if (t >= a.ranges * kXbTiles) return;
+    const int64_t r = t / kXbTiles;
+    const int b = (int)(t % kXbTiles);
     const int rb = a.row_begin[r];
-    tile_ptr[t] = pos[xblk_slot(rb, a.row_begin[r + 1] - rb, b, rb, kXbBlocks)];
+    tile_ptr[t] = pos[xblk_slot(rb, a.row_begin[r + 1] - rb, b, rb, kXbTiles)];
 }
 
 // setup, one wave per row: copy row i's entries into its tiles in their
@@ -220,26 +245,25 @@ __global__ __launch_bounds__(256) void k_xblk_fill(XblkView a, const int* __rest
          i += waves) {
         const int e1 = rowptr[i + 1];
         const int r = row_of(a.row_begin, 0, (int)a.ranges - 1, i);
-        const int rb = a.row_begin[r];
+        const int rb = a.row_begin[r], nr = a.row_begin[r + 1] - rb;
         const uint16_t lr = (uint16_t)(i - rb);
-        // lane b holds the next position of slice b
-        int at = lane < kXbBlocks
-                     ? pos[xblk_slot(rb, a.row_begin[r + 1] - rb, lane, i, kXbBlocks)]
-                     : 0;
+        // lane b holds the next position of tile b
+        int at = lane < kXbTiles ? pos[xblk_slot(rb, nr, lane, i, kXbTiles)] : 0;
         for (int e = rowptr[i] + lane; e - lane < e1; e += 64) {
             const bool in = e < e1;
             const int cv = in ? col[e] : 0;
-            const int b = in ? (int)(cv / a.width) : -1;
+            const int b = in ? xblk_tile(cv, rb, nr, a.band, a.width, kXbBlocks) : -1;
             int o = 0;
 #pragma unroll
-            for (int bb = 0; bb < kXbBlocks; ++bb) {
+            for (int bb = 0; bb < kXbTiles; ++bb) {
                 const uint64_t mk = __ballot(b == bb);
                 const int p = __shfl(at, bb);
                 if (b == bb) o = p + __popcll(mk & below);
                 at += lane == bb ? __popcll(mk) : 0;
             }
             if (in) {
-                ocol[o] = cv;
+                // a band entry: column less the band's first, and row offset
+                ocol[o] = b == kXbBlocks ? (int)xblk_pack(cv, rb, a.band, lr, a.lbits) : cv;
                 oval[o] = val[e];
                 olrow[o] = lr;
             }
@@ -301,7 +325,7 @@ hipError_t launch_xblk_count(const XblkView& a, const int* rowptr, const int* co
 
 hipError_t launch_xblk_tiles(const XblkView& a, const int* pos, int* tile_ptr, hipStream_t s) {
     if (a.n == 0) return hipSuccess;
-    const int64_t t = a.ranges * kXbBlocks;
+    const int64_t t = a.ranges * kXbTiles;
     hipLaunchKernelGGL(k_xblk_tiles, dim3((unsigned)((t + 255) / 256)), dim3(256), 0, s, a, pos,
                        tile_ptr);
     return hipGetLastError();

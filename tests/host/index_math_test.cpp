@@ -224,6 +224,49 @@ static void test_xblk_ranges() {
     }
 }
 
+static void test_xblk_tiles() {
+    // tile of an entry against the plain definition: band tile kS when the
+    // column lies within band of the range's rows, else its slice; no band
+    // tile when band < 0
+    std::mt19937_64 rng(13);
+    for (int trial = 0; trial < 200000; ++trial) {
+        const int64_t n = 1 + (int64_t)(rng() % (trial & 1 ? (1u << 28) : 5000));
+        const int64_t width = (n + 7) / 8, nr = 1 + (int64_t)(rng() % std::min<int64_t>(n, 20480));
+        const int64_t rb = (int64_t)(rng() % (uint64_t)(n - nr + 1));
+        const int64_t band = trial % 3 == 0 ? -1 : (int64_t)(rng() % 60000);
+        const int64_t c = (int64_t)(rng() % (uint64_t)n);
+        const int t = xblk_tile(c, rb, nr, band, width, 8);
+        const bool near = band >= 0 && c >= rb - band && c < rb + nr + band;
+        CHECK(t == (near ? 8 : (int)(c / width)), "tile of column %lld", (long long)c);
+        CHECK(t >= 0 && t <= 8, "tile in range");
+    }
+    // packing: every column of the band of a range of at most cap rows and
+    // every row offset below cap survive the 32-bit word, at both dtypes'
+    // widths, with the band's first column below 0 and the last near 2^28
+    const int lbs[2] = {15, 16};
+    const int64_t caps[2] = {20480, 40960};
+    for (int k = 0; k < 2; ++k) {
+        const int lb = lbs[k];
+        const int64_t cap = caps[k], band = xblk_band(lb, cap);
+        CHECK(band > 0 && cap + 2 * band <= ((int64_t)1 << (32 - lb)), "band %lld", (long long)band);
+        CHECK(cap <= ((int64_t)1 << lb), "row offsets fit");
+        const int64_t n = ((int64_t)INT_MAX - 16) / 9;
+        const int64_t rbs[3] = {0, 777, n - cap};
+        for (int64_t rb : rbs) {
+            const int64_t lo = rb - band, hi = rb + cap + band;  // columns [lo, hi)
+            for (int64_t c : {lo, lo + 1, rb, rb + cap / 2, hi - 2, hi - 1})
+                for (int lr : {0, 1, (int)cap / 3, (int)cap - 1}) {
+                    const uint32_t w = xblk_pack(c, rb, band, lr, lb);
+                    CHECK(xblk_unpack_col(w, rb, band, lb) == c, "column %lld", (long long)c);
+                    CHECK((int)(w & ((1u << lb) - 1)) == lr, "row offset %d", lr);
+                    // the kernel's form: 32-bit band start plus the shifted word
+                    if (rb - band >= INT_MIN && c < INT_MAX)
+                        CHECK((int64_t)((int)(rb - band) + (int)(w >> lb)) == c, "int form");
+                }
+        }
+    }
+}
+
 static void test_in_window() {
     // the window conversions take n < 2^31 - 1 - 2 WL (WL = 40,960 fp32 entries)
     const int WL32 = 40960, WL64 = 20480;
@@ -309,6 +352,7 @@ int main() {
     test_row_of();
     test_run_next_start();
     test_xblk_ranges();
+    test_xblk_tiles();
     test_in_window();
     test_sell_chunks();
     test_launch_pieces();

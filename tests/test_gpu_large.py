@@ -3,8 +3,9 @@ HIP's 2^32 work-item limit (a group of S lanes per row, G wave groups per
 64-row tile): launches are split, and every format still matches the oracle.
 The largest case is the largest n the library takes, 2^31 - 2 (row and column
 indices up to 2^31 - 3, padded row counts of 2^31); the column-slice CSR
-kernel, which counts the entries of every row in each of 8 slices (8 n
-counts), is refused there and run at the most rows it takes.
+kernel, which counts the entries of every row in each of its 9 tiles (8
+column slices and the row range's band; 9 n counts), is refused there and run
+at the most rows it takes.
 
 The matrix has n rows (300,000,000, then 2^31 - 2), at most three entries in
 a row, and its
@@ -45,8 +46,8 @@ def _triples(N, seed=101):
     return r, c.astype(np.int32), v
 
 
-# the most rows the column-slice CSR kernel takes (8 n counts below 2^31 - 16)
-XB_MAX = (2 ** 31 - 1 - 16) // 8
+# the most rows the column-slice CSR kernel takes (9 n counts below 2^31 - 16)
+XB_MAX = (2 ** 31 - 1 - 16) // 9
 
 
 @pytest.fixture(scope="module", params=SIZES, ids=["300M", "2^31-2"])
@@ -108,7 +109,7 @@ def _check(N, M, x, rows, compact, x_used, what):
 def test_many_rows(large, fmt, kw):
     N, M, x, rows, compact, x_used = large
     if kw.get("csr_kernel") == "xblock":
-        # 8 n counts would pass 2^31: refused, handle kept
+        # 9 n counts would pass 2^31: refused, handle kept
         with pytest.raises(sf.SpmvError) as e:
             M.convert(fmt, **kw)
         assert e.value.code == -1
@@ -126,8 +127,8 @@ def test_many_rows(large, fmt, kw):
 
 
 def test_xblock_most_rows(xb_largest):
-    """The column-slice CSR kernel at the most rows it takes: 8 n counts up
-    to 2^31 - 17, about 13,000 row ranges of at most 20,480 rows."""
+    """The column-slice CSR kernel at the most rows it takes: 9 n counts up
+    to 2^31 - 17, about 11,600 row ranges of at most 20,480 rows."""
     N, M, x, rows, compact, x_used = xb_largest
     M.convert("csr", csr_kernel="xblock")
     assert M.info()["csr_kernel"] == "xblock"
