@@ -22,6 +22,7 @@
 #include <vector>
 
 #include "spmv_amd.h"
+#include "common.h"
 #include "index_math.h"
 #include "internal.h"
 
@@ -108,6 +109,7 @@ struct Built {
     // ELL-R, or the ELL part of HYB / HEC
     int64_t ell_width = 0, ell_bh = 0, ell_rows = 0;  // width, rows per block, padded rows
     DevBuf ell_col, ell_val, ell_len;
+    bool ell_records = false;  // ELLPACK-R: ell_col holds (value, column) slot records
     DevBuf ell_perm;      // sorted ELL part: row at each position (else empty)
     int ell_groups = 1;   // wave groups per 64-row tile
     int sort_window = 0;  // rows per sort window in effect (0: none)
@@ -308,14 +310,27 @@ __global__ void k_ell_fill(int64_t n, int64_t rows, int64_t bh, int64_t W,
                 v = val[k0 + j];
             }
         }
-        ecol[t] = c;
-        eval[t] = v;
+        if (eval) {
+            ecol[t] = c;
+            eval[t] = v;
+        } else {
+            st_rec(ecol, t, v, c);  // records in ecol
+        }
     }
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < rows;
          p += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i = perm && p < n ? perm[p] : p;
         elen[p] = i < n ? (int)std::min<int64_t>(rowptr[i + 1] - rowptr[i], W) : 0;
     }
+}
+
+// out[k * w .. k * w + w) = rec[k * r + o .. k * r + o + w): one field (w ints
+// at int offset o) of each of k records of r ints
+__global__ void k_ell_split(int64_t k, int r, int o, int w, const int* __restrict__ rec,
+                            int* __restrict__ out) {
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < k;
+         t += (int64_t)gridDim.x * blockDim.x)
+        for (int q = 0; q < w; ++q) out[t * w + q] = rec[t * r + o + q];
 }
 
 // Windowed sort of one kEllBlock-row block of the ELL part (one workgroup
@@ -569,7 +584,8 @@ uint64_t budget_bytes(const spmv_convert_opts& o) {
 }
 
 // ELL arrays of width W: one column-major block of all rows (block = 0,
-// ELLPACK-R) or column-major blocks of `block` rows (ELL part of HYB/HEC)
+// ELLPACK-R, whose slots are (value, column) records) or column-major blocks
+// of `block` rows (ELL part of HYB/HEC, separate value and column arrays)
 template <typename V>
 void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, int sigma, Built& b,
                     hipStream_t s) {
@@ -578,8 +594,14 @@ void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, int sigma, B
     b.ell_width = W;
     b.ell_bh = bh;
     b.ell_rows = rows;
-    b.ell_col.alloc((size_t)(W * rows) * 4);
-    b.ell_val.alloc((size_t)(W * rows) * sizeof(V));
+    b.ell_records = block == 0;
+    if (b.ell_records) {
+        b.ell_col.alloc((size_t)(W * rows) * (sizeof(V) + 4));
+        b.ell_val.release();
+    } else {
+        b.ell_col.alloc((size_t)(W * rows) * 4);
+        b.ell_val.alloc((size_t)(W * rows) * sizeof(V));
+    }
     b.ell_len.alloc((size_t)rows * 4);
     b.sort_window = 0;
     if (sigma > 0 && rows > 0) {  // block == kEllBlock, sigma divides it
@@ -592,7 +614,7 @@ void build_ell_part(const spmv_handle* h, int64_t W, int64_t block, int sigma, B
     hipLaunchKernelGGL(k_ell_fill<V>, dim3(grid_for(std::max<int64_t>(W * rows, rows))), dim3(256),
                        0, s, h->n, rows, std::max<int64_t>(bh, 1), W, h->rowptr.as<int>(),
                        h->col.as<int>(), h->val.as<V>(), b.ell_perm.as<int>(), b.ell_col.as<int>(),
-                       b.ell_val.as<V>(), b.ell_len.as<int>());
+                       b.ell_records ? nullptr : b.ell_val.as<V>(), b.ell_len.as<int>());
     hip_check(hipGetLastError(), "ell fill");
 }
 
@@ -954,7 +976,8 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
         case SPMV_HEC: {
             EllView a{(int)h->n, std::max<int64_t>(b.ell_bh, 1), b.ell_width * b.ell_bh,
                       (int)b.ell_width, b.ell_len.as<int>(), b.ell_perm.as<int>(),
-                      b.ell_col.as<int>(), b.ell_val.p, b.window, b.ell_groups, b.col_nt};
+                      b.ell_col.as<int>(), b.ell_records ? nullptr : b.ell_val.p, b.ell_records,
+                      b.window, b.ell_groups, b.col_nt};
             e = launch_ell(a, f64, y, x, alpha, beta, s);
             if (e == hipSuccess && format == SPMV_HEC && b.tail_nnz > 0 && b.tail_vector) {
                 const CsrView t{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
@@ -2234,7 +2257,23 @@ int spmv_export(spmv_t h, int array, void* host_dst, int64_t capacity_bytes, int
         if (capacity_bytes < sz)
             fail(SPMV_ERR_INVALID_ARG, "destination holds %lld bytes, array needs %lld",
                  (long long)capacity_bytes, (long long)sz);
-        if (sz > 0) {
+        if (sz > 0 && b.ell_records && (array == SPMV_A_ELL_COL || array == SPMV_A_ELL_VAL)) {
+            // the slots' columns or values out of the records, in pieces
+            const int64_t slots = b.ell_width * b.ell_rows, piece = (int64_t)1 << 25;
+            const int64_t es = array == SPMV_A_ELL_COL ? 4 : vs;
+            DevBuf tmp((size_t)(std::min(slots, piece) * es));
+            for (int64_t s0 = 0; s0 < slots; s0 += piece) {
+                const int64_t k = std::min(slots - s0, piece);
+                hipLaunchKernelGGL(k_ell_split, dim3(grid_for(k)), dim3(256), 0, nullptr, k,
+                                   (int)(vs / 4 + 1), (int)(array == SPMV_A_ELL_COL ? vs / 4 : 0),
+                                   (int)(es / 4), b.ell_col.as<int>() + s0 * (vs / 4 + 1),
+                                   tmp.as<int>());
+                hip_check(hipGetLastError(), "ell split");
+                hip_check(hipMemcpy((char*)host_dst + s0 * es, tmp.p, (size_t)(k * es),
+                                    hipMemcpyDeviceToHost),
+                          "hipMemcpy");
+            }
+        } else if (sz > 0) {
             hip_check(hipMemcpy(host_dst, src, (size_t)sz, hipMemcpyDeviceToHost), "hipMemcpy");
         }
     });

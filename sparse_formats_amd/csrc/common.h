@@ -24,6 +24,44 @@ __device__ __forceinline__ T ld_nt(const T* p) {
     return __builtin_nontemporal_load(p);
 }
 
+// ELL slot records (ELLPACK-R and the ELL part of HYB/HEC): a slot's value and
+// column side by side, 12 bytes in fp64 (4-byte aligned) and 8 in fp32, so a
+// slot read on its own -- a long row's entries lie a whole column height
+// apart -- costs one cache line instead of one for the value and one for the
+// column.  kNT streams the record past the caches.
+template <typename T>
+constexpr int kRecInts = (int)sizeof(T) / 4 + 1;
+typedef double rec_double __attribute__((aligned(4)));  // a record's value: 4-byte aligned
+typedef float rec_float __attribute__((aligned(4)));
+template <typename T>
+struct RecVal;
+template <>
+struct RecVal<double> {
+    typedef rec_double type;
+};
+template <>
+struct RecVal<float> {
+    typedef rec_float type;
+};
+template <typename T, bool kNT>
+__device__ __forceinline__ void ld_rec(const int* rec, int64_t slot, T& v, int& c) {
+    const int* p = rec + kRecInts<T> * slot;
+    const typename RecVal<T>::type* pv = reinterpret_cast<const typename RecVal<T>::type*>(p);
+    if constexpr (kNT) {
+        v = __builtin_nontemporal_load(pv);
+        c = __builtin_nontemporal_load(p + kRecInts<T> - 1);
+    } else {
+        v = *pv;
+        c = p[kRecInts<T> - 1];
+    }
+}
+template <typename T>
+__device__ __forceinline__ void st_rec(int* rec, int64_t slot, T v, int c) {
+    int* p = rec + kRecInts<T> * slot;
+    *reinterpret_cast<typename RecVal<T>::type*>(p) = v;
+    p[kRecInts<T> - 1] = c;
+}
+
 // Column indices: streamed like the values (kNT), or kept in the caches --
 // when the index array fits the last-level cache beside x, it stays there
 // over repeated applies (the format times both and keeps the faster).

@@ -78,11 +78,12 @@ struct EllView {
     int width;        // slots per row (every row's slots j < width exist)
     const int* len;   // [padded rows], by position
     const int* perm;  // row at each position, or nullptr (position = row)
-    const int* col;
-    const void* val;
+    const int* col;   // columns, or the slot records (value, column) when rec
+    const void* val;  // values (nullptr when rec)
+    bool rec;         // records: kRecInts<T> ints per slot in col (ELLPACK-R)
     bool window;      // stage x in LDS (banded matrices)
     int groups;       // wave groups per 64-row tile (1, 4 or 16; without the window)
-    bool col_nt = true;  // col read without caching (else kept in the caches)
+    bool col_nt = true;  // col (or the records) read without caching (else kept in the caches)
 };
 
 // SELL-64 with x staged in LDS: rows sorted inside windows that divide

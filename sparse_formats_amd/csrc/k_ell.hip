@@ -35,6 +35,49 @@ constexpr int kEllCoopLanes = 16;
 constexpr int kEllCoopMin = 64;
 constexpr int kEllCoopUnroll = 8;
 
+// A row's slots in an ELL layout: records (kRec: value and column side by
+// side, c points at the row's first record) or separate value and column
+// arrays (c, v point at the row's first column and value; the value is
+// streamed, the column by kColNT).  o is the slot offset from the row's first
+// (j times the stride between a row's slots).
+template <typename T, bool kColNT, bool kRec>
+__device__ __forceinline__ void ld_slot(const int* __restrict__ c, const T* __restrict__ v,
+                                        int64_t o, T& vo, int& co) {
+    if constexpr (kRec) {
+        ld_rec<T, kColNT>(c, o, vo, co);
+    } else {
+        vo = ld_nt(v + o);
+        co = ld_col<kColNT>(c + o);
+    }
+}
+
+// The row pointers of ld_slot for the row whose first slot is `base`.
+template <typename T, bool kRec>
+__device__ __forceinline__ void row_ptrs(const int* col, const T* val, int64_t base,
+                                         const int*& c, const T*& v) {
+    c = col + (kRec ? kRecInts<T> : 1) * base;
+    v = kRec ? nullptr : val + base;
+}
+
+// Four slots o, o + d, o + 2 d, o + 3 d of a row (a lane's round of four
+// entries): in the split layout the four values first, then the columns.
+template <typename T, bool kColNT, bool kRec>
+__device__ __forceinline__ void ld4(const int* __restrict__ c, const T* __restrict__ v,
+                                    int64_t o, int64_t d, T& v0, T& v1, T& v2, T& v3, int& c0,
+                                    int& c1, int& c2, int& c3) {
+    if constexpr (kRec) {
+        ld_rec<T, kColNT>(c, o, v0, c0);
+        ld_rec<T, kColNT>(c, o + d, v1, c1);
+        ld_rec<T, kColNT>(c, o + 2 * d, v2, c2);
+        ld_rec<T, kColNT>(c, o + 3 * d, v3, c3);
+    } else {
+        v0 = ld_nt(v + o), v1 = ld_nt(v + o + d);
+        v2 = ld_nt(v + o + 2 * d), v3 = ld_nt(v + o + 3 * d);
+        c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + d);
+        c2 = ld_col<kColNT>(c + o + 2 * d), c3 = ld_col<kColNT>(c + o + 3 * d);
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max_len(T v) {
 #pragma unroll
@@ -42,7 +85,7 @@ __device__ __forceinline__ T wave_max_len(T v) {
     return __builtin_amdgcn_readfirstlane(v);
 }
 
-template <typename T, bool kColNT>
+template <typename T, bool kColNT, bool kRec>
 __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
                                              const int* __restrict__ len,
                                              const int* __restrict__ perm,
@@ -53,26 +96,28 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
     const bool valid = i < n;
     const int L = valid ? len[i] : 0;
     const int64_t base = ell_row_base(i, bh, bstride);
-    const int* c = col + base;
-    const T* v = val + base;
+    const int* c;
+    const T* v;
+    row_ptrs<T, kRec>(col, val, base, c, v);
     T s0 = 0, s1 = 0, s2 = 0, s3 = 0;
     const int M = wave_max_len(L);  // wave-uniform
     int j = 0;
     if (M <= kEllCoopMin) {
         for (; j + 4 <= L; j += 4) {
             const int64_t o = (int64_t)j * bh;
-            const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + bh);
-            const T v2 = ld_nt(v + o + 2 * bh), v3 = ld_nt(v + o + 3 * bh);
-            const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + bh);
-            const int c2 = ld_col<kColNT>(c + o + 2 * bh), c3 = ld_col<kColNT>(c + o + 3 * bh);
+            T v0, v1, v2, v3;
+            int c0, c1, c2, c3;
+            ld4<T, kColNT, kRec>(c, v, o, bh, v0, v1, v2, v3, c0, c1, c2, c3);
             s0 = fma(v0, x[c0], s0);
             s1 = fma(v1, x[c1], s1);
             s2 = fma(v2, x[c2], s2);
             s3 = fma(v3, x[c3], s3);
         }
         for (; j < L; ++j) {
-            const int64_t o = (int64_t)j * bh;
-            s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
+            T v0;
+            int c0;
+            ld_slot<T, kColNT, kRec>(c, v, (int64_t)j * bh, v0, c0);
+            s0 = fma(v0, x[c0], s0);
         }
     } else {
         // lane per row in rounds of 4 while many lanes are busy (j is the
@@ -82,18 +127,19 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
             if (act == 0 || (__popcll(act) <= kEllCoopLanes && M - j >= kEllCoopMin)) break;
             if (j + 4 <= L) {
                 const int64_t o = (int64_t)j * bh;
-                const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + bh);
-                const T v2 = ld_nt(v + o + 2 * bh), v3 = ld_nt(v + o + 3 * bh);
-                const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + bh);
-                const int c2 = ld_col<kColNT>(c + o + 2 * bh), c3 = ld_col<kColNT>(c + o + 3 * bh);
+                T v0, v1, v2, v3;
+                int c0, c1, c2, c3;
+                ld4<T, kColNT, kRec>(c, v, o, bh, v0, v1, v2, v3, c0, c1, c2, c3);
                 s0 = fma(v0, x[c0], s0);
                 s1 = fma(v1, x[c1], s1);
                 s2 = fma(v2, x[c2], s2);
                 s3 = fma(v3, x[c3], s3);
             } else {
                 for (int u = j; u < L; ++u) {
-                    const int64_t o = (int64_t)u * bh;
-                    s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
+                    T v0;
+                    int c0;
+                    ld_slot<T, kColNT, kRec>(c, v, (int64_t)u * bh, v0, c0);
+                    s0 = fma(v0, x[c0], s0);
                 }
             }
             j += 4;
@@ -114,8 +160,14 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
 #pragma unroll
                 for (int u = 0; u < kEllCoopUnroll; ++u) {
                     const int q = q0 + 64 * u;
-                    vv[u] = q < Ll ? ld_nt(val + bl + (int64_t)q * bh) : T(0);
-                    cc[u] = q < Ll ? ld_col<kColNT>(col + bl + (int64_t)q * bh) : 0;
+                    if constexpr (kRec) {
+                        vv[u] = T(0);
+                        cc[u] = 0;
+                        if (q < Ll) ld_rec<T, kColNT>(col, bl + (int64_t)q * bh, vv[u], cc[u]);
+                    } else {
+                        vv[u] = q < Ll ? ld_nt(val + bl + (int64_t)q * bh) : T(0);
+                        cc[u] = q < Ll ? ld_col<kColNT>(col + bl + (int64_t)q * bh) : 0;
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < kEllCoopUnroll; ++u) {
@@ -145,7 +197,7 @@ __global__ __launch_bounds__(256) void k_ell(int n, int64_t bh, int64_t bstride,
 // CU: each thread keeps 16 entries of each of its rows in flight per round
 // (values, columns, then the x reads), and the elements entering the window
 // for the next tile are loaded while the current tile computes.
-template <typename T, bool kColNT>
+template <typename T, bool kColNT, bool kRec>
 __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bstride,
                                                   const int* __restrict__ len,
                                                   const int* __restrict__ perm,
@@ -157,7 +209,9 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
     constexpr int TILE = kEllWinTile;
     constexpr int H = TILE / 1024;  // rows per thread per tile
     constexpr int LEAD = (WL - TILE) / 2;
-    constexpr int B = 16;
+    // entries per round: records take 3 VGPRs and their own 64-bit address
+    // each, so 8 of them (16 would spill)
+    constexpr int B = kRec ? 8 : 16;
     __shared__ T win[WL];
     const int64_t g = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t t0 = g * ntiles / gridDim.x, t1 = (g + 1) * ntiles / gridDim.x;
@@ -199,8 +253,12 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
                 for (int u = 0; u < B; ++u) {
                     const int64_t jj = j + u;
                     if (j + u < L[h]) {
-                        vv[h][u] = ld_nt(val + base + jj * bh);
-                        cc[h][u] = ld_col<kColNT>(col + base + jj * bh);
+                        if constexpr (kRec) {
+                            ld_rec<T, kColNT>(col, base + jj * bh, vv[h][u], cc[h][u]);
+                        } else {
+                            vv[h][u] = ld_nt(val + base + jj * bh);
+                            cc[h][u] = ld_col<kColNT>(col + base + jj * bh);
+                        }
                     } else {
                         vv[h][u] = T(0);
                         cc[h][u] = 0;
@@ -244,7 +302,7 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
 // and gives a row several groups to raise the parallelism of matrices with
 // few, long rows.  Wave g takes the columns g, g + G, g + 2G, ... of its
 // lanes' rows (four in flight); the G partial sums of a row meet in LDS.
-template <typename T, int G, bool kColNT>
+template <typename T, int G, bool kColNT, bool kRec>
 __global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bstride,
                                                    const int* __restrict__ len,
                                                    const int* __restrict__ perm,
@@ -259,23 +317,25 @@ __global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bs
     if (i < n) {
         const int L = len[i];
         const int64_t base = ell_row_base(i, bh, bstride);
-        const int* c = col + base;
-        const T* v = val + base;
+        const int* c;
+        const T* v;
+        row_ptrs<T, kRec>(col, val, base, c, v);
         int j = g;
         for (; j + 3 * G < L; j += 4 * G) {
             const int64_t o = (int64_t)j * bh, d = (int64_t)G * bh;
-            const T v0 = ld_nt(v + o), v1 = ld_nt(v + o + d);
-            const T v2 = ld_nt(v + o + 2 * d), v3 = ld_nt(v + o + 3 * d);
-            const int c0 = ld_col<kColNT>(c + o), c1 = ld_col<kColNT>(c + o + d);
-            const int c2 = ld_col<kColNT>(c + o + 2 * d), c3 = ld_col<kColNT>(c + o + 3 * d);
+            T v0, v1, v2, v3;
+            int c0, c1, c2, c3;
+            ld4<T, kColNT, kRec>(c, v, o, d, v0, v1, v2, v3, c0, c1, c2, c3);
             s0 = fma(v0, x[c0], s0);
             s1 = fma(v1, x[c1], s1);
             s2 = fma(v2, x[c2], s2);
             s3 = fma(v3, x[c3], s3);
         }
         for (; j < L; j += G) {
-            const int64_t o = (int64_t)j * bh;
-            s0 = fma(ld_nt(v + o), x[ld_col<kColNT>(c + o)], s0);
+            T v0;
+            int c0;
+            ld_slot<T, kColNT, kRec>(c, v, (int64_t)j * bh, v0, c0);
+            s0 = fma(v0, x[c0], s0);
         }
     }
     part[g][lane] = (s0 + s1) + (s2 + s3);
@@ -289,7 +349,7 @@ __global__ __launch_bounds__(64 * G) void k_ell_mg(int n, int64_t bh, int64_t bs
     }
 }
 
-template <typename T, bool kColNT>
+template <typename T, bool kColNT, bool kRec>
 static hipError_t run_ell_mg(const EllView& a, void* y, const void* x, double alpha,
                              double beta, hipStream_t stream) {
     const int64_t blocks = ((int64_t)a.n + kWave - 1) / kWave;
@@ -298,32 +358,32 @@ static hipError_t run_ell_mg(const EllView& a, void* y, const void* x, double al
     for (int64_t b0 = 0; b0 < blocks; b0 += per) {
         const int64_t nb = std::min<int64_t>(blocks - b0, per);
         if (a.groups == 16)
-            hipLaunchKernelGGL((k_ell_mg<T, 16, kColNT>), dim3((unsigned)nb), dim3(64 * 16), 0,
-                               stream, a.n, a.bh, a.bstride, a.len, a.perm, a.col,
+            hipLaunchKernelGGL((k_ell_mg<T, 16, kColNT, kRec>), dim3((unsigned)nb), dim3(64 * 16),
+                               0, stream, a.n, a.bh, a.bstride, a.len, a.perm, a.col,
                                (const T*)a.val, (const T*)x, (T*)y, (T)alpha, (T)beta, b0);
         else
-            hipLaunchKernelGGL((k_ell_mg<T, 4, kColNT>), dim3((unsigned)nb), dim3(64 * 4), 0,
+            hipLaunchKernelGGL((k_ell_mg<T, 4, kColNT, kRec>), dim3((unsigned)nb), dim3(64 * 4), 0,
                                stream, a.n, a.bh, a.bstride, a.len, a.perm, a.col,
                                (const T*)a.val, (const T*)x, (T*)y, (T)alpha, (T)beta, b0);
     }
     return hipGetLastError();
 }
 
-template <typename T, bool kColNT>
+template <typename T, bool kColNT, bool kRec>
 static hipError_t run_ell(const EllView& a, void* y, const void* x, double alpha, double beta,
                           hipStream_t stream) {
     if (a.window) {
         const int64_t ntiles = ((int64_t)a.n + kEllWinTile - 1) / kEllWinTile;
         const int64_t g = std::min<int64_t>(ntiles, kWinGroups);
-        hipLaunchKernelGGL((k_ell_win<T, kColNT>), dim3((unsigned)g), dim3(1024), 0, stream, a.n,
-                           a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val, (const T*)x,
-                           (T*)y, (T)alpha, (T)beta, ntiles);
+        hipLaunchKernelGGL((k_ell_win<T, kColNT, kRec>), dim3((unsigned)g), dim3(1024), 0, stream,
+                           a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
+                           (const T*)x, (T*)y, (T)alpha, (T)beta, ntiles);
         return hipGetLastError();
     }
-    if (a.groups > 1) return run_ell_mg<T, kColNT>(a, y, x, alpha, beta, stream);
+    if (a.groups > 1) return run_ell_mg<T, kColNT, kRec>(a, y, x, alpha, beta, stream);
     const int64_t blocks = ((int64_t)a.n + 255) / 256;
-    hipLaunchKernelGGL((k_ell<T, kColNT>), dim3((unsigned)blocks), dim3(256), 0, stream, a.n, a.bh,
-                       a.bstride, a.len, a.perm, a.col, (const T*)a.val, (const T*)x, (T*)y,
+    hipLaunchKernelGGL((k_ell<T, kColNT, kRec>), dim3((unsigned)blocks), dim3(256), 0, stream, a.n,
+                       a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val, (const T*)x, (T*)y,
                        (T)alpha, (T)beta);
     return hipGetLastError();
 }
@@ -331,11 +391,18 @@ static hipError_t run_ell(const EllView& a, void* y, const void* x, double alpha
 hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double alpha,
                       double beta, hipStream_t stream) {
     if (a.n <= 0) return hipSuccess;
+    if (a.rec) {
+        if (f64)
+            return a.col_nt ? run_ell<double, true, true>(a, y, x, alpha, beta, stream)
+                            : run_ell<double, false, true>(a, y, x, alpha, beta, stream);
+        return a.col_nt ? run_ell<float, true, true>(a, y, x, alpha, beta, stream)
+                        : run_ell<float, false, true>(a, y, x, alpha, beta, stream);
+    }
     if (f64)
-        return a.col_nt ? run_ell<double, true>(a, y, x, alpha, beta, stream)
-                        : run_ell<double, false>(a, y, x, alpha, beta, stream);
-    return a.col_nt ? run_ell<float, true>(a, y, x, alpha, beta, stream)
-                    : run_ell<float, false>(a, y, x, alpha, beta, stream);
+        return a.col_nt ? run_ell<double, true, false>(a, y, x, alpha, beta, stream)
+                        : run_ell<double, false, false>(a, y, x, alpha, beta, stream);
+    return a.col_nt ? run_ell<float, true, false>(a, y, x, alpha, beta, stream)
+                    : run_ell<float, false, false>(a, y, x, alpha, beta, stream);
 }
 
 // ---------------------------------------------------------------------------
