@@ -14,6 +14,8 @@
  *             (64 on gfx950), plus the length of every row so that work
  *             stops at the row's end ("Sparse matrix-vector multiplication
  *             on GPGPU clusters", Sect. 2.1, Fig. 1, footnote 2, Fig. 2b).
+ *             Each slot keeps its value and column side by side (one
+ *             record), so a slot read on its own costs one cache line.
  *   SELL-64   the pJDS idea of the same page (Sect. 2.2): rows sorted by
  *             length, longest first, cut into blocks of 64 rows each padded
  *             to its longest row, stored block by block, with the row
@@ -208,9 +210,10 @@ typedef struct {
      * directly.  The sums are the same either way.  -1 times both, 0 off,
      * 1 on. */
     int32_t csr_stage;
-    /* Cache policy of the column indices (ELL-R, SELL-64, the ELL part of
-     * HYB/HEC, the staged CSR copy): 0 streams them past the caches like the
-     * values, 1 keeps them in the caches (when they fit the last-level cache
+    /* Cache policy of the column indices (ELL-R, whose records hold value
+     * and column together, SELL-64, the ELL part of HYB/HEC, the staged CSR
+     * copy): 0 streams them past the caches like the values, 1 keeps them
+     * (ELL-R: the records) in the caches (when they fit the last-level cache
      * beside x they stay there over applies that follow one another with
      * nothing else in between), -1 (default) streams them: with other work
      * between two applies (a solver's vector updates, other matrices) the
@@ -265,7 +268,9 @@ typedef enum {
                               column-major blocks of B = ell_stride rows: entry j
                               of row i at (i / B) * width * B + j * B + i % B
                               (ELL-R: a single block, B = 64 * ceil(n / 64);
-                              HYB/HEC: B = 1024) */
+                              HYB/HEC: B = 1024).  ELL-R stores each slot as a
+                              (value, column) record; its columns and values
+                              are exported as these two arrays */
     SPMV_A_ELL_VAL = 4,    /* dtype[width * ell_rows]; pad slots col 0, value +0 */
     SPMV_A_ELL_LEN = 5,    /* int32[ell_rows]: entries of each row held in ELL */
     SPMV_A_SELL_PERM = 6,  /* int32[n]: original row at sorted position r */
