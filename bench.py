@@ -68,6 +68,8 @@ def kernels_of(fmt: str, info: dict) -> str:
                                                     info["tail_stage_slots"]))
     if fmt in ("ellr", "hyb", "hec") and info.get("x_window"):
         k = k.replace("k_ell", "k_ell_win").replace("k_tail", "k_tail_win")
+    if fmt == "ellr" and info.get("ell_long_rows", 0) > 0:
+        k += " + k_ell_long"  # the rows longer than the window kernel's head
     if fmt == "sell64" and info.get("x_window"):
         k = "(k_sell_wide_beta +) k_sell_win"
     return k
@@ -192,6 +194,8 @@ def kernel_bases(fmt: str, info: dict) -> set:
     if fmt == "sell64":
         return {"k_sell_win"} if info.get("x_window") else {"k_sell"}
     out = {"k_ell" + win}
+    if fmt == "ellr" and info.get("ell_long_rows", 0) > 0:
+        out.add("k_ell_long")
     if fmt == "hec" and info.get("tail_nnz", 0) > 0 and info.get("tail_kernel") == "vector":
         out.add("k_csr_staged" if info.get("tail_stage_slots", 0) > 0 else "k_csr_vector")
     elif fmt in ("hyb", "hec") and info.get("tail_nnz", 0) > 0:

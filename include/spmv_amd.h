@@ -257,6 +257,10 @@ typedef struct {
     int32_t tail_rows;     /* group and LDS slots per wave (0: direct); */
     int32_t tail_stage_slots; /* all 0 otherwise */
     int32_t col_cached;    /* 1 when the active kernels keep col in the caches */
+    int32_t ell_head;      /* ELL-R with the x window: slots of every row the
+                              window kernel takes; the ell_long_rows longer rows
+                              get the rest from a wave each (0: no split) */
+    int64_t ell_long_rows;
 } spmv_info_t;
 
 /* arrays readable with spmv_export */

@@ -39,7 +39,7 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 FORMATS = ["csr-vector", "csr-balanced", "csr-xblock", "ellr", "sell64", "hyb", "hec"]
 APPLY = ("k_csr_vector", "k_csr_staged", "k_scale", "k_tail", "k_tail_win", "k_ell", "k_ell_win", "k_sell",
-         "k_sell_chunks", "k_sell_win", "k_sell_wide_beta", "k_xblk")
+         "k_sell_chunks", "k_sell_win", "k_sell_wide_beta", "k_xblk", "k_ell_long")
 # kernels an apply launches only for some matrices: SELL-64's chunk kernel
 # after k_sell, and its beta pass over the wide slices before k_sell_win
 OPTIONAL_AFTER = {"k_sell": "k_sell_chunks"}

@@ -80,7 +80,8 @@ class _Info(ctypes.Structure):
                 ("ell_rows", ctypes.c_int64), ("csr_stage_slots", ctypes.c_int32),
                 ("tail_kernel", ctypes.c_int32), ("tail_subwave", ctypes.c_int32),
                 ("tail_rows", ctypes.c_int32), ("tail_stage_slots", ctypes.c_int32),
-                ("col_cached", ctypes.c_int32)]
+                ("col_cached", ctypes.c_int32), ("ell_head", ctypes.c_int32),
+                ("ell_long_rows", ctypes.c_int64)]
 
 
 def _load():

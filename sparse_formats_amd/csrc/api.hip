@@ -9,6 +9,7 @@
 #include <rocprim/device/device_radix_sort.hpp>
 #include <rocprim/device/device_scan.hpp>
 #include <rocprim/device/device_segmented_radix_sort.hpp>
+#include <rocprim/device/device_select.hpp>
 #include <rocprim/iterator/counting_iterator.hpp>
 
 #include <algorithm>
@@ -110,6 +111,11 @@ struct Built {
     int64_t ell_width = 0, ell_bh = 0, ell_rows = 0;  // width, rows per block, padded rows
     DevBuf ell_col, ell_val, ell_len;
     bool ell_records = false;  // ELLPACK-R: ell_col holds (value, column) slot records
+    // ELLPACK-R with the x window and a few long rows: the window kernel takes
+    // each row's first ell_head slots, a wave per row of ell_long the rest
+    int ell_head = 0x7fffffff;
+    DevBuf ell_long;
+    int64_t ell_nlong = 0;
     DevBuf ell_perm;      // sorted ELL part: row at each position (else empty)
     int ell_groups = 1;   // wave groups per 64-row tile
     int sort_window = 0;  // rows per sort window in effect (0: none)
@@ -149,7 +155,7 @@ struct Built {
                perm.bytes + sell_col.bytes + sell_val.bytes + chunks.bytes + chunk_off.bytes +
                tail_row.bytes +
                tail_ptr.bytes + tail_col.bytes + tail_val.bytes + run_row.bytes + tail_rows.bytes +
-               tail_cptr.bytes + xb_rows.bytes + xb_tiles.bytes + xb_col.bytes + xb_val.bytes +
+               tail_cptr.bytes + ell_long.bytes + xb_rows.bytes + xb_tiles.bytes + xb_col.bytes + xb_val.bytes +
                xb_lrow.bytes;
     }
 };
@@ -978,7 +984,10 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
                       (int)b.ell_width, b.ell_len.as<int>(), b.ell_perm.as<int>(),
                       b.ell_col.as<int>(), b.ell_records ? nullptr : b.ell_val.p, b.ell_records,
                       b.window, b.ell_groups, b.col_nt};
+            if (b.window) a.head = b.ell_head;
             e = launch_ell(a, f64, y, x, alpha, beta, s);
+            if (e == hipSuccess && b.window && b.ell_nlong > 0)
+                e = launch_ell_long(a, b.ell_long.as<int>(), b.ell_nlong, f64, y, x, alpha, s);
             if (e == hipSuccess && format == SPMV_HEC && b.tail_nnz > 0 && b.tail_vector) {
                 const CsrView t{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
                                 b.tail_col.as<int>(), b.tail_val.p, b.tail_rows.as<int>()};
@@ -1422,16 +1431,60 @@ bool window_fits(const spmv_handle* h) {
     return h->n < INT32_MAX - 2 * (int64_t)WinLen<float>::value;
 }
 
+// ELLPACK-R rows longer than kEllWinHeadMax are not run whole by the window
+// kernel (one lane per row): it takes every row's first `head` slots -- the
+// width that holds 99 % of the rows whole, a multiple of 8 up to
+// kEllWinHeadMax -- and a wave per longer row takes the rest
+constexpr int kEllWinHeadMax = 128;
+
+__global__ void k_long_flags(int64_t n, const int* __restrict__ len, int head,
+                             unsigned char* __restrict__ flag) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        flag[i] = len[i] > head ? 1 : 0;
+}
+
+void ell_window_split(const spmv_handle* h, Built& b, hipStream_t s) {
+    b.ell_long.release();
+    b.ell_nlong = 0;
+    b.ell_head = 0x7fffffff;
+    if (h->max_len <= kEllWinHeadMax || h->n == 0) return;
+    std::vector<int> hist;
+    const int64_t k = choose_width(h, kRegularWidth, hist, s);
+    b.ell_head = (int)std::min<int64_t>(std::max<int64_t>((k + 7) / 8 * 8, 8), kEllWinHeadMax);
+    DevBuf flag((size_t)h->n), cnt(8), rows((size_t)h->n * 4);
+    hipLaunchKernelGGL(k_long_flags, dim3(grid_for(h->n)), dim3(256), 0, s, h->n,
+                       b.ell_len.as<int>(), b.ell_head, flag.as<unsigned char>());
+    hip_check(hipGetLastError(), "long rows");
+    rocprim::counting_iterator<int> iota(0);
+    size_t tmp = 0;
+    hip_check(rocprim::select(nullptr, tmp, iota, flag.as<unsigned char>(), rows.as<int>(),
+                              cnt.as<int64_t>(), (size_t)h->n, s),
+              "select");
+    DevBuf work(tmp);
+    hip_check(rocprim::select(work.p, tmp, iota, flag.as<unsigned char>(), rows.as<int>(),
+                              cnt.as<int64_t>(), (size_t)h->n, s),
+              "select");
+    b.ell_nlong = read_scalar<int64_t>(cnt.as<int64_t>(), s);
+    b.ell_long.alloc((size_t)std::max<int64_t>(b.ell_nlong, 1) * 4);
+    hip_check(hipMemcpyAsync(b.ell_long.p, rows.p, (size_t)b.ell_nlong * 4,
+                             hipMemcpyDeviceToDevice, s),
+              "hipMemcpyAsync");
+    sync(s);
+}
+
 void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStream_t s) {
     b.band_fraction = band_fraction(h, s);
     const bool fits = window_fits(h);
+    const bool split = format == SPMV_ELLR;  // ELLPACK-R: long rows past a head
     if (opt >= 0) {
         b.window = opt == 1 && fits;
+        if (b.window && split) ell_window_split(h, b, s);
         return;
     }
-    b.window = fits && h->nnz > 0 && b.band_fraction >= 0.5 &&
-               (format != SPMV_ELLR || h->max_len <= 128);
+    b.window = fits && h->nnz > 0 && b.band_fraction >= 0.5;
     if (!b.window) return;
+    if (split) ell_window_split(h, b, s);
     DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
     hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
     auto run = [&] { return launch_built(h, b, format, ys.p, xs.p, 1.0, 0.0, s); };
@@ -1439,6 +1492,7 @@ void decide_window(const spmv_handle* h, int format, int opt, Built& b, hipStrea
     b.window = false;
     const float without = time_launches(run, s);
     b.window = with < kPreferMargin * without;
+    if (!b.window) b.ell_long.release(), b.ell_nlong = 0, b.ell_head = 0x7fffffff;
 }
 
 int run_guarded(const std::function<void()>& body) {
@@ -2217,6 +2271,8 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
                        ? b.ell_groups
                        : 0;
     i.permuted_basis = h->format == SPMV_SELL64 && b.permuted ? 1 : 0;
+    i.ell_head = h->format == SPMV_ELLR && b.window && b.ell_nlong > 0 ? b.ell_head : 0;
+    i.ell_long_rows = i.ell_head ? b.ell_nlong : 0;
     i.band_fraction = b.band_fraction;
     *out = i;
     return SPMV_OK;

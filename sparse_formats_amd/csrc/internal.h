@@ -84,7 +84,13 @@ struct EllView {
     bool window;      // stage x in LDS (banded matrices)
     int groups;       // wave groups per 64-row tile (1, 4 or 16; without the window)
     bool col_nt = true;  // col (or the records) read without caching (else kept in the caches)
+    int head = 0x7fffffff;  // the window kernel takes each row's first head slots
 };
+// ELLPACK-R records past the window kernel's head: one wave per row of
+// `rows` (nlong rows longer than a.head) adds alpha times the sum of its
+// slots a.head .. len - 1 onto y
+hipError_t launch_ell_long(const EllView& a, const int* rows, int64_t nlong, bool f64, void* y,
+                           const void* x, double alpha, hipStream_t stream);
 
 // SELL-64 with x staged in LDS: rows sorted inside windows that divide
 // kEllWinTile, so a tile of kEllWinTile sorted positions (kEllWinTile / 64

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
                                                   const int* __restrict__ col,
                                                   const T* __restrict__ val,
                                                   const T* __restrict__ x, T* __restrict__ y,
-                                                  T alpha, T beta, int64_t ntiles) {
+                                                  T alpha, T beta, int64_t ntiles, int head) {
     constexpr int WL = WinLen<T>::value;
     constexpr int TILE = kEllWinTile;
     constexpr int H = TILE / 1024;  // rows per thread per tile
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
 #pragma unroll
         for (int h = 0; h < H; ++h) {
             row[h] = t * TILE + tid + 1024 * h;
-            L[h] = row[h] < n ? len[row[h]] : 0;
+            L[h] = row[h] < n ? min(len[row[h]], head) : 0;
             Lmax = max(Lmax, L[h]);
         }
         T sum[H][2] = {};
@@ -427,7 +427,7 @@ static hipError_t run_ell(const EllView& a, void* y, const void* x, double alpha
         const int64_t g = std::min<int64_t>(ntiles, kWinGroups);
         hipLaunchKernelGGL((k_ell_win<T, kColNT, kRec>), dim3((unsigned)g), dim3(1024), 0, stream,
                            a.n, a.bh, a.bstride, a.len, a.perm, a.col, (const T*)a.val,
-                           (const T*)x, (T*)y, (T)alpha, (T)beta, ntiles);
+                           (const T*)x, (T*)y, (T)alpha, (T)beta, ntiles, a.head);
         return hipGetLastError();
     }
     if (a.groups > 1) return run_ell_mg<T, kColNT, kRec>(a, y, x, alpha, beta, stream);
@@ -453,6 +453,63 @@ hipError_t launch_ell(const EllView& a, bool f64, void* y, const void* x, double
                         : run_ell<double, false, false>(a, y, x, alpha, beta, stream);
     return a.col_nt ? run_ell<float, true, false>(a, y, x, alpha, beta, stream)
                     : run_ell<float, false, false>(a, y, x, alpha, beta, stream);
+}
+
+// ELLPACK-R with the x window for a matrix with a few long rows: the window
+// kernel takes every row's first `head` slots, then one wave per long row
+// (the list holds the rows longer than head) takes the rest, with the long-row
+// loop of the plain kernel, and adds alpha times its sum onto y (the row's
+// only writer after the window kernel).  Up to kEllLongWaves waves, each
+// taking rows w, w + waves, ...
+constexpr int kEllLongWaves = 16384;
+template <typename T, bool kColNT>
+__global__ __launch_bounds__(256) void k_ell_long(int64_t bh, const int* __restrict__ len,
+                                                  const int* __restrict__ rows, int64_t nlong,
+                                                  int head, const int* __restrict__ rec,
+                                                  const T* __restrict__ x, T* __restrict__ y,
+                                                  T alpha) {
+    constexpr int U = kEllRecUnroll;
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t)gridDim.x * 4;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < nlong; w += waves) {
+        const int i = rows[w];
+        const int Ll = len[i];  // > head
+        T p0 = 0, p1 = 0;
+        T va[U], vb[U];
+        int ca[U], cb[U];
+        int q0 = head + lane;
+        ell_coop_load<T, kColNT, U>(rec, i, bh, q0, Ll, va, ca);
+        for (;;) {
+            ell_coop_round<T, kColNT, U>(rec, x, i, bh, q0, Ll, va, ca, vb, cb, p0, p1);
+            q0 += 64 * U;
+            if (q0 - lane >= Ll) break;
+            ell_coop_round<T, kColNT, U>(rec, x, i, bh, q0, Ll, vb, cb, va, ca, p0, p1);
+            q0 += 64 * U;
+            if (q0 - lane >= Ll) break;
+        }
+        const T tot = group_sum<64>(p0 + p1);
+        if (lane == 0) y[i] += alpha * tot;
+    }
+}
+
+template <typename T, bool kColNT>
+static hipError_t run_ell_long(const EllView& a, const int* rows, int64_t nlong, void* y,
+                               const void* x, double alpha, hipStream_t stream) {
+    const int64_t g = std::min<int64_t>((nlong + 3) / 4, kEllLongWaves / 4);
+    hipLaunchKernelGGL((k_ell_long<T, kColNT>), dim3((unsigned)g), dim3(256), 0, stream, a.bh,
+                       a.len, rows, nlong, a.head, a.col, (const T*)x, (T*)y, (T)alpha);
+    return hipGetLastError();
+}
+
+hipError_t launch_ell_long(const EllView& a, const int* rows, int64_t nlong, bool f64, void* y,
+                           const void* x, double alpha, hipStream_t stream) {
+    if (nlong <= 0) return hipSuccess;
+    if (!a.rec || a.perm) return hipErrorInvalidValue;  // ELLPACK-R records, rows in place
+    if (f64)
+        return a.col_nt ? run_ell_long<double, true>(a, rows, nlong, y, x, alpha, stream)
+                        : run_ell_long<double, false>(a, rows, nlong, y, x, alpha, stream);
+    return a.col_nt ? run_ell_long<float, true>(a, rows, nlong, y, x, alpha, stream)
+                    : run_ell_long<float, false>(a, rows, nlong, y, x, alpha, stream);
 }
 
 // ---------------------------------------------------------------------------

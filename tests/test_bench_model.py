@@ -250,3 +250,29 @@ def test_profile_attribution_sell_window():
     assert ps.split_apply([("k_copy", "k_copy")] + seq) == seq
     with pytest.raises(AssertionError):
         ps.split_apply([("k_copy", "k_copy")])
+
+
+def test_profile_attribution_ell_window_long_rows():
+    """ELL-R with the LDS window and a few long rows: the window kernel takes
+    every row's head, then k_ell_long the long rows' rest; one apply of two
+    kernels, named alike by the bench and the profile summary (the FEM block's
+    step: column-slice CSR, ELL-R, SELL-64, HYB, HEC)."""
+    import profile_summary as ps
+    info = {"x_window": 1, "ell_long_rows": 80000, "ell_head": 40}
+    assert bench.kernels_of("ellr", info) == "k_ell_win + k_ell_long"
+    assert bench.kernel_bases("ellr", info) == {"k_ell_win", "k_ell_long"}
+    assert bench.kernels_of("ellr", {"x_window": 1, "ell_long_rows": 0}) == "k_ell_win"
+    c5 = {"csr": "k_xblk", "ellr": "k_ell_win + k_ell_long",
+          "sell64": "(k_sell_wide_beta +) k_sell_win", "hyb": "k_ell_win + k_tail_win<COO>",
+          "hec": "k_ell_win + k_tail_win<CSR>"}
+    f5 = list(c5)
+    step = ["k_xblk<double, 8>", "k_ell_win<double, true, true>", "k_ell_long<double, true>",
+            "k_sell_wide_beta<double>", "k_sell_win<double, true>",
+            "k_ell_win<double, true, false>", "k_tail_win<double, true>",
+            "k_ell_win<double, true, false>", "k_tail_win<double, false>"]
+    out = ps.per_format_applies(_trace(step * 3), f5, c5)
+    assert [len(out[f]) for f in f5] == [3] * 5
+    assert out["ellr"][0][0] == "k_ell_win<double, true, true> + k_ell_long<double, true>"
+    assert out["hyb"][2][0] == "k_ell_win<double, true, false> + k_tail_win<double, true>"
+    # durations: dispatch i takes 10 (i + 1) us, the step's second apply is dispatches 1-2
+    assert out["ellr"][0][1] == 20 + 30
