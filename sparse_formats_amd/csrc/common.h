@@ -55,6 +55,21 @@ __device__ __forceinline__ void ld_rec(const int* rec, int64_t slot, T& v, int& 
         c = p[kRecInts<T> - 1];
     }
 }
+// The record at byte offset `off` from a wave-uniform address: one scalar
+// base and a 32-bit offset per lane (no 64-bit address per lane).
+template <typename T, bool kNT>
+__device__ __forceinline__ void ld_rec_at(const int* base, uint32_t off, T& v, int& c) {
+    const char* b = reinterpret_cast<const char*>(base) + off;
+    const typename RecVal<T>::type* pv = reinterpret_cast<const typename RecVal<T>::type*>(b);
+    const int* pc = reinterpret_cast<const int*>(b + sizeof(T));
+    if constexpr (kNT) {
+        v = __builtin_nontemporal_load(pv);
+        c = __builtin_nontemporal_load(pc);
+    } else {
+        v = *pv;
+        c = *pc;
+    }
+}
 template <typename T>
 __device__ __forceinline__ void st_rec(int* rec, int64_t slot, T v, int c) {
     int* p = rec + kRecInts<T> * slot;

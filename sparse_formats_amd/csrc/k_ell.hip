@@ -35,6 +35,8 @@ namespace spmv {
 constexpr int kEllCoopLanes = 16;
 constexpr int kEllCoopMin = 64;
 constexpr int kEllCoopUnroll = 8;
+// ELLPACK-R records in the window kernel: entries per round
+constexpr int kEllWinRecB = 16;
 // ELLPACK-R records: two sets of 4 in turn (the next set loads while the
 // current one's x reads are in flight); measured on the FEM block's long rows
 // against 8 at a time without the second set: 4.81 against 5.01 ms per apply
@@ -259,9 +261,9 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
     constexpr int TILE = kEllWinTile;
     constexpr int H = TILE / 1024;  // rows per thread per tile
     constexpr int LEAD = (WL - TILE) / 2;
-    // entries per round: records take 3 VGPRs and their own 64-bit address
-    // each, so 8 of them (16 would spill)
-    constexpr int B = kRec ? 8 : 16;
+    // entries per round (records: addressed from a uniform base, so 16 fit
+    // the registers as well)
+    constexpr int B = kRec ? kEllWinRecB : 16;
     __shared__ T win[WL];
     const int64_t g = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t t0 = g * ntiles / gridDim.x, t1 = (g + 1) * ntiles / gridDim.x;
@@ -304,7 +306,12 @@ __global__ __launch_bounds__(1024) void k_ell_win(int n, int64_t bh, int64_t bst
                     const int64_t jj = j + u;
                     if (j + u < L[h]) {
                         if constexpr (kRec) {
-                            ld_rec<T, kColNT>(col, base + jj * bh, vv[h][u], cc[h][u]);
+                            // ELLPACK-R is one block: slot j of row r is j bh + r,
+                            // a uniform part plus the thread's place in the tile
+                            const int* rb = col + kRecInts<T> * (t * TILE + jj * bh);
+                            ld_rec_at<T, kColNT>(rb, (uint32_t)(tid + 1024 * h) *
+                                                         (uint32_t)(4 * kRecInts<T>),
+                                                 vv[h][u], cc[h][u]);
                         } else {
                             vv[h][u] = ld_nt(val + base + jj * bh);
                             cc[h][u] = ld_col<kColNT>(col + base + jj * bh);
