@@ -91,7 +91,9 @@ typedef enum {
                               the row lengths ("Load-balancing Sparse Matrix
                               Vector Product Kernels on GPUs", abstract: a
                               CSR kernel for unbalanced matrices) */
-    SPMV_CSR_XBLOCK = 3    /* CSR format only: the columns cut into 8 slices
+    SPMV_CSR_XBLOCK = 3    /* CSR format, and HEC's tail (each range's sum
+                              added onto the ELL part's y): the columns cut
+                              into 8 slices
                               and the rows into ranges of about equal entry
                               counts (at most 20,480 rows in fp64, 40,960
                               in fp32); one workgroup sums a range in LDS,
@@ -164,7 +166,9 @@ typedef struct {
      * x_window it stages x in LDS like the HEC tail.  HEC: the kernel of
      * the tail -- balanced as above, or the vector kernel over the rows that
      * hold tail entries (each adds its sum onto the ELL part's result, no
-     * atomics); auto keeps the balanced one when the LDS window is on. */
+     * atomics), or the column slices over the tail's CSR; auto times the
+     * vector and balanced ones, keeps the balanced one when the LDS window
+     * is on, and times the column slices as the CSR format does. */
     int32_t csr_kernel;
     /* Windowed sorting: the pJDS sort of "Sparse matrix-vector multiplication
      * on GPGPU clusters" (Sect. 2.2: rows ordered by length, longest first)
@@ -252,7 +256,8 @@ typedef struct {
     int32_t csr_stage_slots; /* CSR vector kernel staged in LDS: entries one wave
                                 can stage (0: the kernel reads directly) */
     int32_t tail_kernel;   /* HYB / HEC with tail entries: SPMV_CSR_BALANCED or
-                              (HEC only) SPMV_CSR_VECTOR; otherwise 0 */
+                              (HEC only) SPMV_CSR_VECTOR or SPMV_CSR_XBLOCK;
+                              otherwise 0 */
     int32_t tail_subwave;  /* HEC vector tail: lanes per row, rows per lane */
     int32_t tail_rows;     /* group and LDS slots per wave (0: direct); */
     int32_t tail_stage_slots; /* all 0 otherwise */

@@ -134,6 +134,7 @@ struct Built {
     // HEC: the tail runs as the vector CSR kernel over the compressed rows
     // (added onto the ELL part, no atomics) instead of the balanced kernel
     bool tail_vector = false;
+    bool tail_xblock = false;  // HEC: the tail by column slices (b.xb)
     VecShape tail_vec;
     // CSR: entry-balanced kernel (run rows over the whole matrix)
     bool csr_balanced = false;
@@ -988,7 +989,9 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
             e = launch_ell(a, f64, y, x, alpha, beta, s);
             if (e == hipSuccess && b.window && b.ell_nlong > 0)
                 e = launch_ell_long(a, b.ell_long.as<int>(), b.ell_nlong, f64, y, x, alpha, s);
-            if (e == hipSuccess && format == SPMV_HEC && b.tail_nnz > 0 && b.tail_vector) {
+            if (e == hipSuccess && format == SPMV_HEC && b.tail_nnz > 0 && b.tail_xblock) {
+                e = launch_xblk(b.xb, f64, y, x, alpha, 1.0, s);  // adds alpha A_tail x
+            } else if (e == hipSuccess && format == SPMV_HEC && b.tail_nnz > 0 && b.tail_vector) {
                 const CsrView t{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
                                 b.tail_col.as<int>(), b.tail_val.p, b.tail_rows.as<int>()};
                 const VecShape& v = b.tail_vec;
@@ -1170,14 +1173,25 @@ float tune_vector(const CsrView& v, bool f64, int64_t max_len, int sw_lo, int sw
 // rows allow), the entry counts of every row in every slice at their
 // xblk_slot positions, their scan (every entry's place), the tile starts and
 // the entries in tile order with their row offsets.
-double entries_within(const spmv_handle* h, int64_t lead, hipStream_t s);
+// a CSR matrix on the device: the handle's, or the tail of a HEC handle
+struct CsrSrc {
+    int64_t n, nnz;
+    const int* rowptr;
+    const int* col;
+    const void* val;
+};
+CsrSrc csr_src(const spmv_handle* h) {
+    return CsrSrc{h->n, h->nnz, h->rowptr.as<int>(), h->col.as<int>(), h->val.p};
+}
+double entries_within(const CsrSrc& a, int64_t lead, hipStream_t s);
 
-void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
-    const int64_t n = h->n, nnz = h->nnz;
+// The column-slice copy of a CSR matrix `a` (the handle's own, or a HEC
+// tail) in b.xb and its buffers; the values have the handle's dtype.
+void build_xblock(const spmv_handle* h, const CsrSrc& a, Built& b, hipStream_t s) {
+    const int64_t n = a.n, nnz = a.nnz;
     if ((int64_t)kXbTiles * n > (int64_t)INT32_MAX - 16)
         fail(SPMV_ERR_INVALID_ARG, "csr_kernel 3 (column slices) takes n <= %lld rows (got %lld)",
              (long long)(((int64_t)INT32_MAX - 16) / kXbTiles), (long long)n);
-    b.csr_xblock = true;
     XblkView& v = b.xb;
     v = XblkView{};
     v.n = n;
@@ -1189,14 +1203,14 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
     // (band -1) unless most entries lie that close to their row
     v.lbits = h->dtype == SPMV_F64 ? kXbRowBits<double> : kXbRowBits<float>;
     v.band = xblk_band(v.lbits, cap);
-    if (entries_within(h, v.band, s) < 0.5) v.band = -1;
+    if (entries_within(a, v.band, s) < 0.5) v.band = -1;
     const int64_t passes = std::max<int64_t>(1, (n + (int64_t)kXbGroups * cap - 1) /
                                                     ((int64_t)kXbGroups * cap));
     const int64_t R0 = passes * kXbGroups;
     std::vector<int> cand((size_t)R0 + 1);
     {
         DevBuf dc(cand.size() * 4);
-        hip_check(launch_xblk_bounds(n, nnz, h->rowptr.as<int>(), R0, dc.as<int>(), s),
+        hip_check(launch_xblk_bounds(n, nnz, a.rowptr, R0, dc.as<int>(), s),
                   "column-slice range bounds");
         hip_check(hipMemcpyAsync(cand.data(), dc.p, dc.bytes, hipMemcpyDeviceToHost, s),
                   "hipMemcpyAsync");
@@ -1213,7 +1227,7 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
     DevBuf pos((size_t)(slots + 1) * 4);
     {
         DevBuf cnt((size_t)slots * 4);
-        hip_check(launch_xblk_count(v, h->rowptr.as<int>(), h->col.as<int>(), cnt.as<int>(), s),
+        hip_check(launch_xblk_count(v, a.rowptr, a.col, cnt.as<int>(), s),
                   "column-slice counts");
         hip_check(hipMemsetAsync(pos.p, 0, 4, s), "hipMemsetAsync");
         size_t tmp = 0;
@@ -1236,8 +1250,8 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
     b.xb_col.alloc((size_t)std::max<int64_t>(nnz, 1) * 4);
     b.xb_val.alloc((size_t)std::max<int64_t>(nnz, 1) * h->vsize);
     b.xb_lrow.alloc((size_t)std::max<int64_t>(nnz, 1) * 2);
-    hip_check(launch_xblk_fill(v, h->dtype == SPMV_F64, h->rowptr.as<int>(), h->col.as<int>(),
-                               h->val.p, pos.as<int>(), b.xb_col.as<int>(), b.xb_val.p,
+    hip_check(launch_xblk_fill(v, h->dtype == SPMV_F64, a.rowptr, a.col, a.val, pos.as<int>(),
+                               b.xb_col.as<int>(), b.xb_val.p,
                                b.xb_lrow.as<uint16_t>(), s),
               "column-slice fill");
     if (nnz > 0) {
@@ -1283,7 +1297,8 @@ void build_xblock(const spmv_handle* h, Built& b, hipStream_t s) {
 void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t s) {
     if (o.csr_kernel == SPMV_CSR_XBLOCK) {
         h->subwave = 1, h->csr_rows = 1, h->csr_stage_slots = 0, h->csr_stage_col_nt = false;
-        build_xblock(h, b, s);
+        build_xblock(h, csr_src(h), b, s);
+        b.csr_xblock = true;
         return;
     }
     int rule = 1;  // smallest power of two >= the longest row, at most 64
@@ -1348,7 +1363,8 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
         Built xb;
         bool built = true;
         try {
-            build_xblock(h, xb, s);
+            build_xblock(h, csr_src(h), xb, s);
+            xb.csr_xblock = true;
         } catch (const Error& e) {
             if (e.code != SPMV_ERR_NO_MEMORY) throw;
             built = false;  // no room for the optional copy: not a candidate
@@ -1371,33 +1387,70 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
 // spmv_csr_kernel) fixes the choice; SPMV_CSR_AUTO keeps the faster on the
 // device, the balanced one only when clearly faster, and keeps the balanced
 // one with the LDS window (the vector kernel has no window).
-void tune_hec_tail(const spmv_handle* h, int kernel, int col_cache, Built& b, hipStream_t s) {
+void tune_hec_tail(const spmv_handle* h, int kernel, int col_cache, uint64_t budget, Built& b,
+                   hipStream_t s) {
     b.tail_vector = false;
-    if (b.tail_nnz == 0 || kernel == SPMV_CSR_BALANCED ||
-        (kernel == SPMV_CSR_AUTO && b.window))
+    b.tail_xblock = false;
+    if (b.tail_nnz == 0) return;
+    const CsrSrc tail{h->n, b.tail_nnz, b.tail_ptr.as<int>(), b.tail_col.as<int>(), b.tail_val.p};
+    if (kernel == SPMV_CSR_XBLOCK) {
+        build_xblock(h, tail, b, s);
+        b.tail_xblock = true;
+        b.run_row.release();
         return;
+    }
     const bool f64 = h->dtype == SPMV_F64;
     DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
     hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
     hip_check(hipMemsetAsync(ys.p, 0, ys.bytes, s), "hipMemsetAsync");
-    const TailView t{(int)h->n, b.tail_nnz, nullptr, b.tail_cptr.as<int>(), b.run_row.as<int>(),
-                     b.tail_rows.as<int>(), b.tail_col.as<int>(), b.tail_val.p, false};
-    const float bal_ms = kernel == SPMV_CSR_VECTOR
-                             ? 1e30f
-                             : time_launches([&] { return launch_tail(t, f64, ys.p, xs.p, 1.0, s); },
-                                             s);
-    const CsrView v{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
-                    b.tail_col.as<int>(), b.tail_val.p, b.tail_rows.as<int>()};
-    VecShape best;
-    const float vec_ms =
-        tune_vector(v, f64, h->max_len - b.ell_width, 1, 64, 0, -1, col_cache, ys.p, xs.p, 1.0,
-                    best, s);
-    sync(s);
-    if (!(bal_ms < kPreferMargin * vec_ms)) {
-        b.tail_vector = true;
-        b.tail_vec = best;
-        b.run_row.release();
+    if (kernel != SPMV_CSR_BALANCED && !(kernel == SPMV_CSR_AUTO && b.window)) {
+        const TailView t{(int)h->n, b.tail_nnz, nullptr, b.tail_cptr.as<int>(),
+                         b.run_row.as<int>(), b.tail_rows.as<int>(), b.tail_col.as<int>(),
+                         b.tail_val.p, false};
+        const float bal_ms =
+            kernel == SPMV_CSR_VECTOR
+                ? 1e30f
+                : time_launches([&] { return launch_tail(t, f64, ys.p, xs.p, 1.0, s); }, s);
+        const CsrView v{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
+                        b.tail_col.as<int>(), b.tail_val.p, b.tail_rows.as<int>()};
+        VecShape best;
+        const float vec_ms = tune_vector(v, f64, h->max_len - b.ell_width, 1, 64, 0, -1, col_cache,
+                                         ys.p, xs.p, 1.0, best, s);
+        sync(s);
+        if (!(bal_ms < kPreferMargin * vec_ms)) {
+            b.tail_vector = true;
+            b.tail_vec = best;
+        }
     }
+    // third candidate: the tail by column slices, for an x larger than one
+    // XCD's L2 when its copy fits the budget; kept only when the whole apply
+    // is clearly faster with it
+    const double xb_bytes = (double)b.tail_nnz * (6.0 + (double)h->vsize) +
+                            (double)kXbTiles * (double)h->n * 8.0;
+    if (kernel == SPMV_CSR_AUTO && (double)h->n * (double)h->vsize > (double)kXbMinX &&
+        (int64_t)kXbTiles * h->n <= (int64_t)INT32_MAX - 16 && xb_bytes <= (double)budget) {
+        auto run = [&] { return launch_built(h, b, SPMV_HEC, ys.p, xs.p, 1.0, 0.0, s); };
+        const float cur_ms = time_launches(run, s);
+        bool built = true;
+        try {
+            build_xblock(h, tail, b, s);
+        } catch (const Error& e) {
+            if (e.code != SPMV_ERR_NO_MEMORY) throw;
+            built = false;  // no room for the optional copy: not a candidate
+        }
+        if (built) {
+            b.tail_xblock = true;
+            const float xb_ms = time_launches(run, s);
+            if (!(xb_ms < kPreferMargin * cur_ms)) {
+                b.tail_xblock = false;
+                b.xb = XblkView{};
+                b.xb_rows.release(), b.xb_tiles.release(), b.xb_col.release();
+                b.xb_val.release(), b.xb_lrow.release();
+            }
+        }
+    }
+    if (b.tail_xblock) b.tail_vector = false;
+    if (b.tail_vector || b.tail_xblock) b.run_row.release();
 }
 
 // Share of the entries the LDS window reaches, and whether to use it.  On
@@ -1406,23 +1459,24 @@ void tune_hec_tail(const spmv_handle* h, int kernel, int col_cache, Built& b, hi
 // apply is then timed with and without it and the faster kept (stencils
 // whose x reads already coalesce gain nothing from it).  `b` must hold the
 // built format.
-// share of the entries whose column lies within `lead` of their row
-double entries_within(const spmv_handle* h, int64_t lead, hipStream_t s) {
+// share of the entries of a CSR matrix whose column lies within `lead` of
+// their row
+double entries_within(const CsrSrc& a, int64_t lead, hipStream_t s) {
     DevBuf cnt(8);
     hip_check(hipMemsetAsync(cnt.p, 0, 8, s), "hipMemsetAsync");
-    if (h->n > 0) {
-        hipLaunchKernelGGL(k_band_count, dim3(grid_for(h->n)), dim3(256), 0, s, h->n, lead,
-                           h->rowptr.as<int>(), h->col.as<int>(), cnt.as<unsigned long long>());
+    if (a.n > 0) {
+        hipLaunchKernelGGL(k_band_count, dim3(grid_for(a.n)), dim3(256), 0, s, a.n, lead, a.rowptr,
+                           a.col, cnt.as<unsigned long long>());
         hip_check(hipGetLastError(), "band count");
     }
     const unsigned long long c = read_scalar<unsigned long long>(cnt.p, s);
-    return h->nnz ? (double)c / (double)h->nnz : 0.0;
+    return a.nnz ? (double)c / (double)a.nnz : 0.0;
 }
 
 // share of the entries whose column lies within the window's reach of their row
 double band_fraction(const spmv_handle* h, hipStream_t s) {
-    return entries_within(h, h->dtype == SPMV_F64 ? EllWinLead<double>::value
-                                                  : EllWinLead<float>::value, s);
+    return entries_within(csr_src(h), h->dtype == SPMV_F64 ? EllWinLead<double>::value
+                                                           : EllWinLead<float>::value, s);
 }
 
 // window offsets are computed in 32 bits: rows and columns plus the window
@@ -1529,7 +1583,7 @@ void build_split_tuned(spmv_handle* h, int format, const spmv_convert_opts& o, i
         build_split<float>(h, format, width, o.sort_window, b, s);
     decide_window(h, format, o.x_window, b, s);
     choose_groups(h, o.ell_groups, b);
-    if (format == SPMV_HEC) tune_hec_tail(h, o.csr_kernel, o.col_cache, b, s);
+    if (format == SPMV_HEC) tune_hec_tail(h, o.csr_kernel, o.col_cache, budget_bytes(o), b, s);
     choose_col_policy(o.col_cache, b);
 }
 
@@ -2093,12 +2147,15 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
                  o.subwave);
         if (o.csr_kernel < SPMV_CSR_AUTO || o.csr_kernel > SPMV_CSR_XBLOCK)
             fail(SPMV_ERR_INVALID_ARG, "csr_kernel must be 0, 1, 2 or 3 (got %d)", o.csr_kernel);
-        if (o.csr_kernel == SPMV_CSR_XBLOCK && format != SPMV_CSR)
-            fail(SPMV_ERR_INVALID_ARG, "csr_kernel 3 (column slices) applies to the CSR format only");
-        if (o.csr_kernel == SPMV_CSR_XBLOCK &&
-            (o.subwave || o.csr_rows > 1 || o.csr_stage == 1 || o.x_window == 1))
+        if (o.csr_kernel == SPMV_CSR_XBLOCK && format != SPMV_CSR && format != SPMV_HEC)
             fail(SPMV_ERR_INVALID_ARG,
-                 "csr_kernel 3 (column slices) takes no subwave, csr_rows, csr_stage or x_window");
+                 "csr_kernel 3 (column slices) applies to the CSR format and HEC's tail only");
+        if (o.csr_kernel == SPMV_CSR_XBLOCK &&
+            (o.subwave || o.csr_rows > 1 || o.csr_stage == 1 ||
+             (o.x_window == 1 && format == SPMV_CSR)))
+            fail(SPMV_ERR_INVALID_ARG,
+                 "csr_kernel 3 (column slices) takes no subwave, csr_rows, csr_stage or (CSR) "
+                 "x_window");
         if (o.col_cache < -1 || o.col_cache > 1)
             fail(SPMV_ERR_INVALID_ARG, "col_cache must be -1, 0 or 1 (got %d)", o.col_cache);
         if (o.csr_stage < -1 || o.csr_stage > 1)
@@ -2252,7 +2309,9 @@ int spmv_info(spmv_t h, spmv_info_t* out) {
     i.csr_stage_slots =
         h->format == SPMV_CSR && !b.csr_balanced && !b.csr_xblock ? h->csr_stage_slots : 0;
     i.tail_kernel = (h->format == SPMV_HYB || h->format == SPMV_HEC) && b.tail_nnz > 0
-                        ? (b.tail_vector ? SPMV_CSR_VECTOR : SPMV_CSR_BALANCED)
+                        ? (b.tail_xblock   ? SPMV_CSR_XBLOCK
+                           : b.tail_vector ? SPMV_CSR_VECTOR
+                                           : SPMV_CSR_BALANCED)
                         : SPMV_CSR_AUTO;
     const bool tv = h->format == SPMV_HEC && b.tail_nnz > 0 && b.tail_vector;
     i.tail_subwave = tv ? b.tail_vec.subwave : 0;

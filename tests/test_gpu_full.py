@@ -31,12 +31,14 @@ CASES = [
     ("c5_fem_8m", torch.float64),
 ]
 AB = [(1.0, 0.0), (-1.5, 0.5)]
-# besides each format's automatic choice: the CSR column-slice kernel and
-# SELL-64 with and without the LDS window where those are candidates
+# besides each format's automatic choice: the CSR column-slice kernel, SELL-64
+# with and without the LDS window and HEC's tail kernels where those are
+# candidates
 EXTRA = {
     "c4_powerlaw_4m": [("csr", dict(csr_kernel="xblock")), ("csr", dict(csr_kernel="balanced"))],
     "c5_fem_8m": [("sell64", dict(x_window=0)), ("sell64", dict(x_window=1)),
-                  ("csr", dict(csr_kernel="vector"))],
+                  ("csr", dict(csr_kernel="vector")), ("hec", dict(csr_kernel="xblock")),
+                  ("hec", dict(csr_kernel="balanced"))],
 }
 
 

@@ -131,10 +131,12 @@ def test_csr_staged(sw, name, dtype):
 @pytest.mark.parametrize("dtype", [torch.float64, torch.float32])
 @pytest.mark.parametrize("name", ["c1", "ragged", "every_len", "long_spans", "box27", "nnz0",
                                   "dups_unsorted", "n1"])
-@pytest.mark.parametrize("kernel", ["vector", "balanced", "auto"])
+@pytest.mark.parametrize("kernel", ["vector", "balanced", "xblock", "auto"])
 def test_hec_tail_kernels(kernel, name, dtype):
-    """HEC with either tail kernel (and the timed choice) against the oracle,
-    at the default split and at K = 1 (almost everything in the tail)."""
+    """HEC with each tail kernel (the vector and balanced CSR kernels, the
+    column-slice kernel adding onto the ELL part's y) and the timed choice
+    against the oracle, at the default split and at K = 1 (almost everything
+    in the tail)."""
     a = MATS[name]()
     npdt = np.float64 if dtype == torch.float64 else np.float32
     if dtype == torch.float32:
@@ -776,8 +778,8 @@ def test_csr_xblock(name, dtype):
 def test_csr_xblock_errors():
     a = MATS["c1"]()
     M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
-    for fmt, kw in [("hec", {}), ("hyb", {}), ("ellr", {}), ("sell64", {}), ("auto", {}),
-                    ("csr", dict(subwave=4)), ("csr", dict(csr_rows=2)),
+    for fmt, kw in [("hyb", {}), ("ellr", {}), ("sell64", {}), ("auto", {}),
+                    ("hec", dict(subwave=4)), ("csr", dict(subwave=4)), ("csr", dict(csr_rows=2)),
                     ("csr", dict(csr_stage=1)), ("csr", dict(x_window=1))]:
         with pytest.raises(sf.SpmvError) as e:
             M.convert(fmt, csr_kernel="xblock", **kw)
