@@ -63,8 +63,8 @@ def kernels_of(fmt: str, info: dict) -> str:
     k = KERNELS[fmt]
     if fmt in ("hyb", "hec") and info.get("tail_nnz", 1) == 0:
         k = "k_ell"
-    if fmt == "hec" and info.get("tail_nnz", 1) > 0 and info.get("tail_kernel") == "xblock":
-        k = k.replace("k_tail<CSR>", "k_xblk")
+    if fmt in ("hyb", "hec") and info.get("tail_nnz", 1) > 0 and info.get("tail_kernel") == "xblock":
+        k = k.replace("k_tail<CSR>", "k_xblk").replace("k_tail<COO>", "k_xblk")
     if fmt == "hec" and info.get("tail_kernel") == "vector":
         k = k.replace("k_tail<CSR>", _vector_kernel(info["tail_subwave"], info["tail_rows"],
                                                     info["tail_stage_slots"]))
@@ -198,7 +198,7 @@ def kernel_bases(fmt: str, info: dict) -> set:
     out = {"k_ell" + win}
     if fmt == "ellr" and info.get("ell_long_rows", 0) > 0:
         out.add("k_ell_long")
-    if fmt == "hec" and info.get("tail_nnz", 0) > 0 and info.get("tail_kernel") == "xblock":
+    if fmt in ("hyb", "hec") and info.get("tail_nnz", 0) > 0 and info.get("tail_kernel") == "xblock":
         out.add("k_xblk")
     elif fmt == "hec" and info.get("tail_nnz", 0) > 0 and info.get("tail_kernel") == "vector":
         out.add("k_csr_staged" if info.get("tail_stage_slots", 0) > 0 else "k_csr_vector")

@@ -91,8 +91,9 @@ typedef enum {
                               the row lengths ("Load-balancing Sparse Matrix
                               Vector Product Kernels on GPUs", abstract: a
                               CSR kernel for unbalanced matrices) */
-    SPMV_CSR_XBLOCK = 3    /* CSR format, and HEC's tail (each range's sum
-                              added onto the ELL part's y): the columns cut
+    SPMV_CSR_XBLOCK = 3    /* CSR format, and the tails of HYB and HEC
+                              (each range's sum added onto the ELL part's
+                              y, from a copy of the tail): the columns cut
                               into 8 slices
                               and the rows into ranges of about equal entry
                               counts (at most 20,480 rows in fp64, 40,960
@@ -166,9 +167,12 @@ typedef struct {
      * x_window it stages x in LDS like the HEC tail.  HEC: the kernel of
      * the tail -- balanced as above, or the vector kernel over the rows that
      * hold tail entries (each adds its sum onto the ELL part's result, no
-     * atomics), or the column slices over the tail's CSR; auto times the
+     * atomics), or the column slices over the tail's rows; auto times the
      * vector and balanced ones, keeps the balanced one when the LDS window
-     * is on, and times the column slices as the CSR format does. */
+     * is on, and times the column slices as the CSR format does.  HYB: the
+     * balanced kernel over the COO tail, or the column slices (auto times
+     * them as for HEC); the vector kernel is not a HYB tail kernel and is
+     * ignored there. */
     int32_t csr_kernel;
     /* Windowed sorting: the pJDS sort of "Sparse matrix-vector multiplication
      * on GPGPU clusters" (Sect. 2.2: rows ordered by length, longest first)
@@ -255,8 +259,8 @@ typedef struct {
     int64_t ell_rows;      /* ELL-R / HYB / HEC: rows padded to whole blocks */
     int32_t csr_stage_slots; /* CSR vector kernel staged in LDS: entries one wave
                                 can stage (0: the kernel reads directly) */
-    int32_t tail_kernel;   /* HYB / HEC with tail entries: SPMV_CSR_BALANCED or
-                              (HEC only) SPMV_CSR_VECTOR or SPMV_CSR_XBLOCK;
+    int32_t tail_kernel;   /* HYB / HEC with tail entries: SPMV_CSR_BALANCED,
+                              SPMV_CSR_XBLOCK or (HEC only) SPMV_CSR_VECTOR;
                               otherwise 0 */
     int32_t tail_subwave;  /* HEC vector tail: lanes per row, rows per lane */
     int32_t tail_rows;     /* group and LDS slots per wave (0: direct); */

@@ -927,9 +927,9 @@ void build_split(const spmv_handle* h, int format, int requested, int sort_windo
             hip_check(hipGetLastError(), "run rows");
             sync(s);  // before the temporaries are freed
         }
-    } else {
-        b.tail_ptr.release();  // HYB keeps the COO rows only
     }
+    // (HYB keeps tail_ptr until its tail kernel is chosen: the column-slice
+    // copy is built from the tail's CSR)
     sync(s);
 }
 
@@ -989,7 +989,7 @@ hipError_t launch_built(const spmv_handle* h, const Built& b, int format, void* 
             e = launch_ell(a, f64, y, x, alpha, beta, s);
             if (e == hipSuccess && b.window && b.ell_nlong > 0)
                 e = launch_ell_long(a, b.ell_long.as<int>(), b.ell_nlong, f64, y, x, alpha, s);
-            if (e == hipSuccess && format == SPMV_HEC && b.tail_nnz > 0 && b.tail_xblock) {
+            if (e == hipSuccess && format != SPMV_ELLR && b.tail_nnz > 0 && b.tail_xblock) {
                 e = launch_xblk(b.xb, f64, y, x, alpha, 1.0, s);  // adds alpha A_tail x
             } else if (e == hipSuccess && format == SPMV_HEC && b.tail_nnz > 0 && b.tail_vector) {
                 const CsrView t{(int)b.tail_nrows, (int)b.tail_nnz, b.tail_cptr.as<int>(),
@@ -1381,29 +1381,37 @@ void tune_csr(spmv_handle* h, const spmv_convert_opts& o, Built& b, hipStream_t 
     sync(s);
 }
 
-// HEC tail kernel: the balanced kernel (atomics) or the vector CSR kernel
-// over the rows that hold tail entries (each row added once onto the ELL
-// part's result: no atomics, bit-reproducible).  `kernel` (a
-// spmv_csr_kernel) fixes the choice; SPMV_CSR_AUTO keeps the faster on the
-// device, the balanced one only when clearly faster, and keeps the balanced
-// one with the LDS window (the vector kernel has no window).
-void tune_hec_tail(const spmv_handle* h, int kernel, int col_cache, uint64_t budget, Built& b,
-                   hipStream_t s) {
+// Tail kernel of HYB / HEC: the balanced kernel (atomics; COO for HYB, CSR
+// for HEC), for HEC the vector CSR kernel over the rows that hold tail
+// entries (each row added once onto the ELL part's result: no atomics,
+// bit-reproducible), or for both the column-slice kernel over the tail's
+// rows (a copy of the tail by column slices).  `kernel` (a spmv_csr_kernel)
+// fixes the choice; SPMV_CSR_AUTO keeps the faster on the device, the
+// balanced one only when clearly faster, keeps the balanced one with the LDS
+// window (the vector kernel has no window), and then times the column slices
+// like the CSR format.
+void tune_tail(const spmv_handle* h, int format, int kernel, int col_cache, uint64_t budget,
+               Built& b, hipStream_t s) {
     b.tail_vector = false;
     b.tail_xblock = false;
-    if (b.tail_nnz == 0) return;
+    const bool hyb = format == SPMV_HYB;
+    if (b.tail_nnz == 0) {
+        if (hyb) b.tail_ptr.release();
+        return;
+    }
     const CsrSrc tail{h->n, b.tail_nnz, b.tail_ptr.as<int>(), b.tail_col.as<int>(), b.tail_val.p};
     if (kernel == SPMV_CSR_XBLOCK) {
         build_xblock(h, tail, b, s);
         b.tail_xblock = true;
         b.run_row.release();
+        if (hyb) b.tail_ptr.release();
         return;
     }
     const bool f64 = h->dtype == SPMV_F64;
     DevBuf xs((size_t)h->n * h->vsize), ys((size_t)h->n * h->vsize);
     hip_check(hipMemsetAsync(xs.p, 0, xs.bytes, s), "hipMemsetAsync");
     hip_check(hipMemsetAsync(ys.p, 0, ys.bytes, s), "hipMemsetAsync");
-    if (kernel != SPMV_CSR_BALANCED && !(kernel == SPMV_CSR_AUTO && b.window)) {
+    if (!hyb && kernel != SPMV_CSR_BALANCED && !(kernel == SPMV_CSR_AUTO && b.window)) {
         const TailView t{(int)h->n, b.tail_nnz, nullptr, b.tail_cptr.as<int>(),
                          b.run_row.as<int>(), b.tail_rows.as<int>(), b.tail_col.as<int>(),
                          b.tail_val.p, false};
@@ -1429,7 +1437,7 @@ void tune_hec_tail(const spmv_handle* h, int kernel, int col_cache, uint64_t bud
                             (double)kXbTiles * (double)h->n * 8.0;
     if (kernel == SPMV_CSR_AUTO && (double)h->n * (double)h->vsize > (double)kXbMinX &&
         (int64_t)kXbTiles * h->n <= (int64_t)INT32_MAX - 16 && xb_bytes <= (double)budget) {
-        auto run = [&] { return launch_built(h, b, SPMV_HEC, ys.p, xs.p, 1.0, 0.0, s); };
+        auto run = [&] { return launch_built(h, b, format, ys.p, xs.p, 1.0, 0.0, s); };
         const float cur_ms = time_launches(run, s);
         bool built = true;
         try {
@@ -1451,6 +1459,7 @@ void tune_hec_tail(const spmv_handle* h, int kernel, int col_cache, uint64_t bud
     }
     if (b.tail_xblock) b.tail_vector = false;
     if (b.tail_vector || b.tail_xblock) b.run_row.release();
+    if (hyb) b.tail_ptr.release();  // HYB keeps the COO rows (and the copy)
 }
 
 // Share of the entries the LDS window reaches, and whether to use it.  On
@@ -1583,7 +1592,8 @@ void build_split_tuned(spmv_handle* h, int format, const spmv_convert_opts& o, i
         build_split<float>(h, format, width, o.sort_window, b, s);
     decide_window(h, format, o.x_window, b, s);
     choose_groups(h, o.ell_groups, b);
-    if (format == SPMV_HEC) tune_hec_tail(h, o.csr_kernel, o.col_cache, budget_bytes(o), b, s);
+    if (format == SPMV_HYB || format == SPMV_HEC)
+        tune_tail(h, format, o.csr_kernel, o.col_cache, budget_bytes(o), b, s);
     choose_col_policy(o.col_cache, b);
 }
 
@@ -2147,9 +2157,11 @@ int spmv_convert(spmv_t h, int format, const spmv_convert_opts* opts) {
                  o.subwave);
         if (o.csr_kernel < SPMV_CSR_AUTO || o.csr_kernel > SPMV_CSR_XBLOCK)
             fail(SPMV_ERR_INVALID_ARG, "csr_kernel must be 0, 1, 2 or 3 (got %d)", o.csr_kernel);
-        if (o.csr_kernel == SPMV_CSR_XBLOCK && format != SPMV_CSR && format != SPMV_HEC)
+        if (o.csr_kernel == SPMV_CSR_XBLOCK && format != SPMV_CSR && format != SPMV_HYB &&
+            format != SPMV_HEC)
             fail(SPMV_ERR_INVALID_ARG,
-                 "csr_kernel 3 (column slices) applies to the CSR format and HEC's tail only");
+                 "csr_kernel 3 (column slices) applies to the CSR format and the HYB and HEC "
+                 "tails only");
         if (o.csr_kernel == SPMV_CSR_XBLOCK &&
             (o.subwave || o.csr_rows > 1 || o.csr_stage == 1 ||
              (o.x_window == 1 && format == SPMV_CSR)))

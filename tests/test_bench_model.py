@@ -129,6 +129,11 @@ def test_traffic_record_checks(tmp_path):
     assert bench.kernels_of("hec", hec_vec) == "k_ell + k_csr_vector<S=4,R=2>"
     assert bench.kernels_of("hyb", {"x_window": 1, "tail_nnz": 0}) == "k_ell_win"
     assert bench.kernels_of("hyb", {"x_window": 0, "tail_nnz": 3}) == "k_ell + k_tail<COO>"
+    # HYB / HEC tails by column slices
+    for fmt in ("hyb", "hec"):
+        t = {"x_window": 1, "tail_nnz": 3, "tail_kernel": "xblock"}
+        assert bench.kernels_of(fmt, t) == "k_ell_win + k_xblk"
+        assert bench.kernel_bases(fmt, t) == {"k_ell_win", "k_xblk"}
     # the column-slice CSR kernel and its traffic record
     xb = {"csr_kernel": "xblock", "x_window": 0, "subwave": 1, "csr_rows": 1}
     assert bench.kernel_bases("csr", xb) == {"k_xblk"}

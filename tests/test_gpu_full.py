@@ -32,13 +32,14 @@ CASES = [
 ]
 AB = [(1.0, 0.0), (-1.5, 0.5)]
 # besides each format's automatic choice: the CSR column-slice kernel, SELL-64
-# with and without the LDS window and HEC's tail kernels where those are
+# with and without the LDS window and the HYB/HEC tail kernels where those are
 # candidates
 EXTRA = {
     "c4_powerlaw_4m": [("csr", dict(csr_kernel="xblock")), ("csr", dict(csr_kernel="balanced"))],
     "c5_fem_8m": [("sell64", dict(x_window=0)), ("sell64", dict(x_window=1)),
                   ("csr", dict(csr_kernel="vector")), ("hec", dict(csr_kernel="xblock")),
-                  ("hec", dict(csr_kernel="balanced"))],
+                  ("hec", dict(csr_kernel="balanced")), ("hyb", dict(csr_kernel="xblock")),
+                  ("hyb", dict(csr_kernel="balanced"))],
 }
 
 

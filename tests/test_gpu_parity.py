@@ -132,11 +132,13 @@ def test_csr_staged(sw, name, dtype):
 @pytest.mark.parametrize("name", ["c1", "ragged", "every_len", "long_spans", "box27", "nnz0",
                                   "dups_unsorted", "n1"])
 @pytest.mark.parametrize("kernel", ["vector", "balanced", "xblock", "auto"])
-def test_hec_tail_kernels(kernel, name, dtype):
-    """HEC with each tail kernel (the vector and balanced CSR kernels, the
-    column-slice kernel adding onto the ELL part's y) and the timed choice
-    against the oracle, at the default split and at K = 1 (almost everything
-    in the tail)."""
+@pytest.mark.parametrize("fmt", ["hec", "hyb"])
+def test_tail_kernels(fmt, kernel, name, dtype):
+    """HEC and HYB with each tail kernel (HEC: the vector and balanced CSR
+    kernels; HYB: the balanced COO kernel, the vector kernel being no HYB
+    tail kernel; both: the column-slice kernel adding onto the ELL part's y)
+    and the timed choice against the oracle, at the default split and at K =
+    1 (almost everything in the tail)."""
     a = MATS[name]()
     npdt = np.float64 if dtype == torch.float64 else np.float32
     if dtype == torch.float32:
@@ -145,14 +147,15 @@ def test_hec_tail_kernels(kernel, name, dtype):
     x = torch.from_numpy(x_np).cuda()
     y0 = torch.from_numpy(y0_np).cuda()
     M = sf.Matrix.from_csr(*to_dev(a, dtype), n=a.n)
+    want = "balanced" if fmt == "hyb" and kernel == "vector" else kernel
     for K in (-1, 1):
-        M.convert("hec", ell_width=K, csr_kernel=kernel)
+        M.convert(fmt, ell_width=K, csr_kernel=kernel)
         inf = M.info()
         if inf["tail_nnz"] > 0 and kernel != "auto":
-            assert inf["tail_kernel"] == kernel
+            assert inf["tail_kernel"] == want
         for alpha, beta in AB:
             check(a, x_np, y0_np, alpha, beta, apply(M, x, y0, alpha, beta), dtype,
-                  what="hec tail %s K=%d %s a=%g b=%g" % (kernel, K, name, alpha, beta))
+                  what="%s tail %s K=%d %s a=%g b=%g" % (fmt, kernel, K, name, alpha, beta))
     M.close()
 
 
@@ -778,7 +781,7 @@ def test_csr_xblock(name, dtype):
 def test_csr_xblock_errors():
     a = MATS["c1"]()
     M = sf.Matrix.from_csr(*to_dev(a), n=a.n)
-    for fmt, kw in [("hyb", {}), ("ellr", {}), ("sell64", {}), ("auto", {}),
+    for fmt, kw in [("ellr", {}), ("sell64", {}), ("auto", {}), ("hyb", dict(subwave=4)),
                     ("hec", dict(subwave=4)), ("csr", dict(subwave=4)), ("csr", dict(csr_rows=2)),
                     ("csr", dict(csr_stage=1)), ("csr", dict(x_window=1))]:
         with pytest.raises(sf.SpmvError) as e:
