@@ -4,9 +4,9 @@
 // The columns are cut into kXbBlocks slices and the rows into ranges of at
 // most kXbCap rows with about equal entry counts.  Workgroup g (dispatched to
 // XCD g mod 8) owns ranges g, g + grid, ...: it sums a range's rows in LDS
-// over all slices, starting with slice g mod 8 and going round, so that at any
-// time the 32 workgroups of one XCD read one slice of x, which stays in that
-// XCD's L2 ("Sparse matrix-vector multiplication on GPGPU clusters", Sect.
+// over all slices, starting with slice g mod 8 and going round, so that the
+// 32 workgroups of one XCD read one slice of x at about the same time, which
+// stays in that XCD's L2 ("Sparse matrix-vector multiplication on GPGPU clusters", Sect.
 // 2.3: the reuse of the right-hand side decides the traffic; random columns
 // lose it, and a slice that fits a cache restores it).  The range's rows are
 // then written once, y = alpha * s + beta * y: no atomics in global memory,
@@ -25,10 +25,10 @@
 // after the slices, whose entries pack column and row offset into one 4-byte
 // word (12 bytes per fp64 entry instead of 14).
 //
-// Measured per apply (fp64): power-law matrix (4 M rows, 42 M entries) 0.31
+// Measured per apply (fp64): power-law matrix (4 M rows, 42 M entries) 0.30
 // ms against 0.40 ms with the entries of a tile in row order (products summed
 // per row by a segmented scan over the lanes); FEM block (8 M rows, 398 M
-// entries, 95 % of columns within +-10,000 of the diagonal) 1.05 ms with the
+// entries, 95 % of columns within +-10,000 of the diagonal) 1.03 ms with the
 // packed band tile, 1.16 without it, 3.02 in row order.
 #include "common.h"
 #include "internal.h"
@@ -143,21 +143,24 @@ __global__ __launch_bounds__(kXbThreads) void k_xblk(XblkView a, const T* __rest
         for (int i = threadIdx.x; i < nr; i += kXbThreads) part[i] = T(0);
         __syncthreads();
         // the slices from this XCD's own on (the workgroups of an XCD, with
-        // equal shares of each slice, read the same slice of x at the same
-        // time), then the range's band
-        for (int s = 0; s < kXbTiles; ++s) {
-            const int b = s < kXbBlocks ? (first + s) % kXbBlocks : kXbBlocks;
-            const int e0 = a.tile_ptr[r * kXbTiles + b], e1 = a.tile_ptr[r * kXbTiles + b + 1];
-            if (e0 == e1) continue;  // an empty tile (uniform): no barrier either
-            const int p = e0 + wv * 64 * U;
-            if (p < e1) {  // wave-uniform
-                if (b < kXbBlocks)
-                    xb_tile<T, U, false>(a, x, part, p, e1, lane, 0);
-                else
-                    xb_tile<T, U, true>(a, x, part, p, e1, lane, rb - (int)a.band);
+        // equal shares of each slice, read the same slice of x at about the
+        // same time), as two runs of consecutive tiles, then the range's
+        // band.  The waves do not wait for each other between tiles: the LDS
+        // adds commute, and the packets of a run are dealt to the waves in
+        // turn, so they stay within about a round of each other (a barrier
+        // after every tile was 1 % slower on the FEM block and 3.5 % on the
+        // power-law matrix, whose slice tiles take one or two rounds each).
+        {
+            const int t0 = (int)r * kXbTiles;
+            for (int h = 0; h < 2; ++h) {
+                const int e0 = a.tile_ptr[t0 + (h ? 0 : first)];
+                const int e1 = a.tile_ptr[t0 + (h ? first : kXbBlocks)];
+                const int p = e0 + wv * 64 * U;
+                if (p < e1) xb_tile<T, U, false>(a, x, part, p, e1, lane, 0);  // wave-uniform
             }
-            // the waves move to the next slice together, so that the x
-            // reads of the workgroup stay within one slice
+            const int e0 = a.tile_ptr[t0 + kXbBlocks], e1 = a.tile_ptr[t0 + kXbTiles];
+            const int p = e0 + wv * 64 * U;
+            if (p < e1) xb_tile<T, U, true>(a, x, part, p, e1, lane, rb - (int)a.band);
             __syncthreads();
         }
         // alpha * 0 is NaN for a non-finite alpha, as the definition gives;
