@@ -482,7 +482,9 @@ GRAPH_CASES = [("csr", dict(csr_kernel="vector", csr_stage=1)),
                ("sell64", {}),
                ("hyb", dict(x_window=0)), ("hyb", dict(x_window=1)),
                ("hec", dict(csr_kernel="vector", x_window=0)),
-               ("hec", dict(csr_kernel="balanced", x_window=1))]
+               ("hec", dict(csr_kernel="balanced", x_window=1)),
+               ("hyb", dict(csr_kernel="xblock", x_window=0)),
+               ("hec", dict(csr_kernel="xblock", x_window=1))]
 
 
 @pytest.mark.parametrize("fmt,kw", GRAPH_CASES)
@@ -544,20 +546,24 @@ def test_concurrent_applies_on_two_streams(fmt):
     M.close()
 
 
-@pytest.mark.parametrize("kw", [{}, dict(csr_kernel="xblock")])
-def test_concurrent_applies_scattered_columns(kw):
+@pytest.mark.parametrize("fmt,kw", [("csr", {}), ("csr", dict(csr_kernel="xblock")),
+                                    ("hyb", {}), ("hyb", dict(csr_kernel="xblock")),
+                                    ("hec", {}), ("hec", dict(csr_kernel="xblock"))])
+def test_concurrent_applies_scattered_columns(fmt, kw):
     """Applies on two streams at once on a matrix shaped like the power-law
     workload (600,000 rows, lognormal lengths, 64 rows of 20,000-50,000
     entries, uniform columns: x of 4.8 MB read at random), where the default
-    CSR choice may take the column-slice kernel: with default options and with
-    that kernel forced, every row of both results matches the oracle."""
+    CSR and tail choices may take the column-slice kernel: with default options
+    and with that kernel forced, every row of both results matches the
+    oracle."""
     from gen import c4_powerlaw
     a = c4_powerlaw(n=600_000)
     x1, y01 = vectors(a.n, 73)
     x2, y02 = vectors(a.n, 74)
-    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert("csr", **kw)
+    M = sf.Matrix.from_csr(*to_dev(a), n=a.n).convert(fmt, **kw)
+    key = "csr_kernel" if fmt == "csr" else "tail_kernel"
     if kw:
-        assert M.info()["csr_kernel"] == "xblock"
+        assert M.info()[key] == "xblock"
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     xa, xb = torch.from_numpy(x1).cuda(), torch.from_numpy(x2).cuda()
     ya, yb = torch.from_numpy(y01).cuda(), torch.from_numpy(y02).cuda()
@@ -568,7 +574,7 @@ def test_concurrent_applies_scattered_columns(kw):
         with torch.cuda.stream(s2):
             M.apply(yb, xb, -0.25, 1.0)
     torch.cuda.synchronize()
-    what = "%s (%s)" % (kw or "default", M.info()["csr_kernel"])
+    what = "%s %s (%s)" % (fmt, kw or "default", M.info()[key])
     check(a, x1, y01, 2.0, 1.0, ya.cpu().numpy(), torch.float64, what="stream 1 " + what)
     check(a, x2, y02, -1.0, 1.0, yb.cpu().numpy(), torch.float64, what="stream 2 " + what)
     M.close()
