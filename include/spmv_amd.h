@@ -94,12 +94,12 @@ typedef enum {
     SPMV_CSR_XBLOCK = 3    /* CSR format, and the tails of HYB and HEC
                               (each range's sum added onto the ELL part's
                               y, from a copy of the tail): the columns cut
-                              into 8 slices
-                              and the rows into ranges of about equal entry
-                              counts (at most 20,480 rows in fp64, 40,960
-                              in fp32); one workgroup sums a range in LDS,
-                              slice by slice, starting with the slice of its
-                              XCD, so each XCD's x reads stay in its L2
+                              into 8 slices and the rows into ranges of
+                              about equal entry counts (at most 20,480 rows
+                              in fp64, 40,960 in fp32); one workgroup sums
+                              a range in LDS, slice by slice, starting with
+                              the slice of its XCD, so each XCD's x reads
+                              stay in its L2
                               ("Sparse matrix-vector multiplication on GPGPU
                               clusters", Sect. 2.3, right-hand-side reuse),
                               then writes the range's y once.  When most

@@ -1582,7 +1582,7 @@ bool valid_format(int f) { return f >= SPMV_CSR && f <= SPMV_HEC; }
 void choose_col_policy(int opt, Built& b) { b.col_nt = opt != 1; }
 
 // HYB/HEC at ELL width `width` (as choose_width takes it): the split, the
-// window and group choices, and HEC's tail kernel
+// window and group choices, and the tail kernel
 void build_split_tuned(spmv_handle* h, int format, const spmv_convert_opts& o, int width,
                        Built& b, hipStream_t s) {
     b.format = format;
