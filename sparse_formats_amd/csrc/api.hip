@@ -142,6 +142,11 @@ struct Built {
     bool csr_xblock = false;
     DevBuf xb_rows, xb_tiles, xb_col, xb_val, xb_lrow;
     XblkView xb{};
+    void release_xblock() {
+        xb = XblkView{};
+        xb_rows.release(), xb_tiles.release(), xb_col.release();
+        xb_val.release(), xb_lrow.release();
+    }
     // SELL-64 in the permuted basis (x and y in sorted row order)
     bool permuted = false;
     // x staged in LDS by the ELL / tail kernels
@@ -1445,15 +1450,14 @@ void tune_tail(const spmv_handle* h, int format, int kernel, int col_cache, uint
         } catch (const Error& e) {
             if (e.code != SPMV_ERR_NO_MEMORY) throw;
             built = false;  // no room for the optional copy: not a candidate
+            b.release_xblock();  // nor for what was built of it
         }
         if (built) {
             b.tail_xblock = true;
             const float xb_ms = time_launches(run, s);
             if (!(xb_ms < kPreferMargin * cur_ms)) {
                 b.tail_xblock = false;
-                b.xb = XblkView{};
-                b.xb_rows.release(), b.xb_tiles.release(), b.xb_col.release();
-                b.xb_val.release(), b.xb_lrow.release();
+                b.release_xblock();
             }
         }
     }
